@@ -1,0 +1,155 @@
+"""fp64 CPU oracle: plain definitions of non-causal linear attention.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring): never imported by the
+product path. All arithmetic is numpy float64; no blocking, splitting or
+reordering beyond the definitions written out below.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def decode(x: np.ndarray, dtype: str) -> np.ndarray:
+    """Exact float64 value of stored inputs.
+
+    f32 and f16 widen exactly; bf16 is stored as uint16 bit patterns, whose
+    value is the float32 with those bits in the upper half.
+    """
+    if dtype in ("f32", "f16"):
+        return np.asarray(x, dtype=np.float64)
+    if dtype == "bf16":
+        b = np.asarray(x, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+        return b.view(np.float32).astype(np.float64)
+    raise ValueError(f"unknown dtype {dtype!r}")
+
+
+def phi(x: np.ndarray) -> np.ndarray:
+    """Feature map elu(x) + 1, written piecewise: x + 1 for x > 0, exp(x) else.
+
+    The piecewise form avoids computing exp(x) - 1 + 1, which cancels for
+    x << 0. elu is the feature map of the method's statement (FBi-LA README).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    return np.where(x > 0, x + 1.0, np.exp(np.minimum(x, 0.0)))
+
+
+def dphi(x: np.ndarray) -> np.ndarray:
+    """Derivative of phi: 1 for x > 0, exp(x) for x <= 0 (both sides are 1 at 0)."""
+    x = np.asarray(x, dtype=np.float64)
+    return np.where(x > 0, 1.0, np.exp(np.minimum(x, 0.0)))
+
+
+def quadratic_head(q, k, v, eps: float, simple: bool) -> np.ndarray:
+    """Quadratic ("parallel") form for one (batch, head): [T, D] -> [T, D].
+
+    A = phi(Q) phi(K)^T (T x T); normalised: O = (A V) / (A 1 + eps),
+    simple_la: O = A V. flash-linear-attention README, "Different forms of
+    linear attention", Parallel. Cost O(T^2 D): tiny T only.
+    """
+    a = phi(q) @ phi(k).T
+    num = a @ np.asarray(v, dtype=np.float64)
+    if simple:
+        return num
+    return num / (a.sum(axis=1) + eps)[:, None]
+
+
+def fwd_head(q, k, v, eps: float, simple: bool):
+    """Linear form for one (batch, head): returns (O, S, z).
+
+    S = phi(K)^T V (D x D, S[i, j] = sum_t phi(k_t)[i] v_t[j]),
+    z = sum_t phi(k_t), O = phi(Q) S / (phi(Q) z + eps), or phi(Q) S for
+    simple_la (FBi-LA README, intro and "Update" 2024-12-28).
+    """
+    v = np.asarray(v, dtype=np.float64)
+    kt = phi(k)
+    qt = phi(q)
+    s = kt.T @ v
+    z = kt.sum(axis=0)
+    num = qt @ s
+    if simple:
+        return num, s, z
+    den = qt @ z + eps
+    return num / den[:, None], s, z
+
+
+def bwd_head(q, k, v, do, eps: float, simple: bool):
+    """Vector-Jacobian product of L = sum(O * dO) for one (batch, head).
+
+    Returns (dQ, dK, dV). eps is a constant. Derived by the chain rule from
+    fwd_head (the FBi-LA README's "Update" 2024-12-30 names an optimised
+    backward; it prints no formula):
+      u_t   = S dO_t
+      den_t = phi(q_t) . z + eps,  r_t = phi(q_t) . u_t,  c_t = -r_t / den_t^2
+      dphi(q_t) = u_t / den_t + c_t z            (simple_la: u_t)
+      dS    = sum_t phi(q_t) (dO_t / den_t)^T    (simple_la: sum phi(q_t) dO_t^T)
+      dz    = sum_t c_t phi(q_t)                 (simple_la: 0)
+      dphi(k_t) = dS v_t + dz,   dV_t = dS^T phi(k_t)
+      dQ = dphi(q) * phi'(q),  dK = dphi(k) * phi'(k)
+    """
+    v = np.asarray(v, dtype=np.float64)
+    do = np.asarray(do, dtype=np.float64)
+    qt = phi(q)
+    kt = phi(k)
+    s = kt.T @ v
+    z = kt.sum(axis=0)
+    u = do @ s.T  # row t is S dO_t
+    if simple:
+        dqt = u
+        ds = qt.T @ do
+        dkt = v @ ds.T
+    else:
+        den = qt @ z + eps
+        r = np.einsum("td,td->t", qt, u)
+        c = -r / den**2
+        dqt = u / den[:, None] + c[:, None] * z[None, :]
+        ds = qt.T @ (do / den[:, None])
+        dz = c @ qt
+        dkt = v @ ds.T + dz[None, :]
+    dv = kt @ ds
+    return dqt * dphi(q), dkt * dphi(k), dv
+
+
+def sampled_rows_head(q, k, v, rows, eps: float, simple: bool) -> np.ndarray:
+    """Output rows O_t, t in ``rows``, computed one by one from the quadratic form.
+
+    O_t = sum_s a_ts v_s / (sum_s a_ts + eps) with a_ts = phi(q_t) . phi(k_s);
+    cost O(T D) per row, so it serves full-size sequences.
+    """
+    kt = phi(k)
+    v = np.asarray(v, dtype=np.float64)
+    out = np.empty((len(rows), v.shape[1]))
+    for n, t in enumerate(rows):
+        a = kt @ phi(q[t])
+        out[n] = a @ v
+        if not simple:
+            out[n] /= a.sum() + eps
+    return out
+
+
+def _heads(x: np.ndarray, dtype: str):
+    """Decode a [B, H, T, D] storage array to a float64 [B*H, T, D] view."""
+    d = decode(x, dtype)
+    return d.reshape(-1, d.shape[-2], d.shape[-1])
+
+
+def fwd(q, k, v, dtype: str, eps: float, simple: bool):
+    """Forward over [B, H, T, D] storage arrays: (O [B,H,T,D], S [B,H,D,D], z [B,H,D])."""
+    shape = q.shape
+    qh, kh, vh = _heads(q, dtype), _heads(k, dtype), _heads(v, dtype)
+    n, d = qh.shape[0], shape[-1]
+    o = np.empty(qh.shape)
+    s = np.empty((n, d, d))
+    z = np.empty((n, d))
+    for h in range(n):
+        o[h], s[h], z[h] = fwd_head(qh[h], kh[h], vh[h], eps, simple)
+    return o.reshape(shape), s.reshape(shape[:-2] + (d, d)), z.reshape(shape[:-2] + (d,))
+
+
+def bwd(q, k, v, do, dtype: str, eps: float, simple: bool):
+    """Backward over [B, H, T, D] storage arrays: (dQ, dK, dV), each [B,H,T,D] float64."""
+    shape = q.shape
+    qh, kh, vh, dh = (_heads(x, dtype) for x in (q, k, v, do))
+    dq, dk, dv = (np.empty(qh.shape) for _ in range(3))
+    for h in range(qh.shape[0]):
+        dq[h], dk[h], dv[h] = bwd_head(qh[h], kh[h], vh[h], dh[h], eps, simple)
+    return dq.reshape(shape), dk.reshape(shape), dv.reshape(shape)

@@ -1,0 +1,341 @@
+"""Pins of the fp64 oracle against things other than itself.
+
+Each check is chosen so that a plausible slip in the oracle (a dropped term, a
+wrong sign or index, a transposed operand, eps in the wrong place, the wrong
+branch of phi) fails at least one of them:
+  * pure-Python brute force of the quadratic form (a different formula, no numpy)
+  * the hand-worked example in tests/golden/ (exact rationals)
+  * torch's elu for phi, torch fp64 autograd of the quadratic form for the VJP
+  * central finite differences of L = sum(O * dO)
+  * invariants: V = ones, joint K/V permutation, Q-row permutation, linearity
+    in V, the T = 1 closed form, sum_t dV_t and V = c*1 identities.
+"""
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+from synth import WORKLOADS, make_inputs
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "hand_worked_T2_D2.json")
+
+
+def frac_array(rows):
+    return np.array([[float(Fraction(x)) for x in r] for r in rows]) if isinstance(rows[0], list) \
+        else np.array([float(Fraction(x)) for x in rows])
+
+
+def rand(shape, seed, scale=1.0):
+    return np.random.default_rng(seed).standard_normal(shape) * scale
+
+
+# ---------------------------------------------------------------- phi
+
+def test_phi_matches_torch_elu_plus_one():
+    torch = pytest.importorskip("torch")
+    x = np.concatenate([rand(1000, 1) * 4, [0.0, -0.0, 1e-300, -1e-300, -50.0, 30.0]])
+    ref = (torch.nn.functional.elu(torch.from_numpy(x)) + 1).numpy()
+    # torch forms expm1(x) + 1, which loses up to half an ulp of 1 for x < 0
+    np.testing.assert_allclose(oracle.phi(x), ref, rtol=1e-15, atol=2.3e-16)
+
+
+def test_phi_special_values_and_derivative():
+    assert oracle.phi(np.array([0.0]))[0] == 1.0
+    assert oracle.phi(np.array([1.0]))[0] == 2.0
+    assert oracle.phi(np.array([2.5]))[0] == 3.5
+    assert abs(oracle.phi(np.array([-math.log(2)]))[0] - 0.5) < 1e-16
+    # no cancellation for very negative x: phi(-40) = e^-40, not 0
+    assert oracle.phi(np.array([-40.0]))[0] == pytest.approx(math.exp(-40), rel=1e-15)
+    # phi' from central differences, away from the kink of phi'' at 0
+    x = np.array([-3.0, -0.5, -1e-3, 1e-3, 0.7, 4.0])
+    h = 1e-6
+    fd = (oracle.phi(x + h) - oracle.phi(x - h)) / (2 * h)
+    np.testing.assert_allclose(oracle.dphi(x), fd, rtol=1e-8)
+    assert oracle.dphi(np.array([0.0]))[0] == 1.0
+
+
+# ---------------------------------------------------------------- forward
+
+def brute_force(q, k, v, eps, simple):
+    """Pure-Python quadratic form: O_t = sum_s a_ts v_s / (sum_s a_ts + eps)."""
+    def ph(x):
+        return x + 1.0 if x > 0 else math.exp(x)
+    T, D = len(q), len(q[0])
+    out = []
+    for t in range(T):
+        a = [sum(ph(q[t][i]) * ph(k[s][i]) for i in range(D)) for s in range(T)]
+        row = [sum(a[s] * v[s][j] for s in range(T)) for j in range(D)]
+        if not simple:
+            den = sum(a) + eps
+            row = [x / den for x in row]
+        out.append(row)
+    return np.array(out)
+
+
+@pytest.mark.parametrize("simple", [False, True])
+@pytest.mark.parametrize("T,D", [(1, 5), (7, 5), (16, 8), (40, 64)])
+def test_linear_form_matches_brute_force(T, D, simple):
+    q, k, v = rand((T, D), 1), rand((T, D), 2), rand((T, D), 3)
+    eps = 0.3  # large enough that a misplaced eps shows
+    ref = brute_force(q.tolist(), k.tolist(), v.tolist(), eps, simple)
+    o, _, _ = oracle.fwd_head(q, k, v, eps, simple)
+    assert np.max(np.abs(o - ref)) <= 1e-12 * np.max(np.abs(ref))
+    oq = oracle.quadratic_head(q, k, v, eps, simple)
+    assert np.max(np.abs(oq - ref)) <= 1e-12 * np.max(np.abs(ref))
+    rows = [0, T // 2, T - 1]
+    os_ = oracle.sampled_rows_head(q, k, v, rows, eps, simple)
+    assert np.max(np.abs(os_ - ref[rows])) <= 1e-12 * np.max(np.abs(ref))
+
+
+def test_golden_hand_worked_forward():
+    g = json.load(open(GOLDEN))
+    q, k, v = (np.array(g[n], dtype=np.float64) for n in ("q", "k", "v"))
+    o, s, z = oracle.fwd_head(q, k, v, g["eps"], simple=False)
+    np.testing.assert_allclose(o, frac_array(g["normalised"]["o"]), rtol=1e-15)
+    np.testing.assert_allclose(s, frac_array(g["normalised"]["S"]), rtol=1e-15)
+    np.testing.assert_allclose(z, frac_array(g["normalised"]["z"]), rtol=1e-15)
+    o, _, _ = oracle.fwd_head(q, k, v, g["eps"], simple=True)
+    np.testing.assert_allclose(o, frac_array(g["simple"]["o"]), rtol=1e-15)
+    e = g["exp_branch_T1"]
+    q1, k1, v1 = (np.array([e[n]]) for n in ("q", "k", "v"))
+    o, _, _ = oracle.fwd_head(q1, k1, v1, e["eps"], simple=False)
+    np.testing.assert_allclose(o[0], frac_array(e["o_normalised"]), rtol=1e-15)
+    o, _, _ = oracle.fwd_head(q1, k1, v1, e["eps"], simple=True)
+    np.testing.assert_allclose(o[0], frac_array(e["o_simple"]), rtol=1e-15)
+
+
+def test_v_ones_gives_ones_normalised():
+    T, D = 64, 16
+    q, k = rand((T, D), 4), rand((T, D), 5)
+    v = np.ones((T, D))
+    o, _, z = oracle.fwd_head(q, k, v, 0.0, simple=False)
+    np.testing.assert_allclose(o, 1.0, rtol=1e-14)
+    # with eps: O_t = a_t / (a_t + eps) * 1, a_t = phi(q_t) . z; eps = 5 makes it visible
+    eps = 5.0
+    o, _, _ = oracle.fwd_head(q, k, v, eps, simple=False)
+    a = np.array([sum(oracle.phi(q[t]) * z) for t in range(T)])
+    np.testing.assert_allclose(o, np.repeat((a / (a + eps))[:, None], D, axis=1), rtol=1e-14)
+    assert np.all(o < 1.0)
+
+
+@pytest.mark.parametrize("simple", [False, True])
+def test_joint_kv_permutation_invariance(simple):
+    T, D = 100, 16
+    q, k, v = rand((T, D), 6), rand((T, D), 7), rand((T, D), 8)
+    perm = np.random.default_rng(9).permutation(T)
+    o1, s1, z1 = oracle.fwd_head(q, k, v, 1e-6, simple)
+    o2, s2, z2 = oracle.fwd_head(q, k[perm], v[perm], 1e-6, simple)
+    np.testing.assert_allclose(o2, o1, rtol=1e-12, atol=1e-13 * np.abs(o1).max())
+    # permuting only V (not K) must change the result: pins pairing of k_t with v_t
+    o3, _, _ = oracle.fwd_head(q, k, v[perm], 1e-6, simple)
+    assert np.max(np.abs(o3 - o1)) > 1e-3 * np.abs(o1).max()
+
+
+@pytest.mark.parametrize("simple", [False, True])
+def test_q_row_permutation_equivariance(simple):
+    T, D = 50, 8
+    q, k, v = rand((T, D), 10), rand((T, D), 11), rand((T, D), 12)
+    perm = np.random.default_rng(13).permutation(T)
+    o1, _, _ = oracle.fwd_head(q, k, v, 1e-6, simple)
+    o2, _, _ = oracle.fwd_head(q[perm], k, v, 1e-6, simple)
+    np.testing.assert_allclose(o2, o1[perm], rtol=1e-14)
+
+
+@pytest.mark.parametrize("simple", [False, True])
+def test_t1_closed_form(simple):
+    D = 6
+    q, k, v = rand((1, D), 14), rand((1, D), 15), rand((1, D), 16)
+    eps = 0.25
+    a = sum((qi + 1 if qi > 0 else math.exp(qi)) * (ki + 1 if ki > 0 else math.exp(ki))
+            for qi, ki in zip(q[0], k[0]))
+    expect = a * v[0] if simple else a / (a + eps) * v[0]
+    o, _, _ = oracle.fwd_head(q, k, v, eps, simple)
+    np.testing.assert_allclose(o[0], expect, rtol=1e-14)
+
+
+@pytest.mark.parametrize("simple", [False, True])
+def test_linearity_in_v(simple):
+    T, D = 30, 8
+    q, k = rand((T, D), 17), rand((T, D), 18)
+    v1, v2 = rand((T, D), 19), rand((T, D), 20)
+    a, b = 0.7, -2.5
+    o1, _, _ = oracle.fwd_head(q, k, v1, 1e-3, simple)
+    o2, _, _ = oracle.fwd_head(q, k, v2, 1e-3, simple)
+    o3, _, _ = oracle.fwd_head(q, k, a * v1 + b * v2, 1e-3, simple)
+    np.testing.assert_allclose(o3, a * o1 + b * o2, rtol=1e-12, atol=1e-13 * np.abs(o3).max())
+
+
+def test_batched_fwd_matches_per_head_and_decodes():
+    from synth import Workload
+    w = Workload("t", 2, 3, 20, 8, "bf16", seed=77)
+    x = make_inputs(w, with_grad=False)
+    o, s, z = oracle.fwd(x["q"], x["k"], x["v"], "bf16", 1e-6, False)
+    assert o.shape == (2, 3, 20, 8) and s.shape == (2, 3, 8, 8) and z.shape == (2, 3, 8)
+    qd = oracle.decode(x["q"], "bf16")
+    # bf16 values decode to float32-representable numbers with 8-bit mantissas
+    m, _ = np.frexp(qd)
+    assert np.all((m * 256) == np.round(m * 256))
+    o11, s11, _ = oracle.fwd_head(qd[1, 1], oracle.decode(x["k"], "bf16")[1, 1],
+                                  oracle.decode(x["v"], "bf16")[1, 1], 1e-6, False)
+    np.testing.assert_array_equal(o[1, 1], o11)
+    np.testing.assert_array_equal(s[1, 1], s11)
+
+
+# ---------------------------------------------------------------- backward
+
+def loss(q, k, v, do, eps, simple):
+    o, _, _ = oracle.fwd_head(q, k, v, eps, simple)
+    return float(np.sum(o * do))
+
+
+def finite_difference(q, k, v, do, eps, simple, which, coords, h=1e-6):
+    arrs = {"q": q, "k": k, "v": v}
+    out = []
+    for (t, d) in coords:
+        plus = {n: a.copy() for n, a in arrs.items()}
+        minus = {n: a.copy() for n, a in arrs.items()}
+        plus[which][t, d] += h
+        minus[which][t, d] -= h
+        out.append((loss(plus["q"], plus["k"], plus["v"], do, eps, simple)
+                    - loss(minus["q"], minus["k"], minus["v"], do, eps, simple)) / (2 * h))
+    return np.array(out)
+
+
+def away_from_zero(x, margin):
+    return np.where(np.abs(x) < margin, np.sign(x + 1e-30) * margin * 3, x)
+
+
+@pytest.mark.parametrize("simple", [False, True])
+@pytest.mark.parametrize("T,D", [(5, 3), (16, 8)])
+def test_bwd_matches_finite_differences_all_coords(T, D, simple):
+    # inputs kept away from 0 where phi'' jumps; eps large enough to matter
+    q = away_from_zero(rand((T, D), 21), 1e-4)
+    k = away_from_zero(rand((T, D), 22), 1e-4)
+    v, do = rand((T, D), 23), rand((T, D), 24)
+    eps = 0.5
+    dq, dk, dv = oracle.bwd_head(q, k, v, do, eps, simple)
+    coords = [(t, d) for t in range(T) for d in range(D)]
+    for name, g in (("q", dq), ("k", dk), ("v", dv)):
+        fd = finite_difference(q, k, v, do, eps, simple, name, coords).reshape(T, D)
+        assert np.max(np.abs(g - fd)) <= 1e-6 * max(1.0, np.abs(fd).max()), name
+
+
+@pytest.mark.parametrize("simple", [False, True])
+def test_bwd_finite_differences_sampled_tiny_config_shape(simple):
+    T, D = 128, 64
+    q = away_from_zero(rand((T, D), 31), 1e-4)
+    k = away_from_zero(rand((T, D), 32), 1e-4)
+    v, do = rand((T, D), 33), rand((T, D), 34)
+    eps = 1e-6
+    dq, dk, dv = oracle.bwd_head(q, k, v, do, eps, simple)
+    rng = np.random.default_rng(35)
+    coords = [(int(rng.integers(T)), int(rng.integers(D))) for _ in range(24)]
+    for name, g in (("q", dq), ("k", dk), ("v", dv)):
+        fd = finite_difference(q, k, v, do, eps, simple, name, coords, h=1e-5)
+        got = np.array([g[t, d] for t, d in coords])
+        assert np.max(np.abs(got - fd)) <= 1e-5 * max(np.abs(fd).max(), 1e-12), name
+
+
+@pytest.mark.parametrize("simple", [False, True])
+def test_bwd_matches_torch_autograd_of_quadratic_form(simple):
+    torch = pytest.importorskip("torch")
+    T, D = 48, 16
+    q, k, v, do = (rand((T, D), s) for s in (41, 42, 43, 44))
+    eps = 0.05
+    tq, tk, tv = (torch.tensor(a, dtype=torch.float64, requires_grad=True) for a in (q, k, v))
+    fq = torch.nn.functional.elu(tq) + 1
+    fk = torch.nn.functional.elu(tk) + 1
+    a = fq @ fk.T
+    o = a @ tv
+    if not simple:
+        o = o / (a.sum(dim=1, keepdim=True) + eps)
+    (o * torch.tensor(do)).sum().backward()
+    dq, dk, dv = oracle.bwd_head(q, k, v, do, eps, simple)
+    for g, t in ((dq, tq), (dk, tk), (dv, tv)):
+        ref = t.grad.numpy()
+        assert np.max(np.abs(g - ref)) <= 1e-12 * np.abs(ref).max()
+
+
+def test_golden_hand_worked_backward():
+    g = json.load(open(GOLDEN))
+    q, k, v, do = (np.array(g[n], dtype=np.float64) for n in ("q", "k", "v", "do"))
+    for mode, simple in (("normalised", False), ("simple", True)):
+        dq, dk, dv = oracle.bwd_head(q, k, v, do, g["eps"], simple)
+        np.testing.assert_allclose(dq, frac_array(g[mode]["dq"]), rtol=1e-14, atol=1e-16)
+        np.testing.assert_allclose(dk, frac_array(g[mode]["dk"]), rtol=1e-14, atol=1e-16)
+        np.testing.assert_allclose(dv, frac_array(g[mode]["dv"]), rtol=1e-14, atol=1e-16)
+
+
+def test_bwd_dv_column_sum_identity():
+    # sum_t dV_t = sum_s dO_s * a_s / (a_s + eps), a_s = phi(q_s) . z
+    T, D = 70, 12
+    q, k, v, do = (rand((T, D), s) for s in (51, 52, 53, 54))
+    eps = 2.0
+    _, dk, dv = oracle.bwd_head(q, k, v, do, eps, simple=False)
+    _, _, z = oracle.fwd_head(q, k, v, eps, simple=False)
+    a = np.array([np.dot(oracle.phi(q[s]), z) for s in range(T)])
+    np.testing.assert_allclose(dv.sum(axis=0), (do * (a / (a + eps))[:, None]).sum(axis=0),
+                               rtol=1e-12)
+
+
+def test_bwd_constant_v_gives_zero_dq_dk():
+    # V = c*1 makes O_t = c a_t/(a_t+eps): with eps = 0 O is constant, so dQ = dK = 0
+    T, D = 40, 8
+    q, k, do = rand((T, D), 61), rand((T, D), 62), rand((T, D), 63)
+    v = np.full((T, D), -1.75)
+    dq, dk, dv = oracle.bwd_head(q, k, v, do, 0.0, simple=False)
+    assert np.abs(dq).max() < 1e-14 and np.abs(dk).max() < 1e-14
+    assert np.abs(dv).max() > 1e-2
+
+
+def test_batched_bwd_matches_per_head():
+    from synth import Workload
+    w = Workload("t", 1, 2, 33, 8, "f16", seed=88)
+    x = make_inputs(w)
+    dq, dk, dv = oracle.bwd(x["q"], x["k"], x["v"], x["do"], "f16", 1e-6, False)
+    ref = oracle.bwd_head(*(oracle.decode(x[n], "f16")[0, 1] for n in ("q", "k", "v", "do")),
+                          1e-6, False)
+    for a, b in zip((dq[0, 1], dk[0, 1], dv[0, 1]), ref):
+        np.testing.assert_array_equal(a, b)
+
+
+# ---------------------------------------------------------------- planted mistakes
+
+def test_pins_catch_planted_mistakes(monkeypatch):
+    """Plant plausible slips in a copy of the oracle's forward and check that the
+    pins above would fail on each one (the pins compare against brute force)."""
+    T, D = 9, 4
+    q, k, v = rand((T, D), 71), rand((T, D), 72), rand((T, D), 73)
+    ref = brute_force(q.tolist(), k.tolist(), v.tolist(), 0.3, False)
+
+    def variant(kind):
+        qt, kt = oracle.phi(q), oracle.phi(k)
+        if kind == "elu_no_plus_one":
+            qt, kt = qt - 1, kt - 1
+        s = kt.T @ v
+        if kind == "transposed_state":
+            s = s.T
+        z = kt.sum(0)
+        den = qt @ z + (0.0 if kind == "no_eps" else 0.3)
+        if kind == "eps_multiplied":
+            den = (qt @ z) * (1 + 0.3)
+        return (qt @ s) / den[:, None]
+
+    for kind in ("elu_no_plus_one", "transposed_state", "no_eps", "eps_multiplied"):
+        bad = variant(kind)
+        assert np.max(np.abs(bad - ref)) > 1e-6 * np.abs(ref).max(), kind
+    assert np.max(np.abs(variant("none") - ref)) <= 1e-12 * np.abs(ref).max()
+
+
+def test_workloads_inputs_are_seeded_and_rounded():
+    w = WORKLOADS["B1-H2-T128-D64-f32"]
+    a = make_inputs(w)
+    b = make_inputs(w)
+    for n in a:
+        np.testing.assert_array_equal(a[n], b[n])
+    assert a["q"].dtype == np.float32 and a["q"].shape == (1, 2, 128, 64)
+    assert not np.array_equal(a["q"], a["k"])
