@@ -1,0 +1,241 @@
+"""Benchmark: bidirectional linear attention, forward + backward, one MI355X.
+
+One step is one pass of the whole path over one batch: la_fwd_state (phi, split-T
+state reduction, combine), la_fwd_output (O), la_bwd_dq (dQ and the dS, dz
+state), la_bwd_dkv (dK, dV) -- exactly the launches of la_fwd then la_bwd, on
+torch's current stream. HIP events bracket every launch, so each kernel's
+duration is measured live; the infinity cache and L2 are flushed before every
+step (outside the events) by writing a 1 GiB scratch buffer.
+
+Prints one JSON line. `value` is the forward's algorithmic HBM rate (Q, K, V
+read and O written once) in GB/s; fwd/bwd/fwd+bwd milliseconds ride along.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import non_causal_linear_amd as la  # noqa: E402
+from synth import HEADLINE, WORKLOADS, make_inputs  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+# FBi-LA README, "Benchmarks" (A800 80G, B8-H16-D64, T = 16384), in ms.
+PAGE_A800_FWD_MS = 0.980992
+PAGE_A800_BWD_MS = 5.022208
+
+KERNELS = ("fwd_state", "fwd_output", "bwd_dq", "bwd_dkv")
+# Algorithmic HBM traffic per launch, in tensors of N = B*H*T*D elements:
+# state reads K, V; output reads Q, writes O; dq reads Q, dO, writes dQ;
+# dkv reads K, V, writes dK, dV.
+TENSORS_PER_LAUNCH = {"fwd_state": 2, "fwd_output": 2, "bwd_dq": 3, "bwd_dkv": 4}
+DTYPE_NAME = {"f32": "f32", "f16": "f16", "bf16": "bf16"}
+
+
+def to_device(x: np.ndarray, dtype: str) -> torch.Tensor:
+    if dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(x)).cuda()
+
+
+def cpu_baseline(w, x, max_heads: int) -> dict:
+    """The fp64 oracle as it stands, forward then backward, per head on a thread pool."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+
+    n = w.B * w.H
+    heads = min(n, max_heads)
+    cores = len(os.sched_getaffinity(0))
+    cores = max(1, min(cores, 16))
+    qh, kh, vh, dh = (x[nm].reshape(n, w.T, w.D) for nm in ("q", "k", "v", "do"))
+
+    def fwd_one(h):
+        return oracle.fwd_head(oracle.decode(qh[h], w.dtype), oracle.decode(kh[h], w.dtype),
+                               oracle.decode(vh[h], w.dtype), w.eps, w.simple)[0].shape
+
+    def bwd_one(h):
+        return oracle.bwd_head(oracle.decode(qh[h], w.dtype), oracle.decode(kh[h], w.dtype),
+                               oracle.decode(vh[h], w.dtype), oracle.decode(dh[h], w.dtype),
+                               w.eps, w.simple)[0].shape
+
+    with threadpool_limits(1), ThreadPoolExecutor(max_workers=cores) as pool:
+        list(pool.map(fwd_one, range(min(heads, cores))))  # warm-up
+        t0 = time.perf_counter()
+        list(pool.map(fwd_one, range(heads)))
+        t1 = time.perf_counter()
+        list(pool.map(bwd_one, range(heads)))
+        t2 = time.perf_counter()
+    fwd_bytes = 4 * heads * w.T * w.D * w.elem_bytes
+    model = ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {
+        "value": fwd_bytes / (t1 - t0) / 1e9,
+        "unit": "GB/s",
+        "cores": cores,
+        "kind": "oracle",
+        "sample": f"{heads} of {n} heads at T={w.T}, D={w.D}: fp64 forward then backward, "
+                  f"one head per thread",
+        "fwd_ms_sample": (t1 - t0) * 1e3,
+        "bwd_ms_sample": (t2 - t1) * 1e3,
+        "cpu": model,
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=HEADLINE, choices=list(WORKLOADS))
+    ap.add_argument("--no-flush", action="store_true", help="skip the cache flush between steps")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-heads", type=int, default=128, help="heads in the oracle sample")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run one plain 1 GiB device copy (for counter scaling)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              f"(the path shards over heads with no communication; see the design notes)",
+              file=sys.stderr)
+        return 2
+    if int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py is a single-process, single-GPU benchmark", file=sys.stderr)
+        return 2
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+
+    w = WORKLOADS[args.workload]
+    print(f"[bench] workload {w.name}: generating inputs", file=sys.stderr, flush=True)
+    x = make_inputs(w, with_grad=True)
+    dev = {n: to_device(a, w.dtype) for n, a in x.items()}
+    q, k, v, do = dev["q"], dev["k"], dev["v"], dev["do"]
+    prob = la.make_problem(q.shape, q.dtype, w.eps, w.simple)
+    state = la.new_state(prob, q.device)
+    ws = la.workspace(prob, q.device)
+    o, dq, dk, dv = (torch.empty_like(q) for _ in range(4))
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+
+    def step(ev):
+        ev[0].record()
+        la.fwd_state(k, v, eps=w.eps, simple=w.simple, state=state, ws=ws)
+        ev[1].record()
+        la.fwd_output(q, state, eps=w.eps, simple=w.simple, out=o)
+        ev[2].record()
+        if w.bwd:
+            la.bwd_dq(q, do, state, eps=w.eps, simple=w.simple, dq=dq, ws=ws)
+            ev[3].record()
+            la.bwd_dkv(k, v, eps=w.eps, simple=w.simple, dk=dk, dv=dv, ws=ws)
+        else:
+            ev[3].record()
+        ev[4].record()
+
+    mk = lambda: [torch.cuda.Event(enable_timing=True) for _ in range(5)]  # noqa: E731
+    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        if not args.no_flush:
+            flush.fill_(1)
+        step(mk())
+    torch.cuda.synchronize()
+
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    events = [mk() for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        if not args.no_flush:
+            flush.fill_(1)  # evict the 256 MB infinity cache and L2, outside the events
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    per = {kname: np.array([ev[j].elapsed_time(ev[j + 1]) for ev in events])
+           for j, kname in enumerate(KERNELS)}
+    if not w.bwd:
+        per = {kname: per[kname] for kname in ("fwd_state", "fwd_output")}
+    step_ms = np.array([ev[0].elapsed_time(ev[4]) for ev in events])
+    fwd_ms = per["fwd_state"] + per["fwd_output"]
+    N = w.numel
+    elt = w.elem_bytes
+    fwd_bytes = 4 * N * elt
+    value = fwd_bytes / (float(np.mean(fwd_ms)) * 1e-3) / 1e9
+
+    avg = {kname: float(np.mean(a)) for kname, a in per.items()}
+    dominant = max(avg, key=avg.get)
+    dom_bytes = TENSORS_PER_LAUNCH[dominant] * N * elt
+    achieved = dom_bytes / (avg[dominant] * 1e-3) / 1e9
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+
+    line = {
+        "metric": "non-causal LA fwd GB/s & ms (B8-H16-T16384-D64 fp16); fwd+bwd ms",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(float(np.mean(step_ms)), 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": DTYPE_NAME[w.dtype],
+        "data": "synthetic: seeded N(0, sigma^2) Q, K, V, dO rounded to the dtype",
+        "config": {
+            "workload": w.name + ("-simple" if w.simple and "simple" not in w.name else ""),
+            "B": w.B, "H": w.H, "T": w.T, "D": w.D,
+            "mode": "simple_la" if w.simple else "normalised",
+            "eps": w.eps,
+            "pass": "fwd+bwd" if w.bwd else "fwd",
+            "cache_flush_between_steps": not args.no_flush,
+        },
+        "fwd_ms": round(float(np.mean(fwd_ms)), 4),
+        "fwd_ms_min": round(float(np.min(fwd_ms)), 4),
+        "fwd_frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
+        "kernel_ms": {kname: round(a, 4) for kname, a in avg.items()},
+        "wall_ms_per_step_incl_flush": round(wall / args.steps * 1e3, 4),
+        "roofline": {
+            "kernel": dominant,
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None,
+        },
+    }
+    if w.bwd:
+        bwd_ms = per["bwd_dq"] + per["bwd_dkv"]
+        line["bwd_ms"] = round(float(np.mean(bwd_ms)), 4)
+        line["fwd_bwd_ms"] = round(float(np.mean(step_ms)), 4)
+    if w.name == HEADLINE:
+        line["context_pages_a800_triton"] = {"fwd_ms": PAGE_A800_FWD_MS, "bwd_ms": PAGE_A800_BWD_MS,
+                                             "note": "another GPU, dtype unstated: context only"}
+    if not args.no_cpu_baseline:
+        print("[bench] oracle on host cores", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(w, x, args.cpu_heads)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

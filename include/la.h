@@ -1,0 +1,146 @@
+/*
+ * la.h - C ABI of a gfx950 (MI355X) library for bidirectional (non-causal)
+ * linear attention, forward and backward.
+ *
+ * The operation (Flash Bi-directional Linear Attention README: intro, and
+ * "Update" 2024-12-28 for simple_la, "Update" 2024-12-30 for the backward).
+ * Per batch b and head h, with Q, K, V in R^{T x D} and phi(x) = elu(x) + 1
+ * (x + 1 for x > 0, e^x otherwise):
+ *     S = sum_t phi(k_t) v_t^T          (D x D, S[i][j])
+ *     z = sum_t phi(k_t)                (D)
+ *     O_t = phi(q_t) S / (phi(q_t) . z + eps)      normalised (default)
+ *     O_t = phi(q_t) S                              simple_la (LA_SIMPLE)
+ * The backward returns dQ, dK, dV, the vector-Jacobian product of
+ * L = sum(O * dO) with eps held constant.
+ *
+ * Layout. Every tensor q, k, v, o, dout, dq, dk, dv is a dense row-major
+ * [B, H, T, D] array of `dtype` elements (D contiguous), 16-byte aligned.
+ * `state` is fp32: B*H blocks of S (D*D floats, S[i][j] at i*D + j) followed by
+ * B*H blocks of z (D floats); la_state_bytes() gives its size.
+ *
+ * Ownership. The caller allocates and owns all device memory: tensors, state
+ * and workspace. The library never allocates, frees, synchronises or prints.
+ * Work is enqueued on `stream` (a hipStream_t; NULL is the null stream) and
+ * the call returns without waiting.
+ *
+ * Workspace. `ws` must be at least la_workspace_bytes() bytes, 256-byte
+ * aligned, and ALL ZERO before its first use. The kernels leave it zeroed
+ * where it matters (per-head arrival counters are reset by the workgroup that
+ * finishes each head), so one zero-filled workspace can be reused by any
+ * number of calls in stream order. Calls that overlap in time (different
+ * streams, no ordering) must use different workspaces.
+ *
+ * Errors. Every argument is checked before any HIP call, so a call that
+ * returns a validation error has enqueued nothing. LA_ERR_DEVICE reports a
+ * HIP launch error. Nothing is thrown across the ABI.
+ *
+ * Numerics. Inputs are read in `dtype`; phi is evaluated in fp32; matrix
+ * products run on MFMA with fp32 accumulation (16-bit operands for f16/bf16,
+ * fp32 operands for f32); S, z and their gradients are kept in fp32; outputs
+ * are rounded to nearest-even into `dtype`. For f16 the fp32 states are
+ * scaled by an exact power of two before they become f16 operands and unscaled
+ * in fp32 afterwards. Results are bit-identical across runs for identical
+ * inputs, problem and device: the work split is a pure function of the shape
+ * and every reduction runs in a fixed order (no floating-point atomics).
+ */
+#ifndef LA_H_
+#define LA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LA_VERSION 1
+
+typedef enum {
+    LA_F32 = 0,
+    LA_F16 = 1,
+    LA_BF16 = 2
+} la_dtype;
+
+typedef enum {
+    LA_OK = 0,
+    LA_ERR_NULL = 1,       /* a required pointer is NULL                      */
+    LA_ERR_SHAPE = 2,      /* B, H or T negative, or sizes overflow           */
+    LA_ERR_DTYPE = 3,      /* dtype not one of la_dtype                       */
+    LA_ERR_HEAD_DIM = 4,   /* D not supported (64 and 128 are)                */
+    LA_ERR_FLAGS = 5,      /* unknown bit in flags                            */
+    LA_ERR_EPS = 6,        /* eps negative or not finite                      */
+    LA_ERR_WORKSPACE = 7,  /* ws_bytes below la_workspace_bytes()             */
+    LA_ERR_ALIGN = 8,      /* a tensor is not 16-byte aligned, ws not 256     */
+    LA_ERR_ALIAS = 9,      /* an output overlaps an input or another output   */
+    LA_ERR_DEVICE = 10     /* HIP reported an error on launch                 */
+} la_status;
+
+/* Drop the denominator: simple_la (FBi-LA README, "Update" 2024-12-28). */
+#define LA_SIMPLE 0x1u
+
+/* Problem description shared by every call. B, H, T >= 0 (a zero size is an
+ * empty problem: nothing to compute, LA_OK), D in {64, 128}, eps >= 0 and
+ * finite (used only in normalised mode). */
+typedef struct {
+    int64_t B, H, T, D;
+    int32_t dtype;   /* la_dtype */
+    uint32_t flags;  /* 0 or LA_SIMPLE */
+    float eps;
+} la_problem;
+
+/* Library version (LA_VERSION of the build). */
+int la_version(void);
+
+/* Static string naming a status code; never NULL. */
+const char* la_status_str(int status);
+
+/* Bytes of the fp32 state: B*H*(D*D + D)*4. 0 for an invalid problem. */
+size_t la_state_bytes(const la_problem* p);
+
+/* Bytes of workspace that la_fwd, la_bwd and the step calls below need for
+ * this problem (the largest of them). 0 for an invalid problem. */
+size_t la_workspace_bytes(const la_problem* p);
+
+/* Forward: O (and the state S, z) from Q, K, V. Runs la_fwd_state, then
+ * la_fwd_output. `state` may be NULL when the caller does not keep it; the
+ * workspace then holds it. */
+int la_fwd(const la_problem* p, const void* q, const void* k, const void* v,
+           void* o, void* state, void* ws, size_t ws_bytes, void* stream);
+
+/* Backward: dQ, dK, dV from Q, K, V, dO and the state la_fwd wrote (the
+ * state is required: S and z are not recomputed). Runs la_bwd_dq, then
+ * la_bwd_dkv. */
+int la_bwd(const la_problem* p, const void* q, const void* k, const void* v,
+           const void* dout, const void* state, void* dq, void* dk, void* dv,
+           void* ws, size_t ws_bytes, void* stream);
+
+/* ---- The steps of the path, one call each (la_fwd and la_bwd are exactly
+ * these calls in order). ---- */
+
+/* Steps 1-3: phi on K, split-T reduction of each head's token range into
+ * partial (S, z) on MFMA, then a fixed-order sum of the partials into
+ * `state` (non-NULL here). */
+int la_fwd_state(const la_problem* p, const void* k, const void* v, void* state,
+                 void* ws, size_t ws_bytes, void* stream);
+
+/* Step 4: O_t = phi(q_t) S / (phi(q_t) . z + eps) (or phi(q_t) S) from a
+ * complete state. Needs no workspace. */
+int la_fwd_output(const la_problem* p, const void* q, const void* state, void* o,
+                  void* stream);
+
+/* Steps 5-6: dQ, and the backward state dS = sum_t phi(q_t) (dO_t/den_t)^T,
+ * dz = sum_t c_t phi(q_t) (simple_la: dS = phi(Q)^T dO, dz = 0), reduced split-T
+ * with a fixed-order combine into the workspace. */
+int la_bwd_dq(const la_problem* p, const void* q, const void* dout, const void* state,
+              void* dq, void* ws, size_t ws_bytes, void* stream);
+
+/* Step 7: dK = (dS v_t + dz) * phi'(k_t), dV_t = dS^T phi(k_t), reading the
+ * backward state that la_bwd_dq left in the same workspace. */
+int la_bwd_dkv(const la_problem* p, const void* k, const void* v, void* dk, void* dv,
+               void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LA_H_ */

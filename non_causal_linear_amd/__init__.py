@@ -1,0 +1,230 @@
+"""Python binding of libla.so: bidirectional (non-causal) linear attention on gfx950.
+
+Argument marshalling only. Every step of the computation runs in the HIP
+kernels behind the C ABI declared in include/la.h; this module turns torch
+tensors into device pointers, passes torch's current HIP stream, allocates
+outputs and a zero-filled workspace, and turns status codes into exceptions.
+There is no fallback: if libla.so is missing or a call fails, it raises.
+
+torch is imported before the library is loaded so that libla.so binds to the
+HIP runtime torch already has in the process (both carry the SONAME
+libamdhip64.so.7), which keeps torch's stream handles valid in the library.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "LAError", "lib", "fwd", "bwd", "fwd_state", "fwd_output", "bwd_dq", "bwd_dkv",
+    "state_bytes", "workspace_bytes", "new_state", "workspace", "Problem",
+    "LA_F32", "LA_F16", "LA_BF16", "LA_SIMPLE", "EXPORTS",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libla.so")
+
+LA_F32, LA_F16, LA_BF16 = 0, 1, 2
+LA_SIMPLE = 0x1
+DTYPE_CODE = {torch.float32: LA_F32, torch.float16: LA_F16, torch.bfloat16: LA_BF16}
+
+# Every symbol include/la.h declares.
+EXPORTS = ("la_version", "la_status_str", "la_state_bytes", "la_workspace_bytes", "la_fwd",
+           "la_bwd", "la_fwd_state", "la_fwd_output", "la_bwd_dq", "la_bwd_dkv")
+
+
+class Problem(ctypes.Structure):
+    """Mirror of la_problem."""
+    _fields_ = [("B", ctypes.c_int64), ("H", ctypes.c_int64), ("T", ctypes.c_int64),
+                ("D", ctypes.c_int64), ("dtype", ctypes.c_int32), ("flags", ctypes.c_uint32),
+                ("eps", ctypes.c_float)]
+
+
+class LAError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{message} (status {status})")
+        self.status = status
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libla.so (once) and declare the C signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run `python -m non_causal_linear_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    P = ctypes.POINTER(Problem)
+    vp, sz = ctypes.c_void_p, ctypes.c_size_t
+    L.la_version.restype = ctypes.c_int
+    L.la_version.argtypes = []
+    L.la_status_str.restype = ctypes.c_char_p
+    L.la_status_str.argtypes = [ctypes.c_int]
+    L.la_state_bytes.restype = sz
+    L.la_state_bytes.argtypes = [P]
+    L.la_workspace_bytes.restype = sz
+    L.la_workspace_bytes.argtypes = [P]
+    sigs = {
+        "la_fwd": [P, vp, vp, vp, vp, vp, vp, sz, vp],
+        "la_bwd": [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
+        "la_fwd_state": [P, vp, vp, vp, vp, sz, vp],
+        "la_fwd_output": [P, vp, vp, vp, vp],
+        "la_bwd_dq": [P, vp, vp, vp, vp, vp, sz, vp],
+        "la_bwd_dkv": [P, vp, vp, vp, vp, vp, sz, vp],
+    }
+    for name, args in sigs.items():
+        fn = getattr(L, name)
+        fn.restype = ctypes.c_int
+        fn.argtypes = args
+    _lib = L
+    return L
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise LAError(status, lib().la_status_str(status).decode())
+
+
+def make_problem(shape, dtype: torch.dtype, eps: float, simple: bool) -> Problem:
+    if len(shape) != 4:
+        raise ValueError(f"expected a [B, H, T, D] tensor, got shape {tuple(shape)}")
+    if dtype not in DTYPE_CODE:
+        raise ValueError(f"unsupported dtype {dtype}")
+    B, H, T, D = (int(x) for x in shape)
+    return Problem(B, H, T, D, DTYPE_CODE[dtype], LA_SIMPLE if simple else 0, float(eps))
+
+
+def _tensor(x: torch.Tensor, like: torch.Tensor | None, name: str) -> torch.Tensor:
+    if not isinstance(x, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if x.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU, got {x.device}")
+    if not x.is_contiguous():
+        raise ValueError(f"{name} must be contiguous [B, H, T, D]")
+    if like is not None and (x.shape != like.shape or x.dtype != like.dtype or x.device != like.device):
+        raise ValueError(f"{name} must match q in shape, dtype and device")
+    return x
+
+
+def _ptr(x: torch.Tensor | None):
+    return None if x is None else ctypes.c_void_p(x.data_ptr())
+
+
+def _stream(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def state_bytes(prob: Problem) -> int:
+    return int(lib().la_state_bytes(ctypes.byref(prob)))
+
+
+def workspace_bytes(prob: Problem) -> int:
+    return int(lib().la_workspace_bytes(ctypes.byref(prob)))
+
+
+def new_state(prob: Problem, device) -> torch.Tensor:
+    """fp32 state buffer: B*H blocks of S (D*D) followed by B*H blocks of z (D)."""
+    return torch.empty(state_bytes(prob) // 4, dtype=torch.float32, device=device)
+
+
+_ws_cache: dict = {}
+
+
+def workspace(prob: Problem, device) -> torch.Tensor:
+    """A zero-filled workspace for this device and its current stream, reused across calls.
+
+    The kernels leave the workspace's counters at zero, so reuse in stream order is
+    valid; a different stream gets its own workspace.
+    """
+    device = torch.device(device)
+    key = (device, torch.cuda.current_stream(device).cuda_stream)
+    need = max(workspace_bytes(prob), 256)
+    ws = _ws_cache.get(key)
+    if ws is None or ws.numel() < need:
+        ws = torch.zeros(need, dtype=torch.uint8, device=device)
+        _ws_cache[key] = ws
+    return ws
+
+
+def _ws(prob, device, ws):
+    ws = workspace(prob, device) if ws is None else ws
+    return ws, ctypes.c_size_t(ws.numel() * ws.element_size())
+
+
+def fwd_state(k, v, *, eps=1e-6, simple=False, state=None, ws=None):
+    """Steps 1-3: the fp32 state (S, z) of phi(K), V."""
+    _tensor(k, None, "k")
+    _tensor(v, k, "v")
+    prob = make_problem(k.shape, k.dtype, eps, simple)
+    state = new_state(prob, k.device) if state is None else state
+    ws, wsb = _ws(prob, k.device, ws)
+    _check(lib().la_fwd_state(ctypes.byref(prob), _ptr(k), _ptr(v), _ptr(state), _ptr(ws), wsb,
+                              _stream(k.device)))
+    return state
+
+
+def fwd_output(q, state, *, eps=1e-6, simple=False, out=None):
+    """Step 4: O from Q and a complete state."""
+    _tensor(q, None, "q")
+    prob = make_problem(q.shape, q.dtype, eps, simple)
+    out = torch.empty_like(q) if out is None else _tensor(out, q, "out")
+    _check(lib().la_fwd_output(ctypes.byref(prob), _ptr(q), _ptr(state), _ptr(out), _stream(q.device)))
+    return out
+
+
+def fwd(q, k, v, *, eps=1e-6, simple=False, out=None, state=None, ws=None):
+    """O = phi(Q) S / (phi(Q) z + eps) (or phi(Q) S); returns (O, state)."""
+    _tensor(q, None, "q")
+    _tensor(k, q, "k")
+    _tensor(v, q, "v")
+    prob = make_problem(q.shape, q.dtype, eps, simple)
+    out = torch.empty_like(q) if out is None else _tensor(out, q, "out")
+    state = new_state(prob, q.device) if state is None else state
+    ws, wsb = _ws(prob, q.device, ws)
+    _check(lib().la_fwd(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(state),
+                        _ptr(ws), wsb, _stream(q.device)))
+    return out, state
+
+
+def bwd_dq(q, do, state, *, eps=1e-6, simple=False, dq=None, ws=None):
+    """Steps 5-6: dQ; leaves dS, dz in the workspace for bwd_dkv."""
+    _tensor(q, None, "q")
+    _tensor(do, q, "do")
+    prob = make_problem(q.shape, q.dtype, eps, simple)
+    dq = torch.empty_like(q) if dq is None else _tensor(dq, q, "dq")
+    ws, wsb = _ws(prob, q.device, ws)
+    _check(lib().la_bwd_dq(ctypes.byref(prob), _ptr(q), _ptr(do), _ptr(state), _ptr(dq), _ptr(ws), wsb,
+                           _stream(q.device)))
+    return dq
+
+
+def bwd_dkv(k, v, *, eps=1e-6, simple=False, dk=None, dv=None, ws=None):
+    """Step 7: dK, dV from the backward state bwd_dq left in the same workspace."""
+    _tensor(k, None, "k")
+    _tensor(v, k, "v")
+    prob = make_problem(k.shape, k.dtype, eps, simple)
+    dk = torch.empty_like(k) if dk is None else _tensor(dk, k, "dk")
+    dv = torch.empty_like(k) if dv is None else _tensor(dv, k, "dv")
+    ws, wsb = _ws(prob, k.device, ws)
+    _check(lib().la_bwd_dkv(ctypes.byref(prob), _ptr(k), _ptr(v), _ptr(dk), _ptr(dv), _ptr(ws), wsb,
+                            _stream(k.device)))
+    return dk, dv
+
+
+def bwd(q, k, v, do, state, *, eps=1e-6, simple=False, dq=None, dk=None, dv=None, ws=None):
+    """dQ, dK, dV of L = sum(O * dO), from the state fwd returned."""
+    _tensor(q, None, "q")
+    for n, x in (("k", k), ("v", v), ("do", do)):
+        _tensor(x, q, n)
+    prob = make_problem(q.shape, q.dtype, eps, simple)
+    dq = torch.empty_like(q) if dq is None else _tensor(dq, q, "dq")
+    dk = torch.empty_like(q) if dk is None else _tensor(dk, q, "dk")
+    dv = torch.empty_like(q) if dv is None else _tensor(dv, q, "dv")
+    ws, wsb = _ws(prob, q.device, ws)
+    _check(lib().la_bwd(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(state),
+                        _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws), wsb, _stream(q.device)))
+    return dq, dk, dv

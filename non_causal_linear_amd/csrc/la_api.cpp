@@ -1,0 +1,261 @@
+// C ABI of the library (declared in include/la.h): argument checks, the work
+// planner, workspace carving and the launch sequence of each entry point.
+// Every check runs before the first HIP call, so a rejected call enqueues
+// nothing.
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include <algorithm>
+
+#include "la.h"
+#include "la_internal.h"
+
+namespace {
+
+// Aim for this many workgroups per launch: 256 CUs, several resident each.
+constexpr int64_t kTargetWorkgroups = 1024;
+// Shortest token slice worth a workgroup of its own.
+constexpr int64_t kMinSlice = 256;
+// Largest B*H accepted (grid sizes stay below 2^31).
+constexpr int64_t kMaxHeads = int64_t(1) << 24;
+// Largest T accepted (offsets stay far from int64 overflow).
+constexpr int64_t kMaxTokens = int64_t(1) << 34;
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Split T tokens of each of BH heads into P pieces of L tokens (L a multiple of
+// gran, last piece ragged): P is the largest power of two with BH*P within the
+// target and pieces of at least kMinSlice tokens. Pure function of the shape.
+void split(int64_t BH, int64_t T, int64_t gran, int& P, int64_t& L) {
+    if (T <= 0 || BH <= 0) {
+        P = 1;
+        L = 0;
+        return;
+    }
+    const int64_t want = std::max<int64_t>(1, cdiv(kTargetWorkgroups, BH));
+    const int64_t maxp = std::max<int64_t>(1, T / kMinSlice);
+    int64_t p = 1;
+    while (p * 2 <= want && p * 2 <= maxp) p *= 2;
+    L = cdiv(cdiv(T, p), gran) * gran;
+    P = static_cast<int>(cdiv(T, L));
+}
+
+la_status check_problem(const la_problem* p) {
+    if (!p) return LA_ERR_NULL;
+    if (p->dtype != LA_F32 && p->dtype != LA_F16 && p->dtype != LA_BF16) return LA_ERR_DTYPE;
+    if (p->D != 64 && p->D != 128) return LA_ERR_HEAD_DIM;
+    if (p->B < 0 || p->H < 0 || p->T < 0) return LA_ERR_SHAPE;
+    if (p->B > kMaxHeads || p->H > kMaxHeads || p->B * p->H > kMaxHeads || p->T > kMaxTokens)
+        return LA_ERR_SHAPE;
+    if (p->flags & ~LA_SIMPLE) return LA_ERR_FLAGS;
+    if (!(p->eps >= 0.f) || !isfinite(p->eps)) return LA_ERR_EPS;
+    return LA_OK;
+}
+
+size_t elem_bytes(int dtype) { return dtype == LA_F32 ? 4 : 2; }
+
+la::Plan make_plan(const la_problem* p) {
+    la::Plan pl;
+    pl.BH = p->B * p->H;
+    pl.T = p->T;
+    pl.D = static_cast<int>(p->D);
+    pl.dtype = p->dtype;
+    pl.simple = (p->flags & LA_SIMPLE) != 0;
+    pl.eps = p->eps;
+    split(pl.BH, pl.T, la::state_tile_tokens(pl.dtype, pl.D), pl.P, pl.L);
+    split(pl.BH, pl.T, la::bwdq_group_tokens(pl.dtype, pl.D), pl.PB, pl.LB);
+    split(pl.BH, pl.T, la::stream_group_tokens(pl.dtype, pl.D), pl.NQ, pl.LQ);
+    split(pl.BH, pl.T, la::stream_group_tokens(pl.dtype, pl.D), pl.NK, pl.LK);
+    const size_t E = size_t(pl.D) * pl.D + pl.D;  // floats per (S, z) block
+    const size_t cnt = align256(size_t(pl.BH) * sizeof(int));
+    const int maxp = std::max(pl.P, pl.PB);
+    const size_t part = maxp > 1 ? align256(size_t(pl.BH) * maxp * E * 4) : 0;
+    const size_t st = align256(size_t(pl.BH) * E * 4);
+    pl.off_cnt_fwd = 0;
+    pl.off_cnt_bwd = cnt;
+    pl.off_part = 2 * cnt;
+    pl.off_dstate = pl.off_part + part;
+    pl.off_fstate = pl.off_dstate + st;
+    pl.ws_bytes = pl.off_fstate + st;
+    return pl;
+}
+
+struct Span {
+    const void* ptr;
+    size_t bytes;
+};
+
+bool overlaps(Span a, Span b) {
+    if (!a.ptr || !b.ptr || a.bytes == 0 || b.bytes == 0) return false;
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a.ptr), y = reinterpret_cast<uintptr_t>(b.ptr);
+    return x < y + b.bytes && y < x + a.bytes;
+}
+
+bool aligned(const void* ptr, uintptr_t a) { return (reinterpret_cast<uintptr_t>(ptr) & (a - 1)) == 0; }
+
+// Checks pointers of one call. ins/outs: tensors ([B,H,T,D]); outs must not
+// overlap anything else listed; every listed pointer must be non-NULL when its
+// span is non-empty.
+la_status check_buffers(std::initializer_list<Span> ins, std::initializer_list<Span> outs,
+                        std::initializer_list<uintptr_t> ins_align, std::initializer_list<uintptr_t> outs_align) {
+    auto ia = ins_align.begin();
+    for (const Span& s : ins) {
+        if (s.bytes && !s.ptr) return LA_ERR_NULL;
+        if (s.bytes && !aligned(s.ptr, *ia)) return LA_ERR_ALIGN;
+        ++ia;
+    }
+    auto oa = outs_align.begin();
+    for (const Span& s : outs) {
+        if (s.bytes && !s.ptr) return LA_ERR_NULL;
+        if (s.bytes && !aligned(s.ptr, *oa)) return LA_ERR_ALIGN;
+        ++oa;
+    }
+    for (const Span* o = outs.begin(); o != outs.end(); ++o) {
+        for (const Span& i : ins)
+            if (overlaps(*o, i)) return LA_ERR_ALIAS;
+        for (const Span* o2 = o + 1; o2 != outs.end(); ++o2)
+            if (overlaps(*o, *o2)) return LA_ERR_ALIAS;
+    }
+    return LA_OK;
+}
+
+la_status device_status(hipError_t e) { return e == hipSuccess ? LA_OK : LA_ERR_DEVICE; }
+
+}  // namespace
+
+extern "C" {
+
+int la_version(void) { return LA_VERSION; }
+
+const char* la_status_str(int s) {
+    switch (s) {
+        case LA_OK: return "LA_OK";
+        case LA_ERR_NULL: return "LA_ERR_NULL: required pointer is NULL";
+        case LA_ERR_SHAPE: return "LA_ERR_SHAPE: B, H or T negative or too large";
+        case LA_ERR_DTYPE: return "LA_ERR_DTYPE: unknown dtype";
+        case LA_ERR_HEAD_DIM: return "LA_ERR_HEAD_DIM: D must be 64 or 128";
+        case LA_ERR_FLAGS: return "LA_ERR_FLAGS: unknown flag bit";
+        case LA_ERR_EPS: return "LA_ERR_EPS: eps must be finite and >= 0";
+        case LA_ERR_WORKSPACE: return "LA_ERR_WORKSPACE: workspace smaller than la_workspace_bytes()";
+        case LA_ERR_ALIGN: return "LA_ERR_ALIGN: tensors need 16-byte, workspace 256-byte alignment";
+        case LA_ERR_ALIAS: return "LA_ERR_ALIAS: an output overlaps another buffer";
+        case LA_ERR_DEVICE: return "LA_ERR_DEVICE: HIP launch error";
+        default: return "unknown la_status";
+    }
+}
+
+size_t la_state_bytes(const la_problem* p) {
+    if (check_problem(p) != LA_OK) return 0;
+    return size_t(p->B * p->H) * size_t(p->D * p->D + p->D) * 4;
+}
+
+size_t la_workspace_bytes(const la_problem* p) {
+    if (check_problem(p) != LA_OK) return 0;
+    return make_plan(p).ws_bytes;
+}
+
+int la_fwd_state(const la_problem* p, const void* k, const void* v, void* state, void* ws,
+                 size_t ws_bytes, void* stream) {
+    la_status st = check_problem(p);
+    if (st != LA_OK) return st;
+    const la::Plan pl = make_plan(p);
+    const size_t tb = size_t(pl.BH * pl.T * pl.D) * elem_bytes(pl.dtype);
+    const size_t sb = la_state_bytes(p);
+    if (pl.BH > 0 && !state) return LA_ERR_NULL;
+    if (ws_bytes < pl.ws_bytes) return LA_ERR_WORKSPACE;
+    st = check_buffers({{k, tb}, {v, tb}}, {{state, sb}, {ws, pl.ws_bytes}}, {16, 16}, {16, 256});
+    if (st != LA_OK) return st;
+    if (pl.BH == 0) return LA_OK;
+    return device_status(la::launch_fwd_state(pl, k, v, static_cast<float*>(state), ws,
+                                              static_cast<hipStream_t>(stream)));
+}
+
+int la_fwd_output(const la_problem* p, const void* q, const void* state, void* o, void* stream) {
+    la_status st = check_problem(p);
+    if (st != LA_OK) return st;
+    const la::Plan pl = make_plan(p);
+    const size_t tb = size_t(pl.BH * pl.T * pl.D) * elem_bytes(pl.dtype);
+    const size_t sb = la_state_bytes(p);
+    st = check_buffers({{q, tb}, {state, sb}}, {{o, tb}}, {16, 16}, {16});
+    if (st != LA_OK) return st;
+    if (tb == 0) return LA_OK;
+    return device_status(la::launch_fwd_output(pl, q, static_cast<const float*>(state), o,
+                                               static_cast<hipStream_t>(stream)));
+}
+
+int la_fwd(const la_problem* p, const void* q, const void* k, const void* v, void* o, void* state,
+           void* ws, size_t ws_bytes, void* stream) {
+    la_status st = check_problem(p);
+    if (st != LA_OK) return st;
+    const la::Plan pl = make_plan(p);
+    const size_t tb = size_t(pl.BH * pl.T * pl.D) * elem_bytes(pl.dtype);
+    const size_t sb = la_state_bytes(p);
+    if (ws_bytes < pl.ws_bytes) return LA_ERR_WORKSPACE;
+    st = check_buffers({{q, tb}, {k, tb}, {v, tb}}, {{o, tb}, {state, state ? sb : 0}, {ws, pl.ws_bytes}},
+                       {16, 16, 16}, {16, 16, 256});
+    if (st != LA_OK) return st;
+    if (pl.BH == 0) return LA_OK;
+    float* stp = state ? static_cast<float*>(state)
+                       : reinterpret_cast<float*>(static_cast<char*>(ws) + pl.off_fstate);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    st = device_status(la::launch_fwd_state(pl, k, v, stp, ws, s));
+    if (st != LA_OK || tb == 0) return st;
+    return device_status(la::launch_fwd_output(pl, q, stp, o, s));
+}
+
+int la_bwd_dq(const la_problem* p, const void* q, const void* dout, const void* state, void* dq,
+              void* ws, size_t ws_bytes, void* stream) {
+    la_status st = check_problem(p);
+    if (st != LA_OK) return st;
+    const la::Plan pl = make_plan(p);
+    const size_t tb = size_t(pl.BH * pl.T * pl.D) * elem_bytes(pl.dtype);
+    const size_t sb = la_state_bytes(p);
+    if (pl.BH > 0 && !state) return LA_ERR_NULL;
+    if (ws_bytes < pl.ws_bytes) return LA_ERR_WORKSPACE;
+    st = check_buffers({{q, tb}, {dout, tb}, {state, sb}}, {{dq, tb}, {ws, pl.ws_bytes}}, {16, 16, 16},
+                       {16, 256});
+    if (st != LA_OK) return st;
+    if (tb == 0) return LA_OK;
+    return device_status(la::launch_bwd_dq(pl, q, dout, static_cast<const float*>(state), dq, ws,
+                                           static_cast<hipStream_t>(stream)));
+}
+
+int la_bwd_dkv(const la_problem* p, const void* k, const void* v, void* dk, void* dv, void* ws,
+               size_t ws_bytes, void* stream) {
+    la_status st = check_problem(p);
+    if (st != LA_OK) return st;
+    const la::Plan pl = make_plan(p);
+    const size_t tb = size_t(pl.BH * pl.T * pl.D) * elem_bytes(pl.dtype);
+    if (ws_bytes < pl.ws_bytes) return LA_ERR_WORKSPACE;
+    if (tb && !ws) return LA_ERR_NULL;
+    st = check_buffers({{k, tb}, {v, tb}, {ws, tb ? pl.ws_bytes : 0}}, {{dk, tb}, {dv, tb}},
+                       {16, 16, 256}, {16, 16});
+    if (st != LA_OK) return st;
+    if (tb == 0) return LA_OK;
+    return device_status(la::launch_bwd_dkv(pl, k, v, dk, dv, ws, static_cast<hipStream_t>(stream)));
+}
+
+int la_bwd(const la_problem* p, const void* q, const void* k, const void* v, const void* dout,
+           const void* state, void* dq, void* dk, void* dv, void* ws, size_t ws_bytes, void* stream) {
+    la_status st = check_problem(p);
+    if (st != LA_OK) return st;
+    const la::Plan pl = make_plan(p);
+    const size_t tb = size_t(pl.BH * pl.T * pl.D) * elem_bytes(pl.dtype);
+    const size_t sb = la_state_bytes(p);
+    if (pl.BH > 0 && !state) return LA_ERR_NULL;
+    if (ws_bytes < pl.ws_bytes) return LA_ERR_WORKSPACE;
+    st = check_buffers({{q, tb}, {k, tb}, {v, tb}, {dout, tb}, {state, sb}},
+                       {{dq, tb}, {dk, tb}, {dv, tb}, {ws, pl.ws_bytes}}, {16, 16, 16, 16, 16},
+                       {16, 16, 16, 256});
+    if (st != LA_OK) return st;
+    if (tb == 0) return LA_OK;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    st = device_status(la::launch_bwd_dq(pl, q, dout, static_cast<const float*>(state), dq, ws, s));
+    if (st != LA_OK) return st;
+    return device_status(la::launch_bwd_dkv(pl, k, v, dk, dv, ws, s));
+}
+
+}  // extern "C"

@@ -1,0 +1,49 @@
+// Internal interface between the C-ABI layer (la_api.cpp) and the kernels
+// (la_kernels.hip). Not installed; no HIP types leak into include/la.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace la {
+
+// Work split for one problem. Every field is a pure function of
+// (B*H, T, D, dtype), so the summation order, and with it every output bit,
+// depends only on the shape.
+struct Plan {
+    int64_t BH = 0, T = 0;
+    int D = 0, dtype = 0;
+    bool simple = false;
+    float eps = 0.f;
+    // state reduction (fwd steps 1-3): P slices of L tokens per head
+    int P = 1;
+    int64_t L = 0;
+    // backward Q side (steps 5-6): PB slices of LB tokens per head
+    int PB = 1;
+    int64_t LB = 0;
+    // output (step 4): NQ chunks of LQ tokens per head
+    int NQ = 1;
+    int64_t LQ = 0;
+    // backward K/V side (step 7): NK chunks of LK tokens per head
+    int NK = 1;
+    int64_t LK = 0;
+    // workspace carving (byte offsets)
+    size_t off_cnt_fwd = 0, off_cnt_bwd = 0, off_part = 0, off_dstate = 0, off_fstate = 0;
+    size_t ws_bytes = 0;
+};
+
+// Token granularity the kernels need a split to respect.
+int64_t state_tile_tokens(int dtype, int D);   // fwd state kernel tile
+int64_t bwdq_group_tokens(int dtype, int D);   // bwd Q-side workgroup iteration
+int64_t stream_group_tokens(int dtype, int D); // output / bwd K/V workgroup iteration
+
+hipError_t launch_fwd_state(const Plan& p, const void* k, const void* v, float* state,
+                            void* ws, hipStream_t s);
+hipError_t launch_fwd_output(const Plan& p, const void* q, const float* state, void* o,
+                             hipStream_t s);
+hipError_t launch_bwd_dq(const Plan& p, const void* q, const void* dout, const float* state,
+                         void* dq, void* ws, hipStream_t s);
+hipError_t launch_bwd_dkv(const Plan& p, const void* k, const void* v, void* dk, void* dv,
+                          void* ws, hipStream_t s);
+
+}  // namespace la

@@ -1,0 +1,913 @@
+// gfx950 (MI355X) kernels for bidirectional (non-causal) linear attention.
+//
+// Operation (Flash Bi-directional Linear Attention README, intro; simple_la
+// in its "Update" 2024-12-28; backward in "Update" 2024-12-30): per (batch,
+// head), phi(x) = elu(x) + 1,
+//   S = sum_t phi(k_t) v_t^T,  z = sum_t phi(k_t),
+//   O_t = phi(q_t) S / (phi(q_t) . z + eps)     (simple_la: phi(q_t) S).
+//
+// Four kernels, one per step group of the path:
+//   fwd_state_kernel   phi(K)^T [V | 1] over a token slice on MFMA, partial
+//                      (S, z) per slice, fixed-order combine by the workgroup
+//                      that finishes the head last;
+//   fwd_output_kernel  O = phi(Q) S / (phi(Q) z + eps), S and z as MFMA operands;
+//   bwd_dq_kernel      dQ, plus partial dS = phi(Q)^T (dO / den) on MFMA and
+//                      dz = sum_t c_t phi(q_t), combined like the forward state;
+//   bwd_dkv_kernel     dK = (V dS^T + dz) * phi'(K), dV = phi(K) dS.
+//
+// MFMA conventions (v_mfma_f32_16x16x32_{f16,bf16}; for fp32 operands eight
+// v_mfma_f32_16x16x4f32 cover the same 32-long contraction): a wave holds A
+// rows m = lane % 16, B columns n = lane % 16, each lane carrying 8 values of
+// the contraction index for its lane group g = lane / 16; the result C[m][n]
+// sits in lane (n + 16 g) at register r with m = 4 g + r. Which physical k the
+// 8 values of a lane group stand for is free, as long as A and B agree, and
+// the kernels use that freedom: a lane that loads D/4 contiguous features of
+// one token row can feed them straight into B fragments, and the rows of A are
+// permuted so that the same lane receives D/4 contiguous output features of
+// that token, which it stores contiguously.
+//
+// Tensors are [B, H, T, D] row-major. The work split is a pure function of the
+// shape and there are no floating-point atomics, so results are bit-identical
+// across runs.
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+#include "la_internal.h"
+
+namespace la {
+namespace {
+
+typedef _Float16 f16;
+typedef __bf16 bf16;
+typedef f16 f16x8 __attribute__((ext_vector_type(8)));
+typedef bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kThreads = 256;
+constexpr int kWaves = 4;
+
+template <typename T> struct Elt;
+// kScaled: the fp32 states are multiplied by a power of two before they are
+// rounded to this operand type (f16's range is too narrow for S, z, dS).
+template <> struct Elt<float> { using frag = f32x8; static constexpr bool kScaled = false; };
+template <> struct Elt<f16> { using frag = f16x8; static constexpr bool kScaled = true; };
+template <> struct Elt<bf16> { using frag = bf16x8; static constexpr bool kScaled = false; };
+template <typename T> using Frag = typename Elt<T>::frag;
+
+__device__ __forceinline__ f32x4 mma(f16x8 a, f16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma(f32x8 a, f32x8 b, f32x4 c) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[e], b[e], c, 0, 0, 0);
+    return c;
+}
+
+// phi(x) = elu(x) + 1, evaluated piecewise in fp32 (never as expm1(x) + 1,
+// which cancels for x << 0). fp32 inputs use the accurate expf.
+template <typename T>
+__device__ __forceinline__ float phi(float x) {
+    if constexpr (std::is_same<T, float>::value) {
+        return x > 0.f ? x + 1.f : expf(x);
+    } else {
+        return x > 0.f ? x + 1.f : __expf(x);
+    }
+}
+
+template <typename T>
+__device__ __forceinline__ float to_f32(T x) { return static_cast<float>(x); }
+
+// Hardware places workgroup b on XCD b % 8. Renumber so that consecutive
+// logical ids (the slices or chunks of one head) share an XCD and its L2.
+__device__ __forceinline__ int xcd_remap(int b, int n) {
+    if (n % 8 != 0) return b;
+    return (b % 8) * (n / 8) + b / 8;
+}
+
+// N contiguous elements of a row; N * sizeof(T) is a multiple of 16 bytes.
+template <typename T, int N>
+struct alignas(16) Row {
+    T e[N];
+};
+
+template <typename T, int N>
+__device__ __forceinline__ void load_row(Row<T, N>& r, const T* __restrict__ p, bool valid) {
+    constexpr int NV = N * (int)sizeof(T) / 16;
+    uint4* d = reinterpret_cast<uint4*>(r.e);
+    const uint4* s = reinterpret_cast<const uint4*>(p);
+    if (valid) {
+#pragma unroll
+        for (int i = 0; i < NV; ++i) d[i] = s[i];
+    } else {
+#pragma unroll
+        for (int i = 0; i < NV; ++i) d[i] = make_uint4(0u, 0u, 0u, 0u);
+    }
+}
+
+template <typename T, int N>
+__device__ __forceinline__ void store_row(T* __restrict__ p, const float (&x)[N]) {
+    Row<T, N> r;
+#pragma unroll
+    for (int j = 0; j < N; ++j) r.e[j] = static_cast<T>(x[j]);
+    constexpr int NV = N * (int)sizeof(T) / 16;
+    const uint4* s = reinterpret_cast<const uint4*>(r.e);
+    uint4* d = reinterpret_cast<uint4*>(p);
+#pragma unroll
+    for (int i = 0; i < NV; ++i) d[i] = s[i];
+}
+
+__device__ __forceinline__ float block_max(float v, float* red) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+    __syncthreads();
+    const float r = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    __syncthreads();
+    return r;
+}
+
+__device__ __forceinline__ float block_sum(float v, float* red) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+    __syncthreads();
+    const float r = (red[0] + red[1]) + (red[2] + red[3]);
+    __syncthreads();
+    return r;
+}
+
+// Exponent s with maxabs * 2^s in [2^14, 2^15): the largest state entry lands
+// well inside f16's range and the rest keep f16's relative precision down to
+// 2^-24 of it. Zero, inf or NaN: no scaling (inf/NaN then propagate).
+__device__ __forceinline__ int scale_exp(float maxabs) {
+    if (!(maxabs > 0.f) || !isfinite(maxabs)) return 0;
+    int e;
+    frexpf(maxabs, &e);  // maxabs = m 2^e, m in [0.5, 1)
+    return min(max(15 - e, -120), 120);
+}
+
+// Fixed-order sum of the P partial (S, z) blocks of head bh, run by the last
+// workgroup of that head to arrive. Returns true in that workgroup.
+template <int D>
+__device__ __forceinline__ bool combine_if_last(const float* __restrict__ part, int* __restrict__ cnt,
+                                                float* __restrict__ outS, float* __restrict__ outz,
+                                                int64_t bh, int P, int* s_flag) {
+    constexpr int E = D * D + D;
+    __threadfence();  // publish this workgroup's partial before counting it
+    __syncthreads();
+    if (threadIdx.x == 0) s_flag[0] = (atomicAdd(cnt + bh, 1) == P - 1) ? 1 : 0;
+    __syncthreads();
+    if (!s_flag[0]) return false;
+    __threadfence();  // see every other workgroup's partial
+    const float* pb = part + bh * (int64_t)P * E;
+    for (int idx = threadIdx.x; idx < E; idx += kThreads) {
+        float s = 0.f;
+        for (int p = 0; p < P; ++p)
+            s += __hip_atomic_load(pb + (int64_t)p * E + idx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (idx < D * D)
+            outS[bh * D * D + idx] = s;
+        else
+            outz[bh * D + (idx - D * D)] = s;
+    }
+    if (threadIdx.x == 0) __hip_atomic_store(cnt + bh, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return true;
+}
+
+// ---------------------------------------------------------------------------
+// Steps 1-3: split-T state reduction.
+// ---------------------------------------------------------------------------
+template <typename T, int D>
+struct StateShape {
+    static constexpr int kEPC = 16 / (int)sizeof(T);  // elements per 16-byte chunk
+    static constexpr int kCPR = D / kEPC;             // chunks per row
+    static constexpr int kNG = kThreads / kCPR;       // row groups per load pass
+    static constexpr int kR = 4;                      // rows per thread per tile
+    static constexpr int kTT = kNG * kR;              // tokens per tile
+    static constexpr int kLDT = kTT + kEPC;           // LDS row stride (elements), +16 B pad
+    static constexpr int kNB = D / 16;                // 16-wide blocks along D
+    static constexpr int kNI = kNB / kWaves;          // i-blocks of S per wave
+    static constexpr int kKS = kTT / 32;              // 32-token MFMA steps per tile
+};
+
+// One workgroup reduces tokens [p L, min((p+1) L, T)) of head bh into partial
+// (S, z). The tile is loaded row-major with 16-byte loads (8 consecutive rows
+// per wave instruction), phi is applied to K in fp32 and rounded to the
+// operand type, and both tiles are written to LDS transposed ([feature][token])
+// so that MFMA fragments, which want 8 consecutive tokens per lane, are single
+// 16-byte LDS reads. Token order inside a tile is permuted (thread g's rows
+// g, g + NG, ... land in columns 4g, 4g + 1, ...) identically for K and V,
+// which a sum over tokens does not see. z comes from the same MFMA with an
+// all-ones B block, so it sums exactly the rounded phi(k) that S uses.
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads) void fwd_state_kernel(
+    const T* __restrict__ k, const T* __restrict__ v, float* __restrict__ stS,
+    float* __restrict__ stz, float* __restrict__ part, int* __restrict__ cnt, int64_t T_, int P,
+    int64_t L) {
+    using Sh = StateShape<T, D>;
+    constexpr int EPC = Sh::kEPC, CPR = Sh::kCPR, NG = Sh::kNG, R = Sh::kR, TT = Sh::kTT,
+                  LDT = Sh::kLDT, NB = Sh::kNB, NI = Sh::kNI, KS = Sh::kKS;
+    typedef T tR __attribute__((ext_vector_type(R)));
+    __shared__ __attribute__((aligned(16))) T sK[D * LDT];
+    __shared__ __attribute__((aligned(16))) T sV[D * LDT];
+    __shared__ int s_flag[1];
+
+    const int wid = xcd_remap(blockIdx.x, gridDim.x);
+    const int64_t bh = wid / P;
+    const int p = wid % P;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int m = lane & 15, grp = lane >> 4;
+    const int c = tid % CPR, g = tid / CPR;
+    const int64_t t0 = (int64_t)p * L;
+    const int64_t t1 = min(t0 + L, T_);
+    const T* kb = k + bh * T_ * D + c * EPC;
+    const T* vb = v + bh * T_ * D + c * EPC;
+
+    f32x4 acc[NI][NB + 1];
+#pragma unroll
+    for (int ii = 0; ii < NI; ++ii)
+#pragma unroll
+        for (int jb = 0; jb <= NB; ++jb) acc[ii][jb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    Frag<T> ones;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ones[e] = static_cast<T>(1.f);
+
+    uint4 rk[R], rv[R];
+    auto load_tile = [&](int64_t ts) {
+#pragma unroll
+        for (int rr = 0; rr < R; ++rr) {
+            const int64_t t = ts + g + NG * rr;
+            if (t < t1) {
+                rk[rr] = *reinterpret_cast<const uint4*>(kb + t * D);
+                rv[rr] = *reinterpret_cast<const uint4*>(vb + t * D);
+            } else {
+                rk[rr] = make_uint4(0u, 0u, 0u, 0u);
+                rv[rr] = make_uint4(0u, 0u, 0u, 0u);
+            }
+        }
+    };
+
+    const int64_t ntile = (t1 > t0) ? (t1 - t0 + TT - 1) / TT : 0;
+    if (ntile > 0) load_tile(t0);
+    for (int64_t it = 0; it < ntile; ++it) {
+        const int64_t ts = t0 + it * TT;
+        __syncthreads();  // every wave is done reading the previous tile
+        {
+            tR kt[EPC], vt[EPC];
+#pragma unroll
+            for (int rr = 0; rr < R; ++rr) {
+                const bool ok = ts + g + NG * rr < t1;
+                const T* ke = reinterpret_cast<const T*>(&rk[rr]);
+                const T* ve = reinterpret_cast<const T*>(&rv[rr]);
+#pragma unroll
+                for (int e = 0; e < EPC; ++e) {
+                    // padded rows must add nothing: phi(0) = 1, so mask after phi
+                    kt[e][rr] = ok ? static_cast<T>(phi<T>(to_f32(ke[e]))) : static_cast<T>(0.f);
+                    vt[e][rr] = ve[e];
+                }
+            }
+#pragma unroll
+            for (int e = 0; e < EPC; ++e) {
+                *reinterpret_cast<tR*>(&sK[(c * EPC + e) * LDT + R * g]) = kt[e];
+                *reinterpret_cast<tR*>(&sV[(c * EPC + e) * LDT + R * g]) = vt[e];
+            }
+        }
+        __syncthreads();
+        if (it + 1 < ntile) load_tile(ts + TT);  // in flight during the MFMA below
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const int col = ks * 32 + grp * 8;
+            Frag<T> a[NI];
+#pragma unroll
+            for (int ii = 0; ii < NI; ++ii)
+                a[ii] = *reinterpret_cast<const Frag<T>*>(&sK[((wave * NI + ii) * 16 + m) * LDT + col]);
+#pragma unroll
+            for (int jb = 0; jb < NB; ++jb) {
+                const Frag<T> b = *reinterpret_cast<const Frag<T>*>(&sV[(jb * 16 + m) * LDT + col]);
+#pragma unroll
+                for (int ii = 0; ii < NI; ++ii) acc[ii][jb] = mma(a[ii], b, acc[ii][jb]);
+            }
+#pragma unroll
+            for (int ii = 0; ii < NI; ++ii) acc[ii][NB] = mma(a[ii], ones, acc[ii][NB]);
+        }
+    }
+
+    float* oS;
+    float* oz;
+    if (P == 1) {
+        oS = stS + bh * D * D;
+        oz = stz + bh * D;
+    } else {
+        oS = part + (bh * P + p) * (int64_t)(D * D + D);
+        oz = oS + D * D;
+    }
+#pragma unroll
+    for (int ii = 0; ii < NI; ++ii) {
+        const int i0 = (wave * NI + ii) * 16 + 4 * grp;
+#pragma unroll
+        for (int jb = 0; jb < NB; ++jb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) oS[(i0 + r) * D + jb * 16 + m] = acc[ii][jb][r];
+        if (m == 0)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) oz[i0 + r] = acc[ii][NB][r];
+    }
+    if (P > 1) combine_if_last<D>(part, cnt, stS, stz, bh, P, s_flag);
+}
+
+// ---------------------------------------------------------------------------
+// Shared shape of the streaming kernels (output, bwd Q side, bwd K/V side).
+// ---------------------------------------------------------------------------
+template <typename T, int D>
+struct StreamShape {
+    static constexpr int kF = D / 4;     // features per lane (one quarter row)
+    static constexpr int kNB = D / 16;   // 16-row output blocks
+    static constexpr int kKS = D / 32;   // 32-long contraction steps over D
+    static constexpr int kU = (sizeof(T) == 2 && D == 64) ? 2 : 1;  // 16-token blocks per wave
+    static constexpr int kG = kWaves * kU * 16;  // tokens per workgroup iteration
+};
+
+// Fragment of A = M^T-like operand built from an fp32 D x D matrix M:
+//   rows m of the 16-row block b stand for index F*(m/4) + 4b + m%4,
+//   the lane group's 8 contraction values stand for F*g + 8s + e.
+// If kTransposeSource, element = M[contraction][row] else M[row][contraction].
+template <typename T, int D, bool kTransposeSource>
+__device__ __forceinline__ Frag<T> build_frag(const float* __restrict__ M, int b, int s, int m, int g,
+                                              float scale) {
+    constexpr int F = D / 4;
+    const int row = F * (m >> 2) + 4 * b + (m & 3);
+    const int k0 = F * g + 8 * s;
+    Frag<T> f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const float x = kTransposeSource ? M[(k0 + e) * D + row] : M[row * D + k0 + e];
+        f[e] = static_cast<T>(x * scale);
+    }
+    return f;
+}
+
+// Fragment whose every row is the vector z: z[F*g + 8s + e].
+template <typename T, int D>
+__device__ __forceinline__ Frag<T> build_zfrag(const float* __restrict__ z, int s, int g, float scale) {
+    constexpr int F = D / 4;
+    Frag<T> f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) f[e] = static_cast<T>(z[F * g + 8 * s + e] * scale);
+    return f;
+}
+
+// ---------------------------------------------------------------------------
+// Step 4: output.
+// ---------------------------------------------------------------------------
+// One workgroup streams tokens [ch LQ, min((ch+1) LQ, T)) of head bh. Per
+// 16-token block a lane loads a quarter row of Q (D/4 features), applies phi,
+// and the wave computes O^T = S^T phi(Q)^T (rows permuted so each lane ends
+// with D/4 contiguous outputs of its token) and den = z . phi(q) from one more
+// MFMA block whose rows are all z.
+template <typename T, int D, bool SIMPLE>
+__global__ __launch_bounds__(kThreads) void fwd_output_kernel(
+    const T* __restrict__ q, const float* __restrict__ stS, const float* __restrict__ stz,
+    T* __restrict__ o, int64_t T_, int NQ, int64_t LQ, float eps) {
+    using Sh = StreamShape<T, D>;
+    constexpr int F = Sh::kF, NB = Sh::kNB, KS = Sh::kKS, U = Sh::kU;
+    constexpr int NFS = NB * KS;             // S fragments
+    constexpr int NFR = NFS + (SIMPLE ? 0 : KS);  // + z fragments
+    __shared__ Frag<T> sA[NFR * 64];
+    __shared__ float red[4];
+
+    const int wid = xcd_remap(blockIdx.x, gridDim.x);
+    const int64_t bh = wid / NQ;
+    const int ch = wid % NQ;
+    const int64_t c0 = (int64_t)ch * LQ;
+    const int64_t c1 = min(c0 + LQ, T_);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int m = lane & 15, grp = lane >> 4;
+    const float* S = stS + bh * D * D;
+    const float* z = stz + bh * D;
+
+    int sS = 0, sz = 0;
+    if constexpr (Elt<T>::kScaled) {
+        float mx = 0.f, mz = 0.f;
+        for (int i = tid; i < D * D; i += kThreads) mx = fmaxf(mx, fabsf(S[i]));
+        for (int i = tid; i < D; i += kThreads) mz = fmaxf(mz, fabsf(z[i]));
+        sS = scale_exp(block_max(mx, red));
+        sz = scale_exp(block_max(mz, red));
+    }
+    for (int f = wave; f < NFR; f += kWaves) {
+        Frag<T> fr;
+        if (f < NFS)
+            fr = build_frag<T, D, true>(S, f / KS, f % KS, m, grp, ldexpf(1.f, sS));
+        else
+            fr = build_zfrag<T, D>(z, f - NFS, grp, ldexpf(1.f, sz));
+        sA[f * 64 + lane] = fr;
+    }
+    __syncthreads();
+    const float uS = ldexpf(1.f, -sS), uz = ldexpf(1.f, -sz);
+
+    for (int64_t base = c0 + wave * 16 * U; base < c1; base += 16 * U * kWaves) {
+        Row<T, F> qr[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t t = base + 16 * u + m;
+            load_row<T, F>(qr[u], q + (bh * T_ + t) * D + F * grp, t < c1);
+        }
+        Frag<T> bq[U][KS];
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int s = 0; s < KS; ++s)
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    bq[u][s][e] = static_cast<T>(phi<T>(to_f32(qr[u].e[8 * s + e])));
+        f32x4 acc[U][NB], accd[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            accd[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int b = 0; b < NB; ++b) acc[u][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+            for (int s = 0; s < KS; ++s) {
+                const Frag<T> a = sA[(b * KS + s) * 64 + lane];
+#pragma unroll
+                for (int u = 0; u < U; ++u) acc[u][b] = mma(a, bq[u][s], acc[u][b]);
+            }
+        if constexpr (!SIMPLE) {
+#pragma unroll
+            for (int s = 0; s < KS; ++s) {
+                const Frag<T> a = sA[(NFS + s) * 64 + lane];
+#pragma unroll
+                for (int u = 0; u < U; ++u) accd[u] = mma(a, bq[u][s], accd[u]);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t t = base + 16 * u + m;
+            if (t < c1) {
+                float out[F];
+                if constexpr (SIMPLE) {
+#pragma unroll
+                    for (int b = 0; b < NB; ++b)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) out[4 * b + r] = acc[u][b][r] * uS;
+                } else {
+                    const float den = accd[u][0] * uz + eps;
+#pragma unroll
+                    for (int b = 0; b < NB; ++b)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) out[4 * b + r] = (acc[u][b][r] * uS) / den;
+                }
+                store_row<T, F>(o + (bh * T_ + t) * D + F * grp, out);
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Steps 5-6: backward, Q side.
+// ---------------------------------------------------------------------------
+template <typename T, int D>
+struct BwdQShape {
+    static constexpr int kU = (sizeof(T) == 2 && D == 64) ? 2 : 1;  // 16-token blocks per wave
+    static constexpr int kG = kWaves * kU * 16;                     // tokens per iteration
+    static constexpr int kLDT = kG + 16 / (int)sizeof(T);           // LDS row stride, +16 B
+};
+
+// One workgroup walks tokens [p LB, min((p+1) LB, T)) of head bh. Per token:
+//   u = S dO_t (MFMA, S rows permuted as in the output kernel), den = z . phi(q)
+//   (MFMA), r = phi(q) . u (lane partial + two cross-lane adds),
+//   c = -r / den^2, dphi(q) = u / den + c z, dQ = dphi(q) * phi'(q),
+//   dz += c phi(q) (fp32, per lane), and phi(q), w = dO 2^sw / den are written
+//   to LDS transposed; then the workgroup accumulates dS += phi(Q)^T w on MFMA.
+// w carries the power of two 2^sw ~ sum(z) (f16 only) so that dO / den, about
+// 1e-6 for long sequences, does not fall into f16 subnormals; dS is unscaled
+// in fp32 when written.
+template <typename T, int D, bool SIMPLE>
+__global__ __launch_bounds__(kThreads) void bwd_dq_kernel(
+    const T* __restrict__ q, const T* __restrict__ dout, const float* __restrict__ stS,
+    const float* __restrict__ stz, T* __restrict__ dq, float* __restrict__ part,
+    float* __restrict__ dS_out, float* __restrict__ dz_out, int* __restrict__ cnt, int64_t T_, int PB,
+    int64_t LB, float eps) {
+    using Sh = StreamShape<T, D>;
+    using Bq = BwdQShape<T, D>;
+    constexpr int F = Sh::kF, NB = Sh::kNB, KS = Sh::kKS;
+    constexpr int U = Bq::kU, G = Bq::kG, LDT = Bq::kLDT;
+    constexpr int NI = NB / kWaves;
+    constexpr int NFS = NB * KS;
+    constexpr int NFR = NFS + (SIMPLE ? 0 : KS);
+    __shared__ Frag<T> sA[NFR * 64];
+    __shared__ __attribute__((aligned(16))) T sQ[D * LDT];
+    __shared__ __attribute__((aligned(16))) T sW[D * LDT];
+    __shared__ float sdz[kWaves][D];
+    __shared__ float red[4];
+    __shared__ int s_flag[1];
+
+    const int wid = xcd_remap(blockIdx.x, gridDim.x);
+    const int64_t bh = wid / PB;
+    const int p = wid % PB;
+    const int64_t t0 = (int64_t)p * LB;
+    const int64_t t1 = min(t0 + LB, T_);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int m = lane & 15, grp = lane >> 4;
+    const float* S = stS + bh * D * D;
+    const float* z = stz + bh * D;
+
+    int sS = 0, sz = 0, sw = 0;
+    if constexpr (Elt<T>::kScaled) {
+        float mx = 0.f, mz = 0.f, zs = 0.f;
+        for (int i = tid; i < D * D; i += kThreads) mx = fmaxf(mx, fabsf(S[i]));
+        for (int i = tid; i < D; i += kThreads) {
+            mz = fmaxf(mz, fabsf(z[i]));
+            zs += z[i];
+        }
+        sS = scale_exp(block_max(mx, red));
+        sz = scale_exp(block_max(mz, red));
+        if constexpr (!SIMPLE) {
+            const float zsum = block_sum(zs, red);
+            if (zsum > 0.f && isfinite(zsum)) {
+                int e;
+                frexpf(zsum, &e);
+                sw = min(max(e - 1, -120), 120);  // 2^sw <= sum(z) < 2^(sw+1)
+            }
+        }
+    }
+    for (int f = wave; f < NFR; f += kWaves) {
+        Frag<T> fr;
+        if (f < NFS)
+            fr = build_frag<T, D, false>(S, f / KS, f % KS, m, grp, ldexpf(1.f, sS));
+        else
+            fr = build_zfrag<T, D>(z, f - NFS, grp, ldexpf(1.f, sz));
+        sA[f * 64 + lane] = fr;
+    }
+    float zl[F];
+#pragma unroll
+    for (int o = 0; o < F; ++o) zl[o] = SIMPLE ? 0.f : z[F * grp + o];
+    __syncthreads();
+    const float uS = ldexpf(1.f, -sS), uz = ldexpf(1.f, -sz), fw = ldexpf(1.f, sw);
+
+    f32x4 dsacc[NI][NB];
+#pragma unroll
+    for (int ii = 0; ii < NI; ++ii)
+#pragma unroll
+        for (int jb = 0; jb < NB; ++jb) dsacc[ii][jb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float dzacc[F];
+#pragma unroll
+    for (int o = 0; o < F; ++o) dzacc[o] = 0.f;
+
+    for (int64_t base = t0; base < t1; base += G) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t t = base + (wave * U + u) * 16 + m;
+            const bool valid = t < t1;
+            Row<T, F> qr, dr;
+            load_row<T, F>(qr, q + (bh * T_ + t) * D + F * grp, valid);
+            load_row<T, F>(dr, dout + (bh * T_ + t) * D + F * grp, valid);
+            float qt[F];
+#pragma unroll
+            for (int o = 0; o < F; ++o) qt[o] = phi<T>(to_f32(qr.e[o]));
+            Frag<T> bq[KS], bd[KS];
+#pragma unroll
+            for (int s = 0; s < KS; ++s)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    bq[s][e] = static_cast<T>(qt[8 * s + e]);
+                    bd[s][e] = dr.e[8 * s + e];
+                }
+            f32x4 au[NB];
+#pragma unroll
+            for (int b = 0; b < NB; ++b) au[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int b = 0; b < NB; ++b)
+#pragma unroll
+                for (int s = 0; s < KS; ++s) au[b] = mma(sA[(b * KS + s) * 64 + lane], bd[s], au[b]);
+            float dqt[F], wv[F];
+            if constexpr (SIMPLE) {
+#pragma unroll
+                for (int b = 0; b < NB; ++b)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) dqt[4 * b + r] = au[b][r] * uS;
+#pragma unroll
+                for (int o = 0; o < F; ++o) wv[o] = to_f32(dr.e[o]);
+            } else {
+                f32x4 ad = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int s = 0; s < KS; ++s) ad = mma(sA[(NFS + s) * 64 + lane], bq[s], ad);
+                const float den = ad[0] * uz + eps;
+                float uu[F];
+                float rr = 0.f;
+#pragma unroll
+                for (int b = 0; b < NB; ++b)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        uu[4 * b + r] = au[b][r] * uS;
+                        rr += qt[4 * b + r] * uu[4 * b + r];
+                    }
+                rr += __shfl_xor(rr, 16);
+                rr += __shfl_xor(rr, 32);
+                const float c = -(rr / den) / den;
+                const float ws = fw / den;
+#pragma unroll
+                for (int o = 0; o < F; ++o) {
+                    dqt[o] = uu[o] / den + c * zl[o];
+                    wv[o] = to_f32(dr.e[o]) * ws;
+                    if (valid) dzacc[o] += c * qt[o];
+                }
+            }
+            if (valid) {
+                float out[F];
+#pragma unroll
+                for (int o = 0; o < F; ++o) out[o] = dqt[o] * fminf(qt[o], 1.f);  // phi' = min(phi, 1)
+                store_row<T, F>(dq + (bh * T_ + t) * D + F * grp, out);
+            }
+            const int col = (wave * U + u) * 16 + m;
+#pragma unroll
+            for (int o = 0; o < F; ++o) {
+                sQ[(F * grp + o) * LDT + col] = valid ? static_cast<T>(qt[o]) : static_cast<T>(0.f);
+                sW[(F * grp + o) * LDT + col] = valid ? static_cast<T>(wv[o]) : static_cast<T>(0.f);
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int ks = 0; ks < G / 32; ++ks) {
+            const int col = ks * 32 + grp * 8;
+            Frag<T> a[NI];
+#pragma unroll
+            for (int ii = 0; ii < NI; ++ii)
+                a[ii] = *reinterpret_cast<const Frag<T>*>(&sQ[((wave * NI + ii) * 16 + m) * LDT + col]);
+#pragma unroll
+            for (int jb = 0; jb < NB; ++jb) {
+                const Frag<T> bw = *reinterpret_cast<const Frag<T>*>(&sW[(jb * 16 + m) * LDT + col]);
+#pragma unroll
+                for (int ii = 0; ii < NI; ++ii) dsacc[ii][jb] = mma(a[ii], bw, dsacc[ii][jb]);
+            }
+        }
+        __syncthreads();
+    }
+
+    float* oS;
+    float* oz;
+    if (PB == 1) {
+        oS = dS_out + bh * D * D;
+        oz = dz_out + bh * D;
+    } else {
+        oS = part + (bh * PB + p) * (int64_t)(D * D + D);
+        oz = oS + D * D;
+    }
+    const float uw = ldexpf(1.f, -sw);
+#pragma unroll
+    for (int ii = 0; ii < NI; ++ii) {
+        const int i0 = (wave * NI + ii) * 16 + 4 * grp;
+#pragma unroll
+        for (int jb = 0; jb < NB; ++jb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) oS[(i0 + r) * D + jb * 16 + m] = dsacc[ii][jb][r] * uw;
+    }
+    // dz: sum over the 16 token lanes of each lane group, then over waves, in a
+    // fixed pattern.
+#pragma unroll
+    for (int o = 0; o < F; ++o) {
+        float x = dzacc[o];
+        x += __shfl_xor(x, 1);
+        x += __shfl_xor(x, 2);
+        x += __shfl_xor(x, 4);
+        x += __shfl_xor(x, 8);
+        if (m == 0) sdz[wave][F * grp + o] = x;
+    }
+    __syncthreads();
+    for (int i = tid; i < D; i += kThreads) oz[i] = (sdz[0][i] + sdz[1][i]) + (sdz[2][i] + sdz[3][i]);
+    if (PB > 1) combine_if_last<D>(part, cnt, dS_out, dz_out, bh, PB, s_flag);
+}
+
+// ---------------------------------------------------------------------------
+// Step 7: backward, K/V side.
+// ---------------------------------------------------------------------------
+// dphi(k_t) = dS v_t + dz and dv_t = dS^T phi(k_t): both are products of a
+// fixed D x D matrix with a token's row, so each is one set of MFMA blocks with
+// dS (or dS^T) as the A operand and the loaded K/V quarter rows as B.
+template <typename T, int D, bool SIMPLE>
+__global__ __launch_bounds__(kThreads) void bwd_dkv_kernel(
+    const T* __restrict__ k, const T* __restrict__ v, const float* __restrict__ dSg,
+    const float* __restrict__ dzg, T* __restrict__ dk, T* __restrict__ dv, int64_t T_, int NK,
+    int64_t LK) {
+    using Sh = StreamShape<T, D>;
+    constexpr int F = Sh::kF, NB = Sh::kNB, KS = Sh::kKS, U = Sh::kU;
+    constexpr int NFS = NB * KS;
+    __shared__ Frag<T> sA[2 * NFS * 64];
+    __shared__ float red[4];
+
+    const int wid = xcd_remap(blockIdx.x, gridDim.x);
+    const int64_t bh = wid / NK;
+    const int ch = wid % NK;
+    const int64_t c0 = (int64_t)ch * LK;
+    const int64_t c1 = min(c0 + LK, T_);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int m = lane & 15, grp = lane >> 4;
+    const float* dS = dSg + bh * D * D;
+    const float* dz = dzg + bh * D;
+
+    int sD = 0;
+    if constexpr (Elt<T>::kScaled) {
+        float mx = 0.f;
+        for (int i = tid; i < D * D; i += kThreads) mx = fmaxf(mx, fabsf(dS[i]));
+        sD = scale_exp(block_max(mx, red));
+    }
+    const float fD = ldexpf(1.f, sD), uD = ldexpf(1.f, -sD);
+    for (int f = wave; f < 2 * NFS; f += kWaves) {
+        Frag<T> fr;
+        if (f < NFS)  // dK side: rows i, contraction j -> dS[i][j]
+            fr = build_frag<T, D, false>(dS, f / KS, f % KS, m, grp, fD);
+        else  // dV side: rows j, contraction i -> dS[i][j]
+            fr = build_frag<T, D, true>(dS, (f - NFS) / KS, (f - NFS) % KS, m, grp, fD);
+        sA[f * 64 + lane] = fr;
+    }
+    float dzl[F];
+#pragma unroll
+    for (int o = 0; o < F; ++o) dzl[o] = SIMPLE ? 0.f : dz[F * grp + o];
+    __syncthreads();
+
+    for (int64_t base = c0 + wave * 16 * U; base < c1; base += 16 * U * kWaves) {
+        Row<T, F> kr[U], vr[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t t = base + 16 * u + m;
+            load_row<T, F>(kr[u], k + (bh * T_ + t) * D + F * grp, t < c1);
+            load_row<T, F>(vr[u], v + (bh * T_ + t) * D + F * grp, t < c1);
+        }
+        float kt[U][F];
+        Frag<T> bk[U][KS], bv[U][KS];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+#pragma unroll
+            for (int o = 0; o < F; ++o) kt[u][o] = phi<T>(to_f32(kr[u].e[o]));
+#pragma unroll
+            for (int s = 0; s < KS; ++s)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    bk[u][s][e] = static_cast<T>(kt[u][8 * s + e]);
+                    bv[u][s][e] = vr[u].e[8 * s + e];
+                }
+        }
+        f32x4 ak[U][NB], av[U][NB];
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                ak[u][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+                av[u][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+            for (int s = 0; s < KS; ++s) {
+                const Frag<T> a1 = sA[(b * KS + s) * 64 + lane];
+                const Frag<T> a2 = sA[(NFS + b * KS + s) * 64 + lane];
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    ak[u][b] = mma(a1, bv[u][s], ak[u][b]);
+                    av[u][b] = mma(a2, bk[u][s], av[u][b]);
+                }
+            }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t t = base + 16 * u + m;
+            if (t < c1) {
+                float gk[F], gv[F];
+#pragma unroll
+                for (int b = 0; b < NB; ++b)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int o = 4 * b + r;
+                        gk[o] = (ak[u][b][r] * uD + dzl[o]) * fminf(kt[u][o], 1.f);
+                        gv[o] = av[u][b][r] * uD;
+                    }
+                store_row<T, F>(dk + (bh * T_ + t) * D + F * grp, gk);
+                store_row<T, F>(dv + (bh * T_ + t) * D + F * grp, gv);
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Host-side dispatch.
+// ---------------------------------------------------------------------------
+template <typename T, int D>
+hipError_t fwd_state_t(const Plan& p, const void* k, const void* v, float* state, void* ws,
+                       hipStream_t s) {
+    const int64_t nblk = p.BH * p.P;
+    char* w = static_cast<char*>(ws);
+    hipLaunchKernelGGL((fwd_state_kernel<T, D>), dim3((unsigned)nblk), dim3(kThreads), 0, s,
+                       static_cast<const T*>(k), static_cast<const T*>(v), state,
+                       state + p.BH * D * D, reinterpret_cast<float*>(w + p.off_part),
+                       reinterpret_cast<int*>(w + p.off_cnt_fwd), p.T, p.P, p.L);
+    return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t fwd_output_t(const Plan& p, const void* q, const float* state, void* o, hipStream_t s) {
+    const int64_t nblk = p.BH * p.NQ;
+    if (p.simple)
+        hipLaunchKernelGGL((fwd_output_kernel<T, D, true>), dim3((unsigned)nblk), dim3(kThreads), 0, s,
+                           static_cast<const T*>(q), state, state + p.BH * D * D, static_cast<T*>(o),
+                           p.T, p.NQ, p.LQ, p.eps);
+    else
+        hipLaunchKernelGGL((fwd_output_kernel<T, D, false>), dim3((unsigned)nblk), dim3(kThreads), 0, s,
+                           static_cast<const T*>(q), state, state + p.BH * D * D, static_cast<T*>(o),
+                           p.T, p.NQ, p.LQ, p.eps);
+    return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t bwd_dq_t(const Plan& p, const void* q, const void* dout, const float* state, void* dq,
+                    void* ws, hipStream_t s) {
+    const int64_t nblk = p.BH * p.PB;
+    char* w = static_cast<char*>(ws);
+    float* part = reinterpret_cast<float*>(w + p.off_part);
+    float* dst = reinterpret_cast<float*>(w + p.off_dstate);
+    int* cnt = reinterpret_cast<int*>(w + p.off_cnt_bwd);
+    if (p.simple)
+        hipLaunchKernelGGL((bwd_dq_kernel<T, D, true>), dim3((unsigned)nblk), dim3(kThreads), 0, s,
+                           static_cast<const T*>(q), static_cast<const T*>(dout), state,
+                           state + p.BH * D * D, static_cast<T*>(dq), part, dst, dst + p.BH * D * D,
+                           cnt, p.T, p.PB, p.LB, p.eps);
+    else
+        hipLaunchKernelGGL((bwd_dq_kernel<T, D, false>), dim3((unsigned)nblk), dim3(kThreads), 0, s,
+                           static_cast<const T*>(q), static_cast<const T*>(dout), state,
+                           state + p.BH * D * D, static_cast<T*>(dq), part, dst, dst + p.BH * D * D,
+                           cnt, p.T, p.PB, p.LB, p.eps);
+    return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t bwd_dkv_t(const Plan& p, const void* k, const void* v, void* dk, void* dv, void* ws,
+                     hipStream_t s) {
+    const int64_t nblk = p.BH * p.NK;
+    const float* dst = reinterpret_cast<const float*>(static_cast<char*>(ws) + p.off_dstate);
+    if (p.simple)
+        hipLaunchKernelGGL((bwd_dkv_kernel<T, D, true>), dim3((unsigned)nblk), dim3(kThreads), 0, s,
+                           static_cast<const T*>(k), static_cast<const T*>(v), dst, dst + p.BH * D * D,
+                           static_cast<T*>(dk), static_cast<T*>(dv), p.T, p.NK, p.LK);
+    else
+        hipLaunchKernelGGL((bwd_dkv_kernel<T, D, false>), dim3((unsigned)nblk), dim3(kThreads), 0, s,
+                           static_cast<const T*>(k), static_cast<const T*>(v), dst, dst + p.BH * D * D,
+                           static_cast<T*>(dk), static_cast<T*>(dv), p.T, p.NK, p.LK);
+    return hipGetLastError();
+}
+
+// dtype codes follow la_dtype: 0 = f32, 1 = f16, 2 = bf16.
+#define LA_DISPATCH(FN, ...)                                         \
+    switch (p.dtype * 2 + (p.D == 128 ? 1 : 0)) {                   \
+        case 0: return FN<float, 64>(p, __VA_ARGS__);               \
+        case 1: return FN<float, 128>(p, __VA_ARGS__);              \
+        case 2: return FN<f16, 64>(p, __VA_ARGS__);                 \
+        case 3: return FN<f16, 128>(p, __VA_ARGS__);                \
+        case 4: return FN<bf16, 64>(p, __VA_ARGS__);                \
+        case 5: return FN<bf16, 128>(p, __VA_ARGS__);               \
+        default: return hipErrorInvalidValue;                       \
+    }
+
+template <typename T, int D>
+constexpr int64_t state_tile() { return StateShape<T, D>::kTT; }
+
+}  // namespace
+
+int64_t state_tile_tokens(int dtype, int D) {
+    if (dtype == 0) return D == 128 ? state_tile<float, 128>() : state_tile<float, 64>();
+    return D == 128 ? state_tile<f16, 128>() : state_tile<f16, 64>();
+}
+
+int64_t bwdq_group_tokens(int dtype, int D) {
+    if (dtype == 0) return D == 128 ? BwdQShape<float, 128>::kG : BwdQShape<float, 64>::kG;
+    return D == 128 ? BwdQShape<f16, 128>::kG : BwdQShape<f16, 64>::kG;
+}
+
+int64_t stream_group_tokens(int dtype, int D) {
+    if (dtype == 0) return D == 128 ? StreamShape<float, 128>::kG : StreamShape<float, 64>::kG;
+    return D == 128 ? StreamShape<f16, 128>::kG : StreamShape<f16, 64>::kG;
+}
+
+hipError_t launch_fwd_state(const Plan& p, const void* k, const void* v, float* state, void* ws,
+                            hipStream_t s) {
+    LA_DISPATCH(fwd_state_t, k, v, state, ws, s);
+}
+hipError_t launch_fwd_output(const Plan& p, const void* q, const float* state, void* o, hipStream_t s) {
+    LA_DISPATCH(fwd_output_t, q, state, o, s);
+}
+hipError_t launch_bwd_dq(const Plan& p, const void* q, const void* dout, const float* state, void* dq,
+                         void* ws, hipStream_t s) {
+    LA_DISPATCH(bwd_dq_t, q, dout, state, dq, ws, s);
+}
+hipError_t launch_bwd_dkv(const Plan& p, const void* k, const void* v, void* dk, void* dv, void* ws,
+                          hipStream_t s) {
+    LA_DISPATCH(bwd_dkv_t, k, v, dk, dv, ws, s);
+}
+
+}  // namespace la

@@ -29,7 +29,9 @@ from .la_oracle import (  # noqa: F401
     fwd_head,
     bwd,
     bwd_head,
+    bwd_leading_terms_head,
     phi,
     quadratic_head,
     sampled_rows_head,
+    state_head,
 )

@@ -109,6 +109,33 @@ def bwd_head(q, k, v, do, eps: float, simple: bool):
     return dqt * dphi(q), dkt * dphi(k), dv
 
 
+def bwd_leading_terms_head(q, k, v, do, eps: float):
+    """Largest summands of dQ and dK in normalised mode, for error scaling.
+
+    dphi(q_t) = u_t / den_t + c_t z and dphi(k_t) = dS v_t + dz add terms that
+    cancel almost exactly when the output hardly depends on Q or K (T = 1:
+    O_t = a_t v / (a_t + eps), so both gradients are O(eps)). Returns
+    (max |u/den * phi'(q)|, max |dS v * phi'(k)|): the scale rounding errors of
+    the summands are measured against.
+    """
+    v = np.asarray(v, dtype=np.float64)
+    do = np.asarray(do, dtype=np.float64)
+    qt, kt = phi(q), phi(k)
+    s = kt.T @ v
+    z = kt.sum(axis=0)
+    den = qt @ z + eps
+    u = do @ s.T
+    ds = qt.T @ (do / den[:, None])
+    return (float(np.max(np.abs(u / den[:, None] * dphi(q)))),
+            float(np.max(np.abs((v @ ds.T) * dphi(k)))))
+
+
+def state_head(k, v):
+    """The state alone for one (batch, head): S = phi(K)^T V and z = sum_t phi(k_t)."""
+    kt = phi(k)
+    return kt.T @ np.asarray(v, dtype=np.float64), kt.sum(axis=0)
+
+
 def sampled_rows_head(q, k, v, rows, eps: float, simple: bool) -> np.ndarray:
     """Output rows O_t, t in ``rows``, computed one by one from the quadratic form.
 

@@ -1,0 +1,203 @@
+"""Host-side tests of the C ABI: no GPU needed, no kernel is launched.
+
+Every call here is either a pure query (sizes, strings, version) or carries an
+argument error, which include/la.h promises to report before any HIP call.
+Pointers are fake addresses: they are never dereferenced.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import non_causal_linear_amd as la
+from non_causal_linear_amd import Problem
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "la.h")
+
+OK, NULL, SHAPE, DTYPE, HEAD_DIM, FLAGS, EPS, WORKSPACE, ALIGN, ALIAS, DEVICE = range(11)
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(la.LIB_PATH):
+        from non_causal_linear_amd import build
+        build.build()
+    return la.lib()
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(la_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_what_binding_expects():
+    assert header_functions() == sorted(la.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(L):
+    out = subprocess.run(["nm", "-D", "--defined-only", la.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    exported = set(re.findall(r"\sT\s(la_\w+)$", out, flags=re.M))
+    for name in header_functions():
+        assert name in exported, name
+        assert getattr(L, name) is not None
+
+
+def test_version_and_status_strings(L):
+    assert L.la_version() == 1
+    for s in range(11):
+        txt = L.la_status_str(s).decode()
+        assert txt.startswith("LA_"), txt
+    assert L.la_status_str(99).decode() == "unknown la_status"
+    assert "HEAD_DIM" in L.la_status_str(HEAD_DIM).decode()
+
+
+def prob(B=2, H=3, T=100, D=64, dtype=1, flags=0, eps=1e-6):
+    return Problem(B, H, T, D, dtype, flags, eps)
+
+
+def test_state_bytes_formula(L):
+    for (B, H, D) in ((1, 2, 64), (8, 16, 64), (8, 32, 128)):
+        p = prob(B=B, H=H, D=D)
+        assert L.la_state_bytes(ctypes.byref(p)) == B * H * (D * D + D) * 4
+
+
+def test_workspace_bytes_covers_state_and_partials(L):
+    # B8-H16-T16384-D64: 128 heads, 8 slices per head for the split-T reduction
+    p = prob(B=8, H=16, T=16384, D=64)
+    ws = L.la_workspace_bytes(ctypes.byref(p))
+    E = 64 * 64 + 64
+    assert ws >= 128 * 8 * E * 4 + 2 * 128 * E * 4
+    assert ws % 256 == 0
+    # invalid problems report 0
+    assert L.la_workspace_bytes(ctypes.byref(prob(D=96))) == 0
+    assert L.la_state_bytes(ctypes.byref(prob(dtype=7))) == 0
+    assert L.la_workspace_bytes(None) == 0
+
+
+def test_workspace_is_pure_function_of_shape(L):
+    a = L.la_workspace_bytes(ctypes.byref(prob(B=2, H=8, T=262144, D=64, dtype=2, flags=1)))
+    b = L.la_workspace_bytes(ctypes.byref(prob(B=2, H=8, T=262144, D=64, dtype=2, flags=1)))
+    assert a == b > 0
+
+
+A = 0x100000  # fake, 256-aligned, never dereferenced
+TB = 2 * 3 * 100 * 64 * 2  # bytes of one tensor of prob()
+
+
+def addrs(n, stride=1 << 24):
+    return [ctypes.c_void_p(A + i * stride) for i in range(n)]
+
+
+def fwd_call(L, p, q=None, k=None, v=None, o=None, state=None, ws=None, ws_bytes=None):
+    d = addrs(6)
+    q = d[0] if q is None else q
+    k = d[1] if k is None else k
+    v = d[2] if v is None else v
+    o = d[3] if o is None else o
+    state = d[4] if state is None else state
+    ws = d[5] if ws is None else ws
+    if ws_bytes is not None:
+        need = ws_bytes
+    else:
+        need = L.la_workspace_bytes(ctypes.byref(p)) if p is not None else 1 << 20
+    return L.la_fwd(ctypes.byref(p) if p is not None else None, q, k, v, o, state, ws, need, None)
+
+
+def test_fwd_rejects_bad_problems(L):
+    assert fwd_call(L, None) == NULL
+    assert fwd_call(L, prob(dtype=3)) == DTYPE
+    assert fwd_call(L, prob(dtype=-1)) == DTYPE
+    assert fwd_call(L, prob(D=32)) == HEAD_DIM
+    assert fwd_call(L, prob(D=96)) == HEAD_DIM
+    assert fwd_call(L, prob(B=-1)) == SHAPE
+    assert fwd_call(L, prob(T=-5)) == SHAPE
+    assert fwd_call(L, prob(H=1 << 30)) == SHAPE
+    assert fwd_call(L, prob(flags=2)) == FLAGS
+    assert fwd_call(L, prob(eps=-1e-3)) == EPS
+    assert fwd_call(L, prob(eps=float("nan"))) == EPS
+    assert fwd_call(L, prob(eps=float("inf"))) == EPS
+
+
+def test_fwd_rejects_bad_buffers(L):
+    p = prob()
+    need = L.la_workspace_bytes(ctypes.byref(p))
+    assert fwd_call(L, p, ws_bytes=need - 1) == WORKSPACE
+    assert fwd_call(L, p, q=ctypes.c_void_p(0)) == NULL
+    assert fwd_call(L, p, o=ctypes.c_void_p(0)) == NULL
+    assert fwd_call(L, p, q=ctypes.c_void_p(A + 8)) == ALIGN
+    assert fwd_call(L, p, o=ctypes.c_void_p(A + (3 << 24) + 4)) == ALIGN
+    assert fwd_call(L, p, ws=ctypes.c_void_p(A + (5 << 24) + 16)) == ALIGN
+    # output aliasing an input, fully or partly
+    assert fwd_call(L, p, o=ctypes.c_void_p(A)) == ALIAS
+    assert fwd_call(L, p, o=ctypes.c_void_p(A + (1 << 24) + TB - 16)) == ALIAS
+    # state overlapping the output
+    assert fwd_call(L, p, state=ctypes.c_void_p(A + (3 << 24) + 256)) == ALIAS
+    # workspace overlapping an input
+    assert fwd_call(L, p, ws=ctypes.c_void_p(A + (2 << 24))) == ALIAS
+
+
+def test_empty_problems_need_no_device(L):
+    # B*H = 0: nothing to compute, nothing launched, NULL tensors accepted
+    p = prob(B=0)
+    z = ctypes.c_void_p(0)
+    assert L.la_fwd(ctypes.byref(p), z, z, z, z, z, ctypes.c_void_p(A), 256, None) == OK
+    assert L.la_bwd(ctypes.byref(p), z, z, z, z, z, z, z, z, ctypes.c_void_p(A), 256, None) == OK
+    # T = 0 backward and output: no rows, nothing launched
+    p = prob(T=0)
+    need = L.la_workspace_bytes(ctypes.byref(p))
+    assert L.la_fwd_output(ctypes.byref(p), z, ctypes.c_void_p(A), z, None) == OK
+    assert L.la_bwd(ctypes.byref(p), z, z, z, z, ctypes.c_void_p(A), z, z, z,
+                    ctypes.c_void_p(A + (1 << 24)), need, None) == OK
+
+
+def test_bwd_rejects_bad_buffers(L):
+    p = prob()
+    need = L.la_workspace_bytes(ctypes.byref(p))
+    d = addrs(9)
+
+    def call(**kw):
+        args = dict(q=d[0], k=d[1], v=d[2], do=d[3], state=d[4], dq=d[5], dk=d[6], dv=d[7], ws=d[8])
+        args.update(kw)
+        return L.la_bwd(ctypes.byref(p), args["q"], args["k"], args["v"], args["do"], args["state"],
+                        args["dq"], args["dk"], args["dv"], args["ws"], kw.get("nbytes", need), None)
+
+    assert call(state=ctypes.c_void_p(0)) == NULL
+    assert call(do=ctypes.c_void_p(0)) == NULL
+    assert call(nbytes=need - 256) == WORKSPACE
+    assert call(dk=d[5]) == ALIAS          # two outputs on one buffer
+    assert call(dv=d[3]) == ALIAS          # output on an input
+    assert call(dq=d[4]) == ALIAS          # output on the state
+    assert call(dq=ctypes.c_void_p(A + (5 << 24) + 2)) == ALIGN
+    assert L.la_bwd(ctypes.byref(prob(D=256)), *d[:9], need, None) == HEAD_DIM
+
+
+def test_step_calls_validate(L):
+    p = prob()
+    need = L.la_workspace_bytes(ctypes.byref(p))
+    d = addrs(6)
+    z = ctypes.c_void_p(0)
+    assert L.la_fwd_state(ctypes.byref(p), d[0], d[1], z, d[3], need, None) == NULL
+    assert L.la_fwd_state(ctypes.byref(p), d[0], d[1], d[2], d[3], need - 1, None) == WORKSPACE
+    assert L.la_fwd_state(ctypes.byref(p), d[0], d[1], d[0], d[3], need, None) == ALIAS
+    assert L.la_fwd_output(ctypes.byref(p), d[0], d[1], d[0], None) == ALIAS
+    assert L.la_fwd_output(ctypes.byref(prob(flags=4)), d[0], d[1], d[2], None) == FLAGS
+    assert L.la_bwd_dq(ctypes.byref(p), d[0], d[1], z, d[3], d[4], need, None) == NULL
+    assert L.la_bwd_dq(ctypes.byref(p), d[0], d[1], d[2], d[1], d[4], need, None) == ALIAS
+    assert L.la_bwd_dkv(ctypes.byref(p), d[0], d[1], d[2], d[2], d[4], need, None) == ALIAS
+    assert L.la_bwd_dkv(ctypes.byref(p), d[0], d[1], d[2], d[3], d[4], 0, None) == WORKSPACE
+
+
+def test_binding_marshalling_rejects_cpu_tensors():
+    torch = pytest.importorskip("torch")
+    x = torch.zeros(1, 1, 4, 64, dtype=torch.float16)
+    with pytest.raises(ValueError):
+        la.fwd(x, x, x)
+    with pytest.raises(ValueError):
+        la.make_problem((1, 4, 64), torch.float16, 1e-6, False)
+    with pytest.raises(ValueError):
+        la.make_problem((1, 1, 4, 64), torch.int32, 1e-6, False)

@@ -1,0 +1,264 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Small cases compare every element; they span several tiles and slices and end
+on ragged tails. The five named workloads run at full size in the launch
+configuration the benchmark times: the fp32 state (S, z) is checked for every
+head, O/dQ/dK/dV completely on four heads (first, last, two seeded picks) and
+O on sampled rows of every other head. Results must also be bit-identical
+across reruns.
+"""
+import numpy as np
+import pytest
+import torch
+
+import non_causal_linear_amd as la
+import oracle
+from synth import WORKLOADS, Workload, make_inputs
+from tests.la_testutil import (TIGHT, TOL, TORCH_DTYPE, bytes_equal, decode, max_rel_err,
+                               split_state, to_device)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    la.lib()
+    torch.manual_seed(0)
+
+
+def run(w: Workload, x: dict, bwd: bool):
+    dev = {n: to_device(a, w.dtype) for n, a in x.items()}
+    o, state = la.fwd(dev["q"], dev["k"], dev["v"], eps=w.eps, simple=w.simple)
+    out = {"o": o, "state": state}
+    if bwd:
+        out["dq"], out["dk"], out["dv"] = la.bwd(dev["q"], dev["k"], dev["v"], dev["do"], state,
+                                                 eps=w.eps, simple=w.simple)
+    torch.cuda.synchronize()
+    return dev, out
+
+
+def check(name, got, ref, dtype, where="", scale=None):
+    """Normwise max relative error; ``scale`` (if given) replaces max|ref| when larger:
+    the size of summands that cancel in an ill-conditioned result."""
+    err = max_rel_err(got, ref)
+    if scale is not None and scale > np.max(np.abs(ref)):
+        err = float(np.max(np.abs(got - ref)) / scale)
+        where += " (vs leading terms)"
+    print(f"  {name}{where}: max rel err {err:.3e}", flush=True)
+    assert np.all(np.isfinite(got)), f"{name}{where}: non-finite output"
+    assert err <= TOL[dtype], f"{name}{where}: {err:.3e} > {TOL[dtype]}"
+    if dtype in TIGHT:
+        assert err <= TIGHT[dtype], f"{name}{where}: {err:.3e} > {TIGHT[dtype]} (fp32 bar)"
+    return err
+
+
+def heads_of(x, dtype):
+    d = oracle.decode(x, dtype)
+    return d.reshape(-1, d.shape[-2], d.shape[-1])
+
+
+# ------------------------------------------------------------- small, full compare
+
+SMALL_T = [1, 129, 1000, 4097]
+
+
+@pytest.mark.parametrize("simple", [False, True], ids=["norm", "simple"])
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("T", SMALL_T)
+def test_small_fwd_bwd_all_elements(T, D, dtype, simple):
+    seed = 10_000 + 97 * T + D + 7 * ["f32", "f16", "bf16"].index(dtype) + (3 if simple else 0)
+    w = Workload("small", 2, 3, T, D, dtype, simple=simple, seed=seed)
+    print(f"case T={T} D={D} {dtype} simple={simple} seed={seed}", flush=True)
+    x = make_inputs(w)
+    _, out = run(w, x, bwd=True)
+    o_ref, s_ref, z_ref = oracle.fwd(x["q"], x["k"], x["v"], dtype, w.eps, simple)
+    dq_ref, dk_ref, dv_ref = oracle.bwd(x["q"], x["k"], x["v"], x["do"], dtype, w.eps, simple)
+    s_got, z_got = split_state(out["state"], w.B, w.H, D)
+    check("S", s_got, s_ref, dtype)
+    check("z", z_got, z_ref, dtype)
+    check("O", decode(out["o"], dtype), o_ref, dtype)
+    sq = sk = None
+    if T == 1 and not simple:
+        # the exact dQ, dK are O(eps): two O(1) summands cancel; measure the
+        # error against those summands instead of the result
+        sc = [oracle.bwd_leading_terms_head(*(oracle.decode(x[n], dtype)[b, h]
+                                              for n in ("q", "k", "v", "do")), w.eps)
+              for b in range(w.B) for h in range(w.H)]
+        sq, sk = max(a for a, _ in sc), max(b for _, b in sc)
+    check("dQ", decode(out["dq"], dtype), dq_ref, dtype, scale=sq)
+    check("dK", decode(out["dk"], dtype), dk_ref, dtype, scale=sk)
+    check("dV", decode(out["dv"], dtype), dv_ref, dtype)
+
+
+# ------------------------------------------------------------- full-size workloads
+
+def sampled_heads(n, seed):
+    rng = np.random.default_rng(seed)
+    picks = [0, n - 1] + [int(h) for h in rng.choice(np.arange(1, max(n - 1, 2)), size=2)]
+    return sorted(set(h for h in picks if 0 <= h < n))
+
+
+@pytest.mark.parametrize("name", list(WORKLOADS))
+def test_workload_full_size(name):
+    w = WORKLOADS[name]
+    modes = [False, True] if name.startswith("B1-H2-T128") else [w.simple]
+    print(f"workload {name}", flush=True)
+    x = make_inputs(w, with_grad=True)
+    for simple in modes:
+        wm = Workload(w.name, w.B, w.H, w.T, w.D, w.dtype, w.sigma, simple, w.eps, w.bwd, w.seed)
+        dev, out = run(wm, x, bwd=w.bwd)
+        n = w.B * w.H
+        qh, kh, vh = heads_of(x["q"], w.dtype), heads_of(x["k"], w.dtype), heads_of(x["v"], w.dtype)
+        s_got, z_got = split_state(out["state"], w.B, w.H, w.D)
+        s_got, z_got = s_got.reshape(n, w.D, w.D), z_got.reshape(n, w.D)
+        # state of every head
+        worst_s = worst_z = 0.0
+        for h in range(n):
+            s_ref, z_ref = oracle.state_head(kh[h], vh[h])
+            worst_s = max(worst_s, max_rel_err(s_got[h], s_ref))
+            worst_z = max(worst_z, max_rel_err(z_got[h], z_ref))
+        print(f"  state, all {n} heads: S {worst_s:.3e}  z {worst_z:.3e}", flush=True)
+        assert worst_s <= TOL[w.dtype] and worst_z <= TOL[w.dtype]
+        o_all = out["o"].reshape(n, w.T, w.D)
+        # complete tensors on sampled heads
+        heads = sampled_heads(n, w.seed + 17)
+        for h in heads:
+            o_ref, _, _ = oracle.fwd_head(qh[h], kh[h], vh[h], w.eps, simple)
+            check("O", decode(o_all[h], w.dtype), o_ref, w.dtype, f" head {h}")
+            if w.bwd:
+                dh = heads_of(x["do"], w.dtype)[h]
+                refs = oracle.bwd_head(qh[h], kh[h], vh[h], dh, w.eps, simple)
+                for nm, ref in zip(("dq", "dk", "dv"), refs):
+                    got = decode(out[nm].reshape(n, w.T, w.D)[h], w.dtype)
+                    check(nm, got, ref, w.dtype, f" head {h}")
+        # sampled rows of O on every other head (first and last row included)
+        rng = np.random.default_rng(w.seed + 29)
+        worst = 0.0
+        for h in range(n):
+            if h in heads:
+                continue
+            rows = sorted(set([0, w.T - 1] + [int(r) for r in rng.integers(0, w.T, size=6)]))
+            ref = oracle.sampled_rows_head(qh[h], kh[h], vh[h], rows, w.eps, simple)
+            got = decode(o_all[h][rows], w.dtype)
+            worst = max(worst, max_rel_err(got, ref))
+        print(f"  O sampled rows, other heads: {worst:.3e}", flush=True)
+        assert worst <= TOL[w.dtype]
+        # bit-identical across reruns
+        _, out2 = run(wm, x, bwd=w.bwd)
+        for nm in out:
+            assert bytes_equal(out[nm], out2[nm]), f"{nm} differs between runs"
+        del dev, out, out2
+        torch.cuda.empty_cache()
+
+
+# ------------------------------------------------------------- invariants and edges
+
+def test_v_ones_gives_ones():
+    w = Workload("v1", 2, 2, 3000, 64, "f16", seed=321)
+    x = make_inputs(w, with_grad=False)
+    x["v"] = np.ones_like(x["v"])
+    _, out = run(w, x, bwd=False)
+    o = decode(out["o"], "f16")
+    err = float(np.max(np.abs(o - 1.0)))
+    print(f"  V=ones: max |O-1| = {err:.3e}", flush=True)
+    assert err <= 2.0 ** -10
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_joint_kv_permutation_within_tolerance(dtype):
+    w = Workload("perm", 1, 2, 2048, 64, dtype, seed=654)
+    x = make_inputs(w, with_grad=False)
+    perm = np.random.default_rng(3).permutation(w.T)
+    xp = dict(x, k=np.ascontiguousarray(x["k"][:, :, perm]), v=np.ascontiguousarray(x["v"][:, :, perm]))
+    _, a = run(w, x, bwd=False)
+    _, b = run(w, xp, bwd=False)
+    oa, ob = decode(a["o"], dtype), decode(b["o"], dtype)
+    assert max_rel_err(ob, oa) <= TOL[dtype]
+
+
+def test_q_row_permutation_permutes_output():
+    w = Workload("qperm", 1, 2, 1024, 64, "f16", seed=987)
+    x = make_inputs(w, with_grad=False)
+    perm = np.random.default_rng(4).permutation(w.T)
+    xp = dict(x, q=np.ascontiguousarray(x["q"][:, :, perm]))
+    _, a = run(w, x, bwd=False)
+    _, b = run(w, xp, bwd=False)
+    oa, ob = decode(a["o"], "f16"), decode(b["o"], "f16")
+    assert max_rel_err(ob, oa[:, :, perm]) <= TOL["f16"]
+    print(f"  Q-row permutation bitwise: {np.array_equal(ob, oa[:, :, perm])}", flush=True)
+
+
+def test_large_eps_matters():
+    # eps comparable to phi(q).z: a misplaced eps would show
+    w = Workload("eps", 1, 2, 256, 64, "f32", eps=3000.0, seed=111)
+    x = make_inputs(w)
+    _, out = run(w, x, bwd=True)
+    o_ref, _, _ = oracle.fwd(x["q"], x["k"], x["v"], "f32", w.eps, False)
+    dq_ref, dk_ref, dv_ref = oracle.bwd(x["q"], x["k"], x["v"], x["do"], "f32", w.eps, False)
+    check("O", decode(out["o"], "f32"), o_ref, "f32")
+    check("dQ", decode(out["dq"], "f32"), dq_ref, "f32")
+    check("dK", decode(out["dk"], "f32"), dk_ref, "f32")
+    check("dV", decode(out["dv"], "f32"), dv_ref, "f32")
+
+
+def test_t_zero_writes_zero_state():
+    q = torch.zeros(2, 3, 0, 64, dtype=torch.float16, device="cuda")
+    state = torch.full((2 * 3 * (64 * 64 + 64),), 7.0, device="cuda")
+    o, st = la.fwd(q, q.clone(), q.clone(), state=state)
+    torch.cuda.synchronize()
+    assert o.numel() == 0 and torch.count_nonzero(st).item() == 0
+    dq, dk, dv = la.bwd(q, q.clone(), q.clone(), q.clone(), st)
+    assert dq.numel() == dk.numel() == dv.numel() == 0
+
+
+def test_underflowing_features_give_zero_output():
+    # every phi(q) underflows (q = -120): den = eps, O = 0; simple mode also 0
+    w = Workload("uf", 1, 1, 300, 64, "f32", seed=5)
+    x = make_inputs(w, with_grad=False)
+    x["q"] = np.full_like(x["q"], -120.0)
+    for simple in (False, True):
+        wm = Workload("uf", 1, 1, 300, 64, "f32", simple=simple, seed=5)
+        _, out = run(wm, x, bwd=False)
+        o = decode(out["o"], "f32")
+        assert np.all(np.isfinite(o)) and np.max(np.abs(o)) < 1e-30
+
+
+def test_step_calls_compose_to_fwd_bwd():
+    w = Workload("steps", 2, 4, 3333, 64, "bf16", seed=42)
+    x = make_inputs(w)
+    dev, out = run(w, x, bwd=True)
+    st = la.fwd_state(dev["k"], dev["v"], eps=w.eps)
+    o = la.fwd_output(dev["q"], st, eps=w.eps)
+    dq = la.bwd_dq(dev["q"], dev["do"], st, eps=w.eps)
+    dk, dv = la.bwd_dkv(dev["k"], dev["v"], eps=w.eps)
+    torch.cuda.synchronize()
+    for a, b in ((st, out["state"]), (o, out["o"]), (dq, out["dq"]), (dk, out["dk"]), (dv, out["dv"])):
+        assert bytes_equal(a, b)
+
+
+def test_reruns_bit_identical_many_slices():
+    # B*H = 2 makes the planner split each head into many slices
+    w = Workload("det", 1, 2, 50_000, 64, "f16", seed=77)
+    x = make_inputs(w)
+    _, a = run(w, x, bwd=True)
+    for _ in range(2):
+        _, b = run(w, x, bwd=True)
+        for nm in a:
+            assert bytes_equal(a[nm], b[nm]), nm
+
+
+def test_non_default_stream():
+    w = Workload("stream", 1, 2, 777, 128, "f16", seed=9)
+    x = make_inputs(w)
+    dev = {n: to_device(a, w.dtype) for n, a in x.items()}
+    ref_o, ref_st = la.fwd(dev["q"], dev["k"], dev["v"])
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        o, st = la.fwd(dev["q"], dev["k"], dev["v"])
+    s.synchronize()
+    assert bytes_equal(o, ref_o) and bytes_equal(st, ref_st)

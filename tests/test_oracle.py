@@ -339,3 +339,16 @@ def test_workloads_inputs_are_seeded_and_rounded():
         np.testing.assert_array_equal(a[n], b[n])
     assert a["q"].dtype == np.float32 and a["q"].shape == (1, 2, 128, 64)
     assert not np.array_equal(a["q"], a["k"])
+
+
+def test_leading_terms_cancel_at_t1():
+    # T = 1, normalised: dQ = phi'(q) k~ (v.dO) eps / den^2, tiny next to u/den
+    q, k, v, do = (rand((1, 8), s) for s in (81, 82, 83, 84))
+    eps = 1e-6
+    dq, dk, _ = oracle.bwd_head(q, k, v, do, eps, simple=False)
+    sq, sk = oracle.bwd_leading_terms_head(q, k, v, do, eps)
+    assert np.abs(dq).max() < 1e-4 * sq and np.abs(dk).max() < 1e-4 * sk
+    kt, qt = oracle.phi(k[0]), oracle.phi(q[0])
+    den = qt @ kt + eps
+    np.testing.assert_allclose(dq[0], oracle.dphi(q[0]) * kt * (v[0] @ do[0]) * eps / den**2,
+                               rtol=1e-6, atol=1e-300)
