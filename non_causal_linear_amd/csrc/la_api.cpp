@@ -14,8 +14,6 @@
 
 namespace {
 
-// Aim for this many workgroups per launch: 256 CUs, several resident each.
-constexpr int64_t kTargetWorkgroups = 1024;
 // Shortest token slice worth a workgroup of its own.
 constexpr int64_t kMinSlice = 256;
 // Largest B*H accepted (grid sizes stay below 2^31).
@@ -27,15 +25,17 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 // Split T tokens of each of BH heads into P pieces of L tokens (L a multiple of
-// gran, last piece ragged): P is the largest power of two with BH*P within the
-// target and pieces of at least kMinSlice tokens. Pure function of the shape.
-void split(int64_t BH, int64_t T, int64_t gran, int& P, int64_t& L) {
+// the kernel's granularity, last piece ragged): P is the largest power of two
+// with BH*P within the kernel's target grid and pieces of at least kMinSlice
+// tokens. Pure function of the shape.
+void split(int64_t BH, int64_t T, la::SplitCfg cfg, int& P, int64_t& L) {
     if (T <= 0 || BH <= 0) {
         P = 1;
         L = 0;
         return;
     }
-    const int64_t want = std::max<int64_t>(1, cdiv(kTargetWorkgroups, BH));
+    const int64_t gran = cfg.gran;
+    const int64_t want = std::max<int64_t>(1, cdiv(cfg.target_wgs, BH));
     const int64_t maxp = std::max<int64_t>(1, T / kMinSlice);
     int64_t p = 1;
     while (p * 2 <= want && p * 2 <= maxp) p *= 2;
@@ -65,10 +65,10 @@ la::Plan make_plan(const la_problem* p) {
     pl.dtype = p->dtype;
     pl.simple = (p->flags & LA_SIMPLE) != 0;
     pl.eps = p->eps;
-    split(pl.BH, pl.T, la::state_tile_tokens(pl.dtype, pl.D), pl.P, pl.L);
-    split(pl.BH, pl.T, la::bwdq_group_tokens(pl.dtype, pl.D), pl.PB, pl.LB);
-    split(pl.BH, pl.T, la::stream_group_tokens(pl.dtype, pl.D), pl.NQ, pl.LQ);
-    split(pl.BH, pl.T, la::stream_group_tokens(pl.dtype, pl.D), pl.NK, pl.LK);
+    split(pl.BH, pl.T, la::split_config(la::kStepState, pl.dtype, pl.D), pl.P, pl.L);
+    split(pl.BH, pl.T, la::split_config(la::kStepBwdQ, pl.dtype, pl.D), pl.PB, pl.LB);
+    split(pl.BH, pl.T, la::split_config(la::kStepOutput, pl.dtype, pl.D), pl.NQ, pl.LQ);
+    split(pl.BH, pl.T, la::split_config(la::kStepBwdKV, pl.dtype, pl.D), pl.NK, pl.LK);
     const size_t E = size_t(pl.D) * pl.D + pl.D;  // floats per (S, z) block
     const size_t cnt = align256(size_t(pl.BH) * sizeof(int));
     const int maxp = std::max(pl.P, pl.PB);

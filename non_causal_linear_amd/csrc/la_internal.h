@@ -32,10 +32,15 @@ struct Plan {
     size_t ws_bytes = 0;
 };
 
-// Token granularity the kernels need a split to respect.
-int64_t state_tile_tokens(int dtype, int D);   // fwd state kernel tile
-int64_t bwdq_group_tokens(int dtype, int D);   // bwd Q-side workgroup iteration
-int64_t stream_group_tokens(int dtype, int D); // output / bwd K/V workgroup iteration
+// How a kernel wants its tokens split: pieces are multiples of `gran` tokens
+// (the last one ragged) and the grid should come close to `target_wgs`
+// workgroups (what fits resident on the 256 CUs of the chip at once).
+struct SplitCfg {
+    int64_t gran;
+    int64_t target_wgs;
+};
+enum Step { kStepState = 0, kStepOutput = 1, kStepBwdQ = 2, kStepBwdKV = 3 };
+SplitCfg split_config(int step, int dtype, int D);
 
 hipError_t launch_fwd_state(const Plan& p, const void* k, const void* v, float* state,
                             void* ws, hipStream_t s);

@@ -59,6 +59,42 @@ template <> struct Elt<f16> { using frag = f16x8; static constexpr bool kScaled 
 template <> struct Elt<bf16> { using frag = bf16x8; static constexpr bool kScaled = false; };
 template <typename T> using Frag = typename Elt<T>::frag;
 
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef f16 f16x4 __attribute__((ext_vector_type(4)));
+
+// LDS transpose read (ds_read_b64_tr_b16). Within each group of 16 lanes, the
+// 8 bytes that lane i addresses become row i/4, columns 4(i%4)..4(i%4)+3 of a
+// 4 x 16 block of 16-bit values, and lane j receives column j, rows 0..3 in
+// order. Pointing lane i of group g at row (4 g' + i/4), column (c0 + 4(i%4))
+// of a row-major tile therefore hands lane j the 4 consecutive rows of column
+// c0 + j: an MFMA operand whose contraction index runs over tile rows.
+__device__ __forceinline__ i16x4 lds_read_tr(const void* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) i16x4*)(const_cast<void*>(p)));
+}
+
+template <typename T>
+__device__ __forceinline__ Frag<T> join_frag(i16x4 lo, i16x4 hi) {
+    const i16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_bit_cast(Frag<T>, v);
+}
+
+// 16x16x16 MFMA on 16-bit operands held as raw bits (4 values per lane).
+template <typename T> __device__ __forceinline__ f32x4 mma_k16(i16x4 a, i16x4 b, f32x4 c);
+template <> __device__ __forceinline__ f32x4 mma_k16<f16>(i16x4 a, i16x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, a),
+                                                 __builtin_bit_cast(f16x4, b), c, 0, 0, 0);
+}
+template <> __device__ __forceinline__ f32x4 mma_k16<bf16>(i16x4 a, i16x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+
+// Orders this wave's LDS writes before its following LDS reads.
+__device__ __forceinline__ void wave_lds_sync() {
+    __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+}
+
 __device__ __forceinline__ f32x4 mma(f16x8 a, f16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
@@ -322,6 +358,176 @@ __global__ __launch_bounds__(kThreads) void fwd_state_kernel(
     if (P > 1) combine_if_last<D>(part, cnt, stS, stz, bh, P, s_flag);
 }
 
+// Steps 1-3 for 16-bit inputs at D = 64: every wave streams its own 32-token
+// steps of the workgroup's slice (steps w, w + 4, ...) with two steps of loads
+// in flight, and needs no workgroup barrier until the end. Per step a lane
+// loads 16 bytes of 4 rows of K and of V (8 consecutive rows per wave
+// instruction), applies phi to K in fp32, and stores both tiles row-major in
+// the wave's own LDS area; transpose reads then give the MFMA operands
+// directly: A = phi(K)^T (feature x token) and B = [V | 1] (token x feature).
+// The wave accumulates the whole 64 x 64 S and z; the four waves' sums are
+// added in a fixed order at the end.
+struct StateW64 {
+    static constexpr int kStep = 32;  // tokens per wave step
+    static constexpr int kLDR = 72;   // LDS row stride (elements): 144 B rows
+    static constexpr int kTile = kStep * kLDR;
+};
+
+template <typename T>
+__global__ __launch_bounds__(kThreads, 2) void fwd_state_w64_kernel(
+    const T* __restrict__ k, const T* __restrict__ v, float* __restrict__ stS,
+    float* __restrict__ stz, float* __restrict__ part, int* __restrict__ cnt, int64_t T_, int P,
+    int64_t L) {
+    constexpr int D = 64, NB = 4, E = D * D + D;
+    constexpr int STEP = StateW64::kStep, LDR = StateW64::kLDR, TILE = StateW64::kTile;
+    constexpr int kTileBytes = kWaves * 2 * TILE * (int)sizeof(T);
+    constexpr int kRedBytes = 2 * E * (int)sizeof(float);
+    __shared__ __attribute__((aligned(16))) unsigned char smem[kTileBytes > kRedBytes ? kTileBytes : kRedBytes];
+    __shared__ int s_flag[1];
+
+    const int wid = xcd_remap(blockIdx.x, gridDim.x);
+    const int64_t bh = wid / P;
+    const int p = wid % P;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int m = lane & 15, grp = lane >> 4;
+    const int c = lane & 7, rg = lane >> 3;
+    const int64_t t0 = (int64_t)p * L;
+    const int64_t t1 = min(t0 + L, T_);
+    const int nsteps = (int)(t1 > t0 ? (t1 - t0 + STEP - 1) / STEP : 0);
+    T* sK = reinterpret_cast<T*>(smem) + wave * 2 * TILE;
+    T* sV = sK + TILE;
+    const T* kb = k + bh * T_ * D + c * 8;
+    const T* vb = v + bh * T_ * D + c * 8;
+
+    f32x4 acc[NB][NB + 1];
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int j = 0; j <= NB; ++j) acc[b][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    Frag<T> ones;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ones[e] = static_cast<T>(1.f);
+
+    struct Stage {
+        uint4 k[4], v[4];
+    };
+    auto issue = [&](Stage& st, int step) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int64_t t = t0 + (int64_t)step * STEP + rg + 8 * r;
+            if (step < nsteps && t < t1) {
+                st.k[r] = *reinterpret_cast<const uint4*>(kb + t * D);
+                st.v[r] = *reinterpret_cast<const uint4*>(vb + t * D);
+            } else {
+                st.k[r] = make_uint4(0u, 0u, 0u, 0u);
+                st.v[r] = make_uint4(0u, 0u, 0u, 0u);
+            }
+        }
+    };
+    // phi on K (fp32, rounded to T), padded rows zeroed after phi, row-major to LDS
+    auto consume = [&](const Stage& st, int step) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int row = rg + 8 * r;
+            const bool ok = t0 + (int64_t)step * STEP + row < t1;
+            const T* ke = reinterpret_cast<const T*>(&st.k[r]);
+            Row<T, 8> kt;
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                kt.e[e] = ok ? static_cast<T>(phi<T>(to_f32(ke[e]))) : static_cast<T>(0.f);
+            *reinterpret_cast<uint4*>(&sK[row * LDR + 8 * c]) = *reinterpret_cast<const uint4*>(kt.e);
+            *reinterpret_cast<uint4*>(&sV[row * LDR + 8 * c]) = st.v[r];
+        }
+    };
+    const int rA = 8 * grp + (m >> 2), cA = 4 * (m & 3);
+    auto mma_step = [&]() {
+        wave_lds_sync();
+        Frag<T> a[NB];
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+            a[b] = join_frag<T>(lds_read_tr(&sK[rA * LDR + 16 * b + cA]),
+                                lds_read_tr(&sK[(rA + 4) * LDR + 16 * b + cA]));
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+            const Frag<T> bv = join_frag<T>(lds_read_tr(&sV[rA * LDR + 16 * j + cA]),
+                                            lds_read_tr(&sV[(rA + 4) * LDR + 16 * j + cA]));
+#pragma unroll
+            for (int b = 0; b < NB; ++b) acc[b][j] = mma(a[b], bv, acc[b][j]);
+        }
+#pragma unroll
+        for (int b = 0; b < NB; ++b) acc[b][NB] = mma(a[b], ones, acc[b][NB]);
+        wave_lds_sync();
+    };
+
+    Stage s0, s1;
+    issue(s0, wave);
+    issue(s1, wave + kWaves);
+    for (int st = wave; st < nsteps; st += 2 * kWaves) {
+        consume(s0, st);
+        issue(s0, st + 2 * kWaves);
+        mma_step();
+        if (st + kWaves >= nsteps) break;
+        consume(s1, st + kWaves);
+        issue(s1, st + 3 * kWaves);
+        mma_step();
+    }
+
+    // fixed-order sum of the four waves: (w0 + w2) + (w1 + w3)
+    __syncthreads();
+    float* red = reinterpret_cast<float*>(smem);
+    if (wave >= 2) {
+        float* dst = red + (wave - 2) * E;
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+#pragma unroll
+            for (int j = 0; j < NB; ++j)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) dst[(16 * b + 4 * grp + r) * D + 16 * j + m] = acc[b][j][r];
+            if (m == 0)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) dst[D * D + 16 * b + 4 * grp + r] = acc[b][NB][r];
+        }
+    }
+    __syncthreads();
+    if (wave < 2) {
+        float* dst = red + wave * E;
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+#pragma unroll
+            for (int j = 0; j < NB; ++j)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int idx = (16 * b + 4 * grp + r) * D + 16 * j + m;
+                    dst[idx] = acc[b][j][r] + dst[idx];
+                }
+            if (m == 0)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int idx = D * D + 16 * b + 4 * grp + r;
+                    dst[idx] = acc[b][NB][r] + dst[idx];
+                }
+        }
+    }
+    __syncthreads();
+    float* oS;
+    float* oz;
+    if (P == 1) {
+        oS = stS + bh * D * D;
+        oz = stz + bh * D;
+    } else {
+        oS = part + (bh * P + p) * (int64_t)E;
+        oz = oS + D * D;
+    }
+    for (int i = tid; i < E; i += kThreads) {
+        const float x = red[i] + red[E + i];
+        if (i < D * D)
+            oS[i] = x;
+        else
+            oz[i - D * D] = x;
+    }
+    if (P > 1) combine_if_last<D>(part, cnt, stS, stz, bh, P, s_flag);
+}
+
 // ---------------------------------------------------------------------------
 // Shared shape of the streaming kernels (output, bwd Q side, bwd K/V side).
 // ---------------------------------------------------------------------------
@@ -411,13 +617,17 @@ __global__ __launch_bounds__(kThreads) void fwd_output_kernel(
     __syncthreads();
     const float uS = ldexpf(1.f, -sS), uz = ldexpf(1.f, -sz);
 
-    for (int64_t base = c0 + wave * 16 * U; base < c1; base += 16 * U * kWaves) {
-        Row<T, F> qr[U];
+    // Each wave takes blocks of 16 U tokens, kWaves blocks apart, with the
+    // loads of its next two blocks in flight while it computes one.
+    const int64_t stride = 16 * U * kWaves;
+    auto issue = [&](Row<T, F> (&b)[U], int64_t bs) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int64_t t = base + 16 * u + m;
-            load_row<T, F>(qr[u], q + (bh * T_ + t) * D + F * grp, t < c1);
+            const int64_t t = bs + 16 * u + m;
+            load_row<T, F>(b[u], q + (bh * T_ + t) * D + F * grp, t < c1);
         }
+    };
+    auto body = [&](Row<T, F> (&qr)[U], int64_t base) {
         Frag<T> bq[U][KS];
 #pragma unroll
         for (int u = 0; u < U; ++u)
@@ -426,6 +636,7 @@ __global__ __launch_bounds__(kThreads) void fwd_output_kernel(
 #pragma unroll
                 for (int e = 0; e < 8; ++e)
                     bq[u][s][e] = static_cast<T>(phi<T>(to_f32(qr[u].e[8 * s + e])));
+        issue(qr, base + 2 * stride);
         f32x4 acc[U][NB], accd[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -469,6 +680,15 @@ __global__ __launch_bounds__(kThreads) void fwd_output_kernel(
                 store_row<T, F>(o + (bh * T_ + t) * D + F * grp, out);
             }
         }
+    };
+    Row<T, F> b0[U], b1[U];
+    const int64_t first = c0 + wave * 16 * U;
+    issue(b0, first);
+    issue(b1, first + stride);
+    for (int64_t base = first; base < c1; base += 2 * stride) {
+        body(b0, base);
+        if (base + stride >= c1) break;
+        body(b1, base + stride);
     }
 }
 
@@ -687,6 +907,256 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(
     if (PB > 1) combine_if_last<D>(part, cnt, dS_out, dz_out, bh, PB, s_flag);
 }
 
+// Steps 5-6 for 16-bit inputs at D = 64, per wave: each wave walks its own
+// 16-token steps (w, w + 4, ...) with two steps of Q and dO loads in flight.
+// Per step it computes u = S dO_t, den, dQ as the workgroup kernel above,
+// then writes phi(q) and w = dO 2^sw / den row-major into its own LDS area and
+// reads them back transposed (4 tokens per lane) as the A = phi(Q)^T and
+// B = w operands of sixteen 16x16x16 MFMAs that add the step into the wave's
+// private 64 x 64 dS. Waves are combined in a fixed order at the end.
+template <typename T, bool SIMPLE>
+__global__ __launch_bounds__(kThreads, 2) void bwd_dq_w64_kernel(
+    const T* __restrict__ q, const T* __restrict__ dout, const float* __restrict__ stS,
+    const float* __restrict__ stz, T* __restrict__ dq, float* __restrict__ part,
+    float* __restrict__ dS_out, float* __restrict__ dz_out, int* __restrict__ cnt, int64_t T_, int PB,
+    int64_t LB, float eps) {
+    constexpr int D = 64, F = 16, NB = 4, KS = 2, STEP = 16, LDR = 72, E = D * D + D;
+    constexpr int NFS = NB * KS;
+    constexpr int NFR = NFS + (SIMPLE ? 0 : KS);
+    constexpr int kFragBytes = NFR * 64 * 16;
+    constexpr int kTileBytes = kWaves * 2 * STEP * LDR * (int)sizeof(T);
+    constexpr int kLoopBytes = kFragBytes + kTileBytes;
+    constexpr int kRedBytes = 2 * E * (int)sizeof(float);
+    __shared__ __attribute__((aligned(16))) unsigned char smem[kLoopBytes > kRedBytes ? kLoopBytes : kRedBytes];
+    __shared__ float red4[4];
+    __shared__ int s_flag[1];
+
+    const int wid = xcd_remap(blockIdx.x, gridDim.x);
+    const int64_t bh = wid / PB;
+    const int p = wid % PB;
+    const int64_t t0 = (int64_t)p * LB;
+    const int64_t t1 = min(t0 + LB, T_);
+    const int nsteps = (int)(t1 > t0 ? (t1 - t0 + STEP - 1) / STEP : 0);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int m = lane & 15, grp = lane >> 4;
+    const float* S = stS + bh * D * D;
+    const float* z = stz + bh * D;
+    Frag<T>* sA = reinterpret_cast<Frag<T>*>(smem);
+    T* sQ = reinterpret_cast<T*>(smem + kFragBytes) + wave * 2 * STEP * LDR;
+    T* sW = sQ + STEP * LDR;
+
+    int sS = 0, sz = 0, sw = 0;
+    if constexpr (Elt<T>::kScaled) {
+        float mx = 0.f, mz = 0.f, zs = 0.f;
+        for (int i = tid; i < D * D; i += kThreads) mx = fmaxf(mx, fabsf(S[i]));
+        for (int i = tid; i < D; i += kThreads) {
+            mz = fmaxf(mz, fabsf(z[i]));
+            zs += z[i];
+        }
+        sS = scale_exp(block_max(mx, red4));
+        sz = scale_exp(block_max(mz, red4));
+        if constexpr (!SIMPLE) {
+            const float zsum = block_sum(zs, red4);
+            if (zsum > 0.f && isfinite(zsum)) {
+                int e;
+                frexpf(zsum, &e);
+                sw = min(max(e - 1, -120), 120);  // 2^sw <= sum(z) < 2^(sw+1)
+            }
+        }
+    }
+    for (int f = wave; f < NFR; f += kWaves) {
+        Frag<T> fr;
+        if (f < NFS)
+            fr = build_frag<T, D, false>(S, f / KS, f % KS, m, grp, ldexpf(1.f, sS));
+        else
+            fr = build_zfrag<T, D>(z, f - NFS, grp, ldexpf(1.f, sz));
+        sA[f * 64 + lane] = fr;
+    }
+    float zl[F];
+#pragma unroll
+    for (int o = 0; o < F; ++o) zl[o] = SIMPLE ? 0.f : z[F * grp + o];
+    __syncthreads();
+    const float uS = ldexpf(1.f, -sS), uz = ldexpf(1.f, -sz), fw = ldexpf(1.f, sw);
+
+    f32x4 dsacc[NB][NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int j = 0; j < NB; ++j) dsacc[b][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float dzacc[F];
+#pragma unroll
+    for (int o = 0; o < F; ++o) dzacc[o] = 0.f;
+
+    struct Stage {
+        Row<T, F> q, d;
+    };
+    auto issue = [&](Stage& st, int step) {
+        const int64_t t = t0 + (int64_t)step * STEP + m;
+        const bool valid = step < nsteps && t < t1;
+        load_row<T, F>(st.q, q + (bh * T_ + t) * D + F * grp, valid);
+        load_row<T, F>(st.d, dout + (bh * T_ + t) * D + F * grp, valid);
+    };
+    const int rA = 4 * grp + (m >> 2), cA = 4 * (m & 3);
+    auto body = [&](Stage& st, int step) {
+        const int64_t t = t0 + (int64_t)step * STEP + m;
+        const bool valid = t < t1;
+        float qt[F], dof[F];
+        Frag<T> bq[KS], bd[KS];
+#pragma unroll
+        for (int o = 0; o < F; ++o) {
+            qt[o] = phi<T>(to_f32(st.q.e[o]));
+            dof[o] = to_f32(st.d.e[o]);
+        }
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                bq[s][e] = static_cast<T>(qt[8 * s + e]);
+                bd[s][e] = st.d.e[8 * s + e];
+            }
+        issue(st, step + 2 * kWaves);  // this stage's registers are free again
+        f32x4 au[NB];
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            au[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < KS; ++s) au[b] = mma(sA[(b * KS + s) * 64 + lane], bd[s], au[b]);
+        }
+        float dqt[F], wv[F];
+        if constexpr (SIMPLE) {
+#pragma unroll
+            for (int b = 0; b < NB; ++b)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) dqt[4 * b + r] = au[b][r] * uS;
+#pragma unroll
+            for (int o = 0; o < F; ++o) wv[o] = dof[o];
+        } else {
+            f32x4 ad = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < KS; ++s) ad = mma(sA[(NFS + s) * 64 + lane], bq[s], ad);
+            const float den = ad[0] * uz + eps;
+            float uu[F];
+            float rr = 0.f;
+#pragma unroll
+            for (int b = 0; b < NB; ++b)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    uu[4 * b + r] = au[b][r] * uS;
+                    rr += qt[4 * b + r] * uu[4 * b + r];
+                }
+            rr += __shfl_xor(rr, 16);
+            rr += __shfl_xor(rr, 32);
+            const float cc = -(rr / den) / den;
+            const float ws = fw / den;
+#pragma unroll
+            for (int o = 0; o < F; ++o) {
+                dqt[o] = uu[o] / den + cc * zl[o];
+                wv[o] = dof[o] * ws;
+                if (valid) dzacc[o] += cc * qt[o];
+            }
+        }
+        if (valid) {
+            float out[F];
+#pragma unroll
+            for (int o = 0; o < F; ++o) out[o] = dqt[o] * fminf(qt[o], 1.f);  // phi' = min(phi, 1)
+            store_row<T, F>(dq + (bh * T_ + t) * D + F * grp, out);
+        }
+        Row<T, F> rq, rw;
+#pragma unroll
+        for (int o = 0; o < F; ++o) {
+            rq.e[o] = valid ? static_cast<T>(qt[o]) : static_cast<T>(0.f);
+            rw.e[o] = valid ? static_cast<T>(wv[o]) : static_cast<T>(0.f);
+        }
+        uint4* dq4 = reinterpret_cast<uint4*>(&sQ[m * LDR + F * grp]);
+        uint4* dw4 = reinterpret_cast<uint4*>(&sW[m * LDR + F * grp]);
+        dq4[0] = reinterpret_cast<const uint4*>(rq.e)[0];
+        dq4[1] = reinterpret_cast<const uint4*>(rq.e)[1];
+        dw4[0] = reinterpret_cast<const uint4*>(rw.e)[0];
+        dw4[1] = reinterpret_cast<const uint4*>(rw.e)[1];
+        wave_lds_sync();
+        i16x4 a[NB];
+#pragma unroll
+        for (int b = 0; b < NB; ++b) a[b] = lds_read_tr(&sQ[rA * LDR + 16 * b + cA]);
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+            const i16x4 bw = lds_read_tr(&sW[rA * LDR + 16 * j + cA]);
+#pragma unroll
+            for (int b = 0; b < NB; ++b) dsacc[b][j] = mma_k16<T>(a[b], bw, dsacc[b][j]);
+        }
+        wave_lds_sync();
+    };
+
+    Stage s0, s1;
+    issue(s0, wave);
+    issue(s1, wave + kWaves);
+    for (int st = wave; st < nsteps; st += 2 * kWaves) {
+        body(s0, st);
+        if (st + kWaves >= nsteps) break;
+        body(s1, st + kWaves);
+    }
+
+    // dz: sum over the 16 token lanes of each lane group (fixed butterfly)
+#pragma unroll
+    for (int o = 0; o < F; ++o) {
+        float x = dzacc[o];
+        x += __shfl_xor(x, 1);
+        x += __shfl_xor(x, 2);
+        x += __shfl_xor(x, 4);
+        x += __shfl_xor(x, 8);
+        dzacc[o] = x;
+    }
+    // fixed-order sum of the four waves: (w0 + w2) + (w1 + w3)
+    __syncthreads();
+    float* red = reinterpret_cast<float*>(smem);
+    const float uw = ldexpf(1.f, -sw);
+    if (wave >= 2) {
+        float* dst = red + (wave - 2) * E;
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+            for (int j = 0; j < NB; ++j)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) dst[(16 * b + 4 * grp + r) * D + 16 * j + m] = dsacc[b][j][r] * uw;
+        if (m == 0)
+#pragma unroll
+            for (int o = 0; o < F; ++o) dst[D * D + F * grp + o] = dzacc[o];
+    }
+    __syncthreads();
+    if (wave < 2) {
+        float* dst = red + wave * E;
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+            for (int j = 0; j < NB; ++j)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int idx = (16 * b + 4 * grp + r) * D + 16 * j + m;
+                    dst[idx] = dsacc[b][j][r] * uw + dst[idx];
+                }
+        if (m == 0)
+#pragma unroll
+            for (int o = 0; o < F; ++o) dst[D * D + F * grp + o] = dzacc[o] + dst[D * D + F * grp + o];
+    }
+    __syncthreads();
+    float* oS;
+    float* oz;
+    if (PB == 1) {
+        oS = dS_out + bh * D * D;
+        oz = dz_out + bh * D;
+    } else {
+        oS = part + (bh * PB + p) * (int64_t)E;
+        oz = oS + D * D;
+    }
+    for (int i = tid; i < E; i += kThreads) {
+        const float x = red[i] + red[E + i];
+        if (i < D * D)
+            oS[i] = x;
+        else
+            oz[i - D * D] = x;
+    }
+    if (PB > 1) combine_if_last<D>(part, cnt, dS_out, dz_out, bh, PB, s_flag);
+}
+
 // ---------------------------------------------------------------------------
 // Step 7: backward, K/V side.
 // ---------------------------------------------------------------------------
@@ -699,7 +1169,8 @@ __global__ __launch_bounds__(kThreads) void bwd_dkv_kernel(
     const float* __restrict__ dzg, T* __restrict__ dk, T* __restrict__ dv, int64_t T_, int NK,
     int64_t LK) {
     using Sh = StreamShape<T, D>;
-    constexpr int F = Sh::kF, NB = Sh::kNB, KS = Sh::kKS, U = Sh::kU;
+    constexpr int F = Sh::kF, NB = Sh::kNB, KS = Sh::kKS;
+    constexpr int U = 1;  // one 16-token block per wave step; the prefetch gives the depth
     constexpr int NFS = NB * KS;
     __shared__ Frag<T> sA[2 * NFS * 64];
     __shared__ float red[4];
@@ -734,28 +1205,38 @@ __global__ __launch_bounds__(kThreads) void bwd_dkv_kernel(
     for (int o = 0; o < F; ++o) dzl[o] = SIMPLE ? 0.f : dz[F * grp + o];
     __syncthreads();
 
-    for (int64_t base = c0 + wave * 16 * U; base < c1; base += 16 * U * kWaves) {
-        Row<T, F> kr[U], vr[U];
+    const int64_t stride = 16 * U * kWaves;
+    struct Stage {
+        Row<T, F> k[U], v[U];
+    };
+    auto issue = [&](Stage& st, int64_t bs) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int64_t t = base + 16 * u + m;
-            load_row<T, F>(kr[u], k + (bh * T_ + t) * D + F * grp, t < c1);
-            load_row<T, F>(vr[u], v + (bh * T_ + t) * D + F * grp, t < c1);
+            const int64_t t = bs + 16 * u + m;
+            load_row<T, F>(st.k[u], k + (bh * T_ + t) * D + F * grp, t < c1);
+            load_row<T, F>(st.v[u], v + (bh * T_ + t) * D + F * grp, t < c1);
         }
-        float kt[U][F];
+    };
+    auto body = [&](Stage& st, int64_t base) {
+        float dphik[U][F];
         Frag<T> bk[U][KS], bv[U][KS];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
+            float kt[F];
 #pragma unroll
-            for (int o = 0; o < F; ++o) kt[u][o] = phi<T>(to_f32(kr[u].e[o]));
+            for (int o = 0; o < F; ++o) {
+                kt[o] = phi<T>(to_f32(st.k[u].e[o]));
+                dphik[u][o] = fminf(kt[o], 1.f);  // phi' = min(phi, 1)
+            }
 #pragma unroll
             for (int s = 0; s < KS; ++s)
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    bk[u][s][e] = static_cast<T>(kt[u][8 * s + e]);
-                    bv[u][s][e] = vr[u].e[8 * s + e];
+                    bk[u][s][e] = static_cast<T>(kt[8 * s + e]);
+                    bv[u][s][e] = st.v[u].e[8 * s + e];
                 }
         }
+        issue(st, base + 2 * stride);
         f32x4 ak[U][NB], av[U][NB];
 #pragma unroll
         for (int u = 0; u < U; ++u)
@@ -786,13 +1267,22 @@ __global__ __launch_bounds__(kThreads) void bwd_dkv_kernel(
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         const int o = 4 * b + r;
-                        gk[o] = (ak[u][b][r] * uD + dzl[o]) * fminf(kt[u][o], 1.f);
+                        gk[o] = (ak[u][b][r] * uD + dzl[o]) * dphik[u][o];
                         gv[o] = av[u][b][r] * uD;
                     }
                 store_row<T, F>(dk + (bh * T_ + t) * D + F * grp, gk);
                 store_row<T, F>(dv + (bh * T_ + t) * D + F * grp, gv);
             }
         }
+    };
+    Stage s0, s1;
+    const int64_t first = c0 + wave * 16 * U;
+    issue(s0, first);
+    issue(s1, first + stride);
+    for (int64_t base = first; base < c1; base += 2 * stride) {
+        body(s0, base);
+        if (base + stride >= c1) break;
+        body(s1, base + stride);
     }
 }
 
@@ -800,14 +1290,23 @@ __global__ __launch_bounds__(kThreads) void bwd_dkv_kernel(
 // Host-side dispatch.
 // ---------------------------------------------------------------------------
 template <typename T, int D>
+constexpr bool kWaveKernels = (sizeof(T) == 2 && D == 64);
+
+template <typename T, int D>
 hipError_t fwd_state_t(const Plan& p, const void* k, const void* v, float* state, void* ws,
                        hipStream_t s) {
     const int64_t nblk = p.BH * p.P;
     char* w = static_cast<char*>(ws);
-    hipLaunchKernelGGL((fwd_state_kernel<T, D>), dim3((unsigned)nblk), dim3(kThreads), 0, s,
-                       static_cast<const T*>(k), static_cast<const T*>(v), state,
-                       state + p.BH * D * D, reinterpret_cast<float*>(w + p.off_part),
-                       reinterpret_cast<int*>(w + p.off_cnt_fwd), p.T, p.P, p.L);
+    float* part = reinterpret_cast<float*>(w + p.off_part);
+    int* cnt = reinterpret_cast<int*>(w + p.off_cnt_fwd);
+    if constexpr (kWaveKernels<T, D>)
+        hipLaunchKernelGGL((fwd_state_w64_kernel<T>), dim3((unsigned)nblk), dim3(kThreads), 0, s,
+                           static_cast<const T*>(k), static_cast<const T*>(v), state,
+                           state + p.BH * D * D, part, cnt, p.T, p.P, p.L);
+    else
+        hipLaunchKernelGGL((fwd_state_kernel<T, D>), dim3((unsigned)nblk), dim3(kThreads), 0, s,
+                           static_cast<const T*>(k), static_cast<const T*>(v), state,
+                           state + p.BH * D * D, part, cnt, p.T, p.P, p.L);
     return hipGetLastError();
 }
 
@@ -833,16 +1332,28 @@ hipError_t bwd_dq_t(const Plan& p, const void* q, const void* dout, const float*
     float* part = reinterpret_cast<float*>(w + p.off_part);
     float* dst = reinterpret_cast<float*>(w + p.off_dstate);
     int* cnt = reinterpret_cast<int*>(w + p.off_cnt_bwd);
-    if (p.simple)
-        hipLaunchKernelGGL((bwd_dq_kernel<T, D, true>), dim3((unsigned)nblk), dim3(kThreads), 0, s,
-                           static_cast<const T*>(q), static_cast<const T*>(dout), state,
-                           state + p.BH * D * D, static_cast<T*>(dq), part, dst, dst + p.BH * D * D,
-                           cnt, p.T, p.PB, p.LB, p.eps);
-    else
-        hipLaunchKernelGGL((bwd_dq_kernel<T, D, false>), dim3((unsigned)nblk), dim3(kThreads), 0, s,
-                           static_cast<const T*>(q), static_cast<const T*>(dout), state,
-                           state + p.BH * D * D, static_cast<T*>(dq), part, dst, dst + p.BH * D * D,
-                           cnt, p.T, p.PB, p.LB, p.eps);
+    const T* qq = static_cast<const T*>(q);
+    const T* dd = static_cast<const T*>(dout);
+    const float* sS = state;
+    const float* sz = state + p.BH * D * D;
+    T* g = static_cast<T*>(dq);
+    float* dS = dst;
+    float* dz = dst + p.BH * D * D;
+    if constexpr (kWaveKernels<T, D>) {
+        if (p.simple)
+            hipLaunchKernelGGL((bwd_dq_w64_kernel<T, true>), dim3((unsigned)nblk), dim3(kThreads), 0, s,
+                               qq, dd, sS, sz, g, part, dS, dz, cnt, p.T, p.PB, p.LB, p.eps);
+        else
+            hipLaunchKernelGGL((bwd_dq_w64_kernel<T, false>), dim3((unsigned)nblk), dim3(kThreads), 0, s,
+                               qq, dd, sS, sz, g, part, dS, dz, cnt, p.T, p.PB, p.LB, p.eps);
+    } else {
+        if (p.simple)
+            hipLaunchKernelGGL((bwd_dq_kernel<T, D, true>), dim3((unsigned)nblk), dim3(kThreads), 0, s,
+                               qq, dd, sS, sz, g, part, dS, dz, cnt, p.T, p.PB, p.LB, p.eps);
+        else
+            hipLaunchKernelGGL((bwd_dq_kernel<T, D, false>), dim3((unsigned)nblk), dim3(kThreads), 0, s,
+                               qq, dd, sS, sz, g, part, dS, dz, cnt, p.T, p.PB, p.LB, p.eps);
+    }
     return hipGetLastError();
 }
 
@@ -875,23 +1386,30 @@ hipError_t bwd_dkv_t(const Plan& p, const void* k, const void* v, void* dk, void
     }
 
 template <typename T, int D>
-constexpr int64_t state_tile() { return StateShape<T, D>::kTT; }
+SplitCfg split_config_t(int step) {
+    switch (step) {
+        case kStepState:
+            if constexpr (kWaveKernels<T, D>) return {int64_t(StateW64::kStep) * kWaves, 512};
+            else return {StateShape<T, D>::kTT, 1024};
+        case kStepBwdQ:
+            if constexpr (kWaveKernels<T, D>) return {int64_t(16) * kWaves, 512};
+            else return {BwdQShape<T, D>::kG, 1024};
+        default:
+            return {StreamShape<T, D>::kG, 1024};
+    }
+}
 
 }  // namespace
 
-int64_t state_tile_tokens(int dtype, int D) {
-    if (dtype == 0) return D == 128 ? state_tile<float, 128>() : state_tile<float, 64>();
-    return D == 128 ? state_tile<f16, 128>() : state_tile<f16, 64>();
-}
-
-int64_t bwdq_group_tokens(int dtype, int D) {
-    if (dtype == 0) return D == 128 ? BwdQShape<float, 128>::kG : BwdQShape<float, 64>::kG;
-    return D == 128 ? BwdQShape<f16, 128>::kG : BwdQShape<f16, 64>::kG;
-}
-
-int64_t stream_group_tokens(int dtype, int D) {
-    if (dtype == 0) return D == 128 ? StreamShape<float, 128>::kG : StreamShape<float, 64>::kG;
-    return D == 128 ? StreamShape<f16, 128>::kG : StreamShape<f16, 64>::kG;
+SplitCfg split_config(int step, int dtype, int D) {
+    switch (dtype * 2 + (D == 128 ? 1 : 0)) {
+        case 0: return split_config_t<float, 64>(step);
+        case 1: return split_config_t<float, 128>(step);
+        case 2: return split_config_t<f16, 64>(step);
+        case 3: return split_config_t<f16, 128>(step);
+        case 4: return split_config_t<bf16, 64>(step);
+        default: return split_config_t<bf16, 128>(step);
+    }
 }
 
 hipError_t launch_fwd_state(const Plan& p, const void* k, const void* v, float* state, void* ws,
