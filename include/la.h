@@ -23,12 +23,12 @@
  * Work is enqueued on `stream` (a hipStream_t; NULL is the null stream) and
  * the call returns without waiting.
  *
- * Workspace. `ws` must be at least la_workspace_bytes() bytes, 256-byte
- * aligned, and ALL ZERO before its first use. The kernels leave it zeroed
- * where it matters (per-head arrival counters are reset by the workgroup that
- * finishes each head), so one zero-filled workspace can be reused by any
- * number of calls in stream order. Calls that overlap in time (different
- * streams, no ordering) must use different workspaces.
+ * Workspace. `ws` must be at least la_workspace_bytes() bytes and 256-byte
+ * aligned; its contents need no initialisation. It carries the partial sums
+ * of the split-T reductions, the backward state (dS, dz) from la_bwd_dq to
+ * la_bwd_dkv, and the forward state when la_fwd is given state == NULL.
+ * Calls that overlap in time (different streams, no ordering) must use
+ * different workspaces.
  *
  * Errors. Every argument is checked before any HIP call, so a call that
  * returns a validation error has enqueued nothing. LA_ERR_DEVICE reports a

@@ -3,7 +3,7 @@
 Argument marshalling only. Every step of the computation runs in the HIP
 kernels behind the C ABI declared in include/la.h; this module turns torch
 tensors into device pointers, passes torch's current HIP stream, allocates
-outputs and a zero-filled workspace, and turns status codes into exceptions.
+outputs and a workspace, and turns status codes into exceptions.
 There is no fallback: if libla.so is missing or a call fails, it raises.
 
 torch is imported before the library is loaded so that libla.so binds to the
@@ -135,17 +135,16 @@ _ws_cache: dict = {}
 
 
 def workspace(prob: Problem, device) -> torch.Tensor:
-    """A zero-filled workspace for this device and its current stream, reused across calls.
+    """A workspace for this device and its current stream, reused across calls.
 
-    The kernels leave the workspace's counters at zero, so reuse in stream order is
-    valid; a different stream gets its own workspace.
+    Reuse in stream order is valid; a different stream gets its own workspace.
     """
     device = torch.device(device)
     key = (device, torch.cuda.current_stream(device).cuda_stream)
     need = max(workspace_bytes(prob), 256)
     ws = _ws_cache.get(key)
     if ws is None or ws.numel() < need:
-        ws = torch.zeros(need, dtype=torch.uint8, device=device)
+        ws = torch.empty(need, dtype=torch.uint8, device=device)
         _ws_cache[key] = ws
     return ws
 

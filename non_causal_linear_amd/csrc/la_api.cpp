@@ -70,14 +70,11 @@ la::Plan make_plan(const la_problem* p) {
     split(pl.BH, pl.T, la::split_config(la::kStepOutput, pl.dtype, pl.D), pl.NQ, pl.LQ);
     split(pl.BH, pl.T, la::split_config(la::kStepBwdKV, pl.dtype, pl.D), pl.NK, pl.LK);
     const size_t E = size_t(pl.D) * pl.D + pl.D;  // floats per (S, z) block
-    const size_t cnt = align256(size_t(pl.BH) * sizeof(int));
     const int maxp = std::max(pl.P, pl.PB);
     const size_t part = maxp > 1 ? align256(size_t(pl.BH) * maxp * E * 4) : 0;
     const size_t st = align256(size_t(pl.BH) * E * 4);
-    pl.off_cnt_fwd = 0;
-    pl.off_cnt_bwd = cnt;
-    pl.off_part = 2 * cnt;
-    pl.off_dstate = pl.off_part + part;
+    pl.off_part = 0;
+    pl.off_dstate = part;
     pl.off_fstate = pl.off_dstate + st;
     pl.ws_bytes = pl.off_fstate + st;
     return pl;

@@ -28,7 +28,7 @@ struct Plan {
     int NK = 1;
     int64_t LK = 0;
     // workspace carving (byte offsets)
-    size_t off_cnt_fwd = 0, off_cnt_bwd = 0, off_part = 0, off_dstate = 0, off_fstate = 0;
+    size_t off_part = 0, off_dstate = 0, off_fstate = 0;
     size_t ws_bytes = 0;
 };
 

@@ -90,6 +90,12 @@ template <> __device__ __forceinline__ f32x4 mma_k16<bf16>(i16x4 a, i16x4 b, f32
     return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
 }
 
+// Keeps the compiler from moving instructions across this point. Used between
+// the load batches of a prefetch pipeline: the vector-memory counter retires
+// loads in issue order, so batches must stay in the order they are consumed
+// or the wait for the older batch would also drain the newer one.
+__device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
+
 // Orders this wave's LDS writes before its following LDS reads.
 __device__ __forceinline__ void wave_lds_sync() {
     __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
@@ -108,14 +114,18 @@ __device__ __forceinline__ f32x4 mma(f32x8 a, f32x8 b, f32x4 c) {
 }
 
 // phi(x) = elu(x) + 1, evaluated piecewise in fp32 (never as expm1(x) + 1,
-// which cancels for x << 0). fp32 inputs use the accurate expf.
+// which cancels for x << 0). Both sides are computed and one is selected, so
+// no branch splits the wave (NaN falls to the exp side and propagates). 16-bit
+// inputs use the hardware exp2 on x log2(e); fp32 inputs use the accurate expf.
 template <typename T>
 __device__ __forceinline__ float phi(float x) {
+    float e;
     if constexpr (std::is_same<T, float>::value) {
-        return x > 0.f ? x + 1.f : expf(x);
+        e = expf(x);
     } else {
-        return x > 0.f ? x + 1.f : __expf(x);
+        e = __builtin_amdgcn_exp2f(x * 1.4426950408889634f);
     }
+    return x > 0.f ? x + 1.f : e;
 }
 
 template <typename T>
@@ -134,17 +144,29 @@ struct alignas(16) Row {
     T e[N];
 };
 
+// Loads are unconditional: callers clamp the row index into the valid range
+// and discard or zero what belongs to rows past the end. (Loads under a branch
+// make the compiler drain every outstanding load at the join, which would
+// serialise the prefetch pipelines.)
 template <typename T, int N>
-__device__ __forceinline__ void load_row(Row<T, N>& r, const T* __restrict__ p, bool valid) {
+__device__ __forceinline__ void load_row(Row<T, N>& r, const T* __restrict__ p) {
     constexpr int NV = N * (int)sizeof(T) / 16;
     uint4* d = reinterpret_cast<uint4*>(r.e);
     const uint4* s = reinterpret_cast<const uint4*>(p);
-    if (valid) {
 #pragma unroll
-        for (int i = 0; i < NV; ++i) d[i] = s[i];
-    } else {
+    for (int i = 0; i < NV; ++i) d[i] = s[i];
+}
+
+template <typename T, int N>
+__device__ __forceinline__ void zero_row_unless(Row<T, N>& r, bool keep) {
+    constexpr int NV = N * (int)sizeof(T) / 16;
+    uint4* d = reinterpret_cast<uint4*>(r.e);
 #pragma unroll
-        for (int i = 0; i < NV; ++i) d[i] = make_uint4(0u, 0u, 0u, 0u);
+    for (int i = 0; i < NV; ++i) {
+        d[i].x = keep ? d[i].x : 0u;
+        d[i].y = keep ? d[i].y : 0u;
+        d[i].z = keep ? d[i].z : 0u;
+        d[i].w = keep ? d[i].w : 0u;
     }
 }
 
@@ -190,31 +212,66 @@ __device__ __forceinline__ int scale_exp(float maxabs) {
     return min(max(15 - e, -120), 120);
 }
 
-// Fixed-order sum of the P partial (S, z) blocks of head bh, run by the last
-// workgroup of that head to arrive. Returns true in that workgroup.
+// Fixed-order sum of the P partial (S, z) blocks of every head: one thread per
+// 4 consecutive floats of a head's D*D + D block, slices added in ascending
+// order, eight 16-byte loads in flight per batch. A kernel of its own: the
+// launch boundary makes every partial visible, which costs far less here than
+// device-scope fences inside the producing kernel (each of those writes back
+// and invalidates the XCD's L2).
 template <int D>
-__device__ __forceinline__ bool combine_if_last(const float* __restrict__ part, int* __restrict__ cnt,
-                                                float* __restrict__ outS, float* __restrict__ outz,
-                                                int64_t bh, int P, int* s_flag) {
-    constexpr int E = D * D + D;
-    __threadfence();  // publish this workgroup's partial before counting it
-    __syncthreads();
-    if (threadIdx.x == 0) s_flag[0] = (atomicAdd(cnt + bh, 1) == P - 1) ? 1 : 0;
-    __syncthreads();
-    if (!s_flag[0]) return false;
-    __threadfence();  // see every other workgroup's partial
-    const float* pb = part + bh * (int64_t)P * E;
-    for (int idx = threadIdx.x; idx < E; idx += kThreads) {
-        float s = 0.f;
-        for (int p = 0; p < P; ++p)
-            s += __hip_atomic_load(pb + (int64_t)p * E + idx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (idx < D * D)
-            outS[bh * D * D + idx] = s;
-        else
-            outz[bh * D + (idx - D * D)] = s;
+__global__ __launch_bounds__(kThreads) void combine_kernel(const float* __restrict__ part, int P,
+                                                           float* __restrict__ outS,
+                                                           float* __restrict__ outz, int64_t BH) {
+    constexpr int E4 = (D * D + D) / 4;
+    constexpr int BPH = (E4 + kThreads - 1) / kThreads;  // blocks per head
+    const int64_t bh = blockIdx.x / BPH;
+    const int i = (blockIdx.x % BPH) * kThreads + threadIdx.x;
+    if (bh >= BH || i >= E4) return;
+    const float4* pb = reinterpret_cast<const float4*>(part) + bh * (int64_t)P * E4 + i;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int p0 = 0; p0 < P; p0 += 8) {
+        float4 x[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) x[j] = pb[(int64_t)min(p0 + j, P - 1) * E4];
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            if (p0 + j < P) {
+                acc.x += x[j].x;
+                acc.y += x[j].y;
+                acc.z += x[j].z;
+                acc.w += x[j].w;
+            }
     }
-    if (threadIdx.x == 0) __hip_atomic_store(cnt + bh, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    return true;
+    const int idx = 4 * i;
+    if (idx < D * D)
+        *reinterpret_cast<float4*>(outS + bh * D * D + idx) = acc;
+    else
+        *reinterpret_cast<float4*>(outz + bh * D + (idx - D * D)) = acc;
+}
+
+// Largest |x| over the D x D matrix at M, block-wide: every thread issues its
+// 16-byte loads at once (D*D/4 is a multiple of the block size).
+template <int D>
+__device__ __forceinline__ float block_absmax_matrix(const float* __restrict__ M, float* red) {
+    constexpr int PER = D * D / 4 / kThreads;
+    float4 v[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) v[i] = reinterpret_cast<const float4*>(M)[threadIdx.x + i * kThreads];
+    float mx = 0.f;
+#pragma unroll
+    for (int i = 0; i < PER; ++i)
+        mx = fmaxf(mx, fmaxf(fmaxf(fabsf(v[i].x), fabsf(v[i].y)), fmaxf(fabsf(v[i].z), fabsf(v[i].w))));
+    return block_max(mx, red);
+}
+
+// max |z_i| and sum z_i over the D-vector z, block-wide, in a fixed order.
+template <int D>
+__device__ __forceinline__ void block_vector_stats(const float* __restrict__ z, float* red, float& mx,
+                                                   float& sum) {
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (threadIdx.x < D / 4) v = reinterpret_cast<const float4*>(z)[threadIdx.x];
+    mx = block_max(fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))), red);
+    sum = block_sum((v.x + v.y) + (v.z + v.w), red);
 }
 
 // ---------------------------------------------------------------------------
@@ -245,7 +302,7 @@ struct StateShape {
 template <typename T, int D>
 __global__ __launch_bounds__(kThreads) void fwd_state_kernel(
     const T* __restrict__ k, const T* __restrict__ v, float* __restrict__ stS,
-    float* __restrict__ stz, float* __restrict__ part, int* __restrict__ cnt, int64_t T_, int P,
+    float* __restrict__ stz, float* __restrict__ part, int64_t T_, int P,
     int64_t L) {
     using Sh = StateShape<T, D>;
     constexpr int EPC = Sh::kEPC, CPR = Sh::kCPR, NG = Sh::kNG, R = Sh::kR, TT = Sh::kTT,
@@ -253,7 +310,6 @@ __global__ __launch_bounds__(kThreads) void fwd_state_kernel(
     typedef T tR __attribute__((ext_vector_type(R)));
     __shared__ __attribute__((aligned(16))) T sK[D * LDT];
     __shared__ __attribute__((aligned(16))) T sV[D * LDT];
-    __shared__ int s_flag[1];
 
     const int wid = xcd_remap(blockIdx.x, gridDim.x);
     const int64_t bh = wid / P;
@@ -279,14 +335,9 @@ __global__ __launch_bounds__(kThreads) void fwd_state_kernel(
     auto load_tile = [&](int64_t ts) {
 #pragma unroll
         for (int rr = 0; rr < R; ++rr) {
-            const int64_t t = ts + g + NG * rr;
-            if (t < t1) {
-                rk[rr] = *reinterpret_cast<const uint4*>(kb + t * D);
-                rv[rr] = *reinterpret_cast<const uint4*>(vb + t * D);
-            } else {
-                rk[rr] = make_uint4(0u, 0u, 0u, 0u);
-                rv[rr] = make_uint4(0u, 0u, 0u, 0u);
-            }
+            const int64_t t = min(ts + g + NG * rr, t1 - 1);  // masked when written to LDS
+            rk[rr] = *reinterpret_cast<const uint4*>(kb + t * D);
+            rv[rr] = *reinterpret_cast<const uint4*>(vb + t * D);
         }
     };
 
@@ -306,7 +357,7 @@ __global__ __launch_bounds__(kThreads) void fwd_state_kernel(
                 for (int e = 0; e < EPC; ++e) {
                     // padded rows must add nothing: phi(0) = 1, so mask after phi
                     kt[e][rr] = ok ? static_cast<T>(phi<T>(to_f32(ke[e]))) : static_cast<T>(0.f);
-                    vt[e][rr] = ve[e];
+                    vt[e][rr] = ok ? ve[e] : static_cast<T>(0.f);
                 }
             }
 #pragma unroll
@@ -355,7 +406,6 @@ __global__ __launch_bounds__(kThreads) void fwd_state_kernel(
 #pragma unroll
             for (int r = 0; r < 4; ++r) oz[i0 + r] = acc[ii][NB][r];
     }
-    if (P > 1) combine_if_last<D>(part, cnt, stS, stz, bh, P, s_flag);
 }
 
 // Steps 1-3 for 16-bit inputs at D = 64: every wave streams its own 32-token
@@ -376,14 +426,13 @@ struct StateW64 {
 template <typename T>
 __global__ __launch_bounds__(kThreads, 2) void fwd_state_w64_kernel(
     const T* __restrict__ k, const T* __restrict__ v, float* __restrict__ stS,
-    float* __restrict__ stz, float* __restrict__ part, int* __restrict__ cnt, int64_t T_, int P,
+    float* __restrict__ stz, float* __restrict__ part, int64_t T_, int P,
     int64_t L) {
     constexpr int D = 64, NB = 4, E = D * D + D;
     constexpr int STEP = StateW64::kStep, LDR = StateW64::kLDR, TILE = StateW64::kTile;
     constexpr int kTileBytes = kWaves * 2 * TILE * (int)sizeof(T);
     constexpr int kRedBytes = 2 * E * (int)sizeof(float);
     __shared__ __attribute__((aligned(16))) unsigned char smem[kTileBytes > kRedBytes ? kTileBytes : kRedBytes];
-    __shared__ int s_flag[1];
 
     const int wid = xcd_remap(blockIdx.x, gridDim.x);
     const int64_t bh = wid / P;
@@ -414,14 +463,9 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_state_w64_kernel(
     auto issue = [&](Stage& st, int step) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int64_t t = t0 + (int64_t)step * STEP + rg + 8 * r;
-            if (step < nsteps && t < t1) {
-                st.k[r] = *reinterpret_cast<const uint4*>(kb + t * D);
-                st.v[r] = *reinterpret_cast<const uint4*>(vb + t * D);
-            } else {
-                st.k[r] = make_uint4(0u, 0u, 0u, 0u);
-                st.v[r] = make_uint4(0u, 0u, 0u, 0u);
-            }
+            const int64_t t = min(t0 + (int64_t)step * STEP + rg + 8 * r, t1 - 1);  // masked in consume
+            st.k[r] = *reinterpret_cast<const uint4*>(kb + t * D);
+            st.v[r] = *reinterpret_cast<const uint4*>(vb + t * D);
         }
     };
     // phi on K (fp32, rounded to T), padded rows zeroed after phi, row-major to LDS
@@ -435,8 +479,13 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_state_w64_kernel(
 #pragma unroll
             for (int e = 0; e < 8; ++e)
                 kt.e[e] = ok ? static_cast<T>(phi<T>(to_f32(ke[e]))) : static_cast<T>(0.f);
+            uint4 vv = st.v[r];
+            vv.x = ok ? vv.x : 0u;
+            vv.y = ok ? vv.y : 0u;
+            vv.z = ok ? vv.z : 0u;
+            vv.w = ok ? vv.w : 0u;
             *reinterpret_cast<uint4*>(&sK[row * LDR + 8 * c]) = *reinterpret_cast<const uint4*>(kt.e);
-            *reinterpret_cast<uint4*>(&sV[row * LDR + 8 * c]) = st.v[r];
+            *reinterpret_cast<uint4*>(&sV[row * LDR + 8 * c]) = vv;
         }
     };
     const int rA = 8 * grp + (m >> 2), cA = 4 * (m & 3);
@@ -459,17 +508,25 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_state_w64_kernel(
         wave_lds_sync();
     };
 
-    Stage s0, s1;
-    issue(s0, wave);
-    issue(s1, wave + kWaves);
-    for (int st = wave; st < nsteps; st += 2 * kWaves) {
-        consume(s0, st);
-        issue(s0, st + 2 * kWaves);
-        mma_step();
-        if (st + kWaves >= nsteps) break;
-        consume(s1, st + kWaves);
-        issue(s1, st + 3 * kWaves);
-        mma_step();
+    if (nsteps > 0) {
+        Stage s0, s1;
+        issue(s0, wave);
+        sched_fence();
+        issue(s1, wave + kWaves);
+        sched_fence();
+        for (int st = wave; st < nsteps; st += 2 * kWaves) {
+            consume(s0, st);
+            sched_fence();
+            issue(s0, st + 2 * kWaves);
+            sched_fence();
+            mma_step();
+            if (st + kWaves >= nsteps) break;
+            consume(s1, st + kWaves);
+            sched_fence();
+            issue(s1, st + 3 * kWaves);
+            sched_fence();
+            mma_step();
+        }
     }
 
     // fixed-order sum of the four waves: (w0 + w2) + (w1 + w3)
@@ -525,7 +582,6 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_state_w64_kernel(
         else
             oz[i - D * D] = x;
     }
-    if (P > 1) combine_if_last<D>(part, cnt, stS, stz, bh, P, s_flag);
 }
 
 // ---------------------------------------------------------------------------
@@ -569,6 +625,21 @@ __device__ __forceinline__ Frag<T> build_zfrag(const float* __restrict__ z, int 
     return f;
 }
 
+// Writes the workgroup's operand fragments to sA[f * 64 + lane], f < NF; wave w
+// builds fragments w, w + 4, ... with all their loads issued together. make(f)
+// returns fragment f (f is clamped, so its loads are unconditional).
+template <typename T, int NF, typename Make>
+__device__ __forceinline__ void build_frags(Frag<T>* sA, Make make) {
+    constexpr int PER = (NF + kWaves - 1) / kWaves;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    Frag<T> fr[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) fr[i] = make(min(wave + kWaves * i, NF - 1));
+#pragma unroll
+    for (int i = 0; i < PER; ++i)
+        if (wave + kWaves * i < NF) sA[(wave + kWaves * i) * 64 + lane] = fr[i];
+}
+
 // ---------------------------------------------------------------------------
 // Step 4: output.
 // ---------------------------------------------------------------------------
@@ -600,19 +671,17 @@ __global__ __launch_bounds__(kThreads) void fwd_output_kernel(
 
     int sS = 0, sz = 0;
     if constexpr (Elt<T>::kScaled) {
-        float mx = 0.f, mz = 0.f;
-        for (int i = tid; i < D * D; i += kThreads) mx = fmaxf(mx, fabsf(S[i]));
-        for (int i = tid; i < D; i += kThreads) mz = fmaxf(mz, fabsf(z[i]));
-        sS = scale_exp(block_max(mx, red));
-        sz = scale_exp(block_max(mz, red));
+        float mz, zsum;
+        sS = scale_exp(block_absmax_matrix<D>(S, red));
+        block_vector_stats<D>(z, red, mz, zsum);
+        sz = scale_exp(mz);
     }
-    for (int f = wave; f < NFR; f += kWaves) {
-        Frag<T> fr;
-        if (f < NFS)
-            fr = build_frag<T, D, true>(S, f / KS, f % KS, m, grp, ldexpf(1.f, sS));
-        else
-            fr = build_zfrag<T, D>(z, f - NFS, grp, ldexpf(1.f, sz));
-        sA[f * 64 + lane] = fr;
+    {
+        const float fS = ldexpf(1.f, sS), fz = ldexpf(1.f, sz);
+        build_frags<T, NFR>(sA, [&](int f) {
+            return f < NFS ? build_frag<T, D, true>(S, f / KS, f % KS, m, grp, fS)
+                           : build_zfrag<T, D>(z, max(f - NFS, 0), grp, fz);
+        });
     }
     __syncthreads();
     const float uS = ldexpf(1.f, -sS), uz = ldexpf(1.f, -sz);
@@ -623,8 +692,8 @@ __global__ __launch_bounds__(kThreads) void fwd_output_kernel(
     auto issue = [&](Row<T, F> (&b)[U], int64_t bs) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int64_t t = bs + 16 * u + m;
-            load_row<T, F>(b[u], q + (bh * T_ + t) * D + F * grp, t < c1);
+            const int64_t t = min(bs + 16 * u + m, c1 - 1);  // rows past c1 are computed, not stored
+            load_row<T, F>(b[u], q + (bh * T_ + t) * D + F * grp);
         }
     };
     auto body = [&](Row<T, F> (&qr)[U], int64_t base) {
@@ -636,7 +705,9 @@ __global__ __launch_bounds__(kThreads) void fwd_output_kernel(
 #pragma unroll
                 for (int e = 0; e < 8; ++e)
                     bq[u][s][e] = static_cast<T>(phi<T>(to_f32(qr[u].e[8 * s + e])));
+        sched_fence();
         issue(qr, base + 2 * stride);
+        sched_fence();
         f32x4 acc[U][NB], accd[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -671,11 +742,12 @@ __global__ __launch_bounds__(kThreads) void fwd_output_kernel(
 #pragma unroll
                         for (int r = 0; r < 4; ++r) out[4 * b + r] = acc[u][b][r] * uS;
                 } else {
-                    const float den = accd[u][0] * uz + eps;
+                    // one division per token: O = num 2^-sS / (den 2^-sz + eps)
+                    const float inv = uS / (accd[u][0] * uz + eps);
 #pragma unroll
                     for (int b = 0; b < NB; ++b)
 #pragma unroll
-                        for (int r = 0; r < 4; ++r) out[4 * b + r] = (acc[u][b][r] * uS) / den;
+                        for (int r = 0; r < 4; ++r) out[4 * b + r] = acc[u][b][r] * inv;
                 }
                 store_row<T, F>(o + (bh * T_ + t) * D + F * grp, out);
             }
@@ -684,7 +756,9 @@ __global__ __launch_bounds__(kThreads) void fwd_output_kernel(
     Row<T, F> b0[U], b1[U];
     const int64_t first = c0 + wave * 16 * U;
     issue(b0, first);
+    sched_fence();
     issue(b1, first + stride);
+    sched_fence();
     for (int64_t base = first; base < c1; base += 2 * stride) {
         body(b0, base);
         if (base + stride >= c1) break;
@@ -715,7 +789,7 @@ template <typename T, int D, bool SIMPLE>
 __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(
     const T* __restrict__ q, const T* __restrict__ dout, const float* __restrict__ stS,
     const float* __restrict__ stz, T* __restrict__ dq, float* __restrict__ part,
-    float* __restrict__ dS_out, float* __restrict__ dz_out, int* __restrict__ cnt, int64_t T_, int PB,
+    float* __restrict__ dS_out, float* __restrict__ dz_out, int64_t T_, int PB,
     int64_t LB, float eps) {
     using Sh = StreamShape<T, D>;
     using Bq = BwdQShape<T, D>;
@@ -729,7 +803,6 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(
     __shared__ __attribute__((aligned(16))) T sW[D * LDT];
     __shared__ float sdz[kWaves][D];
     __shared__ float red[4];
-    __shared__ int s_flag[1];
 
     const int wid = xcd_remap(blockIdx.x, gridDim.x);
     const int64_t bh = wid / PB;
@@ -743,16 +816,11 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(
 
     int sS = 0, sz = 0, sw = 0;
     if constexpr (Elt<T>::kScaled) {
-        float mx = 0.f, mz = 0.f, zs = 0.f;
-        for (int i = tid; i < D * D; i += kThreads) mx = fmaxf(mx, fabsf(S[i]));
-        for (int i = tid; i < D; i += kThreads) {
-            mz = fmaxf(mz, fabsf(z[i]));
-            zs += z[i];
-        }
-        sS = scale_exp(block_max(mx, red));
-        sz = scale_exp(block_max(mz, red));
+        float mz, zsum;
+        sS = scale_exp(block_absmax_matrix<D>(S, red));
+        block_vector_stats<D>(z, red, mz, zsum);
+        sz = scale_exp(mz);
         if constexpr (!SIMPLE) {
-            const float zsum = block_sum(zs, red);
             if (zsum > 0.f && isfinite(zsum)) {
                 int e;
                 frexpf(zsum, &e);
@@ -760,13 +828,12 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(
             }
         }
     }
-    for (int f = wave; f < NFR; f += kWaves) {
-        Frag<T> fr;
-        if (f < NFS)
-            fr = build_frag<T, D, false>(S, f / KS, f % KS, m, grp, ldexpf(1.f, sS));
-        else
-            fr = build_zfrag<T, D>(z, f - NFS, grp, ldexpf(1.f, sz));
-        sA[f * 64 + lane] = fr;
+    {
+        const float fS = ldexpf(1.f, sS), fz = ldexpf(1.f, sz);
+        build_frags<T, NFR>(sA, [&](int f) {
+            return f < NFS ? build_frag<T, D, false>(S, f / KS, f % KS, m, grp, fS)
+                           : build_zfrag<T, D>(z, max(f - NFS, 0), grp, fz);
+        });
     }
     float zl[F];
 #pragma unroll
@@ -789,8 +856,9 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(
             const int64_t t = base + (wave * U + u) * 16 + m;
             const bool valid = t < t1;
             Row<T, F> qr, dr;
-            load_row<T, F>(qr, q + (bh * T_ + t) * D + F * grp, valid);
-            load_row<T, F>(dr, dout + (bh * T_ + t) * D + F * grp, valid);
+            const int64_t tc = min(t, t1 - 1);  // rows past t1 are masked below
+            load_row<T, F>(qr, q + (bh * T_ + tc) * D + F * grp);
+            load_row<T, F>(dr, dout + (bh * T_ + tc) * D + F * grp);
             float qt[F];
 #pragma unroll
             for (int o = 0; o < F; ++o) qt[o] = phi<T>(to_f32(qr.e[o]));
@@ -833,11 +901,12 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(
                     }
                 rr += __shfl_xor(rr, 16);
                 rr += __shfl_xor(rr, 32);
-                const float c = -(rr / den) / den;
-                const float ws = fw / den;
+                const float inv = 1.f / den;
+                const float c = -(rr * inv) * inv;
+                const float ws = fw * inv;
 #pragma unroll
                 for (int o = 0; o < F; ++o) {
-                    dqt[o] = uu[o] / den + c * zl[o];
+                    dqt[o] = uu[o] * inv + c * zl[o];
                     wv[o] = to_f32(dr.e[o]) * ws;
                     if (valid) dzacc[o] += c * qt[o];
                 }
@@ -904,23 +973,28 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(
     }
     __syncthreads();
     for (int i = tid; i < D; i += kThreads) oz[i] = (sdz[0][i] + sdz[1][i]) + (sdz[2][i] + sdz[3][i]);
-    if (PB > 1) combine_if_last<D>(part, cnt, dS_out, dz_out, bh, PB, s_flag);
 }
 
 // Steps 5-6 for 16-bit inputs at D = 64, per wave: each wave walks its own
 // 16-token steps (w, w + 4, ...) with two steps of Q and dO loads in flight.
-// Per step it computes u = S dO_t, den, dQ as the workgroup kernel above,
-// then writes phi(q) and w = dO 2^sw / den row-major into its own LDS area and
-// reads them back transposed (4 tokens per lane) as the A = phi(Q)^T and
-// B = w operands of sixteen 16x16x16 MFMAs that add the step into the wave's
-// private 64 x 64 dS. Waves are combined in a fixed order at the end.
+// Per step it computes u = S dO_t, den and dQ as the workgroup kernel above.
+// For the reduction over tokens it writes A_t = phi(q_t) 2^sw / den_t and the
+// raw dO_t row-major into its own LDS area, plus one more column
+// beta_t = -r_t / den_t next to dO, and reads them back transposed (4 tokens
+// per lane) as the operands of 16x16x16 MFMAs:
+//   sum_t A_t dO_t^T = 2^sw dS   and   sum_t A_t beta_t = 2^sw dz
+// (c_t phi(q_t) = (-r_t / den_t)(phi(q_t) / den_t)), so dS and dz share one
+// operand and need no per-element work beyond the scaling of phi(q). Each
+// wave holds its own 64 x 65 sums; waves are combined in a fixed order.
 template <typename T, bool SIMPLE>
 __global__ __launch_bounds__(kThreads, 2) void bwd_dq_w64_kernel(
     const T* __restrict__ q, const T* __restrict__ dout, const float* __restrict__ stS,
     const float* __restrict__ stz, T* __restrict__ dq, float* __restrict__ part,
-    float* __restrict__ dS_out, float* __restrict__ dz_out, int* __restrict__ cnt, int64_t T_, int PB,
+    float* __restrict__ dS_out, float* __restrict__ dz_out, int64_t T_, int PB,
     int64_t LB, float eps) {
-    constexpr int D = 64, F = 16, NB = 4, KS = 2, STEP = 16, LDR = 72, E = D * D + D;
+    constexpr int D = 64, F = 16, NB = 4, KS = 2, STEP = 16, E = D * D + D;
+    constexpr int LDR = 88;                   // 176-byte rows: 64 features + the beta column block
+    constexpr int NJ = NB + (SIMPLE ? 0 : 1);  // dS column blocks (+ dz)
     constexpr int NFS = NB * KS;
     constexpr int NFR = NFS + (SIMPLE ? 0 : KS);
     constexpr int kFragBytes = NFR * 64 * 16;
@@ -929,7 +1003,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_w64_kernel(
     constexpr int kRedBytes = 2 * E * (int)sizeof(float);
     __shared__ __attribute__((aligned(16))) unsigned char smem[kLoopBytes > kRedBytes ? kLoopBytes : kRedBytes];
     __shared__ float red4[4];
-    __shared__ int s_flag[1];
+    __shared__ __attribute__((aligned(16))) float sZ[D];
 
     const int wid = xcd_remap(blockIdx.x, gridDim.x);
     const int64_t bh = wid / PB;
@@ -947,16 +1021,11 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_w64_kernel(
 
     int sS = 0, sz = 0, sw = 0;
     if constexpr (Elt<T>::kScaled) {
-        float mx = 0.f, mz = 0.f, zs = 0.f;
-        for (int i = tid; i < D * D; i += kThreads) mx = fmaxf(mx, fabsf(S[i]));
-        for (int i = tid; i < D; i += kThreads) {
-            mz = fmaxf(mz, fabsf(z[i]));
-            zs += z[i];
-        }
-        sS = scale_exp(block_max(mx, red4));
-        sz = scale_exp(block_max(mz, red4));
+        float mz, zsum;
+        sS = scale_exp(block_absmax_matrix<D>(S, red4));
+        block_vector_stats<D>(z, red4, mz, zsum);
+        sz = scale_exp(mz);
         if constexpr (!SIMPLE) {
-            const float zsum = block_sum(zs, red4);
             if (zsum > 0.f && isfinite(zsum)) {
                 int e;
                 frexpf(zsum, &e);
@@ -964,57 +1033,54 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_w64_kernel(
             }
         }
     }
-    for (int f = wave; f < NFR; f += kWaves) {
-        Frag<T> fr;
-        if (f < NFS)
-            fr = build_frag<T, D, false>(S, f / KS, f % KS, m, grp, ldexpf(1.f, sS));
-        else
-            fr = build_zfrag<T, D>(z, f - NFS, grp, ldexpf(1.f, sz));
-        sA[f * 64 + lane] = fr;
+    {
+        const float fS = ldexpf(1.f, sS), fz = ldexpf(1.f, sz);
+        build_frags<T, NFR>(sA, [&](int f) {
+            return f < NFS ? build_frag<T, D, false>(S, f / KS, f % KS, m, grp, fS)
+                           : build_zfrag<T, D>(z, max(f - NFS, 0), grp, fz);
+        });
     }
-    float zl[F];
-#pragma unroll
-    for (int o = 0; o < F; ++o) zl[o] = SIMPLE ? 0.f : z[F * grp + o];
+    for (int i = tid; i < D; i += kThreads) sZ[i] = z[i];
     __syncthreads();
     const float uS = ldexpf(1.f, -sS), uz = ldexpf(1.f, -sz), fw = ldexpf(1.f, sw);
 
-    f32x4 dsacc[NB][NB];
+    f32x4 dsacc[NB][NJ];
 #pragma unroll
     for (int b = 0; b < NB; ++b)
 #pragma unroll
-        for (int j = 0; j < NB; ++j) dsacc[b][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float dzacc[F];
-#pragma unroll
-    for (int o = 0; o < F; ++o) dzacc[o] = 0.f;
+        for (int j = 0; j < NJ; ++j) dsacc[b][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     struct Stage {
         Row<T, F> q, d;
     };
     auto issue = [&](Stage& st, int step) {
-        const int64_t t = t0 + (int64_t)step * STEP + m;
-        const bool valid = step < nsteps && t < t1;
-        load_row<T, F>(st.q, q + (bh * T_ + t) * D + F * grp, valid);
-        load_row<T, F>(st.d, dout + (bh * T_ + t) * D + F * grp, valid);
+        const int64_t t = min(t0 + (int64_t)step * STEP + m, t1 - 1);  // masked in body
+        load_row<T, F>(st.q, q + (bh * T_ + t) * D + F * grp);
+        load_row<T, F>(st.d, dout + (bh * T_ + t) * D + F * grp);
     };
     const int rA = 4 * grp + (m >> 2), cA = 4 * (m & 3);
     auto body = [&](Stage& st, int step) {
         const int64_t t = t0 + (int64_t)step * STEP + m;
         const bool valid = t < t1;
-        float qt[F], dof[F];
+        float qt[F];
         Frag<T> bq[KS], bd[KS];
 #pragma unroll
-        for (int o = 0; o < F; ++o) {
-            qt[o] = phi<T>(to_f32(st.q.e[o]));
-            dof[o] = to_f32(st.d.e[o]);
-        }
+        for (int o = 0; o < F; ++o) qt[o] = phi<T>(to_f32(st.q.e[o]));
 #pragma unroll
         for (int s = 0; s < KS; ++s)
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                bq[s][e] = static_cast<T>(qt[8 * s + e]);
+                if constexpr (!SIMPLE) bq[s][e] = static_cast<T>(qt[8 * s + e]);
                 bd[s][e] = st.d.e[8 * s + e];
             }
+        // dO rows go to LDS as loaded (zero for rows past the slice)
+        zero_row_unless(st.d, valid);
+        uint4* dw4 = reinterpret_cast<uint4*>(&sW[m * LDR + F * grp]);
+        dw4[0] = reinterpret_cast<const uint4*>(st.d.e)[0];
+        dw4[1] = reinterpret_cast<const uint4*>(st.d.e)[1];
+        sched_fence();
         issue(st, step + 2 * kWaves);  // this stage's registers are free again
+        sched_fence();
         f32x4 au[NB];
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
@@ -1022,38 +1088,35 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_w64_kernel(
 #pragma unroll
             for (int s = 0; s < KS; ++s) au[b] = mma(sA[(b * KS + s) * 64 + lane], bd[s], au[b]);
         }
-        float dqt[F], wv[F];
+        float dqt[F];
+        float aq = 1.f;  // factor on phi(q) in the reduction operand
         if constexpr (SIMPLE) {
 #pragma unroll
             for (int b = 0; b < NB; ++b)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) dqt[4 * b + r] = au[b][r] * uS;
-#pragma unroll
-            for (int o = 0; o < F; ++o) wv[o] = dof[o];
         } else {
             f32x4 ad = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int s = 0; s < KS; ++s) ad = mma(sA[(NFS + s) * 64 + lane], bq[s], ad);
-            const float den = ad[0] * uz + eps;
-            float uu[F];
+            const float inv = 1.f / (ad[0] * uz + eps);
             float rr = 0.f;
 #pragma unroll
             for (int b = 0; b < NB; ++b)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    uu[4 * b + r] = au[b][r] * uS;
-                    rr += qt[4 * b + r] * uu[4 * b + r];
-                }
+                for (int r = 0; r < 4; ++r) rr += qt[4 * b + r] * au[b][r];
             rr += __shfl_xor(rr, 16);
             rr += __shfl_xor(rr, 32);
-            const float cc = -(rr / den) / den;
-            const float ws = fw / den;
+            const float beta = -(rr * uS) * inv;  // -r / den
+            const float cc = beta * inv;          // -r / den^2
+            const float ku = uS * inv;
+            const float* zl = &sZ[F * grp];
 #pragma unroll
-            for (int o = 0; o < F; ++o) {
-                dqt[o] = uu[o] / den + cc * zl[o];
-                wv[o] = dof[o] * ws;
-                if (valid) dzacc[o] += cc * qt[o];
-            }
+            for (int b = 0; b < NB; ++b)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) dqt[4 * b + r] = au[b][r] * ku + cc * zl[4 * b + r];
+            aq = fw * inv;
+            if (grp == 0) sW[m * LDR + D] = valid ? static_cast<T>(beta) : static_cast<T>(0.f);
         }
         if (valid) {
             float out[F];
@@ -1061,24 +1124,18 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_w64_kernel(
             for (int o = 0; o < F; ++o) out[o] = dqt[o] * fminf(qt[o], 1.f);  // phi' = min(phi, 1)
             store_row<T, F>(dq + (bh * T_ + t) * D + F * grp, out);
         }
-        Row<T, F> rq, rw;
+        Row<T, F> rq;
 #pragma unroll
-        for (int o = 0; o < F; ++o) {
-            rq.e[o] = valid ? static_cast<T>(qt[o]) : static_cast<T>(0.f);
-            rw.e[o] = valid ? static_cast<T>(wv[o]) : static_cast<T>(0.f);
-        }
+        for (int o = 0; o < F; ++o) rq.e[o] = valid ? static_cast<T>(qt[o] * aq) : static_cast<T>(0.f);
         uint4* dq4 = reinterpret_cast<uint4*>(&sQ[m * LDR + F * grp]);
-        uint4* dw4 = reinterpret_cast<uint4*>(&sW[m * LDR + F * grp]);
         dq4[0] = reinterpret_cast<const uint4*>(rq.e)[0];
         dq4[1] = reinterpret_cast<const uint4*>(rq.e)[1];
-        dw4[0] = reinterpret_cast<const uint4*>(rw.e)[0];
-        dw4[1] = reinterpret_cast<const uint4*>(rw.e)[1];
         wave_lds_sync();
         i16x4 a[NB];
 #pragma unroll
         for (int b = 0; b < NB; ++b) a[b] = lds_read_tr(&sQ[rA * LDR + 16 * b + cA]);
 #pragma unroll
-        for (int j = 0; j < NB; ++j) {
+        for (int j = 0; j < NJ; ++j) {
             const i16x4 bw = lds_read_tr(&sW[rA * LDR + 16 * j + cA]);
 #pragma unroll
             for (int b = 0; b < NB; ++b) dsacc[b][j] = mma_k16<T>(a[b], bw, dsacc[b][j]);
@@ -1086,46 +1143,42 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_w64_kernel(
         wave_lds_sync();
     };
 
-    Stage s0, s1;
-    issue(s0, wave);
-    issue(s1, wave + kWaves);
-    for (int st = wave; st < nsteps; st += 2 * kWaves) {
-        body(s0, st);
-        if (st + kWaves >= nsteps) break;
-        body(s1, st + kWaves);
+    if (nsteps > 0) {
+        Stage s0, s1;
+        issue(s0, wave);
+        sched_fence();
+        issue(s1, wave + kWaves);
+        sched_fence();
+        for (int st = wave; st < nsteps; st += 2 * kWaves) {
+            body(s0, st);
+            if (st + kWaves >= nsteps) break;
+            body(s1, st + kWaves);
+        }
     }
 
-    // dz: sum over the 16 token lanes of each lane group (fixed butterfly)
-#pragma unroll
-    for (int o = 0; o < F; ++o) {
-        float x = dzacc[o];
-        x += __shfl_xor(x, 1);
-        x += __shfl_xor(x, 2);
-        x += __shfl_xor(x, 4);
-        x += __shfl_xor(x, 8);
-        dzacc[o] = x;
-    }
-    // fixed-order sum of the four waves: (w0 + w2) + (w1 + w3)
+    // fixed-order sum of the four waves: (w0 + w2) + (w1 + w3); column 0 of
+    // the last block holds dz
     __syncthreads();
     float* red = reinterpret_cast<float*>(smem);
     const float uw = ldexpf(1.f, -sw);
     if (wave >= 2) {
         float* dst = red + (wave - 2) * E;
 #pragma unroll
-        for (int b = 0; b < NB; ++b)
+        for (int b = 0; b < NB; ++b) {
 #pragma unroll
             for (int j = 0; j < NB; ++j)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) dst[(16 * b + 4 * grp + r) * D + 16 * j + m] = dsacc[b][j][r] * uw;
-        if (m == 0)
+            if (m == 0)
 #pragma unroll
-            for (int o = 0; o < F; ++o) dst[D * D + F * grp + o] = dzacc[o];
+                for (int r = 0; r < 4; ++r) dst[D * D + 16 * b + 4 * grp + r] = SIMPLE ? 0.f : dsacc[b][NJ - 1][r] * uw;
+        }
     }
     __syncthreads();
     if (wave < 2) {
         float* dst = red + wave * E;
 #pragma unroll
-        for (int b = 0; b < NB; ++b)
+        for (int b = 0; b < NB; ++b) {
 #pragma unroll
             for (int j = 0; j < NB; ++j)
 #pragma unroll
@@ -1133,9 +1186,13 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_w64_kernel(
                     const int idx = (16 * b + 4 * grp + r) * D + 16 * j + m;
                     dst[idx] = dsacc[b][j][r] * uw + dst[idx];
                 }
-        if (m == 0)
+            if (m == 0)
 #pragma unroll
-            for (int o = 0; o < F; ++o) dst[D * D + F * grp + o] = dzacc[o] + dst[D * D + F * grp + o];
+                for (int r = 0; r < 4; ++r) {
+                    const int idx = D * D + 16 * b + 4 * grp + r;
+                    dst[idx] = (SIMPLE ? 0.f : dsacc[b][NJ - 1][r] * uw) + dst[idx];
+                }
+        }
     }
     __syncthreads();
     float* oS;
@@ -1154,7 +1211,6 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_w64_kernel(
         else
             oz[i - D * D] = x;
     }
-    if (PB > 1) combine_if_last<D>(part, cnt, dS_out, dz_out, bh, PB, s_flag);
 }
 
 // ---------------------------------------------------------------------------
@@ -1186,20 +1242,14 @@ __global__ __launch_bounds__(kThreads) void bwd_dkv_kernel(
     const float* dz = dzg + bh * D;
 
     int sD = 0;
-    if constexpr (Elt<T>::kScaled) {
-        float mx = 0.f;
-        for (int i = tid; i < D * D; i += kThreads) mx = fmaxf(mx, fabsf(dS[i]));
-        sD = scale_exp(block_max(mx, red));
-    }
+    if constexpr (Elt<T>::kScaled) sD = scale_exp(block_absmax_matrix<D>(dS, red));
     const float fD = ldexpf(1.f, sD), uD = ldexpf(1.f, -sD);
-    for (int f = wave; f < 2 * NFS; f += kWaves) {
-        Frag<T> fr;
-        if (f < NFS)  // dK side: rows i, contraction j -> dS[i][j]
-            fr = build_frag<T, D, false>(dS, f / KS, f % KS, m, grp, fD);
-        else  // dV side: rows j, contraction i -> dS[i][j]
-            fr = build_frag<T, D, true>(dS, (f - NFS) / KS, (f - NFS) % KS, m, grp, fD);
-        sA[f * 64 + lane] = fr;
-    }
+    // fragments [0, NFS): dK side, rows i, contraction j -> dS[i][j];
+    // [NFS, 2 NFS): dV side, rows j, contraction i -> dS[i][j]
+    build_frags<T, 2 * NFS>(sA, [&](int f) {
+        return f < NFS ? build_frag<T, D, false>(dS, f / KS, f % KS, m, grp, fD)
+                       : build_frag<T, D, true>(dS, (f - NFS) / KS, (f - NFS) % KS, m, grp, fD);
+    });
     float dzl[F];
 #pragma unroll
     for (int o = 0; o < F; ++o) dzl[o] = SIMPLE ? 0.f : dz[F * grp + o];
@@ -1212,9 +1262,9 @@ __global__ __launch_bounds__(kThreads) void bwd_dkv_kernel(
     auto issue = [&](Stage& st, int64_t bs) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int64_t t = bs + 16 * u + m;
-            load_row<T, F>(st.k[u], k + (bh * T_ + t) * D + F * grp, t < c1);
-            load_row<T, F>(st.v[u], v + (bh * T_ + t) * D + F * grp, t < c1);
+            const int64_t t = min(bs + 16 * u + m, c1 - 1);  // rows past c1 are computed, not stored
+            load_row<T, F>(st.k[u], k + (bh * T_ + t) * D + F * grp);
+            load_row<T, F>(st.v[u], v + (bh * T_ + t) * D + F * grp);
         }
     };
     auto body = [&](Stage& st, int64_t base) {
@@ -1236,7 +1286,9 @@ __global__ __launch_bounds__(kThreads) void bwd_dkv_kernel(
                     bv[u][s][e] = st.v[u].e[8 * s + e];
                 }
         }
+        sched_fence();
         issue(st, base + 2 * stride);
+        sched_fence();
         f32x4 ak[U][NB], av[U][NB];
 #pragma unroll
         for (int u = 0; u < U; ++u)
@@ -1278,7 +1330,9 @@ __global__ __launch_bounds__(kThreads) void bwd_dkv_kernel(
     Stage s0, s1;
     const int64_t first = c0 + wave * 16 * U;
     issue(s0, first);
+    sched_fence();
     issue(s1, first + stride);
+    sched_fence();
     for (int64_t base = first; base < c1; base += 2 * stride) {
         body(s0, base);
         if (base + stride >= c1) break;
@@ -1292,22 +1346,32 @@ __global__ __launch_bounds__(kThreads) void bwd_dkv_kernel(
 template <typename T, int D>
 constexpr bool kWaveKernels = (sizeof(T) == 2 && D == 64);
 
+// After a split reduction (P > 1 slices per head), sum the partials.
+template <int D>
+hipError_t launch_combine(int P, const float* part, float* outS, float* outz, int64_t BH, hipStream_t s) {
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || P <= 1) return e;
+    constexpr int E4 = (D * D + D) / 4;
+    const int64_t nblk = BH * ((E4 + kThreads - 1) / kThreads);
+    hipLaunchKernelGGL((combine_kernel<D>), dim3((unsigned)nblk), dim3(kThreads), 0, s, part, P, outS, outz, BH);
+    return hipGetLastError();
+}
+
 template <typename T, int D>
 hipError_t fwd_state_t(const Plan& p, const void* k, const void* v, float* state, void* ws,
                        hipStream_t s) {
     const int64_t nblk = p.BH * p.P;
     char* w = static_cast<char*>(ws);
     float* part = reinterpret_cast<float*>(w + p.off_part);
-    int* cnt = reinterpret_cast<int*>(w + p.off_cnt_fwd);
     if constexpr (kWaveKernels<T, D>)
         hipLaunchKernelGGL((fwd_state_w64_kernel<T>), dim3((unsigned)nblk), dim3(kThreads), 0, s,
                            static_cast<const T*>(k), static_cast<const T*>(v), state,
-                           state + p.BH * D * D, part, cnt, p.T, p.P, p.L);
+                           state + p.BH * D * D, part, p.T, p.P, p.L);
     else
         hipLaunchKernelGGL((fwd_state_kernel<T, D>), dim3((unsigned)nblk), dim3(kThreads), 0, s,
                            static_cast<const T*>(k), static_cast<const T*>(v), state,
-                           state + p.BH * D * D, part, cnt, p.T, p.P, p.L);
-    return hipGetLastError();
+                           state + p.BH * D * D, part, p.T, p.P, p.L);
+    return launch_combine<D>(p.P, part, state, state + p.BH * D * D, p.BH, s);
 }
 
 template <typename T, int D>
@@ -1331,7 +1395,6 @@ hipError_t bwd_dq_t(const Plan& p, const void* q, const void* dout, const float*
     char* w = static_cast<char*>(ws);
     float* part = reinterpret_cast<float*>(w + p.off_part);
     float* dst = reinterpret_cast<float*>(w + p.off_dstate);
-    int* cnt = reinterpret_cast<int*>(w + p.off_cnt_bwd);
     const T* qq = static_cast<const T*>(q);
     const T* dd = static_cast<const T*>(dout);
     const float* sS = state;
@@ -1342,19 +1405,19 @@ hipError_t bwd_dq_t(const Plan& p, const void* q, const void* dout, const float*
     if constexpr (kWaveKernels<T, D>) {
         if (p.simple)
             hipLaunchKernelGGL((bwd_dq_w64_kernel<T, true>), dim3((unsigned)nblk), dim3(kThreads), 0, s,
-                               qq, dd, sS, sz, g, part, dS, dz, cnt, p.T, p.PB, p.LB, p.eps);
+                               qq, dd, sS, sz, g, part, dS, dz, p.T, p.PB, p.LB, p.eps);
         else
             hipLaunchKernelGGL((bwd_dq_w64_kernel<T, false>), dim3((unsigned)nblk), dim3(kThreads), 0, s,
-                               qq, dd, sS, sz, g, part, dS, dz, cnt, p.T, p.PB, p.LB, p.eps);
+                               qq, dd, sS, sz, g, part, dS, dz, p.T, p.PB, p.LB, p.eps);
     } else {
         if (p.simple)
             hipLaunchKernelGGL((bwd_dq_kernel<T, D, true>), dim3((unsigned)nblk), dim3(kThreads), 0, s,
-                               qq, dd, sS, sz, g, part, dS, dz, cnt, p.T, p.PB, p.LB, p.eps);
+                               qq, dd, sS, sz, g, part, dS, dz, p.T, p.PB, p.LB, p.eps);
         else
             hipLaunchKernelGGL((bwd_dq_kernel<T, D, false>), dim3((unsigned)nblk), dim3(kThreads), 0, s,
-                               qq, dd, sS, sz, g, part, dS, dz, cnt, p.T, p.PB, p.LB, p.eps);
+                               qq, dd, sS, sz, g, part, dS, dz, p.T, p.PB, p.LB, p.eps);
     }
-    return hipGetLastError();
+    return launch_combine<D>(p.PB, part, dS, dz, p.BH, s);
 }
 
 template <typename T, int D>
