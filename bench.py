@@ -4,8 +4,11 @@ One step is one pass of the whole path over one batch: la_fwd_state (phi, split-
 state reduction, combine), la_fwd_output (O), la_bwd_dq (dQ and the dS, dz
 state), la_bwd_dkv (dK, dV) -- exactly the launches of la_fwd then la_bwd, on
 torch's current stream. HIP events bracket every launch, so each kernel's
-duration is measured live; the infinity cache and L2 are flushed before every
-step (outside the events) by writing a 1 GiB scratch buffer.
+duration is measured live. Before every step (outside the events) the 256 MB
+infinity cache and the L2s are flushed by reading a 1 GiB scratch buffer: a
+read leaves them holding clean lines, so every input is fetched from HBM and
+no write-back of the flush's own data is charged to the step (a writing flush
+would leave 256 MB of dirty lines to evict during the next kernel).
 
 Prints one JSON line. `value` is the forward's algorithmic HBM rate (Q, K, V
 read and O written once) in GB/s; fwd/bwd/fwd+bwd milliseconds ride along.
@@ -104,7 +107,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=HEADLINE, choices=list(WORKLOADS))
-    ap.add_argument("--no-flush", action="store_true", help="skip the cache flush between steps")
+    ap.add_argument("--flush", choices=("read", "write", "none"), default="read",
+                    help="cache flush before each step: read 1 GiB (default), write 1 GiB, or none")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=128, help="heads in the oracle sample")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -130,7 +134,13 @@ def main() -> int:
     state = la.new_state(prob, q.device)
     ws = la.workspace(prob, q.device)
     o, dq, dk, dv = (torch.empty_like(q) for _ in range(4))
-    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda")  # 1 GiB
+
+    def do_flush(mode):
+        if mode == "read":
+            flush.sum()
+        elif mode == "write":
+            flush.fill_(1.0)
 
     def step(ev):
         ev[0].record()
@@ -149,8 +159,7 @@ def main() -> int:
     mk = lambda: [torch.cuda.Event(enable_timing=True) for _ in range(5)]  # noqa: E731
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
-        if not args.no_flush:
-            flush.fill_(1)
+        do_flush(args.flush)
         step(mk())
     torch.cuda.synchronize()
 
@@ -159,11 +168,27 @@ def main() -> int:
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        if not args.no_flush:
-            flush.fill_(1)  # evict the 256 MB infinity cache and L2, outside the events
+        do_flush(args.flush)  # evict the infinity cache and L2s, outside the events
         step(events[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+
+    # The same step under the other two cache conditions, for context: a
+    # writing flush (what L2-flushing benchmark helpers usually do) and none
+    # (back-to-back steps: each pays the write-back of the previous one's
+    # outputs that the 256 MB infinity cache still holds).
+    other = {}
+    for mode in ("read", "write", "none"):
+        if mode == args.flush:
+            continue
+        evs = [mk() for _ in range(min(args.steps, 10))]
+        for ev in evs:
+            do_flush(mode)
+            step(ev)
+        torch.cuda.synchronize()
+        f = np.mean([ev[0].elapsed_time(ev[2]) for ev in evs])
+        other[mode] = {"fwd_ms": round(float(f), 4),
+                       "fwd_bwd_ms": round(float(np.mean([ev[0].elapsed_time(ev[4]) for ev in evs])), 4)}
 
     per = {kname: np.array([ev[j].elapsed_time(ev[j + 1]) for ev in events])
            for j, kname in enumerate(KERNELS)}
@@ -206,13 +231,15 @@ def main() -> int:
             "mode": "simple_la" if w.simple else "normalised",
             "eps": w.eps,
             "pass": "fwd+bwd" if w.bwd else "fwd",
-            "cache_flush_between_steps": not args.no_flush,
+            "cache_flush_before_step": {"read": "read 1 GiB", "write": "write 1 GiB",
+                                        "none": "none"}[args.flush],
         },
         "fwd_ms": round(float(np.mean(fwd_ms)), 4),
         "fwd_ms_min": round(float(np.min(fwd_ms)), 4),
         "fwd_frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
         "kernel_ms": {kname: round(a, 4) for kname, a in avg.items()},
         "wall_ms_per_step_incl_flush": round(wall / args.steps * 1e3, 4),
+        "other_cache_conditions": other,
         "roofline": {
             "kernel": dominant,
             "bound": "hbm",
