@@ -144,6 +144,74 @@ struct alignas(16) Row {
     T e[N];
 };
 
+// Buffer-descriptor access to one head's rows. The descriptor covers exactly
+// the head's T rows (T * D * sizeof(T) bytes, below 2^31), so loads past the
+// last row read zeros and stores there are dropped by the hardware: the
+// kernels need no clamping or branches at the ragged end of a sequence.
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+struct HeadBuf {
+    __amdgpu_buffer_rsrc_t rsrc;
+};
+template <typename T>
+__device__ __forceinline__ HeadBuf head_buf(const T* base, int64_t bh, int64_t T_, int D) {
+    const T* p = base + bh * T_ * D;
+    return HeadBuf{__builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(p), 0, (int)(T_ * D * (int64_t)sizeof(T)),
+                                                     0x00020000)};
+}
+__device__ __forceinline__ uint4 buf_load16(const HeadBuf& b, int byte_off) {
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(b.rsrc, byte_off, 0, 0);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void buf_store16(const HeadBuf& b, int byte_off, uint4 x) {
+    const u32x4 v = {x.x, x.y, x.z, x.w};
+    __builtin_amdgcn_raw_buffer_store_b128(v, b.rsrc, byte_off, 0, 0);
+}
+
+// N contiguous elements of row `row` starting at element `col`, by buffer loads.
+template <typename T, int N>
+__device__ __forceinline__ void load_row_buf(Row<T, N>& r, const HeadBuf& b, int64_t row, int D, int col) {
+    constexpr int NV = N * (int)sizeof(T) / 16;
+    uint4* d = reinterpret_cast<uint4*>(r.e);
+    const int off = (int)(row * D + col) * (int)sizeof(T);
+#pragma unroll
+    for (int i = 0; i < NV; ++i) d[i] = buf_load16(b, off + 16 * i);
+}
+
+// Stores a 16-row x D tile whose row n, columns [F g, F g + F), sit in lane
+// n + 16 g, as full contiguous rows: the lanes first write their quarter rows
+// to this wave's LDS staging area (row stride D + 16 bytes), then each lane
+// reads 16 bytes back so that one store instruction covers whole 128-byte lines.
+template <typename T, int D>
+__device__ __forceinline__ void store_tile_rows(T* stage, const Row<T, D / 4>& vals, const HeadBuf& b,
+                                                int64_t row0) {
+    constexpr int F = D / 4, EPC = 16 / (int)sizeof(T), LDR = D + EPC;
+    constexpr int CPR = D / EPC;       // 16-byte chunks per row
+    constexpr int RPI = 64 / CPR;      // rows per store instruction
+    const int lane = threadIdx.x & 63, m = lane & 15, g = lane >> 4;
+#pragma unroll
+    for (int i = 0; i < F / EPC; ++i)
+        *reinterpret_cast<uint4*>(&stage[m * LDR + F * g + EPC * i]) = reinterpret_cast<const uint4*>(vals.e)[i];
+    wave_lds_sync();
+    const int r = lane / CPR, c = lane % CPR;
+#pragma unroll
+    for (int k = 0; k < 16 / RPI; ++k) {
+        const uint4 x = *reinterpret_cast<const uint4*>(&stage[(k * RPI + r) * LDR + EPC * c]);
+        buf_store16(b, (int)((row0 + k * RPI + r) * D) * (int)sizeof(T) + 16 * c, x);
+    }
+    wave_lds_sync();
+}
+
+// Same tile, each lane storing its own quarter row (for shapes whose LDS
+// budget leaves no room for the staging area).
+template <typename T, int D>
+__device__ __forceinline__ void store_tile_quarters(const Row<T, D / 4>& vals, const HeadBuf& b, int64_t row0) {
+    constexpr int F = D / 4, NV = F * (int)sizeof(T) / 16;
+    const int lane = threadIdx.x & 63, m = lane & 15, g = lane >> 4;
+    const int off = (int)((row0 + m) * D + F * g) * (int)sizeof(T);
+#pragma unroll
+    for (int i = 0; i < NV; ++i) buf_store16(b, off + 16 * i, reinterpret_cast<const uint4*>(vals.e)[i]);
+}
+
 // Loads are unconditional: callers clamp the row index into the valid range
 // and discard or zero what belongs to rows past the end. (Loads under a branch
 // make the compiler drain every outstanding load at the join, which would
@@ -445,9 +513,6 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_state_w64_kernel(
     const int nsteps = (int)(t1 > t0 ? (t1 - t0 + STEP - 1) / STEP : 0);
     T* sK = reinterpret_cast<T*>(smem) + wave * 2 * TILE;
     T* sV = sK + TILE;
-    const T* kb = k + bh * T_ * D + c * 8;
-    const T* vb = v + bh * T_ * D + c * 8;
-
     f32x4 acc[NB][NB + 1];
 #pragma unroll
     for (int b = 0; b < NB; ++b)
@@ -460,12 +525,15 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_state_w64_kernel(
     struct Stage {
         uint4 k[4], v[4];
     };
+    // Slices are multiples of 4 steps, so a step never straddles a slice end
+    // before T; rows past T load as zeros, and phi(k) is masked for them.
+    const HeadBuf bk = head_buf(k, bh, T_, D), bv = head_buf(v, bh, T_, D);
     auto issue = [&](Stage& st, int step) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int64_t t = min(t0 + (int64_t)step * STEP + rg + 8 * r, t1 - 1);  // masked in consume
-            st.k[r] = *reinterpret_cast<const uint4*>(kb + t * D);
-            st.v[r] = *reinterpret_cast<const uint4*>(vb + t * D);
+            const int off = (int)((t0 + (int64_t)step * STEP + rg + 8 * r) * D + 8 * c) * (int)sizeof(T);
+            st.k[r] = buf_load16(bk, off);
+            st.v[r] = buf_load16(bv, off);
         }
     };
     // phi on K (fp32, rounded to T), padded rows zeroed after phi, row-major to LDS
@@ -479,13 +547,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_state_w64_kernel(
 #pragma unroll
             for (int e = 0; e < 8; ++e)
                 kt.e[e] = ok ? static_cast<T>(phi<T>(to_f32(ke[e]))) : static_cast<T>(0.f);
-            uint4 vv = st.v[r];
-            vv.x = ok ? vv.x : 0u;
-            vv.y = ok ? vv.y : 0u;
-            vv.z = ok ? vv.z : 0u;
-            vv.w = ok ? vv.w : 0u;
             *reinterpret_cast<uint4*>(&sK[row * LDR + 8 * c]) = *reinterpret_cast<const uint4*>(kt.e);
-            *reinterpret_cast<uint4*>(&sV[row * LDR + 8 * c]) = vv;
+            *reinterpret_cast<uint4*>(&sV[row * LDR + 8 * c]) = st.v[r];
         }
     };
     const int rA = 8 * grp + (m >> 2), cA = 4 * (m & 3);
@@ -656,7 +719,9 @@ __global__ __launch_bounds__(kThreads) void fwd_output_kernel(
     constexpr int F = Sh::kF, NB = Sh::kNB, KS = Sh::kKS, U = Sh::kU;
     constexpr int NFS = NB * KS;             // S fragments
     constexpr int NFR = NFS + (SIMPLE ? 0 : KS);  // + z fragments
+    constexpr int LDR = D + 16 / (int)sizeof(T);
     __shared__ Frag<T> sA[NFR * 64];
+    __shared__ __attribute__((aligned(16))) T stage[kWaves * 16 * LDR];
     __shared__ float red[4];
 
     const int wid = xcd_remap(blockIdx.x, gridDim.x);
@@ -689,12 +754,13 @@ __global__ __launch_bounds__(kThreads) void fwd_output_kernel(
     // Each wave takes blocks of 16 U tokens, kWaves blocks apart, with the
     // loads of its next two blocks in flight while it computes one.
     const int64_t stride = 16 * U * kWaves;
+    // Chunk lengths are multiples of a wave block, so a block never straddles
+    // a chunk boundary; rows past T load as zeros and their stores are dropped.
+    const HeadBuf bq = head_buf(q, bh, T_, D), bo = head_buf(o, bh, T_, D);
+    T* stg = stage + wave * 16 * LDR;
     auto issue = [&](Row<T, F> (&b)[U], int64_t bs) {
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int64_t t = min(bs + 16 * u + m, c1 - 1);  // rows past c1 are computed, not stored
-            load_row<T, F>(b[u], q + (bh * T_ + t) * D + F * grp);
-        }
+        for (int u = 0; u < U; ++u) load_row_buf<T, F>(b[u], bq, bs + 16 * u + m, D, F * grp);
     };
     auto body = [&](Row<T, F> (&qr)[U], int64_t base) {
         Frag<T> bq[U][KS];
@@ -733,24 +799,21 @@ __global__ __launch_bounds__(kThreads) void fwd_output_kernel(
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int64_t t = base + 16 * u + m;
-            if (t < c1) {
-                float out[F];
-                if constexpr (SIMPLE) {
+            Row<T, F> out;
+            if constexpr (SIMPLE) {
 #pragma unroll
-                    for (int b = 0; b < NB; ++b)
+                for (int b = 0; b < NB; ++b)
 #pragma unroll
-                        for (int r = 0; r < 4; ++r) out[4 * b + r] = acc[u][b][r] * uS;
-                } else {
-                    // one division per token: O = num 2^-sS / (den 2^-sz + eps)
-                    const float inv = uS / (accd[u][0] * uz + eps);
+                    for (int r = 0; r < 4; ++r) out.e[4 * b + r] = static_cast<T>(acc[u][b][r] * uS);
+            } else {
+                // one division per token: O = num 2^-sS / (den 2^-sz + eps)
+                const float inv = uS / (accd[u][0] * uz + eps);
 #pragma unroll
-                    for (int b = 0; b < NB; ++b)
+                for (int b = 0; b < NB; ++b)
 #pragma unroll
-                        for (int r = 0; r < 4; ++r) out[4 * b + r] = acc[u][b][r] * inv;
-                }
-                store_row<T, F>(o + (bh * T_ + t) * D + F * grp, out);
+                    for (int r = 0; r < 4; ++r) out.e[4 * b + r] = static_cast<T>(acc[u][b][r] * inv);
             }
+            store_tile_rows<T, D>(stg, out, bo, base + 16 * u);
         }
     };
     Row<T, F> b0[U], b1[U];
@@ -998,7 +1061,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_w64_kernel(
     constexpr int NFS = NB * KS;
     constexpr int NFR = NFS + (SIMPLE ? 0 : KS);
     constexpr int kFragBytes = NFR * 64 * 16;
-    constexpr int kTileBytes = kWaves * 2 * STEP * LDR * (int)sizeof(T);
+    constexpr int LDO = D + 16 / (int)sizeof(T);  // dQ staging row stride
+    constexpr int kTileBytes = kWaves * (2 * STEP * LDR + 16 * LDO) * (int)sizeof(T);
     constexpr int kLoopBytes = kFragBytes + kTileBytes;
     constexpr int kRedBytes = 2 * E * (int)sizeof(float);
     __shared__ __attribute__((aligned(16))) unsigned char smem[kLoopBytes > kRedBytes ? kLoopBytes : kRedBytes];
@@ -1016,8 +1080,9 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_w64_kernel(
     const float* S = stS + bh * D * D;
     const float* z = stz + bh * D;
     Frag<T>* sA = reinterpret_cast<Frag<T>*>(smem);
-    T* sQ = reinterpret_cast<T*>(smem + kFragBytes) + wave * 2 * STEP * LDR;
+    T* sQ = reinterpret_cast<T*>(smem + kFragBytes) + wave * (2 * STEP * LDR + 16 * LDO);
     T* sW = sQ + STEP * LDR;
+    T* sO = sW + STEP * LDR;
 
     int sS = 0, sz = 0, sw = 0;
     if constexpr (Elt<T>::kScaled) {
@@ -1053,15 +1118,17 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_w64_kernel(
     struct Stage {
         Row<T, F> q, d;
     };
+    // Slices are multiples of 4 steps, so a step never straddles a slice end
+    // before T; rows past T load as zeros (dO = 0 gives u = 0, r = 0, beta = 0,
+    // so such rows add nothing to dS or dz) and their dQ stores are dropped.
+    const HeadBuf bq = head_buf(q, bh, T_, D), bd = head_buf(dout, bh, T_, D), bdq = head_buf(dq, bh, T_, D);
     auto issue = [&](Stage& st, int step) {
-        const int64_t t = min(t0 + (int64_t)step * STEP + m, t1 - 1);  // masked in body
-        load_row<T, F>(st.q, q + (bh * T_ + t) * D + F * grp);
-        load_row<T, F>(st.d, dout + (bh * T_ + t) * D + F * grp);
+        const int64_t t = t0 + (int64_t)step * STEP + m;
+        load_row_buf<T, F>(st.q, bq, t, D, F * grp);
+        load_row_buf<T, F>(st.d, bd, t, D, F * grp);
     };
     const int rA = 4 * grp + (m >> 2), cA = 4 * (m & 3);
     auto body = [&](Stage& st, int step) {
-        const int64_t t = t0 + (int64_t)step * STEP + m;
-        const bool valid = t < t1;
         float qt[F];
         Frag<T> bq[KS], bd[KS];
 #pragma unroll
@@ -1073,8 +1140,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_w64_kernel(
                 if constexpr (!SIMPLE) bq[s][e] = static_cast<T>(qt[8 * s + e]);
                 bd[s][e] = st.d.e[8 * s + e];
             }
-        // dO rows go to LDS as loaded (zero for rows past the slice)
-        zero_row_unless(st.d, valid);
+        // dO rows go to LDS as loaded
         uint4* dw4 = reinterpret_cast<uint4*>(&sW[m * LDR + F * grp]);
         dw4[0] = reinterpret_cast<const uint4*>(st.d.e)[0];
         dw4[1] = reinterpret_cast<const uint4*>(st.d.e)[1];
@@ -1116,20 +1182,20 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_w64_kernel(
 #pragma unroll
                 for (int r = 0; r < 4; ++r) dqt[4 * b + r] = au[b][r] * ku + cc * zl[4 * b + r];
             aq = fw * inv;
-            if (grp == 0) sW[m * LDR + D] = valid ? static_cast<T>(beta) : static_cast<T>(0.f);
-        }
-        if (valid) {
-            float out[F];
-#pragma unroll
-            for (int o = 0; o < F; ++o) out[o] = dqt[o] * fminf(qt[o], 1.f);  // phi' = min(phi, 1)
-            store_row<T, F>(dq + (bh * T_ + t) * D + F * grp, out);
+            if (grp == 0) sW[m * LDR + D] = static_cast<T>(beta);
         }
         Row<T, F> rq;
 #pragma unroll
-        for (int o = 0; o < F; ++o) rq.e[o] = valid ? static_cast<T>(qt[o] * aq) : static_cast<T>(0.f);
+        for (int o = 0; o < F; ++o) rq.e[o] = static_cast<T>(qt[o] * aq);
         uint4* dq4 = reinterpret_cast<uint4*>(&sQ[m * LDR + F * grp]);
         dq4[0] = reinterpret_cast<const uint4*>(rq.e)[0];
         dq4[1] = reinterpret_cast<const uint4*>(rq.e)[1];
+        {
+            Row<T, F> out;
+#pragma unroll
+            for (int o = 0; o < F; ++o) out.e[o] = static_cast<T>(dqt[o] * fminf(qt[o], 1.f));  // phi' = min(phi, 1)
+            store_tile_rows<T, D>(sO, out, bdq, t0 + (int64_t)step * STEP);
+        }
         wave_lds_sync();
         i16x4 a[NB];
 #pragma unroll
@@ -1228,7 +1294,11 @@ __global__ __launch_bounds__(kThreads) void bwd_dkv_kernel(
     constexpr int F = Sh::kF, NB = Sh::kNB, KS = Sh::kKS;
     constexpr int U = 1;  // one 16-token block per wave step; the prefetch gives the depth
     constexpr int NFS = NB * KS;
+    constexpr int LDR = D + 16 / (int)sizeof(T);
+    // fp32 at D = 128: the fragments fill the LDS, stores go out per lane
+    constexpr bool kStage = !(sizeof(T) == 4 && D == 128);
     __shared__ Frag<T> sA[2 * NFS * 64];
+    __shared__ __attribute__((aligned(16))) T stage[kStage ? kWaves * 16 * LDR : 8];
     __shared__ float red[4];
 
     const int wid = xcd_remap(blockIdx.x, gridDim.x);
@@ -1256,15 +1326,19 @@ __global__ __launch_bounds__(kThreads) void bwd_dkv_kernel(
     __syncthreads();
 
     const int64_t stride = 16 * U * kWaves;
+    // as in the output kernel: blocks never straddle a chunk boundary, rows
+    // past T load as zeros and their stores are dropped
+    const HeadBuf bk = head_buf(k, bh, T_, D), bv_ = head_buf(v, bh, T_, D);
+    const HeadBuf bdk = head_buf(dk, bh, T_, D), bdv = head_buf(dv, bh, T_, D);
+    T* stg = stage + (kStage ? wave * 16 * LDR : 0);
     struct Stage {
         Row<T, F> k[U], v[U];
     };
     auto issue = [&](Stage& st, int64_t bs) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int64_t t = min(bs + 16 * u + m, c1 - 1);  // rows past c1 are computed, not stored
-            load_row<T, F>(st.k[u], k + (bh * T_ + t) * D + F * grp);
-            load_row<T, F>(st.v[u], v + (bh * T_ + t) * D + F * grp);
+            load_row_buf<T, F>(st.k[u], bk, bs + 16 * u + m, D, F * grp);
+            load_row_buf<T, F>(st.v[u], bv_, bs + 16 * u + m, D, F * grp);
         }
     };
     auto body = [&](Stage& st, int64_t base) {
@@ -1311,19 +1385,21 @@ __global__ __launch_bounds__(kThreads) void bwd_dkv_kernel(
             }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int64_t t = base + 16 * u + m;
-            if (t < c1) {
-                float gk[F], gv[F];
+            Row<T, F> gk, gv;
 #pragma unroll
-                for (int b = 0; b < NB; ++b)
+            for (int b = 0; b < NB; ++b)
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int o = 4 * b + r;
-                        gk[o] = (ak[u][b][r] * uD + dzl[o]) * dphik[u][o];
-                        gv[o] = av[u][b][r] * uD;
-                    }
-                store_row<T, F>(dk + (bh * T_ + t) * D + F * grp, gk);
-                store_row<T, F>(dv + (bh * T_ + t) * D + F * grp, gv);
+                for (int r = 0; r < 4; ++r) {
+                    const int o = 4 * b + r;
+                    gk.e[o] = static_cast<T>((ak[u][b][r] * uD + dzl[o]) * dphik[u][o]);
+                    gv.e[o] = static_cast<T>(av[u][b][r] * uD);
+                }
+            if constexpr (kStage) {
+                store_tile_rows<T, D>(stg, gk, bdk, base + 16 * u);
+                store_tile_rows<T, D>(stg, gv, bdv, base + 16 * u);
+            } else {
+                store_tile_quarters<T, D>(gk, bdk, base + 16 * u);
+                store_tile_quarters<T, D>(gv, bdv, base + 16 * u);
             }
         }
     };
