@@ -96,10 +96,12 @@ template <> __device__ __forceinline__ f32x4 mma_k16<bf16>(i16x4 a, i16x4 b, f32
 // or the wait for the older batch would also drain the newer one.
 __device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
 
-// Orders this wave's LDS writes before its following LDS reads.
-__device__ __forceinline__ void wave_lds_sync() {
-    __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-}
+// Keeps this wave's LDS accesses in program order across the point. LDS
+// instructions from one wave execute in order, so a read issued after a write
+// to the same address sees the written value without waiting for it; only
+// the compiler must not move accesses across (it would be free to for the
+// transpose-read builtins it cannot prove alias the writes).
+__device__ __forceinline__ void wave_lds_sync() { __asm__ volatile("" ::: "memory"); }
 
 __device__ __forceinline__ f32x4 mma(f16x8 a, f16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
