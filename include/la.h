@@ -64,7 +64,7 @@ typedef enum {
 typedef enum {
     LA_OK = 0,
     LA_ERR_NULL = 1,       /* a required pointer is NULL                      */
-    LA_ERR_SHAPE = 2,      /* B, H or T negative, or sizes overflow           */
+    LA_ERR_SHAPE = 2,      /* B, H or T negative; B*H > 2^24; T*D*elt >= 2^31 */
     LA_ERR_DTYPE = 3,      /* dtype not one of la_dtype                       */
     LA_ERR_HEAD_DIM = 4,   /* D not supported (64 and 128 are)                */
     LA_ERR_FLAGS = 5,      /* unknown bit in flags                            */
@@ -79,7 +79,8 @@ typedef enum {
 #define LA_SIMPLE 0x1u
 
 /* Problem description shared by every call. B, H, T >= 0 (a zero size is an
- * empty problem: nothing to compute, LA_OK), D in {64, 128}, eps >= 0 and
+ * empty problem: nothing to compute, LA_OK), B*H <= 2^24, one head's rows
+ * below 2^31 bytes (T * D * element size), D in {64, 128}, eps >= 0 and
  * finite (used only in normalised mode). */
 typedef struct {
     int64_t B, H, T, D;

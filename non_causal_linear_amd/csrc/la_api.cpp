@@ -18,8 +18,9 @@ namespace {
 constexpr int64_t kMinSlice = 256;
 // Largest B*H accepted (grid sizes stay below 2^31).
 constexpr int64_t kMaxHeads = int64_t(1) << 24;
-// Largest T accepted (offsets stay far from int64 overflow).
-constexpr int64_t kMaxTokens = int64_t(1) << 34;
+// One head's rows are addressed through a buffer descriptor with 32-bit
+// offsets: T * D * sizeof(element) must stay below 2^31 bytes.
+constexpr int64_t kMaxHeadBytes = (int64_t(1) << 31) - 1;
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -48,8 +49,8 @@ la_status check_problem(const la_problem* p) {
     if (p->dtype != LA_F32 && p->dtype != LA_F16 && p->dtype != LA_BF16) return LA_ERR_DTYPE;
     if (p->D != 64 && p->D != 128) return LA_ERR_HEAD_DIM;
     if (p->B < 0 || p->H < 0 || p->T < 0) return LA_ERR_SHAPE;
-    if (p->B > kMaxHeads || p->H > kMaxHeads || p->B * p->H > kMaxHeads || p->T > kMaxTokens)
-        return LA_ERR_SHAPE;
+    if (p->B > kMaxHeads || p->H > kMaxHeads || p->B * p->H > kMaxHeads) return LA_ERR_SHAPE;
+    if (p->T > kMaxHeadBytes / (p->D * (p->dtype == LA_F32 ? 4 : 2))) return LA_ERR_SHAPE;
     if (p->flags & ~LA_SIMPLE) return LA_ERR_FLAGS;
     if (!(p->eps >= 0.f) || !isfinite(p->eps)) return LA_ERR_EPS;
     return LA_OK;

@@ -121,6 +121,10 @@ def test_fwd_rejects_bad_problems(L):
     assert fwd_call(L, prob(B=-1)) == SHAPE
     assert fwd_call(L, prob(T=-5)) == SHAPE
     assert fwd_call(L, prob(H=1 << 30)) == SHAPE
+    # one head's rows must stay below 2^31 bytes (32-bit buffer offsets)
+    assert fwd_call(L, prob(T=(1 << 31) // (128 * 2), D=128)) == SHAPE
+    assert L.la_workspace_bytes(ctypes.byref(prob(T=(1 << 31) // (128 * 2) - 1, D=128))) > 0
+    assert L.la_workspace_bytes(ctypes.byref(prob(T=(1 << 31) // (64 * 4), D=64, dtype=0))) == 0
     assert fwd_call(L, prob(flags=2)) == FLAGS
     assert fwd_call(L, prob(eps=-1e-3)) == EPS
     assert fwd_call(L, prob(eps=float("nan"))) == EPS
