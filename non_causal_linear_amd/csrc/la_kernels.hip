@@ -6,12 +6,15 @@
 //   S = sum_t phi(k_t) v_t^T,  z = sum_t phi(k_t),
 //   O_t = phi(q_t) S / (phi(q_t) . z + eps)     (simple_la: phi(q_t) S).
 //
-// Four kernels, one per step group of the path:
-//   fwd_state_kernel   phi(K)^T [V | 1] over a token slice on MFMA, partial
-//                      (S, z) per slice, fixed-order combine by the workgroup
-//                      that finishes the head last;
+// Kernels, by step of the path:
+//   fwd_state_w64_kernel (16-bit, D = 64) and fwd_state_kernel (the rest):
+//                      phi(K)^T [V | 1] over a token slice on MFMA, one partial
+//                      (S, z) per slice, or the state itself when a head is
+//                      one slice;
+//   combine_kernel     sums the partials of each head in ascending slice order;
 //   fwd_output_kernel  O = phi(Q) S / (phi(Q) z + eps), S and z as MFMA operands;
-//   bwd_dq_kernel      dQ, plus partial dS = phi(Q)^T (dO / den) on MFMA and
+//   bwd_dq_w64_kernel (16-bit, D = 64) and bwd_dq_kernel (the rest): dQ, plus
+//                      partial dS = phi(Q)^T (dO / den) on MFMA and
 //                      dz = sum_t c_t phi(q_t), combined like the forward state;
 //   bwd_dkv_kernel     dK = (V dS^T + dz) * phi'(K), dV = phi(K) dS.
 //
