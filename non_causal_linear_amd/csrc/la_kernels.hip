@@ -133,6 +133,14 @@ __device__ __forceinline__ float phi(float x) {
     return x > 0.f ? x + 1.f : e;
 }
 
+// The exponential branch of phi (and of phi' = 1 for x > 0, e^x otherwise),
+// for kernels that need both: x > 0 then selects x + 1 or 1.
+template <typename T>
+__device__ __forceinline__ float phi_exp(float x) {
+    if constexpr (std::is_same<T, float>::value) return expf(x);
+    else return __builtin_amdgcn_exp2f(x * 1.4426950408889634f);
+}
+
 template <typename T>
 __device__ __forceinline__ float to_f32(T x) { return static_cast<float>(x); }
 
@@ -163,6 +171,37 @@ __device__ __forceinline__ HeadBuf head_buf(const T* base, int64_t bh, int64_t T
     return HeadBuf{__builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(p), 0, (int)(T_ * D * (int64_t)sizeof(T)),
                                                      0x00020000)};
 }
+// Descriptor over rows [r0, r1) of one head only: rows are then counted from
+// r0, and loads past r1 read zeros even where the head continues.
+template <typename T>
+__device__ __forceinline__ HeadBuf slice_buf(const T* base, int64_t bh, int64_t T_, int D, int64_t r0,
+                                             int64_t r1) {
+    const T* p = base + (bh * T_ + r0) * D;
+    return HeadBuf{__builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(p), 0,
+                                                     (int)((r1 - r0) * D * (int64_t)sizeof(T)), 0x00020000)};
+}
+// The order in which a workgroup visits the n blocks of its slice, n padded
+// up to a multiple of `group`: rotated by a per-workgroup multiple of `group`.
+// Workgroups stream their slices side by side at the same pace; unrotated,
+// they would all be at the same offset of slices whose bases are a fixed
+// stride apart, and whether those simultaneous accesses pile onto the same
+// DRAM channels would depend on where the buffers sit in physical memory.
+// Indices at or past the padded count map past the slice end, where the
+// slice's buffer descriptors read zeros and drop stores.
+struct Rotation {
+    int npad, R;
+    __device__ Rotation(int n, int group, int wid) {
+        npad = (n + group - 1) / group * group;
+        const int nr = npad / group;
+        R = nr > 0 ? group * ((wid * 7) % nr) : 0;
+    }
+    __device__ int operator()(int blk) const {
+        if (blk >= npad) return npad + blk;
+        const int x = blk + R;
+        return x >= npad ? x - npad : x;
+    }
+};
+
 __device__ __forceinline__ uint4 buf_load16(const HeadBuf& b, int byte_off) {
     const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(b.rsrc, byte_off, 0, 0);
     return make_uint4(v.x, v.y, v.z, v.w);
@@ -530,13 +569,17 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_state_w64_kernel(
     struct Stage {
         uint4 k[4], v[4];
     };
-    // Slices are multiples of 4 steps, so a step never straddles a slice end
-    // before T; rows past T load as zeros, and phi(k) is masked for them.
-    const HeadBuf bk = head_buf(k, bh, T_, D), bv = head_buf(v, bh, T_, D);
+    // Rows are counted from t0; rows past the slice end load as zeros and
+    // phi(k) is masked for them. Steps go in rotated order, two per wave and
+    // turn, with no early exit (an exit makes the compiler wait for every
+    // load in flight where the paths join).
+    const HeadBuf bk = slice_buf(k, bh, T_, D, t0, t1), bv = slice_buf(v, bh, T_, D, t0, t1);
+    const Rotation rot(nsteps, 2 * kWaves, wid);
     auto issue = [&](Stage& st, int step) {
+        const int ps = rot(step);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int off = (int)((t0 + (int64_t)step * STEP + rg + 8 * r) * D + 8 * c) * (int)sizeof(T);
+            const int off = (int)(((int64_t)ps * STEP + rg + 8 * r) * D + 8 * c) * (int)sizeof(T);
             st.k[r] = buf_load16(bk, off);
             st.v[r] = buf_load16(bv, off);
         }
@@ -546,7 +589,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_state_w64_kernel(
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int row = rg + 8 * r;
-            const bool ok = t0 + (int64_t)step * STEP + row < t1;
+            const bool ok = (int64_t)rot(step) * STEP + row < t1 - t0;
             const T* ke = reinterpret_cast<const T*>(&st.k[r]);
             Row<T, 8> kt;
 #pragma unroll
@@ -582,13 +625,12 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_state_w64_kernel(
         sched_fence();
         issue(s1, wave + kWaves);
         sched_fence();
-        for (int st = wave; st < nsteps; st += 2 * kWaves) {
+        for (int st = wave; st < rot.npad; st += 2 * kWaves) {
             consume(s0, st);
             sched_fence();
             issue(s0, st + 2 * kWaves);
             sched_fence();
             mma_step();
-            if (st + kWaves >= nsteps) break;
             consume(s1, st + kWaves);
             sched_fence();
             issue(s1, st + 3 * kWaves);
@@ -757,17 +799,19 @@ __global__ __launch_bounds__(kThreads) void fwd_output_kernel(
     const float uS = ldexpf(1.f, -sS), uz = ldexpf(1.f, -sz);
 
     // Each wave takes blocks of 16 U tokens, kWaves blocks apart, with the
-    // loads of its next two blocks in flight while it computes one.
-    const int64_t stride = 16 * U * kWaves;
-    // Chunk lengths are multiples of a wave block, so a block never straddles
-    // a chunk boundary; rows past T load as zeros and their stores are dropped.
-    const HeadBuf bq = head_buf(q, bh, T_, D), bo = head_buf(o, bh, T_, D);
+    // loads of its next two blocks in flight while it computes one. Blocks go
+    // in rotated order, two per turn with no early exit; rows are counted from
+    // c0, rows past the chunk end load as zeros and their stores are dropped.
+    constexpr int BT = 16 * U;
+    const HeadBuf bq = slice_buf(q, bh, T_, D, c0, c1), bo = slice_buf(o, bh, T_, D, c0, c1);
+    const Rotation rot((int)((c1 - c0 + BT - 1) / BT), 2 * kWaves, wid);
     T* stg = stage + wave * 16 * LDR;
-    auto issue = [&](Row<T, F> (&b)[U], int64_t bs) {
+    auto issue = [&](Row<T, F> (&b)[U], int blk) {
+        const int64_t bs = (int64_t)rot(blk) * BT;
 #pragma unroll
         for (int u = 0; u < U; ++u) load_row_buf<T, F>(b[u], bq, bs + 16 * u + m, D, F * grp);
     };
-    auto body = [&](Row<T, F> (&qr)[U], int64_t base) {
+    auto body = [&](Row<T, F> (&qr)[U], int blk) {
         Frag<T> bq[U][KS];
 #pragma unroll
         for (int u = 0; u < U; ++u)
@@ -777,7 +821,7 @@ __global__ __launch_bounds__(kThreads) void fwd_output_kernel(
                 for (int e = 0; e < 8; ++e)
                     bq[u][s][e] = static_cast<T>(phi<T>(to_f32(qr[u].e[8 * s + e])));
         sched_fence();
-        issue(qr, base + 2 * stride);
+        issue(qr, blk + 2 * kWaves);
         sched_fence();
         f32x4 acc[U][NB], accd[U];
 #pragma unroll
@@ -818,19 +862,17 @@ __global__ __launch_bounds__(kThreads) void fwd_output_kernel(
 #pragma unroll
                     for (int r = 0; r < 4; ++r) out.e[4 * b + r] = static_cast<T>(acc[u][b][r] * inv);
             }
-            store_tile_rows<T, D>(stg, out, bo, base + 16 * u);
+            store_tile_rows<T, D>(stg, out, bo, (int64_t)rot(blk) * BT + 16 * u);
         }
     };
     Row<T, F> b0[U], b1[U];
-    const int64_t first = c0 + wave * 16 * U;
-    issue(b0, first);
+    issue(b0, wave);
     sched_fence();
-    issue(b1, first + stride);
+    issue(b1, wave + kWaves);
     sched_fence();
-    for (int64_t base = first; base < c1; base += 2 * stride) {
-        body(b0, base);
-        if (base + stride >= c1) break;
-        body(b1, base + stride);
+    for (int blk = wave; blk < rot.npad; blk += 2 * kWaves) {
+        body(b0, blk);
+        body(b1, blk + kWaves);
     }
 }
 
@@ -1045,6 +1087,10 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(
 
 // Steps 5-6 for 16-bit inputs at D = 64, per wave: each wave walks its own
 // 16-token steps (w, w + 4, ...) with two steps of Q and dO loads in flight.
+// The loop takes two steps per turn with no early exit (an exit makes the
+// compiler wait for every load in flight where the paths join): the slice's
+// buffer descriptors read steps past the slice end as zeros, which add
+// nothing, and drop their dQ stores.
 // Per step it computes u = S dO_t, den and dQ as the workgroup kernel above.
 // For the reduction over tokens it writes A_t = phi(q_t) 2^sw / den_t and the
 // raw dO_t row-major into its own LDS area, plus one more column
@@ -1054,13 +1100,19 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(
 // (c_t phi(q_t) = (-r_t / den_t)(phi(q_t) / den_t)), so dS and dz share one
 // operand and need no per-element work beyond the scaling of phi(q). Each
 // wave holds its own 64 x 65 sums; waves are combined in a fixed order.
+struct BwdQW64 {
+    static constexpr int kStep = 16;   // tokens per wave step
+    static constexpr int kStages = 2;  // steps of loads in flight per wave
+    static constexpr int kRound = kStep * kWaves;
+};
+
 template <typename T, bool SIMPLE>
 __global__ __launch_bounds__(kThreads, 2) void bwd_dq_w64_kernel(
     const T* __restrict__ q, const T* __restrict__ dout, const float* __restrict__ stS,
     const float* __restrict__ stz, T* __restrict__ dq, float* __restrict__ part,
     float* __restrict__ dS_out, float* __restrict__ dz_out, int64_t T_, int PB,
     int64_t LB, float eps) {
-    constexpr int D = 64, F = 16, NB = 4, KS = 2, STEP = 16, E = D * D + D;
+    constexpr int D = 64, F = 16, NB = 4, KS = 2, STEP = BwdQW64::kStep, E = D * D + D;
     constexpr int LDR = 88;                   // 176-byte rows: 64 features + the beta column block
     constexpr int NJ = NB + (SIMPLE ? 0 : 1);  // dS column blocks (+ dz)
     constexpr int NFS = NB * KS;
@@ -1120,38 +1172,50 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_w64_kernel(
 #pragma unroll
         for (int j = 0; j < NJ; ++j) dsacc[b][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+    // A stage holds the loaded words as they are; unpacked at the load, the
+    // halves would be carried around the loop and unpacking them would wait
+    // for the loads right after they are issued.
     struct Stage {
-        Row<T, F> q, d;
+        u32x4 q[2], d[2];
     };
-    // Slices are multiples of 4 steps, so a step never straddles a slice end
-    // before T; rows past T load as zeros (dO = 0 gives u = 0, r = 0, beta = 0,
-    // so such rows add nothing to dS or dz) and their dQ stores are dropped.
-    const HeadBuf bq = head_buf(q, bh, T_, D), bd = head_buf(dout, bh, T_, D), bdq = head_buf(dq, bh, T_, D);
+    // Rows past the slice end load as zeros (dO = 0 gives u = 0, r = 0,
+    // beta = 0, so such rows add nothing to dS or dz) and their dQ stores are
+    // dropped. Rows are counted from t0.
+    const HeadBuf bq = slice_buf(q, bh, T_, D, t0, t1), bd = slice_buf(dout, bh, T_, D, t0, t1),
+                  bdq = slice_buf(dq, bh, T_, D, t0, t1);
+    const Rotation rot(nsteps, BwdQW64::kStages * kWaves, wid);
     auto issue = [&](Stage& st, int step) {
-        const int64_t t = t0 + (int64_t)step * STEP + m;
-        load_row_buf<T, F>(st.q, bq, t, D, F * grp);
-        load_row_buf<T, F>(st.d, bd, t, D, F * grp);
+        const int off = (int)(((int64_t)rot(step) * STEP + m) * D + F * grp) * (int)sizeof(T);
+        st.q[0] = __builtin_amdgcn_raw_buffer_load_b128(bq.rsrc, off, 0, 0);
+        st.q[1] = __builtin_amdgcn_raw_buffer_load_b128(bq.rsrc, off + 16, 0, 0);
+        st.d[0] = __builtin_amdgcn_raw_buffer_load_b128(bd.rsrc, off, 0, 0);
+        st.d[1] = __builtin_amdgcn_raw_buffer_load_b128(bd.rsrc, off + 16, 0, 0);
     };
     const int rA = 4 * grp + (m >> 2), cA = 4 * (m & 3);
     auto body = [&](Stage& st, int step) {
-        float qt[F];
+        sched_fence();  // keeps this stage's unpacking out of the previous step
+        Row<T, F> lq;
+        __builtin_memcpy(lq.e, st.q, sizeof(lq));
+        float qt[F], dph[F];
         Frag<T> bq[KS], bd[KS];
 #pragma unroll
-        for (int o = 0; o < F; ++o) qt[o] = phi<T>(to_f32(st.q.e[o]));
+        for (int o = 0; o < F; ++o) {
+            const float x = to_f32(lq.e[o]);
+            const float e = phi_exp<T>(x);
+            qt[o] = x > 0.f ? x + 1.f : e;  // phi
+            dph[o] = x > 0.f ? 1.f : e;     // phi'
+        }
 #pragma unroll
-        for (int s = 0; s < KS; ++s)
+        for (int s = 0; s < KS; ++s) {
+            if constexpr (!SIMPLE)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                if constexpr (!SIMPLE) bq[s][e] = static_cast<T>(qt[8 * s + e]);
-                bd[s][e] = st.d.e[8 * s + e];
-            }
+                for (int e = 0; e < 8; ++e) bq[s][e] = static_cast<T>(qt[8 * s + e]);
+            bd[s] = __builtin_bit_cast(Frag<T>, st.d[s]);
+        }
         // dO rows go to LDS as loaded
-        uint4* dw4 = reinterpret_cast<uint4*>(&sW[m * LDR + F * grp]);
-        dw4[0] = reinterpret_cast<const uint4*>(st.d.e)[0];
-        dw4[1] = reinterpret_cast<const uint4*>(st.d.e)[1];
-        sched_fence();
-        issue(st, step + 2 * kWaves);  // this stage's registers are free again
-        sched_fence();
+        u32x4* dw4 = reinterpret_cast<u32x4*>(&sW[m * LDR + F * grp]);
+        dw4[0] = st.d[0];
+        dw4[1] = st.d[1];
         f32x4 au[NB];
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
@@ -1159,6 +1223,12 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_w64_kernel(
 #pragma unroll
             for (int s = 0; s < KS; ++s) au[b] = mma(sA[(b * KS + s) * 64 + lane], bd[s], au[b]);
         }
+        // The stage's registers are free once the u products have read dO, so
+        // the next load lands in the same registers and nothing is copied (and
+        // waited for) where the loop closes.
+        sched_fence();
+        issue(st, step + BwdQW64::kStages * kWaves);
+        sched_fence();
         float dqt[F];
         float aq = 1.f;  // factor on phi(q) in the reduction operand
         if constexpr (SIMPLE) {
@@ -1198,8 +1268,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_w64_kernel(
         {
             Row<T, F> out;
 #pragma unroll
-            for (int o = 0; o < F; ++o) out.e[o] = static_cast<T>(dqt[o] * fminf(qt[o], 1.f));  // phi' = min(phi, 1)
-            store_tile_rows<T, D>(sO, out, bdq, t0 + (int64_t)step * STEP);
+            for (int o = 0; o < F; ++o) out.e[o] = static_cast<T>(dqt[o] * dph[o]);
+            store_tile_rows<T, D>(sO, out, bdq, (int64_t)rot(step) * STEP);
         }
         wave_lds_sync();
         i16x4 a[NB];
@@ -1215,15 +1285,16 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_w64_kernel(
     };
 
     if (nsteps > 0) {
-        Stage s0, s1;
-        issue(s0, wave);
-        sched_fence();
-        issue(s1, wave + kWaves);
-        sched_fence();
-        for (int st = wave; st < nsteps; st += 2 * kWaves) {
-            body(s0, st);
-            if (st + kWaves >= nsteps) break;
-            body(s1, st + kWaves);
+        constexpr int kStages = BwdQW64::kStages;
+        Stage stg[kStages];
+#pragma unroll
+        for (int i = 0; i < kStages; ++i) {
+            issue(stg[i], wave + i * kWaves);
+            sched_fence();
+        }
+        for (int st = wave; st < rot.npad; st += kStages * kWaves) {
+#pragma unroll
+            for (int i = 0; i < kStages; ++i) body(stg[i], st + i * kWaves);
         }
     }
 
@@ -1330,44 +1401,57 @@ __global__ __launch_bounds__(kThreads) void bwd_dkv_kernel(
     for (int o = 0; o < F; ++o) dzl[o] = SIMPLE ? 0.f : dz[F * grp + o];
     __syncthreads();
 
-    const int64_t stride = 16 * U * kWaves;
-    // as in the output kernel: blocks never straddle a chunk boundary, rows
-    // past T load as zeros and their stores are dropped
-    const HeadBuf bk = head_buf(k, bh, T_, D), bv_ = head_buf(v, bh, T_, D);
-    const HeadBuf bdk = head_buf(dk, bh, T_, D), bdv = head_buf(dv, bh, T_, D);
+    // Rows are counted from c0. The loop takes two blocks per turn with no
+    // early exit (an exit makes the compiler wait for every load in flight
+    // where the paths join): the chunk's buffer descriptors read rows past its
+    // end as zeros and drop their stores.
+    const HeadBuf bk = slice_buf(k, bh, T_, D, c0, c1), bv_ = slice_buf(v, bh, T_, D, c0, c1);
+    const HeadBuf bdk = slice_buf(dk, bh, T_, D, c0, c1), bdv = slice_buf(dv, bh, T_, D, c0, c1);
     T* stg = stage + (kStage ? wave * 16 * LDR : 0);
+    // The loaded words as they are (see the dQ kernel).
+    constexpr int NW = F * (int)sizeof(T) / 16;
     struct Stage {
-        Row<T, F> k[U], v[U];
+        u32x4 k[U][NW], v[U][NW];
     };
-    auto issue = [&](Stage& st, int64_t bs) {
+    const Rotation rot((int)((c1 - c0 + 16 * U - 1) / (16 * U)), 2 * kWaves, wid);
+    auto issue = [&](Stage& st, int blk) {
+        const int64_t bs = (int64_t)rot(blk) * 16 * U;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            load_row_buf<T, F>(st.k[u], bk, bs + 16 * u + m, D, F * grp);
-            load_row_buf<T, F>(st.v[u], bv_, bs + 16 * u + m, D, F * grp);
+            const int off = (int)((bs + 16 * u + m) * D + F * grp) * (int)sizeof(T);
+#pragma unroll
+            for (int i = 0; i < NW; ++i) {
+                st.k[u][i] = __builtin_amdgcn_raw_buffer_load_b128(bk.rsrc, off + 16 * i, 0, 0);
+                st.v[u][i] = __builtin_amdgcn_raw_buffer_load_b128(bv_.rsrc, off + 16 * i, 0, 0);
+            }
         }
     };
-    auto body = [&](Stage& st, int64_t base) {
+    auto body = [&](Stage& st, int blk) {
+        const int64_t base = (int64_t)rot(blk) * 16 * U;
+        sched_fence();
         float dphik[U][F];
         Frag<T> bk[U][KS], bv[U][KS];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
+            Row<T, F> lk, lv;
+            __builtin_memcpy(lk.e, st.k[u], sizeof(lk));
+            __builtin_memcpy(lv.e, st.v[u], sizeof(lv));
             float kt[F];
 #pragma unroll
             for (int o = 0; o < F; ++o) {
-                kt[o] = phi<T>(to_f32(st.k[u].e[o]));
-                dphik[u][o] = fminf(kt[o], 1.f);  // phi' = min(phi, 1)
+                const float x = to_f32(lk.e[o]);
+                const float e = phi_exp<T>(x);
+                kt[o] = x > 0.f ? x + 1.f : e;         // phi
+                dphik[u][o] = x > 0.f ? 1.f : e;       // phi'
             }
 #pragma unroll
             for (int s = 0; s < KS; ++s)
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     bk[u][s][e] = static_cast<T>(kt[8 * s + e]);
-                    bv[u][s][e] = st.v[u].e[8 * s + e];
+                    bv[u][s][e] = lv.e[8 * s + e];
                 }
         }
-        sched_fence();
-        issue(st, base + 2 * stride);
-        sched_fence();
         f32x4 ak[U][NB], av[U][NB];
 #pragma unroll
         for (int u = 0; u < U; ++u)
@@ -1388,6 +1472,10 @@ __global__ __launch_bounds__(kThreads) void bwd_dkv_kernel(
                     av[u][b] = mma(a2, bk[u][s], av[u][b]);
                 }
             }
+        // the stage's registers are free once the products have read V
+        sched_fence();
+        issue(st, blk + 2 * kWaves);
+        sched_fence();
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             Row<T, F> gk, gv;
@@ -1409,15 +1497,13 @@ __global__ __launch_bounds__(kThreads) void bwd_dkv_kernel(
         }
     };
     Stage s0, s1;
-    const int64_t first = c0 + wave * 16 * U;
-    issue(s0, first);
+    issue(s0, wave);
     sched_fence();
-    issue(s1, first + stride);
+    issue(s1, wave + kWaves);
     sched_fence();
-    for (int64_t base = first; base < c1; base += 2 * stride) {
-        body(s0, base);
-        if (base + stride >= c1) break;
-        body(s1, base + stride);
+    for (int blk = wave; blk < rot.npad; blk += 2 * kWaves) {
+        body(s0, blk);
+        body(s1, blk + kWaves);
     }
 }
 
@@ -1536,10 +1622,12 @@ SplitCfg split_config_t(int step) {
             if constexpr (kWaveKernels<T, D>) return {int64_t(StateW64::kStep) * kWaves, 512};
             else return {StateShape<T, D>::kTT, 1024};
         case kStepBwdQ:
-            if constexpr (kWaveKernels<T, D>) return {int64_t(16) * kWaves, 512};
+            if constexpr (kWaveKernels<T, D>) return {int64_t(BwdQW64::kRound) * BwdQW64::kStages, 512};
             else return {BwdQShape<T, D>::kG, 1024};
+        case kStepBwdKV:
+            return {int64_t(2) * 16 * kWaves, 1024};
         default:
-            return {StreamShape<T, D>::kG, 1024};
+            return {2 * StreamShape<T, D>::kG, 2048};
     }
 }
 
