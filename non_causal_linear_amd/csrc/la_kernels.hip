@@ -386,6 +386,64 @@ __device__ __forceinline__ void block_vector_stats(const float* __restrict__ z, 
     sum = block_sum((v.x + v.y) + (v.z + v.w), red);
 }
 
+// A D x D fp32 matrix and a D-vector staged in LDS, with their statistics.
+// The matrix rows are D + 1 floats apart, so that the fragment builders'
+// column walks (lanes 16 rows or 16 columns apart) spread over the banks.
+template <int D>
+struct StagedState {
+    static constexpr int kLD = D + 1;
+    static constexpr int kFloats = D * kLD + D;  // matrix, then the vector
+    float max_m, max_z, sum_z;
+};
+
+// Copies M and z from global memory into s (StagedState<D>::kFloats floats)
+// with all of each thread's 16-byte loads in flight at once, and reduces
+// max |M|, max |z| and sum z over the workgroup in a fixed order (xor tree per
+// wave, then waves (0 + 1) + (2 + 3)). Ends with a barrier; red holds 12
+// floats.
+template <int D>
+__device__ __forceinline__ StagedState<D> stage_state(const float* __restrict__ M,
+                                                      const float* __restrict__ z, float* s, float* red) {
+    constexpr int PER = D * D / 4 / kThreads, LD = StagedState<D>::kLD;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    float4 v[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) v[i] = reinterpret_cast<const float4*>(M)[tid + i * kThreads];
+    float4 w = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (tid < D / 4) w = reinterpret_cast<const float4*>(z)[tid];
+    float a = 0.f;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        const int e = 4 * (tid + i * kThreads), r = e / D, c = e % D;
+        float* d = s + r * LD + c;
+        d[0] = v[i].x;
+        d[1] = v[i].y;
+        d[2] = v[i].z;
+        d[3] = v[i].w;
+        a = fmaxf(a, fmaxf(fmaxf(fabsf(v[i].x), fabsf(v[i].y)), fmaxf(fabsf(v[i].z), fabsf(v[i].w))));
+    }
+    if (tid < D / 4) *reinterpret_cast<float4*>(s + D * LD + 4 * tid) = w;
+    float b = fmaxf(fmaxf(fabsf(w.x), fabsf(w.y)), fmaxf(fabsf(w.z), fabsf(w.w)));
+    float c = (w.x + w.y) + (w.z + w.w);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+        a = fmaxf(a, __shfl_xor(a, off));
+        b = fmaxf(b, __shfl_xor(b, off));
+        c += __shfl_xor(c, off);
+    }
+    if (lane == 0) {
+        red[wave] = a;
+        red[4 + wave] = b;
+        red[8 + wave] = c;
+    }
+    __syncthreads();
+    StagedState<D> st;
+    st.max_m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    st.max_z = fmaxf(fmaxf(red[4], red[5]), fmaxf(red[6], red[7]));
+    st.sum_z = (red[8] + red[9]) + (red[10] + red[11]);
+    return st;
+}
+
 // ---------------------------------------------------------------------------
 // Steps 1-3: split-T state reduction.
 // ---------------------------------------------------------------------------
@@ -531,6 +589,7 @@ __global__ __launch_bounds__(kThreads) void fwd_state_kernel(
 // added in a fixed order at the end.
 struct StateW64 {
     static constexpr int kStep = 32;  // tokens per wave step
+    static constexpr int kStages = 2; // steps of loads in flight per wave
     static constexpr int kLDR = 72;   // LDS row stride (elements): 144 B rows
     static constexpr int kTile = kStep * kLDR;
 };
@@ -574,7 +633,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_state_w64_kernel(
     // turn, with no early exit (an exit makes the compiler wait for every
     // load in flight where the paths join).
     const HeadBuf bk = slice_buf(k, bh, T_, D, t0, t1), bv = slice_buf(v, bh, T_, D, t0, t1);
-    const Rotation rot(nsteps, 2 * kWaves, wid);
+    constexpr int NS = StateW64::kStages;
+    const Rotation rot(nsteps, NS * kWaves, wid);
     auto issue = [&](Stage& st, int step) {
         const int ps = rot(step);
 #pragma unroll
@@ -619,6 +679,9 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_state_w64_kernel(
         wave_lds_sync();
     };
 
+    // (written out for two stages: a loop over a stage array compiles to
+    // register copies and shallower waits here)
+    static_assert(NS == 2, "the loop below is written for two stages");
     if (nsteps > 0) {
         Stage s0, s1;
         issue(s0, wave);
@@ -704,13 +767,16 @@ struct StreamShape {
     static constexpr int kKS = D / 32;   // 32-long contraction steps over D
     static constexpr int kU = (sizeof(T) == 2 && D == 64) ? 2 : 1;  // 16-token blocks per wave
     static constexpr int kG = kWaves * kU * 16;  // tokens per workgroup iteration
+    static constexpr int kStages = 2;            // blocks of loads in flight per wave
+    // 16-bit D = 64: four workgroups per CU (128 registers per lane)
+    static constexpr int kMinBlocks = (sizeof(T) == 2 && D == 64) ? 4 : 1;
 };
 
 // Fragment of A = M^T-like operand built from an fp32 D x D matrix M:
 //   rows m of the 16-row block b stand for index F*(m/4) + 4b + m%4,
 //   the lane group's 8 contraction values stand for F*g + 8s + e.
 // If kTransposeSource, element = M[contraction][row] else M[row][contraction].
-template <typename T, int D, bool kTransposeSource>
+template <typename T, int D, bool kTransposeSource, int LD = D>
 __device__ __forceinline__ Frag<T> build_frag(const float* __restrict__ M, int b, int s, int m, int g,
                                               float scale) {
     constexpr int F = D / 4;
@@ -719,7 +785,7 @@ __device__ __forceinline__ Frag<T> build_frag(const float* __restrict__ M, int b
     Frag<T> f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-        const float x = kTransposeSource ? M[(k0 + e) * D + row] : M[row * D + k0 + e];
+        const float x = kTransposeSource ? M[(k0 + e) * LD + row] : M[row * LD + k0 + e];
         f[e] = static_cast<T>(x * scale);
     }
     return f;
@@ -759,7 +825,7 @@ __device__ __forceinline__ void build_frags(Frag<T>* sA, Make make) {
 // with D/4 contiguous outputs of its token) and den = z . phi(q) from one more
 // MFMA block whose rows are all z.
 template <typename T, int D, bool SIMPLE>
-__global__ __launch_bounds__(kThreads) void fwd_output_kernel(
+__global__ __launch_bounds__(kThreads, (StreamShape<T, D>::kMinBlocks)) void fwd_output_kernel(
     const T* __restrict__ q, const float* __restrict__ stS, const float* __restrict__ stz,
     T* __restrict__ o, int64_t T_, int NQ, int64_t LQ, float eps) {
     using Sh = StreamShape<T, D>;
@@ -767,9 +833,15 @@ __global__ __launch_bounds__(kThreads) void fwd_output_kernel(
     constexpr int NFS = NB * KS;             // S fragments
     constexpr int NFR = NFS + (SIMPLE ? 0 : KS);  // + z fragments
     constexpr int LDR = D + 16 / (int)sizeof(T);
+    // At D = 64 the state is staged in LDS (sharing the store staging area,
+    // which the loop alone uses) and the fragments are built from there.
+    constexpr bool kStaged = (D == 64);
+    constexpr int kStoreBytes = kWaves * 16 * LDR * (int)sizeof(T);
+    constexpr int kStBytes = kStaged ? StagedState<D>::kFloats * 4 : 0;
     __shared__ Frag<T> sA[NFR * 64];
-    __shared__ __attribute__((aligned(16))) T stage[kWaves * 16 * LDR];
-    __shared__ float red[4];
+    __shared__ __attribute__((aligned(16))) unsigned char sraw[kStoreBytes > kStBytes ? kStoreBytes : kStBytes];
+    __shared__ float red[12];
+    T* stage = reinterpret_cast<T*>(sraw);
 
     const int wid = xcd_remap(blockIdx.x, gridDim.x);
     const int64_t bh = wid / NQ;
@@ -782,13 +854,26 @@ __global__ __launch_bounds__(kThreads) void fwd_output_kernel(
     const float* z = stz + bh * D;
 
     int sS = 0, sz = 0;
-    if constexpr (Elt<T>::kScaled) {
-        float mz, zsum;
-        sS = scale_exp(block_absmax_matrix<D>(S, red));
-        block_vector_stats<D>(z, red, mz, zsum);
-        sz = scale_exp(mz);
-    }
-    {
+    if constexpr (kStaged) {
+        constexpr int LD = StagedState<D>::kLD;
+        float* sSt = reinterpret_cast<float*>(sraw);
+        const StagedState<D> st = stage_state<D>(S, z, sSt, red);
+        if constexpr (Elt<T>::kScaled) {
+            sS = scale_exp(st.max_m);
+            sz = scale_exp(st.max_z);
+        }
+        const float fS = ldexpf(1.f, sS), fz = ldexpf(1.f, sz);
+        build_frags<T, NFR>(sA, [&](int f) {
+            return f < NFS ? build_frag<T, D, true, LD>(sSt, f / KS, f % KS, m, grp, fS)
+                           : build_zfrag<T, D>(sSt + D * LD, max(f - NFS, 0), grp, fz);
+        });
+    } else {
+        if constexpr (Elt<T>::kScaled) {
+            float mz, zsum;
+            sS = scale_exp(block_absmax_matrix<D>(S, red));
+            block_vector_stats<D>(z, red, mz, zsum);
+            sz = scale_exp(mz);
+        }
         const float fS = ldexpf(1.f, sS), fz = ldexpf(1.f, sz);
         build_frags<T, NFR>(sA, [&](int f) {
             return f < NFS ? build_frag<T, D, true>(S, f / KS, f % KS, m, grp, fS)
@@ -804,7 +889,8 @@ __global__ __launch_bounds__(kThreads) void fwd_output_kernel(
     // c0, rows past the chunk end load as zeros and their stores are dropped.
     constexpr int BT = 16 * U;
     const HeadBuf bq = slice_buf(q, bh, T_, D, c0, c1), bo = slice_buf(o, bh, T_, D, c0, c1);
-    const Rotation rot((int)((c1 - c0 + BT - 1) / BT), 2 * kWaves, wid);
+    constexpr int NS = Sh::kStages;
+    const Rotation rot((int)((c1 - c0 + BT - 1) / BT), NS * kWaves, wid);
     T* stg = stage + wave * 16 * LDR;
     auto issue = [&](Row<T, F> (&b)[U], int blk) {
         const int64_t bs = (int64_t)rot(blk) * BT;
@@ -821,7 +907,7 @@ __global__ __launch_bounds__(kThreads) void fwd_output_kernel(
                 for (int e = 0; e < 8; ++e)
                     bq[u][s][e] = static_cast<T>(phi<T>(to_f32(qr[u].e[8 * s + e])));
         sched_fence();
-        issue(qr, blk + 2 * kWaves);
+        issue(qr, blk + NS * kWaves);
         sched_fence();
         f32x4 acc[U][NB], accd[U];
 #pragma unroll
@@ -865,14 +951,15 @@ __global__ __launch_bounds__(kThreads) void fwd_output_kernel(
             store_tile_rows<T, D>(stg, out, bo, (int64_t)rot(blk) * BT + 16 * u);
         }
     };
-    Row<T, F> b0[U], b1[U];
-    issue(b0, wave);
-    sched_fence();
-    issue(b1, wave + kWaves);
-    sched_fence();
-    for (int blk = wave; blk < rot.npad; blk += 2 * kWaves) {
-        body(b0, blk);
-        body(b1, blk + kWaves);
+    Row<T, F> stg_q[NS][U];
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+        issue(stg_q[i], wave + i * kWaves);
+        sched_fence();
+    }
+    for (int blk = wave; blk < rot.npad; blk += NS * kWaves) {
+#pragma unroll
+        for (int i = 0; i < NS; ++i) body(stg_q[i], blk + i * kWaves);
     }
 }
 
@@ -1123,7 +1210,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_w64_kernel(
     constexpr int kLoopBytes = kFragBytes + kTileBytes;
     constexpr int kRedBytes = 2 * E * (int)sizeof(float);
     __shared__ __attribute__((aligned(16))) unsigned char smem[kLoopBytes > kRedBytes ? kLoopBytes : kRedBytes];
-    __shared__ float red4[4];
+    __shared__ float red12[12];
     __shared__ __attribute__((aligned(16))) float sZ[D];
 
     const int wid = xcd_remap(blockIdx.x, gridDim.x);
@@ -1141,28 +1228,32 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_w64_kernel(
     T* sW = sQ + STEP * LDR;
     T* sO = sW + STEP * LDR;
 
+    // The state is staged in the tile area (which the loop alone uses) and
+    // the fragments are built from there.
+    static_assert(StagedState<D>::kFloats * 4 <= kTileBytes, "state staging exceeds the tile area");
     int sS = 0, sz = 0, sw = 0;
-    if constexpr (Elt<T>::kScaled) {
-        float mz, zsum;
-        sS = scale_exp(block_absmax_matrix<D>(S, red4));
-        block_vector_stats<D>(z, red4, mz, zsum);
-        sz = scale_exp(mz);
-        if constexpr (!SIMPLE) {
-            if (zsum > 0.f && isfinite(zsum)) {
-                int e;
-                frexpf(zsum, &e);
-                sw = min(max(e - 1, -120), 120);  // 2^sw <= sum(z) < 2^(sw+1)
+    {
+        constexpr int LD = StagedState<D>::kLD;
+        float* sSt = reinterpret_cast<float*>(smem + kFragBytes);
+        const StagedState<D> st = stage_state<D>(S, z, sSt, red12);
+        if constexpr (Elt<T>::kScaled) {
+            sS = scale_exp(st.max_m);
+            sz = scale_exp(st.max_z);
+            if constexpr (!SIMPLE) {
+                if (st.sum_z > 0.f && isfinite(st.sum_z)) {
+                    int e;
+                    frexpf(st.sum_z, &e);
+                    sw = min(max(e - 1, -120), 120);  // 2^sw <= sum(z) < 2^(sw+1)
+                }
             }
         }
-    }
-    {
         const float fS = ldexpf(1.f, sS), fz = ldexpf(1.f, sz);
         build_frags<T, NFR>(sA, [&](int f) {
-            return f < NFS ? build_frag<T, D, false>(S, f / KS, f % KS, m, grp, fS)
-                           : build_zfrag<T, D>(z, max(f - NFS, 0), grp, fz);
+            return f < NFS ? build_frag<T, D, false, LD>(sSt, f / KS, f % KS, m, grp, fS)
+                           : build_zfrag<T, D>(sSt + D * LD, max(f - NFS, 0), grp, fz);
         });
+        for (int i = tid; i < D; i += kThreads) sZ[i] = sSt[D * LD + i];
     }
-    for (int i = tid; i < D; i += kThreads) sZ[i] = z[i];
     __syncthreads();
     const float uS = ldexpf(1.f, -sS), uz = ldexpf(1.f, -sz), fw = ldexpf(1.f, sw);
 
@@ -1362,7 +1453,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_w64_kernel(
 // fixed D x D matrix with a token's row, so each is one set of MFMA blocks with
 // dS (or dS^T) as the A operand and the loaded K/V quarter rows as B.
 template <typename T, int D, bool SIMPLE>
-__global__ __launch_bounds__(kThreads) void bwd_dkv_kernel(
+__global__ __launch_bounds__(kThreads, (StreamShape<T, D>::kMinBlocks)) void bwd_dkv_kernel(
     const T* __restrict__ k, const T* __restrict__ v, const float* __restrict__ dSg,
     const float* __restrict__ dzg, T* __restrict__ dk, T* __restrict__ dv, int64_t T_, int NK,
     int64_t LK) {
@@ -1373,9 +1464,16 @@ __global__ __launch_bounds__(kThreads) void bwd_dkv_kernel(
     constexpr int LDR = D + 16 / (int)sizeof(T);
     // fp32 at D = 128: the fragments fill the LDS, stores go out per lane
     constexpr bool kStage = !(sizeof(T) == 4 && D == 128);
+    // At D = 64 the backward state is staged in LDS (sharing the store
+    // staging area, which the loop alone uses) and the fragments are built
+    // from there.
+    constexpr bool kStaged = (D == 64);
+    constexpr int kStoreBytes = kStage ? kWaves * 16 * LDR * (int)sizeof(T) : 16;
+    constexpr int kStBytes = kStaged ? StagedState<D>::kFloats * 4 : 0;
     __shared__ Frag<T> sA[2 * NFS * 64];
-    __shared__ __attribute__((aligned(16))) T stage[kStage ? kWaves * 16 * LDR : 8];
-    __shared__ float red[4];
+    __shared__ __attribute__((aligned(16))) unsigned char sraw[kStoreBytes > kStBytes ? kStoreBytes : kStBytes];
+    __shared__ float red[12];
+    T* stage = reinterpret_cast<T*>(sraw);
 
     const int wid = xcd_remap(blockIdx.x, gridDim.x);
     const int64_t bh = wid / NK;
@@ -1387,18 +1485,33 @@ __global__ __launch_bounds__(kThreads) void bwd_dkv_kernel(
     const float* dS = dSg + bh * D * D;
     const float* dz = dzg + bh * D;
 
-    int sD = 0;
-    if constexpr (Elt<T>::kScaled) sD = scale_exp(block_absmax_matrix<D>(dS, red));
-    const float fD = ldexpf(1.f, sD), uD = ldexpf(1.f, -sD);
     // fragments [0, NFS): dK side, rows i, contraction j -> dS[i][j];
     // [NFS, 2 NFS): dV side, rows j, contraction i -> dS[i][j]
-    build_frags<T, 2 * NFS>(sA, [&](int f) {
-        return f < NFS ? build_frag<T, D, false>(dS, f / KS, f % KS, m, grp, fD)
-                       : build_frag<T, D, true>(dS, (f - NFS) / KS, (f - NFS) % KS, m, grp, fD);
-    });
+    int sD = 0;
     float dzl[F];
+    if constexpr (kStaged) {
+        constexpr int LD = StagedState<D>::kLD;
+        float* sSt = reinterpret_cast<float*>(sraw);
+        const StagedState<D> st = stage_state<D>(dS, dz, sSt, red);
+        if constexpr (Elt<T>::kScaled) sD = scale_exp(st.max_m);
+        const float fD = ldexpf(1.f, sD);
+        build_frags<T, 2 * NFS>(sA, [&](int f) {
+            return f < NFS ? build_frag<T, D, false, LD>(sSt, f / KS, f % KS, m, grp, fD)
+                           : build_frag<T, D, true, LD>(sSt, (f - NFS) / KS, (f - NFS) % KS, m, grp, fD);
+        });
 #pragma unroll
-    for (int o = 0; o < F; ++o) dzl[o] = SIMPLE ? 0.f : dz[F * grp + o];
+        for (int o = 0; o < F; ++o) dzl[o] = SIMPLE ? 0.f : sSt[D * LD + F * grp + o];
+    } else {
+        if constexpr (Elt<T>::kScaled) sD = scale_exp(block_absmax_matrix<D>(dS, red));
+        const float fD = ldexpf(1.f, sD);
+        build_frags<T, 2 * NFS>(sA, [&](int f) {
+            return f < NFS ? build_frag<T, D, false>(dS, f / KS, f % KS, m, grp, fD)
+                           : build_frag<T, D, true>(dS, (f - NFS) / KS, (f - NFS) % KS, m, grp, fD);
+        });
+#pragma unroll
+        for (int o = 0; o < F; ++o) dzl[o] = SIMPLE ? 0.f : dz[F * grp + o];
+    }
+    const float uD = ldexpf(1.f, -sD);
     __syncthreads();
 
     // Rows are counted from c0. The loop takes two blocks per turn with no
@@ -1413,7 +1526,8 @@ __global__ __launch_bounds__(kThreads) void bwd_dkv_kernel(
     struct Stage {
         u32x4 k[U][NW], v[U][NW];
     };
-    const Rotation rot((int)((c1 - c0 + 16 * U - 1) / (16 * U)), 2 * kWaves, wid);
+    constexpr int NS = Sh::kStages;
+    const Rotation rot((int)((c1 - c0 + 16 * U - 1) / (16 * U)), NS * kWaves, wid);
     auto issue = [&](Stage& st, int blk) {
         const int64_t bs = (int64_t)rot(blk) * 16 * U;
 #pragma unroll
@@ -1474,7 +1588,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dkv_kernel(
             }
         // the stage's registers are free once the products have read V
         sched_fence();
-        issue(st, blk + 2 * kWaves);
+        issue(st, blk + NS * kWaves);
         sched_fence();
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -1496,14 +1610,15 @@ __global__ __launch_bounds__(kThreads) void bwd_dkv_kernel(
             }
         }
     };
-    Stage s0, s1;
-    issue(s0, wave);
-    sched_fence();
-    issue(s1, wave + kWaves);
-    sched_fence();
-    for (int blk = wave; blk < rot.npad; blk += 2 * kWaves) {
-        body(s0, blk);
-        body(s1, blk + kWaves);
+    Stage stq[NS];
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+        issue(stq[i], wave + i * kWaves);
+        sched_fence();
+    }
+    for (int blk = wave; blk < rot.npad; blk += NS * kWaves) {
+#pragma unroll
+        for (int i = 0; i < NS; ++i) body(stq[i], blk + i * kWaves);
     }
 }
 
@@ -1619,15 +1734,15 @@ template <typename T, int D>
 SplitCfg split_config_t(int step) {
     switch (step) {
         case kStepState:
-            if constexpr (kWaveKernels<T, D>) return {int64_t(StateW64::kStep) * kWaves, 512};
+            if constexpr (kWaveKernels<T, D>) return {int64_t(StateW64::kStep) * kWaves * StateW64::kStages, 512};
             else return {StateShape<T, D>::kTT, 1024};
         case kStepBwdQ:
             if constexpr (kWaveKernels<T, D>) return {int64_t(BwdQW64::kRound) * BwdQW64::kStages, 512};
             else return {BwdQShape<T, D>::kG, 1024};
         case kStepBwdKV:
-            return {int64_t(2) * 16 * kWaves, 1024};
+            return {int64_t(StreamShape<T, D>::kStages) * 16 * kWaves, 1024};
         default:
-            return {2 * StreamShape<T, D>::kG, 2048};
+            return {StreamShape<T, D>::kStages * StreamShape<T, D>::kG, 2048};
     }
 }
 
