@@ -757,6 +757,155 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_state_w64_kernel(
     }
 }
 
+// Steps 1-3 for 16-bit inputs at D = 128, where one wave cannot hold all of
+// S. The four waves share 64-token tiles: every thread loads its part of a
+// tile (full 256-byte rows per wave instruction), applies phi to K and writes
+// both tiles row-major to LDS; after one barrier each wave reduces the tile
+// into its own 32 rows of S, and of z through an all-ones B block, with
+// 16x16x32 MFMAs on transposed LDS reads. Tiles alternate between two LDS
+// buffers, so the one barrier per tile orders both that tile's writes before
+// its reads and the earlier reads of the other buffer before it is written
+// again. Two tiles of loads are in flight; tiles go in rotated order with no
+// early exit, and rows past the slice end load as zeros with phi(k) masked.
+struct StateC128 {
+    static constexpr int kTile = 64;   // tokens per tile
+    static constexpr int kLDR = 144;   // LDS row stride (elements): 288-byte rows
+    static constexpr int kStages = 2;  // tiles of loads in flight
+};
+
+template <typename T>
+__global__ __launch_bounds__(kThreads, 2) void fwd_state_c128_kernel(
+    const T* __restrict__ k, const T* __restrict__ v, float* __restrict__ stS,
+    float* __restrict__ stz, float* __restrict__ part, int64_t T_, int P,
+    int64_t L) {
+    constexpr int D = 128, NB = D / 16, NI = NB / kWaves, TT = StateC128::kTile, LDR = StateC128::kLDR;
+    constexpr int CPR = D * (int)sizeof(T) / 16;  // 16-byte chunks per row
+    constexpr int RPP = kThreads / CPR;           // rows per pass of the workgroup
+    constexpr int CPT = TT / RPP;                 // chunks per thread per tensor and tile
+    constexpr int BUF = TT * LDR;
+    static_assert(StateC128::kStages == 2, "the loop below is written for two stages");
+    __shared__ __attribute__((aligned(16))) T sK[2 * BUF];
+    __shared__ __attribute__((aligned(16))) T sV[2 * BUF];
+
+    const int wid = xcd_remap(blockIdx.x, gridDim.x);
+    const int64_t bh = wid / P;
+    const int p = wid % P;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int m = lane & 15, grp = lane >> 4;
+    const int c = tid % CPR, r0 = tid / CPR;
+    const int64_t t0 = (int64_t)p * L;
+    const int64_t t1 = min(t0 + L, T_);
+    const int64_t len = t1 - t0;
+    const int ntiles = (int)(len > 0 ? (len + TT - 1) / TT : 0);
+
+    f32x4 acc[NI][NB + 1];
+#pragma unroll
+    for (int ii = 0; ii < NI; ++ii)
+#pragma unroll
+        for (int j = 0; j <= NB; ++j) acc[ii][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    Frag<T> ones;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ones[e] = static_cast<T>(1.f);
+
+    struct Stage {
+        u32x4 k[CPT], v[CPT];
+    };
+    const HeadBuf bk = slice_buf(k, bh, T_, D, t0, t1), bv = slice_buf(v, bh, T_, D, t0, t1);
+    const Rotation rot(ntiles, StateC128::kStages, wid);
+    auto issue = [&](Stage& st, int tile) {
+        const int row0 = rot(tile) * TT;
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) {
+            const int off = (row0 + r0 + RPP * i) * D * (int)sizeof(T) + 16 * c;
+            st.k[i] = __builtin_amdgcn_raw_buffer_load_b128(bk.rsrc, off, 0, 0);
+            st.v[i] = __builtin_amdgcn_raw_buffer_load_b128(bv.rsrc, off, 0, 0);
+        }
+    };
+    auto consume = [&](const Stage& st, int tile, int buf) {
+        const int64_t row0 = (int64_t)rot(tile) * TT;
+        T* dK = sK + buf * BUF;
+        T* dV = sV + buf * BUF;
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) {
+            const int row = r0 + RPP * i;
+            const bool ok = row0 + row < len;
+            Row<T, 8> kin, kt;
+            __builtin_memcpy(kin.e, &st.k[i], sizeof(kin));
+#pragma unroll
+            for (int e = 0; e < 8; ++e) kt.e[e] = ok ? static_cast<T>(phi<T>(to_f32(kin.e[e]))) : static_cast<T>(0.f);
+            *reinterpret_cast<Row<T, 8>*>(&dK[row * LDR + 8 * c]) = kt;
+            *reinterpret_cast<u32x4*>(&dV[row * LDR + 8 * c]) = st.v[i];
+        }
+    };
+    const int rA = 8 * grp + (m >> 2), cA = 4 * (m & 3);
+    auto mma_tile = [&](int buf) {
+        const T* K_ = sK + buf * BUF;
+        const T* V_ = sV + buf * BUF;
+#pragma unroll
+        for (int ks = 0; ks < TT / 32; ++ks) {
+            const int rb = 32 * ks + rA;
+            Frag<T> a[NI];
+#pragma unroll
+            for (int ii = 0; ii < NI; ++ii) {
+                const int col = 16 * (wave * NI + ii) + cA;
+                a[ii] = join_frag<T>(lds_read_tr(&K_[rb * LDR + col]), lds_read_tr(&K_[(rb + 4) * LDR + col]));
+            }
+#pragma unroll
+            for (int j = 0; j < NB; ++j) {
+                const Frag<T> b = join_frag<T>(lds_read_tr(&V_[rb * LDR + 16 * j + cA]),
+                                               lds_read_tr(&V_[(rb + 4) * LDR + 16 * j + cA]));
+#pragma unroll
+                for (int ii = 0; ii < NI; ++ii) acc[ii][j] = mma(a[ii], b, acc[ii][j]);
+            }
+#pragma unroll
+            for (int ii = 0; ii < NI; ++ii) acc[ii][NB] = mma(a[ii], ones, acc[ii][NB]);
+        }
+    };
+
+    if (ntiles > 0) {
+        Stage s0, s1;
+        issue(s0, 0);
+        sched_fence();
+        issue(s1, 1);
+        sched_fence();
+        for (int it = 0; it < rot.npad; it += 2) {
+            consume(s0, it, 0);
+            sched_fence();
+            issue(s0, it + 2);
+            sched_fence();
+            __syncthreads();
+            mma_tile(0);
+            consume(s1, it + 1, 1);
+            sched_fence();
+            issue(s1, it + 3);
+            sched_fence();
+            __syncthreads();
+            mma_tile(1);
+        }
+    }
+
+    float* oS;
+    float* oz;
+    if (P == 1) {
+        oS = stS + bh * D * D;
+        oz = stz + bh * D;
+    } else {
+        oS = part + (bh * P + p) * (int64_t)(D * D + D);
+        oz = oS + D * D;
+    }
+#pragma unroll
+    for (int ii = 0; ii < NI; ++ii) {
+        const int i0 = (wave * NI + ii) * 16 + 4 * grp;
+#pragma unroll
+        for (int j = 0; j < NB; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) oS[(i0 + r) * D + j * 16 + m] = acc[ii][j][r];
+        if (m == 0)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) oz[i0 + r] = acc[ii][NB][r];
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Shared shape of the streaming kernels (output, bwd Q side, bwd K/V side).
 // ---------------------------------------------------------------------------
@@ -1627,6 +1776,8 @@ __global__ __launch_bounds__(kThreads, (StreamShape<T, D>::kMinBlocks)) void bwd
 // ---------------------------------------------------------------------------
 template <typename T, int D>
 constexpr bool kWaveKernels = (sizeof(T) == 2 && D == 64);
+template <typename T, int D>
+constexpr bool kTileKernels = (sizeof(T) == 2 && D == 128);
 
 // After a split reduction (P > 1 slices per head), sum the partials.
 template <int D>
@@ -1647,6 +1798,10 @@ hipError_t fwd_state_t(const Plan& p, const void* k, const void* v, float* state
     float* part = reinterpret_cast<float*>(w + p.off_part);
     if constexpr (kWaveKernels<T, D>)
         hipLaunchKernelGGL((fwd_state_w64_kernel<T>), dim3((unsigned)nblk), dim3(kThreads), 0, s,
+                           static_cast<const T*>(k), static_cast<const T*>(v), state,
+                           state + p.BH * D * D, part, p.T, p.P, p.L);
+    else if constexpr (kTileKernels<T, D>)
+        hipLaunchKernelGGL((fwd_state_c128_kernel<T>), dim3((unsigned)nblk), dim3(kThreads), 0, s,
                            static_cast<const T*>(k), static_cast<const T*>(v), state,
                            state + p.BH * D * D, part, p.T, p.P, p.L);
     else
@@ -1735,6 +1890,7 @@ SplitCfg split_config_t(int step) {
     switch (step) {
         case kStepState:
             if constexpr (kWaveKernels<T, D>) return {int64_t(StateW64::kStep) * kWaves * StateW64::kStages, 512};
+            else if constexpr (kTileKernels<T, D>) return {int64_t(StateC128::kTile) * StateC128::kStages, 512};
             else return {StateShape<T, D>::kTT, 1024};
         case kStepBwdQ:
             if constexpr (kWaveKernels<T, D>) return {int64_t(BwdQW64::kRound) * BwdQW64::kStages, 512};
