@@ -398,23 +398,24 @@ struct StagedState {
 
 // Copies M and z from global memory into s (StagedState<D>::kFloats floats)
 // with all of each thread's 16-byte loads in flight at once, and reduces
-// max |M|, max |z| and sum z over the workgroup in a fixed order (xor tree per
-// wave, then waves (0 + 1) + (2 + 3)). Ends with a barrier; red holds 12
-// floats.
-template <int D>
+// max |M|, max |z| and sum z over the NT-thread workgroup in a fixed order
+// (xor tree per wave, then a pairwise tree over the waves). Ends with a
+// barrier; red holds 3 NT / 64 floats.
+template <int D, int NT = kThreads>
 __device__ __forceinline__ StagedState<D> stage_state(const float* __restrict__ M,
                                                       const float* __restrict__ z, float* s, float* red) {
-    constexpr int PER = D * D / 4 / kThreads, LD = StagedState<D>::kLD;
+    constexpr int PER = D * D / 4 / NT, LD = StagedState<D>::kLD, NW = NT / 64;
+    static_assert(PER * 4 * NT == D * D && D / 4 <= NT, "thread count must tile the matrix");
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     float4 v[PER];
 #pragma unroll
-    for (int i = 0; i < PER; ++i) v[i] = reinterpret_cast<const float4*>(M)[tid + i * kThreads];
+    for (int i = 0; i < PER; ++i) v[i] = reinterpret_cast<const float4*>(M)[tid + i * NT];
     float4 w = make_float4(0.f, 0.f, 0.f, 0.f);
     if (tid < D / 4) w = reinterpret_cast<const float4*>(z)[tid];
     float a = 0.f;
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-        const int e = 4 * (tid + i * kThreads), r = e / D, c = e % D;
+        const int e = 4 * (tid + i * NT), r = e / D, c = e % D;
         float* d = s + r * LD + c;
         d[0] = v[i].x;
         d[1] = v[i].y;
@@ -433,14 +434,29 @@ __device__ __forceinline__ StagedState<D> stage_state(const float* __restrict__ 
     }
     if (lane == 0) {
         red[wave] = a;
-        red[4 + wave] = b;
-        red[8 + wave] = c;
+        red[NW + wave] = b;
+        red[2 * NW + wave] = c;
     }
     __syncthreads();
+    float xa[NW], xb[NW], xc[NW];
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+        xa[w] = red[w];
+        xb[w] = red[NW + w];
+        xc[w] = red[2 * NW + w];
+    }
+#pragma unroll
+    for (int n = NW / 2; n > 0; n /= 2)
+#pragma unroll
+        for (int w = 0; w < n; ++w) {
+            xa[w] = fmaxf(xa[2 * w], xa[2 * w + 1]);
+            xb[w] = fmaxf(xb[2 * w], xb[2 * w + 1]);
+            xc[w] = xc[2 * w] + xc[2 * w + 1];
+        }
     StagedState<D> st;
-    st.max_m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-    st.max_z = fmaxf(fmaxf(red[4], red[5]), fmaxf(red[6], red[7]));
-    st.sum_z = (red[8] + red[9]) + (red[10] + red[11]);
+    st.max_m = xa[0];
+    st.max_z = xb[0];
+    st.sum_z = xc[0];
     return st;
 }
 
@@ -953,16 +969,16 @@ __device__ __forceinline__ Frag<T> build_zfrag(const float* __restrict__ z, int 
 // Writes the workgroup's operand fragments to sA[f * 64 + lane], f < NF; wave w
 // builds fragments w, w + 4, ... with all their loads issued together. make(f)
 // returns fragment f (f is clamped, so its loads are unconditional).
-template <typename T, int NF, typename Make>
+template <typename T, int NF, int NW = kWaves, typename Make>
 __device__ __forceinline__ void build_frags(Frag<T>* sA, Make make) {
-    constexpr int PER = (NF + kWaves - 1) / kWaves;
+    constexpr int PER = (NF + NW - 1) / NW;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     Frag<T> fr[PER];
 #pragma unroll
-    for (int i = 0; i < PER; ++i) fr[i] = make(min(wave + kWaves * i, NF - 1));
+    for (int i = 0; i < PER; ++i) fr[i] = make(min(wave + NW * i, NF - 1));
 #pragma unroll
     for (int i = 0; i < PER; ++i)
-        if (wave + kWaves * i < NF) sA[(wave + kWaves * i) * 64 + lane] = fr[i];
+        if (wave + NW * i < NF) sA[(wave + NW * i) * 64 + lane] = fr[i];
 }
 
 // ---------------------------------------------------------------------------
@@ -1595,6 +1611,236 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_w64_kernel(
     }
 }
 
+// Steps 5-6 for 16-bit inputs at D = 128. Eight waves (512 threads) take the
+// eight 16-token steps of a 128-token round, each with two rounds of Q and dO
+// loads in flight. Per step a wave computes u = S dO_t, den and dQ (staged
+// for full-line stores through its own rows of the round tile), then writes
+// A_t = phi(q_t) 2^sw / den_t, the raw dO_t and beta_t = -r_t / den_t to the
+// round tile. After a barrier, wave w reduces the whole round into its 16
+// rows of
+//   sum_t A_t dO_t^T = 2^sw dS   and   sum_t A_t beta_t = 2^sw dz
+// with 16x16x32 MFMAs on transposed LDS reads; a second barrier frees the
+// tile for the next round. Rounds go in rotated order with no early exit;
+// rows past the slice end load as zeros and add nothing.
+struct BwdQC128 {
+    static constexpr int kWaves = 8;
+    static constexpr int kThreads = 64 * kWaves;
+    static constexpr int kStep = 16;                // tokens per wave step
+    static constexpr int kRound = kStep * kWaves;   // tokens per round
+    static constexpr int kLDR = 144;                // tile row stride (elements): 288-byte rows
+    static constexpr int kStages = 2;               // rounds of loads in flight
+};
+
+template <typename T, bool SIMPLE>
+__global__ __launch_bounds__(BwdQC128::kThreads, 1) void bwd_dq_c128_kernel(
+    const T* __restrict__ q, const T* __restrict__ dout, const float* __restrict__ stS,
+    const float* __restrict__ stz, T* __restrict__ dq, float* __restrict__ part,
+    float* __restrict__ dS_out, float* __restrict__ dz_out, int64_t T_, int PB,
+    int64_t LB, float eps) {
+    constexpr int D = 128, F = D / 4, NB = D / 16, KS = D / 32, E = D * D + D;
+    constexpr int NW = BwdQC128::kWaves, NT = BwdQC128::kThreads, STEP = BwdQC128::kStep;
+    constexpr int RT = BwdQC128::kRound, LDR = BwdQC128::kLDR;
+    constexpr int NJ = NB + (SIMPLE ? 0 : 1);  // dS column blocks (+ dz)
+    constexpr int NFS = NB * KS;
+    constexpr int NFR = NFS + (SIMPLE ? 0 : KS);
+    constexpr int NW16 = F * (int)sizeof(T) / 16;  // 16-byte words per quarter row
+    constexpr int kFragBytes = NFR * 64 * 16;
+    constexpr int kTileBytes = 2 * RT * LDR * (int)sizeof(T);  // A tile, then W tile
+    static_assert(StagedState<D>::kFloats * 4 <= kTileBytes, "state staging exceeds the tile area");
+    static_assert(BwdQC128::kStages == 2, "the loop below is written for two stages");
+    __shared__ __attribute__((aligned(16))) unsigned char smem[kFragBytes + kTileBytes];
+    __shared__ float red[3 * NW];
+    __shared__ __attribute__((aligned(16))) float sZ[D];
+
+    const int wid = xcd_remap(blockIdx.x, gridDim.x);
+    const int64_t bh = wid / PB;
+    const int p = wid % PB;
+    const int64_t t0 = (int64_t)p * LB;
+    const int64_t t1 = min(t0 + LB, T_);
+    const int nrounds = (int)(t1 > t0 ? (t1 - t0 + RT - 1) / RT : 0);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int m = lane & 15, grp = lane >> 4;
+    const float* S = stS + bh * D * D;
+    const float* z = stz + bh * D;
+    Frag<T>* sA = reinterpret_cast<Frag<T>*>(smem);
+    T* tA = reinterpret_cast<T*>(smem + kFragBytes);
+    T* tW = tA + RT * LDR;
+
+    // The state is staged in the tile area (which the rounds alone use) and
+    // the fragments are built from there.
+    int sS = 0, sz = 0, sw = 0;
+    {
+        constexpr int LD = StagedState<D>::kLD;
+        float* sSt = reinterpret_cast<float*>(tA);
+        const StagedState<D> st = stage_state<D, NT>(S, z, sSt, red);
+        if constexpr (Elt<T>::kScaled) {
+            sS = scale_exp(st.max_m);
+            sz = scale_exp(st.max_z);
+            if constexpr (!SIMPLE) {
+                if (st.sum_z > 0.f && isfinite(st.sum_z)) {
+                    int e;
+                    frexpf(st.sum_z, &e);
+                    sw = min(max(e - 1, -120), 120);  // 2^sw <= sum(z) < 2^(sw+1)
+                }
+            }
+        }
+        const float fS = ldexpf(1.f, sS), fz = ldexpf(1.f, sz);
+        build_frags<T, NFR, NW>(sA, [&](int f) {
+            return f < NFS ? build_frag<T, D, false, LD>(sSt, f / KS, f % KS, m, grp, fS)
+                           : build_zfrag<T, D>(sSt + D * LD, max(f - NFS, 0), grp, fz);
+        });
+        for (int i = tid; i < D; i += NT) sZ[i] = sSt[D * LD + i];
+    }
+    __syncthreads();
+    const float uS = ldexpf(1.f, -sS), uz = ldexpf(1.f, -sz), fw = ldexpf(1.f, sw);
+
+    f32x4 dsacc[NJ];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) dsacc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // The loaded words as they are (see the D = 64 kernel).
+    struct Stage {
+        u32x4 q[NW16], d[NW16];
+    };
+    const HeadBuf bq = slice_buf(q, bh, T_, D, t0, t1), bd = slice_buf(dout, bh, T_, D, t0, t1),
+                  bdq = slice_buf(dq, bh, T_, D, t0, t1);
+    const Rotation rot(nrounds, BwdQC128::kStages, wid);
+    auto issue = [&](Stage& st, int round) {
+        const int off = ((rot(round) * RT + wave * STEP + m) * D + F * grp) * (int)sizeof(T);
+#pragma unroll
+        for (int i = 0; i < NW16; ++i) {
+            st.q[i] = __builtin_amdgcn_raw_buffer_load_b128(bq.rsrc, off + 16 * i, 0, 0);
+            st.d[i] = __builtin_amdgcn_raw_buffer_load_b128(bd.rsrc, off + 16 * i, 0, 0);
+        }
+    };
+    const int rA = 8 * grp + (m >> 2), cA = 4 * (m & 3);
+    const int row = wave * STEP + m;  // this lane's token within the round tile
+    auto body = [&](Stage& st, int round) {
+        sched_fence();
+        Row<T, F> lq;
+        __builtin_memcpy(lq.e, st.q, sizeof(lq));
+        float qt[F];
+        Frag<T> bqf[KS], bdf[KS];
+#pragma unroll
+        for (int o = 0; o < F; ++o) qt[o] = phi<T>(to_f32(lq.e[o]));
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            if constexpr (!SIMPLE)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) bqf[s][e] = static_cast<T>(qt[8 * s + e]);
+            bdf[s] = __builtin_bit_cast(Frag<T>, st.d[s]);
+        }
+        // den first, so that the phi(q) fragments are dead before u
+        float inv = 1.f;
+        if constexpr (!SIMPLE) {
+            f32x4 ad = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < KS; ++s) ad = mma(sA[(NFS + s) * 64 + lane], bqf[s], ad);
+            inv = 1.f / (ad[0] * uz + eps);
+        }
+        f32x4 au[NB];
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            au[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < KS; ++s) au[b] = mma(sA[(b * KS + s) * 64 + lane], bdf[s], au[b]);
+        }
+        // dO rows go to the round tile as loaded; then the stage is free
+        {
+            u32x4* dw = reinterpret_cast<u32x4*>(&tW[row * LDR + F * grp]);
+#pragma unroll
+            for (int i = 0; i < NW16; ++i) dw[i] = st.d[i];
+        }
+        sched_fence();
+        issue(st, round + BwdQC128::kStages);
+        sched_fence();
+        float aq = 1.f;  // factor on phi(q) in the reduction operand
+        float ku = uS, cc = 0.f;
+        if constexpr (!SIMPLE) {
+            float rr = 0.f;
+#pragma unroll
+            for (int b = 0; b < NB; ++b)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) rr += qt[4 * b + r] * au[b][r];
+            rr += __shfl_xor(rr, 16);
+            rr += __shfl_xor(rr, 32);
+            const float beta = -(rr * uS) * inv;  // -r / den
+            cc = beta * inv;                      // -r / den^2
+            ku = uS * inv;
+            aq = fw * inv;
+            if (grp == 0) tW[row * LDR + D] = static_cast<T>(beta);
+        }
+        sched_fence();
+        {
+            Row<T, F> out;
+            const float* zl = &sZ[F * grp];
+#pragma unroll
+            for (int b = 0; b < NB; ++b)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int o = 4 * b + r;
+                    const float dqt = SIMPLE ? au[b][r] * ku : au[b][r] * ku + cc * zl[o];
+                    out.e[o] = static_cast<T>(dqt * fminf(qt[o], 1.f));  // phi' = min(phi, 1)
+                }
+            // staged through this wave's own rows of the A tile, which are
+            // written with A right after
+            store_tile_rows<T, D>(tA + wave * STEP * LDR, out, bdq, (int64_t)rot(round) * RT + wave * STEP);
+        }
+        {
+            Row<T, F> rq;
+#pragma unroll
+            for (int o = 0; o < F; ++o) rq.e[o] = static_cast<T>(qt[o] * aq);
+            *reinterpret_cast<Row<T, F>*>(&tA[row * LDR + F * grp]) = rq;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int ks = 0; ks < RT / 32; ++ks) {
+            const int rb = 32 * ks + rA;
+            const int col = 16 * wave + cA;
+            const Frag<T> a = join_frag<T>(lds_read_tr(&tA[rb * LDR + col]), lds_read_tr(&tA[(rb + 4) * LDR + col]));
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) {
+                const Frag<T> b = join_frag<T>(lds_read_tr(&tW[rb * LDR + 16 * j + cA]),
+                                               lds_read_tr(&tW[(rb + 4) * LDR + 16 * j + cA]));
+                dsacc[j] = mma(a, b, dsacc[j]);
+            }
+        }
+        __syncthreads();
+    };
+
+    if (nrounds > 0) {
+        Stage s0, s1;
+        issue(s0, 0);
+        sched_fence();
+        issue(s1, 1);
+        sched_fence();
+        for (int r = 0; r < rot.npad; r += 2) {
+            body(s0, r);
+            body(s1, r + 1);
+        }
+    }
+
+    // wave w holds rows [16 w, 16 w + 16) of 2^sw dS; column 0 of the last
+    // block holds 2^sw dz
+    const float uw = ldexpf(1.f, -sw);
+    float* oS;
+    float* oz;
+    if (PB == 1) {
+        oS = dS_out + bh * D * D;
+        oz = dz_out + bh * D;
+    } else {
+        oS = part + (bh * PB + p) * (int64_t)E;
+        oz = oS + D * D;
+    }
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) oS[(16 * wave + 4 * grp + r) * D + 16 * j + m] = dsacc[j][r] * uw;
+    if (m == 0)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) oz[16 * wave + 4 * grp + r] = SIMPLE ? 0.f : dsacc[NJ - 1][r] * uw;
+}
+
 // ---------------------------------------------------------------------------
 // Step 7: backward, K/V side.
 // ---------------------------------------------------------------------------
@@ -1846,6 +2092,13 @@ hipError_t bwd_dq_t(const Plan& p, const void* q, const void* dout, const float*
         else
             hipLaunchKernelGGL((bwd_dq_w64_kernel<T, false>), dim3((unsigned)nblk), dim3(kThreads), 0, s,
                                qq, dd, sS, sz, g, part, dS, dz, p.T, p.PB, p.LB, p.eps);
+    } else if constexpr (kTileKernels<T, D>) {
+        if (p.simple)
+            hipLaunchKernelGGL((bwd_dq_c128_kernel<T, true>), dim3((unsigned)nblk), dim3(BwdQC128::kThreads), 0, s,
+                               qq, dd, sS, sz, g, part, dS, dz, p.T, p.PB, p.LB, p.eps);
+        else
+            hipLaunchKernelGGL((bwd_dq_c128_kernel<T, false>), dim3((unsigned)nblk), dim3(BwdQC128::kThreads), 0, s,
+                               qq, dd, sS, sz, g, part, dS, dz, p.T, p.PB, p.LB, p.eps);
     } else {
         if (p.simple)
             hipLaunchKernelGGL((bwd_dq_kernel<T, D, true>), dim3((unsigned)nblk), dim3(kThreads), 0, s,
@@ -1894,6 +2147,7 @@ SplitCfg split_config_t(int step) {
             else return {StateShape<T, D>::kTT, 1024};
         case kStepBwdQ:
             if constexpr (kWaveKernels<T, D>) return {int64_t(BwdQW64::kRound) * BwdQW64::kStages, 512};
+            else if constexpr (kTileKernels<T, D>) return {int64_t(BwdQC128::kRound) * BwdQC128::kStages, 256};
             else return {BwdQShape<T, D>::kG, 1024};
         case kStepBwdKV:
             return {int64_t(StreamShape<T, D>::kStages) * 16 * kWaves, 1024};
