@@ -294,24 +294,40 @@ __device__ __forceinline__ void store_row(T* __restrict__ p, const float (&x)[N]
     for (int i = 0; i < NV; ++i) d[i] = s[i];
 }
 
+// Workgroup-wide max and sum over NW waves: an xor tree inside each wave,
+// then a pairwise tree over the waves in a fixed order. red holds NW floats.
+template <int NW = kWaves>
 __device__ __forceinline__ float block_max(float v, float* red) {
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
     __syncthreads();
-    const float r = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    float x[NW];
+#pragma unroll
+    for (int w = 0; w < NW; ++w) x[w] = red[w];
+#pragma unroll
+    for (int n = NW / 2; n > 0; n /= 2)
+#pragma unroll
+        for (int w = 0; w < n; ++w) x[w] = fmaxf(x[2 * w], x[2 * w + 1]);
     __syncthreads();
-    return r;
+    return x[0];
 }
 
+template <int NW = kWaves>
 __device__ __forceinline__ float block_sum(float v, float* red) {
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
     __syncthreads();
-    const float r = (red[0] + red[1]) + (red[2] + red[3]);
+    float x[NW];
+#pragma unroll
+    for (int w = 0; w < NW; ++w) x[w] = red[w];
+#pragma unroll
+    for (int n = NW / 2; n > 0; n /= 2)
+#pragma unroll
+        for (int w = 0; w < n; ++w) x[w] = x[2 * w] + x[2 * w + 1];
     __syncthreads();
-    return r;
+    return x[0];
 }
 
 // Exponent s with maxabs * 2^s in [2^14, 2^15): the largest state entry lands
@@ -361,29 +377,29 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const float* __restri
         *reinterpret_cast<float4*>(outz + bh * D + (idx - D * D)) = acc;
 }
 
-// Largest |x| over the D x D matrix at M, block-wide: every thread issues its
-// 16-byte loads at once (D*D/4 is a multiple of the block size).
-template <int D>
+// Largest |x| over the D x D matrix at M, over an NT-thread workgroup: every
+// thread issues its 16-byte loads at once (D*D/4 is a multiple of NT).
+template <int D, int NT = kThreads>
 __device__ __forceinline__ float block_absmax_matrix(const float* __restrict__ M, float* red) {
-    constexpr int PER = D * D / 4 / kThreads;
+    constexpr int PER = D * D / 4 / NT;
     float4 v[PER];
 #pragma unroll
-    for (int i = 0; i < PER; ++i) v[i] = reinterpret_cast<const float4*>(M)[threadIdx.x + i * kThreads];
+    for (int i = 0; i < PER; ++i) v[i] = reinterpret_cast<const float4*>(M)[threadIdx.x + i * NT];
     float mx = 0.f;
 #pragma unroll
     for (int i = 0; i < PER; ++i)
         mx = fmaxf(mx, fmaxf(fmaxf(fabsf(v[i].x), fabsf(v[i].y)), fmaxf(fabsf(v[i].z), fabsf(v[i].w))));
-    return block_max(mx, red);
+    return block_max<NT / 64>(mx, red);
 }
 
-// max |z_i| and sum z_i over the D-vector z, block-wide, in a fixed order.
-template <int D>
+// max |z_i| and sum z_i over the D-vector z, workgroup-wide, in a fixed order.
+template <int D, int NT = kThreads>
 __device__ __forceinline__ void block_vector_stats(const float* __restrict__ z, float* red, float& mx,
                                                    float& sum) {
     float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
     if (threadIdx.x < D / 4) v = reinterpret_cast<const float4*>(z)[threadIdx.x];
-    mx = block_max(fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))), red);
-    sum = block_sum((v.x + v.y) + (v.z + v.w), red);
+    mx = block_max<NT / 64>(fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))), red);
+    sum = block_sum<NT / 64>((v.x + v.y) + (v.z + v.w), red);
 }
 
 // A D x D fp32 matrix and a D-vector staged in LDS, with their statistics.
@@ -931,10 +947,16 @@ struct StreamShape {
     static constexpr int kNB = D / 16;   // 16-row output blocks
     static constexpr int kKS = D / 32;   // 32-long contraction steps over D
     static constexpr int kU = (sizeof(T) == 2 && D == 64) ? 2 : 1;  // 16-token blocks per wave
+    // 16-bit D = 128: eight waves share one copy of the (larger) fragments
+    static constexpr int kWaves = (sizeof(T) == 2 && D == 128) ? 8 : ::la::kWaves;
+    static constexpr int kThreads = 64 * kWaves;
     static constexpr int kG = kWaves * kU * 16;  // tokens per workgroup iteration
     static constexpr int kStages = 2;            // blocks of loads in flight per wave
-    // 16-bit D = 64: four workgroups per CU (128 registers per lane)
-    static constexpr int kMinBlocks = (sizeof(T) == 2 && D == 64) ? 4 : 1;
+    // workgroups per CU the register budget is set for: 16-bit D = 64, four
+    // (128 registers per lane); 16-bit D = 128, two for the output kernel
+    // (128 registers) and one for the K/V kernel (256)
+    static constexpr int kOutMinBlocks = (sizeof(T) == 2) ? (D == 64 ? 4 : 2) : 1;
+    static constexpr int kKvMinBlocks = (sizeof(T) == 2 && D == 64) ? 4 : 1;
 };
 
 // Fragment of A = M^T-like operand built from an fp32 D x D matrix M:
@@ -990,22 +1012,22 @@ __device__ __forceinline__ void build_frags(Frag<T>* sA, Make make) {
 // with D/4 contiguous outputs of its token) and den = z . phi(q) from one more
 // MFMA block whose rows are all z.
 template <typename T, int D, bool SIMPLE>
-__global__ __launch_bounds__(kThreads, (StreamShape<T, D>::kMinBlocks)) void fwd_output_kernel(
+__global__ __launch_bounds__((StreamShape<T, D>::kThreads), (StreamShape<T, D>::kOutMinBlocks)) void fwd_output_kernel(
     const T* __restrict__ q, const float* __restrict__ stS, const float* __restrict__ stz,
     T* __restrict__ o, int64_t T_, int NQ, int64_t LQ, float eps) {
     using Sh = StreamShape<T, D>;
-    constexpr int F = Sh::kF, NB = Sh::kNB, KS = Sh::kKS, U = Sh::kU;
+    constexpr int F = Sh::kF, NB = Sh::kNB, KS = Sh::kKS, U = Sh::kU, NW = Sh::kWaves, NT = Sh::kThreads;
     constexpr int NFS = NB * KS;             // S fragments
     constexpr int NFR = NFS + (SIMPLE ? 0 : KS);  // + z fragments
     constexpr int LDR = D + 16 / (int)sizeof(T);
     // At D = 64 the state is staged in LDS (sharing the store staging area,
     // which the loop alone uses) and the fragments are built from there.
     constexpr bool kStaged = (D == 64);
-    constexpr int kStoreBytes = kWaves * 16 * LDR * (int)sizeof(T);
+    constexpr int kStoreBytes = NW * 16 * LDR * (int)sizeof(T);
     constexpr int kStBytes = kStaged ? StagedState<D>::kFloats * 4 : 0;
     __shared__ Frag<T> sA[NFR * 64];
     __shared__ __attribute__((aligned(16))) unsigned char sraw[kStoreBytes > kStBytes ? kStoreBytes : kStBytes];
-    __shared__ float red[12];
+    __shared__ float red[3 * NW];
     T* stage = reinterpret_cast<T*>(sraw);
 
     const int wid = xcd_remap(blockIdx.x, gridDim.x);
@@ -1022,25 +1044,25 @@ __global__ __launch_bounds__(kThreads, (StreamShape<T, D>::kMinBlocks)) void fwd
     if constexpr (kStaged) {
         constexpr int LD = StagedState<D>::kLD;
         float* sSt = reinterpret_cast<float*>(sraw);
-        const StagedState<D> st = stage_state<D>(S, z, sSt, red);
+        const StagedState<D> st = stage_state<D, NT>(S, z, sSt, red);
         if constexpr (Elt<T>::kScaled) {
             sS = scale_exp(st.max_m);
             sz = scale_exp(st.max_z);
         }
         const float fS = ldexpf(1.f, sS), fz = ldexpf(1.f, sz);
-        build_frags<T, NFR>(sA, [&](int f) {
+        build_frags<T, NFR, NW>(sA, [&](int f) {
             return f < NFS ? build_frag<T, D, true, LD>(sSt, f / KS, f % KS, m, grp, fS)
                            : build_zfrag<T, D>(sSt + D * LD, max(f - NFS, 0), grp, fz);
         });
     } else {
         if constexpr (Elt<T>::kScaled) {
             float mz, zsum;
-            sS = scale_exp(block_absmax_matrix<D>(S, red));
-            block_vector_stats<D>(z, red, mz, zsum);
+            sS = scale_exp(block_absmax_matrix<D, NT>(S, red));
+            block_vector_stats<D, NT>(z, red, mz, zsum);
             sz = scale_exp(mz);
         }
         const float fS = ldexpf(1.f, sS), fz = ldexpf(1.f, sz);
-        build_frags<T, NFR>(sA, [&](int f) {
+        build_frags<T, NFR, NW>(sA, [&](int f) {
             return f < NFS ? build_frag<T, D, true>(S, f / KS, f % KS, m, grp, fS)
                            : build_zfrag<T, D>(z, max(f - NFS, 0), grp, fz);
         });
@@ -1048,14 +1070,14 @@ __global__ __launch_bounds__(kThreads, (StreamShape<T, D>::kMinBlocks)) void fwd
     __syncthreads();
     const float uS = ldexpf(1.f, -sS), uz = ldexpf(1.f, -sz);
 
-    // Each wave takes blocks of 16 U tokens, kWaves blocks apart, with the
+    // Each wave takes blocks of 16 U tokens, NW blocks apart, with the
     // loads of its next two blocks in flight while it computes one. Blocks go
     // in rotated order, two per turn with no early exit; rows are counted from
     // c0, rows past the chunk end load as zeros and their stores are dropped.
     constexpr int BT = 16 * U;
     const HeadBuf bq = slice_buf(q, bh, T_, D, c0, c1), bo = slice_buf(o, bh, T_, D, c0, c1);
     constexpr int NS = Sh::kStages;
-    const Rotation rot((int)((c1 - c0 + BT - 1) / BT), NS * kWaves, wid);
+    const Rotation rot((int)((c1 - c0 + BT - 1) / BT), NS * NW, wid);
     T* stg = stage + wave * 16 * LDR;
     auto issue = [&](Row<T, F> (&b)[U], int blk) {
         const int64_t bs = (int64_t)rot(blk) * BT;
@@ -1072,7 +1094,7 @@ __global__ __launch_bounds__(kThreads, (StreamShape<T, D>::kMinBlocks)) void fwd
                 for (int e = 0; e < 8; ++e)
                     bq[u][s][e] = static_cast<T>(phi<T>(to_f32(qr[u].e[8 * s + e])));
         sched_fence();
-        issue(qr, blk + NS * kWaves);
+        issue(qr, blk + NS * NW);
         sched_fence();
         f32x4 acc[U][NB], accd[U];
 #pragma unroll
@@ -1119,12 +1141,12 @@ __global__ __launch_bounds__(kThreads, (StreamShape<T, D>::kMinBlocks)) void fwd
     Row<T, F> stg_q[NS][U];
 #pragma unroll
     for (int i = 0; i < NS; ++i) {
-        issue(stg_q[i], wave + i * kWaves);
+        issue(stg_q[i], wave + i * NW);
         sched_fence();
     }
-    for (int blk = wave; blk < rot.npad; blk += NS * kWaves) {
+    for (int blk = wave; blk < rot.npad; blk += NS * NW) {
 #pragma unroll
-        for (int i = 0; i < NS; ++i) body(stg_q[i], blk + i * kWaves);
+        for (int i = 0; i < NS; ++i) body(stg_q[i], blk + i * NW);
     }
 }
 
@@ -1848,12 +1870,12 @@ __global__ __launch_bounds__(BwdQC128::kThreads, 1) void bwd_dq_c128_kernel(
 // fixed D x D matrix with a token's row, so each is one set of MFMA blocks with
 // dS (or dS^T) as the A operand and the loaded K/V quarter rows as B.
 template <typename T, int D, bool SIMPLE>
-__global__ __launch_bounds__(kThreads, (StreamShape<T, D>::kMinBlocks)) void bwd_dkv_kernel(
+__global__ __launch_bounds__((StreamShape<T, D>::kThreads), (StreamShape<T, D>::kKvMinBlocks)) void bwd_dkv_kernel(
     const T* __restrict__ k, const T* __restrict__ v, const float* __restrict__ dSg,
     const float* __restrict__ dzg, T* __restrict__ dk, T* __restrict__ dv, int64_t T_, int NK,
     int64_t LK) {
     using Sh = StreamShape<T, D>;
-    constexpr int F = Sh::kF, NB = Sh::kNB, KS = Sh::kKS;
+    constexpr int F = Sh::kF, NB = Sh::kNB, KS = Sh::kKS, NW = Sh::kWaves, NT = Sh::kThreads;
     constexpr int U = 1;  // one 16-token block per wave step; the prefetch gives the depth
     constexpr int NFS = NB * KS;
     constexpr int LDR = D + 16 / (int)sizeof(T);
@@ -1863,11 +1885,11 @@ __global__ __launch_bounds__(kThreads, (StreamShape<T, D>::kMinBlocks)) void bwd
     // staging area, which the loop alone uses) and the fragments are built
     // from there.
     constexpr bool kStaged = (D == 64);
-    constexpr int kStoreBytes = kStage ? kWaves * 16 * LDR * (int)sizeof(T) : 16;
+    constexpr int kStoreBytes = kStage ? NW * 16 * LDR * (int)sizeof(T) : 16;
     constexpr int kStBytes = kStaged ? StagedState<D>::kFloats * 4 : 0;
     __shared__ Frag<T> sA[2 * NFS * 64];
     __shared__ __attribute__((aligned(16))) unsigned char sraw[kStoreBytes > kStBytes ? kStoreBytes : kStBytes];
-    __shared__ float red[12];
+    __shared__ float red[3 * NW];
     T* stage = reinterpret_cast<T*>(sraw);
 
     const int wid = xcd_remap(blockIdx.x, gridDim.x);
@@ -1887,19 +1909,19 @@ __global__ __launch_bounds__(kThreads, (StreamShape<T, D>::kMinBlocks)) void bwd
     if constexpr (kStaged) {
         constexpr int LD = StagedState<D>::kLD;
         float* sSt = reinterpret_cast<float*>(sraw);
-        const StagedState<D> st = stage_state<D>(dS, dz, sSt, red);
+        const StagedState<D> st = stage_state<D, NT>(dS, dz, sSt, red);
         if constexpr (Elt<T>::kScaled) sD = scale_exp(st.max_m);
         const float fD = ldexpf(1.f, sD);
-        build_frags<T, 2 * NFS>(sA, [&](int f) {
+        build_frags<T, 2 * NFS, NW>(sA, [&](int f) {
             return f < NFS ? build_frag<T, D, false, LD>(sSt, f / KS, f % KS, m, grp, fD)
                            : build_frag<T, D, true, LD>(sSt, (f - NFS) / KS, (f - NFS) % KS, m, grp, fD);
         });
 #pragma unroll
         for (int o = 0; o < F; ++o) dzl[o] = SIMPLE ? 0.f : sSt[D * LD + F * grp + o];
     } else {
-        if constexpr (Elt<T>::kScaled) sD = scale_exp(block_absmax_matrix<D>(dS, red));
+        if constexpr (Elt<T>::kScaled) sD = scale_exp(block_absmax_matrix<D, NT>(dS, red));
         const float fD = ldexpf(1.f, sD);
-        build_frags<T, 2 * NFS>(sA, [&](int f) {
+        build_frags<T, 2 * NFS, NW>(sA, [&](int f) {
             return f < NFS ? build_frag<T, D, false>(dS, f / KS, f % KS, m, grp, fD)
                            : build_frag<T, D, true>(dS, (f - NFS) / KS, (f - NFS) % KS, m, grp, fD);
         });
@@ -1917,19 +1939,19 @@ __global__ __launch_bounds__(kThreads, (StreamShape<T, D>::kMinBlocks)) void bwd
     const HeadBuf bdk = slice_buf(dk, bh, T_, D, c0, c1), bdv = slice_buf(dv, bh, T_, D, c0, c1);
     T* stg = stage + (kStage ? wave * 16 * LDR : 0);
     // The loaded words as they are (see the dQ kernel).
-    constexpr int NW = F * (int)sizeof(T) / 16;
+    constexpr int NQW = F * (int)sizeof(T) / 16;  // 16-byte words per quarter row
     struct Stage {
-        u32x4 k[U][NW], v[U][NW];
+        u32x4 k[U][NQW], v[U][NQW];
     };
     constexpr int NS = Sh::kStages;
-    const Rotation rot((int)((c1 - c0 + 16 * U - 1) / (16 * U)), NS * kWaves, wid);
+    const Rotation rot((int)((c1 - c0 + 16 * U - 1) / (16 * U)), NS * NW, wid);
     auto issue = [&](Stage& st, int blk) {
         const int64_t bs = (int64_t)rot(blk) * 16 * U;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int off = (int)((bs + 16 * u + m) * D + F * grp) * (int)sizeof(T);
 #pragma unroll
-            for (int i = 0; i < NW; ++i) {
+            for (int i = 0; i < NQW; ++i) {
                 st.k[u][i] = __builtin_amdgcn_raw_buffer_load_b128(bk.rsrc, off + 16 * i, 0, 0);
                 st.v[u][i] = __builtin_amdgcn_raw_buffer_load_b128(bv_.rsrc, off + 16 * i, 0, 0);
             }
@@ -1983,7 +2005,7 @@ __global__ __launch_bounds__(kThreads, (StreamShape<T, D>::kMinBlocks)) void bwd
             }
         // the stage's registers are free once the products have read V
         sched_fence();
-        issue(st, blk + NS * kWaves);
+        issue(st, blk + NS * NW);
         sched_fence();
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -2008,12 +2030,12 @@ __global__ __launch_bounds__(kThreads, (StreamShape<T, D>::kMinBlocks)) void bwd
     Stage stq[NS];
 #pragma unroll
     for (int i = 0; i < NS; ++i) {
-        issue(stq[i], wave + i * kWaves);
+        issue(stq[i], wave + i * NW);
         sched_fence();
     }
-    for (int blk = wave; blk < rot.npad; blk += NS * kWaves) {
+    for (int blk = wave; blk < rot.npad; blk += NS * NW) {
 #pragma unroll
-        for (int i = 0; i < NS; ++i) body(stq[i], blk + i * kWaves);
+        for (int i = 0; i < NS; ++i) body(stq[i], blk + i * NW);
     }
 }
 
@@ -2061,11 +2083,11 @@ template <typename T, int D>
 hipError_t fwd_output_t(const Plan& p, const void* q, const float* state, void* o, hipStream_t s) {
     const int64_t nblk = p.BH * p.NQ;
     if (p.simple)
-        hipLaunchKernelGGL((fwd_output_kernel<T, D, true>), dim3((unsigned)nblk), dim3(kThreads), 0, s,
+        hipLaunchKernelGGL((fwd_output_kernel<T, D, true>), dim3((unsigned)nblk), dim3(StreamShape<T, D>::kThreads), 0, s,
                            static_cast<const T*>(q), state, state + p.BH * D * D, static_cast<T*>(o),
                            p.T, p.NQ, p.LQ, p.eps);
     else
-        hipLaunchKernelGGL((fwd_output_kernel<T, D, false>), dim3((unsigned)nblk), dim3(kThreads), 0, s,
+        hipLaunchKernelGGL((fwd_output_kernel<T, D, false>), dim3((unsigned)nblk), dim3(StreamShape<T, D>::kThreads), 0, s,
                            static_cast<const T*>(q), state, state + p.BH * D * D, static_cast<T*>(o),
                            p.T, p.NQ, p.LQ, p.eps);
     return hipGetLastError();
@@ -2116,11 +2138,11 @@ hipError_t bwd_dkv_t(const Plan& p, const void* k, const void* v, void* dk, void
     const int64_t nblk = p.BH * p.NK;
     const float* dst = reinterpret_cast<const float*>(static_cast<char*>(ws) + p.off_dstate);
     if (p.simple)
-        hipLaunchKernelGGL((bwd_dkv_kernel<T, D, true>), dim3((unsigned)nblk), dim3(kThreads), 0, s,
+        hipLaunchKernelGGL((bwd_dkv_kernel<T, D, true>), dim3((unsigned)nblk), dim3(StreamShape<T, D>::kThreads), 0, s,
                            static_cast<const T*>(k), static_cast<const T*>(v), dst, dst + p.BH * D * D,
                            static_cast<T*>(dk), static_cast<T*>(dv), p.T, p.NK, p.LK);
     else
-        hipLaunchKernelGGL((bwd_dkv_kernel<T, D, false>), dim3((unsigned)nblk), dim3(kThreads), 0, s,
+        hipLaunchKernelGGL((bwd_dkv_kernel<T, D, false>), dim3((unsigned)nblk), dim3(StreamShape<T, D>::kThreads), 0, s,
                            static_cast<const T*>(k), static_cast<const T*>(v), dst, dst + p.BH * D * D,
                            static_cast<T*>(dk), static_cast<T*>(dv), p.T, p.NK, p.LK);
     return hipGetLastError();
@@ -2150,7 +2172,7 @@ SplitCfg split_config_t(int step) {
             else if constexpr (kTileKernels<T, D>) return {int64_t(BwdQC128::kRound) * BwdQC128::kStages, 256};
             else return {BwdQShape<T, D>::kG, 1024};
         case kStepBwdKV:
-            return {int64_t(StreamShape<T, D>::kStages) * 16 * kWaves, 1024};
+            return {int64_t(StreamShape<T, D>::kStages) * 16 * StreamShape<T, D>::kWaves, 1024};
         default:
             return {StreamShape<T, D>::kStages * StreamShape<T, D>::kG, 2048};
     }
