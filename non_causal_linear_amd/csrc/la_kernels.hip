@@ -1633,8 +1633,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_w64_kernel(
     }
 }
 
-// Steps 5-6 for 16-bit inputs at D = 128. Eight waves (512 threads) take the
-// eight 16-token steps of a 128-token round, each with two rounds of Q and dO
+// Steps 5-6 for 16-bit inputs, one wave per 16 rows of dS: D / 16 waves take
+// the 16-token steps of a round of D tokens, each with two rounds of Q and dO
 // loads in flight. Per step a wave computes u = S dO_t, den and dQ (staged
 // for full-line stores through its own rows of the round tile), then writes
 // A_t = phi(q_t) 2^sw / den_t, the raw dO_t and beta_t = -r_t / den_t to the
@@ -1644,24 +1644,30 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_w64_kernel(
 // with 16x16x32 MFMAs on transposed LDS reads; a second barrier frees the
 // tile for the next round. Rounds go in rotated order with no early exit;
 // rows past the slice end load as zeros and add nothing.
-struct BwdQC128 {
-    static constexpr int kWaves = 8;
+template <int D>
+struct BwdQTile {
+    static constexpr int kWaves = D / 16;
     static constexpr int kThreads = 64 * kWaves;
     static constexpr int kStep = 16;                // tokens per wave step
     static constexpr int kRound = kStep * kWaves;   // tokens per round
-    static constexpr int kLDR = 144;                // tile row stride (elements): 288-byte rows
+    // tile row stride (elements) with the beta block after D columns; four
+    // consecutive rows start 8 or more banks apart, so a transposed read of
+    // 4 rows x 32 bytes hits distinct banks
+    static constexpr int kLDR = D == 64 ? 80 : 144;
     static constexpr int kStages = 2;               // rounds of loads in flight
+    static constexpr int kMinBlocks = D == 64 ? 3 : 1;
 };
 
-template <typename T, bool SIMPLE>
-__global__ __launch_bounds__(BwdQC128::kThreads, 1) void bwd_dq_c128_kernel(
+template <typename T, int D, bool SIMPLE>
+__global__ __launch_bounds__(BwdQTile<D>::kThreads, BwdQTile<D>::kMinBlocks) void bwd_dq_tile_kernel(
     const T* __restrict__ q, const T* __restrict__ dout, const float* __restrict__ stS,
     const float* __restrict__ stz, T* __restrict__ dq, float* __restrict__ part,
     float* __restrict__ dS_out, float* __restrict__ dz_out, int64_t T_, int PB,
     int64_t LB, float eps) {
-    constexpr int D = 128, F = D / 4, NB = D / 16, KS = D / 32, E = D * D + D;
-    constexpr int NW = BwdQC128::kWaves, NT = BwdQC128::kThreads, STEP = BwdQC128::kStep;
-    constexpr int RT = BwdQC128::kRound, LDR = BwdQC128::kLDR;
+    using Sh = BwdQTile<D>;
+    constexpr int F = D / 4, NB = D / 16, KS = D / 32, E = D * D + D;
+    constexpr int NW = Sh::kWaves, NT = Sh::kThreads, STEP = Sh::kStep;
+    constexpr int RT = Sh::kRound, LDR = Sh::kLDR;
     constexpr int NJ = NB + (SIMPLE ? 0 : 1);  // dS column blocks (+ dz)
     constexpr int NFS = NB * KS;
     constexpr int NFR = NFS + (SIMPLE ? 0 : KS);
@@ -1669,7 +1675,7 @@ __global__ __launch_bounds__(BwdQC128::kThreads, 1) void bwd_dq_c128_kernel(
     constexpr int kFragBytes = NFR * 64 * 16;
     constexpr int kTileBytes = 2 * RT * LDR * (int)sizeof(T);  // A tile, then W tile
     static_assert(StagedState<D>::kFloats * 4 <= kTileBytes, "state staging exceeds the tile area");
-    static_assert(BwdQC128::kStages == 2, "the loop below is written for two stages");
+    static_assert(Sh::kStages == 2, "the loop below is written for two stages");
     __shared__ __attribute__((aligned(16))) unsigned char smem[kFragBytes + kTileBytes];
     __shared__ float red[3 * NW];
     __shared__ __attribute__((aligned(16))) float sZ[D];
@@ -1726,7 +1732,7 @@ __global__ __launch_bounds__(BwdQC128::kThreads, 1) void bwd_dq_c128_kernel(
     };
     const HeadBuf bq = slice_buf(q, bh, T_, D, t0, t1), bd = slice_buf(dout, bh, T_, D, t0, t1),
                   bdq = slice_buf(dq, bh, T_, D, t0, t1);
-    const Rotation rot(nrounds, BwdQC128::kStages, wid);
+    const Rotation rot(nrounds, Sh::kStages, wid);
     auto issue = [&](Stage& st, int round) {
         const int off = ((rot(round) * RT + wave * STEP + m) * D + F * grp) * (int)sizeof(T);
 #pragma unroll
@@ -1774,7 +1780,7 @@ __global__ __launch_bounds__(BwdQC128::kThreads, 1) void bwd_dq_c128_kernel(
             for (int i = 0; i < NW16; ++i) dw[i] = st.d[i];
         }
         sched_fence();
-        issue(st, round + BwdQC128::kStages);
+        issue(st, round + Sh::kStages);
         sched_fence();
         float aq = 1.f;  // factor on phi(q) in the reduction operand
         float ku = uS, cc = 0.f;
@@ -2116,10 +2122,10 @@ hipError_t bwd_dq_t(const Plan& p, const void* q, const void* dout, const float*
                                qq, dd, sS, sz, g, part, dS, dz, p.T, p.PB, p.LB, p.eps);
     } else if constexpr (kTileKernels<T, D>) {
         if (p.simple)
-            hipLaunchKernelGGL((bwd_dq_c128_kernel<T, true>), dim3((unsigned)nblk), dim3(BwdQC128::kThreads), 0, s,
+            hipLaunchKernelGGL((bwd_dq_tile_kernel<T, D, true>), dim3((unsigned)nblk), dim3(BwdQTile<D>::kThreads), 0, s,
                                qq, dd, sS, sz, g, part, dS, dz, p.T, p.PB, p.LB, p.eps);
         else
-            hipLaunchKernelGGL((bwd_dq_c128_kernel<T, false>), dim3((unsigned)nblk), dim3(BwdQC128::kThreads), 0, s,
+            hipLaunchKernelGGL((bwd_dq_tile_kernel<T, D, false>), dim3((unsigned)nblk), dim3(BwdQTile<D>::kThreads), 0, s,
                                qq, dd, sS, sz, g, part, dS, dz, p.T, p.PB, p.LB, p.eps);
     } else {
         if (p.simple)
@@ -2169,7 +2175,7 @@ SplitCfg split_config_t(int step) {
             else return {StateShape<T, D>::kTT, 1024};
         case kStepBwdQ:
             if constexpr (kWaveKernels<T, D>) return {int64_t(BwdQW64::kRound) * BwdQW64::kStages, 512};
-            else if constexpr (kTileKernels<T, D>) return {int64_t(BwdQC128::kRound) * BwdQC128::kStages, 256};
+            else if constexpr (kTileKernels<T, D>) return {int64_t(BwdQTile<D>::kRound) * BwdQTile<D>::kStages, 256};
             else return {BwdQShape<T, D>::kG, 1024};
         case kStepBwdKV:
             return {int64_t(StreamShape<T, D>::kStages) * 16 * StreamShape<T, D>::kWaves, 1024};

@@ -93,6 +93,29 @@ def test_small_fwd_bwd_all_elements(T, D, dtype, simple):
     check("dV", decode(out["dv"], dtype), dv_ref, dtype)
 
 
+@pytest.mark.parametrize("simple", [False, True], ids=["norm", "simple"])
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("D", [64, 128])
+def test_many_heads_single_slice_ragged(D, dtype, simple):
+    """640 heads of 300 tokens: enough heads that every step runs one slice or
+    chunk per head (the state and dS go straight to their outputs, no
+    partials), each ending on a ragged tail inside its first rounds."""
+    seed = 20_000 + D + 7 * ["f16", "bf16"].index(dtype) + (3 if simple else 0)
+    w = Workload("many-heads", 4, 160, 300, D, dtype, simple=simple, seed=seed)
+    print(f"case B4 H160 T300 D={D} {dtype} simple={simple} seed={seed}", flush=True)
+    x = make_inputs(w)
+    _, out = run(w, x, bwd=True)
+    o_ref, s_ref, z_ref = oracle.fwd(x["q"], x["k"], x["v"], dtype, w.eps, simple)
+    dq_ref, dk_ref, dv_ref = oracle.bwd(x["q"], x["k"], x["v"], x["do"], dtype, w.eps, simple)
+    s_got, z_got = split_state(out["state"], w.B, w.H, D)
+    check("S", s_got, s_ref, dtype)
+    check("z", z_got, z_ref, dtype)
+    check("O", decode(out["o"], dtype), o_ref, dtype)
+    check("dQ", decode(out["dq"], dtype), dq_ref, dtype)
+    check("dK", decode(out["dk"], dtype), dk_ref, dtype)
+    check("dV", decode(out["dv"], dtype), dv_ref, dtype)
+
+
 # ------------------------------------------------------------- full-size workloads
 
 def sampled_heads(n, seed):
