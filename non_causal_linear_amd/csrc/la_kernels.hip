@@ -157,22 +157,15 @@ struct alignas(16) Row {
     T e[N];
 };
 
-// Buffer-descriptor access to one head's rows. The descriptor covers exactly
-// the head's T rows (T * D * sizeof(T) bytes, below 2^31), so loads past the
-// last row read zeros and stores there are dropped by the hardware: the
-// kernels need no clamping or branches at the ragged end of a sequence.
+// Buffer-descriptor access to a slice of one head's rows. The descriptor
+// covers exactly rows [r0, r1) (below 2^31 bytes, as a whole head is), rows
+// are counted from r0, and the hardware reads zeros for loads past r1 and
+// drops stores there, even where the head continues: the kernels need no
+// clamping or branches at the ragged end of a slice.
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 struct HeadBuf {
     __amdgpu_buffer_rsrc_t rsrc;
 };
-template <typename T>
-__device__ __forceinline__ HeadBuf head_buf(const T* base, int64_t bh, int64_t T_, int D) {
-    const T* p = base + bh * T_ * D;
-    return HeadBuf{__builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(p), 0, (int)(T_ * D * (int64_t)sizeof(T)),
-                                                     0x00020000)};
-}
-// Descriptor over rows [r0, r1) of one head only: rows are then counted from
-// r0, and loads past r1 read zeros even where the head continues.
 template <typename T>
 __device__ __forceinline__ HeadBuf slice_buf(const T* base, int64_t bh, int64_t T_, int D, int64_t r0,
                                              int64_t r1) {
@@ -186,8 +179,10 @@ __device__ __forceinline__ HeadBuf slice_buf(const T* base, int64_t bh, int64_t 
 // they would all be at the same offset of slices whose bases are a fixed
 // stride apart, and whether those simultaneous accesses pile onto the same
 // DRAM channels would depend on where the buffers sit in physical memory.
-// Indices at or past the padded count map past the slice end, where the
-// slice's buffer descriptors read zeros and drop stores.
+// Indices at or past the padded count (the prefetches of the last turn, at
+// most a few blocks) map to themselves, past the slice end, where the slice's
+// buffer descriptors read zeros and drop stores; the clamp keeps them within
+// 64 blocks of the end whatever the caller passes.
 struct Rotation {
     int npad, R;
     __device__ Rotation(int n, int group, int wid) {
@@ -196,11 +191,22 @@ struct Rotation {
         R = nr > 0 ? group * ((wid * 7) % nr) : 0;
     }
     __device__ int operator()(int blk) const {
-        if (blk >= npad) return npad + blk;
+        if (blk >= npad) return min(blk, npad + 64);
         const int x = blk + R;
         return x >= npad ? x - npad : x;
     }
 };
+
+// Byte offset of element (row, col) of a slice with rows of D elements, for a
+// buffer access, in unsigned 32-bit arithmetic (exact modulo 2^32). Offsets
+// inside a slice are below 2^31 (the head size limit); rows past the end,
+// which the kernels visit at most a few padded blocks far, stay below 2^32,
+// so their offsets still lie past the descriptor's range: such loads read
+// zeros and such stores are dropped.
+template <typename T>
+__device__ __forceinline__ int buf_off(int64_t row, int D, int col) {
+    return (int)((uint32_t)row * (uint32_t)(D * (int)sizeof(T)) + (uint32_t)(col * (int)sizeof(T)));
+}
 
 __device__ __forceinline__ uint4 buf_load16(const HeadBuf& b, int byte_off) {
     const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(b.rsrc, byte_off, 0, 0);
@@ -216,7 +222,7 @@ template <typename T, int N>
 __device__ __forceinline__ void load_row_buf(Row<T, N>& r, const HeadBuf& b, int64_t row, int D, int col) {
     constexpr int NV = N * (int)sizeof(T) / 16;
     uint4* d = reinterpret_cast<uint4*>(r.e);
-    const int off = (int)(row * D + col) * (int)sizeof(T);
+    const int off = buf_off<T>(row, D, col);
 #pragma unroll
     for (int i = 0; i < NV; ++i) d[i] = buf_load16(b, off + 16 * i);
 }
@@ -240,7 +246,7 @@ __device__ __forceinline__ void store_tile_rows(T* stage, const Row<T, D / 4>& v
 #pragma unroll
     for (int k = 0; k < 16 / RPI; ++k) {
         const uint4 x = *reinterpret_cast<const uint4*>(&stage[(k * RPI + r) * LDR + EPC * c]);
-        buf_store16(b, (int)((row0 + k * RPI + r) * D) * (int)sizeof(T) + 16 * c, x);
+        buf_store16(b, buf_off<T>(row0 + k * RPI + r, D, EPC * c), x);
     }
     wave_lds_sync();
 }
@@ -251,7 +257,7 @@ template <typename T, int D>
 __device__ __forceinline__ void store_tile_quarters(const Row<T, D / 4>& vals, const HeadBuf& b, int64_t row0) {
     constexpr int F = D / 4, NV = F * (int)sizeof(T) / 16;
     const int lane = threadIdx.x & 63, m = lane & 15, g = lane >> 4;
-    const int off = (int)((row0 + m) * D + F * g) * (int)sizeof(T);
+    const int off = buf_off<T>(row0 + m, D, F * g);
 #pragma unroll
     for (int i = 0; i < NV; ++i) buf_store16(b, off + 16 * i, reinterpret_cast<const uint4*>(vals.e)[i]);
 }
@@ -671,7 +677,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_state_w64_kernel(
         const int ps = rot(step);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int off = (int)(((int64_t)ps * STEP + rg + 8 * r) * D + 8 * c) * (int)sizeof(T);
+            const int off = buf_off<T>((int64_t)ps * STEP + rg + 8 * r, D, 8 * c);
             st.k[r] = buf_load16(bk, off);
             st.v[r] = buf_load16(bv, off);
         }
@@ -848,7 +854,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_state_c128_kernel(
         const int row0 = rot(tile) * TT;
 #pragma unroll
         for (int i = 0; i < CPT; ++i) {
-            const int off = (row0 + r0 + RPP * i) * D * (int)sizeof(T) + 16 * c;
+            const int off = buf_off<T>((int64_t)row0 + r0 + RPP * i, D, 8 * c);
             st.k[i] = __builtin_amdgcn_raw_buffer_load_b128(bk.rsrc, off, 0, 0);
             st.v[i] = __builtin_amdgcn_raw_buffer_load_b128(bv.rsrc, off, 0, 0);
         }
@@ -1463,7 +1469,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_w64_kernel(
                   bdq = slice_buf(dq, bh, T_, D, t0, t1);
     const Rotation rot(nsteps, BwdQW64::kStages * kWaves, wid);
     auto issue = [&](Stage& st, int step) {
-        const int off = (int)(((int64_t)rot(step) * STEP + m) * D + F * grp) * (int)sizeof(T);
+        const int off = buf_off<T>((int64_t)rot(step) * STEP + m, D, F * grp);
         st.q[0] = __builtin_amdgcn_raw_buffer_load_b128(bq.rsrc, off, 0, 0);
         st.q[1] = __builtin_amdgcn_raw_buffer_load_b128(bq.rsrc, off + 16, 0, 0);
         st.d[0] = __builtin_amdgcn_raw_buffer_load_b128(bd.rsrc, off, 0, 0);
@@ -1734,7 +1740,7 @@ __global__ __launch_bounds__(BwdQTile<D>::kThreads, BwdQTile<D>::kMinBlocks) voi
                   bdq = slice_buf(dq, bh, T_, D, t0, t1);
     const Rotation rot(nrounds, Sh::kStages, wid);
     auto issue = [&](Stage& st, int round) {
-        const int off = ((rot(round) * RT + wave * STEP + m) * D + F * grp) * (int)sizeof(T);
+        const int off = buf_off<T>((int64_t)rot(round) * RT + wave * STEP + m, D, F * grp);
 #pragma unroll
         for (int i = 0; i < NW16; ++i) {
             st.q[i] = __builtin_amdgcn_raw_buffer_load_b128(bq.rsrc, off + 16 * i, 0, 0);
@@ -1955,7 +1961,7 @@ __global__ __launch_bounds__((StreamShape<T, D>::kThreads), (StreamShape<T, D>::
         const int64_t bs = (int64_t)rot(blk) * 16 * U;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int off = (int)((bs + 16 * u + m) * D + F * grp) * (int)sizeof(T);
+            const int off = buf_off<T>(bs + 16 * u + m, D, F * grp);
 #pragma unroll
             for (int i = 0; i < NQW; ++i) {
                 st.k[u][i] = __builtin_amdgcn_raw_buffer_load_b128(bk.rsrc, off + 16 * i, 0, 0);

@@ -27,9 +27,12 @@ from .la_oracle import (  # noqa: F401
     dphi,
     fwd,
     fwd_head,
+    output_head,
     bwd,
     bwd_head,
+    bwd_kv_side_head,
     bwd_leading_terms_head,
+    bwd_q_side_head,
     phi,
     quadratic_head,
     sampled_rows_head,

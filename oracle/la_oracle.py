@@ -53,23 +53,59 @@ def quadratic_head(q, k, v, eps: float, simple: bool) -> np.ndarray:
     return num / (a.sum(axis=1) + eps)[:, None]
 
 
+def output_head(q, s, z, eps: float, simple: bool) -> np.ndarray:
+    """Last step of the forward for one (batch, head), from a given state:
+    O = phi(Q) S / (phi(Q) z + eps), or phi(Q) S for simple_la (FBi-LA
+    README, intro and "Update" 2024-12-28)."""
+    qt = phi(q)
+    num = qt @ s
+    if simple:
+        return num
+    den = qt @ z + eps
+    return num / den[:, None]
+
+
 def fwd_head(q, k, v, eps: float, simple: bool):
     """Linear form for one (batch, head): returns (O, S, z).
 
     S = phi(K)^T V (D x D, S[i, j] = sum_t phi(k_t)[i] v_t[j]),
-    z = sum_t phi(k_t), O = phi(Q) S / (phi(Q) z + eps), or phi(Q) S for
-    simple_la (FBi-LA README, intro and "Update" 2024-12-28).
+    z = sum_t phi(k_t), then O from output_head.
     """
+    s, z = state_head(k, v)
+    return output_head(q, s, z, eps, simple), s, z
+
+
+def bwd_q_side_head(q, do, s, z, eps: float, simple: bool):
+    """Q side of the backward for one (batch, head), from the forward state.
+
+    Returns (dQ, dS, dz) for the rows given (dS and dz summed over them):
+      u_t   = S dO_t
+      den_t = phi(q_t) . z + eps,  r_t = phi(q_t) . u_t,  c_t = -r_t / den_t^2
+      dphi(q_t) = u_t / den_t + c_t z            (simple_la: u_t)
+      dS    = sum_t phi(q_t) (dO_t / den_t)^T    (simple_la: sum phi(q_t) dO_t^T)
+      dz    = sum_t c_t phi(q_t)                 (simple_la: 0)
+      dQ = dphi(q) * phi'(q)
+    """
+    do = np.asarray(do, dtype=np.float64)
+    qt = phi(q)
+    u = do @ s.T  # row t is S dO_t
+    if simple:
+        return u * dphi(q), qt.T @ do, np.zeros_like(z)
+    den = qt @ z + eps
+    r = np.einsum("td,td->t", qt, u)
+    c = -r / den**2
+    dqt = u / den[:, None] + c[:, None] * z[None, :]
+    return dqt * dphi(q), qt.T @ (do / den[:, None]), c @ qt
+
+
+def bwd_kv_side_head(k, v, ds, dz, simple: bool):
+    """K/V side of the backward for one (batch, head), from (dS, dz):
+    dphi(k_t) = dS v_t + dz (simple_la: dS v_t), dK = dphi(k) * phi'(k),
+    dV_t = dS^T phi(k_t). Returns (dK, dV)."""
     v = np.asarray(v, dtype=np.float64)
     kt = phi(k)
-    qt = phi(q)
-    s = kt.T @ v
-    z = kt.sum(axis=0)
-    num = qt @ s
-    if simple:
-        return num, s, z
-    den = qt @ z + eps
-    return num / den[:, None], s, z
+    dkt = v @ ds.T if simple else v @ ds.T + dz[None, :]
+    return dkt * dphi(k), kt @ ds
 
 
 def bwd_head(q, k, v, do, eps: float, simple: bool):
@@ -77,36 +113,13 @@ def bwd_head(q, k, v, do, eps: float, simple: bool):
 
     Returns (dQ, dK, dV). eps is a constant. Derived by the chain rule from
     fwd_head (the FBi-LA README's "Update" 2024-12-30 names an optimised
-    backward; it prints no formula):
-      u_t   = S dO_t
-      den_t = phi(q_t) . z + eps,  r_t = phi(q_t) . u_t,  c_t = -r_t / den_t^2
-      dphi(q_t) = u_t / den_t + c_t z            (simple_la: u_t)
-      dS    = sum_t phi(q_t) (dO_t / den_t)^T    (simple_la: sum phi(q_t) dO_t^T)
-      dz    = sum_t c_t phi(q_t)                 (simple_la: 0)
-      dphi(k_t) = dS v_t + dz,   dV_t = dS^T phi(k_t)
-      dQ = dphi(q) * phi'(q),  dK = dphi(k) * phi'(k)
+    backward; it prints no formula): the state, then bwd_q_side_head, then
+    bwd_kv_side_head.
     """
-    v = np.asarray(v, dtype=np.float64)
-    do = np.asarray(do, dtype=np.float64)
-    qt = phi(q)
-    kt = phi(k)
-    s = kt.T @ v
-    z = kt.sum(axis=0)
-    u = do @ s.T  # row t is S dO_t
-    if simple:
-        dqt = u
-        ds = qt.T @ do
-        dkt = v @ ds.T
-    else:
-        den = qt @ z + eps
-        r = np.einsum("td,td->t", qt, u)
-        c = -r / den**2
-        dqt = u / den[:, None] + c[:, None] * z[None, :]
-        ds = qt.T @ (do / den[:, None])
-        dz = c @ qt
-        dkt = v @ ds.T + dz[None, :]
-    dv = kt @ ds
-    return dqt * dphi(q), dkt * dphi(k), dv
+    s, z = state_head(k, v)
+    dq, ds, dz = bwd_q_side_head(q, do, s, z, eps, simple)
+    dk, dv = bwd_kv_side_head(k, v, ds, dz, simple)
+    return dq, dk, dv
 
 
 def bwd_leading_terms_head(q, k, v, do, eps: float):

@@ -116,6 +116,51 @@ def test_many_heads_single_slice_ragged(D, dtype, simple):
     check("dV", decode(out["dv"], dtype), dv_ref, dtype)
 
 
+@pytest.mark.parametrize("D,dtype", [(64, "f16"), (128, "bf16")])
+def test_max_head_size_periodic(D, dtype):
+    """The largest head the library accepts (T * D * 2 bytes just below 2^31),
+    one head, ragged against every tile and slice size. The inputs repeat a
+    seeded 4096-row block, so the exact state is n S(block) + S(first r rows)
+    and dS, dz likewise (given the full S, z), and any output row follows from
+    its own inputs and the states: the state and sampled rows of O, dQ, dK,
+    dV are compared with the oracle."""
+    from synth import normal
+    T = (1 << 31) // (D * 2) - 1
+    period, eps = 4096, 1e-6
+    nfull, rem = divmod(T, period)
+    seed = 30_000 + D
+    sigma = 1.0 if D == 64 else 0.5
+    blk = {n: normal((period, D), seed + i, sigma, dtype) for i, n in enumerate(("q", "k", "v", "do"))}
+    print(f"case B1 H1 T={T} D={D} {dtype} period={period} seed={seed}", flush=True)
+    dev = {n: to_device(np.resize(a, (T, D)), dtype).view(1, 1, T, D) for n, a in blk.items()}
+    o, state = la.fwd(dev["q"], dev["k"], dev["v"], eps=eps)
+    dq, dk, dv = la.bwd(dev["q"], dev["k"], dev["v"], dev["do"], state, eps=eps)
+    torch.cuda.synchronize()
+    x = {n: oracle.decode(a, dtype) for n, a in blk.items()}
+    s1, z1 = oracle.state_head(x["k"], x["v"])
+    s2, z2 = oracle.state_head(x["k"][:rem], x["v"][:rem])
+    s_ref, z_ref = nfull * s1 + s2, nfull * z1 + z2
+    s_got, z_got = split_state(state, 1, 1, D)
+    check("S", s_got[0, 0], s_ref, dtype)
+    check("z", z_got[0, 0], z_ref, dtype)
+    _, ds1, dz1 = oracle.bwd_q_side_head(x["q"], x["do"], s_ref, z_ref, eps, False)
+    _, ds2, dz2 = oracle.bwd_q_side_head(x["q"][:rem], x["do"][:rem], s_ref, z_ref, eps, False)
+    ds_ref, dz_ref = nfull * ds1 + ds2, nfull * dz1 + dz2
+    rng = np.random.default_rng(seed)
+    rows = sorted(set([0, 1, period - 1, period, T // 2, T - rem - 1, T - rem, T - 2, T - 1]
+                      + [int(t) for t in rng.integers(0, T, size=48)]))
+    idx = torch.tensor(rows, device="cuda")
+    b = [t % period for t in rows]
+    got = {n: decode(t[0, 0].index_select(0, idx), dtype) for n, t in
+           (("O", o), ("dQ", dq), ("dK", dk), ("dV", dv))}
+    dq_ref, _, _ = oracle.bwd_q_side_head(x["q"][b], x["do"][b], s_ref, z_ref, eps, False)
+    dk_ref, dv_ref = oracle.bwd_kv_side_head(x["k"][b], x["v"][b], ds_ref, dz_ref, False)
+    check("O", got["O"], oracle.output_head(x["q"][b], s_ref, z_ref, eps, False), dtype, " (sampled rows)")
+    check("dQ", got["dQ"], dq_ref, dtype, " (sampled rows)")
+    check("dK", got["dK"], dk_ref, dtype, " (sampled rows)")
+    check("dV", got["dV"], dv_ref, dtype, " (sampled rows)")
+
+
 # ------------------------------------------------------------- full-size workloads
 
 def sampled_heads(n, seed):
