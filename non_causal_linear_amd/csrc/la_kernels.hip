@@ -2059,50 +2059,59 @@ constexpr bool kWaveKernels = (sizeof(T) == 2 && D == 64);
 template <typename T, int D>
 constexpr bool kTileKernels = (sizeof(T) == 2 && D == 128);
 
+template <typename X>
+struct Same {
+    using type = X;
+};
+
+// Launches kernel on stream s with the arguments converted to its parameter
+// types, and returns the status of this launch (not an error that an earlier
+// HIP call of the caller left behind).
+template <typename... KArgs>
+hipError_t launch(void (*kernel)(KArgs...), int64_t blocks, int threads, hipStream_t s,
+                  typename Same<KArgs>::type... args) {
+    void* argv[] = {static_cast<void*>(&args)...};
+    return hipLaunchKernel(reinterpret_cast<const void*>(kernel), dim3((unsigned)blocks), dim3(threads), argv, 0,
+                           s);
+}
+
 // After a split reduction (P > 1 slices per head), sum the partials.
 template <int D>
 hipError_t launch_combine(int P, const float* part, float* outS, float* outz, int64_t BH, hipStream_t s) {
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess || P <= 1) return e;
+    if (P <= 1) return hipSuccess;
     constexpr int E4 = (D * D + D) / 4;
-    const int64_t nblk = BH * ((E4 + kThreads - 1) / kThreads);
-    hipLaunchKernelGGL((combine_kernel<D>), dim3((unsigned)nblk), dim3(kThreads), 0, s, part, P, outS, outz, BH);
-    return hipGetLastError();
+    return launch(combine_kernel<D>, BH * ((E4 + kThreads - 1) / kThreads), kThreads, s, part, P, outS, outz, BH);
 }
 
 template <typename T, int D>
 hipError_t fwd_state_t(const Plan& p, const void* k, const void* v, float* state, void* ws,
                        hipStream_t s) {
     const int64_t nblk = p.BH * p.P;
-    char* w = static_cast<char*>(ws);
-    float* part = reinterpret_cast<float*>(w + p.off_part);
+    float* part = reinterpret_cast<float*>(static_cast<char*>(ws) + p.off_part);
+    const T* kk = static_cast<const T*>(k);
+    const T* vv = static_cast<const T*>(v);
+    float* sz = state + p.BH * D * D;
+    hipError_t e;
     if constexpr (kWaveKernels<T, D>)
-        hipLaunchKernelGGL((fwd_state_w64_kernel<T>), dim3((unsigned)nblk), dim3(kThreads), 0, s,
-                           static_cast<const T*>(k), static_cast<const T*>(v), state,
-                           state + p.BH * D * D, part, p.T, p.P, p.L);
+        e = launch(fwd_state_w64_kernel<T>, nblk, kThreads, s, kk, vv, state, sz, part, p.T, p.P, p.L);
     else if constexpr (kTileKernels<T, D>)
-        hipLaunchKernelGGL((fwd_state_c128_kernel<T>), dim3((unsigned)nblk), dim3(kThreads), 0, s,
-                           static_cast<const T*>(k), static_cast<const T*>(v), state,
-                           state + p.BH * D * D, part, p.T, p.P, p.L);
+        e = launch(fwd_state_c128_kernel<T>, nblk, kThreads, s, kk, vv, state, sz, part, p.T, p.P, p.L);
     else
-        hipLaunchKernelGGL((fwd_state_kernel<T, D>), dim3((unsigned)nblk), dim3(kThreads), 0, s,
-                           static_cast<const T*>(k), static_cast<const T*>(v), state,
-                           state + p.BH * D * D, part, p.T, p.P, p.L);
-    return launch_combine<D>(p.P, part, state, state + p.BH * D * D, p.BH, s);
+        e = launch(fwd_state_kernel<T, D>, nblk, kThreads, s, kk, vv, state, sz, part, p.T, p.P, p.L);
+    if (e != hipSuccess) return e;
+    return launch_combine<D>(p.P, part, state, sz, p.BH, s);
 }
 
 template <typename T, int D>
 hipError_t fwd_output_t(const Plan& p, const void* q, const float* state, void* o, hipStream_t s) {
     const int64_t nblk = p.BH * p.NQ;
+    constexpr int nt = StreamShape<T, D>::kThreads;
+    const T* qq = static_cast<const T*>(q);
+    const float* sz = state + p.BH * D * D;
+    T* oo = static_cast<T*>(o);
     if (p.simple)
-        hipLaunchKernelGGL((fwd_output_kernel<T, D, true>), dim3((unsigned)nblk), dim3(StreamShape<T, D>::kThreads), 0, s,
-                           static_cast<const T*>(q), state, state + p.BH * D * D, static_cast<T*>(o),
-                           p.T, p.NQ, p.LQ, p.eps);
-    else
-        hipLaunchKernelGGL((fwd_output_kernel<T, D, false>), dim3((unsigned)nblk), dim3(StreamShape<T, D>::kThreads), 0, s,
-                           static_cast<const T*>(q), state, state + p.BH * D * D, static_cast<T*>(o),
-                           p.T, p.NQ, p.LQ, p.eps);
-    return hipGetLastError();
+        return launch(fwd_output_kernel<T, D, true>, nblk, nt, s, qq, state, sz, oo, p.T, p.NQ, p.LQ, p.eps);
+    return launch(fwd_output_kernel<T, D, false>, nblk, nt, s, qq, state, sz, oo, p.T, p.NQ, p.LQ, p.eps);
 }
 
 template <typename T, int D>
@@ -2119,28 +2128,25 @@ hipError_t bwd_dq_t(const Plan& p, const void* q, const void* dout, const float*
     T* g = static_cast<T*>(dq);
     float* dS = dst;
     float* dz = dst + p.BH * D * D;
+    hipError_t e;
     if constexpr (kWaveKernels<T, D>) {
-        if (p.simple)
-            hipLaunchKernelGGL((bwd_dq_w64_kernel<T, true>), dim3((unsigned)nblk), dim3(kThreads), 0, s,
-                               qq, dd, sS, sz, g, part, dS, dz, p.T, p.PB, p.LB, p.eps);
-        else
-            hipLaunchKernelGGL((bwd_dq_w64_kernel<T, false>), dim3((unsigned)nblk), dim3(kThreads), 0, s,
-                               qq, dd, sS, sz, g, part, dS, dz, p.T, p.PB, p.LB, p.eps);
+        e = p.simple ? launch(bwd_dq_w64_kernel<T, true>, nblk, kThreads, s, qq, dd, sS, sz, g, part, dS, dz, p.T,
+                              p.PB, p.LB, p.eps)
+                     : launch(bwd_dq_w64_kernel<T, false>, nblk, kThreads, s, qq, dd, sS, sz, g, part, dS, dz, p.T,
+                              p.PB, p.LB, p.eps);
     } else if constexpr (kTileKernels<T, D>) {
-        if (p.simple)
-            hipLaunchKernelGGL((bwd_dq_tile_kernel<T, D, true>), dim3((unsigned)nblk), dim3(BwdQTile<D>::kThreads), 0, s,
-                               qq, dd, sS, sz, g, part, dS, dz, p.T, p.PB, p.LB, p.eps);
-        else
-            hipLaunchKernelGGL((bwd_dq_tile_kernel<T, D, false>), dim3((unsigned)nblk), dim3(BwdQTile<D>::kThreads), 0, s,
-                               qq, dd, sS, sz, g, part, dS, dz, p.T, p.PB, p.LB, p.eps);
+        constexpr int nt = BwdQTile<D>::kThreads;
+        e = p.simple ? launch(bwd_dq_tile_kernel<T, D, true>, nblk, nt, s, qq, dd, sS, sz, g, part, dS, dz, p.T,
+                              p.PB, p.LB, p.eps)
+                     : launch(bwd_dq_tile_kernel<T, D, false>, nblk, nt, s, qq, dd, sS, sz, g, part, dS, dz, p.T,
+                              p.PB, p.LB, p.eps);
     } else {
-        if (p.simple)
-            hipLaunchKernelGGL((bwd_dq_kernel<T, D, true>), dim3((unsigned)nblk), dim3(kThreads), 0, s,
-                               qq, dd, sS, sz, g, part, dS, dz, p.T, p.PB, p.LB, p.eps);
-        else
-            hipLaunchKernelGGL((bwd_dq_kernel<T, D, false>), dim3((unsigned)nblk), dim3(kThreads), 0, s,
-                               qq, dd, sS, sz, g, part, dS, dz, p.T, p.PB, p.LB, p.eps);
+        e = p.simple ? launch(bwd_dq_kernel<T, D, true>, nblk, kThreads, s, qq, dd, sS, sz, g, part, dS, dz, p.T,
+                              p.PB, p.LB, p.eps)
+                     : launch(bwd_dq_kernel<T, D, false>, nblk, kThreads, s, qq, dd, sS, sz, g, part, dS, dz, p.T,
+                              p.PB, p.LB, p.eps);
     }
+    if (e != hipSuccess) return e;
     return launch_combine<D>(p.PB, part, dS, dz, p.BH, s);
 }
 
@@ -2148,16 +2154,16 @@ template <typename T, int D>
 hipError_t bwd_dkv_t(const Plan& p, const void* k, const void* v, void* dk, void* dv, void* ws,
                      hipStream_t s) {
     const int64_t nblk = p.BH * p.NK;
+    constexpr int nt = StreamShape<T, D>::kThreads;
     const float* dst = reinterpret_cast<const float*>(static_cast<char*>(ws) + p.off_dstate);
+    const float* dz = dst + p.BH * D * D;
+    const T* kk = static_cast<const T*>(k);
+    const T* vv = static_cast<const T*>(v);
+    T* gk = static_cast<T*>(dk);
+    T* gv = static_cast<T*>(dv);
     if (p.simple)
-        hipLaunchKernelGGL((bwd_dkv_kernel<T, D, true>), dim3((unsigned)nblk), dim3(StreamShape<T, D>::kThreads), 0, s,
-                           static_cast<const T*>(k), static_cast<const T*>(v), dst, dst + p.BH * D * D,
-                           static_cast<T*>(dk), static_cast<T*>(dv), p.T, p.NK, p.LK);
-    else
-        hipLaunchKernelGGL((bwd_dkv_kernel<T, D, false>), dim3((unsigned)nblk), dim3(StreamShape<T, D>::kThreads), 0, s,
-                           static_cast<const T*>(k), static_cast<const T*>(v), dst, dst + p.BH * D * D,
-                           static_cast<T*>(dk), static_cast<T*>(dv), p.T, p.NK, p.LK);
-    return hipGetLastError();
+        return launch(bwd_dkv_kernel<T, D, true>, nblk, nt, s, kk, vv, dst, dz, gk, gv, p.T, p.NK, p.LK);
+    return launch(bwd_dkv_kernel<T, D, false>, nblk, nt, s, kk, vv, dst, dz, gk, gv, p.T, p.NK, p.LK);
 }
 
 // dtype codes follow la_dtype: 0 = f32, 1 = f16, 2 = bf16.

@@ -330,3 +330,20 @@ def test_non_default_stream():
         o, st = la.fwd(dev["q"], dev["k"], dev["v"])
     s.synchronize()
     assert bytes_equal(o, ref_o) and bytes_equal(st, ref_st)
+
+
+def test_earlier_hip_error_is_not_reported():
+    """A HIP error that an earlier, unrelated call left in this thread (here
+    an attribute query for a device that does not exist) is not mistaken for
+    a failed launch of the library's kernels."""
+    import ctypes
+    hip = ctypes.CDLL("libamdhip64.so.7")
+    val = ctypes.c_int(0)
+    status = hip.hipDeviceGetAttribute(ctypes.byref(val), ctypes.c_int(0), ctypes.c_int(1 << 20))
+    assert status != 0, "the query for a nonexistent device was expected to fail"
+    w = Workload("stale-error", 1, 2, 300, 64, "f16", seed=11)
+    x = make_inputs(w, with_grad=True)
+    _, out = run(w, x, bwd=True)
+    o_ref, _, _ = oracle.fwd(x["q"], x["k"], x["v"], w.dtype, w.eps, False)
+    check("O", decode(out["o"], w.dtype), o_ref, w.dtype)
+    hip.hipGetLastError()
