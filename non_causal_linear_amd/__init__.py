@@ -110,6 +110,17 @@ def _tensor(x: torch.Tensor, like: torch.Tensor | None, name: str) -> torch.Tens
     return x
 
 
+def _state(state, prob: Problem, device: torch.device, name: str = "state") -> torch.Tensor:
+    """A state buffer: contiguous fp32 on the tensors' device, large enough."""
+    if not isinstance(state, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if state.dtype != torch.float32 or state.device != device or not state.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous float32 tensor on {device}")
+    if state.numel() * 4 < state_bytes(prob):
+        raise ValueError(f"{name} holds {state.numel() * 4} bytes; the problem needs {state_bytes(prob)}")
+    return state
+
+
 def _ptr(x: torch.Tensor | None):
     return None if x is None else ctypes.c_void_p(x.data_ptr())
 
@@ -150,7 +161,10 @@ def workspace(prob: Problem, device) -> torch.Tensor:
 
 
 def _ws(prob, device, ws):
-    ws = workspace(prob, device) if ws is None else ws
+    if ws is None:
+        ws = workspace(prob, device)
+    elif not isinstance(ws, torch.Tensor) or ws.device != torch.device(device) or not ws.is_contiguous():
+        raise ValueError(f"ws must be a contiguous tensor on {device}")
     return ws, ctypes.c_size_t(ws.numel() * ws.element_size())
 
 
@@ -159,7 +173,7 @@ def fwd_state(k, v, *, eps=1e-6, simple=False, state=None, ws=None):
     _tensor(k, None, "k")
     _tensor(v, k, "v")
     prob = make_problem(k.shape, k.dtype, eps, simple)
-    state = new_state(prob, k.device) if state is None else state
+    state = new_state(prob, k.device) if state is None else _state(state, prob, k.device)
     ws, wsb = _ws(prob, k.device, ws)
     _check(lib().la_fwd_state(ctypes.byref(prob), _ptr(k), _ptr(v), _ptr(state), _ptr(ws), wsb,
                               _stream(k.device)))
@@ -170,6 +184,7 @@ def fwd_output(q, state, *, eps=1e-6, simple=False, out=None):
     """Step 4: O from Q and a complete state."""
     _tensor(q, None, "q")
     prob = make_problem(q.shape, q.dtype, eps, simple)
+    _state(state, prob, q.device)
     out = torch.empty_like(q) if out is None else _tensor(out, q, "out")
     _check(lib().la_fwd_output(ctypes.byref(prob), _ptr(q), _ptr(state), _ptr(out), _stream(q.device)))
     return out
@@ -182,7 +197,7 @@ def fwd(q, k, v, *, eps=1e-6, simple=False, out=None, state=None, ws=None):
     _tensor(v, q, "v")
     prob = make_problem(q.shape, q.dtype, eps, simple)
     out = torch.empty_like(q) if out is None else _tensor(out, q, "out")
-    state = new_state(prob, q.device) if state is None else state
+    state = new_state(prob, q.device) if state is None else _state(state, prob, q.device)
     ws, wsb = _ws(prob, q.device, ws)
     _check(lib().la_fwd(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(state),
                         _ptr(ws), wsb, _stream(q.device)))
@@ -194,6 +209,7 @@ def bwd_dq(q, do, state, *, eps=1e-6, simple=False, dq=None, ws=None):
     _tensor(q, None, "q")
     _tensor(do, q, "do")
     prob = make_problem(q.shape, q.dtype, eps, simple)
+    _state(state, prob, q.device)
     dq = torch.empty_like(q) if dq is None else _tensor(dq, q, "dq")
     ws, wsb = _ws(prob, q.device, ws)
     _check(lib().la_bwd_dq(ctypes.byref(prob), _ptr(q), _ptr(do), _ptr(state), _ptr(dq), _ptr(ws), wsb,
@@ -220,6 +236,7 @@ def bwd(q, k, v, do, state, *, eps=1e-6, simple=False, dq=None, dk=None, dv=None
     for n, x in (("k", k), ("v", v), ("do", do)):
         _tensor(x, q, n)
     prob = make_problem(q.shape, q.dtype, eps, simple)
+    _state(state, prob, q.device)
     dq = torch.empty_like(q) if dq is None else _tensor(dq, q, "dq")
     dk = torch.empty_like(q) if dk is None else _tensor(dk, q, "dk")
     dv = torch.empty_like(q) if dv is None else _tensor(dv, q, "dv")

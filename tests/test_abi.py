@@ -209,3 +209,19 @@ def test_binding_marshalling_rejects_cpu_tensors():
         la.make_problem((1, 4, 64), torch.float16, 1e-6, False)
     with pytest.raises(ValueError):
         la.make_problem((1, 1, 4, 64), torch.int32, 1e-6, False)
+
+
+def test_binding_validates_state_buffers():
+    """A caller-supplied state must be contiguous fp32 on the tensors' device and
+    hold la_state_bytes(); the check runs before any call into the library."""
+    torch = pytest.importorskip("torch")
+    dev = torch.device("cpu")
+    prob = la.make_problem((2, 3, 100, 64), torch.float16, 1e-6, False)
+    need = la.state_bytes(prob) // 4
+    assert la._state(torch.zeros(need), prob, dev).numel() == need
+    for bad in (torch.zeros(need - 1), torch.zeros(need, dtype=torch.float64),
+                torch.zeros(2 * need)[::2], torch.zeros(need, dtype=torch.float16)):
+        with pytest.raises(ValueError):
+            la._state(bad, prob, dev)
+    with pytest.raises(TypeError):
+        la._state(None, prob, dev)
