@@ -347,3 +347,32 @@ def test_earlier_hip_error_is_not_reported():
     o_ref, _, _ = oracle.fwd(x["q"], x["k"], x["v"], w.dtype, w.eps, False)
     check("O", decode(out["o"], w.dtype), o_ref, w.dtype)
     hip.hipGetLastError()
+
+
+def _digest_of_run(B, H, T, D, dtype, seed):
+    """sha256 over O, state, dQ, dK, dV of one fixed problem (used in two processes)."""
+    import hashlib
+    w = Workload("proc", B, H, T, D, dtype, seed=seed)
+    x = make_inputs(w, with_grad=True)
+    _, out = run(w, x, bwd=True)
+    h = hashlib.sha256()
+    for n in ("o", "state", "dq", "dk", "dv"):
+        h.update(out[n].contiguous().view(torch.uint8).cpu().numpy().tobytes())
+    return h.hexdigest()
+
+
+def test_outputs_identical_across_processes():
+    """The work split is a pure function of the shape and no reduction uses
+    atomics, so a second process computes the same bytes."""
+    import os
+    import subprocess
+    import sys
+    args = (4, 8, 5000, 64, "f16", 77)
+    mine = _digest_of_run(*args)
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    code = ("import sys; sys.path.insert(0, %r); import torch; import non_causal_linear_amd as la; la.lib(); "
+            "from tests.test_gpu_parity import _digest_of_run; print(_digest_of_run%r)" % (root, args))
+    print("case: second process, B4 H8 T5000 D64 f16 seed 77", flush=True)
+    res = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300, cwd=root)
+    assert res.returncode == 0, res.stderr[-2000:]
+    assert res.stdout.strip().splitlines()[-1] == mine
