@@ -78,6 +78,8 @@ def fwd_head(q, k, v, eps: float, simple: bool):
 def bwd_q_side_head(q, do, s, z, eps: float, simple: bool):
     """Q side of the backward for one (batch, head), from the forward state.
 
+    The chain rule applied to the formula of fwd_head (the FBi-LA README's
+    "Update" 2024-12-30 names an optimised backward; it prints no formula).
     Returns (dQ, dS, dz) for the rows given (dS and dz summed over them):
       u_t   = S dO_t
       den_t = phi(q_t) . z + eps,  r_t = phi(q_t) . u_t,  c_t = -r_t / den_t^2
@@ -99,7 +101,9 @@ def bwd_q_side_head(q, do, s, z, eps: float, simple: bool):
 
 
 def bwd_kv_side_head(k, v, ds, dz, simple: bool):
-    """K/V side of the backward for one (batch, head), from (dS, dz):
+    """K/V side of the backward for one (batch, head), from (dS, dz), by the
+    chain rule through S = phi(K)^T V and z = sum_t phi(k_t) (FBi-LA README,
+    "Update" 2024-12-30; no formula printed there):
     dphi(k_t) = dS v_t + dz (simple_la: dS v_t), dK = dphi(k) * phi'(k),
     dV_t = dS^T phi(k_t). Returns (dK, dV)."""
     v = np.asarray(v, dtype=np.float64)

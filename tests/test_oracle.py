@@ -352,3 +352,26 @@ def test_leading_terms_cancel_at_t1():
     den = qt @ kt + eps
     np.testing.assert_allclose(dq[0], oracle.dphi(q[0]) * kt * (v[0] @ do[0]) * eps / den**2,
                                rtol=1e-6, atol=1e-300)
+
+
+@pytest.mark.parametrize("simple", [False, True])
+def test_backward_halves_compose_and_add_over_tokens(simple):
+    """The Q side and K/V side of the backward, taken one at a time: with the
+    full state they give bwd_head's dQ, their dS and dz add up over any split
+    of the tokens (a sum over t), and the K/V side then gives bwd_head's dK, dV."""
+    T, D = 23, 6
+    q, k, v, do = (rand((T, D), 91 + i) for i in range(4))
+    dq_ref, dk_ref, dv_ref = oracle.bwd_head(q, k, v, do, 0.25, simple)
+    s, z = oracle.state_head(k, v)
+    dq, ds, dz = oracle.bwd_q_side_head(q, do, s, z, 0.25, simple)
+    np.testing.assert_allclose(dq, dq_ref, rtol=1e-13, atol=1e-13)
+    _, ds_a, dz_a = oracle.bwd_q_side_head(q[:9], do[:9], s, z, 0.25, simple)
+    dq_b, ds_b, dz_b = oracle.bwd_q_side_head(q[9:], do[9:], s, z, 0.25, simple)
+    np.testing.assert_allclose(ds_a + ds_b, ds, rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(dz_a + dz_b, dz, rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(dq_b, dq_ref[9:], rtol=1e-13, atol=1e-13)
+    dk, dv = oracle.bwd_kv_side_head(k, v, ds, dz, simple)
+    np.testing.assert_allclose(dk, dk_ref, rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(dv, dv_ref, rtol=1e-13, atol=1e-13)
+    o = oracle.output_head(q, s, z, 0.25, simple)
+    np.testing.assert_allclose(o, oracle.quadratic_head(q, k, v, 0.25, simple), rtol=1e-12, atol=1e-13)
