@@ -18,7 +18,7 @@ import os
 import torch
 
 __all__ = [
-    "LAError", "lib", "fwd", "bwd", "fwd_state", "fwd_output", "bwd_dq", "bwd_dkv",
+    "LAError", "lib", "fwd", "bwd", "fwd_state", "fwd_output", "bwd_dq", "bwd_dkv", "linear_attention",
     "state_bytes", "workspace_bytes", "new_state", "workspace", "Problem",
     "LA_F32", "LA_F16", "LA_BF16", "LA_SIMPLE", "EXPORTS",
 ]
@@ -244,3 +244,30 @@ def bwd(q, k, v, do, state, *, eps=1e-6, simple=False, dq=None, dk=None, dv=None
     _check(lib().la_bwd(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(state),
                         _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws), wsb, _stream(q.device)))
     return dq, dk, dv
+
+
+class _LinearAttention(torch.autograd.Function):
+    """Autograd node over la_fwd / la_bwd. The forward keeps the fp32 state
+    (S, z) for the backward, which therefore reads Q, K, V, dO and the state
+    and does not recompute S."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, eps, simple):
+        q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
+        o, state = fwd(q, k, v, eps=eps, simple=simple)
+        ctx.save_for_backward(q, k, v, state)
+        ctx.eps, ctx.simple = eps, simple
+        return o
+
+    @staticmethod
+    def backward(ctx, do):
+        q, k, v, state = ctx.saved_tensors
+        dq, dk, dv = bwd(q, k, v, do.contiguous(), state, eps=ctx.eps, simple=ctx.simple)
+        return dq, dk, dv, None, None
+
+
+def linear_attention(q, k, v, *, eps: float = 1e-6, simple: bool = False) -> torch.Tensor:
+    """O = phi(Q) S / (phi(Q) z + eps) (or phi(Q) S with simple=True), with
+    gradients for q, k and v through the library's backward. Tensors are
+    [B, H, T, D] on a GPU in float32, float16 or bfloat16, D in {64, 128}."""
+    return _LinearAttention.apply(q, k, v, float(eps), bool(simple))

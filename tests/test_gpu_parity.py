@@ -376,3 +376,22 @@ def test_outputs_identical_across_processes():
     res = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300, cwd=root)
     assert res.returncode == 0, res.stderr[-2000:]
     assert res.stdout.strip().splitlines()[-1] == mine
+
+
+@pytest.mark.parametrize("simple", [False, True], ids=["norm", "simple"])
+def test_autograd_wrapper_matches_oracle(simple):
+    """linear_attention under torch.autograd: the output and the gradients of
+    sum(O * dO) for q, k, v against the oracle."""
+    w = Workload("autograd", 2, 3, 777, 64, "bf16", simple=simple, seed=51)
+    x = make_inputs(w, with_grad=True)
+    dev = {n: to_device(a, w.dtype) for n, a in x.items()}
+    q, k, v = (dev[n].clone().requires_grad_(True) for n in ("q", "k", "v"))
+    o = la.linear_attention(q, k, v, eps=w.eps, simple=simple)
+    (o.float() * dev["do"].float()).sum().backward()
+    torch.cuda.synchronize()
+    o_ref, _, _ = oracle.fwd(x["q"], x["k"], x["v"], w.dtype, w.eps, simple)
+    dq_ref, dk_ref, dv_ref = oracle.bwd(x["q"], x["k"], x["v"], x["do"], w.dtype, w.eps, simple)
+    check("O", decode(o, w.dtype), o_ref, w.dtype)
+    check("dQ", decode(q.grad, w.dtype), dq_ref, w.dtype)
+    check("dK", decode(k.grad, w.dtype), dk_ref, w.dtype)
+    check("dV", decode(v.grad, w.dtype), dv_ref, w.dtype)
