@@ -14,7 +14,9 @@
  * L = sum(O * dO) with eps held constant.
  *
  * Layout. Every tensor q, k, v, o, dout, dq, dk, dv is a dense row-major
- * [B, H, T, D] array of `dtype` elements (D contiguous), 16-byte aligned.
+ * [B, H, T, D] array of `dtype` elements (D contiguous), 16-byte aligned;
+ * with LA_LAYOUT_BTHD in flags they are [B, T, H, D] instead (each row of D
+ * elements still contiguous, heads interleaved token by token).
  * `state` is fp32: B*H blocks of S (D*D floats, S[i][j] at i*D + j) followed by
  * B*H blocks of z (D floats); la_state_bytes() gives its size.
  *
@@ -53,7 +55,7 @@
 extern "C" {
 #endif
 
-#define LA_VERSION 1
+#define LA_VERSION 2
 
 typedef enum {
     LA_F32 = 0,
@@ -64,7 +66,7 @@ typedef enum {
 typedef enum {
     LA_OK = 0,
     LA_ERR_NULL = 1,       /* a required pointer is NULL                      */
-    LA_ERR_SHAPE = 2,      /* B, H or T negative; B*H > 2^24; T*D*elt >= 2^31 */
+    LA_ERR_SHAPE = 2,      /* B, H or T negative; B*H > 2^24; head too large  */
     LA_ERR_DTYPE = 3,      /* dtype not one of la_dtype                       */
     LA_ERR_HEAD_DIM = 4,   /* D not supported (64 and 128 are)                */
     LA_ERR_FLAGS = 5,      /* unknown bit in flags                            */
@@ -77,15 +79,20 @@ typedef enum {
 
 /* Drop the denominator: simple_la (FBi-LA README, "Update" 2024-12-28). */
 #define LA_SIMPLE 0x1u
+/* Tensors are [B, T, H, D] rather than [B, H, T, D]. */
+#define LA_LAYOUT_BTHD 0x2u
 
 /* Problem description shared by every call. B, H, T >= 0 (a zero size is an
- * empty problem: nothing to compute, LA_OK), B*H <= 2^24, one head's rows
- * below 2^31 bytes (T * D * element size), D in {64, 128}, eps >= 0 and
- * finite (used only in normalised mode). */
+ * empty problem: nothing to compute, LA_OK), B*H <= 2^24, D in {64, 128},
+ * eps >= 0 and finite (used only in normalised mode). One head must span
+ * less than 2^31 bytes, addressed with 32-bit offsets: T * D * elt < 2^31 in
+ * [B, H, T, D]; (T + 1024) * H * D * elt < 2^31 in [B, T, H, D], where a
+ * head's rows are H * D elements apart (the 1024 rows keep the offsets of the
+ * padded blocks past a slice below 2^31 too). elt is the element size. */
 typedef struct {
     int64_t B, H, T, D;
     int32_t dtype;   /* la_dtype */
-    uint32_t flags;  /* 0 or LA_SIMPLE */
+    uint32_t flags;  /* LA_SIMPLE and / or LA_LAYOUT_BTHD */
     float eps;
 } la_problem;
 

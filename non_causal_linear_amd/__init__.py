@@ -20,13 +20,15 @@ import torch
 __all__ = [
     "LAError", "lib", "fwd", "bwd", "fwd_state", "fwd_output", "bwd_dq", "bwd_dkv", "linear_attention",
     "state_bytes", "workspace_bytes", "new_state", "workspace", "Problem",
-    "LA_F32", "LA_F16", "LA_BF16", "LA_SIMPLE", "EXPORTS",
+    "LA_F32", "LA_F16", "LA_BF16", "LA_SIMPLE", "LA_LAYOUT_BTHD", "EXPORTS",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libla.so")
 
 LA_F32, LA_F16, LA_BF16 = 0, 1, 2
 LA_SIMPLE = 0x1
+LA_LAYOUT_BTHD = 0x2
+LAYOUTS = ("bhtd", "bthd")
 DTYPE_CODE = {torch.float32: LA_F32, torch.float16: LA_F16, torch.bfloat16: LA_BF16}
 
 # Every symbol include/la.h declares.
@@ -89,13 +91,21 @@ def _check(status: int) -> None:
         raise LAError(status, lib().la_status_str(status).decode())
 
 
-def make_problem(shape, dtype: torch.dtype, eps: float, simple: bool) -> Problem:
+def make_problem(shape, dtype: torch.dtype, eps: float, simple: bool, layout: str = "bhtd") -> Problem:
+    """Problem for tensors of ``shape``: [B, H, T, D] (layout "bhtd") or
+    [B, T, H, D] (layout "bthd")."""
+    if layout not in LAYOUTS:
+        raise ValueError(f"layout must be one of {LAYOUTS}, got {layout!r}")
     if len(shape) != 4:
-        raise ValueError(f"expected a [B, H, T, D] tensor, got shape {tuple(shape)}")
+        raise ValueError(f"expected a 4-d tensor ({layout}), got shape {tuple(shape)}")
     if dtype not in DTYPE_CODE:
         raise ValueError(f"unsupported dtype {dtype}")
-    B, H, T, D = (int(x) for x in shape)
-    return Problem(B, H, T, D, DTYPE_CODE[dtype], LA_SIMPLE if simple else 0, float(eps))
+    if layout == "bhtd":
+        B, H, T, D = (int(x) for x in shape)
+    else:
+        B, T, H, D = (int(x) for x in shape)
+    flags = (LA_SIMPLE if simple else 0) | (LA_LAYOUT_BTHD if layout == "bthd" else 0)
+    return Problem(B, H, T, D, DTYPE_CODE[dtype], flags, float(eps))
 
 
 def _tensor(x: torch.Tensor, like: torch.Tensor | None, name: str) -> torch.Tensor:
@@ -168,11 +178,11 @@ def _ws(prob, device, ws):
     return ws, ctypes.c_size_t(ws.numel() * ws.element_size())
 
 
-def fwd_state(k, v, *, eps=1e-6, simple=False, state=None, ws=None):
+def fwd_state(k, v, *, eps=1e-6, simple=False, layout="bhtd", state=None, ws=None):
     """Steps 1-3: the fp32 state (S, z) of phi(K), V."""
     _tensor(k, None, "k")
     _tensor(v, k, "v")
-    prob = make_problem(k.shape, k.dtype, eps, simple)
+    prob = make_problem(k.shape, k.dtype, eps, simple, layout)
     state = new_state(prob, k.device) if state is None else _state(state, prob, k.device)
     ws, wsb = _ws(prob, k.device, ws)
     _check(lib().la_fwd_state(ctypes.byref(prob), _ptr(k), _ptr(v), _ptr(state), _ptr(ws), wsb,
@@ -180,22 +190,22 @@ def fwd_state(k, v, *, eps=1e-6, simple=False, state=None, ws=None):
     return state
 
 
-def fwd_output(q, state, *, eps=1e-6, simple=False, out=None):
+def fwd_output(q, state, *, eps=1e-6, simple=False, layout="bhtd", out=None):
     """Step 4: O from Q and a complete state."""
     _tensor(q, None, "q")
-    prob = make_problem(q.shape, q.dtype, eps, simple)
+    prob = make_problem(q.shape, q.dtype, eps, simple, layout)
     _state(state, prob, q.device)
     out = torch.empty_like(q) if out is None else _tensor(out, q, "out")
     _check(lib().la_fwd_output(ctypes.byref(prob), _ptr(q), _ptr(state), _ptr(out), _stream(q.device)))
     return out
 
 
-def fwd(q, k, v, *, eps=1e-6, simple=False, out=None, state=None, ws=None):
+def fwd(q, k, v, *, eps=1e-6, simple=False, layout="bhtd", out=None, state=None, ws=None):
     """O = phi(Q) S / (phi(Q) z + eps) (or phi(Q) S); returns (O, state)."""
     _tensor(q, None, "q")
     _tensor(k, q, "k")
     _tensor(v, q, "v")
-    prob = make_problem(q.shape, q.dtype, eps, simple)
+    prob = make_problem(q.shape, q.dtype, eps, simple, layout)
     out = torch.empty_like(q) if out is None else _tensor(out, q, "out")
     state = new_state(prob, q.device) if state is None else _state(state, prob, q.device)
     ws, wsb = _ws(prob, q.device, ws)
@@ -204,11 +214,11 @@ def fwd(q, k, v, *, eps=1e-6, simple=False, out=None, state=None, ws=None):
     return out, state
 
 
-def bwd_dq(q, do, state, *, eps=1e-6, simple=False, dq=None, ws=None):
+def bwd_dq(q, do, state, *, eps=1e-6, simple=False, layout="bhtd", dq=None, ws=None):
     """Steps 5-6: dQ; leaves dS, dz in the workspace for bwd_dkv."""
     _tensor(q, None, "q")
     _tensor(do, q, "do")
-    prob = make_problem(q.shape, q.dtype, eps, simple)
+    prob = make_problem(q.shape, q.dtype, eps, simple, layout)
     _state(state, prob, q.device)
     dq = torch.empty_like(q) if dq is None else _tensor(dq, q, "dq")
     ws, wsb = _ws(prob, q.device, ws)
@@ -217,11 +227,11 @@ def bwd_dq(q, do, state, *, eps=1e-6, simple=False, dq=None, ws=None):
     return dq
 
 
-def bwd_dkv(k, v, *, eps=1e-6, simple=False, dk=None, dv=None, ws=None):
+def bwd_dkv(k, v, *, eps=1e-6, simple=False, layout="bhtd", dk=None, dv=None, ws=None):
     """Step 7: dK, dV from the backward state bwd_dq left in the same workspace."""
     _tensor(k, None, "k")
     _tensor(v, k, "v")
-    prob = make_problem(k.shape, k.dtype, eps, simple)
+    prob = make_problem(k.shape, k.dtype, eps, simple, layout)
     dk = torch.empty_like(k) if dk is None else _tensor(dk, k, "dk")
     dv = torch.empty_like(k) if dv is None else _tensor(dv, k, "dv")
     ws, wsb = _ws(prob, k.device, ws)
@@ -230,12 +240,12 @@ def bwd_dkv(k, v, *, eps=1e-6, simple=False, dk=None, dv=None, ws=None):
     return dk, dv
 
 
-def bwd(q, k, v, do, state, *, eps=1e-6, simple=False, dq=None, dk=None, dv=None, ws=None):
+def bwd(q, k, v, do, state, *, eps=1e-6, simple=False, layout="bhtd", dq=None, dk=None, dv=None, ws=None):
     """dQ, dK, dV of L = sum(O * dO), from the state fwd returned."""
     _tensor(q, None, "q")
     for n, x in (("k", k), ("v", v), ("do", do)):
         _tensor(x, q, n)
-    prob = make_problem(q.shape, q.dtype, eps, simple)
+    prob = make_problem(q.shape, q.dtype, eps, simple, layout)
     _state(state, prob, q.device)
     dq = torch.empty_like(q) if dq is None else _tensor(dq, q, "dq")
     dk = torch.empty_like(q) if dk is None else _tensor(dk, q, "dk")
@@ -252,22 +262,23 @@ class _LinearAttention(torch.autograd.Function):
     and does not recompute S."""
 
     @staticmethod
-    def forward(ctx, q, k, v, eps, simple):
+    def forward(ctx, q, k, v, eps, simple, layout):
         q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
-        o, state = fwd(q, k, v, eps=eps, simple=simple)
+        o, state = fwd(q, k, v, eps=eps, simple=simple, layout=layout)
         ctx.save_for_backward(q, k, v, state)
-        ctx.eps, ctx.simple = eps, simple
+        ctx.eps, ctx.simple, ctx.layout = eps, simple, layout
         return o
 
     @staticmethod
     def backward(ctx, do):
         q, k, v, state = ctx.saved_tensors
-        dq, dk, dv = bwd(q, k, v, do.contiguous(), state, eps=ctx.eps, simple=ctx.simple)
-        return dq, dk, dv, None, None
+        dq, dk, dv = bwd(q, k, v, do.contiguous(), state, eps=ctx.eps, simple=ctx.simple, layout=ctx.layout)
+        return dq, dk, dv, None, None, None
 
 
-def linear_attention(q, k, v, *, eps: float = 1e-6, simple: bool = False) -> torch.Tensor:
+def linear_attention(q, k, v, *, eps: float = 1e-6, simple: bool = False, layout: str = "bhtd") -> torch.Tensor:
     """O = phi(Q) S / (phi(Q) z + eps) (or phi(Q) S with simple=True), with
     gradients for q, k and v through the library's backward. Tensors are
-    [B, H, T, D] on a GPU in float32, float16 or bfloat16, D in {64, 128}."""
-    return _LinearAttention.apply(q, k, v, float(eps), bool(simple))
+    [B, H, T, D] (layout "bhtd") or [B, T, H, D] (layout "bthd") on a GPU in
+    float32, float16 or bfloat16, D in {64, 128}."""
+    return _LinearAttention.apply(q, k, v, float(eps), bool(simple), layout)

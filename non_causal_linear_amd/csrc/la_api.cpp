@@ -19,8 +19,11 @@ constexpr int64_t kMinSlice = 256;
 // Largest B*H accepted (grid sizes stay below 2^31).
 constexpr int64_t kMaxHeads = int64_t(1) << 24;
 // One head's rows are addressed through a buffer descriptor with 32-bit
-// offsets: T * D * sizeof(element) must stay below 2^31 bytes.
+// offsets: a head's span must stay below 2^31 bytes. In [B, T, H, D] the
+// span is counted with kRowSlack more rows, which covers the padded blocks a
+// workgroup may address past the end of its slice.
 constexpr int64_t kMaxHeadBytes = (int64_t(1) << 31) - 1;
+constexpr int64_t kRowSlack = 1024;
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -50,8 +53,13 @@ la_status check_problem(const la_problem* p) {
     if (p->D != 64 && p->D != 128) return LA_ERR_HEAD_DIM;
     if (p->B < 0 || p->H < 0 || p->T < 0) return LA_ERR_SHAPE;
     if (p->B > kMaxHeads || p->H > kMaxHeads || p->B * p->H > kMaxHeads) return LA_ERR_SHAPE;
-    if (p->T > kMaxHeadBytes / (p->D * (p->dtype == LA_F32 ? 4 : 2))) return LA_ERR_SHAPE;
-    if (p->flags & ~LA_SIMPLE) return LA_ERR_FLAGS;
+    if (p->flags & ~(LA_SIMPLE | LA_LAYOUT_BTHD)) return LA_ERR_FLAGS;
+    const int64_t row_bytes = p->D * (p->dtype == LA_F32 ? 4 : 2);
+    if (p->flags & LA_LAYOUT_BTHD) {
+        if (p->H > 0 && p->T + kRowSlack > kMaxHeadBytes / (p->H * row_bytes)) return LA_ERR_SHAPE;
+    } else if (p->T > kMaxHeadBytes / row_bytes) {
+        return LA_ERR_SHAPE;
+    }
     if (!(p->eps >= 0.f) || !isfinite(p->eps)) return LA_ERR_EPS;
     return LA_OK;
 }
@@ -66,6 +74,16 @@ la::Plan make_plan(const la_problem* p) {
     pl.dtype = p->dtype;
     pl.simple = (p->flags & LA_SIMPLE) != 0;
     pl.eps = p->eps;
+    pl.lay.H = p->H > 0 ? p->H : 1;
+    if (p->flags & LA_LAYOUT_BTHD) {
+        pl.lay.sb = p->T * p->H * p->D;
+        pl.lay.sh = p->D;
+        pl.lay.rs = p->H * p->D;
+    } else {
+        pl.lay.sb = p->H * p->T * p->D;
+        pl.lay.sh = p->T * p->D;
+        pl.lay.rs = p->D;
+    }
     split(pl.BH, pl.T, la::split_config(la::kStepState, pl.dtype, pl.D), pl.P, pl.L);
     split(pl.BH, pl.T, la::split_config(la::kStepBwdQ, pl.dtype, pl.D), pl.PB, pl.LB);
     split(pl.BH, pl.T, la::split_config(la::kStepOutput, pl.dtype, pl.D), pl.NQ, pl.LQ);

@@ -7,6 +7,14 @@
 
 namespace la {
 
+// Where the rows of head bh = b H + h live, in elements: the head's row 0 at
+// (bh / H) sb + (bh % H) sh, consecutive rows rs apart.
+//   [B, H, T, D]: sb = H T D, sh = T D, rs = D
+//   [B, T, H, D]: sb = T H D, sh = D,   rs = H D
+struct Layout {
+    int64_t H = 1, sb = 0, sh = 0, rs = 0;
+};
+
 // Work split for one problem. Every field is a pure function of
 // (B*H, T, D, dtype), so the summation order, and with it every output bit,
 // depends only on the shape.
@@ -15,6 +23,7 @@ struct Plan {
     int D = 0, dtype = 0;
     bool simple = false;
     float eps = 0.f;
+    Layout lay;
     // state reduction (fwd steps 1-3): P slices of L tokens per head
     int P = 1;
     int64_t L = 0;

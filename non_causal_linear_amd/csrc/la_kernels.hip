@@ -158,20 +158,27 @@ struct alignas(16) Row {
 };
 
 // Buffer-descriptor access to a slice of one head's rows. The descriptor
-// covers exactly rows [r0, r1) (below 2^31 bytes, as a whole head is), rows
-// are counted from r0, and the hardware reads zeros for loads past r1 and
-// drops stores there, even where the head continues: the kernels need no
-// clamping or branches at the ragged end of a slice.
+// covers exactly rows [r0, r1) of the head (rows rs elements apart; the span
+// is below 2^31 bytes, as a whole head is), rows are counted from r0, and the
+// hardware reads zeros for loads past r1 and drops stores there, even where
+// the head continues: the kernels need no clamping or branches at the ragged
+// end of a slice.
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 struct HeadBuf {
     __amdgpu_buffer_rsrc_t rsrc;
 };
+// Element offset of row 0 of head bh (B * H <= 2^24, so 32-bit division).
+__device__ __forceinline__ int64_t head_offset(const Layout& L, int64_t bh) {
+    const int64_t b = (int)bh / (int)L.H;
+    return b * L.sb + (bh - b * L.H) * L.sh;
+}
+
 template <typename T>
-__device__ __forceinline__ HeadBuf slice_buf(const T* base, int64_t bh, int64_t T_, int D, int64_t r0,
+__device__ __forceinline__ HeadBuf slice_buf(const T* base, const Layout& L, int64_t bh, int D, int64_t r0,
                                              int64_t r1) {
-    const T* p = base + (bh * T_ + r0) * D;
-    return HeadBuf{__builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(p), 0,
-                                                     (int)((r1 - r0) * D * (int64_t)sizeof(T)), 0x00020000)};
+    const T* p = base + head_offset(L, bh) + r0 * L.rs;
+    const int64_t bytes = r1 > r0 ? ((r1 - r0 - 1) * L.rs + D) * (int64_t)sizeof(T) : 0;
+    return HeadBuf{__builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(p), 0, (int)bytes, 0x00020000)};
 }
 // The order in which a workgroup visits the n blocks of its slice, n padded
 // up to a multiple of `group`: rotated by a per-workgroup multiple of `group`.
@@ -197,15 +204,15 @@ struct Rotation {
     }
 };
 
-// Byte offset of element (row, col) of a slice with rows of D elements, for a
-// buffer access, in unsigned 32-bit arithmetic (exact modulo 2^32). Offsets
-// inside a slice are below 2^31 (the head size limit); rows past the end,
-// which the kernels visit at most a few padded blocks far, stay below 2^32,
-// so their offsets still lie past the descriptor's range: such loads read
-// zeros and such stores are dropped.
+// Byte offset of element (row, col) of a slice whose rows are rs elements
+// apart, for a buffer access, in unsigned 32-bit arithmetic (exact modulo
+// 2^32). Offsets inside a slice are below 2^31 (the head size limit); rows
+// past the end, which the kernels visit at most a few padded blocks (under
+// a thousand rows) far, stay below 2^32, so their offsets still lie past the
+// descriptor's range: such loads read zeros and such stores are dropped.
 template <typename T>
-__device__ __forceinline__ int buf_off(int64_t row, int D, int col) {
-    return (int)((uint32_t)row * (uint32_t)(D * (int)sizeof(T)) + (uint32_t)(col * (int)sizeof(T)));
+__device__ __forceinline__ int buf_off(int64_t row, int64_t rs, int col) {
+    return (int)((uint32_t)row * (uint32_t)(rs * (int)sizeof(T)) + (uint32_t)(col * (int)sizeof(T)));
 }
 
 __device__ __forceinline__ uint4 buf_load16(const HeadBuf& b, int byte_off) {
@@ -217,12 +224,13 @@ __device__ __forceinline__ void buf_store16(const HeadBuf& b, int byte_off, uint
     __builtin_amdgcn_raw_buffer_store_b128(v, b.rsrc, byte_off, 0, 0);
 }
 
-// N contiguous elements of row `row` starting at element `col`, by buffer loads.
+// N contiguous elements of row `row` (rows rs elements apart) starting at
+// element `col`, by buffer loads.
 template <typename T, int N>
-__device__ __forceinline__ void load_row_buf(Row<T, N>& r, const HeadBuf& b, int64_t row, int D, int col) {
+__device__ __forceinline__ void load_row_buf(Row<T, N>& r, const HeadBuf& b, int64_t row, int64_t rs, int col) {
     constexpr int NV = N * (int)sizeof(T) / 16;
     uint4* d = reinterpret_cast<uint4*>(r.e);
-    const int off = buf_off<T>(row, D, col);
+    const int off = buf_off<T>(row, rs, col);
 #pragma unroll
     for (int i = 0; i < NV; ++i) d[i] = buf_load16(b, off + 16 * i);
 }
@@ -233,7 +241,7 @@ __device__ __forceinline__ void load_row_buf(Row<T, N>& r, const HeadBuf& b, int
 // reads 16 bytes back so that one store instruction covers whole 128-byte lines.
 template <typename T, int D>
 __device__ __forceinline__ void store_tile_rows(T* stage, const Row<T, D / 4>& vals, const HeadBuf& b,
-                                                int64_t row0) {
+                                                int64_t row0, int64_t rs) {
     constexpr int F = D / 4, EPC = 16 / (int)sizeof(T), LDR = D + EPC;
     constexpr int CPR = D / EPC;       // 16-byte chunks per row
     constexpr int RPI = 64 / CPR;      // rows per store instruction
@@ -246,7 +254,7 @@ __device__ __forceinline__ void store_tile_rows(T* stage, const Row<T, D / 4>& v
 #pragma unroll
     for (int k = 0; k < 16 / RPI; ++k) {
         const uint4 x = *reinterpret_cast<const uint4*>(&stage[(k * RPI + r) * LDR + EPC * c]);
-        buf_store16(b, buf_off<T>(row0 + k * RPI + r, D, EPC * c), x);
+        buf_store16(b, buf_off<T>(row0 + k * RPI + r, rs, EPC * c), x);
     }
     wave_lds_sync();
 }
@@ -254,10 +262,11 @@ __device__ __forceinline__ void store_tile_rows(T* stage, const Row<T, D / 4>& v
 // Same tile, each lane storing its own quarter row (for shapes whose LDS
 // budget leaves no room for the staging area).
 template <typename T, int D>
-__device__ __forceinline__ void store_tile_quarters(const Row<T, D / 4>& vals, const HeadBuf& b, int64_t row0) {
+__device__ __forceinline__ void store_tile_quarters(const Row<T, D / 4>& vals, const HeadBuf& b, int64_t row0,
+                                                    int64_t rs) {
     constexpr int F = D / 4, NV = F * (int)sizeof(T) / 16;
     const int lane = threadIdx.x & 63, m = lane & 15, g = lane >> 4;
-    const int off = buf_off<T>(row0 + m, D, F * g);
+    const int off = buf_off<T>(row0 + m, rs, F * g);
 #pragma unroll
     for (int i = 0; i < NV; ++i) buf_store16(b, off + 16 * i, reinterpret_cast<const uint4*>(vals.e)[i]);
 }
@@ -510,7 +519,7 @@ struct StateShape {
 template <typename T, int D>
 __global__ __launch_bounds__(kThreads) void fwd_state_kernel(
     const T* __restrict__ k, const T* __restrict__ v, float* __restrict__ stS,
-    float* __restrict__ stz, float* __restrict__ part, int64_t T_, int P,
+    float* __restrict__ stz, float* __restrict__ part, int64_t T_, const Layout lay, int P,
     int64_t L) {
     using Sh = StateShape<T, D>;
     constexpr int EPC = Sh::kEPC, CPR = Sh::kCPR, NG = Sh::kNG, R = Sh::kR, TT = Sh::kTT,
@@ -527,8 +536,8 @@ __global__ __launch_bounds__(kThreads) void fwd_state_kernel(
     const int c = tid % CPR, g = tid / CPR;
     const int64_t t0 = (int64_t)p * L;
     const int64_t t1 = min(t0 + L, T_);
-    const T* kb = k + bh * T_ * D + c * EPC;
-    const T* vb = v + bh * T_ * D + c * EPC;
+    const T* kb = k + head_offset(lay, bh) + c * EPC;
+    const T* vb = v + head_offset(lay, bh) + c * EPC;
 
     f32x4 acc[NI][NB + 1];
 #pragma unroll
@@ -544,8 +553,8 @@ __global__ __launch_bounds__(kThreads) void fwd_state_kernel(
 #pragma unroll
         for (int rr = 0; rr < R; ++rr) {
             const int64_t t = min(ts + g + NG * rr, t1 - 1);  // masked when written to LDS
-            rk[rr] = *reinterpret_cast<const uint4*>(kb + t * D);
-            rv[rr] = *reinterpret_cast<const uint4*>(vb + t * D);
+            rk[rr] = *reinterpret_cast<const uint4*>(kb + t * lay.rs);
+            rv[rr] = *reinterpret_cast<const uint4*>(vb + t * lay.rs);
         }
     };
 
@@ -635,7 +644,7 @@ struct StateW64 {
 template <typename T>
 __global__ __launch_bounds__(kThreads, 2) void fwd_state_w64_kernel(
     const T* __restrict__ k, const T* __restrict__ v, float* __restrict__ stS,
-    float* __restrict__ stz, float* __restrict__ part, int64_t T_, int P,
+    float* __restrict__ stz, float* __restrict__ part, int64_t T_, const Layout lay, int P,
     int64_t L) {
     constexpr int D = 64, NB = 4, E = D * D + D;
     constexpr int STEP = StateW64::kStep, LDR = StateW64::kLDR, TILE = StateW64::kTile;
@@ -670,14 +679,14 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_state_w64_kernel(
     // phi(k) is masked for them. Steps go in rotated order, two per wave and
     // turn, with no early exit (an exit makes the compiler wait for every
     // load in flight where the paths join).
-    const HeadBuf bk = slice_buf(k, bh, T_, D, t0, t1), bv = slice_buf(v, bh, T_, D, t0, t1);
+    const HeadBuf bk = slice_buf(k, lay, bh, D, t0, t1), bv = slice_buf(v, lay, bh, D, t0, t1);
     constexpr int NS = StateW64::kStages;
     const Rotation rot(nsteps, NS * kWaves, wid);
     auto issue = [&](Stage& st, int step) {
         const int ps = rot(step);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int off = buf_off<T>((int64_t)ps * STEP + rg + 8 * r, D, 8 * c);
+            const int off = buf_off<T>((int64_t)ps * STEP + rg + 8 * r, lay.rs, 8 * c);
             st.k[r] = buf_load16(bk, off);
             st.v[r] = buf_load16(bv, off);
         }
@@ -814,7 +823,7 @@ struct StateC128 {
 template <typename T>
 __global__ __launch_bounds__(kThreads, 2) void fwd_state_c128_kernel(
     const T* __restrict__ k, const T* __restrict__ v, float* __restrict__ stS,
-    float* __restrict__ stz, float* __restrict__ part, int64_t T_, int P,
+    float* __restrict__ stz, float* __restrict__ part, int64_t T_, const Layout lay, int P,
     int64_t L) {
     constexpr int D = 128, NB = D / 16, NI = NB / kWaves, TT = StateC128::kTile, LDR = StateC128::kLDR;
     constexpr int CPR = D * (int)sizeof(T) / 16;  // 16-byte chunks per row
@@ -848,13 +857,13 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_state_c128_kernel(
     struct Stage {
         u32x4 k[CPT], v[CPT];
     };
-    const HeadBuf bk = slice_buf(k, bh, T_, D, t0, t1), bv = slice_buf(v, bh, T_, D, t0, t1);
+    const HeadBuf bk = slice_buf(k, lay, bh, D, t0, t1), bv = slice_buf(v, lay, bh, D, t0, t1);
     const Rotation rot(ntiles, StateC128::kStages, wid);
     auto issue = [&](Stage& st, int tile) {
         const int row0 = rot(tile) * TT;
 #pragma unroll
         for (int i = 0; i < CPT; ++i) {
-            const int off = buf_off<T>((int64_t)row0 + r0 + RPP * i, D, 8 * c);
+            const int off = buf_off<T>((int64_t)row0 + r0 + RPP * i, lay.rs, 8 * c);
             st.k[i] = __builtin_amdgcn_raw_buffer_load_b128(bk.rsrc, off, 0, 0);
             st.v[i] = __builtin_amdgcn_raw_buffer_load_b128(bv.rsrc, off, 0, 0);
         }
@@ -1020,7 +1029,7 @@ __device__ __forceinline__ void build_frags(Frag<T>* sA, Make make) {
 template <typename T, int D, bool SIMPLE>
 __global__ __launch_bounds__((StreamShape<T, D>::kThreads), (StreamShape<T, D>::kOutMinBlocks)) void fwd_output_kernel(
     const T* __restrict__ q, const float* __restrict__ stS, const float* __restrict__ stz,
-    T* __restrict__ o, int64_t T_, int NQ, int64_t LQ, float eps) {
+    T* __restrict__ o, int64_t T_, const Layout lay, int NQ, int64_t LQ, float eps) {
     using Sh = StreamShape<T, D>;
     constexpr int F = Sh::kF, NB = Sh::kNB, KS = Sh::kKS, U = Sh::kU, NW = Sh::kWaves, NT = Sh::kThreads;
     constexpr int NFS = NB * KS;             // S fragments
@@ -1081,14 +1090,14 @@ __global__ __launch_bounds__((StreamShape<T, D>::kThreads), (StreamShape<T, D>::
     // in rotated order, two per turn with no early exit; rows are counted from
     // c0, rows past the chunk end load as zeros and their stores are dropped.
     constexpr int BT = 16 * U;
-    const HeadBuf bq = slice_buf(q, bh, T_, D, c0, c1), bo = slice_buf(o, bh, T_, D, c0, c1);
+    const HeadBuf bq = slice_buf(q, lay, bh, D, c0, c1), bo = slice_buf(o, lay, bh, D, c0, c1);
     constexpr int NS = Sh::kStages;
     const Rotation rot((int)((c1 - c0 + BT - 1) / BT), NS * NW, wid);
     T* stg = stage + wave * 16 * LDR;
     auto issue = [&](Row<T, F> (&b)[U], int blk) {
         const int64_t bs = (int64_t)rot(blk) * BT;
 #pragma unroll
-        for (int u = 0; u < U; ++u) load_row_buf<T, F>(b[u], bq, bs + 16 * u + m, D, F * grp);
+        for (int u = 0; u < U; ++u) load_row_buf<T, F>(b[u], bq, bs + 16 * u + m, lay.rs, F * grp);
     };
     auto body = [&](Row<T, F> (&qr)[U], int blk) {
         Frag<T> bq[U][KS];
@@ -1141,7 +1150,7 @@ __global__ __launch_bounds__((StreamShape<T, D>::kThreads), (StreamShape<T, D>::
 #pragma unroll
                     for (int r = 0; r < 4; ++r) out.e[4 * b + r] = static_cast<T>(acc[u][b][r] * inv);
             }
-            store_tile_rows<T, D>(stg, out, bo, (int64_t)rot(blk) * BT + 16 * u);
+            store_tile_rows<T, D>(stg, out, bo, (int64_t)rot(blk) * BT + 16 * u, lay.rs);
         }
     };
     Row<T, F> stg_q[NS][U];
@@ -1179,7 +1188,7 @@ template <typename T, int D, bool SIMPLE>
 __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(
     const T* __restrict__ q, const T* __restrict__ dout, const float* __restrict__ stS,
     const float* __restrict__ stz, T* __restrict__ dq, float* __restrict__ part,
-    float* __restrict__ dS_out, float* __restrict__ dz_out, int64_t T_, int PB,
+    float* __restrict__ dS_out, float* __restrict__ dz_out, int64_t T_, const Layout lay, int PB,
     int64_t LB, float eps) {
     using Sh = StreamShape<T, D>;
     using Bq = BwdQShape<T, D>;
@@ -1247,8 +1256,8 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(
             const bool valid = t < t1;
             Row<T, F> qr, dr;
             const int64_t tc = min(t, t1 - 1);  // rows past t1 are masked below
-            load_row<T, F>(qr, q + (bh * T_ + tc) * D + F * grp);
-            load_row<T, F>(dr, dout + (bh * T_ + tc) * D + F * grp);
+            load_row<T, F>(qr, q + head_offset(lay, bh) + tc * lay.rs + F * grp);
+            load_row<T, F>(dr, dout + head_offset(lay, bh) + tc * lay.rs + F * grp);
             float qt[F];
 #pragma unroll
             for (int o = 0; o < F; ++o) qt[o] = phi<T>(to_f32(qr.e[o]));
@@ -1305,7 +1314,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(
                 float out[F];
 #pragma unroll
                 for (int o = 0; o < F; ++o) out[o] = dqt[o] * fminf(qt[o], 1.f);  // phi' = min(phi, 1)
-                store_row<T, F>(dq + (bh * T_ + t) * D + F * grp, out);
+                store_row<T, F>(dq + head_offset(lay, bh) + t * lay.rs + F * grp, out);
             }
             const int col = (wave * U + u) * 16 + m;
 #pragma unroll
@@ -1390,7 +1399,7 @@ template <typename T, bool SIMPLE>
 __global__ __launch_bounds__(kThreads, 2) void bwd_dq_w64_kernel(
     const T* __restrict__ q, const T* __restrict__ dout, const float* __restrict__ stS,
     const float* __restrict__ stz, T* __restrict__ dq, float* __restrict__ part,
-    float* __restrict__ dS_out, float* __restrict__ dz_out, int64_t T_, int PB,
+    float* __restrict__ dS_out, float* __restrict__ dz_out, int64_t T_, const Layout lay, int PB,
     int64_t LB, float eps) {
     constexpr int D = 64, F = 16, NB = 4, KS = 2, STEP = BwdQW64::kStep, E = D * D + D;
     constexpr int LDR = 88;                   // 176-byte rows: 64 features + the beta column block
@@ -1465,11 +1474,11 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_w64_kernel(
     // Rows past the slice end load as zeros (dO = 0 gives u = 0, r = 0,
     // beta = 0, so such rows add nothing to dS or dz) and their dQ stores are
     // dropped. Rows are counted from t0.
-    const HeadBuf bq = slice_buf(q, bh, T_, D, t0, t1), bd = slice_buf(dout, bh, T_, D, t0, t1),
-                  bdq = slice_buf(dq, bh, T_, D, t0, t1);
+    const HeadBuf bq = slice_buf(q, lay, bh, D, t0, t1), bd = slice_buf(dout, lay, bh, D, t0, t1),
+                  bdq = slice_buf(dq, lay, bh, D, t0, t1);
     const Rotation rot(nsteps, BwdQW64::kStages * kWaves, wid);
     auto issue = [&](Stage& st, int step) {
-        const int off = buf_off<T>((int64_t)rot(step) * STEP + m, D, F * grp);
+        const int off = buf_off<T>((int64_t)rot(step) * STEP + m, lay.rs, F * grp);
         st.q[0] = __builtin_amdgcn_raw_buffer_load_b128(bq.rsrc, off, 0, 0);
         st.q[1] = __builtin_amdgcn_raw_buffer_load_b128(bq.rsrc, off + 16, 0, 0);
         st.d[0] = __builtin_amdgcn_raw_buffer_load_b128(bd.rsrc, off, 0, 0);
@@ -1553,7 +1562,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_w64_kernel(
             Row<T, F> out;
 #pragma unroll
             for (int o = 0; o < F; ++o) out.e[o] = static_cast<T>(dqt[o] * dph[o]);
-            store_tile_rows<T, D>(sO, out, bdq, (int64_t)rot(step) * STEP);
+            store_tile_rows<T, D>(sO, out, bdq, (int64_t)rot(step) * STEP, lay.rs);
         }
         wave_lds_sync();
         i16x4 a[NB];
@@ -1668,7 +1677,7 @@ template <typename T, int D, bool SIMPLE>
 __global__ __launch_bounds__(BwdQTile<D>::kThreads, BwdQTile<D>::kMinBlocks) void bwd_dq_tile_kernel(
     const T* __restrict__ q, const T* __restrict__ dout, const float* __restrict__ stS,
     const float* __restrict__ stz, T* __restrict__ dq, float* __restrict__ part,
-    float* __restrict__ dS_out, float* __restrict__ dz_out, int64_t T_, int PB,
+    float* __restrict__ dS_out, float* __restrict__ dz_out, int64_t T_, const Layout lay, int PB,
     int64_t LB, float eps) {
     using Sh = BwdQTile<D>;
     constexpr int F = D / 4, NB = D / 16, KS = D / 32, E = D * D + D;
@@ -1736,11 +1745,11 @@ __global__ __launch_bounds__(BwdQTile<D>::kThreads, BwdQTile<D>::kMinBlocks) voi
     struct Stage {
         u32x4 q[NW16], d[NW16];
     };
-    const HeadBuf bq = slice_buf(q, bh, T_, D, t0, t1), bd = slice_buf(dout, bh, T_, D, t0, t1),
-                  bdq = slice_buf(dq, bh, T_, D, t0, t1);
+    const HeadBuf bq = slice_buf(q, lay, bh, D, t0, t1), bd = slice_buf(dout, lay, bh, D, t0, t1),
+                  bdq = slice_buf(dq, lay, bh, D, t0, t1);
     const Rotation rot(nrounds, Sh::kStages, wid);
     auto issue = [&](Stage& st, int round) {
-        const int off = buf_off<T>((int64_t)rot(round) * RT + wave * STEP + m, D, F * grp);
+        const int off = buf_off<T>((int64_t)rot(round) * RT + wave * STEP + m, lay.rs, F * grp);
 #pragma unroll
         for (int i = 0; i < NW16; ++i) {
             st.q[i] = __builtin_amdgcn_raw_buffer_load_b128(bq.rsrc, off + 16 * i, 0, 0);
@@ -1818,7 +1827,7 @@ __global__ __launch_bounds__(BwdQTile<D>::kThreads, BwdQTile<D>::kMinBlocks) voi
                 }
             // staged through this wave's own rows of the A tile, which are
             // written with A right after
-            store_tile_rows<T, D>(tA + wave * STEP * LDR, out, bdq, (int64_t)rot(round) * RT + wave * STEP);
+            store_tile_rows<T, D>(tA + wave * STEP * LDR, out, bdq, (int64_t)rot(round) * RT + wave * STEP, lay.rs);
         }
         {
             Row<T, F> rq;
@@ -1884,7 +1893,7 @@ __global__ __launch_bounds__(BwdQTile<D>::kThreads, BwdQTile<D>::kMinBlocks) voi
 template <typename T, int D, bool SIMPLE>
 __global__ __launch_bounds__((StreamShape<T, D>::kThreads), (StreamShape<T, D>::kKvMinBlocks)) void bwd_dkv_kernel(
     const T* __restrict__ k, const T* __restrict__ v, const float* __restrict__ dSg,
-    const float* __restrict__ dzg, T* __restrict__ dk, T* __restrict__ dv, int64_t T_, int NK,
+    const float* __restrict__ dzg, T* __restrict__ dk, T* __restrict__ dv, int64_t T_, const Layout lay, int NK,
     int64_t LK) {
     using Sh = StreamShape<T, D>;
     constexpr int F = Sh::kF, NB = Sh::kNB, KS = Sh::kKS, NW = Sh::kWaves, NT = Sh::kThreads;
@@ -1947,8 +1956,8 @@ __global__ __launch_bounds__((StreamShape<T, D>::kThreads), (StreamShape<T, D>::
     // early exit (an exit makes the compiler wait for every load in flight
     // where the paths join): the chunk's buffer descriptors read rows past its
     // end as zeros and drop their stores.
-    const HeadBuf bk = slice_buf(k, bh, T_, D, c0, c1), bv_ = slice_buf(v, bh, T_, D, c0, c1);
-    const HeadBuf bdk = slice_buf(dk, bh, T_, D, c0, c1), bdv = slice_buf(dv, bh, T_, D, c0, c1);
+    const HeadBuf bk = slice_buf(k, lay, bh, D, c0, c1), bv_ = slice_buf(v, lay, bh, D, c0, c1);
+    const HeadBuf bdk = slice_buf(dk, lay, bh, D, c0, c1), bdv = slice_buf(dv, lay, bh, D, c0, c1);
     T* stg = stage + (kStage ? wave * 16 * LDR : 0);
     // The loaded words as they are (see the dQ kernel).
     constexpr int NQW = F * (int)sizeof(T) / 16;  // 16-byte words per quarter row
@@ -1961,7 +1970,7 @@ __global__ __launch_bounds__((StreamShape<T, D>::kThreads), (StreamShape<T, D>::
         const int64_t bs = (int64_t)rot(blk) * 16 * U;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int off = buf_off<T>(bs + 16 * u + m, D, F * grp);
+            const int off = buf_off<T>(bs + 16 * u + m, lay.rs, F * grp);
 #pragma unroll
             for (int i = 0; i < NQW; ++i) {
                 st.k[u][i] = __builtin_amdgcn_raw_buffer_load_b128(bk.rsrc, off + 16 * i, 0, 0);
@@ -2031,11 +2040,11 @@ __global__ __launch_bounds__((StreamShape<T, D>::kThreads), (StreamShape<T, D>::
                     gv.e[o] = static_cast<T>(av[u][b][r] * uD);
                 }
             if constexpr (kStage) {
-                store_tile_rows<T, D>(stg, gk, bdk, base + 16 * u);
-                store_tile_rows<T, D>(stg, gv, bdv, base + 16 * u);
+                store_tile_rows<T, D>(stg, gk, bdk, base + 16 * u, lay.rs);
+                store_tile_rows<T, D>(stg, gv, bdv, base + 16 * u, lay.rs);
             } else {
-                store_tile_quarters<T, D>(gk, bdk, base + 16 * u);
-                store_tile_quarters<T, D>(gv, bdv, base + 16 * u);
+                store_tile_quarters<T, D>(gk, bdk, base + 16 * u, lay.rs);
+                store_tile_quarters<T, D>(gv, bdv, base + 16 * u, lay.rs);
             }
         }
     };
@@ -2093,11 +2102,11 @@ hipError_t fwd_state_t(const Plan& p, const void* k, const void* v, float* state
     float* sz = state + p.BH * D * D;
     hipError_t e;
     if constexpr (kWaveKernels<T, D>)
-        e = launch(fwd_state_w64_kernel<T>, nblk, kThreads, s, kk, vv, state, sz, part, p.T, p.P, p.L);
+        e = launch(fwd_state_w64_kernel<T>, nblk, kThreads, s, kk, vv, state, sz, part, p.T, p.lay, p.P, p.L);
     else if constexpr (kTileKernels<T, D>)
-        e = launch(fwd_state_c128_kernel<T>, nblk, kThreads, s, kk, vv, state, sz, part, p.T, p.P, p.L);
+        e = launch(fwd_state_c128_kernel<T>, nblk, kThreads, s, kk, vv, state, sz, part, p.T, p.lay, p.P, p.L);
     else
-        e = launch(fwd_state_kernel<T, D>, nblk, kThreads, s, kk, vv, state, sz, part, p.T, p.P, p.L);
+        e = launch(fwd_state_kernel<T, D>, nblk, kThreads, s, kk, vv, state, sz, part, p.T, p.lay, p.P, p.L);
     if (e != hipSuccess) return e;
     return launch_combine<D>(p.P, part, state, sz, p.BH, s);
 }
@@ -2110,8 +2119,8 @@ hipError_t fwd_output_t(const Plan& p, const void* q, const float* state, void* 
     const float* sz = state + p.BH * D * D;
     T* oo = static_cast<T*>(o);
     if (p.simple)
-        return launch(fwd_output_kernel<T, D, true>, nblk, nt, s, qq, state, sz, oo, p.T, p.NQ, p.LQ, p.eps);
-    return launch(fwd_output_kernel<T, D, false>, nblk, nt, s, qq, state, sz, oo, p.T, p.NQ, p.LQ, p.eps);
+        return launch(fwd_output_kernel<T, D, true>, nblk, nt, s, qq, state, sz, oo, p.T, p.lay, p.NQ, p.LQ, p.eps);
+    return launch(fwd_output_kernel<T, D, false>, nblk, nt, s, qq, state, sz, oo, p.T, p.lay, p.NQ, p.LQ, p.eps);
 }
 
 template <typename T, int D>
@@ -2131,20 +2140,20 @@ hipError_t bwd_dq_t(const Plan& p, const void* q, const void* dout, const float*
     hipError_t e;
     if constexpr (kWaveKernels<T, D>) {
         e = p.simple ? launch(bwd_dq_w64_kernel<T, true>, nblk, kThreads, s, qq, dd, sS, sz, g, part, dS, dz, p.T,
-                              p.PB, p.LB, p.eps)
+                              p.lay, p.PB, p.LB, p.eps)
                      : launch(bwd_dq_w64_kernel<T, false>, nblk, kThreads, s, qq, dd, sS, sz, g, part, dS, dz, p.T,
-                              p.PB, p.LB, p.eps);
+                              p.lay, p.PB, p.LB, p.eps);
     } else if constexpr (kTileKernels<T, D>) {
         constexpr int nt = BwdQTile<D>::kThreads;
         e = p.simple ? launch(bwd_dq_tile_kernel<T, D, true>, nblk, nt, s, qq, dd, sS, sz, g, part, dS, dz, p.T,
-                              p.PB, p.LB, p.eps)
+                              p.lay, p.PB, p.LB, p.eps)
                      : launch(bwd_dq_tile_kernel<T, D, false>, nblk, nt, s, qq, dd, sS, sz, g, part, dS, dz, p.T,
-                              p.PB, p.LB, p.eps);
+                              p.lay, p.PB, p.LB, p.eps);
     } else {
         e = p.simple ? launch(bwd_dq_kernel<T, D, true>, nblk, kThreads, s, qq, dd, sS, sz, g, part, dS, dz, p.T,
-                              p.PB, p.LB, p.eps)
+                              p.lay, p.PB, p.LB, p.eps)
                      : launch(bwd_dq_kernel<T, D, false>, nblk, kThreads, s, qq, dd, sS, sz, g, part, dS, dz, p.T,
-                              p.PB, p.LB, p.eps);
+                              p.lay, p.PB, p.LB, p.eps);
     }
     if (e != hipSuccess) return e;
     return launch_combine<D>(p.PB, part, dS, dz, p.BH, s);
@@ -2162,8 +2171,8 @@ hipError_t bwd_dkv_t(const Plan& p, const void* k, const void* v, void* dk, void
     T* gk = static_cast<T*>(dk);
     T* gv = static_cast<T*>(dv);
     if (p.simple)
-        return launch(bwd_dkv_kernel<T, D, true>, nblk, nt, s, kk, vv, dst, dz, gk, gv, p.T, p.NK, p.LK);
-    return launch(bwd_dkv_kernel<T, D, false>, nblk, nt, s, kk, vv, dst, dz, gk, gv, p.T, p.NK, p.LK);
+        return launch(bwd_dkv_kernel<T, D, true>, nblk, nt, s, kk, vv, dst, dz, gk, gv, p.T, p.lay, p.NK, p.LK);
+    return launch(bwd_dkv_kernel<T, D, false>, nblk, nt, s, kk, vv, dst, dz, gk, gv, p.T, p.lay, p.NK, p.LK);
 }
 
 // dtype codes follow la_dtype: 0 = f32, 1 = f16, 2 = bf16.

@@ -48,7 +48,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.la_version() == 1
+    assert L.la_version() == 2
     for s in range(11):
         txt = L.la_status_str(s).decode()
         assert txt.startswith("LA_"), txt
@@ -125,7 +125,8 @@ def test_fwd_rejects_bad_problems(L):
     assert fwd_call(L, prob(T=(1 << 31) // (128 * 2), D=128)) == SHAPE
     assert L.la_workspace_bytes(ctypes.byref(prob(T=(1 << 31) // (128 * 2) - 1, D=128))) > 0
     assert L.la_workspace_bytes(ctypes.byref(prob(T=(1 << 31) // (64 * 4), D=64, dtype=0))) == 0
-    assert fwd_call(L, prob(flags=2)) == FLAGS
+    assert fwd_call(L, prob(flags=4)) == FLAGS
+    assert fwd_call(L, prob(flags=0x80000000)) == FLAGS
     assert fwd_call(L, prob(eps=-1e-3)) == EPS
     assert fwd_call(L, prob(eps=float("nan"))) == EPS
     assert fwd_call(L, prob(eps=float("inf"))) == EPS
@@ -225,3 +226,21 @@ def test_binding_validates_state_buffers():
             la._state(bad, prob, dev)
     with pytest.raises(TypeError):
         la._state(None, prob, dev)
+
+
+def test_token_major_layout_limits(L):
+    """[B, T, H, D] (LA_LAYOUT_BTHD): the flag is accepted, the workspace does not
+    depend on the layout, and a head's span (T + 1024 rows of H * D elements)
+    must stay below 2^31 bytes."""
+    BTHD = 2
+    base = L.la_workspace_bytes(ctypes.byref(prob(B=2, H=3, T=1000)))
+    assert L.la_workspace_bytes(ctypes.byref(prob(B=2, H=3, T=1000, flags=BTHD))) == base
+    assert L.la_workspace_bytes(ctypes.byref(prob(B=2, H=3, T=1000, flags=BTHD | 1))) > 0
+    H, D, elt = 16, 64, 2
+    t_max = ((1 << 31) - 1) // (H * D * elt) - 1024
+    assert L.la_workspace_bytes(ctypes.byref(prob(B=1, H=H, T=t_max, D=D, flags=BTHD))) > 0
+    assert fwd_call(L, prob(B=1, H=H, T=t_max + 1, D=D, flags=BTHD)) == SHAPE
+    # the same T is fine in [B, H, T, D], where only T * D * elt counts
+    assert L.la_workspace_bytes(ctypes.byref(prob(B=1, H=H, T=t_max + 1, D=D))) > 0
+    # B = 0 stays an empty problem (nothing launched) in either layout
+    assert fwd_call(L, prob(B=0, flags=BTHD)) == 0
