@@ -239,6 +239,7 @@ def main() -> int:
         },
         "fwd_ms": round(float(np.mean(fwd_ms)), 4),
         "fwd_ms_min": round(float(np.min(fwd_ms)), 4),
+        "fwd_ms_median": round(float(np.median(fwd_ms)), 4),
         "fwd_frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
         "kernel_ms": {kname: round(a, 4) for kname, a in avg.items()},
         "wall_ms_per_step_incl_flush": round(wall / args.steps * 1e3, 4),
@@ -269,6 +270,8 @@ def main() -> int:
         bwd_ms = per["bwd_dq"] + per["bwd_dkv"]
         line["bwd_ms"] = round(float(np.mean(bwd_ms)), 4)
         line["fwd_bwd_ms"] = round(float(np.mean(step_ms)), 4)
+        line["fwd_bwd_ms_min"] = round(float(np.min(step_ms)), 4)
+        line["fwd_bwd_ms_median"] = round(float(np.median(step_ms)), 4)
     if w.name == HEADLINE:
         line["context_pages_a800_triton"] = {"fwd_ms": PAGE_A800_FWD_MS, "bwd_ms": PAGE_A800_BWD_MS,
                                              "note": "another GPU, dtype unstated: context only"}
