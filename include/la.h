@@ -5,7 +5,8 @@
  * The operation (Flash Bi-directional Linear Attention README: intro, and
  * "Update" 2024-12-28 for simple_la, "Update" 2024-12-30 for the backward).
  * Per batch b and head h, with Q, K, V in R^{T x D} and phi(x) = elu(x) + 1
- * (x + 1 for x > 0, e^x otherwise):
+ * (x + 1 for x > 0, e^x otherwise; LA_PHI_RELU and LA_PHI_IDENTITY select
+ * relu(x) or x instead):
  *     S = sum_t phi(k_t) v_t^T          (D x D, S[i][j])
  *     z = sum_t phi(k_t)                (D)
  *     O_t = phi(q_t) S / (phi(q_t) . z + eps)      normalised (default)
@@ -69,7 +70,7 @@ typedef enum {
     LA_ERR_SHAPE = 2,      /* B, H or T negative; B*H > 2^24; head too large  */
     LA_ERR_DTYPE = 3,      /* dtype not one of la_dtype                       */
     LA_ERR_HEAD_DIM = 4,   /* D not supported (64 and 128 are)                */
-    LA_ERR_FLAGS = 5,      /* unknown bit in flags                            */
+    LA_ERR_FLAGS = 5,      /* unknown bit in flags, or two feature maps       */
     LA_ERR_EPS = 6,        /* eps negative or not finite                      */
     LA_ERR_WORKSPACE = 7,  /* ws_bytes below la_workspace_bytes()             */
     LA_ERR_ALIGN = 8,      /* a tensor is not 16-byte aligned, ws not 256     */
@@ -81,6 +82,11 @@ typedef enum {
 #define LA_SIMPLE 0x1u
 /* Tensors are [B, T, H, D] rather than [B, H, T, D]. */
 #define LA_LAYOUT_BTHD 0x2u
+/* Feature map (at most one; default elu(x) + 1). relu: phi'(0) = 0. With the
+ * identity map the normalised denominator phi(q) . z + eps can vanish or
+ * change sign; that is the caller's to avoid (simple_la has none). */
+#define LA_PHI_RELU 0x4u
+#define LA_PHI_IDENTITY 0x8u
 
 /* Problem description shared by every call. B, H, T >= 0 (a zero size is an
  * empty problem: nothing to compute, LA_OK), B*H <= 2^24, D in {64, 128},
@@ -92,7 +98,7 @@ typedef enum {
 typedef struct {
     int64_t B, H, T, D;
     int32_t dtype;   /* la_dtype */
-    uint32_t flags;  /* LA_SIMPLE and / or LA_LAYOUT_BTHD */
+    uint32_t flags;  /* LA_SIMPLE, LA_LAYOUT_BTHD, one of LA_PHI_RELU, LA_PHI_IDENTITY */
     float eps;
 } la_problem;
 

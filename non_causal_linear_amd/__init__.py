@@ -20,7 +20,8 @@ import torch
 __all__ = [
     "LAError", "lib", "fwd", "bwd", "fwd_state", "fwd_output", "bwd_dq", "bwd_dkv", "linear_attention",
     "state_bytes", "workspace_bytes", "new_state", "workspace", "Problem",
-    "LA_F32", "LA_F16", "LA_BF16", "LA_SIMPLE", "LA_LAYOUT_BTHD", "EXPORTS",
+    "LA_F32", "LA_F16", "LA_BF16", "LA_SIMPLE", "LA_LAYOUT_BTHD", "LA_PHI_RELU", "LA_PHI_IDENTITY",
+    "EXPORTS",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libla.so")
@@ -28,7 +29,9 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libla.so")
 LA_F32, LA_F16, LA_BF16 = 0, 1, 2
 LA_SIMPLE = 0x1
 LA_LAYOUT_BTHD = 0x2
+LA_PHI_RELU, LA_PHI_IDENTITY = 0x4, 0x8
 LAYOUTS = ("bhtd", "bthd")
+FEATURE_MAPS = {"elu1": 0, "relu": LA_PHI_RELU, "identity": LA_PHI_IDENTITY}
 DTYPE_CODE = {torch.float32: LA_F32, torch.float16: LA_F16, torch.bfloat16: LA_BF16}
 
 # Every symbol include/la.h declares.
@@ -91,11 +94,15 @@ def _check(status: int) -> None:
         raise LAError(status, lib().la_status_str(status).decode())
 
 
-def make_problem(shape, dtype: torch.dtype, eps: float, simple: bool, layout: str = "bhtd") -> Problem:
+def make_problem(shape, dtype: torch.dtype, eps: float, simple: bool, layout: str = "bhtd",
+                 phi: str = "elu1") -> Problem:
     """Problem for tensors of ``shape``: [B, H, T, D] (layout "bhtd") or
-    [B, T, H, D] (layout "bthd")."""
+    [B, T, H, D] (layout "bthd"); feature map phi "elu1" (elu(x) + 1), "relu"
+    or "identity"."""
     if layout not in LAYOUTS:
         raise ValueError(f"layout must be one of {LAYOUTS}, got {layout!r}")
+    if phi not in FEATURE_MAPS:
+        raise ValueError(f"phi must be one of {tuple(FEATURE_MAPS)}, got {phi!r}")
     if len(shape) != 4:
         raise ValueError(f"expected a 4-d tensor ({layout}), got shape {tuple(shape)}")
     if dtype not in DTYPE_CODE:
@@ -104,7 +111,7 @@ def make_problem(shape, dtype: torch.dtype, eps: float, simple: bool, layout: st
         B, H, T, D = (int(x) for x in shape)
     else:
         B, T, H, D = (int(x) for x in shape)
-    flags = (LA_SIMPLE if simple else 0) | (LA_LAYOUT_BTHD if layout == "bthd" else 0)
+    flags = (LA_SIMPLE if simple else 0) | (LA_LAYOUT_BTHD if layout == "bthd" else 0) | FEATURE_MAPS[phi]
     return Problem(B, H, T, D, DTYPE_CODE[dtype], flags, float(eps))
 
 
@@ -178,11 +185,11 @@ def _ws(prob, device, ws):
     return ws, ctypes.c_size_t(ws.numel() * ws.element_size())
 
 
-def fwd_state(k, v, *, eps=1e-6, simple=False, layout="bhtd", state=None, ws=None):
+def fwd_state(k, v, *, eps=1e-6, simple=False, layout="bhtd", phi="elu1", state=None, ws=None):
     """Steps 1-3: the fp32 state (S, z) of phi(K), V."""
     _tensor(k, None, "k")
     _tensor(v, k, "v")
-    prob = make_problem(k.shape, k.dtype, eps, simple, layout)
+    prob = make_problem(k.shape, k.dtype, eps, simple, layout, phi)
     state = new_state(prob, k.device) if state is None else _state(state, prob, k.device)
     ws, wsb = _ws(prob, k.device, ws)
     _check(lib().la_fwd_state(ctypes.byref(prob), _ptr(k), _ptr(v), _ptr(state), _ptr(ws), wsb,
@@ -190,22 +197,22 @@ def fwd_state(k, v, *, eps=1e-6, simple=False, layout="bhtd", state=None, ws=Non
     return state
 
 
-def fwd_output(q, state, *, eps=1e-6, simple=False, layout="bhtd", out=None):
+def fwd_output(q, state, *, eps=1e-6, simple=False, layout="bhtd", phi="elu1", out=None):
     """Step 4: O from Q and a complete state."""
     _tensor(q, None, "q")
-    prob = make_problem(q.shape, q.dtype, eps, simple, layout)
+    prob = make_problem(q.shape, q.dtype, eps, simple, layout, phi)
     _state(state, prob, q.device)
     out = torch.empty_like(q) if out is None else _tensor(out, q, "out")
     _check(lib().la_fwd_output(ctypes.byref(prob), _ptr(q), _ptr(state), _ptr(out), _stream(q.device)))
     return out
 
 
-def fwd(q, k, v, *, eps=1e-6, simple=False, layout="bhtd", out=None, state=None, ws=None):
+def fwd(q, k, v, *, eps=1e-6, simple=False, layout="bhtd", phi="elu1", out=None, state=None, ws=None):
     """O = phi(Q) S / (phi(Q) z + eps) (or phi(Q) S); returns (O, state)."""
     _tensor(q, None, "q")
     _tensor(k, q, "k")
     _tensor(v, q, "v")
-    prob = make_problem(q.shape, q.dtype, eps, simple, layout)
+    prob = make_problem(q.shape, q.dtype, eps, simple, layout, phi)
     out = torch.empty_like(q) if out is None else _tensor(out, q, "out")
     state = new_state(prob, q.device) if state is None else _state(state, prob, q.device)
     ws, wsb = _ws(prob, q.device, ws)
@@ -214,11 +221,11 @@ def fwd(q, k, v, *, eps=1e-6, simple=False, layout="bhtd", out=None, state=None,
     return out, state
 
 
-def bwd_dq(q, do, state, *, eps=1e-6, simple=False, layout="bhtd", dq=None, ws=None):
+def bwd_dq(q, do, state, *, eps=1e-6, simple=False, layout="bhtd", phi="elu1", dq=None, ws=None):
     """Steps 5-6: dQ; leaves dS, dz in the workspace for bwd_dkv."""
     _tensor(q, None, "q")
     _tensor(do, q, "do")
-    prob = make_problem(q.shape, q.dtype, eps, simple, layout)
+    prob = make_problem(q.shape, q.dtype, eps, simple, layout, phi)
     _state(state, prob, q.device)
     dq = torch.empty_like(q) if dq is None else _tensor(dq, q, "dq")
     ws, wsb = _ws(prob, q.device, ws)
@@ -227,11 +234,11 @@ def bwd_dq(q, do, state, *, eps=1e-6, simple=False, layout="bhtd", dq=None, ws=N
     return dq
 
 
-def bwd_dkv(k, v, *, eps=1e-6, simple=False, layout="bhtd", dk=None, dv=None, ws=None):
+def bwd_dkv(k, v, *, eps=1e-6, simple=False, layout="bhtd", phi="elu1", dk=None, dv=None, ws=None):
     """Step 7: dK, dV from the backward state bwd_dq left in the same workspace."""
     _tensor(k, None, "k")
     _tensor(v, k, "v")
-    prob = make_problem(k.shape, k.dtype, eps, simple, layout)
+    prob = make_problem(k.shape, k.dtype, eps, simple, layout, phi)
     dk = torch.empty_like(k) if dk is None else _tensor(dk, k, "dk")
     dv = torch.empty_like(k) if dv is None else _tensor(dv, k, "dv")
     ws, wsb = _ws(prob, k.device, ws)
@@ -240,12 +247,12 @@ def bwd_dkv(k, v, *, eps=1e-6, simple=False, layout="bhtd", dk=None, dv=None, ws
     return dk, dv
 
 
-def bwd(q, k, v, do, state, *, eps=1e-6, simple=False, layout="bhtd", dq=None, dk=None, dv=None, ws=None):
+def bwd(q, k, v, do, state, *, eps=1e-6, simple=False, layout="bhtd", phi="elu1", dq=None, dk=None, dv=None, ws=None):
     """dQ, dK, dV of L = sum(O * dO), from the state fwd returned."""
     _tensor(q, None, "q")
     for n, x in (("k", k), ("v", v), ("do", do)):
         _tensor(x, q, n)
-    prob = make_problem(q.shape, q.dtype, eps, simple, layout)
+    prob = make_problem(q.shape, q.dtype, eps, simple, layout, phi)
     _state(state, prob, q.device)
     dq = torch.empty_like(q) if dq is None else _tensor(dq, q, "dq")
     dk = torch.empty_like(q) if dk is None else _tensor(dk, q, "dk")
@@ -262,23 +269,26 @@ class _LinearAttention(torch.autograd.Function):
     and does not recompute S."""
 
     @staticmethod
-    def forward(ctx, q, k, v, eps, simple, layout):
+    def forward(ctx, q, k, v, eps, simple, layout, phi):
         q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
-        o, state = fwd(q, k, v, eps=eps, simple=simple, layout=layout)
+        o, state = fwd(q, k, v, eps=eps, simple=simple, layout=layout, phi=phi)
         ctx.save_for_backward(q, k, v, state)
-        ctx.eps, ctx.simple, ctx.layout = eps, simple, layout
+        ctx.eps, ctx.simple, ctx.layout, ctx.phi = eps, simple, layout, phi
         return o
 
     @staticmethod
     def backward(ctx, do):
         q, k, v, state = ctx.saved_tensors
-        dq, dk, dv = bwd(q, k, v, do.contiguous(), state, eps=ctx.eps, simple=ctx.simple, layout=ctx.layout)
-        return dq, dk, dv, None, None, None
+        dq, dk, dv = bwd(q, k, v, do.contiguous(), state, eps=ctx.eps, simple=ctx.simple, layout=ctx.layout,
+                         phi=ctx.phi)
+        return dq, dk, dv, None, None, None, None
 
 
-def linear_attention(q, k, v, *, eps: float = 1e-6, simple: bool = False, layout: str = "bhtd") -> torch.Tensor:
+def linear_attention(q, k, v, *, eps: float = 1e-6, simple: bool = False, layout: str = "bhtd",
+                     phi: str = "elu1") -> torch.Tensor:
     """O = phi(Q) S / (phi(Q) z + eps) (or phi(Q) S with simple=True), with
     gradients for q, k and v through the library's backward. Tensors are
     [B, H, T, D] (layout "bhtd") or [B, T, H, D] (layout "bthd") on a GPU in
-    float32, float16 or bfloat16, D in {64, 128}."""
-    return _LinearAttention.apply(q, k, v, float(eps), bool(simple), layout)
+    float32, float16 or bfloat16, D in {64, 128}; phi is "elu1" (elu + 1),
+    "relu" or "identity"."""
+    return _LinearAttention.apply(q, k, v, float(eps), bool(simple), layout, phi)

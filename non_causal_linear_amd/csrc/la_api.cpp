@@ -53,7 +53,8 @@ la_status check_problem(const la_problem* p) {
     if (p->D != 64 && p->D != 128) return LA_ERR_HEAD_DIM;
     if (p->B < 0 || p->H < 0 || p->T < 0) return LA_ERR_SHAPE;
     if (p->B > kMaxHeads || p->H > kMaxHeads || p->B * p->H > kMaxHeads) return LA_ERR_SHAPE;
-    if (p->flags & ~(LA_SIMPLE | LA_LAYOUT_BTHD)) return LA_ERR_FLAGS;
+    if (p->flags & ~(LA_SIMPLE | LA_LAYOUT_BTHD | LA_PHI_RELU | LA_PHI_IDENTITY)) return LA_ERR_FLAGS;
+    if ((p->flags & LA_PHI_RELU) && (p->flags & LA_PHI_IDENTITY)) return LA_ERR_FLAGS;
     const int64_t row_bytes = p->D * (p->dtype == LA_F32 ? 4 : 2);
     if (p->flags & LA_LAYOUT_BTHD) {
         if (p->H > 0 && p->T + kRowSlack > kMaxHeadBytes / (p->H * row_bytes)) return LA_ERR_SHAPE;
@@ -74,6 +75,7 @@ la::Plan make_plan(const la_problem* p) {
     pl.dtype = p->dtype;
     pl.simple = (p->flags & LA_SIMPLE) != 0;
     pl.eps = p->eps;
+    pl.fm = (p->flags & LA_PHI_RELU) ? 1 : (p->flags & LA_PHI_IDENTITY) ? 2 : 0;
     pl.lay.H = p->H > 0 ? p->H : 1;
     if (p->flags & LA_LAYOUT_BTHD) {
         pl.lay.sb = p->T * p->H * p->D;
@@ -153,7 +155,7 @@ const char* la_status_str(int s) {
         case LA_ERR_SHAPE: return "LA_ERR_SHAPE: B, H or T negative or too large";
         case LA_ERR_DTYPE: return "LA_ERR_DTYPE: unknown dtype";
         case LA_ERR_HEAD_DIM: return "LA_ERR_HEAD_DIM: D must be 64 or 128";
-        case LA_ERR_FLAGS: return "LA_ERR_FLAGS: unknown flag bit";
+        case LA_ERR_FLAGS: return "LA_ERR_FLAGS: unknown flag bit or two feature maps";
         case LA_ERR_EPS: return "LA_ERR_EPS: eps must be finite and >= 0";
         case LA_ERR_WORKSPACE: return "LA_ERR_WORKSPACE: workspace smaller than la_workspace_bytes()";
         case LA_ERR_ALIGN: return "LA_ERR_ALIGN: tensors need 16-byte, workspace 256-byte alignment";

@@ -23,6 +23,7 @@ struct Plan {
     int D = 0, dtype = 0;
     bool simple = false;
     float eps = 0.f;
+    int fm = 0;  // feature map: 0 elu + 1, 1 relu, 2 identity
     Layout lay;
     // state reduction (fwd steps 1-3): P slices of L tokens per head
     int P = 1;

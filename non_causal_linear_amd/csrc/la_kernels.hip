@@ -53,6 +53,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
 constexpr int kWaves = 4;
+enum FeatureMap { kPhiElu1 = 0, kPhiRelu = 1, kPhiIdentity = 2 };
 
 template <typename T> struct Elt;
 // kScaled: the fp32 states are multiplied by a power of two before they are
@@ -118,27 +119,50 @@ __device__ __forceinline__ f32x4 mma(f32x8 a, f32x8 b, f32x4 c) {
     return c;
 }
 
-// phi(x) = elu(x) + 1, evaluated piecewise in fp32 (never as expm1(x) + 1,
-// which cancels for x << 0). Both sides are computed and one is selected, so
-// no branch splits the wave (NaN falls to the exp side and propagates). 16-bit
-// inputs use the hardware exp2 on x log2(e); fp32 inputs use the accurate expf.
-template <typename T>
-__device__ __forceinline__ float phi(float x) {
-    float e;
-    if constexpr (std::is_same<T, float>::value) {
-        e = expf(x);
+// The feature map phi, chosen by la_problem.flags: elu(x) + 1 (the default),
+// relu(x) or x. feature() returns phi(x) and phi'(x) in fp32.
+//   elu + 1: evaluated piecewise, x + 1 for x > 0 and e^x otherwise (never
+//     as expm1(x) + 1, which cancels for x << 0); both sides are computed and
+//     one is selected, so no branch splits the wave (NaN falls to the exp
+//     side and propagates). 16-bit inputs use the hardware exp2 on
+//     x log2(e), fp32 inputs the accurate expf. phi' = 1 for x > 0, else e^x.
+//   relu: x < 0 ? 0 : x (NaN propagates); phi' = 1 for x > 0, else 0.
+//   identity: phi = x, phi' = 1.
+template <int FM, typename T>
+__device__ __forceinline__ void feature(float x, float& p, float& dp) {
+    if constexpr (FM == kPhiRelu) {
+        p = x < 0.f ? 0.f : x;
+        dp = x > 0.f ? 1.f : 0.f;
+    } else if constexpr (FM == kPhiIdentity) {
+        p = x;
+        dp = 1.f;
     } else {
-        e = __builtin_amdgcn_exp2f(x * 1.4426950408889634f);
+        float e;
+        if constexpr (std::is_same<T, float>::value) {
+            e = expf(x);
+        } else {
+            e = __builtin_amdgcn_exp2f(x * 1.4426950408889634f);
+        }
+        p = x > 0.f ? x + 1.f : e;
+        dp = x > 0.f ? 1.f : e;
     }
-    return x > 0.f ? x + 1.f : e;
 }
 
-// The exponential branch of phi (and of phi' = 1 for x > 0, e^x otherwise),
-// for kernels that need both: x > 0 then selects x + 1 or 1.
-template <typename T>
-__device__ __forceinline__ float phi_exp(float x) {
-    if constexpr (std::is_same<T, float>::value) return expf(x);
-    else return __builtin_amdgcn_exp2f(x * 1.4426950408889634f);
+template <int FM, typename T>
+__device__ __forceinline__ float phi(float x) {
+    float p, dp;
+    feature<FM, T>(x, p, dp);
+    return p;
+}
+
+// phi'(x) from phi(x) alone: min(phi, 1) for elu + 1 (phi > 1 exactly where
+// x > 0 and phi' = 1; elsewhere phi = e^x = phi'), [phi > 0] for relu, 1 for
+// the identity.
+template <int FM>
+__device__ __forceinline__ float dphi_of(float p) {
+    if constexpr (FM == kPhiRelu) return p > 0.f ? 1.f : 0.f;
+    else if constexpr (FM == kPhiIdentity) return 1.f;
+    else return fminf(p, 1.f);
 }
 
 template <typename T>
@@ -516,7 +540,7 @@ struct StateShape {
 // g, g + NG, ... land in columns 4g, 4g + 1, ...) identically for K and V,
 // which a sum over tokens does not see. z comes from the same MFMA with an
 // all-ones B block, so it sums exactly the rounded phi(k) that S uses.
-template <typename T, int D>
+template <typename T, int D, int FM>
 __global__ __launch_bounds__(kThreads) void fwd_state_kernel(
     const T* __restrict__ k, const T* __restrict__ v, float* __restrict__ stS,
     float* __restrict__ stz, float* __restrict__ part, int64_t T_, const Layout lay, int P,
@@ -573,7 +597,7 @@ __global__ __launch_bounds__(kThreads) void fwd_state_kernel(
 #pragma unroll
                 for (int e = 0; e < EPC; ++e) {
                     // padded rows must add nothing: phi(0) = 1, so mask after phi
-                    kt[e][rr] = ok ? static_cast<T>(phi<T>(to_f32(ke[e]))) : static_cast<T>(0.f);
+                    kt[e][rr] = ok ? static_cast<T>(phi<FM, T>(to_f32(ke[e]))) : static_cast<T>(0.f);
                     vt[e][rr] = ok ? ve[e] : static_cast<T>(0.f);
                 }
             }
@@ -641,7 +665,7 @@ struct StateW64 {
     static constexpr int kTile = kStep * kLDR;
 };
 
-template <typename T>
+template <typename T, int FM>
 __global__ __launch_bounds__(kThreads, 2) void fwd_state_w64_kernel(
     const T* __restrict__ k, const T* __restrict__ v, float* __restrict__ stS,
     float* __restrict__ stz, float* __restrict__ part, int64_t T_, const Layout lay, int P,
@@ -701,7 +725,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_state_w64_kernel(
             Row<T, 8> kt;
 #pragma unroll
             for (int e = 0; e < 8; ++e)
-                kt.e[e] = ok ? static_cast<T>(phi<T>(to_f32(ke[e]))) : static_cast<T>(0.f);
+                kt.e[e] = ok ? static_cast<T>(phi<FM, T>(to_f32(ke[e]))) : static_cast<T>(0.f);
             *reinterpret_cast<uint4*>(&sK[row * LDR + 8 * c]) = *reinterpret_cast<const uint4*>(kt.e);
             *reinterpret_cast<uint4*>(&sV[row * LDR + 8 * c]) = st.v[r];
         }
@@ -820,7 +844,7 @@ struct StateC128 {
     static constexpr int kStages = 2;  // tiles of loads in flight
 };
 
-template <typename T>
+template <typename T, int FM>
 __global__ __launch_bounds__(kThreads, 2) void fwd_state_c128_kernel(
     const T* __restrict__ k, const T* __restrict__ v, float* __restrict__ stS,
     float* __restrict__ stz, float* __restrict__ part, int64_t T_, const Layout lay, int P,
@@ -879,7 +903,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_state_c128_kernel(
             Row<T, 8> kin, kt;
             __builtin_memcpy(kin.e, &st.k[i], sizeof(kin));
 #pragma unroll
-            for (int e = 0; e < 8; ++e) kt.e[e] = ok ? static_cast<T>(phi<T>(to_f32(kin.e[e]))) : static_cast<T>(0.f);
+            for (int e = 0; e < 8; ++e) kt.e[e] = ok ? static_cast<T>(phi<FM, T>(to_f32(kin.e[e]))) : static_cast<T>(0.f);
             *reinterpret_cast<Row<T, 8>*>(&dK[row * LDR + 8 * c]) = kt;
             *reinterpret_cast<u32x4*>(&dV[row * LDR + 8 * c]) = st.v[i];
         }
@@ -1026,7 +1050,7 @@ __device__ __forceinline__ void build_frags(Frag<T>* sA, Make make) {
 // and the wave computes O^T = S^T phi(Q)^T (rows permuted so each lane ends
 // with D/4 contiguous outputs of its token) and den = z . phi(q) from one more
 // MFMA block whose rows are all z.
-template <typename T, int D, bool SIMPLE>
+template <typename T, int D, bool SIMPLE, int FM>
 __global__ __launch_bounds__((StreamShape<T, D>::kThreads), (StreamShape<T, D>::kOutMinBlocks)) void fwd_output_kernel(
     const T* __restrict__ q, const float* __restrict__ stS, const float* __restrict__ stz,
     T* __restrict__ o, int64_t T_, const Layout lay, int NQ, int64_t LQ, float eps) {
@@ -1107,7 +1131,7 @@ __global__ __launch_bounds__((StreamShape<T, D>::kThreads), (StreamShape<T, D>::
             for (int s = 0; s < KS; ++s)
 #pragma unroll
                 for (int e = 0; e < 8; ++e)
-                    bq[u][s][e] = static_cast<T>(phi<T>(to_f32(qr[u].e[8 * s + e])));
+                    bq[u][s][e] = static_cast<T>(phi<FM, T>(to_f32(qr[u].e[8 * s + e])));
         sched_fence();
         issue(qr, blk + NS * NW);
         sched_fence();
@@ -1184,7 +1208,7 @@ struct BwdQShape {
 // w carries the power of two 2^sw ~ sum(z) (f16 only) so that dO / den, about
 // 1e-6 for long sequences, does not fall into f16 subnormals; dS is unscaled
 // in fp32 when written.
-template <typename T, int D, bool SIMPLE>
+template <typename T, int D, bool SIMPLE, int FM>
 __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(
     const T* __restrict__ q, const T* __restrict__ dout, const float* __restrict__ stS,
     const float* __restrict__ stz, T* __restrict__ dq, float* __restrict__ part,
@@ -1260,7 +1284,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(
             load_row<T, F>(dr, dout + head_offset(lay, bh) + tc * lay.rs + F * grp);
             float qt[F];
 #pragma unroll
-            for (int o = 0; o < F; ++o) qt[o] = phi<T>(to_f32(qr.e[o]));
+            for (int o = 0; o < F; ++o) qt[o] = phi<FM, T>(to_f32(qr.e[o]));
             Frag<T> bq[KS], bd[KS];
 #pragma unroll
             for (int s = 0; s < KS; ++s)
@@ -1313,7 +1337,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(
             if (valid) {
                 float out[F];
 #pragma unroll
-                for (int o = 0; o < F; ++o) out[o] = dqt[o] * fminf(qt[o], 1.f);  // phi' = min(phi, 1)
+                for (int o = 0; o < F; ++o) out[o] = dqt[o] * dphi_of<FM>(qt[o]);
                 store_row<T, F>(dq + head_offset(lay, bh) + t * lay.rs + F * grp, out);
             }
             const int col = (wave * U + u) * 16 + m;
@@ -1395,7 +1419,7 @@ struct BwdQW64 {
     static constexpr int kRound = kStep * kWaves;
 };
 
-template <typename T, bool SIMPLE>
+template <typename T, bool SIMPLE, int FM>
 __global__ __launch_bounds__(kThreads, 2) void bwd_dq_w64_kernel(
     const T* __restrict__ q, const T* __restrict__ dout, const float* __restrict__ stS,
     const float* __restrict__ stz, T* __restrict__ dq, float* __restrict__ part,
@@ -1493,10 +1517,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_w64_kernel(
         Frag<T> bq[KS], bd[KS];
 #pragma unroll
         for (int o = 0; o < F; ++o) {
-            const float x = to_f32(lq.e[o]);
-            const float e = phi_exp<T>(x);
-            qt[o] = x > 0.f ? x + 1.f : e;  // phi
-            dph[o] = x > 0.f ? 1.f : e;     // phi'
+            feature<FM, T>(to_f32(lq.e[o]), qt[o], dph[o]);
         }
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
@@ -1673,7 +1694,7 @@ struct BwdQTile {
     static constexpr int kMinBlocks = D == 64 ? 3 : 1;
 };
 
-template <typename T, int D, bool SIMPLE>
+template <typename T, int D, bool SIMPLE, int FM>
 __global__ __launch_bounds__(BwdQTile<D>::kThreads, BwdQTile<D>::kMinBlocks) void bwd_dq_tile_kernel(
     const T* __restrict__ q, const T* __restrict__ dout, const float* __restrict__ stS,
     const float* __restrict__ stz, T* __restrict__ dq, float* __restrict__ part,
@@ -1765,7 +1786,7 @@ __global__ __launch_bounds__(BwdQTile<D>::kThreads, BwdQTile<D>::kMinBlocks) voi
         float qt[F];
         Frag<T> bqf[KS], bdf[KS];
 #pragma unroll
-        for (int o = 0; o < F; ++o) qt[o] = phi<T>(to_f32(lq.e[o]));
+        for (int o = 0; o < F; ++o) qt[o] = phi<FM, T>(to_f32(lq.e[o]));
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
             if constexpr (!SIMPLE)
@@ -1823,7 +1844,7 @@ __global__ __launch_bounds__(BwdQTile<D>::kThreads, BwdQTile<D>::kMinBlocks) voi
                 for (int r = 0; r < 4; ++r) {
                     const int o = 4 * b + r;
                     const float dqt = SIMPLE ? au[b][r] * ku : au[b][r] * ku + cc * zl[o];
-                    out.e[o] = static_cast<T>(dqt * fminf(qt[o], 1.f));  // phi' = min(phi, 1)
+                    out.e[o] = static_cast<T>(dqt * dphi_of<FM>(qt[o]));
                 }
             // staged through this wave's own rows of the A tile, which are
             // written with A right after
@@ -1890,7 +1911,7 @@ __global__ __launch_bounds__(BwdQTile<D>::kThreads, BwdQTile<D>::kMinBlocks) voi
 // dphi(k_t) = dS v_t + dz and dv_t = dS^T phi(k_t): both are products of a
 // fixed D x D matrix with a token's row, so each is one set of MFMA blocks with
 // dS (or dS^T) as the A operand and the loaded K/V quarter rows as B.
-template <typename T, int D, bool SIMPLE>
+template <typename T, int D, bool SIMPLE, int FM>
 __global__ __launch_bounds__((StreamShape<T, D>::kThreads), (StreamShape<T, D>::kKvMinBlocks)) void bwd_dkv_kernel(
     const T* __restrict__ k, const T* __restrict__ v, const float* __restrict__ dSg,
     const float* __restrict__ dzg, T* __restrict__ dk, T* __restrict__ dv, int64_t T_, const Layout lay, int NK,
@@ -1991,10 +2012,7 @@ __global__ __launch_bounds__((StreamShape<T, D>::kThreads), (StreamShape<T, D>::
             float kt[F];
 #pragma unroll
             for (int o = 0; o < F; ++o) {
-                const float x = to_f32(lk.e[o]);
-                const float e = phi_exp<T>(x);
-                kt[o] = x > 0.f ? x + 1.f : e;         // phi
-                dphik[u][o] = x > 0.f ? 1.f : e;       // phi'
+                feature<FM, T>(to_f32(lk.e[o]), kt[o], dphik[u][o]);
             }
 #pragma unroll
             for (int s = 0; s < KS; ++s)
@@ -2092,8 +2110,8 @@ hipError_t launch_combine(int P, const float* part, float* outS, float* outz, in
     return launch(combine_kernel<D>, BH * ((E4 + kThreads - 1) / kThreads), kThreads, s, part, P, outS, outz, BH);
 }
 
-template <typename T, int D>
-hipError_t fwd_state_t(const Plan& p, const void* k, const void* v, float* state, void* ws,
+template <typename T, int D, int FM>
+hipError_t fwd_state_fm(const Plan& p, const void* k, const void* v, float* state, void* ws,
                        hipStream_t s) {
     const int64_t nblk = p.BH * p.P;
     float* part = reinterpret_cast<float*>(static_cast<char*>(ws) + p.off_part);
@@ -2102,29 +2120,29 @@ hipError_t fwd_state_t(const Plan& p, const void* k, const void* v, float* state
     float* sz = state + p.BH * D * D;
     hipError_t e;
     if constexpr (kWaveKernels<T, D>)
-        e = launch(fwd_state_w64_kernel<T>, nblk, kThreads, s, kk, vv, state, sz, part, p.T, p.lay, p.P, p.L);
+        e = launch(fwd_state_w64_kernel<T, FM>, nblk, kThreads, s, kk, vv, state, sz, part, p.T, p.lay, p.P, p.L);
     else if constexpr (kTileKernels<T, D>)
-        e = launch(fwd_state_c128_kernel<T>, nblk, kThreads, s, kk, vv, state, sz, part, p.T, p.lay, p.P, p.L);
+        e = launch(fwd_state_c128_kernel<T, FM>, nblk, kThreads, s, kk, vv, state, sz, part, p.T, p.lay, p.P, p.L);
     else
-        e = launch(fwd_state_kernel<T, D>, nblk, kThreads, s, kk, vv, state, sz, part, p.T, p.lay, p.P, p.L);
+        e = launch(fwd_state_kernel<T, D, FM>, nblk, kThreads, s, kk, vv, state, sz, part, p.T, p.lay, p.P, p.L);
     if (e != hipSuccess) return e;
     return launch_combine<D>(p.P, part, state, sz, p.BH, s);
 }
 
-template <typename T, int D>
-hipError_t fwd_output_t(const Plan& p, const void* q, const float* state, void* o, hipStream_t s) {
+template <typename T, int D, int FM>
+hipError_t fwd_output_fm(const Plan& p, const void* q, const float* state, void* o, hipStream_t s) {
     const int64_t nblk = p.BH * p.NQ;
     constexpr int nt = StreamShape<T, D>::kThreads;
     const T* qq = static_cast<const T*>(q);
     const float* sz = state + p.BH * D * D;
     T* oo = static_cast<T*>(o);
     if (p.simple)
-        return launch(fwd_output_kernel<T, D, true>, nblk, nt, s, qq, state, sz, oo, p.T, p.lay, p.NQ, p.LQ, p.eps);
-    return launch(fwd_output_kernel<T, D, false>, nblk, nt, s, qq, state, sz, oo, p.T, p.lay, p.NQ, p.LQ, p.eps);
+        return launch(fwd_output_kernel<T, D, true, FM>, nblk, nt, s, qq, state, sz, oo, p.T, p.lay, p.NQ, p.LQ, p.eps);
+    return launch(fwd_output_kernel<T, D, false, FM>, nblk, nt, s, qq, state, sz, oo, p.T, p.lay, p.NQ, p.LQ, p.eps);
 }
 
-template <typename T, int D>
-hipError_t bwd_dq_t(const Plan& p, const void* q, const void* dout, const float* state, void* dq,
+template <typename T, int D, int FM>
+hipError_t bwd_dq_fm(const Plan& p, const void* q, const void* dout, const float* state, void* dq,
                     void* ws, hipStream_t s) {
     const int64_t nblk = p.BH * p.PB;
     char* w = static_cast<char*>(ws);
@@ -2139,28 +2157,28 @@ hipError_t bwd_dq_t(const Plan& p, const void* q, const void* dout, const float*
     float* dz = dst + p.BH * D * D;
     hipError_t e;
     if constexpr (kWaveKernels<T, D>) {
-        e = p.simple ? launch(bwd_dq_w64_kernel<T, true>, nblk, kThreads, s, qq, dd, sS, sz, g, part, dS, dz, p.T,
+        e = p.simple ? launch(bwd_dq_w64_kernel<T, true, FM>, nblk, kThreads, s, qq, dd, sS, sz, g, part, dS, dz, p.T,
                               p.lay, p.PB, p.LB, p.eps)
-                     : launch(bwd_dq_w64_kernel<T, false>, nblk, kThreads, s, qq, dd, sS, sz, g, part, dS, dz, p.T,
+                     : launch(bwd_dq_w64_kernel<T, false, FM>, nblk, kThreads, s, qq, dd, sS, sz, g, part, dS, dz, p.T,
                               p.lay, p.PB, p.LB, p.eps);
     } else if constexpr (kTileKernels<T, D>) {
         constexpr int nt = BwdQTile<D>::kThreads;
-        e = p.simple ? launch(bwd_dq_tile_kernel<T, D, true>, nblk, nt, s, qq, dd, sS, sz, g, part, dS, dz, p.T,
+        e = p.simple ? launch(bwd_dq_tile_kernel<T, D, true, FM>, nblk, nt, s, qq, dd, sS, sz, g, part, dS, dz, p.T,
                               p.lay, p.PB, p.LB, p.eps)
-                     : launch(bwd_dq_tile_kernel<T, D, false>, nblk, nt, s, qq, dd, sS, sz, g, part, dS, dz, p.T,
+                     : launch(bwd_dq_tile_kernel<T, D, false, FM>, nblk, nt, s, qq, dd, sS, sz, g, part, dS, dz, p.T,
                               p.lay, p.PB, p.LB, p.eps);
     } else {
-        e = p.simple ? launch(bwd_dq_kernel<T, D, true>, nblk, kThreads, s, qq, dd, sS, sz, g, part, dS, dz, p.T,
+        e = p.simple ? launch(bwd_dq_kernel<T, D, true, FM>, nblk, kThreads, s, qq, dd, sS, sz, g, part, dS, dz, p.T,
                               p.lay, p.PB, p.LB, p.eps)
-                     : launch(bwd_dq_kernel<T, D, false>, nblk, kThreads, s, qq, dd, sS, sz, g, part, dS, dz, p.T,
+                     : launch(bwd_dq_kernel<T, D, false, FM>, nblk, kThreads, s, qq, dd, sS, sz, g, part, dS, dz, p.T,
                               p.lay, p.PB, p.LB, p.eps);
     }
     if (e != hipSuccess) return e;
     return launch_combine<D>(p.PB, part, dS, dz, p.BH, s);
 }
 
-template <typename T, int D>
-hipError_t bwd_dkv_t(const Plan& p, const void* k, const void* v, void* dk, void* dv, void* ws,
+template <typename T, int D, int FM>
+hipError_t bwd_dkv_fm(const Plan& p, const void* k, const void* v, void* dk, void* dv, void* ws,
                      hipStream_t s) {
     const int64_t nblk = p.BH * p.NK;
     constexpr int nt = StreamShape<T, D>::kThreads;
@@ -2171,8 +2189,34 @@ hipError_t bwd_dkv_t(const Plan& p, const void* k, const void* v, void* dk, void
     T* gk = static_cast<T*>(dk);
     T* gv = static_cast<T*>(dv);
     if (p.simple)
-        return launch(bwd_dkv_kernel<T, D, true>, nblk, nt, s, kk, vv, dst, dz, gk, gv, p.T, p.lay, p.NK, p.LK);
-    return launch(bwd_dkv_kernel<T, D, false>, nblk, nt, s, kk, vv, dst, dz, gk, gv, p.T, p.lay, p.NK, p.LK);
+        return launch(bwd_dkv_kernel<T, D, true, FM>, nblk, nt, s, kk, vv, dst, dz, gk, gv, p.T, p.lay, p.NK, p.LK);
+    return launch(bwd_dkv_kernel<T, D, false, FM>, nblk, nt, s, kk, vv, dst, dz, gk, gv, p.T, p.lay, p.NK, p.LK);
+}
+
+// The feature map is a template parameter of every kernel: one switch here.
+#define LA_FEATURE_MAP(FN, ...)                                      \
+    switch (p.fm) {                                                  \
+        case kPhiRelu: return FN<T, D, kPhiRelu>(p, __VA_ARGS__);    \
+        case kPhiIdentity: return FN<T, D, kPhiIdentity>(p, __VA_ARGS__); \
+        default: return FN<T, D, kPhiElu1>(p, __VA_ARGS__);          \
+    }
+
+template <typename T, int D>
+hipError_t fwd_state_t(const Plan& p, const void* k, const void* v, float* state, void* ws, hipStream_t s) {
+    LA_FEATURE_MAP(fwd_state_fm, k, v, state, ws, s);
+}
+template <typename T, int D>
+hipError_t fwd_output_t(const Plan& p, const void* q, const float* state, void* o, hipStream_t s) {
+    LA_FEATURE_MAP(fwd_output_fm, q, state, o, s);
+}
+template <typename T, int D>
+hipError_t bwd_dq_t(const Plan& p, const void* q, const void* dout, const float* state, void* dq, void* ws,
+                    hipStream_t s) {
+    LA_FEATURE_MAP(bwd_dq_fm, q, dout, state, dq, ws, s);
+}
+template <typename T, int D>
+hipError_t bwd_dkv_t(const Plan& p, const void* k, const void* v, void* dk, void* dv, void* ws, hipStream_t s) {
+    LA_FEATURE_MAP(bwd_dkv_fm, k, v, dk, dv, ws, s);
 }
 
 // dtype codes follow la_dtype: 0 = f32, 1 = f16, 2 = bf16.

@@ -23,41 +23,55 @@ def decode(x: np.ndarray, dtype: str) -> np.ndarray:
     raise ValueError(f"unknown dtype {dtype!r}")
 
 
-def phi(x: np.ndarray) -> np.ndarray:
-    """Feature map elu(x) + 1, written piecewise: x + 1 for x > 0, exp(x) else.
+FEATURE_MAPS = ("elu1", "relu", "identity")
 
-    The piecewise form avoids computing exp(x) - 1 + 1, which cancels for
-    x << 0. elu is the feature map of the method's statement (FBi-LA README).
-    """
+
+def phi(x: np.ndarray, fm: str = "elu1") -> np.ndarray:
+    """Feature map. "elu1" (the method's statement): elu(x) + 1, written
+    piecewise, x + 1 for x > 0 and exp(x) else (the piecewise form avoids
+    exp(x) - 1 + 1, which cancels for x << 0). The pages' models vary the
+    kernelised map (FBi-LA README, "Models"); "relu" (max(x, 0)) and
+    "identity" (x) are the two plain alternatives offered."""
     x = np.asarray(x, dtype=np.float64)
+    if fm == "relu":
+        return np.maximum(x, 0.0)
+    if fm == "identity":
+        return x.copy()
+    assert fm == "elu1", fm
     return np.where(x > 0, x + 1.0, np.exp(np.minimum(x, 0.0)))
 
 
-def dphi(x: np.ndarray) -> np.ndarray:
-    """Derivative of phi: 1 for x > 0, exp(x) for x <= 0 (both sides are 1 at 0)."""
+def dphi(x: np.ndarray, fm: str = "elu1") -> np.ndarray:
+    """Derivative of phi. elu1: 1 for x > 0, exp(x) for x <= 0 (both sides are
+    1 at 0). relu: 1 for x > 0, 0 for x <= 0 (0 at the kink). identity: 1."""
     x = np.asarray(x, dtype=np.float64)
+    if fm == "relu":
+        return np.where(x > 0, 1.0, 0.0)
+    if fm == "identity":
+        return np.ones_like(x)
+    assert fm == "elu1", fm
     return np.where(x > 0, 1.0, np.exp(np.minimum(x, 0.0)))
 
 
-def quadratic_head(q, k, v, eps: float, simple: bool) -> np.ndarray:
+def quadratic_head(q, k, v, eps: float, simple: bool, fm: str = "elu1") -> np.ndarray:
     """Quadratic ("parallel") form for one (batch, head): [T, D] -> [T, D].
 
     A = phi(Q) phi(K)^T (T x T); normalised: O = (A V) / (A 1 + eps),
     simple_la: O = A V. flash-linear-attention README, "Different forms of
     linear attention", Parallel. Cost O(T^2 D): tiny T only.
     """
-    a = phi(q) @ phi(k).T
+    a = phi(q, fm) @ phi(k, fm).T
     num = a @ np.asarray(v, dtype=np.float64)
     if simple:
         return num
     return num / (a.sum(axis=1) + eps)[:, None]
 
 
-def output_head(q, s, z, eps: float, simple: bool) -> np.ndarray:
+def output_head(q, s, z, eps: float, simple: bool, fm: str = "elu1") -> np.ndarray:
     """Last step of the forward for one (batch, head), from a given state:
     O = phi(Q) S / (phi(Q) z + eps), or phi(Q) S for simple_la (FBi-LA
     README, intro and "Update" 2024-12-28)."""
-    qt = phi(q)
+    qt = phi(q, fm)
     num = qt @ s
     if simple:
         return num
@@ -65,17 +79,17 @@ def output_head(q, s, z, eps: float, simple: bool) -> np.ndarray:
     return num / den[:, None]
 
 
-def fwd_head(q, k, v, eps: float, simple: bool):
+def fwd_head(q, k, v, eps: float, simple: bool, fm: str = "elu1"):
     """Linear form for one (batch, head): returns (O, S, z).
 
     S = phi(K)^T V (D x D, S[i, j] = sum_t phi(k_t)[i] v_t[j]),
     z = sum_t phi(k_t), then O from output_head.
     """
-    s, z = state_head(k, v)
-    return output_head(q, s, z, eps, simple), s, z
+    s, z = state_head(k, v, fm)
+    return output_head(q, s, z, eps, simple, fm), s, z
 
 
-def bwd_q_side_head(q, do, s, z, eps: float, simple: bool):
+def bwd_q_side_head(q, do, s, z, eps: float, simple: bool, fm: str = "elu1"):
     """Q side of the backward for one (batch, head), from the forward state.
 
     The chain rule applied to the formula of fwd_head (the FBi-LA README's
@@ -89,30 +103,30 @@ def bwd_q_side_head(q, do, s, z, eps: float, simple: bool):
       dQ = dphi(q) * phi'(q)
     """
     do = np.asarray(do, dtype=np.float64)
-    qt = phi(q)
+    qt = phi(q, fm)
     u = do @ s.T  # row t is S dO_t
     if simple:
-        return u * dphi(q), qt.T @ do, np.zeros_like(z)
+        return u * dphi(q, fm), qt.T @ do, np.zeros_like(z)
     den = qt @ z + eps
     r = np.einsum("td,td->t", qt, u)
     c = -r / den**2
     dqt = u / den[:, None] + c[:, None] * z[None, :]
-    return dqt * dphi(q), qt.T @ (do / den[:, None]), c @ qt
+    return dqt * dphi(q, fm), qt.T @ (do / den[:, None]), c @ qt
 
 
-def bwd_kv_side_head(k, v, ds, dz, simple: bool):
+def bwd_kv_side_head(k, v, ds, dz, simple: bool, fm: str = "elu1"):
     """K/V side of the backward for one (batch, head), from (dS, dz), by the
     chain rule through S = phi(K)^T V and z = sum_t phi(k_t) (FBi-LA README,
     "Update" 2024-12-30; no formula printed there):
     dphi(k_t) = dS v_t + dz (simple_la: dS v_t), dK = dphi(k) * phi'(k),
     dV_t = dS^T phi(k_t). Returns (dK, dV)."""
     v = np.asarray(v, dtype=np.float64)
-    kt = phi(k)
+    kt = phi(k, fm)
     dkt = v @ ds.T if simple else v @ ds.T + dz[None, :]
-    return dkt * dphi(k), kt @ ds
+    return dkt * dphi(k, fm), kt @ ds
 
 
-def bwd_head(q, k, v, do, eps: float, simple: bool):
+def bwd_head(q, k, v, do, eps: float, simple: bool, fm: str = "elu1"):
     """Vector-Jacobian product of L = sum(O * dO) for one (batch, head).
 
     Returns (dQ, dK, dV). eps is a constant. Derived by the chain rule from
@@ -120,13 +134,13 @@ def bwd_head(q, k, v, do, eps: float, simple: bool):
     backward; it prints no formula): the state, then bwd_q_side_head, then
     bwd_kv_side_head.
     """
-    s, z = state_head(k, v)
-    dq, ds, dz = bwd_q_side_head(q, do, s, z, eps, simple)
-    dk, dv = bwd_kv_side_head(k, v, ds, dz, simple)
+    s, z = state_head(k, v, fm)
+    dq, ds, dz = bwd_q_side_head(q, do, s, z, eps, simple, fm)
+    dk, dv = bwd_kv_side_head(k, v, ds, dz, simple, fm)
     return dq, dk, dv
 
 
-def bwd_leading_terms_head(q, k, v, do, eps: float):
+def bwd_leading_terms_head(q, k, v, do, eps: float, fm: str = "elu1"):
     """Largest summands of dQ and dK in normalised mode, for error scaling.
 
     dphi(q_t) = u_t / den_t + c_t z and dphi(k_t) = dS v_t + dz add terms that
@@ -137,33 +151,33 @@ def bwd_leading_terms_head(q, k, v, do, eps: float):
     """
     v = np.asarray(v, dtype=np.float64)
     do = np.asarray(do, dtype=np.float64)
-    qt, kt = phi(q), phi(k)
+    qt, kt = phi(q, fm), phi(k, fm)
     s = kt.T @ v
     z = kt.sum(axis=0)
     den = qt @ z + eps
     u = do @ s.T
     ds = qt.T @ (do / den[:, None])
-    return (float(np.max(np.abs(u / den[:, None] * dphi(q)))),
-            float(np.max(np.abs((v @ ds.T) * dphi(k)))))
+    return (float(np.max(np.abs(u / den[:, None] * dphi(q, fm)))),
+            float(np.max(np.abs((v @ ds.T) * dphi(k, fm)))))
 
 
-def state_head(k, v):
+def state_head(k, v, fm: str = "elu1"):
     """The state alone for one (batch, head): S = phi(K)^T V and z = sum_t phi(k_t)."""
-    kt = phi(k)
+    kt = phi(k, fm)
     return kt.T @ np.asarray(v, dtype=np.float64), kt.sum(axis=0)
 
 
-def sampled_rows_head(q, k, v, rows, eps: float, simple: bool) -> np.ndarray:
+def sampled_rows_head(q, k, v, rows, eps: float, simple: bool, fm: str = "elu1") -> np.ndarray:
     """Output rows O_t, t in ``rows``, computed one by one from the quadratic form.
 
     O_t = sum_s a_ts v_s / (sum_s a_ts + eps) with a_ts = phi(q_t) . phi(k_s);
     cost O(T D) per row, so it serves full-size sequences.
     """
-    kt = phi(k)
+    kt = phi(k, fm)
     v = np.asarray(v, dtype=np.float64)
     out = np.empty((len(rows), v.shape[1]))
     for n, t in enumerate(rows):
-        a = kt @ phi(q[t])
+        a = kt @ phi(q[t], fm)
         out[n] = a @ v
         if not simple:
             out[n] /= a.sum() + eps
@@ -176,7 +190,7 @@ def _heads(x: np.ndarray, dtype: str):
     return d.reshape(-1, d.shape[-2], d.shape[-1])
 
 
-def fwd(q, k, v, dtype: str, eps: float, simple: bool):
+def fwd(q, k, v, dtype: str, eps: float, simple: bool, fm: str = "elu1"):
     """Forward over [B, H, T, D] storage arrays: (O [B,H,T,D], S [B,H,D,D], z [B,H,D])."""
     shape = q.shape
     qh, kh, vh = _heads(q, dtype), _heads(k, dtype), _heads(v, dtype)
@@ -185,15 +199,15 @@ def fwd(q, k, v, dtype: str, eps: float, simple: bool):
     s = np.empty((n, d, d))
     z = np.empty((n, d))
     for h in range(n):
-        o[h], s[h], z[h] = fwd_head(qh[h], kh[h], vh[h], eps, simple)
+        o[h], s[h], z[h] = fwd_head(qh[h], kh[h], vh[h], eps, simple, fm)
     return o.reshape(shape), s.reshape(shape[:-2] + (d, d)), z.reshape(shape[:-2] + (d,))
 
 
-def bwd(q, k, v, do, dtype: str, eps: float, simple: bool):
+def bwd(q, k, v, do, dtype: str, eps: float, simple: bool, fm: str = "elu1"):
     """Backward over [B, H, T, D] storage arrays: (dQ, dK, dV), each [B,H,T,D] float64."""
     shape = q.shape
     qh, kh, vh, dh = (_heads(x, dtype) for x in (q, k, v, do))
     dq, dk, dv = (np.empty(qh.shape) for _ in range(3))
     for h in range(qh.shape[0]):
-        dq[h], dk[h], dv[h] = bwd_head(qh[h], kh[h], vh[h], dh[h], eps, simple)
+        dq[h], dk[h], dv[h] = bwd_head(qh[h], kh[h], vh[h], dh[h], eps, simple, fm)
     return dq.reshape(shape), dk.reshape(shape), dv.reshape(shape)

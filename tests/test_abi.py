@@ -125,8 +125,9 @@ def test_fwd_rejects_bad_problems(L):
     assert fwd_call(L, prob(T=(1 << 31) // (128 * 2), D=128)) == SHAPE
     assert L.la_workspace_bytes(ctypes.byref(prob(T=(1 << 31) // (128 * 2) - 1, D=128))) > 0
     assert L.la_workspace_bytes(ctypes.byref(prob(T=(1 << 31) // (64 * 4), D=64, dtype=0))) == 0
-    assert fwd_call(L, prob(flags=4)) == FLAGS
+    assert fwd_call(L, prob(flags=0x10)) == FLAGS
     assert fwd_call(L, prob(flags=0x80000000)) == FLAGS
+    assert fwd_call(L, prob(flags=0x4 | 0x8)) == FLAGS  # two feature maps
     assert fwd_call(L, prob(eps=-1e-3)) == EPS
     assert fwd_call(L, prob(eps=float("nan"))) == EPS
     assert fwd_call(L, prob(eps=float("inf"))) == EPS
@@ -194,7 +195,7 @@ def test_step_calls_validate(L):
     assert L.la_fwd_state(ctypes.byref(p), d[0], d[1], d[2], d[3], need - 1, None) == WORKSPACE
     assert L.la_fwd_state(ctypes.byref(p), d[0], d[1], d[0], d[3], need, None) == ALIAS
     assert L.la_fwd_output(ctypes.byref(p), d[0], d[1], d[0], None) == ALIAS
-    assert L.la_fwd_output(ctypes.byref(prob(flags=4)), d[0], d[1], d[2], None) == FLAGS
+    assert L.la_fwd_output(ctypes.byref(prob(flags=0x10)), d[0], d[1], d[2], None) == FLAGS
     assert L.la_bwd_dq(ctypes.byref(p), d[0], d[1], z, d[3], d[4], need, None) == NULL
     assert L.la_bwd_dq(ctypes.byref(p), d[0], d[1], d[2], d[1], d[4], need, None) == ALIAS
     assert L.la_bwd_dkv(ctypes.byref(p), d[0], d[1], d[2], d[2], d[4], need, None) == ALIAS

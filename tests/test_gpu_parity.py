@@ -432,3 +432,35 @@ def test_autograd_wrapper_token_major():
     dq_ref, dk_ref, dv_ref = oracle.bwd(x["q"], x["k"], x["v"], x["do"], w.dtype, w.eps, False)
     for name, g, ref in (("dQ", q.grad, dq_ref), ("dK", k.grad, dk_ref), ("dV", v.grad, dv_ref)):
         check(name, decode(g.transpose(1, 2).contiguous(), w.dtype), ref, w.dtype)
+
+
+@pytest.mark.parametrize("fm,simple", [("relu", False), ("relu", True), ("identity", True), ("identity", False)],
+                         ids=["relu-norm", "relu-simple", "identity-simple", "identity-norm"])
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("T", [129, 4097])
+def test_other_feature_maps(T, D, dtype, fm, simple):
+    """phi = relu or identity (LA_PHI_RELU, LA_PHI_IDENTITY) against the oracle,
+    every element. With the identity map a normalised denominator can vanish,
+    so that case takes positive Q and K."""
+    from synth import to_storage
+    seed = 50_000 + 97 * T + D + 7 * ["f32", "f16", "bf16"].index(dtype) + 3 * ["relu", "identity"].index(fm)
+    w = Workload("maps", 2, 3, T, D, dtype, simple=simple, seed=seed)
+    print(f"case phi={fm} simple={simple} T={T} D={D} {dtype} seed={seed}", flush=True)
+    x = make_inputs(w, with_grad=True)
+    if fm == "identity" and not simple:
+        for n in ("q", "k"):
+            x[n] = to_storage((np.abs(oracle.decode(x[n], dtype)) + 0.5).astype(np.float32), dtype)
+    dev = {n: to_device(a, dtype) for n, a in x.items()}
+    o, state = la.fwd(dev["q"], dev["k"], dev["v"], eps=w.eps, simple=simple, phi=fm)
+    dq, dk, dv = la.bwd(dev["q"], dev["k"], dev["v"], dev["do"], state, eps=w.eps, simple=simple, phi=fm)
+    torch.cuda.synchronize()
+    o_ref, s_ref, z_ref = oracle.fwd(x["q"], x["k"], x["v"], dtype, w.eps, simple, fm)
+    dq_ref, dk_ref, dv_ref = oracle.bwd(x["q"], x["k"], x["v"], x["do"], dtype, w.eps, simple, fm)
+    s_got, z_got = split_state(state, w.B, w.H, D)
+    check("S", s_got, s_ref, dtype)
+    check("z", z_got, z_ref, dtype)
+    check("O", decode(o, dtype), o_ref, dtype)
+    check("dQ", decode(dq, dtype), dq_ref, dtype)
+    check("dK", decode(dk, dtype), dk_ref, dtype)
+    check("dV", decode(dv, dtype), dv_ref, dtype)

@@ -60,9 +60,13 @@ def test_phi_special_values_and_derivative():
 
 # ---------------------------------------------------------------- forward
 
-def brute_force(q, k, v, eps, simple):
+def brute_force(q, k, v, eps, simple, fm="elu1"):
     """Pure-Python quadratic form: O_t = sum_s a_ts v_s / (sum_s a_ts + eps)."""
     def ph(x):
+        if fm == "relu":
+            return x if x > 0 else 0.0
+        if fm == "identity":
+            return x
         return x + 1.0 if x > 0 else math.exp(x)
     T, D = len(q), len(q[0])
     out = []
@@ -187,12 +191,12 @@ def test_batched_fwd_matches_per_head_and_decodes():
 
 # ---------------------------------------------------------------- backward
 
-def loss(q, k, v, do, eps, simple):
-    o, _, _ = oracle.fwd_head(q, k, v, eps, simple)
+def loss(q, k, v, do, eps, simple, fm="elu1"):
+    o, _, _ = oracle.fwd_head(q, k, v, eps, simple, fm)
     return float(np.sum(o * do))
 
 
-def finite_difference(q, k, v, do, eps, simple, which, coords, h=1e-6):
+def finite_difference(q, k, v, do, eps, simple, which, coords, h=1e-6, fm="elu1"):
     arrs = {"q": q, "k": k, "v": v}
     out = []
     for (t, d) in coords:
@@ -200,8 +204,8 @@ def finite_difference(q, k, v, do, eps, simple, which, coords, h=1e-6):
         minus = {n: a.copy() for n, a in arrs.items()}
         plus[which][t, d] += h
         minus[which][t, d] -= h
-        out.append((loss(plus["q"], plus["k"], plus["v"], do, eps, simple)
-                    - loss(minus["q"], minus["k"], minus["v"], do, eps, simple)) / (2 * h))
+        out.append((loss(plus["q"], plus["k"], plus["v"], do, eps, simple, fm)
+                    - loss(minus["q"], minus["k"], minus["v"], do, eps, simple, fm)) / (2 * h))
     return np.array(out)
 
 
@@ -375,3 +379,66 @@ def test_backward_halves_compose_and_add_over_tokens(simple):
     np.testing.assert_allclose(dv, dv_ref, rtol=1e-13, atol=1e-13)
     o = oracle.output_head(q, s, z, 0.25, simple)
     np.testing.assert_allclose(o, oracle.quadratic_head(q, k, v, 0.25, simple), rtol=1e-12, atol=1e-13)
+
+
+# ---------------------------------------------------------------- relu and identity maps
+
+def test_relu_and_identity_maps():
+    torch = pytest.importorskip("torch")
+    x = np.concatenate([rand((1000,), 61, 3.0), [0.0, -0.0, 1e-300, -1e-300]])
+    np.testing.assert_array_equal(oracle.phi(x, "relu"), torch.relu(torch.tensor(x)).numpy())
+    np.testing.assert_array_equal(oracle.phi(x, "identity"), x)
+    np.testing.assert_array_equal(oracle.dphi(x, "relu"), (x > 0).astype(np.float64))
+    assert oracle.dphi(np.array([0.0]), "relu")[0] == 0.0
+    np.testing.assert_array_equal(oracle.dphi(x, "identity"), np.ones_like(x))
+    assert np.isnan(oracle.phi(np.array([np.nan]), "relu")[0])
+
+
+CASES_OTHER_MAPS = [("relu", False), ("relu", True), ("identity", True), ("identity", False)]
+
+
+def positive_if_identity_normalised(x, fm, simple):
+    # with the identity map a normalised denominator can vanish; keep it away
+    return np.abs(x) + 0.5 if (fm == "identity" and not simple) else x
+
+
+@pytest.mark.parametrize("fm,simple", CASES_OTHER_MAPS)
+@pytest.mark.parametrize("T,D", [(1, 5), (7, 5), (16, 8)])
+def test_other_maps_linear_form_matches_brute_force(T, D, fm, simple):
+    q, k, v = (rand((T, D), 71 + i) for i in range(3))
+    q, k = (positive_if_identity_normalised(a, fm, simple) for a in (q, k))
+    ref = brute_force(q.tolist(), k.tolist(), v.tolist(), 0.3, simple, fm)
+    o, _, _ = oracle.fwd_head(q, k, v, 0.3, simple, fm)
+    assert np.max(np.abs(o - ref)) <= 1e-12 * max(1.0, np.abs(ref).max())
+
+
+@pytest.mark.parametrize("fm,simple", CASES_OTHER_MAPS)
+def test_other_maps_bwd_matches_finite_differences(fm, simple):
+    T, D = 9, 6
+    q = away_from_zero(rand((T, D), 81), 1e-3)
+    k = away_from_zero(rand((T, D), 82), 1e-3)
+    q, k = (positive_if_identity_normalised(a, fm, simple) for a in (q, k))
+    v, do = rand((T, D), 83), rand((T, D), 84)
+    eps = 0.5
+    grads = dict(zip("qkv", oracle.bwd_head(q, k, v, do, eps, simple, fm)))
+    coords = [(t, d) for t in range(T) for d in range(D)]
+    for name, g in grads.items():
+        fd = finite_difference(q, k, v, do, eps, simple, name, coords, fm=fm).reshape(T, D)
+        assert np.max(np.abs(g - fd)) <= 1e-6 * max(1.0, np.abs(fd).max()), (fm, name)
+
+
+@pytest.mark.parametrize("simple", [False, True])
+def test_relu_bwd_matches_torch_autograd_of_quadratic_form(simple):
+    torch = pytest.importorskip("torch")
+    T, D = 40, 12
+    q, k, v, do = (rand((T, D), s) for s in (91, 92, 93, 94))
+    eps = 0.05
+    tq, tk, tv = (torch.tensor(a, dtype=torch.float64, requires_grad=True) for a in (q, k, v))
+    a = torch.relu(tq) @ torch.relu(tk).T
+    o = a @ tv
+    if not simple:
+        o = o / (a.sum(dim=1, keepdim=True) + eps)
+    (o * torch.tensor(do)).sum().backward()
+    for g, t in zip(oracle.bwd_head(q, k, v, do, eps, simple, "relu"), (tq, tk, tv)):
+        ref = t.grad.numpy()
+        assert np.max(np.abs(g - ref)) <= 1e-12 * np.abs(ref).max()
