@@ -54,7 +54,8 @@ def dphi(x: np.ndarray, fm: str = "elu1") -> np.ndarray:
 
 
 def quadratic_head(q, k, v, eps: float, simple: bool, fm: str = "elu1") -> np.ndarray:
-    """Quadratic ("parallel") form for one (batch, head): [T, D] -> [T, D].
+    """Quadratic ("parallel") form for one (batch, head): Q, K [T, Dk] and
+    V [T, Dv] -> O [T, Dv].
 
     A = phi(Q) phi(K)^T (T x T); normalised: O = (A V) / (A 1 + eps),
     simple_la: O = A V. flash-linear-attention README, "Different forms of
@@ -82,7 +83,7 @@ def output_head(q, s, z, eps: float, simple: bool, fm: str = "elu1") -> np.ndarr
 def fwd_head(q, k, v, eps: float, simple: bool, fm: str = "elu1"):
     """Linear form for one (batch, head): returns (O, S, z).
 
-    S = phi(K)^T V (D x D, S[i, j] = sum_t phi(k_t)[i] v_t[j]),
+    S = phi(K)^T V (Dk x Dv, S[i, j] = sum_t phi(k_t)[i] v_t[j]),
     z = sum_t phi(k_t), then O from output_head.
     """
     s, z = state_head(k, v, fm)
@@ -191,23 +192,25 @@ def _heads(x: np.ndarray, dtype: str):
 
 
 def fwd(q, k, v, dtype: str, eps: float, simple: bool, fm: str = "elu1"):
-    """Forward over [B, H, T, D] storage arrays: (O [B,H,T,D], S [B,H,D,D], z [B,H,D])."""
-    shape = q.shape
+    """Forward over storage arrays Q, K [B, H, T, Dk] and V [B, H, T, Dv]:
+    (O [B,H,T,Dv], S [B,H,Dk,Dv], z [B,H,Dk])."""
+    lead = q.shape[:-1]
     qh, kh, vh = _heads(q, dtype), _heads(k, dtype), _heads(v, dtype)
-    n, d = qh.shape[0], shape[-1]
-    o = np.empty(qh.shape)
-    s = np.empty((n, d, d))
-    z = np.empty((n, d))
+    n, dk, dv = qh.shape[0], q.shape[-1], v.shape[-1]
+    o = np.empty(vh.shape)
+    s = np.empty((n, dk, dv))
+    z = np.empty((n, dk))
     for h in range(n):
         o[h], s[h], z[h] = fwd_head(qh[h], kh[h], vh[h], eps, simple, fm)
-    return o.reshape(shape), s.reshape(shape[:-2] + (d, d)), z.reshape(shape[:-2] + (d,))
+    return (o.reshape(lead + (dv,)), s.reshape(lead[:-1] + (dk, dv)),
+            z.reshape(lead[:-1] + (dk,)))
 
 
 def bwd(q, k, v, do, dtype: str, eps: float, simple: bool, fm: str = "elu1"):
-    """Backward over [B, H, T, D] storage arrays: (dQ, dK, dV), each [B,H,T,D] float64."""
-    shape = q.shape
+    """Backward over storage arrays Q, K [B, H, T, Dk] and V, dO [B, H, T, Dv]:
+    (dQ, dK, dV), float64, shaped like Q, K, V."""
     qh, kh, vh, dh = (_heads(x, dtype) for x in (q, k, v, do))
-    dq, dk, dv = (np.empty(qh.shape) for _ in range(3))
+    dq, dk, dv = np.empty(qh.shape), np.empty(kh.shape), np.empty(vh.shape)
     for h in range(qh.shape[0]):
         dq[h], dk[h], dv[h] = bwd_head(qh[h], kh[h], vh[h], dh[h], eps, simple, fm)
-    return dq.reshape(shape), dk.reshape(shape), dv.reshape(shape)
+    return dq.reshape(q.shape), dk.reshape(k.shape), dv.reshape(v.shape)

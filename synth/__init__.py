@@ -57,7 +57,8 @@ def normal(shape, seed: int, sigma: float, dtype: str) -> np.ndarray:
 
 @dataclass(frozen=True)
 class Workload:
-    """One synthetic problem: shape [B, H, T, D], dtype, distribution, mode."""
+    """One synthetic problem: Q and K [B, H, T, D], V and dO [B, H, T, Dv]
+    (Dv = 0 stands for Dv = D), dtype, distribution, mode."""
 
     name: str
     B: int
@@ -70,15 +71,33 @@ class Workload:
     eps: float = 1e-6
     bwd: bool = True
     seed: int = 0
+    Dv: int = 0
     extra: dict = field(default_factory=dict, compare=False)
 
     @property
+    def dv(self) -> int:
+        """Head size of V, O, dO and dV."""
+        return self.Dv or self.D
+
+    @property
     def shape(self):
+        """Shape of Q, K, dQ, dK."""
         return (self.B, self.H, self.T, self.D)
 
     @property
+    def shape_v(self):
+        """Shape of V, O, dO, dV."""
+        return (self.B, self.H, self.T, self.dv)
+
+    @property
     def numel(self) -> int:
+        """Elements of one Q-side tensor."""
         return self.B * self.H * self.T * self.D
+
+    @property
+    def numel_v(self) -> int:
+        """Elements of one V-side tensor."""
+        return self.B * self.H * self.T * self.dv
 
     @property
     def elem_bytes(self) -> int:
@@ -94,10 +113,10 @@ def make_inputs(w: Workload, with_grad: bool | None = None) -> dict:
     out = {
         "q": normal(w.shape, w.seed + 0, w.sigma, w.dtype),
         "k": normal(w.shape, w.seed + 1, w.sigma, w.dtype),
-        "v": normal(w.shape, w.seed + 2, w.sigma, w.dtype),
+        "v": normal(w.shape_v, w.seed + 2, w.sigma, w.dtype),
     }
     if with_grad:
-        out["do"] = normal(w.shape, w.seed + 3, 1.0, w.dtype)
+        out["do"] = normal(w.shape_v, w.seed + 3, 1.0, w.dtype)
     return out
 
 

@@ -68,11 +68,11 @@ def brute_force(q, k, v, eps, simple, fm="elu1"):
         if fm == "identity":
             return x
         return x + 1.0 if x > 0 else math.exp(x)
-    T, D = len(q), len(q[0])
+    T, D, Dv = len(q), len(q[0]), len(v[0])
     out = []
     for t in range(T):
         a = [sum(ph(q[t][i]) * ph(k[s][i]) for i in range(D)) for s in range(T)]
-        row = [sum(a[s] * v[s][j] for s in range(T)) for j in range(D)]
+        row = [sum(a[s] * v[s][j] for s in range(T)) for j in range(Dv)]
         if not simple:
             den = sum(a) + eps
             row = [x / den for x in row]
@@ -81,9 +81,10 @@ def brute_force(q, k, v, eps, simple, fm="elu1"):
 
 
 @pytest.mark.parametrize("simple", [False, True])
-@pytest.mark.parametrize("T,D", [(1, 5), (7, 5), (16, 8), (40, 64)])
-def test_linear_form_matches_brute_force(T, D, simple):
-    q, k, v = rand((T, D), 1), rand((T, D), 2), rand((T, D), 3)
+@pytest.mark.parametrize("T,D,Dv", [(1, 5, 5), (7, 5, 5), (16, 8, 8), (40, 64, 64),
+                                    (7, 5, 3), (16, 8, 12), (40, 32, 96)])
+def test_linear_form_matches_brute_force(T, D, Dv, simple):
+    q, k, v = rand((T, D), 1), rand((T, D), 2), rand((T, Dv), 3)
     eps = 0.3  # large enough that a misplaced eps shows
     ref = brute_force(q.tolist(), k.tolist(), v.tolist(), eps, simple)
     o, _, _ = oracle.fwd_head(q, k, v, eps, simple)
@@ -179,6 +180,11 @@ def test_batched_fwd_matches_per_head_and_decodes():
     x = make_inputs(w, with_grad=False)
     o, s, z = oracle.fwd(x["q"], x["k"], x["v"], "bf16", 1e-6, False)
     assert o.shape == (2, 3, 20, 8) and s.shape == (2, 3, 8, 8) and z.shape == (2, 3, 8)
+    wr = Workload("t", 2, 3, 20, 8, "bf16", seed=77, Dv=12)
+    xr = make_inputs(wr, with_grad=False)
+    assert xr["q"].shape == (2, 3, 20, 8) and xr["v"].shape == (2, 3, 20, 12)
+    orr, sr, zr = oracle.fwd(xr["q"], xr["k"], xr["v"], "bf16", 1e-6, False)
+    assert orr.shape == (2, 3, 20, 12) and sr.shape == (2, 3, 8, 12) and zr.shape == (2, 3, 8)
     qd = oracle.decode(x["q"], "bf16")
     # bf16 values decode to float32-representable numbers with 8-bit mantissas
     m, _ = np.frexp(qd)
@@ -214,17 +220,19 @@ def away_from_zero(x, margin):
 
 
 @pytest.mark.parametrize("simple", [False, True])
-@pytest.mark.parametrize("T,D", [(5, 3), (16, 8)])
-def test_bwd_matches_finite_differences_all_coords(T, D, simple):
+@pytest.mark.parametrize("T,D,Dv", [(5, 3, 3), (16, 8, 8), (6, 3, 5), (9, 7, 2)])
+def test_bwd_matches_finite_differences_all_coords(T, D, Dv, simple):
     # inputs kept away from 0 where phi'' jumps; eps large enough to matter
     q = away_from_zero(rand((T, D), 21), 1e-4)
     k = away_from_zero(rand((T, D), 22), 1e-4)
-    v, do = rand((T, D), 23), rand((T, D), 24)
+    v, do = rand((T, Dv), 23), rand((T, Dv), 24)
     eps = 0.5
     dq, dk, dv = oracle.bwd_head(q, k, v, do, eps, simple)
-    coords = [(t, d) for t in range(T) for d in range(D)]
+    assert dq.shape == (T, D) and dk.shape == (T, D) and dv.shape == (T, Dv)
     for name, g in (("q", dq), ("k", dk), ("v", dv)):
-        fd = finite_difference(q, k, v, do, eps, simple, name, coords).reshape(T, D)
+        cols = Dv if name == "v" else D
+        coords = [(t, d) for t in range(T) for d in range(cols)]
+        fd = finite_difference(q, k, v, do, eps, simple, name, coords).reshape(T, cols)
         assert np.max(np.abs(g - fd)) <= 1e-6 * max(1.0, np.abs(fd).max()), name
 
 
@@ -245,10 +253,12 @@ def test_bwd_finite_differences_sampled_tiny_config_shape(simple):
 
 
 @pytest.mark.parametrize("simple", [False, True])
-def test_bwd_matches_torch_autograd_of_quadratic_form(simple):
+@pytest.mark.parametrize("D,Dv", [(16, 16), (16, 24)])
+def test_bwd_matches_torch_autograd_of_quadratic_form(D, Dv, simple):
     torch = pytest.importorskip("torch")
-    T, D = 48, 16
-    q, k, v, do = (rand((T, D), s) for s in (41, 42, 43, 44))
+    T = 48
+    q, k = rand((T, D), 41), rand((T, D), 42)
+    v, do = rand((T, Dv), 43), rand((T, Dv), 44)
     eps = 0.05
     tq, tk, tv = (torch.tensor(a, dtype=torch.float64, requires_grad=True) for a in (q, k, v))
     fq = torch.nn.functional.elu(tq) + 1
@@ -298,13 +308,15 @@ def test_bwd_constant_v_gives_zero_dq_dk():
 
 def test_batched_bwd_matches_per_head():
     from synth import Workload
-    w = Workload("t", 1, 2, 33, 8, "f16", seed=88)
-    x = make_inputs(w)
-    dq, dk, dv = oracle.bwd(x["q"], x["k"], x["v"], x["do"], "f16", 1e-6, False)
-    ref = oracle.bwd_head(*(oracle.decode(x[n], "f16")[0, 1] for n in ("q", "k", "v", "do")),
-                          1e-6, False)
-    for a, b in zip((dq[0, 1], dk[0, 1], dv[0, 1]), ref):
-        np.testing.assert_array_equal(a, b)
+    for dv_ in (0, 16):
+        w = Workload("t", 1, 2, 33, 8, "f16", seed=88, Dv=dv_)
+        x = make_inputs(w)
+        dq, dk, dv = oracle.bwd(x["q"], x["k"], x["v"], x["do"], "f16", 1e-6, False)
+        assert dq.shape == dk.shape == w.shape and dv.shape == w.shape_v
+        ref = oracle.bwd_head(*(oracle.decode(x[n], "f16")[0, 1] for n in ("q", "k", "v", "do")),
+                              1e-6, False)
+        for a, b in zip((dq[0, 1], dk[0, 1], dv[0, 1]), ref):
+            np.testing.assert_array_equal(a, b)
 
 
 # ---------------------------------------------------------------- planted mistakes
