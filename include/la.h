@@ -4,22 +4,23 @@
  *
  * The operation (Flash Bi-directional Linear Attention README: intro, and
  * "Update" 2024-12-28 for simple_la, "Update" 2024-12-30 for the backward).
- * Per batch b and head h, with Q, K, V in R^{T x D} and phi(x) = elu(x) + 1
- * (x + 1 for x > 0, e^x otherwise; LA_PHI_RELU and LA_PHI_IDENTITY select
- * relu(x) or x instead):
- *     S = sum_t phi(k_t) v_t^T          (D x D, S[i][j])
+ * Per batch b and head h, with Q, K in R^{T x D}, V in R^{T x Dv} and
+ * phi(x) = elu(x) + 1 (x + 1 for x > 0, e^x otherwise; LA_PHI_RELU and
+ * LA_PHI_IDENTITY select relu(x) or x instead):
+ *     S = sum_t phi(k_t) v_t^T          (D x Dv, S[i][j])
  *     z = sum_t phi(k_t)                (D)
  *     O_t = phi(q_t) S / (phi(q_t) . z + eps)      normalised (default)
  *     O_t = phi(q_t) S                              simple_la (LA_SIMPLE)
  * The backward returns dQ, dK, dV, the vector-Jacobian product of
  * L = sum(O * dO) with eps held constant.
  *
- * Layout. Every tensor q, k, v, o, dout, dq, dk, dv is a dense row-major
- * [B, H, T, D] array of `dtype` elements (D contiguous), 16-byte aligned;
- * with LA_LAYOUT_BTHD in flags they are [B, T, H, D] instead (each row of D
- * elements still contiguous, heads interleaved token by token).
- * `state` is fp32: B*H blocks of S (D*D floats, S[i][j] at i*D + j) followed by
- * B*H blocks of z (D floats); la_state_bytes() gives its size.
+ * Layout. q, k, dq, dk are dense row-major [B, H, T, D] arrays and v, o,
+ * dout, dv dense row-major [B, H, T, Dv] arrays of `dtype` elements (the last
+ * dimension contiguous), each 16-byte aligned; with LA_LAYOUT_BTHD in flags
+ * they are [B, T, H, D] and [B, T, H, Dv] instead (each row still contiguous,
+ * heads interleaved token by token). `state` is fp32: B*H blocks of S (D*Dv
+ * floats, S[i][j] at i*Dv + j) followed by B*H blocks of z (D floats);
+ * la_state_bytes() gives its size.
  *
  * Ownership. The caller allocates and owns all device memory: tensors, state
  * and workspace. The library never allocates, frees, synchronises or prints.
@@ -56,7 +57,7 @@
 extern "C" {
 #endif
 
-#define LA_VERSION 2
+#define LA_VERSION 3
 
 typedef enum {
     LA_F32 = 0,
@@ -69,7 +70,7 @@ typedef enum {
     LA_ERR_NULL = 1,       /* a required pointer is NULL                      */
     LA_ERR_SHAPE = 2,      /* B, H or T negative; B*H > 2^24; head too large  */
     LA_ERR_DTYPE = 3,      /* dtype not one of la_dtype                       */
-    LA_ERR_HEAD_DIM = 4,   /* D not supported (64 and 128 are)                */
+    LA_ERR_HEAD_DIM = 4,   /* D or Dv not one of 32, 64, 96, 128              */
     LA_ERR_FLAGS = 5,      /* unknown bit in flags, or two feature maps       */
     LA_ERR_EPS = 6,        /* eps negative or not finite                      */
     LA_ERR_WORKSPACE = 7,  /* ws_bytes below la_workspace_bytes()             */
@@ -89,14 +90,18 @@ typedef enum {
 #define LA_PHI_IDENTITY 0x8u
 
 /* Problem description shared by every call. B, H, T >= 0 (a zero size is an
- * empty problem: nothing to compute, LA_OK), B*H <= 2^24, D in {64, 128},
- * eps >= 0 and finite (used only in normalised mode). One head must span
- * less than 2^31 bytes, addressed with 32-bit offsets: T * D * elt < 2^31 in
- * [B, H, T, D]; (T + 1024) * H * D * elt < 2^31 in [B, T, H, D], where a
- * head's rows are H * D elements apart (the 1024 rows keep the offsets of the
- * padded blocks past a slice below 2^31 too). elt is the element size. */
+ * empty problem: nothing to compute, LA_OK), B*H <= 2^24. D is the head size
+ * of Q and K (and of dQ, dK), Dv that of V (and of O, dO, dV); 0 in Dv stands
+ * for Dv = D. Each of D and Dv is 32, 64, 96 or 128, in any combination.
+ * eps >= 0 and finite (used only in normalised mode). One head of each tensor
+ * must span less than 2^31 bytes, addressed with 32-bit offsets: with
+ * M = max(D, Dv), T * M * elt < 2^31 in [B, H, T, *]; (T + 1024) * H * M * elt
+ * < 2^31 in [B, T, H, *], where a head's rows are H * M elements apart at most
+ * (the 1024 rows keep the offsets of the padded blocks past a slice below 2^31
+ * too). elt is the element size. */
 typedef struct {
     int64_t B, H, T, D;
+    int64_t Dv;      /* head size of V, O, dO, dV; 0 means D */
     int32_t dtype;   /* la_dtype */
     uint32_t flags;  /* LA_SIMPLE, LA_LAYOUT_BTHD, one of LA_PHI_RELU, LA_PHI_IDENTITY */
     float eps;
@@ -108,7 +113,7 @@ int la_version(void);
 /* Static string naming a status code; never NULL. */
 const char* la_status_str(int status);
 
-/* Bytes of the fp32 state: B*H*(D*D + D)*4. 0 for an invalid problem. */
+/* Bytes of the fp32 state: B*H*(D*Dv + D)*4. 0 for an invalid problem. */
 size_t la_state_bytes(const la_problem* p);
 
 /* Bytes of workspace that la_fwd, la_bwd and the step calls below need for
@@ -148,7 +153,7 @@ int la_fwd_output(const la_problem* p, const void* q, const void* state, void* o
 int la_bwd_dq(const la_problem* p, const void* q, const void* dout, const void* state,
               void* dq, void* ws, size_t ws_bytes, void* stream);
 
-/* Step 7: dK = (dS v_t + dz) * phi'(k_t), dV_t = dS^T phi(k_t), reading the
+/* Step 7: dK = (dS v_t + dz) * phi'(k_t), dV_t = dS^T phi(k_t) (dS is D x Dv), reading the
  * backward state that la_bwd_dq left in the same workspace. */
 int la_bwd_dkv(const la_problem* p, const void* k, const void* v, void* dk, void* dv,
                void* ws, size_t ws_bytes, void* stream);

@@ -42,8 +42,8 @@ EXPORTS = ("la_version", "la_status_str", "la_state_bytes", "la_workspace_bytes"
 class Problem(ctypes.Structure):
     """Mirror of la_problem."""
     _fields_ = [("B", ctypes.c_int64), ("H", ctypes.c_int64), ("T", ctypes.c_int64),
-                ("D", ctypes.c_int64), ("dtype", ctypes.c_int32), ("flags", ctypes.c_uint32),
-                ("eps", ctypes.c_float)]
+                ("D", ctypes.c_int64), ("Dv", ctypes.c_int64), ("dtype", ctypes.c_int32),
+                ("flags", ctypes.c_uint32), ("eps", ctypes.c_float)]
 
 
 class LAError(RuntimeError):
@@ -95,10 +95,10 @@ def _check(status: int) -> None:
 
 
 def make_problem(shape, dtype: torch.dtype, eps: float, simple: bool, layout: str = "bhtd",
-                 phi: str = "elu1") -> Problem:
-    """Problem for tensors of ``shape``: [B, H, T, D] (layout "bhtd") or
-    [B, T, H, D] (layout "bthd"); feature map phi "elu1" (elu(x) + 1), "relu"
-    or "identity"."""
+                 phi: str = "elu1", dv: int | None = None) -> Problem:
+    """Problem for Q/K-side tensors of ``shape``: [B, H, T, D] (layout "bhtd")
+    or [B, T, H, D] (layout "bthd"), V-side tensors with head size ``dv``
+    (None: D); feature map phi "elu1" (elu(x) + 1), "relu" or "identity"."""
     if layout not in LAYOUTS:
         raise ValueError(f"layout must be one of {LAYOUTS}, got {layout!r}")
     if phi not in FEATURE_MAPS:
@@ -112,19 +112,29 @@ def make_problem(shape, dtype: torch.dtype, eps: float, simple: bool, layout: st
     else:
         B, T, H, D = (int(x) for x in shape)
     flags = (LA_SIMPLE if simple else 0) | (LA_LAYOUT_BTHD if layout == "bthd" else 0) | FEATURE_MAPS[phi]
-    return Problem(B, H, T, D, DTYPE_CODE[dtype], flags, float(eps))
+    return Problem(B, H, T, D, D if dv is None else int(dv), DTYPE_CODE[dtype], flags, float(eps))
 
 
-def _tensor(x: torch.Tensor, like: torch.Tensor | None, name: str) -> torch.Tensor:
+def _tensor(x: torch.Tensor, like: torch.Tensor | None, name: str, last: int | None = None) -> torch.Tensor:
+    """x must be a contiguous GPU tensor; given ``like``, with its dtype,
+    device and leading three dimensions, and a last dimension of ``last``
+    (None: like's)."""
     if not isinstance(x, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
     if x.device.type != "cuda":
         raise ValueError(f"{name} must be on a GPU, got {x.device}")
     if not x.is_contiguous():
         raise ValueError(f"{name} must be contiguous [B, H, T, D]")
-    if like is not None and (x.shape != like.shape or x.dtype != like.dtype or x.device != like.device):
-        raise ValueError(f"{name} must match q in shape, dtype and device")
+    if like is not None:
+        want = tuple(like.shape[:-1]) + ((like.shape[-1] if last is None else last),)
+        if tuple(x.shape) != want or x.dtype != like.dtype or x.device != like.device:
+            raise ValueError(f"{name} must be {want} {like.dtype} on {like.device}, got "
+                             f"{tuple(x.shape)} {x.dtype} on {x.device}")
     return x
+
+
+def _new_like(x: torch.Tensor, last: int) -> torch.Tensor:
+    return torch.empty(tuple(x.shape[:-1]) + (last,), dtype=x.dtype, device=x.device)
 
 
 def _state(state, prob: Problem, device: torch.device, name: str = "state") -> torch.Tensor:
@@ -155,7 +165,7 @@ def workspace_bytes(prob: Problem) -> int:
 
 
 def new_state(prob: Problem, device) -> torch.Tensor:
-    """fp32 state buffer: B*H blocks of S (D*D) followed by B*H blocks of z (D)."""
+    """fp32 state buffer: B*H blocks of S (D*Dv) followed by B*H blocks of z (D)."""
     return torch.empty(state_bytes(prob) // 4, dtype=torch.float32, device=device)
 
 
@@ -188,8 +198,8 @@ def _ws(prob, device, ws):
 def fwd_state(k, v, *, eps=1e-6, simple=False, layout="bhtd", phi="elu1", state=None, ws=None):
     """Steps 1-3: the fp32 state (S, z) of phi(K), V."""
     _tensor(k, None, "k")
-    _tensor(v, k, "v")
-    prob = make_problem(k.shape, k.dtype, eps, simple, layout, phi)
+    _tensor(v, k, "v", v.shape[-1] if isinstance(v, torch.Tensor) else None)
+    prob = make_problem(k.shape, k.dtype, eps, simple, layout, phi, v.shape[-1])
     state = new_state(prob, k.device) if state is None else _state(state, prob, k.device)
     ws, wsb = _ws(prob, k.device, ws)
     _check(lib().la_fwd_state(ctypes.byref(prob), _ptr(k), _ptr(v), _ptr(state), _ptr(ws), wsb,
@@ -197,12 +207,15 @@ def fwd_state(k, v, *, eps=1e-6, simple=False, layout="bhtd", phi="elu1", state=
     return state
 
 
-def fwd_output(q, state, *, eps=1e-6, simple=False, layout="bhtd", phi="elu1", out=None):
-    """Step 4: O from Q and a complete state."""
+def fwd_output(q, state, *, eps=1e-6, simple=False, layout="bhtd", phi="elu1", out=None, dv=None):
+    """Step 4: O from Q and a complete state; dv is the head size of V and O
+    (None: that of out if given, else D)."""
     _tensor(q, None, "q")
-    prob = make_problem(q.shape, q.dtype, eps, simple, layout, phi)
+    if dv is None:
+        dv = out.shape[-1] if isinstance(out, torch.Tensor) else q.shape[-1]
+    prob = make_problem(q.shape, q.dtype, eps, simple, layout, phi, dv)
     _state(state, prob, q.device)
-    out = torch.empty_like(q) if out is None else _tensor(out, q, "out")
+    out = _new_like(q, dv) if out is None else _tensor(out, q, "out", dv)
     _check(lib().la_fwd_output(ctypes.byref(prob), _ptr(q), _ptr(state), _ptr(out), _stream(q.device)))
     return out
 
@@ -211,9 +224,10 @@ def fwd(q, k, v, *, eps=1e-6, simple=False, layout="bhtd", phi="elu1", out=None,
     """O = phi(Q) S / (phi(Q) z + eps) (or phi(Q) S); returns (O, state)."""
     _tensor(q, None, "q")
     _tensor(k, q, "k")
-    _tensor(v, q, "v")
-    prob = make_problem(q.shape, q.dtype, eps, simple, layout, phi)
-    out = torch.empty_like(q) if out is None else _tensor(out, q, "out")
+    dv = v.shape[-1] if isinstance(v, torch.Tensor) else None
+    _tensor(v, q, "v", dv)
+    prob = make_problem(q.shape, q.dtype, eps, simple, layout, phi, dv)
+    out = _new_like(q, dv) if out is None else _tensor(out, q, "out", dv)
     state = new_state(prob, q.device) if state is None else _state(state, prob, q.device)
     ws, wsb = _ws(prob, q.device, ws)
     _check(lib().la_fwd(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(state),
@@ -224,8 +238,9 @@ def fwd(q, k, v, *, eps=1e-6, simple=False, layout="bhtd", phi="elu1", out=None,
 def bwd_dq(q, do, state, *, eps=1e-6, simple=False, layout="bhtd", phi="elu1", dq=None, ws=None):
     """Steps 5-6: dQ; leaves dS, dz in the workspace for bwd_dkv."""
     _tensor(q, None, "q")
-    _tensor(do, q, "do")
-    prob = make_problem(q.shape, q.dtype, eps, simple, layout, phi)
+    dv = do.shape[-1] if isinstance(do, torch.Tensor) else None
+    _tensor(do, q, "do", dv)
+    prob = make_problem(q.shape, q.dtype, eps, simple, layout, phi, dv)
     _state(state, prob, q.device)
     dq = torch.empty_like(q) if dq is None else _tensor(dq, q, "dq")
     ws, wsb = _ws(prob, q.device, ws)
@@ -237,10 +252,11 @@ def bwd_dq(q, do, state, *, eps=1e-6, simple=False, layout="bhtd", phi="elu1", d
 def bwd_dkv(k, v, *, eps=1e-6, simple=False, layout="bhtd", phi="elu1", dk=None, dv=None, ws=None):
     """Step 7: dK, dV from the backward state bwd_dq left in the same workspace."""
     _tensor(k, None, "k")
-    _tensor(v, k, "v")
-    prob = make_problem(k.shape, k.dtype, eps, simple, layout, phi)
+    hv = v.shape[-1] if isinstance(v, torch.Tensor) else None
+    _tensor(v, k, "v", hv)
+    prob = make_problem(k.shape, k.dtype, eps, simple, layout, phi, hv)
     dk = torch.empty_like(k) if dk is None else _tensor(dk, k, "dk")
-    dv = torch.empty_like(k) if dv is None else _tensor(dv, k, "dv")
+    dv = _new_like(k, hv) if dv is None else _tensor(dv, k, "dv", hv)
     ws, wsb = _ws(prob, k.device, ws)
     _check(lib().la_bwd_dkv(ctypes.byref(prob), _ptr(k), _ptr(v), _ptr(dk), _ptr(dv), _ptr(ws), wsb,
                             _stream(k.device)))
@@ -250,13 +266,15 @@ def bwd_dkv(k, v, *, eps=1e-6, simple=False, layout="bhtd", phi="elu1", dk=None,
 def bwd(q, k, v, do, state, *, eps=1e-6, simple=False, layout="bhtd", phi="elu1", dq=None, dk=None, dv=None, ws=None):
     """dQ, dK, dV of L = sum(O * dO), from the state fwd returned."""
     _tensor(q, None, "q")
-    for n, x in (("k", k), ("v", v), ("do", do)):
-        _tensor(x, q, n)
-    prob = make_problem(q.shape, q.dtype, eps, simple, layout, phi)
+    _tensor(k, q, "k")
+    hv = v.shape[-1] if isinstance(v, torch.Tensor) else None
+    _tensor(v, q, "v", hv)
+    _tensor(do, q, "do", hv)
+    prob = make_problem(q.shape, q.dtype, eps, simple, layout, phi, hv)
     _state(state, prob, q.device)
     dq = torch.empty_like(q) if dq is None else _tensor(dq, q, "dq")
     dk = torch.empty_like(q) if dk is None else _tensor(dk, q, "dk")
-    dv = torch.empty_like(q) if dv is None else _tensor(dv, q, "dv")
+    dv = _new_like(q, hv) if dv is None else _tensor(dv, q, "dv", hv)
     ws, wsb = _ws(prob, q.device, ws)
     _check(lib().la_bwd(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(state),
                         _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws), wsb, _stream(q.device)))
@@ -289,6 +307,7 @@ def linear_attention(q, k, v, *, eps: float = 1e-6, simple: bool = False, layout
     """O = phi(Q) S / (phi(Q) z + eps) (or phi(Q) S with simple=True), with
     gradients for q, k and v through the library's backward. Tensors are
     [B, H, T, D] (layout "bhtd") or [B, T, H, D] (layout "bthd") on a GPU in
-    float32, float16 or bfloat16, D in {64, 128}; phi is "elu1" (elu + 1),
+    float32, float16 or bfloat16, with D (of q, k) and Dv (of v) each in
+    {32, 64, 96, 128}; phi is "elu1" (elu + 1),
     "relu" or "identity"."""
     return _LinearAttention.apply(q, k, v, float(eps), bool(simple), layout, phi)

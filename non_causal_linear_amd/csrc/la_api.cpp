@@ -47,15 +47,20 @@ void split(int64_t BH, int64_t T, la::SplitCfg cfg, int& P, int64_t& L) {
     P = static_cast<int>(cdiv(T, L));
 }
 
+bool head_size_ok(int64_t d) { return d == 32 || d == 64 || d == 96 || d == 128; }
+
+// Head size of V, O, dO and dV (0 in la_problem stands for D).
+int64_t dv_of(const la_problem* p) { return p->Dv ? p->Dv : p->D; }
+
 la_status check_problem(const la_problem* p) {
     if (!p) return LA_ERR_NULL;
     if (p->dtype != LA_F32 && p->dtype != LA_F16 && p->dtype != LA_BF16) return LA_ERR_DTYPE;
-    if (p->D != 64 && p->D != 128) return LA_ERR_HEAD_DIM;
+    if (!head_size_ok(p->D) || !head_size_ok(dv_of(p))) return LA_ERR_HEAD_DIM;
     if (p->B < 0 || p->H < 0 || p->T < 0) return LA_ERR_SHAPE;
     if (p->B > kMaxHeads || p->H > kMaxHeads || p->B * p->H > kMaxHeads) return LA_ERR_SHAPE;
     if (p->flags & ~(LA_SIMPLE | LA_LAYOUT_BTHD | LA_PHI_RELU | LA_PHI_IDENTITY)) return LA_ERR_FLAGS;
     if ((p->flags & LA_PHI_RELU) && (p->flags & LA_PHI_IDENTITY)) return LA_ERR_FLAGS;
-    const int64_t row_bytes = p->D * (p->dtype == LA_F32 ? 4 : 2);
+    const int64_t row_bytes = std::max(p->D, dv_of(p)) * (p->dtype == LA_F32 ? 4 : 2);
     if (p->flags & LA_LAYOUT_BTHD) {
         if (p->H > 0 && p->T + kRowSlack > kMaxHeadBytes / (p->H * row_bytes)) return LA_ERR_SHAPE;
     } else if (p->T > kMaxHeadBytes / row_bytes) {
@@ -67,11 +72,21 @@ la_status check_problem(const la_problem* p) {
 
 size_t elem_bytes(int dtype) { return dtype == LA_F32 ? 4 : 2; }
 
+// The kernels of one (dtype, DK); the problem has been checked.
+const la::KernelSet* kernel_set(int dtype, int DK) {
+#define LA_PICK_UNIT(dt, dk) \
+    if (dtype == dt && DK == dk) return la::kernel_set_##dt##_##dk();
+    LA_KERNEL_UNITS(LA_PICK_UNIT)
+#undef LA_PICK_UNIT
+    return nullptr;
+}
+
 la::Plan make_plan(const la_problem* p) {
     la::Plan pl;
     pl.BH = p->B * p->H;
     pl.T = p->T;
-    pl.D = static_cast<int>(p->D);
+    pl.DK = static_cast<int>(p->D);
+    pl.DV = static_cast<int>(dv_of(p));
     pl.dtype = p->dtype;
     pl.simple = (p->flags & LA_SIMPLE) != 0;
     pl.eps = p->eps;
@@ -86,11 +101,12 @@ la::Plan make_plan(const la_problem* p) {
         pl.lay.sh = p->T * p->D;
         pl.lay.rs = p->D;
     }
-    split(pl.BH, pl.T, la::split_config(la::kStepState, pl.dtype, pl.D), pl.P, pl.L);
-    split(pl.BH, pl.T, la::split_config(la::kStepBwdQ, pl.dtype, pl.D), pl.PB, pl.LB);
-    split(pl.BH, pl.T, la::split_config(la::kStepOutput, pl.dtype, pl.D), pl.NQ, pl.LQ);
-    split(pl.BH, pl.T, la::split_config(la::kStepBwdKV, pl.dtype, pl.D), pl.NK, pl.LK);
-    const size_t E = size_t(pl.D) * pl.D + pl.D;  // floats per (S, z) block
+    const la::KernelSet* ks = kernel_set(pl.dtype, pl.DK);
+    split(pl.BH, pl.T, ks->split_config(la::kStepState, pl.DV), pl.P, pl.L);
+    split(pl.BH, pl.T, ks->split_config(la::kStepBwdQ, pl.DV), pl.PB, pl.LB);
+    split(pl.BH, pl.T, ks->split_config(la::kStepOutput, pl.DV), pl.NQ, pl.LQ);
+    split(pl.BH, pl.T, ks->split_config(la::kStepBwdKV, pl.DV), pl.NK, pl.LK);
+    const size_t E = size_t(pl.DK) * pl.DV + pl.DK;  // floats per (S, z) block
     const int maxp = std::max(pl.P, pl.PB);
     const size_t part = maxp > 1 ? align256(size_t(pl.BH) * maxp * E * 4) : 0;
     const size_t st = align256(size_t(pl.BH) * E * 4);
@@ -154,7 +170,7 @@ const char* la_status_str(int s) {
         case LA_ERR_NULL: return "LA_ERR_NULL: required pointer is NULL";
         case LA_ERR_SHAPE: return "LA_ERR_SHAPE: B, H or T negative or too large";
         case LA_ERR_DTYPE: return "LA_ERR_DTYPE: unknown dtype";
-        case LA_ERR_HEAD_DIM: return "LA_ERR_HEAD_DIM: D must be 64 or 128";
+        case LA_ERR_HEAD_DIM: return "LA_ERR_HEAD_DIM: D and Dv must be 32, 64, 96 or 128";
         case LA_ERR_FLAGS: return "LA_ERR_FLAGS: unknown flag bit or two feature maps";
         case LA_ERR_EPS: return "LA_ERR_EPS: eps must be finite and >= 0";
         case LA_ERR_WORKSPACE: return "LA_ERR_WORKSPACE: workspace smaller than la_workspace_bytes()";
@@ -167,7 +183,7 @@ const char* la_status_str(int s) {
 
 size_t la_state_bytes(const la_problem* p) {
     if (check_problem(p) != LA_OK) return 0;
-    return size_t(p->B * p->H) * size_t(p->D * p->D + p->D) * 4;
+    return size_t(p->B * p->H) * size_t(p->D * dv_of(p) + p->D) * 4;
 }
 
 size_t la_workspace_bytes(const la_problem* p) {
@@ -180,14 +196,15 @@ int la_fwd_state(const la_problem* p, const void* k, const void* v, void* state,
     la_status st = check_problem(p);
     if (st != LA_OK) return st;
     const la::Plan pl = make_plan(p);
-    const size_t tb = size_t(pl.BH * pl.T * pl.D) * elem_bytes(pl.dtype);
+    const size_t tk = size_t(pl.BH * pl.T * pl.DK) * elem_bytes(pl.dtype);
+    const size_t tv = size_t(pl.BH * pl.T * pl.DV) * elem_bytes(pl.dtype);
     const size_t sb = la_state_bytes(p);
     if (pl.BH > 0 && !state) return LA_ERR_NULL;
     if (ws_bytes < pl.ws_bytes) return LA_ERR_WORKSPACE;
-    st = check_buffers({{k, tb}, {v, tb}}, {{state, sb}, {ws, pl.ws_bytes}}, {16, 16}, {16, 256});
+    st = check_buffers({{k, tk}, {v, tv}}, {{state, sb}, {ws, pl.ws_bytes}}, {16, 16}, {16, 256});
     if (st != LA_OK) return st;
     if (pl.BH == 0) return LA_OK;
-    return device_status(la::launch_fwd_state(pl, k, v, static_cast<float*>(state), ws,
+    return device_status(kernel_set(pl.dtype, pl.DK)->fwd_state(pl, k, v, static_cast<float*>(state), ws,
                                               static_cast<hipStream_t>(stream)));
 }
 
@@ -195,12 +212,13 @@ int la_fwd_output(const la_problem* p, const void* q, const void* state, void* o
     la_status st = check_problem(p);
     if (st != LA_OK) return st;
     const la::Plan pl = make_plan(p);
-    const size_t tb = size_t(pl.BH * pl.T * pl.D) * elem_bytes(pl.dtype);
+    const size_t tk = size_t(pl.BH * pl.T * pl.DK) * elem_bytes(pl.dtype);
+    const size_t tv = size_t(pl.BH * pl.T * pl.DV) * elem_bytes(pl.dtype);
     const size_t sb = la_state_bytes(p);
-    st = check_buffers({{q, tb}, {state, sb}}, {{o, tb}}, {16, 16}, {16});
+    st = check_buffers({{q, tk}, {state, sb}}, {{o, tv}}, {16, 16}, {16});
     if (st != LA_OK) return st;
-    if (tb == 0) return LA_OK;
-    return device_status(la::launch_fwd_output(pl, q, static_cast<const float*>(state), o,
+    if (tk == 0) return LA_OK;
+    return device_status(kernel_set(pl.dtype, pl.DK)->fwd_output(pl, q, static_cast<const float*>(state), o,
                                                static_cast<hipStream_t>(stream)));
 }
 
@@ -209,19 +227,20 @@ int la_fwd(const la_problem* p, const void* q, const void* k, const void* v, voi
     la_status st = check_problem(p);
     if (st != LA_OK) return st;
     const la::Plan pl = make_plan(p);
-    const size_t tb = size_t(pl.BH * pl.T * pl.D) * elem_bytes(pl.dtype);
+    const size_t tk = size_t(pl.BH * pl.T * pl.DK) * elem_bytes(pl.dtype);
+    const size_t tv = size_t(pl.BH * pl.T * pl.DV) * elem_bytes(pl.dtype);
     const size_t sb = la_state_bytes(p);
     if (ws_bytes < pl.ws_bytes) return LA_ERR_WORKSPACE;
-    st = check_buffers({{q, tb}, {k, tb}, {v, tb}}, {{o, tb}, {state, state ? sb : 0}, {ws, pl.ws_bytes}},
+    st = check_buffers({{q, tk}, {k, tk}, {v, tv}}, {{o, tv}, {state, state ? sb : 0}, {ws, pl.ws_bytes}},
                        {16, 16, 16}, {16, 16, 256});
     if (st != LA_OK) return st;
     if (pl.BH == 0) return LA_OK;
     float* stp = state ? static_cast<float*>(state)
                        : reinterpret_cast<float*>(static_cast<char*>(ws) + pl.off_fstate);
     hipStream_t s = static_cast<hipStream_t>(stream);
-    st = device_status(la::launch_fwd_state(pl, k, v, stp, ws, s));
-    if (st != LA_OK || tb == 0) return st;
-    return device_status(la::launch_fwd_output(pl, q, stp, o, s));
+    st = device_status(kernel_set(pl.dtype, pl.DK)->fwd_state(pl, k, v, stp, ws, s));
+    if (st != LA_OK || tk == 0) return st;
+    return device_status(kernel_set(pl.dtype, pl.DK)->fwd_output(pl, q, stp, o, s));
 }
 
 int la_bwd_dq(const la_problem* p, const void* q, const void* dout, const void* state, void* dq,
@@ -229,15 +248,16 @@ int la_bwd_dq(const la_problem* p, const void* q, const void* dout, const void* 
     la_status st = check_problem(p);
     if (st != LA_OK) return st;
     const la::Plan pl = make_plan(p);
-    const size_t tb = size_t(pl.BH * pl.T * pl.D) * elem_bytes(pl.dtype);
+    const size_t tk = size_t(pl.BH * pl.T * pl.DK) * elem_bytes(pl.dtype);
+    const size_t tv = size_t(pl.BH * pl.T * pl.DV) * elem_bytes(pl.dtype);
     const size_t sb = la_state_bytes(p);
     if (pl.BH > 0 && !state) return LA_ERR_NULL;
     if (ws_bytes < pl.ws_bytes) return LA_ERR_WORKSPACE;
-    st = check_buffers({{q, tb}, {dout, tb}, {state, sb}}, {{dq, tb}, {ws, pl.ws_bytes}}, {16, 16, 16},
+    st = check_buffers({{q, tk}, {dout, tv}, {state, sb}}, {{dq, tk}, {ws, pl.ws_bytes}}, {16, 16, 16},
                        {16, 256});
     if (st != LA_OK) return st;
-    if (tb == 0) return LA_OK;
-    return device_status(la::launch_bwd_dq(pl, q, dout, static_cast<const float*>(state), dq, ws,
+    if (tk == 0) return LA_OK;
+    return device_status(kernel_set(pl.dtype, pl.DK)->bwd_dq(pl, q, dout, static_cast<const float*>(state), dq, ws,
                                            static_cast<hipStream_t>(stream)));
 }
 
@@ -246,14 +266,15 @@ int la_bwd_dkv(const la_problem* p, const void* k, const void* v, void* dk, void
     la_status st = check_problem(p);
     if (st != LA_OK) return st;
     const la::Plan pl = make_plan(p);
-    const size_t tb = size_t(pl.BH * pl.T * pl.D) * elem_bytes(pl.dtype);
+    const size_t tk = size_t(pl.BH * pl.T * pl.DK) * elem_bytes(pl.dtype);
+    const size_t tv = size_t(pl.BH * pl.T * pl.DV) * elem_bytes(pl.dtype);
     if (ws_bytes < pl.ws_bytes) return LA_ERR_WORKSPACE;
-    if (tb && !ws) return LA_ERR_NULL;
-    st = check_buffers({{k, tb}, {v, tb}, {ws, tb ? pl.ws_bytes : 0}}, {{dk, tb}, {dv, tb}},
+    if (tk && !ws) return LA_ERR_NULL;
+    st = check_buffers({{k, tk}, {v, tv}, {ws, tk ? pl.ws_bytes : 0}}, {{dk, tk}, {dv, tv}},
                        {16, 16, 256}, {16, 16});
     if (st != LA_OK) return st;
-    if (tb == 0) return LA_OK;
-    return device_status(la::launch_bwd_dkv(pl, k, v, dk, dv, ws, static_cast<hipStream_t>(stream)));
+    if (tk == 0) return LA_OK;
+    return device_status(kernel_set(pl.dtype, pl.DK)->bwd_dkv(pl, k, v, dk, dv, ws, static_cast<hipStream_t>(stream)));
 }
 
 int la_bwd(const la_problem* p, const void* q, const void* k, const void* v, const void* dout,
@@ -261,19 +282,20 @@ int la_bwd(const la_problem* p, const void* q, const void* k, const void* v, con
     la_status st = check_problem(p);
     if (st != LA_OK) return st;
     const la::Plan pl = make_plan(p);
-    const size_t tb = size_t(pl.BH * pl.T * pl.D) * elem_bytes(pl.dtype);
+    const size_t tk = size_t(pl.BH * pl.T * pl.DK) * elem_bytes(pl.dtype);
+    const size_t tv = size_t(pl.BH * pl.T * pl.DV) * elem_bytes(pl.dtype);
     const size_t sb = la_state_bytes(p);
     if (pl.BH > 0 && !state) return LA_ERR_NULL;
     if (ws_bytes < pl.ws_bytes) return LA_ERR_WORKSPACE;
-    st = check_buffers({{q, tb}, {k, tb}, {v, tb}, {dout, tb}, {state, sb}},
-                       {{dq, tb}, {dk, tb}, {dv, tb}, {ws, pl.ws_bytes}}, {16, 16, 16, 16, 16},
+    st = check_buffers({{q, tk}, {k, tk}, {v, tv}, {dout, tv}, {state, sb}},
+                       {{dq, tk}, {dk, tk}, {dv, tv}, {ws, pl.ws_bytes}}, {16, 16, 16, 16, 16},
                        {16, 16, 16, 256});
     if (st != LA_OK) return st;
-    if (tb == 0) return LA_OK;
+    if (tk == 0) return LA_OK;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    st = device_status(la::launch_bwd_dq(pl, q, dout, static_cast<const float*>(state), dq, ws, s));
+    st = device_status(kernel_set(pl.dtype, pl.DK)->bwd_dq(pl, q, dout, static_cast<const float*>(state), dq, ws, s));
     if (st != LA_OK) return st;
-    return device_status(la::launch_bwd_dkv(pl, k, v, dk, dv, ws, s));
+    return device_status(kernel_set(pl.dtype, pl.DK)->bwd_dkv(pl, k, v, dk, dv, ws, s));
 }
 
 }  // extern "C"

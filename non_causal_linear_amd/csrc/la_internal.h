@@ -8,7 +8,10 @@
 namespace la {
 
 // Where the rows of head bh = b H + h live, in elements: the head's row 0 at
-// (bh / H) sb + (bh % H) sh, consecutive rows rs apart.
+// (bh / H) sb + (bh % H) sh, consecutive rows rs apart. Given for the Q-side
+// tensors (Q, K, dQ, dK: rows of DK elements); the V-side tensors (V, O, dO,
+// dV) have the same layout with rows of DV elements, every stride scaled by
+// DV / DK.
 //   [B, H, T, D]: sb = H T D, sh = T D, rs = D
 //   [B, T, H, D]: sb = T H D, sh = D,   rs = H D
 struct Layout {
@@ -16,11 +19,11 @@ struct Layout {
 };
 
 // Work split for one problem. Every field is a pure function of
-// (B*H, T, D, dtype), so the summation order, and with it every output bit,
-// depends only on the shape.
+// (B*H, T, DK, DV, dtype), so the summation order, and with it every output
+// bit, depends only on the shape.
 struct Plan {
     int64_t BH = 0, T = 0;
-    int D = 0, dtype = 0;
+    int DK = 0, DV = 0, dtype = 0;
     bool simple = false;
     float eps = 0.f;
     int fm = 0;  // feature map: 0 elu + 1, 1 relu, 2 identity
@@ -50,15 +53,27 @@ struct SplitCfg {
     int64_t target_wgs;
 };
 enum Step { kStepState = 0, kStepOutput = 1, kStepBwdQ = 2, kStepBwdKV = 3 };
-SplitCfg split_config(int step, int dtype, int D);
 
-hipError_t launch_fwd_state(const Plan& p, const void* k, const void* v, float* state,
-                            void* ws, hipStream_t s);
-hipError_t launch_fwd_output(const Plan& p, const void* q, const float* state, void* o,
-                             hipStream_t s);
-hipError_t launch_bwd_dq(const Plan& p, const void* q, const void* dout, const float* state,
-                         void* dq, void* ws, hipStream_t s);
-hipError_t launch_bwd_dkv(const Plan& p, const void* k, const void* v, void* dk, void* dv,
-                          void* ws, hipStream_t s);
+// The launchers of one compilation unit of la_kernels.hip: one element type
+// and one DK, every DV (dispatched on Plan::DV). split_config gives the
+// token split each step's kernel wants for that DV.
+struct KernelSet {
+    hipError_t (*fwd_state)(const Plan& p, const void* k, const void* v, float* state, void* ws,
+                            hipStream_t s);
+    hipError_t (*fwd_output)(const Plan& p, const void* q, const float* state, void* o, hipStream_t s);
+    hipError_t (*bwd_dq)(const Plan& p, const void* q, const void* dout, const float* state, void* dq,
+                         void* ws, hipStream_t s);
+    hipError_t (*bwd_dkv)(const Plan& p, const void* k, const void* v, void* dk, void* dv, void* ws,
+                          hipStream_t s);
+    SplitCfg (*split_config)(int step, int DV);
+};
+
+// One unit per (la_dtype, DK): kernel_set_<dtype>_<DK>().
+#define LA_KERNEL_UNITS(X) \
+    X(0, 32) X(0, 64) X(0, 96) X(0, 128) X(1, 32) X(1, 64) X(1, 96) X(1, 128) \
+    X(2, 32) X(2, 64) X(2, 96) X(2, 128)
+#define LA_DECLARE_UNIT(dt, dk) const KernelSet* kernel_set_##dt##_##dk();
+LA_KERNEL_UNITS(LA_DECLARE_UNIT)
+#undef LA_DECLARE_UNIT
 
 }  // namespace la

@@ -197,6 +197,23 @@ __device__ __forceinline__ int64_t head_offset(const Layout& L, int64_t bh) {
     return b * L.sb + (bh - b * L.H) * L.sh;
 }
 
+// The layout of the V-side tensors (V, O, dO, dV: rows of DV elements) from
+// that of the Q-side ones (rows of DK elements): every stride is a multiple
+// of the row size, so the rescaling is exact, and the identity when DK = DV.
+template <int DK, int DV>
+__device__ __forceinline__ Layout v_layout(const Layout& L) {
+    if constexpr (DK == DV) {
+        return L;
+    } else {
+        Layout r;
+        r.H = L.H;
+        r.sb = L.sb / DK * DV;
+        r.sh = L.sh / DK * DV;
+        r.rs = L.rs / DK * DV;
+        return r;
+    }
+}
+
 template <typename T>
 __device__ __forceinline__ HeadBuf slice_buf(const T* base, const Layout& L, int64_t bh, int D, int64_t r0,
                                              int64_t r1) {
@@ -268,17 +285,18 @@ __device__ __forceinline__ void store_tile_rows(T* stage, const Row<T, D / 4>& v
                                                 int64_t row0, int64_t rs) {
     constexpr int F = D / 4, EPC = 16 / (int)sizeof(T), LDR = D + EPC;
     constexpr int CPR = D / EPC;       // 16-byte chunks per row
-    constexpr int RPI = 64 / CPR;      // rows per store instruction
+    constexpr int NC = 16 * CPR / 64;  // chunks per lane (rows of CPR chunks, 16 rows)
     const int lane = threadIdx.x & 63, m = lane & 15, g = lane >> 4;
 #pragma unroll
     for (int i = 0; i < F / EPC; ++i)
         *reinterpret_cast<uint4*>(&stage[m * LDR + F * g + EPC * i]) = reinterpret_cast<const uint4*>(vals.e)[i];
     wave_lds_sync();
-    const int r = lane / CPR, c = lane % CPR;
+    // chunk n = 64 k + lane of the tile: row n / CPR, chunk n % CPR of that row
 #pragma unroll
-    for (int k = 0; k < 16 / RPI; ++k) {
-        const uint4 x = *reinterpret_cast<const uint4*>(&stage[(k * RPI + r) * LDR + EPC * c]);
-        buf_store16(b, buf_off<T>(row0 + k * RPI + r, rs, EPC * c), x);
+    for (int k = 0; k < NC; ++k) {
+        const int n = 64 * k + lane, r = n / CPR, c = n % CPR;
+        const uint4 x = *reinterpret_cast<const uint4*>(&stage[r * LDR + EPC * c]);
+        buf_store16(b, buf_off<T>(row0 + r, rs, EPC * c), x);
     }
     wave_lds_sync();
 }
@@ -380,16 +398,16 @@ __device__ __forceinline__ int scale_exp(float maxabs) {
 }
 
 // Fixed-order sum of the P partial (S, z) blocks of every head: one thread per
-// 4 consecutive floats of a head's D*D + D block, slices added in ascending
+// 4 consecutive floats of a head's DK*DV + DK block, slices added in ascending
 // order, eight 16-byte loads in flight per batch. A kernel of its own: the
 // launch boundary makes every partial visible, which costs far less here than
 // device-scope fences inside the producing kernel (each of those writes back
 // and invalidates the XCD's L2).
-template <int D>
+template <int DK, int DV>
 __global__ __launch_bounds__(kThreads) void combine_kernel(const float* __restrict__ part, int P,
                                                            float* __restrict__ outS,
                                                            float* __restrict__ outz, int64_t BH) {
-    constexpr int E4 = (D * D + D) / 4;
+    constexpr int E4 = (DK * DV + DK) / 4;
     constexpr int BPH = (E4 + kThreads - 1) / kThreads;  // blocks per head
     const int64_t bh = blockIdx.x / BPH;
     const int i = (blockIdx.x % BPH) * kThreads + threadIdx.x;
@@ -410,17 +428,18 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const float* __restri
             }
     }
     const int idx = 4 * i;
-    if (idx < D * D)
-        *reinterpret_cast<float4*>(outS + bh * D * D + idx) = acc;
+    if (idx < DK * DV)
+        *reinterpret_cast<float4*>(outS + bh * DK * DV + idx) = acc;
     else
-        *reinterpret_cast<float4*>(outz + bh * D + (idx - D * D)) = acc;
+        *reinterpret_cast<float4*>(outz + bh * DK + (idx - DK * DV)) = acc;
 }
 
-// Largest |x| over the D x D matrix at M, over an NT-thread workgroup: every
-// thread issues its 16-byte loads at once (D*D/4 is a multiple of NT).
-template <int D, int NT = kThreads>
+// Largest |x| over the NE floats at M, over an NT-thread workgroup: every
+// thread issues its 16-byte loads at once (NE/4 is a multiple of NT).
+template <int NE, int NT = kThreads>
 __device__ __forceinline__ float block_absmax_matrix(const float* __restrict__ M, float* red) {
-    constexpr int PER = D * D / 4 / NT;
+    constexpr int PER = NE / 4 / NT;
+    static_assert(PER * 4 * NT == NE, "thread count must tile the matrix");
     float4 v[PER];
 #pragma unroll
     for (int i = 0; i < PER; ++i) v[i] = reinterpret_cast<const float4*>(M)[threadIdx.x + i * NT];
@@ -441,36 +460,36 @@ __device__ __forceinline__ void block_vector_stats(const float* __restrict__ z, 
     sum = block_sum<NT / 64>((v.x + v.y) + (v.z + v.w), red);
 }
 
-// A D x D fp32 matrix and a D-vector staged in LDS, with their statistics.
-// The matrix rows are D + 1 floats apart, so that the fragment builders'
+// A DK x DV fp32 matrix and a DK-vector staged in LDS, with their statistics.
+// The matrix rows are DV + 1 floats apart, so that the fragment builders'
 // column walks (lanes 16 rows or 16 columns apart) spread over the banks.
-template <int D>
+template <int DK, int DV>
 struct StagedState {
-    static constexpr int kLD = D + 1;
-    static constexpr int kFloats = D * kLD + D;  // matrix, then the vector
+    static constexpr int kLD = DV + 1;
+    static constexpr int kFloats = DK * kLD + DK;  // matrix, then the vector
     float max_m, max_z, sum_z;
 };
 
-// Copies M and z from global memory into s (StagedState<D>::kFloats floats)
+// Copies M and z from global memory into s (StagedState<DK, DV>::kFloats floats)
 // with all of each thread's 16-byte loads in flight at once, and reduces
 // max |M|, max |z| and sum z over the NT-thread workgroup in a fixed order
 // (xor tree per wave, then a pairwise tree over the waves). Ends with a
 // barrier; red holds 3 NT / 64 floats.
-template <int D, int NT = kThreads>
-__device__ __forceinline__ StagedState<D> stage_state(const float* __restrict__ M,
-                                                      const float* __restrict__ z, float* s, float* red) {
-    constexpr int PER = D * D / 4 / NT, LD = StagedState<D>::kLD, NW = NT / 64;
-    static_assert(PER * 4 * NT == D * D && D / 4 <= NT, "thread count must tile the matrix");
+template <int DK, int DV, int NT = kThreads>
+__device__ __forceinline__ StagedState<DK, DV> stage_state(const float* __restrict__ M,
+                                                           const float* __restrict__ z, float* s, float* red) {
+    constexpr int PER = DK * DV / 4 / NT, LD = StagedState<DK, DV>::kLD, NW = NT / 64;
+    static_assert(PER * 4 * NT == DK * DV && DK / 4 <= NT, "thread count must tile the matrix");
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     float4 v[PER];
 #pragma unroll
     for (int i = 0; i < PER; ++i) v[i] = reinterpret_cast<const float4*>(M)[tid + i * NT];
     float4 w = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (tid < D / 4) w = reinterpret_cast<const float4*>(z)[tid];
+    if (tid < DK / 4) w = reinterpret_cast<const float4*>(z)[tid];
     float a = 0.f;
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-        const int e = 4 * (tid + i * NT), r = e / D, c = e % D;
+        const int e = 4 * (tid + i * NT), r = e / DV, c = e % DV;
         float* d = s + r * LD + c;
         d[0] = v[i].x;
         d[1] = v[i].y;
@@ -478,7 +497,7 @@ __device__ __forceinline__ StagedState<D> stage_state(const float* __restrict__ 
         d[3] = v[i].w;
         a = fmaxf(a, fmaxf(fmaxf(fabsf(v[i].x), fabsf(v[i].y)), fmaxf(fabsf(v[i].z), fabsf(v[i].w))));
     }
-    if (tid < D / 4) *reinterpret_cast<float4*>(s + D * LD + 4 * tid) = w;
+    if (tid < DK / 4) *reinterpret_cast<float4*>(s + DK * LD + 4 * tid) = w;
     float b = fmaxf(fmaxf(fabsf(w.x), fabsf(w.y)), fmaxf(fabsf(w.z), fabsf(w.w)));
     float c = (w.x + w.y) + (w.z + w.w);
 #pragma unroll
@@ -508,7 +527,7 @@ __device__ __forceinline__ StagedState<D> stage_state(const float* __restrict__ 
             xb[w] = fmaxf(xb[2 * w], xb[2 * w + 1]);
             xc[w] = xc[2 * w] + xc[2 * w + 1];
         }
-    StagedState<D> st;
+    StagedState<DK, DV> st;
     st.max_m = xa[0];
     st.max_z = xb[0];
     st.sum_z = xc[0];
@@ -518,67 +537,73 @@ __device__ __forceinline__ StagedState<D> stage_state(const float* __restrict__ 
 // ---------------------------------------------------------------------------
 // Steps 1-3: split-T state reduction.
 // ---------------------------------------------------------------------------
-template <typename T, int D>
+template <typename T, int DK, int DV>
 struct StateShape {
     static constexpr int kEPC = 16 / (int)sizeof(T);  // elements per 16-byte chunk
-    static constexpr int kCPR = D / kEPC;             // chunks per row
-    static constexpr int kNG = kThreads / kCPR;       // row groups per load pass
-    static constexpr int kR = 4;                      // rows per thread per tile
-    static constexpr int kTT = kNG * kR;              // tokens per tile
+    static constexpr int kTT = 64;                    // tokens per tile
     static constexpr int kLDT = kTT + kEPC;           // LDS row stride (elements), +16 B pad
-    static constexpr int kNB = D / 16;                // 16-wide blocks along D
-    static constexpr int kNI = kNB / kWaves;          // i-blocks of S per wave
+    static constexpr int kCK = DK / kEPC;             // chunks per K row
+    static constexpr int kCV = DV / kEPC;             // chunks per V row
+    static constexpr int kNK = kTT * kCK / kThreads;  // K chunks per thread per tile
+    static constexpr int kNV = kTT * kCV / kThreads;  // V chunks per thread per tile
+    static constexpr int kNI = DK / 32;               // 16-row blocks of S per wave
+    static constexpr int kNJ = DV / 32;               // 16-column blocks of S per wave
     static constexpr int kKS = kTT / 32;              // 32-token MFMA steps per tile
+    static_assert(kNK * kThreads == kTT * kCK && kNV * kThreads == kTT * kCV, "tile must split evenly");
 };
 
 // One workgroup reduces tokens [p L, min((p+1) L, T)) of head bh into partial
-// (S, z). The tile is loaded row-major with 16-byte loads (8 consecutive rows
-// per wave instruction), phi is applied to K in fp32 and rounded to the
-// operand type, and both tiles are written to LDS transposed ([feature][token])
-// so that MFMA fragments, which want 8 consecutive tokens per lane, are single
-// 16-byte LDS reads. Token order inside a tile is permuted (thread g's rows
-// g, g + NG, ... land in columns 4g, 4g + 1, ...) identically for K and V,
-// which a sum over tokens does not see. z comes from the same MFMA with an
-// all-ones B block, so it sums exactly the rounded phi(k) that S uses.
-template <typename T, int D, int FM>
+// (S, z), S = phi(K)^T V (DK x DV). Per 64-token tile the threads load the
+// tile's 16-byte chunks in order (chunk n: row n / chunks-per-row), apply phi
+// to K in fp32 and round it to the operand type, and write both tiles to LDS
+// transposed ([feature][token]), so that MFMA fragments, which want 8
+// consecutive tokens per lane, are single 16-byte LDS reads. The four waves
+// split S two by two: wave w owns the row blocks of half (w % 2) and the
+// column blocks of half (w / 2). z is summed in fp32 from the same rounded
+// phi(k) values in LDS that the MFMA reads, one feature per thread, tokens in
+// order. Rows past the slice end load a clamped row and are written as zeros.
+template <typename T, int DK, int DV, int FM>
 __global__ __launch_bounds__(kThreads) void fwd_state_kernel(
     const T* __restrict__ k, const T* __restrict__ v, float* __restrict__ stS,
-    float* __restrict__ stz, float* __restrict__ part, int64_t T_, const Layout lay, int P,
-    int64_t L) {
-    using Sh = StateShape<T, D>;
-    constexpr int EPC = Sh::kEPC, CPR = Sh::kCPR, NG = Sh::kNG, R = Sh::kR, TT = Sh::kTT,
-                  LDT = Sh::kLDT, NB = Sh::kNB, NI = Sh::kNI, KS = Sh::kKS;
-    typedef T tR __attribute__((ext_vector_type(R)));
-    __shared__ __attribute__((aligned(16))) T sK[D * LDT];
-    __shared__ __attribute__((aligned(16))) T sV[D * LDT];
+    float* __restrict__ stz, float* __restrict__ part, int64_t T_, const Layout lay, int P, int64_t L) {
+    using Sh = StateShape<T, DK, DV>;
+    const Layout lk = lay, lv = v_layout<DK, DV>(lay);
+    constexpr int EPC = Sh::kEPC, TT = Sh::kTT, LDT = Sh::kLDT, CK = Sh::kCK, CV = Sh::kCV, NK = Sh::kNK,
+                  NV = Sh::kNV, NI = Sh::kNI, NJ = Sh::kNJ, KS = Sh::kKS;
+    __shared__ __attribute__((aligned(16))) T sK[DK * LDT];
+    __shared__ __attribute__((aligned(16))) T sV[DV * LDT];
 
     const int wid = xcd_remap(blockIdx.x, gridDim.x);
     const int64_t bh = wid / P;
     const int p = wid % P;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int m = lane & 15, grp = lane >> 4;
-    const int c = tid % CPR, g = tid / CPR;
+    const int wi = wave & 1, wj = wave >> 1;
     const int64_t t0 = (int64_t)p * L;
     const int64_t t1 = min(t0 + L, T_);
-    const T* kb = k + head_offset(lay, bh) + c * EPC;
-    const T* vb = v + head_offset(lay, bh) + c * EPC;
+    const T* kb = k + head_offset(lk, bh);
+    const T* vb = v + head_offset(lv, bh);
 
-    f32x4 acc[NI][NB + 1];
+    f32x4 acc[NI][NJ];
 #pragma unroll
     for (int ii = 0; ii < NI; ++ii)
 #pragma unroll
-        for (int jb = 0; jb <= NB; ++jb) acc[ii][jb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    Frag<T> ones;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) ones[e] = static_cast<T>(1.f);
+        for (int jj = 0; jj < NJ; ++jj) acc[ii][jj] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float zacc = 0.f;
 
-    uint4 rk[R], rv[R];
+    uint4 rk[NK], rv[NV];
     auto load_tile = [&](int64_t ts) {
 #pragma unroll
-        for (int rr = 0; rr < R; ++rr) {
-            const int64_t t = min(ts + g + NG * rr, t1 - 1);  // masked when written to LDS
-            rk[rr] = *reinterpret_cast<const uint4*>(kb + t * lay.rs);
-            rv[rr] = *reinterpret_cast<const uint4*>(vb + t * lay.rs);
+        for (int i = 0; i < NK; ++i) {
+            const int n = tid + kThreads * i, r = n / CK, c = n % CK;
+            const int64_t t = min(ts + r, t1 - 1);  // masked when written to LDS
+            rk[i] = *reinterpret_cast<const uint4*>(kb + t * lk.rs + c * EPC);
+        }
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            const int n = tid + kThreads * i, r = n / CV, c = n % CV;
+            const int64_t t = min(ts + r, t1 - 1);
+            rv[i] = *reinterpret_cast<const uint4*>(vb + t * lv.rs + c * EPC);
         }
     };
 
@@ -587,25 +612,23 @@ __global__ __launch_bounds__(kThreads) void fwd_state_kernel(
     for (int64_t it = 0; it < ntile; ++it) {
         const int64_t ts = t0 + it * TT;
         __syncthreads();  // every wave is done reading the previous tile
-        {
-            tR kt[EPC], vt[EPC];
 #pragma unroll
-            for (int rr = 0; rr < R; ++rr) {
-                const bool ok = ts + g + NG * rr < t1;
-                const T* ke = reinterpret_cast<const T*>(&rk[rr]);
-                const T* ve = reinterpret_cast<const T*>(&rv[rr]);
+        for (int i = 0; i < NK; ++i) {
+            const int n = tid + kThreads * i, r = n / CK, c = n % CK;
+            const bool ok = ts + r < t1;
+            const T* ke = reinterpret_cast<const T*>(&rk[i]);
 #pragma unroll
-                for (int e = 0; e < EPC; ++e) {
-                    // padded rows must add nothing: phi(0) = 1, so mask after phi
-                    kt[e][rr] = ok ? static_cast<T>(phi<FM, T>(to_f32(ke[e]))) : static_cast<T>(0.f);
-                    vt[e][rr] = ok ? ve[e] : static_cast<T>(0.f);
-                }
-            }
+            for (int e = 0; e < EPC; ++e)
+                // padded rows must add nothing: phi(0) = 1, so mask after phi
+                sK[(c * EPC + e) * LDT + r] = ok ? static_cast<T>(phi<FM, T>(to_f32(ke[e]))) : static_cast<T>(0.f);
+        }
 #pragma unroll
-            for (int e = 0; e < EPC; ++e) {
-                *reinterpret_cast<tR*>(&sK[(c * EPC + e) * LDT + R * g]) = kt[e];
-                *reinterpret_cast<tR*>(&sV[(c * EPC + e) * LDT + R * g]) = vt[e];
-            }
+        for (int i = 0; i < NV; ++i) {
+            const int n = tid + kThreads * i, r = n / CV, c = n % CV;
+            const bool ok = ts + r < t1;
+            const T* ve = reinterpret_cast<const T*>(&rv[i]);
+#pragma unroll
+            for (int e = 0; e < EPC; ++e) sV[(c * EPC + e) * LDT + r] = ok ? ve[e] : static_cast<T>(0.f);
         }
         __syncthreads();
         if (it + 1 < ntile) load_tile(ts + TT);  // in flight during the MFMA below
@@ -615,38 +638,44 @@ __global__ __launch_bounds__(kThreads) void fwd_state_kernel(
             Frag<T> a[NI];
 #pragma unroll
             for (int ii = 0; ii < NI; ++ii)
-                a[ii] = *reinterpret_cast<const Frag<T>*>(&sK[((wave * NI + ii) * 16 + m) * LDT + col]);
+                a[ii] = *reinterpret_cast<const Frag<T>*>(&sK[((wi * NI + ii) * 16 + m) * LDT + col]);
 #pragma unroll
-            for (int jb = 0; jb < NB; ++jb) {
-                const Frag<T> b = *reinterpret_cast<const Frag<T>*>(&sV[(jb * 16 + m) * LDT + col]);
+            for (int jj = 0; jj < NJ; ++jj) {
+                const Frag<T> b = *reinterpret_cast<const Frag<T>*>(&sV[((wj * NJ + jj) * 16 + m) * LDT + col]);
 #pragma unroll
-                for (int ii = 0; ii < NI; ++ii) acc[ii][jb] = mma(a[ii], b, acc[ii][jb]);
+                for (int ii = 0; ii < NI; ++ii) acc[ii][jj] = mma(a[ii], b, acc[ii][jj]);
             }
+        }
+        if (tid < DK) {
+            const T* row = &sK[tid * LDT];
 #pragma unroll
-            for (int ii = 0; ii < NI; ++ii) acc[ii][NB] = mma(a[ii], ones, acc[ii][NB]);
+            for (int c = 0; c < TT / EPC; ++c) {
+                const uint4 x = *reinterpret_cast<const uint4*>(row + c * EPC);
+                const T* xe = reinterpret_cast<const T*>(&x);
+#pragma unroll
+                for (int e = 0; e < EPC; ++e) zacc += to_f32(xe[e]);
+            }
         }
     }
 
     float* oS;
     float* oz;
     if (P == 1) {
-        oS = stS + bh * D * D;
-        oz = stz + bh * D;
+        oS = stS + bh * DK * DV;
+        oz = stz + bh * DK;
     } else {
-        oS = part + (bh * P + p) * (int64_t)(D * D + D);
-        oz = oS + D * D;
+        oS = part + (bh * P + p) * (int64_t)(DK * DV + DK);
+        oz = oS + DK * DV;
     }
 #pragma unroll
     for (int ii = 0; ii < NI; ++ii) {
-        const int i0 = (wave * NI + ii) * 16 + 4 * grp;
+        const int i0 = (wi * NI + ii) * 16 + 4 * grp;
 #pragma unroll
-        for (int jb = 0; jb < NB; ++jb)
+        for (int jj = 0; jj < NJ; ++jj)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) oS[(i0 + r) * D + jb * 16 + m] = acc[ii][jb][r];
-        if (m == 0)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) oz[i0 + r] = acc[ii][NB][r];
+            for (int r = 0; r < 4; ++r) oS[(i0 + r) * DV + (wj * NJ + jj) * 16 + m] = acc[ii][jj][r];
     }
+    if (tid < DK) oz[tid] = zacc;
 }
 
 // Steps 1-3 for 16-bit inputs at D = 64: every wave streams its own 32-token
@@ -980,34 +1009,42 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_state_c128_kernel(
 // ---------------------------------------------------------------------------
 // Shared shape of the streaming kernels (output, bwd Q side, bwd K/V side).
 // ---------------------------------------------------------------------------
-template <typename T, int D>
+template <typename T, int DK, int DV>
 struct StreamShape {
-    static constexpr int kF = D / 4;     // features per lane (one quarter row)
-    static constexpr int kNB = D / 16;   // 16-row output blocks
-    static constexpr int kKS = D / 32;   // 32-long contraction steps over D
-    static constexpr int kU = (sizeof(T) == 2 && D == 64) ? 2 : 1;  // 16-token blocks per wave
-    // 16-bit D = 128: eight waves share one copy of the (larger) fragments
-    static constexpr int kWaves = (sizeof(T) == 2 && D == 128) ? 8 : ::la::kWaves;
+    static constexpr int kFK = DK / 4;    // Q/K-side features per lane (one quarter row)
+    static constexpr int kFV = DV / 4;    // V/O-side features per lane
+    static constexpr int kNBK = DK / 16;  // 16-row blocks over DK
+    static constexpr int kNBV = DV / 16;  // 16-row blocks over DV
+    static constexpr int kKSK = DK / 32;  // 32-long contraction steps over DK
+    static constexpr int kKSV = DV / 32;  // 32-long contraction steps over DV
+    static constexpr bool kSmall = sizeof(T) == 2 && DK <= 64 && DV <= 64;
+    static constexpr int kU = kSmall ? 2 : 1;  // 16-token blocks per wave
+    // 16-bit DK = DV = 128: eight waves share one copy of the (larger) fragments
+    static constexpr int kWaves = (sizeof(T) == 2 && DK == 128 && DV == 128) ? 8 : ::la::kWaves;
     static constexpr int kThreads = 64 * kWaves;
     static constexpr int kG = kWaves * kU * 16;  // tokens per workgroup iteration
     static constexpr int kStages = 2;            // blocks of loads in flight per wave
-    // workgroups per CU the register budget is set for: 16-bit D = 64, four
-    // (128 registers per lane); 16-bit D = 128, two for the output kernel
-    // (128 registers) and one for the K/V kernel (256)
-    static constexpr int kOutMinBlocks = (sizeof(T) == 2) ? (D == 64 ? 4 : 2) : 1;
-    static constexpr int kKvMinBlocks = (sizeof(T) == 2 && D == 64) ? 4 : 1;
+    // workgroups per CU the register budget is set for: 16-bit heads up to 64,
+    // four (128 registers per lane); wider 16-bit heads, two for the output
+    // kernel (128 registers) and one for the K/V kernel (256)
+    static constexpr int kOutMinBlocks = (sizeof(T) == 2) ? (kSmall ? 4 : 2) : 1;
+    static constexpr int kKvMinBlocks = kSmall ? 4 : 1;
+    // The state is staged in LDS for the fragment builds except at
+    // DK = DV = 128, where the staging area would halve the occupancy.
+    static constexpr bool kStaged = !(DK == 128 && DV == 128);
 };
 
-// Fragment of A = M^T-like operand built from an fp32 D x D matrix M:
-//   rows m of the 16-row block b stand for index F*(m/4) + 4b + m%4,
-//   the lane group's 8 contraction values stand for F*g + 8s + e.
+// Fragment of an A operand built from an fp32 matrix M (rows LD floats apart)
+// whose A rows run over DR indices and whose contraction runs over DC:
+//   rows m of the 16-row block b stand for index (DR/4)*(m/4) + 4b + m%4,
+//   the lane group's 8 contraction values stand for (DC/4)*g + 8s + e.
 // If kTransposeSource, element = M[contraction][row] else M[row][contraction].
-template <typename T, int D, bool kTransposeSource, int LD = D>
+template <typename T, int DR, int DC, bool kTransposeSource, int LD>
 __device__ __forceinline__ Frag<T> build_frag(const float* __restrict__ M, int b, int s, int m, int g,
                                               float scale) {
-    constexpr int F = D / 4;
-    const int row = F * (m >> 2) + 4 * b + (m & 3);
-    const int k0 = F * g + 8 * s;
+    constexpr int FR = DR / 4, FC = DC / 4;
+    const int row = FR * (m >> 2) + 4 * b + (m & 3);
+    const int k0 = FC * g + 8 * s;
     Frag<T> f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -1017,10 +1054,11 @@ __device__ __forceinline__ Frag<T> build_frag(const float* __restrict__ M, int b
     return f;
 }
 
-// Fragment whose every row is the vector z: z[F*g + 8s + e].
-template <typename T, int D>
+// Fragment whose every row is the vector z: z[(DC/4)*g + 8s + e] (the
+// contraction runs over DC).
+template <typename T, int DC>
 __device__ __forceinline__ Frag<T> build_zfrag(const float* __restrict__ z, int s, int g, float scale) {
-    constexpr int F = D / 4;
+    constexpr int F = DC / 4;
     Frag<T> f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) f[e] = static_cast<T>(z[F * g + 8 * s + e] * scale);
@@ -1046,24 +1084,26 @@ __device__ __forceinline__ void build_frags(Frag<T>* sA, Make make) {
 // Step 4: output.
 // ---------------------------------------------------------------------------
 // One workgroup streams tokens [ch LQ, min((ch+1) LQ, T)) of head bh. Per
-// 16-token block a lane loads a quarter row of Q (D/4 features), applies phi,
+// 16-token block a lane loads a quarter row of Q (DK/4 features), applies phi,
 // and the wave computes O^T = S^T phi(Q)^T (rows permuted so each lane ends
-// with D/4 contiguous outputs of its token) and den = z . phi(q) from one more
+// with DV/4 contiguous outputs of its token) and den = z . phi(q) from one more
 // MFMA block whose rows are all z.
-template <typename T, int D, bool SIMPLE, int FM>
-__global__ __launch_bounds__((StreamShape<T, D>::kThreads), (StreamShape<T, D>::kOutMinBlocks)) void fwd_output_kernel(
+template <typename T, int DK, int DV, bool SIMPLE, int FM>
+__global__ __launch_bounds__((StreamShape<T, DK, DV>::kThreads), (StreamShape<T, DK, DV>::kOutMinBlocks)) void fwd_output_kernel(
     const T* __restrict__ q, const float* __restrict__ stS, const float* __restrict__ stz,
     T* __restrict__ o, int64_t T_, const Layout lay, int NQ, int64_t LQ, float eps) {
-    using Sh = StreamShape<T, D>;
-    constexpr int F = Sh::kF, NB = Sh::kNB, KS = Sh::kKS, U = Sh::kU, NW = Sh::kWaves, NT = Sh::kThreads;
+    using Sh = StreamShape<T, DK, DV>;
+    const Layout lk = lay, lv = v_layout<DK, DV>(lay);
+    constexpr int FK = Sh::kFK, FV = Sh::kFV, NB = Sh::kNBV, KS = Sh::kKSK, U = Sh::kU, NW = Sh::kWaves,
+                  NT = Sh::kThreads;
     constexpr int NFS = NB * KS;             // S fragments
     constexpr int NFR = NFS + (SIMPLE ? 0 : KS);  // + z fragments
-    constexpr int LDR = D + 16 / (int)sizeof(T);
-    // At D = 64 the state is staged in LDS (sharing the store staging area,
-    // which the loop alone uses) and the fragments are built from there.
-    constexpr bool kStaged = (D == 64);
+    constexpr int LDR = DV + 16 / (int)sizeof(T);
+    // The state is staged in LDS (sharing the store staging area, which the
+    // loop alone uses) and the fragments are built from there.
+    constexpr bool kStaged = Sh::kStaged;
     constexpr int kStoreBytes = NW * 16 * LDR * (int)sizeof(T);
-    constexpr int kStBytes = kStaged ? StagedState<D>::kFloats * 4 : 0;
+    constexpr int kStBytes = kStaged ? StagedState<DK, DV>::kFloats * 4 : 0;
     __shared__ Frag<T> sA[NFR * 64];
     __shared__ __attribute__((aligned(16))) unsigned char sraw[kStoreBytes > kStBytes ? kStoreBytes : kStBytes];
     __shared__ float red[3 * NW];
@@ -1076,34 +1116,34 @@ __global__ __launch_bounds__((StreamShape<T, D>::kThreads), (StreamShape<T, D>::
     const int64_t c1 = min(c0 + LQ, T_);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int m = lane & 15, grp = lane >> 4;
-    const float* S = stS + bh * D * D;
-    const float* z = stz + bh * D;
+    const float* S = stS + bh * DK * DV;
+    const float* z = stz + bh * DK;
 
     int sS = 0, sz = 0;
     if constexpr (kStaged) {
-        constexpr int LD = StagedState<D>::kLD;
+        constexpr int LD = StagedState<DK, DV>::kLD;
         float* sSt = reinterpret_cast<float*>(sraw);
-        const StagedState<D> st = stage_state<D, NT>(S, z, sSt, red);
+        const StagedState<DK, DV> st = stage_state<DK, DV, NT>(S, z, sSt, red);
         if constexpr (Elt<T>::kScaled) {
             sS = scale_exp(st.max_m);
             sz = scale_exp(st.max_z);
         }
         const float fS = ldexpf(1.f, sS), fz = ldexpf(1.f, sz);
         build_frags<T, NFR, NW>(sA, [&](int f) {
-            return f < NFS ? build_frag<T, D, true, LD>(sSt, f / KS, f % KS, m, grp, fS)
-                           : build_zfrag<T, D>(sSt + D * LD, max(f - NFS, 0), grp, fz);
+            return f < NFS ? build_frag<T, DV, DK, true, LD>(sSt, f / KS, f % KS, m, grp, fS)
+                           : build_zfrag<T, DK>(sSt + DK * LD, max(f - NFS, 0), grp, fz);
         });
     } else {
         if constexpr (Elt<T>::kScaled) {
             float mz, zsum;
-            sS = scale_exp(block_absmax_matrix<D, NT>(S, red));
-            block_vector_stats<D, NT>(z, red, mz, zsum);
+            sS = scale_exp(block_absmax_matrix<DK * DV, NT>(S, red));
+            block_vector_stats<DK, NT>(z, red, mz, zsum);
             sz = scale_exp(mz);
         }
         const float fS = ldexpf(1.f, sS), fz = ldexpf(1.f, sz);
         build_frags<T, NFR, NW>(sA, [&](int f) {
-            return f < NFS ? build_frag<T, D, true>(S, f / KS, f % KS, m, grp, fS)
-                           : build_zfrag<T, D>(z, max(f - NFS, 0), grp, fz);
+            return f < NFS ? build_frag<T, DV, DK, true, DV>(S, f / KS, f % KS, m, grp, fS)
+                           : build_zfrag<T, DK>(z, max(f - NFS, 0), grp, fz);
         });
     }
     __syncthreads();
@@ -1114,16 +1154,16 @@ __global__ __launch_bounds__((StreamShape<T, D>::kThreads), (StreamShape<T, D>::
     // in rotated order, two per turn with no early exit; rows are counted from
     // c0, rows past the chunk end load as zeros and their stores are dropped.
     constexpr int BT = 16 * U;
-    const HeadBuf bq = slice_buf(q, lay, bh, D, c0, c1), bo = slice_buf(o, lay, bh, D, c0, c1);
+    const HeadBuf bq = slice_buf(q, lk, bh, DK, c0, c1), bo = slice_buf(o, lv, bh, DV, c0, c1);
     constexpr int NS = Sh::kStages;
     const Rotation rot((int)((c1 - c0 + BT - 1) / BT), NS * NW, wid);
     T* stg = stage + wave * 16 * LDR;
-    auto issue = [&](Row<T, F> (&b)[U], int blk) {
+    auto issue = [&](Row<T, FK> (&b)[U], int blk) {
         const int64_t bs = (int64_t)rot(blk) * BT;
 #pragma unroll
-        for (int u = 0; u < U; ++u) load_row_buf<T, F>(b[u], bq, bs + 16 * u + m, lay.rs, F * grp);
+        for (int u = 0; u < U; ++u) load_row_buf<T, FK>(b[u], bq, bs + 16 * u + m, lk.rs, FK * grp);
     };
-    auto body = [&](Row<T, F> (&qr)[U], int blk) {
+    auto body = [&](Row<T, FK> (&qr)[U], int blk) {
         Frag<T> bq[U][KS];
 #pragma unroll
         for (int u = 0; u < U; ++u)
@@ -1160,7 +1200,7 @@ __global__ __launch_bounds__((StreamShape<T, D>::kThreads), (StreamShape<T, D>::
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            Row<T, F> out;
+            Row<T, FV> out;
             if constexpr (SIMPLE) {
 #pragma unroll
                 for (int b = 0; b < NB; ++b)
@@ -1174,10 +1214,10 @@ __global__ __launch_bounds__((StreamShape<T, D>::kThreads), (StreamShape<T, D>::
 #pragma unroll
                     for (int r = 0; r < 4; ++r) out.e[4 * b + r] = static_cast<T>(acc[u][b][r] * inv);
             }
-            store_tile_rows<T, D>(stg, out, bo, (int64_t)rot(blk) * BT + 16 * u, lay.rs);
+            store_tile_rows<T, DV>(stg, out, bo, (int64_t)rot(blk) * BT + 16 * u, lv.rs);
         }
     };
-    Row<T, F> stg_q[NS][U];
+    Row<T, FK> stg_q[NS][U];
 #pragma unroll
     for (int i = 0; i < NS; ++i) {
         issue(stg_q[i], wave + i * NW);
@@ -1192,9 +1232,9 @@ __global__ __launch_bounds__((StreamShape<T, D>::kThreads), (StreamShape<T, D>::
 // ---------------------------------------------------------------------------
 // Steps 5-6: backward, Q side.
 // ---------------------------------------------------------------------------
-template <typename T, int D>
+template <typename T, int DK, int DV>
 struct BwdQShape {
-    static constexpr int kU = (sizeof(T) == 2 && D == 64) ? 2 : 1;  // 16-token blocks per wave
+    static constexpr int kU = StreamShape<T, DK, DV>::kU;          // 16-token blocks per wave
     static constexpr int kG = kWaves * kU * 16;                     // tokens per iteration
     static constexpr int kLDT = kG + 16 / (int)sizeof(T);           // LDS row stride, +16 B
 };
@@ -1204,27 +1244,29 @@ struct BwdQShape {
 //   (MFMA), r = phi(q) . u (lane partial + two cross-lane adds),
 //   c = -r / den^2, dphi(q) = u / den + c z, dQ = dphi(q) * phi'(q),
 //   dz += c phi(q) (fp32, per lane), and phi(q), w = dO 2^sw / den are written
-//   to LDS transposed; then the workgroup accumulates dS += phi(Q)^T w on MFMA.
+//   to LDS transposed; then the workgroup accumulates dS += phi(Q)^T w on MFMA,
+//   the four waves splitting dS two by two as in the state kernel.
 // w carries the power of two 2^sw ~ sum(z) (f16 only) so that dO / den, about
 // 1e-6 for long sequences, does not fall into f16 subnormals; dS is unscaled
 // in fp32 when written.
-template <typename T, int D, bool SIMPLE, int FM>
+template <typename T, int DK, int DV, bool SIMPLE, int FM>
 __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(
     const T* __restrict__ q, const T* __restrict__ dout, const float* __restrict__ stS,
     const float* __restrict__ stz, T* __restrict__ dq, float* __restrict__ part,
     float* __restrict__ dS_out, float* __restrict__ dz_out, int64_t T_, const Layout lay, int PB,
     int64_t LB, float eps) {
-    using Sh = StreamShape<T, D>;
-    using Bq = BwdQShape<T, D>;
-    constexpr int F = Sh::kF, NB = Sh::kNB, KS = Sh::kKS;
+    using Sh = StreamShape<T, DK, DV>;
+    const Layout lk = lay, lv = v_layout<DK, DV>(lay);
+    using Bq = BwdQShape<T, DK, DV>;
+    constexpr int FK = Sh::kFK, FV = Sh::kFV, NBK = Sh::kNBK, KSK = Sh::kKSK, KSV = Sh::kKSV;
     constexpr int U = Bq::kU, G = Bq::kG, LDT = Bq::kLDT;
-    constexpr int NI = NB / kWaves;
-    constexpr int NFS = NB * KS;
-    constexpr int NFR = NFS + (SIMPLE ? 0 : KS);
+    constexpr int NI = DK / 32, NJ = DV / 32;  // dS blocks per wave
+    constexpr int NFS = NBK * KSV;
+    constexpr int NFR = NFS + (SIMPLE ? 0 : KSK);
     __shared__ Frag<T> sA[NFR * 64];
-    __shared__ __attribute__((aligned(16))) T sQ[D * LDT];
-    __shared__ __attribute__((aligned(16))) T sW[D * LDT];
-    __shared__ float sdz[kWaves][D];
+    __shared__ __attribute__((aligned(16))) T sQ[DK * LDT];
+    __shared__ __attribute__((aligned(16))) T sW[DV * LDT];
+    __shared__ float sdz[kWaves][DK];
     __shared__ float red[4];
 
     const int wid = xcd_remap(blockIdx.x, gridDim.x);
@@ -1234,14 +1276,15 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(
     const int64_t t1 = min(t0 + LB, T_);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int m = lane & 15, grp = lane >> 4;
-    const float* S = stS + bh * D * D;
-    const float* z = stz + bh * D;
+    const int wi = wave & 1, wj = wave >> 1;
+    const float* S = stS + bh * DK * DV;
+    const float* z = stz + bh * DK;
 
     int sS = 0, sz = 0, sw = 0;
     if constexpr (Elt<T>::kScaled) {
         float mz, zsum;
-        sS = scale_exp(block_absmax_matrix<D>(S, red));
-        block_vector_stats<D>(z, red, mz, zsum);
+        sS = scale_exp(block_absmax_matrix<DK * DV>(S, red));
+        block_vector_stats<DK>(z, red, mz, zsum);
         sz = scale_exp(mz);
         if constexpr (!SIMPLE) {
             if (zsum > 0.f && isfinite(zsum)) {
@@ -1253,70 +1296,77 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(
     }
     {
         const float fS = ldexpf(1.f, sS), fz = ldexpf(1.f, sz);
-        build_frags<T, NFR>(sA, [&](int f) {
-            return f < NFS ? build_frag<T, D, false>(S, f / KS, f % KS, m, grp, fS)
-                           : build_zfrag<T, D>(z, max(f - NFS, 0), grp, fz);
+        // captures by value: by reference, the choice between S and z
+        // became a dynamically indexed load from a private copy of the captures
+        build_frags<T, NFR>(sA, [=](int f) {
+            return f < NFS ? build_frag<T, DK, DV, false, DV>(S, f / KSV, f % KSV, m, grp, fS)
+                           : build_zfrag<T, DK>(z, max(f - NFS, 0), grp, fz);
         });
     }
-    float zl[F];
+    float zl[FK];
 #pragma unroll
-    for (int o = 0; o < F; ++o) zl[o] = SIMPLE ? 0.f : z[F * grp + o];
+    for (int o = 0; o < FK; ++o) zl[o] = SIMPLE ? 0.f : z[FK * grp + o];
     __syncthreads();
     const float uS = ldexpf(1.f, -sS), uz = ldexpf(1.f, -sz), fw = ldexpf(1.f, sw);
 
-    f32x4 dsacc[NI][NB];
+    f32x4 dsacc[NI][NJ];
 #pragma unroll
     for (int ii = 0; ii < NI; ++ii)
 #pragma unroll
-        for (int jb = 0; jb < NB; ++jb) dsacc[ii][jb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float dzacc[F];
+        for (int jj = 0; jj < NJ; ++jj) dsacc[ii][jj] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float dzacc[FK];
 #pragma unroll
-    for (int o = 0; o < F; ++o) dzacc[o] = 0.f;
+    for (int o = 0; o < FK; ++o) dzacc[o] = 0.f;
 
+    const T* qh = q + head_offset(lk, bh);
+    const T* dh = dout + head_offset(lv, bh);
+    T* gh = dq + head_offset(lk, bh);
     for (int64_t base = t0; base < t1; base += G) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int64_t t = base + (wave * U + u) * 16 + m;
             const bool valid = t < t1;
-            Row<T, F> qr, dr;
+            Row<T, FK> qr;
+            Row<T, FV> dr;
             const int64_t tc = min(t, t1 - 1);  // rows past t1 are masked below
-            load_row<T, F>(qr, q + head_offset(lay, bh) + tc * lay.rs + F * grp);
-            load_row<T, F>(dr, dout + head_offset(lay, bh) + tc * lay.rs + F * grp);
-            float qt[F];
+            load_row<T, FK>(qr, qh + tc * lk.rs + FK * grp);
+            load_row<T, FV>(dr, dh + tc * lv.rs + FV * grp);
+            float qt[FK];
 #pragma unroll
-            for (int o = 0; o < F; ++o) qt[o] = phi<FM, T>(to_f32(qr.e[o]));
-            Frag<T> bq[KS], bd[KS];
+            for (int o = 0; o < FK; ++o) qt[o] = phi<FM, T>(to_f32(qr.e[o]));
+            Frag<T> bq[KSK], bd[KSV];
 #pragma unroll
-            for (int s = 0; s < KS; ++s)
+            for (int s = 0; s < KSK; ++s)
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    bq[s][e] = static_cast<T>(qt[8 * s + e]);
-                    bd[s][e] = dr.e[8 * s + e];
-                }
-            f32x4 au[NB];
+                for (int e = 0; e < 8; ++e) bq[s][e] = static_cast<T>(qt[8 * s + e]);
 #pragma unroll
-            for (int b = 0; b < NB; ++b) au[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int s = 0; s < KSV; ++s)
 #pragma unroll
-            for (int b = 0; b < NB; ++b)
+                for (int e = 0; e < 8; ++e) bd[s][e] = dr.e[8 * s + e];
+            f32x4 au[NBK];
 #pragma unroll
-                for (int s = 0; s < KS; ++s) au[b] = mma(sA[(b * KS + s) * 64 + lane], bd[s], au[b]);
-            float dqt[F], wv[F];
+            for (int b = 0; b < NBK; ++b) au[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int b = 0; b < NBK; ++b)
+#pragma unroll
+                for (int s = 0; s < KSV; ++s) au[b] = mma(sA[(b * KSV + s) * 64 + lane], bd[s], au[b]);
+            float dqt[FK], wv[FV];
             if constexpr (SIMPLE) {
 #pragma unroll
-                for (int b = 0; b < NB; ++b)
+                for (int b = 0; b < NBK; ++b)
 #pragma unroll
                     for (int r = 0; r < 4; ++r) dqt[4 * b + r] = au[b][r] * uS;
 #pragma unroll
-                for (int o = 0; o < F; ++o) wv[o] = to_f32(dr.e[o]);
+                for (int o = 0; o < FV; ++o) wv[o] = to_f32(dr.e[o]);
             } else {
                 f32x4 ad = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int s = 0; s < KS; ++s) ad = mma(sA[(NFS + s) * 64 + lane], bq[s], ad);
+                for (int s = 0; s < KSK; ++s) ad = mma(sA[(NFS + s) * 64 + lane], bq[s], ad);
                 const float den = ad[0] * uz + eps;
-                float uu[F];
+                float uu[FK];
                 float rr = 0.f;
 #pragma unroll
-                for (int b = 0; b < NB; ++b)
+                for (int b = 0; b < NBK; ++b)
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         uu[4 * b + r] = au[b][r] * uS;
@@ -1328,24 +1378,26 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(
                 const float c = -(rr * inv) * inv;
                 const float ws = fw * inv;
 #pragma unroll
-                for (int o = 0; o < F; ++o) {
+                for (int o = 0; o < FK; ++o) {
                     dqt[o] = uu[o] * inv + c * zl[o];
-                    wv[o] = to_f32(dr.e[o]) * ws;
                     if (valid) dzacc[o] += c * qt[o];
                 }
+#pragma unroll
+                for (int o = 0; o < FV; ++o) wv[o] = to_f32(dr.e[o]) * ws;
             }
             if (valid) {
-                float out[F];
+                float out[FK];
 #pragma unroll
-                for (int o = 0; o < F; ++o) out[o] = dqt[o] * dphi_of<FM>(qt[o]);
-                store_row<T, F>(dq + head_offset(lay, bh) + t * lay.rs + F * grp, out);
+                for (int o = 0; o < FK; ++o) out[o] = dqt[o] * dphi_of<FM>(qt[o]);
+                store_row<T, FK>(gh + t * lk.rs + FK * grp, out);
             }
             const int col = (wave * U + u) * 16 + m;
 #pragma unroll
-            for (int o = 0; o < F; ++o) {
-                sQ[(F * grp + o) * LDT + col] = valid ? static_cast<T>(qt[o]) : static_cast<T>(0.f);
-                sW[(F * grp + o) * LDT + col] = valid ? static_cast<T>(wv[o]) : static_cast<T>(0.f);
-            }
+            for (int o = 0; o < FK; ++o)
+                sQ[(FK * grp + o) * LDT + col] = valid ? static_cast<T>(qt[o]) : static_cast<T>(0.f);
+#pragma unroll
+            for (int o = 0; o < FV; ++o)
+                sW[(FV * grp + o) * LDT + col] = valid ? static_cast<T>(wv[o]) : static_cast<T>(0.f);
         }
         __syncthreads();
 #pragma unroll
@@ -1354,12 +1406,12 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(
             Frag<T> a[NI];
 #pragma unroll
             for (int ii = 0; ii < NI; ++ii)
-                a[ii] = *reinterpret_cast<const Frag<T>*>(&sQ[((wave * NI + ii) * 16 + m) * LDT + col]);
+                a[ii] = *reinterpret_cast<const Frag<T>*>(&sQ[((wi * NI + ii) * 16 + m) * LDT + col]);
 #pragma unroll
-            for (int jb = 0; jb < NB; ++jb) {
-                const Frag<T> bw = *reinterpret_cast<const Frag<T>*>(&sW[(jb * 16 + m) * LDT + col]);
+            for (int jj = 0; jj < NJ; ++jj) {
+                const Frag<T> bw = *reinterpret_cast<const Frag<T>*>(&sW[((wj * NJ + jj) * 16 + m) * LDT + col]);
 #pragma unroll
-                for (int ii = 0; ii < NI; ++ii) dsacc[ii][jb] = mma(a[ii], bw, dsacc[ii][jb]);
+                for (int ii = 0; ii < NI; ++ii) dsacc[ii][jj] = mma(a[ii], bw, dsacc[ii][jj]);
             }
         }
         __syncthreads();
@@ -1368,34 +1420,34 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(
     float* oS;
     float* oz;
     if (PB == 1) {
-        oS = dS_out + bh * D * D;
-        oz = dz_out + bh * D;
+        oS = dS_out + bh * DK * DV;
+        oz = dz_out + bh * DK;
     } else {
-        oS = part + (bh * PB + p) * (int64_t)(D * D + D);
-        oz = oS + D * D;
+        oS = part + (bh * PB + p) * (int64_t)(DK * DV + DK);
+        oz = oS + DK * DV;
     }
     const float uw = ldexpf(1.f, -sw);
 #pragma unroll
     for (int ii = 0; ii < NI; ++ii) {
-        const int i0 = (wave * NI + ii) * 16 + 4 * grp;
+        const int i0 = (wi * NI + ii) * 16 + 4 * grp;
 #pragma unroll
-        for (int jb = 0; jb < NB; ++jb)
+        for (int jj = 0; jj < NJ; ++jj)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) oS[(i0 + r) * D + jb * 16 + m] = dsacc[ii][jb][r] * uw;
+            for (int r = 0; r < 4; ++r) oS[(i0 + r) * DV + (wj * NJ + jj) * 16 + m] = dsacc[ii][jj][r] * uw;
     }
     // dz: sum over the 16 token lanes of each lane group, then over waves, in a
     // fixed pattern.
 #pragma unroll
-    for (int o = 0; o < F; ++o) {
+    for (int o = 0; o < FK; ++o) {
         float x = dzacc[o];
         x += __shfl_xor(x, 1);
         x += __shfl_xor(x, 2);
         x += __shfl_xor(x, 4);
         x += __shfl_xor(x, 8);
-        if (m == 0) sdz[wave][F * grp + o] = x;
+        if (m == 0) sdz[wave][FK * grp + o] = x;
     }
     __syncthreads();
-    for (int i = tid; i < D; i += kThreads) oz[i] = (sdz[0][i] + sdz[1][i]) + (sdz[2][i] + sdz[3][i]);
+    for (int i = tid; i < DK; i += kThreads) oz[i] = (sdz[0][i] + sdz[1][i]) + (sdz[2][i] + sdz[3][i]);
 }
 
 // Steps 5-6 for 16-bit inputs at D = 64, per wave: each wave walks its own
@@ -1456,12 +1508,12 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_w64_kernel(
 
     // The state is staged in the tile area (which the loop alone uses) and
     // the fragments are built from there.
-    static_assert(StagedState<D>::kFloats * 4 <= kTileBytes, "state staging exceeds the tile area");
+    static_assert(StagedState<D, D>::kFloats * 4 <= kTileBytes, "state staging exceeds the tile area");
     int sS = 0, sz = 0, sw = 0;
     {
-        constexpr int LD = StagedState<D>::kLD;
+        constexpr int LD = StagedState<D, D>::kLD;
         float* sSt = reinterpret_cast<float*>(smem + kFragBytes);
-        const StagedState<D> st = stage_state<D>(S, z, sSt, red12);
+        const StagedState<D, D> st = stage_state<D, D>(S, z, sSt, red12);
         if constexpr (Elt<T>::kScaled) {
             sS = scale_exp(st.max_m);
             sz = scale_exp(st.max_z);
@@ -1475,7 +1527,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_w64_kernel(
         }
         const float fS = ldexpf(1.f, sS), fz = ldexpf(1.f, sz);
         build_frags<T, NFR>(sA, [&](int f) {
-            return f < NFS ? build_frag<T, D, false, LD>(sSt, f / KS, f % KS, m, grp, fS)
+            return f < NFS ? build_frag<T, D, D, false, LD>(sSt, f / KS, f % KS, m, grp, fS)
                            : build_zfrag<T, D>(sSt + D * LD, max(f - NFS, 0), grp, fz);
         });
         for (int i = tid; i < D; i += kThreads) sZ[i] = sSt[D * LD + i];
@@ -1710,7 +1762,7 @@ __global__ __launch_bounds__(BwdQTile<D>::kThreads, BwdQTile<D>::kMinBlocks) voi
     constexpr int NW16 = F * (int)sizeof(T) / 16;  // 16-byte words per quarter row
     constexpr int kFragBytes = NFR * 64 * 16;
     constexpr int kTileBytes = 2 * RT * LDR * (int)sizeof(T);  // A tile, then W tile
-    static_assert(StagedState<D>::kFloats * 4 <= kTileBytes, "state staging exceeds the tile area");
+    static_assert(StagedState<D, D>::kFloats * 4 <= kTileBytes, "state staging exceeds the tile area");
     static_assert(Sh::kStages == 2, "the loop below is written for two stages");
     __shared__ __attribute__((aligned(16))) unsigned char smem[kFragBytes + kTileBytes];
     __shared__ float red[3 * NW];
@@ -1734,9 +1786,9 @@ __global__ __launch_bounds__(BwdQTile<D>::kThreads, BwdQTile<D>::kMinBlocks) voi
     // the fragments are built from there.
     int sS = 0, sz = 0, sw = 0;
     {
-        constexpr int LD = StagedState<D>::kLD;
+        constexpr int LD = StagedState<D, D>::kLD;
         float* sSt = reinterpret_cast<float*>(tA);
-        const StagedState<D> st = stage_state<D, NT>(S, z, sSt, red);
+        const StagedState<D, D> st = stage_state<D, D, NT>(S, z, sSt, red);
         if constexpr (Elt<T>::kScaled) {
             sS = scale_exp(st.max_m);
             sz = scale_exp(st.max_z);
@@ -1750,7 +1802,7 @@ __global__ __launch_bounds__(BwdQTile<D>::kThreads, BwdQTile<D>::kMinBlocks) voi
         }
         const float fS = ldexpf(1.f, sS), fz = ldexpf(1.f, sz);
         build_frags<T, NFR, NW>(sA, [&](int f) {
-            return f < NFS ? build_frag<T, D, false, LD>(sSt, f / KS, f % KS, m, grp, fS)
+            return f < NFS ? build_frag<T, D, D, false, LD>(sSt, f / KS, f % KS, m, grp, fS)
                            : build_zfrag<T, D>(sSt + D * LD, max(f - NFS, 0), grp, fz);
         });
         for (int i = tid; i < D; i += NT) sZ[i] = sSt[D * LD + i];
@@ -1911,25 +1963,31 @@ __global__ __launch_bounds__(BwdQTile<D>::kThreads, BwdQTile<D>::kMinBlocks) voi
 // dphi(k_t) = dS v_t + dz and dv_t = dS^T phi(k_t): both are products of a
 // fixed D x D matrix with a token's row, so each is one set of MFMA blocks with
 // dS (or dS^T) as the A operand and the loaded K/V quarter rows as B.
-template <typename T, int D, bool SIMPLE, int FM>
-__global__ __launch_bounds__((StreamShape<T, D>::kThreads), (StreamShape<T, D>::kKvMinBlocks)) void bwd_dkv_kernel(
+template <typename T, int DK, int DV, bool SIMPLE, int FM>
+__global__ __launch_bounds__((StreamShape<T, DK, DV>::kThreads), (StreamShape<T, DK, DV>::kKvMinBlocks)) void bwd_dkv_kernel(
     const T* __restrict__ k, const T* __restrict__ v, const float* __restrict__ dSg,
     const float* __restrict__ dzg, T* __restrict__ dk, T* __restrict__ dv, int64_t T_, const Layout lay, int NK,
     int64_t LK) {
-    using Sh = StreamShape<T, D>;
-    constexpr int F = Sh::kF, NB = Sh::kNB, KS = Sh::kKS, NW = Sh::kWaves, NT = Sh::kThreads;
+    using Sh = StreamShape<T, DK, DV>;
+    const Layout lk = lay, lv = v_layout<DK, DV>(lay);
+    constexpr int FK = Sh::kFK, FV = Sh::kFV, NBK = Sh::kNBK, NBV = Sh::kNBV, KSK = Sh::kKSK, KSV = Sh::kKSV,
+                  NW = Sh::kWaves, NT = Sh::kThreads;
     constexpr int U = 1;  // one 16-token block per wave step; the prefetch gives the depth
-    constexpr int NFS = NB * KS;
-    constexpr int LDR = D + 16 / (int)sizeof(T);
-    // fp32 at D = 128: the fragments fill the LDS, stores go out per lane
-    constexpr bool kStage = !(sizeof(T) == 4 && D == 128);
-    // At D = 64 the backward state is staged in LDS (sharing the store
-    // staging area, which the loop alone uses) and the fragments are built
-    // from there.
-    constexpr bool kStaged = (D == 64);
+    constexpr int NF1 = NBK * KSV;  // dK side: rows over DK, contraction over DV
+    constexpr int NF2 = NBV * KSK;  // dV side: rows over DV, contraction over DK
+    constexpr int DM = DK > DV ? DK : DV;
+    constexpr int LDR = DM + 16 / (int)sizeof(T);
+    constexpr int kFragBytes = (NF1 + NF2) * 64 * (int)sizeof(Frag<T>);
+    // Store staging unless the fragments leave no room for it (fp32 at
+    // DK = DV = 128): then the stores go out per lane.
+    constexpr bool kStage = kFragBytes + NW * 16 * LDR * (int)sizeof(T) <= 150 * 1024;
+    // The backward state is staged in LDS (sharing the store staging area,
+    // which the loop alone uses) and the fragments are built from there,
+    // where it fits beside them and except at DK = DV = 128.
+    constexpr bool kStaged = Sh::kStaged && kFragBytes + StagedState<DK, DV>::kFloats * 4 <= 150 * 1024;
     constexpr int kStoreBytes = kStage ? NW * 16 * LDR * (int)sizeof(T) : 16;
-    constexpr int kStBytes = kStaged ? StagedState<D>::kFloats * 4 : 0;
-    __shared__ Frag<T> sA[2 * NFS * 64];
+    constexpr int kStBytes = kStaged ? StagedState<DK, DV>::kFloats * 4 : 0;
+    __shared__ Frag<T> sA[(NF1 + NF2) * 64];
     __shared__ __attribute__((aligned(16))) unsigned char sraw[kStoreBytes > kStBytes ? kStoreBytes : kStBytes];
     __shared__ float red[3 * NW];
     T* stage = reinterpret_cast<T*>(sraw);
@@ -1941,34 +1999,34 @@ __global__ __launch_bounds__((StreamShape<T, D>::kThreads), (StreamShape<T, D>::
     const int64_t c1 = min(c0 + LK, T_);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int m = lane & 15, grp = lane >> 4;
-    const float* dS = dSg + bh * D * D;
-    const float* dz = dzg + bh * D;
+    const float* dS = dSg + bh * DK * DV;
+    const float* dz = dzg + bh * DK;
 
-    // fragments [0, NFS): dK side, rows i, contraction j -> dS[i][j];
-    // [NFS, 2 NFS): dV side, rows j, contraction i -> dS[i][j]
+    // fragments [0, NF1): dK side, rows i, contraction j -> dS[i][j];
+    // [NF1, NF1 + NF2): dV side, rows j, contraction i -> dS[i][j]
     int sD = 0;
-    float dzl[F];
+    float dzl[FK];
     if constexpr (kStaged) {
-        constexpr int LD = StagedState<D>::kLD;
+        constexpr int LD = StagedState<DK, DV>::kLD;
         float* sSt = reinterpret_cast<float*>(sraw);
-        const StagedState<D> st = stage_state<D, NT>(dS, dz, sSt, red);
+        const StagedState<DK, DV> st = stage_state<DK, DV, NT>(dS, dz, sSt, red);
         if constexpr (Elt<T>::kScaled) sD = scale_exp(st.max_m);
         const float fD = ldexpf(1.f, sD);
-        build_frags<T, 2 * NFS, NW>(sA, [&](int f) {
-            return f < NFS ? build_frag<T, D, false, LD>(sSt, f / KS, f % KS, m, grp, fD)
-                           : build_frag<T, D, true, LD>(sSt, (f - NFS) / KS, (f - NFS) % KS, m, grp, fD);
+        build_frags<T, NF1 + NF2, NW>(sA, [&](int f) {
+            return f < NF1 ? build_frag<T, DK, DV, false, LD>(sSt, f / KSV, f % KSV, m, grp, fD)
+                           : build_frag<T, DV, DK, true, LD>(sSt, (f - NF1) / KSK, (f - NF1) % KSK, m, grp, fD);
         });
 #pragma unroll
-        for (int o = 0; o < F; ++o) dzl[o] = SIMPLE ? 0.f : sSt[D * LD + F * grp + o];
+        for (int o = 0; o < FK; ++o) dzl[o] = SIMPLE ? 0.f : sSt[DK * LD + FK * grp + o];
     } else {
-        if constexpr (Elt<T>::kScaled) sD = scale_exp(block_absmax_matrix<D, NT>(dS, red));
+        if constexpr (Elt<T>::kScaled) sD = scale_exp(block_absmax_matrix<DK * DV, NT>(dS, red));
         const float fD = ldexpf(1.f, sD);
-        build_frags<T, 2 * NFS, NW>(sA, [&](int f) {
-            return f < NFS ? build_frag<T, D, false>(dS, f / KS, f % KS, m, grp, fD)
-                           : build_frag<T, D, true>(dS, (f - NFS) / KS, (f - NFS) % KS, m, grp, fD);
+        build_frags<T, NF1 + NF2, NW>(sA, [&](int f) {
+            return f < NF1 ? build_frag<T, DK, DV, false, DV>(dS, f / KSV, f % KSV, m, grp, fD)
+                           : build_frag<T, DV, DK, true, DV>(dS, (f - NF1) / KSK, (f - NF1) % KSK, m, grp, fD);
         });
 #pragma unroll
-        for (int o = 0; o < F; ++o) dzl[o] = SIMPLE ? 0.f : dz[F * grp + o];
+        for (int o = 0; o < FK; ++o) dzl[o] = SIMPLE ? 0.f : dz[FK * grp + o];
     }
     const float uD = ldexpf(1.f, -sD);
     __syncthreads();
@@ -1977,13 +2035,14 @@ __global__ __launch_bounds__((StreamShape<T, D>::kThreads), (StreamShape<T, D>::
     // early exit (an exit makes the compiler wait for every load in flight
     // where the paths join): the chunk's buffer descriptors read rows past its
     // end as zeros and drop their stores.
-    const HeadBuf bk = slice_buf(k, lay, bh, D, c0, c1), bv_ = slice_buf(v, lay, bh, D, c0, c1);
-    const HeadBuf bdk = slice_buf(dk, lay, bh, D, c0, c1), bdv = slice_buf(dv, lay, bh, D, c0, c1);
+    const HeadBuf bk = slice_buf(k, lk, bh, DK, c0, c1), bv_ = slice_buf(v, lv, bh, DV, c0, c1);
+    const HeadBuf bdk = slice_buf(dk, lk, bh, DK, c0, c1), bdv = slice_buf(dv, lv, bh, DV, c0, c1);
     T* stg = stage + (kStage ? wave * 16 * LDR : 0);
     // The loaded words as they are (see the dQ kernel).
-    constexpr int NQW = F * (int)sizeof(T) / 16;  // 16-byte words per quarter row
+    constexpr int NQK = FK * (int)sizeof(T) / 16;  // 16-byte words per quarter row of K
+    constexpr int NQV = FV * (int)sizeof(T) / 16;  // ... of V
     struct Stage {
-        u32x4 k[U][NQW], v[U][NQW];
+        u32x4 k[U][NQK], v[U][NQV];
     };
     constexpr int NS = Sh::kStages;
     const Rotation rot((int)((c1 - c0 + 16 * U - 1) / (16 * U)), NS * NW, wid);
@@ -1991,78 +2050,105 @@ __global__ __launch_bounds__((StreamShape<T, D>::kThreads), (StreamShape<T, D>::
         const int64_t bs = (int64_t)rot(blk) * 16 * U;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int off = buf_off<T>(bs + 16 * u + m, lay.rs, F * grp);
+            const int ok_ = buf_off<T>(bs + 16 * u + m, lk.rs, FK * grp);
+            const int ov_ = buf_off<T>(bs + 16 * u + m, lv.rs, FV * grp);
 #pragma unroll
-            for (int i = 0; i < NQW; ++i) {
-                st.k[u][i] = __builtin_amdgcn_raw_buffer_load_b128(bk.rsrc, off + 16 * i, 0, 0);
-                st.v[u][i] = __builtin_amdgcn_raw_buffer_load_b128(bv_.rsrc, off + 16 * i, 0, 0);
+            for (int i = 0; i < (NQK > NQV ? NQK : NQV); ++i) {
+                if (i < NQK) st.k[u][i] = __builtin_amdgcn_raw_buffer_load_b128(bk.rsrc, ok_ + 16 * i, 0, 0);
+                if (i < NQV) st.v[u][i] = __builtin_amdgcn_raw_buffer_load_b128(bv_.rsrc, ov_ + 16 * i, 0, 0);
             }
         }
     };
     auto body = [&](Stage& st, int blk) {
         const int64_t base = (int64_t)rot(blk) * 16 * U;
         sched_fence();
-        float dphik[U][F];
-        Frag<T> bk[U][KS], bv[U][KS];
+        float dphik[U][FK];
+        Frag<T> bk[U][KSK], bv[U][KSV];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            Row<T, F> lk, lv;
-            __builtin_memcpy(lk.e, st.k[u], sizeof(lk));
-            __builtin_memcpy(lv.e, st.v[u], sizeof(lv));
-            float kt[F];
+            Row<T, FK> lk_;
+            Row<T, FV> lv_;
+            __builtin_memcpy(lk_.e, st.k[u], sizeof(lk_));
+            __builtin_memcpy(lv_.e, st.v[u], sizeof(lv_));
+            float kt[FK];
 #pragma unroll
-            for (int o = 0; o < F; ++o) {
-                feature<FM, T>(to_f32(lk.e[o]), kt[o], dphik[u][o]);
+            for (int o = 0; o < FK; ++o) {
+                feature<FM, T>(to_f32(lk_.e[o]), kt[o], dphik[u][o]);
             }
 #pragma unroll
-            for (int s = 0; s < KS; ++s)
+            for (int s = 0; s < KSK; ++s)
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    bk[u][s][e] = static_cast<T>(kt[8 * s + e]);
-                    bv[u][s][e] = lv.e[8 * s + e];
+                for (int e = 0; e < 8; ++e) bk[u][s][e] = static_cast<T>(kt[8 * s + e]);
+#pragma unroll
+            for (int s = 0; s < KSV; ++s)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) bv[u][s][e] = lv_.e[8 * s + e];
+        }
+        f32x4 ak[U][NBK], av[U][NBV];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+#pragma unroll
+            for (int b = 0; b < NBK; ++b) ak[u][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int b = 0; b < NBV; ++b) av[u][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+        if constexpr (DK == DV) {
+            // interleaved, as the two products share their loop shape
+#pragma unroll
+            for (int b = 0; b < NBK; ++b)
+#pragma unroll
+                for (int s = 0; s < KSV; ++s) {
+                    const Frag<T> a1 = sA[(b * KSV + s) * 64 + lane];
+                    const Frag<T> a2 = sA[(NF1 + b * KSK + s) * 64 + lane];
+#pragma unroll
+                    for (int u = 0; u < U; ++u) {
+                        ak[u][b] = mma(a1, bv[u][s], ak[u][b]);
+                        av[u][b] = mma(a2, bk[u][s], av[u][b]);
+                    }
+                }
+        } else {
+#pragma unroll
+            for (int b = 0; b < NBK; ++b)
+#pragma unroll
+                for (int s = 0; s < KSV; ++s) {
+                    const Frag<T> a1 = sA[(b * KSV + s) * 64 + lane];
+#pragma unroll
+                    for (int u = 0; u < U; ++u) ak[u][b] = mma(a1, bv[u][s], ak[u][b]);
+                }
+#pragma unroll
+            for (int b = 0; b < NBV; ++b)
+#pragma unroll
+                for (int s = 0; s < KSK; ++s) {
+                    const Frag<T> a2 = sA[(NF1 + b * KSK + s) * 64 + lane];
+#pragma unroll
+                    for (int u = 0; u < U; ++u) av[u][b] = mma(a2, bk[u][s], av[u][b]);
                 }
         }
-        f32x4 ak[U][NB], av[U][NB];
-#pragma unroll
-        for (int u = 0; u < U; ++u)
-#pragma unroll
-            for (int b = 0; b < NB; ++b) {
-                ak[u][b] = f32x4{0.f, 0.f, 0.f, 0.f};
-                av[u][b] = f32x4{0.f, 0.f, 0.f, 0.f};
-            }
-#pragma unroll
-        for (int b = 0; b < NB; ++b)
-#pragma unroll
-            for (int s = 0; s < KS; ++s) {
-                const Frag<T> a1 = sA[(b * KS + s) * 64 + lane];
-                const Frag<T> a2 = sA[(NFS + b * KS + s) * 64 + lane];
-#pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    ak[u][b] = mma(a1, bv[u][s], ak[u][b]);
-                    av[u][b] = mma(a2, bk[u][s], av[u][b]);
-                }
-            }
         // the stage's registers are free once the products have read V
         sched_fence();
         issue(st, blk + NS * NW);
         sched_fence();
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            Row<T, F> gk, gv;
+            Row<T, FK> gk;
+            Row<T, FV> gv;
 #pragma unroll
-            for (int b = 0; b < NB; ++b)
+            for (int b = 0; b < NBK; ++b)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int o = 4 * b + r;
                     gk.e[o] = static_cast<T>((ak[u][b][r] * uD + dzl[o]) * dphik[u][o]);
-                    gv.e[o] = static_cast<T>(av[u][b][r] * uD);
                 }
+#pragma unroll
+            for (int b = 0; b < NBV; ++b)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) gv.e[4 * b + r] = static_cast<T>(av[u][b][r] * uD);
             if constexpr (kStage) {
-                store_tile_rows<T, D>(stg, gk, bdk, base + 16 * u, lay.rs);
-                store_tile_rows<T, D>(stg, gv, bdv, base + 16 * u, lay.rs);
+                store_tile_rows<T, DK>(stg, gk, bdk, base + 16 * u, lk.rs);
+                store_tile_rows<T, DV>(stg, gv, bdv, base + 16 * u, lv.rs);
             } else {
-                store_tile_quarters<T, D>(gk, bdk, base + 16 * u, lay.rs);
-                store_tile_quarters<T, D>(gv, bdv, base + 16 * u, lay.rs);
+                store_tile_quarters<T, DK>(gk, bdk, base + 16 * u, lk.rs);
+                store_tile_quarters<T, DV>(gv, bdv, base + 16 * u, lv.rs);
             }
         }
     };
@@ -2081,10 +2167,10 @@ __global__ __launch_bounds__((StreamShape<T, D>::kThreads), (StreamShape<T, D>::
 // ---------------------------------------------------------------------------
 // Host-side dispatch.
 // ---------------------------------------------------------------------------
-template <typename T, int D>
-constexpr bool kWaveKernels = (sizeof(T) == 2 && D == 64);
-template <typename T, int D>
-constexpr bool kTileKernels = (sizeof(T) == 2 && D == 128);
+template <typename T, int DK, int DV>
+constexpr bool kWaveKernels = (sizeof(T) == 2 && DK == 64 && DV == 64);
+template <typename T, int DK, int DV>
+constexpr bool kTileKernels = (sizeof(T) == 2 && DK == 128 && DV == 128);
 
 template <typename X>
 struct Same {
@@ -2103,45 +2189,49 @@ hipError_t launch(void (*kernel)(KArgs...), int64_t blocks, int threads, hipStre
 }
 
 // After a split reduction (P > 1 slices per head), sum the partials.
-template <int D>
+template <int DK, int DV>
 hipError_t launch_combine(int P, const float* part, float* outS, float* outz, int64_t BH, hipStream_t s) {
     if (P <= 1) return hipSuccess;
-    constexpr int E4 = (D * D + D) / 4;
-    return launch(combine_kernel<D>, BH * ((E4 + kThreads - 1) / kThreads), kThreads, s, part, P, outS, outz, BH);
+    constexpr int E4 = (DK * DV + DK) / 4;
+    return launch(combine_kernel<DK, DV>, BH * ((E4 + kThreads - 1) / kThreads), kThreads, s, part, P, outS, outz,
+                  BH);
 }
 
-template <typename T, int D, int FM>
+template <typename T, int DK, int DV, int FM>
 hipError_t fwd_state_fm(const Plan& p, const void* k, const void* v, float* state, void* ws,
                        hipStream_t s) {
     const int64_t nblk = p.BH * p.P;
     float* part = reinterpret_cast<float*>(static_cast<char*>(ws) + p.off_part);
     const T* kk = static_cast<const T*>(k);
     const T* vv = static_cast<const T*>(v);
-    float* sz = state + p.BH * D * D;
+    float* sz = state + p.BH * DK * DV;
     hipError_t e;
-    if constexpr (kWaveKernels<T, D>)
+    if constexpr (kWaveKernels<T, DK, DV>)
         e = launch(fwd_state_w64_kernel<T, FM>, nblk, kThreads, s, kk, vv, state, sz, part, p.T, p.lay, p.P, p.L);
-    else if constexpr (kTileKernels<T, D>)
+    else if constexpr (kTileKernels<T, DK, DV>)
         e = launch(fwd_state_c128_kernel<T, FM>, nblk, kThreads, s, kk, vv, state, sz, part, p.T, p.lay, p.P, p.L);
     else
-        e = launch(fwd_state_kernel<T, D, FM>, nblk, kThreads, s, kk, vv, state, sz, part, p.T, p.lay, p.P, p.L);
+        e = launch(fwd_state_kernel<T, DK, DV, FM>, nblk, kThreads, s, kk, vv, state, sz, part, p.T, p.lay, p.P,
+                   p.L);
     if (e != hipSuccess) return e;
-    return launch_combine<D>(p.P, part, state, sz, p.BH, s);
+    return launch_combine<DK, DV>(p.P, part, state, sz, p.BH, s);
 }
 
-template <typename T, int D, int FM>
+template <typename T, int DK, int DV, int FM>
 hipError_t fwd_output_fm(const Plan& p, const void* q, const float* state, void* o, hipStream_t s) {
     const int64_t nblk = p.BH * p.NQ;
-    constexpr int nt = StreamShape<T, D>::kThreads;
+    constexpr int nt = StreamShape<T, DK, DV>::kThreads;
     const T* qq = static_cast<const T*>(q);
-    const float* sz = state + p.BH * D * D;
+    const float* sz = state + p.BH * DK * DV;
     T* oo = static_cast<T*>(o);
     if (p.simple)
-        return launch(fwd_output_kernel<T, D, true, FM>, nblk, nt, s, qq, state, sz, oo, p.T, p.lay, p.NQ, p.LQ, p.eps);
-    return launch(fwd_output_kernel<T, D, false, FM>, nblk, nt, s, qq, state, sz, oo, p.T, p.lay, p.NQ, p.LQ, p.eps);
+        return launch(fwd_output_kernel<T, DK, DV, true, FM>, nblk, nt, s, qq, state, sz, oo, p.T, p.lay, p.NQ, p.LQ,
+                      p.eps);
+    return launch(fwd_output_kernel<T, DK, DV, false, FM>, nblk, nt, s, qq, state, sz, oo, p.T, p.lay, p.NQ, p.LQ,
+                  p.eps);
 }
 
-template <typename T, int D, int FM>
+template <typename T, int DK, int DV, int FM>
 hipError_t bwd_dq_fm(const Plan& p, const void* q, const void* dout, const float* state, void* dq,
                     void* ws, hipStream_t s) {
     const int64_t nblk = p.BH * p.PB;
@@ -2151,131 +2241,147 @@ hipError_t bwd_dq_fm(const Plan& p, const void* q, const void* dout, const float
     const T* qq = static_cast<const T*>(q);
     const T* dd = static_cast<const T*>(dout);
     const float* sS = state;
-    const float* sz = state + p.BH * D * D;
+    const float* sz = state + p.BH * DK * DV;
     T* g = static_cast<T*>(dq);
     float* dS = dst;
-    float* dz = dst + p.BH * D * D;
+    float* dz = dst + p.BH * DK * DV;
     hipError_t e;
-    if constexpr (kWaveKernels<T, D>) {
+    if constexpr (kWaveKernels<T, DK, DV>) {
         e = p.simple ? launch(bwd_dq_w64_kernel<T, true, FM>, nblk, kThreads, s, qq, dd, sS, sz, g, part, dS, dz, p.T,
                               p.lay, p.PB, p.LB, p.eps)
                      : launch(bwd_dq_w64_kernel<T, false, FM>, nblk, kThreads, s, qq, dd, sS, sz, g, part, dS, dz, p.T,
                               p.lay, p.PB, p.LB, p.eps);
-    } else if constexpr (kTileKernels<T, D>) {
-        constexpr int nt = BwdQTile<D>::kThreads;
-        e = p.simple ? launch(bwd_dq_tile_kernel<T, D, true, FM>, nblk, nt, s, qq, dd, sS, sz, g, part, dS, dz, p.T,
+    } else if constexpr (kTileKernels<T, DK, DV>) {
+        constexpr int nt = BwdQTile<DK>::kThreads;
+        e = p.simple ? launch(bwd_dq_tile_kernel<T, DK, true, FM>, nblk, nt, s, qq, dd, sS, sz, g, part, dS, dz, p.T,
                               p.lay, p.PB, p.LB, p.eps)
-                     : launch(bwd_dq_tile_kernel<T, D, false, FM>, nblk, nt, s, qq, dd, sS, sz, g, part, dS, dz, p.T,
+                     : launch(bwd_dq_tile_kernel<T, DK, false, FM>, nblk, nt, s, qq, dd, sS, sz, g, part, dS, dz, p.T,
                               p.lay, p.PB, p.LB, p.eps);
     } else {
-        e = p.simple ? launch(bwd_dq_kernel<T, D, true, FM>, nblk, kThreads, s, qq, dd, sS, sz, g, part, dS, dz, p.T,
-                              p.lay, p.PB, p.LB, p.eps)
-                     : launch(bwd_dq_kernel<T, D, false, FM>, nblk, kThreads, s, qq, dd, sS, sz, g, part, dS, dz, p.T,
-                              p.lay, p.PB, p.LB, p.eps);
+        e = p.simple ? launch(bwd_dq_kernel<T, DK, DV, true, FM>, nblk, kThreads, s, qq, dd, sS, sz, g, part, dS, dz,
+                              p.T, p.lay, p.PB, p.LB, p.eps)
+                     : launch(bwd_dq_kernel<T, DK, DV, false, FM>, nblk, kThreads, s, qq, dd, sS, sz, g, part, dS, dz,
+                              p.T, p.lay, p.PB, p.LB, p.eps);
     }
     if (e != hipSuccess) return e;
-    return launch_combine<D>(p.PB, part, dS, dz, p.BH, s);
+    return launch_combine<DK, DV>(p.PB, part, dS, dz, p.BH, s);
 }
 
-template <typename T, int D, int FM>
+template <typename T, int DK, int DV, int FM>
 hipError_t bwd_dkv_fm(const Plan& p, const void* k, const void* v, void* dk, void* dv, void* ws,
                      hipStream_t s) {
     const int64_t nblk = p.BH * p.NK;
-    constexpr int nt = StreamShape<T, D>::kThreads;
+    constexpr int nt = StreamShape<T, DK, DV>::kThreads;
     const float* dst = reinterpret_cast<const float*>(static_cast<char*>(ws) + p.off_dstate);
-    const float* dz = dst + p.BH * D * D;
+    const float* dz = dst + p.BH * DK * DV;
     const T* kk = static_cast<const T*>(k);
     const T* vv = static_cast<const T*>(v);
     T* gk = static_cast<T*>(dk);
     T* gv = static_cast<T*>(dv);
     if (p.simple)
-        return launch(bwd_dkv_kernel<T, D, true, FM>, nblk, nt, s, kk, vv, dst, dz, gk, gv, p.T, p.lay, p.NK, p.LK);
-    return launch(bwd_dkv_kernel<T, D, false, FM>, nblk, nt, s, kk, vv, dst, dz, gk, gv, p.T, p.lay, p.NK, p.LK);
+        return launch(bwd_dkv_kernel<T, DK, DV, true, FM>, nblk, nt, s, kk, vv, dst, dz, gk, gv, p.T, p.lay, p.NK,
+                      p.LK);
+    return launch(bwd_dkv_kernel<T, DK, DV, false, FM>, nblk, nt, s, kk, vv, dst, dz, gk, gv, p.T, p.lay, p.NK,
+                  p.LK);
 }
 
 // The feature map is a template parameter of every kernel: one switch here.
-#define LA_FEATURE_MAP(FN, ...)                                      \
-    switch (p.fm) {                                                  \
-        case kPhiRelu: return FN<T, D, kPhiRelu>(p, __VA_ARGS__);    \
-        case kPhiIdentity: return FN<T, D, kPhiIdentity>(p, __VA_ARGS__); \
-        default: return FN<T, D, kPhiElu1>(p, __VA_ARGS__);          \
+#define LA_FEATURE_MAP(FN, ...)                                                    \
+    switch (p.fm) {                                                                \
+        case kPhiRelu: return FN<T, DK, DV, kPhiRelu>(p, __VA_ARGS__);             \
+        case kPhiIdentity: return FN<T, DK, DV, kPhiIdentity>(p, __VA_ARGS__);     \
+        default: return FN<T, DK, DV, kPhiElu1>(p, __VA_ARGS__);                   \
     }
 
-template <typename T, int D>
+template <typename T, int DK, int DV>
 hipError_t fwd_state_t(const Plan& p, const void* k, const void* v, float* state, void* ws, hipStream_t s) {
     LA_FEATURE_MAP(fwd_state_fm, k, v, state, ws, s);
 }
-template <typename T, int D>
+template <typename T, int DK, int DV>
 hipError_t fwd_output_t(const Plan& p, const void* q, const float* state, void* o, hipStream_t s) {
     LA_FEATURE_MAP(fwd_output_fm, q, state, o, s);
 }
-template <typename T, int D>
+template <typename T, int DK, int DV>
 hipError_t bwd_dq_t(const Plan& p, const void* q, const void* dout, const float* state, void* dq, void* ws,
                     hipStream_t s) {
     LA_FEATURE_MAP(bwd_dq_fm, q, dout, state, dq, ws, s);
 }
-template <typename T, int D>
+template <typename T, int DK, int DV>
 hipError_t bwd_dkv_t(const Plan& p, const void* k, const void* v, void* dk, void* dv, void* ws, hipStream_t s) {
     LA_FEATURE_MAP(bwd_dkv_fm, k, v, dk, dv, ws, s);
 }
 
-// dtype codes follow la_dtype: 0 = f32, 1 = f16, 2 = bf16.
-#define LA_DISPATCH(FN, ...)                                         \
-    switch (p.dtype * 2 + (p.D == 128 ? 1 : 0)) {                   \
-        case 0: return FN<float, 64>(p, __VA_ARGS__);               \
-        case 1: return FN<float, 128>(p, __VA_ARGS__);              \
-        case 2: return FN<f16, 64>(p, __VA_ARGS__);                 \
-        case 3: return FN<f16, 128>(p, __VA_ARGS__);                \
-        case 4: return FN<bf16, 64>(p, __VA_ARGS__);                \
-        case 5: return FN<bf16, 128>(p, __VA_ARGS__);               \
-        default: return hipErrorInvalidValue;                       \
-    }
-
-template <typename T, int D>
+template <typename T, int DK, int DV>
 SplitCfg split_config_t(int step) {
     switch (step) {
         case kStepState:
-            if constexpr (kWaveKernels<T, D>) return {int64_t(StateW64::kStep) * kWaves * StateW64::kStages, 512};
-            else if constexpr (kTileKernels<T, D>) return {int64_t(StateC128::kTile) * StateC128::kStages, 512};
-            else return {StateShape<T, D>::kTT, 1024};
+            if constexpr (kWaveKernels<T, DK, DV>) return {int64_t(StateW64::kStep) * kWaves * StateW64::kStages, 512};
+            else if constexpr (kTileKernels<T, DK, DV>) return {int64_t(StateC128::kTile) * StateC128::kStages, 512};
+            else return {StateShape<T, DK, DV>::kTT, 1024};
         case kStepBwdQ:
-            if constexpr (kWaveKernels<T, D>) return {int64_t(BwdQW64::kRound) * BwdQW64::kStages, 512};
-            else if constexpr (kTileKernels<T, D>) return {int64_t(BwdQTile<D>::kRound) * BwdQTile<D>::kStages, 256};
-            else return {BwdQShape<T, D>::kG, 1024};
+            if constexpr (kWaveKernels<T, DK, DV>) return {int64_t(BwdQW64::kRound) * BwdQW64::kStages, 512};
+            else if constexpr (kTileKernels<T, DK, DV>)
+                return {int64_t(BwdQTile<DK>::kRound) * BwdQTile<DK>::kStages, 256};
+            else return {BwdQShape<T, DK, DV>::kG, 1024};
         case kStepBwdKV:
-            return {int64_t(StreamShape<T, D>::kStages) * 16 * StreamShape<T, D>::kWaves, 1024};
+            return {int64_t(StreamShape<T, DK, DV>::kStages) * 16 * StreamShape<T, DK, DV>::kWaves, 1024};
         default:
-            return {StreamShape<T, D>::kStages * StreamShape<T, D>::kG, 2048};
+            return {StreamShape<T, DK, DV>::kStages * StreamShape<T, DK, DV>::kG, 2048};
     }
 }
+
+// ---------------------------------------------------------------------------
+// This compilation unit: one element type and one Q/K head size, every V head
+// size. The build compiles the file once per (LA_UNIT_DTYPE, LA_UNIT_DK).
+// ---------------------------------------------------------------------------
+#if !defined(LA_UNIT_DTYPE) || !defined(LA_UNIT_DK)
+#error "compile once per unit with -DLA_UNIT_DTYPE=<0|1|2> (la_dtype) -DLA_UNIT_DK=<32|64|96|128>"
+#endif
+
+template <int DT> struct UnitType;
+template <> struct UnitType<0> { using type = float; };
+template <> struct UnitType<1> { using type = f16; };
+template <> struct UnitType<2> { using type = bf16; };
+using UT = UnitType<LA_UNIT_DTYPE>::type;
+constexpr int UDK = LA_UNIT_DK;
+
+#define LA_DV_DISPATCH(FN, ...)                                       \
+    switch (p.DV) {                                                   \
+        case 32: return FN<UT, UDK, 32>(p, __VA_ARGS__);              \
+        case 64: return FN<UT, UDK, 64>(p, __VA_ARGS__);              \
+        case 96: return FN<UT, UDK, 96>(p, __VA_ARGS__);              \
+        case 128: return FN<UT, UDK, 128>(p, __VA_ARGS__);            \
+        default: return hipErrorInvalidValue;                         \
+    }
+
+hipError_t unit_fwd_state(const Plan& p, const void* k, const void* v, float* state, void* ws, hipStream_t s) {
+    LA_DV_DISPATCH(fwd_state_t, k, v, state, ws, s);
+}
+hipError_t unit_fwd_output(const Plan& p, const void* q, const float* state, void* o, hipStream_t s) {
+    LA_DV_DISPATCH(fwd_output_t, q, state, o, s);
+}
+hipError_t unit_bwd_dq(const Plan& p, const void* q, const void* dout, const float* state, void* dq, void* ws,
+                       hipStream_t s) {
+    LA_DV_DISPATCH(bwd_dq_t, q, dout, state, dq, ws, s);
+}
+hipError_t unit_bwd_dkv(const Plan& p, const void* k, const void* v, void* dk, void* dv, void* ws, hipStream_t s) {
+    LA_DV_DISPATCH(bwd_dkv_t, k, v, dk, dv, ws, s);
+}
+SplitCfg unit_split_config(int step, int DV) {
+    switch (DV) {
+        case 32: return split_config_t<UT, UDK, 32>(step);
+        case 64: return split_config_t<UT, UDK, 64>(step);
+        case 96: return split_config_t<UT, UDK, 96>(step);
+        default: return split_config_t<UT, UDK, 128>(step);
+    }
+}
+
+const KernelSet kUnitSet = {unit_fwd_state, unit_fwd_output, unit_bwd_dq, unit_bwd_dkv, unit_split_config};
 
 }  // namespace
 
-SplitCfg split_config(int step, int dtype, int D) {
-    switch (dtype * 2 + (D == 128 ? 1 : 0)) {
-        case 0: return split_config_t<float, 64>(step);
-        case 1: return split_config_t<float, 128>(step);
-        case 2: return split_config_t<f16, 64>(step);
-        case 3: return split_config_t<f16, 128>(step);
-        case 4: return split_config_t<bf16, 64>(step);
-        default: return split_config_t<bf16, 128>(step);
-    }
-}
-
-hipError_t launch_fwd_state(const Plan& p, const void* k, const void* v, float* state, void* ws,
-                            hipStream_t s) {
-    LA_DISPATCH(fwd_state_t, k, v, state, ws, s);
-}
-hipError_t launch_fwd_output(const Plan& p, const void* q, const float* state, void* o, hipStream_t s) {
-    LA_DISPATCH(fwd_output_t, q, state, o, s);
-}
-hipError_t launch_bwd_dq(const Plan& p, const void* q, const void* dout, const float* state, void* dq,
-                         void* ws, hipStream_t s) {
-    LA_DISPATCH(bwd_dq_t, q, dout, state, dq, ws, s);
-}
-hipError_t launch_bwd_dkv(const Plan& p, const void* k, const void* v, void* dk, void* dv, void* ws,
-                          hipStream_t s) {
-    LA_DISPATCH(bwd_dkv_t, k, v, dk, dv, ws, s);
-}
+#define LA_UNIT_NAME2(dt, dk) kernel_set_##dt##_##dk
+#define LA_UNIT_NAME(dt, dk) LA_UNIT_NAME2(dt, dk)
+const KernelSet* LA_UNIT_NAME(LA_UNIT_DTYPE, LA_UNIT_DK)() { return &kUnitSet; }
 
 }  // namespace la

@@ -48,11 +48,12 @@ def max_rel_err(x: np.ndarray, ref: np.ndarray) -> float:
     return float(np.max(np.abs(np.asarray(x, dtype=np.float64) - ref)) / scale)
 
 
-def split_state(state: torch.Tensor, B: int, H: int, D: int):
-    """fp32 state buffer -> (S [B,H,D,D], z [B,H,D]) as float64 numpy."""
+def split_state(state: torch.Tensor, B: int, H: int, D: int, Dv: int | None = None):
+    """fp32 state buffer -> (S [B,H,D,Dv], z [B,H,D]) as float64 numpy."""
+    Dv = D if Dv is None else Dv
     s = state.detach().cpu().numpy().astype(np.float64)
     n = B * H
-    return s[: n * D * D].reshape(B, H, D, D), s[n * D * D: n * D * D + n * D].reshape(B, H, D)
+    return s[: n * D * Dv].reshape(B, H, D, Dv), s[n * D * Dv: n * D * Dv + n * D].reshape(B, H, D)
 
 
 def bytes_equal(a: torch.Tensor, b: torch.Tensor) -> bool:

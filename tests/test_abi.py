@@ -48,7 +48,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.la_version() == 2
+    assert L.la_version() == 3
     for s in range(11):
         txt = L.la_status_str(s).decode()
         assert txt.startswith("LA_"), txt
@@ -56,14 +56,20 @@ def test_version_and_status_strings(L):
     assert "HEAD_DIM" in L.la_status_str(HEAD_DIM).decode()
 
 
-def prob(B=2, H=3, T=100, D=64, dtype=1, flags=0, eps=1e-6):
-    return Problem(B, H, T, D, dtype, flags, eps)
+def prob(B=2, H=3, T=100, D=64, dtype=1, flags=0, eps=1e-6, Dv=0):
+    return Problem(B, H, T, D, Dv, dtype, flags, eps)
+
+
+def test_problem_struct_matches_header():
+    # int64 B, H, T, D, Dv; int32 dtype; uint32 flags; float eps; padded to 8
+    assert ctypes.sizeof(Problem) == 56
+    assert [f[0] for f in Problem._fields_] == ["B", "H", "T", "D", "Dv", "dtype", "flags", "eps"]
 
 
 def test_state_bytes_formula(L):
-    for (B, H, D) in ((1, 2, 64), (8, 16, 64), (8, 32, 128)):
-        p = prob(B=B, H=H, D=D)
-        assert L.la_state_bytes(ctypes.byref(p)) == B * H * (D * D + D) * 4
+    for (B, H, D, Dv) in ((1, 2, 64, 0), (8, 16, 64, 64), (8, 32, 128, 0), (2, 3, 32, 96), (2, 3, 128, 32)):
+        p = prob(B=B, H=H, D=D, Dv=Dv)
+        assert L.la_state_bytes(ctypes.byref(p)) == B * H * (D * (Dv or D) + D) * 4
 
 
 def test_workspace_bytes_covers_state_and_partials(L):
@@ -78,7 +84,8 @@ def test_workspace_bytes_covers_state_and_partials(L):
     one = L.la_workspace_bytes(ctypes.byref(prob(B=1, H=1, T=1 << 20, D=64)))
     assert one >= 64 * E * 4
     # invalid problems report 0
-    assert L.la_workspace_bytes(ctypes.byref(prob(D=96))) == 0
+    assert L.la_workspace_bytes(ctypes.byref(prob(D=256))) == 0
+    assert L.la_workspace_bytes(ctypes.byref(prob(Dv=48))) == 0
     assert L.la_state_bytes(ctypes.byref(prob(dtype=7))) == 0
     assert L.la_workspace_bytes(None) == 0
 
@@ -116,8 +123,8 @@ def test_fwd_rejects_bad_problems(L):
     assert fwd_call(L, None) == NULL
     assert fwd_call(L, prob(dtype=3)) == DTYPE
     assert fwd_call(L, prob(dtype=-1)) == DTYPE
-    assert fwd_call(L, prob(D=32)) == HEAD_DIM
-    assert fwd_call(L, prob(D=96)) == HEAD_DIM
+    for d, dv in ((48, 0), (256, 0), (0, 64), (16, 0), (64, 256), (64, 16), (64, -64), (96, 160)):
+        assert fwd_call(L, prob(D=d, Dv=dv)) == HEAD_DIM, (d, dv)
     assert fwd_call(L, prob(B=-1)) == SHAPE
     assert fwd_call(L, prob(T=-5)) == SHAPE
     assert fwd_call(L, prob(H=1 << 30)) == SHAPE
@@ -125,6 +132,10 @@ def test_fwd_rejects_bad_problems(L):
     assert fwd_call(L, prob(T=(1 << 31) // (128 * 2), D=128)) == SHAPE
     assert L.la_workspace_bytes(ctypes.byref(prob(T=(1 << 31) // (128 * 2) - 1, D=128))) > 0
     assert L.la_workspace_bytes(ctypes.byref(prob(T=(1 << 31) // (64 * 4), D=64, dtype=0))) == 0
+    # the wider of the two head sizes sets the limit
+    assert fwd_call(L, prob(T=(1 << 31) // (128 * 2), D=32, Dv=128)) == SHAPE
+    assert fwd_call(L, prob(T=(1 << 31) // (128 * 2), D=128, Dv=32)) == SHAPE
+    assert L.la_workspace_bytes(ctypes.byref(prob(T=(1 << 31) // (128 * 2) - 1, D=32, Dv=128))) > 0
     assert fwd_call(L, prob(flags=0x10)) == FLAGS
     assert fwd_call(L, prob(flags=0x80000000)) == FLAGS
     assert fwd_call(L, prob(flags=0x4 | 0x8)) == FLAGS  # two feature maps
@@ -149,6 +160,34 @@ def test_fwd_rejects_bad_buffers(L):
     assert fwd_call(L, p, state=ctypes.c_void_p(A + (3 << 24) + 256)) == ALIAS
     # workspace overlapping an input
     assert fwd_call(L, p, ws=ctypes.c_void_p(A + (2 << 24))) == ALIAS
+
+
+def test_buffer_checks_use_each_tensors_head_size(L):
+    """With D != Dv, q/k/dq/dk span T*D and v/o/dout/dv span T*Dv elements per
+    head: overlaps are judged on those spans. Every call below is rejected."""
+    p = prob(D=32, Dv=128)
+    tk, tv = 2 * 3 * 100 * 32 * 2, 2 * 3 * 100 * 128 * 2
+    need = L.la_workspace_bytes(ctypes.byref(p))
+    assert L.la_state_bytes(ctypes.byref(p)) == 6 * (32 * 128 + 32) * 4
+    # o placed tk bytes after v: apart if v spanned tk bytes, but v spans tv
+    v = ctypes.c_void_p(A + (2 << 24))
+    assert fwd_call(L, p, v=v, o=ctypes.c_void_p(A + (2 << 24) + tk)) == ALIAS
+    # the state placed inside o's tv bytes, past its first tk bytes
+    assert fwd_call(L, p, state=ctypes.c_void_p(A + (3 << 24) + tk + 256)) == ALIAS
+    d = addrs(9)
+
+    def bwd_call(**kw):
+        args = dict(q=d[0], k=d[1], v=d[2], do=d[3], state=d[4], dq=d[5], dk=d[6], dv=d[7], ws=d[8])
+        args.update(kw)
+        return L.la_bwd(ctypes.byref(p), args["q"], args["k"], args["v"], args["do"], args["state"],
+                        args["dq"], args["dk"], args["dv"], args["ws"], need, None)
+
+    # dq (tk bytes) placed inside dout's tv bytes, past its first tk bytes
+    assert bwd_call(dq=ctypes.c_void_p(A + (3 << 24) + tk + 256)) == ALIAS
+    # dv (tv bytes) starting just before dk ends
+    assert bwd_call(dv=ctypes.c_void_p(A + (6 << 24) + tk - 16)) == ALIAS
+    # dk (tk bytes) starting inside v's tv bytes
+    assert bwd_call(dk=ctypes.c_void_p(A + (2 << 24) + tv - 16)) == ALIAS
 
 
 def test_empty_problems_need_no_device(L):
