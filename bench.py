@@ -29,7 +29,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 import non_causal_linear_amd as la  # noqa: E402
-from synth import HEADLINE, WORKLOADS, make_inputs  # noqa: E402
+from synth import HEAD_SIZE_WORKLOADS, HEADLINE, WORKLOADS, make_inputs  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
 # FBi-LA README, "Benchmarks" (A800 80G, B8-H16-D64, T = 16384), in ms.
@@ -37,10 +37,16 @@ PAGE_A800_FWD_MS = 0.980992
 PAGE_A800_BWD_MS = 5.022208
 
 KERNELS = ("fwd_state", "fwd_output", "bwd_dq", "bwd_dkv")
-# Algorithmic HBM traffic per launch, in tensors of N = B*H*T*D elements:
-# state reads K, V; output reads Q, writes O; dq reads Q, dO, writes dQ;
-# dkv reads K, V, writes dK, dV.
-TENSORS_PER_LAUNCH = {"fwd_state": 2, "fwd_output": 2, "bwd_dq": 3, "bwd_dkv": 4}
+ALL_WORKLOADS = {**WORKLOADS, **HEAD_SIZE_WORKLOADS}
+
+
+def launch_bytes(w) -> dict:
+    """Algorithmic HBM bytes per launch: each tensor read or written once.
+    Q-side tensors (Q, K, dQ, dK) hold B*H*T*D elements, V-side ones (V, O,
+    dO, dV) B*H*T*Dv. state reads K, V; output reads Q, writes O; dq reads Q,
+    dO, writes dQ; dkv reads K, V, writes dK, dV."""
+    nk, nv = w.numel * w.elem_bytes, w.numel_v * w.elem_bytes
+    return {"fwd_state": nk + nv, "fwd_output": nk + nv, "bwd_dq": 2 * nk + nv, "bwd_dkv": 2 * nk + 2 * nv}
 DTYPE_NAME = {"f32": "f32", "f16": "f16", "bf16": "bf16"}
 
 
@@ -62,7 +68,8 @@ def cpu_baseline(w, x, max_heads: int) -> dict:
     heads = min(n, max_heads)
     cores = len(os.sched_getaffinity(0))
     cores = max(1, min(cores, 16))
-    qh, kh, vh, dh = (x[nm].reshape(n, w.T, w.D) for nm in ("q", "k", "v", "do"))
+    qh, kh = (x[nm].reshape(n, w.T, w.D) for nm in ("q", "k"))
+    vh, dh = (x[nm].reshape(n, w.T, w.dv) for nm in ("v", "do"))
 
     def fwd_one(h):
         return oracle.fwd_head(oracle.decode(qh[h], w.dtype), oracle.decode(kh[h], w.dtype),
@@ -80,7 +87,7 @@ def cpu_baseline(w, x, max_heads: int) -> dict:
         t1 = time.perf_counter()
         list(pool.map(bwd_one, range(heads)))
         t2 = time.perf_counter()
-    fwd_bytes = 4 * heads * w.T * w.D * w.elem_bytes
+    fwd_bytes = 2 * heads * w.T * (w.D + w.dv) * w.elem_bytes
     model = ""
     try:
         for line in open("/proc/cpuinfo"):
@@ -94,7 +101,7 @@ def cpu_baseline(w, x, max_heads: int) -> dict:
         "unit": "GB/s",
         "cores": cores,
         "kind": "oracle",
-        "sample": f"{heads} of {n} heads at T={w.T}, D={w.D}: fp64 forward then backward, "
+        "sample": f"{heads} of {n} heads at T={w.T}, D={w.D}, Dv={w.dv}: fp64 forward then backward, "
                   f"one head per thread",
         "fwd_ms_sample": (t1 - t0) * 1e3,
         "bwd_ms_sample": (t2 - t1) * 1e3,
@@ -107,7 +114,7 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default=HEADLINE, choices=list(WORKLOADS))
+    ap.add_argument("--workload", default=HEADLINE, choices=list(ALL_WORKLOADS))
     ap.add_argument("--flush", choices=("read", "write", "none"), default="read",
                     help="cache flush before each step: read 1 GiB (default), write 1 GiB, or none")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -128,15 +135,16 @@ def main() -> int:
         return 2
     assert torch.cuda.is_available(), "bench.py needs a GPU"
 
-    w = WORKLOADS[args.workload]
+    w = ALL_WORKLOADS[args.workload]
     print(f"[bench] workload {w.name}: generating inputs", file=sys.stderr, flush=True)
     x = make_inputs(w, with_grad=True)
     dev = {n: to_device(a, w.dtype) for n, a in x.items()}
     q, k, v, do = dev["q"], dev["k"], dev["v"], dev["do"]
-    prob = la.make_problem(q.shape, q.dtype, w.eps, w.simple)
+    prob = la.make_problem(q.shape, q.dtype, w.eps, w.simple, dv=w.dv)
     state = la.new_state(prob, q.device)
     ws = la.workspace(prob, q.device)
-    o, dq, dk, dv = (torch.empty_like(q) for _ in range(4))
+    o, dv = torch.empty_like(v), torch.empty_like(v)
+    dq, dk = torch.empty_like(q), torch.empty_like(q)
     flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda")  # 1 GiB
 
     def do_flush(mode):
@@ -199,14 +207,13 @@ def main() -> int:
         per = {kname: per[kname] for kname in ("fwd_state", "fwd_output")}
     step_ms = np.array([ev[0].elapsed_time(ev[4]) for ev in events])
     fwd_ms = per["fwd_state"] + per["fwd_output"]
-    N = w.numel
-    elt = w.elem_bytes
-    fwd_bytes = 4 * N * elt
+    lb = launch_bytes(w)
+    fwd_bytes = lb["fwd_state"] + lb["fwd_output"]
     value = fwd_bytes / (float(np.mean(fwd_ms)) * 1e-3) / 1e9
 
     avg = {kname: float(np.mean(a)) for kname, a in per.items()}
     dominant = max(avg, key=avg.get)
-    dom_bytes = TENSORS_PER_LAUNCH[dominant] * N * elt
+    dom_bytes = lb[dominant]
     achieved = dom_bytes / (avg[dominant] * 1e-3) / 1e9
 
     if args.copy_calibration:
@@ -230,7 +237,7 @@ def main() -> int:
         "data": "synthetic: seeded N(0, sigma^2) Q, K, V, dO rounded to the dtype",
         "config": {
             "workload": w.name + ("-simple" if w.simple and "simple" not in w.name else ""),
-            "B": w.B, "H": w.H, "T": w.T, "D": w.D,
+            "B": w.B, "H": w.H, "T": w.T, "D": w.D, "Dv": w.dv,
             "mode": "simple_la" if w.simple else "normalised",
             "eps": w.eps,
             "pass": "fwd+bwd" if w.bwd else "fwd",

@@ -6,14 +6,17 @@
 //   S = sum_t phi(k_t) v_t^T,  z = sum_t phi(k_t),
 //   O_t = phi(q_t) S / (phi(q_t) . z + eps)     (simple_la: phi(q_t) S).
 //
+// Q and K have head size DK, V and O head size DV (each 32, 64, 96 or 128).
 // Kernels, by step of the path:
-//   fwd_state_w64_kernel (16-bit, D = 64) and fwd_state_kernel (the rest):
+//   fwd_state_w64_kernel (16-bit, DK = DV = 64), fwd_state_tile_kernel (the
+//                      other 16-bit sizes) and fwd_state_kernel (fp32):
 //                      phi(K)^T [V | 1] over a token slice on MFMA, one partial
 //                      (S, z) per slice, or the state itself when a head is
 //                      one slice;
 //   combine_kernel     sums the partials of each head in ascending slice order;
 //   fwd_output_kernel  O = phi(Q) S / (phi(Q) z + eps), S and z as MFMA operands;
-//   bwd_dq_w64_kernel (16-bit, D = 64) and bwd_dq_kernel (the rest): dQ, plus
+//   bwd_dq_w64_kernel (16-bit, DK = DV = 64), bwd_dq_tile_kernel (the other
+//                      16-bit sizes) and bwd_dq_kernel (fp32): dQ, plus
 //                      partial dS = phi(Q)^T (dO / den) on MFMA and
 //                      dz = sum_t c_t phi(q_t), combined like the forward state;
 //   bwd_dkv_kernel     dK = (V dS^T + dz) * phi'(K), dV = phi(K) dS.
@@ -29,9 +32,9 @@
 // permuted so that the same lane receives D/4 contiguous output features of
 // that token, which it stores contiguously.
 //
-// Tensors are [B, H, T, D] row-major. The work split is a pure function of the
-// shape and there are no floating-point atomics, so results are bit-identical
-// across runs.
+// Tensors are [B, H, T, D] (or [B, T, H, D]) row-major. The work split is a
+// pure function of the shape and there are no floating-point atomics, so
+// results are bit-identical across runs.
 
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -857,108 +860,127 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_state_w64_kernel(
     }
 }
 
-// Steps 1-3 for 16-bit inputs at D = 128, where one wave cannot hold all of
-// S. The four waves share 64-token tiles: every thread loads its part of a
-// tile (full 256-byte rows per wave instruction), applies phi to K and writes
-// both tiles row-major to LDS; after one barrier each wave reduces the tile
-// into its own 32 rows of S, and of z through an all-ones B block, with
-// 16x16x32 MFMAs on transposed LDS reads. Tiles alternate between two LDS
-// buffers, so the one barrier per tile orders both that tile's writes before
-// its reads and the earlier reads of the other buffer before it is written
-// again. Two tiles of loads are in flight; tiles go in rotated order with no
-// early exit, and rows past the slice end load as zeros with phi(k) masked.
-struct StateC128 {
-    static constexpr int kTile = 64;   // tokens per tile
-    static constexpr int kLDR = 144;   // LDS row stride (elements): 288-byte rows
-    static constexpr int kStages = 2;  // tiles of loads in flight
+// Steps 1-3 for 16-bit inputs, any (DK, DV): 64-token tiles of K and V
+// staged row-major in LDS, double-buffered with one barrier per tile, the
+// next two tiles' loads in flight. Each thread loads the tile's 16-byte
+// chunks in order (chunk n: row n / chunks-per-row) and writes them to LDS as
+// they are, K through phi; MFMA operands come from transposed LDS reads
+// (A = phi(K)^T: feature x token, B = V: token x feature). The four waves
+// split S two by two (wave w: row half w % 2, column half w / 2); the waves of
+// column half 0 also multiply by a block of ones, which gives z from the same
+// rounded phi(k). Rows past the slice end read as zeros (slice descriptors)
+// and are zeroed after phi.
+template <int DK, int DV>
+struct StateTile {
+    static constexpr int kTile = 64;     // tokens per tile
+    // LDS row strides (elements): D + 16 puts four consecutive rows at least
+    // 8 banks apart, so a transposed read of 4 rows x 32 bytes hits distinct banks
+    static constexpr int kLDK = DK + 16;
+    static constexpr int kLDV = DV + 16;
+    static constexpr int kStages = 2;    // tiles of loads in flight
+    static constexpr int kNI = DK / 32;  // 16-row blocks of S per wave
+    static constexpr int kNJ = DV / 32;  // 16-column blocks of S per wave
 };
 
-template <typename T, int FM>
-__global__ __launch_bounds__(kThreads, 2) void fwd_state_c128_kernel(
+template <typename T, int DK, int DV, int FM>
+__global__ __launch_bounds__(kThreads, 2) void fwd_state_tile_kernel(
     const T* __restrict__ k, const T* __restrict__ v, float* __restrict__ stS,
     float* __restrict__ stz, float* __restrict__ part, int64_t T_, const Layout lay, int P,
     int64_t L) {
-    constexpr int D = 128, NB = D / 16, NI = NB / kWaves, TT = StateC128::kTile, LDR = StateC128::kLDR;
-    constexpr int CPR = D * (int)sizeof(T) / 16;  // 16-byte chunks per row
-    constexpr int RPP = kThreads / CPR;           // rows per pass of the workgroup
-    constexpr int CPT = TT / RPP;                 // chunks per thread per tensor and tile
-    constexpr int BUF = TT * LDR;
-    static_assert(StateC128::kStages == 2, "the loop below is written for two stages");
-    __shared__ __attribute__((aligned(16))) T sK[2 * BUF];
-    __shared__ __attribute__((aligned(16))) T sV[2 * BUF];
+    using Sh = StateTile<DK, DV>;
+    constexpr int TT = Sh::kTile, LDK = Sh::kLDK, LDV = Sh::kLDV, NI = Sh::kNI, NJ = Sh::kNJ;
+    constexpr int CK = DK * (int)sizeof(T) / 16, CV = DV * (int)sizeof(T) / 16;  // chunks per row
+    constexpr int NCK = TT * CK / kThreads, NCV = TT * CV / kThreads;           // per thread per tile
+    constexpr int BUFK = TT * LDK, BUFV = TT * LDV;
+    static_assert(sizeof(T) == 2, "transposed LDS reads take 16-bit elements");
+    static_assert(NCK * kThreads == TT * CK && NCV * kThreads == TT * CV, "tile must split evenly");
+    static_assert(Sh::kStages == 2, "the loop below is written for two stages");
+    __shared__ __attribute__((aligned(16))) T sK[2 * BUFK];
+    __shared__ __attribute__((aligned(16))) T sV[2 * BUFV];
 
     const int wid = xcd_remap(blockIdx.x, gridDim.x);
     const int64_t bh = wid / P;
     const int p = wid % P;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int m = lane & 15, grp = lane >> 4;
-    const int c = tid % CPR, r0 = tid / CPR;
+    const int wi = wave & 1, wj = wave >> 1;
     const int64_t t0 = (int64_t)p * L;
     const int64_t t1 = min(t0 + L, T_);
     const int64_t len = t1 - t0;
     const int ntiles = (int)(len > 0 ? (len + TT - 1) / TT : 0);
+    const Layout lk = lay, lv = v_layout<DK, DV>(lay);
 
-    f32x4 acc[NI][NB + 1];
+    f32x4 acc[NI][NJ + 1];  // column NJ: z (waves of column half 0)
 #pragma unroll
     for (int ii = 0; ii < NI; ++ii)
 #pragma unroll
-        for (int j = 0; j <= NB; ++j) acc[ii][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j <= NJ; ++j) acc[ii][j] = f32x4{0.f, 0.f, 0.f, 0.f};
     Frag<T> ones;
 #pragma unroll
     for (int e = 0; e < 8; ++e) ones[e] = static_cast<T>(1.f);
 
     struct Stage {
-        u32x4 k[CPT], v[CPT];
+        u32x4 k[NCK], v[NCV];
     };
-    const HeadBuf bk = slice_buf(k, lay, bh, D, t0, t1), bv = slice_buf(v, lay, bh, D, t0, t1);
-    const Rotation rot(ntiles, StateC128::kStages, wid);
+    const HeadBuf bk = slice_buf(k, lk, bh, DK, t0, t1), bv = slice_buf(v, lv, bh, DV, t0, t1);
+    const Rotation rot(ntiles, Sh::kStages, wid);
     auto issue = [&](Stage& st, int tile) {
         const int row0 = rot(tile) * TT;
 #pragma unroll
-        for (int i = 0; i < CPT; ++i) {
-            const int off = buf_off<T>((int64_t)row0 + r0 + RPP * i, lay.rs, 8 * c);
-            st.k[i] = __builtin_amdgcn_raw_buffer_load_b128(bk.rsrc, off, 0, 0);
-            st.v[i] = __builtin_amdgcn_raw_buffer_load_b128(bv.rsrc, off, 0, 0);
+        for (int i = 0; i < NCK; ++i) {
+            const int n = tid + kThreads * i, r = n / CK, c = n % CK;
+            st.k[i] = __builtin_amdgcn_raw_buffer_load_b128(bk.rsrc, buf_off<T>((int64_t)row0 + r, lk.rs, 8 * c), 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < NCV; ++i) {
+            const int n = tid + kThreads * i, r = n / CV, c = n % CV;
+            st.v[i] = __builtin_amdgcn_raw_buffer_load_b128(bv.rsrc, buf_off<T>((int64_t)row0 + r, lv.rs, 8 * c), 0, 0);
         }
     };
     auto consume = [&](const Stage& st, int tile, int buf) {
         const int64_t row0 = (int64_t)rot(tile) * TT;
-        T* dK = sK + buf * BUF;
-        T* dV = sV + buf * BUF;
+        T* dK = sK + buf * BUFK;
+        T* dV = sV + buf * BUFV;
 #pragma unroll
-        for (int i = 0; i < CPT; ++i) {
-            const int row = r0 + RPP * i;
-            const bool ok = row0 + row < len;
+        for (int i = 0; i < NCK; ++i) {
+            const int n = tid + kThreads * i, r = n / CK, c = n % CK;
+            const bool ok = row0 + r < len;
             Row<T, 8> kin, kt;
             __builtin_memcpy(kin.e, &st.k[i], sizeof(kin));
 #pragma unroll
             for (int e = 0; e < 8; ++e) kt.e[e] = ok ? static_cast<T>(phi<FM, T>(to_f32(kin.e[e]))) : static_cast<T>(0.f);
-            *reinterpret_cast<Row<T, 8>*>(&dK[row * LDR + 8 * c]) = kt;
-            *reinterpret_cast<u32x4*>(&dV[row * LDR + 8 * c]) = st.v[i];
+            *reinterpret_cast<Row<T, 8>*>(&dK[r * LDK + 8 * c]) = kt;
+        }
+#pragma unroll
+        for (int i = 0; i < NCV; ++i) {
+            const int n = tid + kThreads * i, r = n / CV, c = n % CV;
+            *reinterpret_cast<u32x4*>(&dV[r * LDV + 8 * c]) = st.v[i];
         }
     };
     const int rA = 8 * grp + (m >> 2), cA = 4 * (m & 3);
     auto mma_tile = [&](int buf) {
-        const T* K_ = sK + buf * BUF;
-        const T* V_ = sV + buf * BUF;
+        const T* K_ = sK + buf * BUFK;
+        const T* V_ = sV + buf * BUFV;
 #pragma unroll
         for (int ks = 0; ks < TT / 32; ++ks) {
             const int rb = 32 * ks + rA;
             Frag<T> a[NI];
 #pragma unroll
             for (int ii = 0; ii < NI; ++ii) {
-                const int col = 16 * (wave * NI + ii) + cA;
-                a[ii] = join_frag<T>(lds_read_tr(&K_[rb * LDR + col]), lds_read_tr(&K_[(rb + 4) * LDR + col]));
+                const int col = 16 * (wi * NI + ii) + cA;
+                a[ii] = join_frag<T>(lds_read_tr(&K_[rb * LDK + col]), lds_read_tr(&K_[(rb + 4) * LDK + col]));
             }
 #pragma unroll
-            for (int j = 0; j < NB; ++j) {
-                const Frag<T> b = join_frag<T>(lds_read_tr(&V_[rb * LDR + 16 * j + cA]),
-                                               lds_read_tr(&V_[(rb + 4) * LDR + 16 * j + cA]));
+            for (int jj = 0; jj < NJ; ++jj) {
+                const int col = 16 * (wj * NJ + jj) + cA;
+                const Frag<T> b = join_frag<T>(lds_read_tr(&V_[rb * LDV + col]), lds_read_tr(&V_[(rb + 4) * LDV + col]));
 #pragma unroll
-                for (int ii = 0; ii < NI; ++ii) acc[ii][j] = mma(a[ii], b, acc[ii][j]);
+                for (int ii = 0; ii < NI; ++ii) acc[ii][jj] = mma(a[ii], b, acc[ii][jj]);
             }
+            if (wj == 0) {
 #pragma unroll
-            for (int ii = 0; ii < NI; ++ii) acc[ii][NB] = mma(a[ii], ones, acc[ii][NB]);
+                for (int ii = 0; ii < NI; ++ii) acc[ii][NJ] = mma(a[ii], ones, acc[ii][NJ]);
+            }
         }
     };
 
@@ -987,22 +1009,22 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_state_c128_kernel(
     float* oS;
     float* oz;
     if (P == 1) {
-        oS = stS + bh * D * D;
-        oz = stz + bh * D;
+        oS = stS + bh * DK * DV;
+        oz = stz + bh * DK;
     } else {
-        oS = part + (bh * P + p) * (int64_t)(D * D + D);
-        oz = oS + D * D;
+        oS = part + (bh * P + p) * (int64_t)(DK * DV + DK);
+        oz = oS + DK * DV;
     }
 #pragma unroll
     for (int ii = 0; ii < NI; ++ii) {
-        const int i0 = (wave * NI + ii) * 16 + 4 * grp;
+        const int i0 = (wi * NI + ii) * 16 + 4 * grp;
 #pragma unroll
-        for (int j = 0; j < NB; ++j)
+        for (int jj = 0; jj < NJ; ++jj)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) oS[(i0 + r) * D + j * 16 + m] = acc[ii][j][r];
-        if (m == 0)
+            for (int r = 0; r < 4; ++r) oS[(i0 + r) * DV + (wj * NJ + jj) * 16 + m] = acc[ii][jj][r];
+        if (wj == 0 && m == 0)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) oz[i0 + r] = acc[ii][NB][r];
+            for (int r = 0; r < 4; ++r) oz[i0 + r] = acc[ii][NJ][r];
     }
 }
 
@@ -1721,8 +1743,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_w64_kernel(
     }
 }
 
-// Steps 5-6 for 16-bit inputs, one wave per 16 rows of dS: D / 16 waves take
-// the 16-token steps of a round of D tokens, each with two rounds of Q and dO
+// Steps 5-6 for 16-bit inputs, one wave per 16 rows of dS: DK / 16 waves take
+// the 16-token steps of a round of DK tokens, each with two rounds of Q and dO
 // loads in flight. Per step a wave computes u = S dO_t, den and dQ (staged
 // for full-line stores through its own rows of the round tile), then writes
 // A_t = phi(q_t) 2^sw / den_t, the raw dO_t and beta_t = -r_t / den_t to the
@@ -1732,41 +1754,46 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_w64_kernel(
 // with 16x16x32 MFMAs on transposed LDS reads; a second barrier frees the
 // tile for the next round. Rounds go in rotated order with no early exit;
 // rows past the slice end load as zeros and add nothing.
-template <int D>
+template <int DK, int DV>
 struct BwdQTile {
-    static constexpr int kWaves = D / 16;
+    static constexpr int kWaves = DK / 16;
     static constexpr int kThreads = 64 * kWaves;
     static constexpr int kStep = 16;                // tokens per wave step
     static constexpr int kRound = kStep * kWaves;   // tokens per round
-    // tile row stride (elements) with the beta block after D columns; four
-    // consecutive rows start 8 or more banks apart, so a transposed read of
-    // 4 rows x 32 bytes hits distinct banks
-    static constexpr int kLDR = D == 64 ? 80 : 144;
+    // tile row strides (elements), the beta block after DV columns of the W
+    // tile; D + 16 puts four consecutive rows 8 or more banks apart, so a
+    // transposed read of 4 rows x 32 bytes hits distinct banks
+    static constexpr int kLDA = DK + 16;
+    static constexpr int kLDW = DV + 16;
     static constexpr int kStages = 2;               // rounds of loads in flight
-    static constexpr int kMinBlocks = D == 64 ? 3 : 1;
+    static constexpr int kMinBlocks = DK == 128 ? 1 : 2;
 };
 
-template <typename T, int D, bool SIMPLE, int FM>
-__global__ __launch_bounds__(BwdQTile<D>::kThreads, BwdQTile<D>::kMinBlocks) void bwd_dq_tile_kernel(
+template <typename T, int DK, int DV, bool SIMPLE, int FM>
+__global__ __launch_bounds__((BwdQTile<DK, DV>::kThreads), (BwdQTile<DK, DV>::kMinBlocks)) void bwd_dq_tile_kernel(
     const T* __restrict__ q, const T* __restrict__ dout, const float* __restrict__ stS,
     const float* __restrict__ stz, T* __restrict__ dq, float* __restrict__ part,
     float* __restrict__ dS_out, float* __restrict__ dz_out, int64_t T_, const Layout lay, int PB,
     int64_t LB, float eps) {
-    using Sh = BwdQTile<D>;
-    constexpr int F = D / 4, NB = D / 16, KS = D / 32, E = D * D + D;
+    using Sh = BwdQTile<DK, DV>;
+    constexpr int FK = DK / 4, FV = DV / 4, NBK = DK / 16, NBV = DV / 16, KSK = DK / 32, KSV = DV / 32;
+    constexpr int E = DK * DV + DK;
     constexpr int NW = Sh::kWaves, NT = Sh::kThreads, STEP = Sh::kStep;
-    constexpr int RT = Sh::kRound, LDR = Sh::kLDR;
-    constexpr int NJ = NB + (SIMPLE ? 0 : 1);  // dS column blocks (+ dz)
-    constexpr int NFS = NB * KS;
-    constexpr int NFR = NFS + (SIMPLE ? 0 : KS);
-    constexpr int NW16 = F * (int)sizeof(T) / 16;  // 16-byte words per quarter row
+    constexpr int RT = Sh::kRound, LDA = Sh::kLDA, LDW = Sh::kLDW;
+    constexpr int NJ = NBV + (SIMPLE ? 0 : 1);  // dS column blocks (+ dz)
+    constexpr int NFS = NBK * KSV;
+    constexpr int NFR = NFS + (SIMPLE ? 0 : KSK);
+    constexpr int NQK = FK * (int)sizeof(T) / 16;  // 16-byte words per quarter row of Q
+    constexpr int NQV = FV * (int)sizeof(T) / 16;  // ... of dO
     constexpr int kFragBytes = NFR * 64 * 16;
-    constexpr int kTileBytes = 2 * RT * LDR * (int)sizeof(T);  // A tile, then W tile
-    static_assert(StagedState<D, D>::kFloats * 4 <= kTileBytes, "state staging exceeds the tile area");
+    constexpr int kTileBytes = RT * (LDA + LDW) * (int)sizeof(T);  // A tile, then W tile
+    constexpr int kStBytes = StagedState<DK, DV>::kFloats * 4;
+    constexpr int kAreaBytes = kTileBytes > kStBytes ? kTileBytes : kStBytes;
+    static_assert(sizeof(T) == 2, "transposed LDS reads take 16-bit elements");
     static_assert(Sh::kStages == 2, "the loop below is written for two stages");
-    __shared__ __attribute__((aligned(16))) unsigned char smem[kFragBytes + kTileBytes];
+    __shared__ __attribute__((aligned(16))) unsigned char smem[kFragBytes + kAreaBytes];
     __shared__ float red[3 * NW];
-    __shared__ __attribute__((aligned(16))) float sZ[D];
+    __shared__ __attribute__((aligned(16))) float sZ[DK];
 
     const int wid = xcd_remap(blockIdx.x, gridDim.x);
     const int64_t bh = wid / PB;
@@ -1776,19 +1803,20 @@ __global__ __launch_bounds__(BwdQTile<D>::kThreads, BwdQTile<D>::kMinBlocks) voi
     const int nrounds = (int)(t1 > t0 ? (t1 - t0 + RT - 1) / RT : 0);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int m = lane & 15, grp = lane >> 4;
-    const float* S = stS + bh * D * D;
-    const float* z = stz + bh * D;
+    const Layout lk = lay, lv = v_layout<DK, DV>(lay);
+    const float* S = stS + bh * DK * DV;
+    const float* z = stz + bh * DK;
     Frag<T>* sA = reinterpret_cast<Frag<T>*>(smem);
     T* tA = reinterpret_cast<T*>(smem + kFragBytes);
-    T* tW = tA + RT * LDR;
+    T* tW = tA + RT * LDA;
 
     // The state is staged in the tile area (which the rounds alone use) and
     // the fragments are built from there.
     int sS = 0, sz = 0, sw = 0;
     {
-        constexpr int LD = StagedState<D, D>::kLD;
+        constexpr int LD = StagedState<DK, DV>::kLD;
         float* sSt = reinterpret_cast<float*>(tA);
-        const StagedState<D, D> st = stage_state<D, D, NT>(S, z, sSt, red);
+        const StagedState<DK, DV> st = stage_state<DK, DV, NT>(S, z, sSt, red);
         if constexpr (Elt<T>::kScaled) {
             sS = scale_exp(st.max_m);
             sz = scale_exp(st.max_z);
@@ -1801,11 +1829,12 @@ __global__ __launch_bounds__(BwdQTile<D>::kThreads, BwdQTile<D>::kMinBlocks) voi
             }
         }
         const float fS = ldexpf(1.f, sS), fz = ldexpf(1.f, sz);
-        build_frags<T, NFR, NW>(sA, [&](int f) {
-            return f < NFS ? build_frag<T, D, D, false, LD>(sSt, f / KS, f % KS, m, grp, fS)
-                           : build_zfrag<T, D>(sSt + D * LD, max(f - NFS, 0), grp, fz);
+        // captures by value (see the generic dQ kernel)
+        build_frags<T, NFR, NW>(sA, [=](int f) {
+            return f < NFS ? build_frag<T, DK, DV, false, LD>(sSt, f / KSV, f % KSV, m, grp, fS)
+                           : build_zfrag<T, DK>(sSt + DK * LD, max(f - NFS, 0), grp, fz);
         });
-        for (int i = tid; i < D; i += NT) sZ[i] = sSt[D * LD + i];
+        for (int i = tid; i < DK; i += NT) sZ[i] = sSt[DK * LD + i];
     }
     __syncthreads();
     const float uS = ldexpf(1.f, -sS), uz = ldexpf(1.f, -sz), fw = ldexpf(1.f, sw);
@@ -1816,56 +1845,57 @@ __global__ __launch_bounds__(BwdQTile<D>::kThreads, BwdQTile<D>::kMinBlocks) voi
 
     // The loaded words as they are (see the D = 64 kernel).
     struct Stage {
-        u32x4 q[NW16], d[NW16];
+        u32x4 q[NQK], d[NQV];
     };
-    const HeadBuf bq = slice_buf(q, lay, bh, D, t0, t1), bd = slice_buf(dout, lay, bh, D, t0, t1),
-                  bdq = slice_buf(dq, lay, bh, D, t0, t1);
+    const HeadBuf bq = slice_buf(q, lk, bh, DK, t0, t1), bd = slice_buf(dout, lv, bh, DV, t0, t1),
+                  bdq = slice_buf(dq, lk, bh, DK, t0, t1);
     const Rotation rot(nrounds, Sh::kStages, wid);
     auto issue = [&](Stage& st, int round) {
-        const int off = buf_off<T>((int64_t)rot(round) * RT + wave * STEP + m, lay.rs, F * grp);
+        const int64_t row = (int64_t)rot(round) * RT + wave * STEP + m;
+        const int oq = buf_off<T>(row, lk.rs, FK * grp), od = buf_off<T>(row, lv.rs, FV * grp);
 #pragma unroll
-        for (int i = 0; i < NW16; ++i) {
-            st.q[i] = __builtin_amdgcn_raw_buffer_load_b128(bq.rsrc, off + 16 * i, 0, 0);
-            st.d[i] = __builtin_amdgcn_raw_buffer_load_b128(bd.rsrc, off + 16 * i, 0, 0);
+        for (int i = 0; i < (NQK > NQV ? NQK : NQV); ++i) {
+            if (i < NQK) st.q[i] = __builtin_amdgcn_raw_buffer_load_b128(bq.rsrc, oq + 16 * i, 0, 0);
+            if (i < NQV) st.d[i] = __builtin_amdgcn_raw_buffer_load_b128(bd.rsrc, od + 16 * i, 0, 0);
         }
     };
     const int rA = 8 * grp + (m >> 2), cA = 4 * (m & 3);
     const int row = wave * STEP + m;  // this lane's token within the round tile
     auto body = [&](Stage& st, int round) {
         sched_fence();
-        Row<T, F> lq;
+        Row<T, FK> lq;
         __builtin_memcpy(lq.e, st.q, sizeof(lq));
-        float qt[F];
-        Frag<T> bqf[KS], bdf[KS];
+        float qt[FK];
+        Frag<T> bqf[KSK], bdf[KSV];
 #pragma unroll
-        for (int o = 0; o < F; ++o) qt[o] = phi<FM, T>(to_f32(lq.e[o]));
+        for (int o = 0; o < FK; ++o) qt[o] = phi<FM, T>(to_f32(lq.e[o]));
+        if constexpr (!SIMPLE)
 #pragma unroll
-        for (int s = 0; s < KS; ++s) {
-            if constexpr (!SIMPLE)
+            for (int s = 0; s < KSK; ++s)
 #pragma unroll
                 for (int e = 0; e < 8; ++e) bqf[s][e] = static_cast<T>(qt[8 * s + e]);
-            bdf[s] = __builtin_bit_cast(Frag<T>, st.d[s]);
-        }
+#pragma unroll
+        for (int s = 0; s < KSV; ++s) bdf[s] = __builtin_bit_cast(Frag<T>, st.d[s]);
         // den first, so that the phi(q) fragments are dead before u
         float inv = 1.f;
         if constexpr (!SIMPLE) {
             f32x4 ad = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int s = 0; s < KS; ++s) ad = mma(sA[(NFS + s) * 64 + lane], bqf[s], ad);
+            for (int s = 0; s < KSK; ++s) ad = mma(sA[(NFS + s) * 64 + lane], bqf[s], ad);
             inv = 1.f / (ad[0] * uz + eps);
         }
-        f32x4 au[NB];
+        f32x4 au[NBK];
 #pragma unroll
-        for (int b = 0; b < NB; ++b) {
+        for (int b = 0; b < NBK; ++b) {
             au[b] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int s = 0; s < KS; ++s) au[b] = mma(sA[(b * KS + s) * 64 + lane], bdf[s], au[b]);
+            for (int s = 0; s < KSV; ++s) au[b] = mma(sA[(b * KSV + s) * 64 + lane], bdf[s], au[b]);
         }
         // dO rows go to the round tile as loaded; then the stage is free
         {
-            u32x4* dw = reinterpret_cast<u32x4*>(&tW[row * LDR + F * grp]);
+            u32x4* dw = reinterpret_cast<u32x4*>(&tW[row * LDW + FV * grp]);
 #pragma unroll
-            for (int i = 0; i < NW16; ++i) dw[i] = st.d[i];
+            for (int i = 0; i < NQV; ++i) dw[i] = st.d[i];
         }
         sched_fence();
         issue(st, round + Sh::kStages);
@@ -1875,7 +1905,7 @@ __global__ __launch_bounds__(BwdQTile<D>::kThreads, BwdQTile<D>::kMinBlocks) voi
         if constexpr (!SIMPLE) {
             float rr = 0.f;
 #pragma unroll
-            for (int b = 0; b < NB; ++b)
+            for (int b = 0; b < NBK; ++b)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) rr += qt[4 * b + r] * au[b][r];
             rr += __shfl_xor(rr, 16);
@@ -1884,40 +1914,41 @@ __global__ __launch_bounds__(BwdQTile<D>::kThreads, BwdQTile<D>::kMinBlocks) voi
             cc = beta * inv;                      // -r / den^2
             ku = uS * inv;
             aq = fw * inv;
-            if (grp == 0) tW[row * LDR + D] = static_cast<T>(beta);
+            if (grp == 0) tW[row * LDW + DV] = static_cast<T>(beta);
         }
         sched_fence();
         {
-            Row<T, F> out;
-            const float* zl = &sZ[F * grp];
+            Row<T, FK> out;
+            const float* zl = &sZ[FK * grp];
 #pragma unroll
-            for (int b = 0; b < NB; ++b)
+            for (int b = 0; b < NBK; ++b)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int o = 4 * b + r;
                     const float dqt = SIMPLE ? au[b][r] * ku : au[b][r] * ku + cc * zl[o];
                     out.e[o] = static_cast<T>(dqt * dphi_of<FM>(qt[o]));
                 }
-            // staged through this wave's own rows of the A tile, which are
-            // written with A right after
-            store_tile_rows<T, D>(tA + wave * STEP * LDR, out, bdq, (int64_t)rot(round) * RT + wave * STEP, lay.rs);
+            // staged through this wave's own rows of the A tile (16 rows of
+            // DK + 8 elements fit in its 16 rows of LDA), which are written
+            // with A right after
+            store_tile_rows<T, DK>(tA + wave * STEP * LDA, out, bdq, (int64_t)rot(round) * RT + wave * STEP, lk.rs);
         }
         {
-            Row<T, F> rq;
+            Row<T, FK> rq;
 #pragma unroll
-            for (int o = 0; o < F; ++o) rq.e[o] = static_cast<T>(qt[o] * aq);
-            *reinterpret_cast<Row<T, F>*>(&tA[row * LDR + F * grp]) = rq;
+            for (int o = 0; o < FK; ++o) rq.e[o] = static_cast<T>(qt[o] * aq);
+            *reinterpret_cast<Row<T, FK>*>(&tA[row * LDA + FK * grp]) = rq;
         }
         __syncthreads();
 #pragma unroll
         for (int ks = 0; ks < RT / 32; ++ks) {
             const int rb = 32 * ks + rA;
             const int col = 16 * wave + cA;
-            const Frag<T> a = join_frag<T>(lds_read_tr(&tA[rb * LDR + col]), lds_read_tr(&tA[(rb + 4) * LDR + col]));
+            const Frag<T> a = join_frag<T>(lds_read_tr(&tA[rb * LDA + col]), lds_read_tr(&tA[(rb + 4) * LDA + col]));
 #pragma unroll
             for (int j = 0; j < NJ; ++j) {
-                const Frag<T> b = join_frag<T>(lds_read_tr(&tW[rb * LDR + 16 * j + cA]),
-                                               lds_read_tr(&tW[(rb + 4) * LDR + 16 * j + cA]));
+                const Frag<T> b = join_frag<T>(lds_read_tr(&tW[rb * LDW + 16 * j + cA]),
+                                               lds_read_tr(&tW[(rb + 4) * LDW + 16 * j + cA]));
                 dsacc[j] = mma(a, b, dsacc[j]);
             }
         }
@@ -1942,16 +1973,16 @@ __global__ __launch_bounds__(BwdQTile<D>::kThreads, BwdQTile<D>::kMinBlocks) voi
     float* oS;
     float* oz;
     if (PB == 1) {
-        oS = dS_out + bh * D * D;
-        oz = dz_out + bh * D;
+        oS = dS_out + bh * DK * DV;
+        oz = dz_out + bh * DK;
     } else {
         oS = part + (bh * PB + p) * (int64_t)E;
-        oz = oS + D * D;
+        oz = oS + DK * DV;
     }
 #pragma unroll
-    for (int j = 0; j < NB; ++j)
+    for (int j = 0; j < NBV; ++j)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) oS[(16 * wave + 4 * grp + r) * D + 16 * j + m] = dsacc[j][r] * uw;
+        for (int r = 0; r < 4; ++r) oS[(16 * wave + 4 * grp + r) * DV + 16 * j + m] = dsacc[j][r] * uw;
     if (m == 0)
 #pragma unroll
         for (int r = 0; r < 4; ++r) oz[16 * wave + 4 * grp + r] = SIMPLE ? 0.f : dsacc[NJ - 1][r] * uw;
@@ -2170,7 +2201,7 @@ __global__ __launch_bounds__((StreamShape<T, DK, DV>::kThreads), (StreamShape<T,
 template <typename T, int DK, int DV>
 constexpr bool kWaveKernels = (sizeof(T) == 2 && DK == 64 && DV == 64);
 template <typename T, int DK, int DV>
-constexpr bool kTileKernels = (sizeof(T) == 2 && DK == 128 && DV == 128);
+constexpr bool kTileKernels = (sizeof(T) == 2 && !kWaveKernels<T, DK, DV>);
 
 template <typename X>
 struct Same {
@@ -2209,7 +2240,8 @@ hipError_t fwd_state_fm(const Plan& p, const void* k, const void* v, float* stat
     if constexpr (kWaveKernels<T, DK, DV>)
         e = launch(fwd_state_w64_kernel<T, FM>, nblk, kThreads, s, kk, vv, state, sz, part, p.T, p.lay, p.P, p.L);
     else if constexpr (kTileKernels<T, DK, DV>)
-        e = launch(fwd_state_c128_kernel<T, FM>, nblk, kThreads, s, kk, vv, state, sz, part, p.T, p.lay, p.P, p.L);
+        e = launch(fwd_state_tile_kernel<T, DK, DV, FM>, nblk, kThreads, s, kk, vv, state, sz, part, p.T, p.lay,
+                   p.P, p.L);
     else
         e = launch(fwd_state_kernel<T, DK, DV, FM>, nblk, kThreads, s, kk, vv, state, sz, part, p.T, p.lay, p.P,
                    p.L);
@@ -2252,11 +2284,11 @@ hipError_t bwd_dq_fm(const Plan& p, const void* q, const void* dout, const float
                      : launch(bwd_dq_w64_kernel<T, false, FM>, nblk, kThreads, s, qq, dd, sS, sz, g, part, dS, dz, p.T,
                               p.lay, p.PB, p.LB, p.eps);
     } else if constexpr (kTileKernels<T, DK, DV>) {
-        constexpr int nt = BwdQTile<DK>::kThreads;
-        e = p.simple ? launch(bwd_dq_tile_kernel<T, DK, true, FM>, nblk, nt, s, qq, dd, sS, sz, g, part, dS, dz, p.T,
-                              p.lay, p.PB, p.LB, p.eps)
-                     : launch(bwd_dq_tile_kernel<T, DK, false, FM>, nblk, nt, s, qq, dd, sS, sz, g, part, dS, dz, p.T,
-                              p.lay, p.PB, p.LB, p.eps);
+        constexpr int nt = BwdQTile<DK, DV>::kThreads;
+        e = p.simple ? launch(bwd_dq_tile_kernel<T, DK, DV, true, FM>, nblk, nt, s, qq, dd, sS, sz, g, part, dS, dz,
+                              p.T, p.lay, p.PB, p.LB, p.eps)
+                     : launch(bwd_dq_tile_kernel<T, DK, DV, false, FM>, nblk, nt, s, qq, dd, sS, sz, g, part, dS, dz,
+                              p.T, p.lay, p.PB, p.LB, p.eps);
     } else {
         e = p.simple ? launch(bwd_dq_kernel<T, DK, DV, true, FM>, nblk, kThreads, s, qq, dd, sS, sz, g, part, dS, dz,
                               p.T, p.lay, p.PB, p.LB, p.eps)
@@ -2311,17 +2343,31 @@ hipError_t bwd_dkv_t(const Plan& p, const void* k, const void* v, void* dk, void
     LA_FEATURE_MAP(bwd_dkv_fm, k, v, dk, dv, ws, s);
 }
 
+// Grid targets of the tile kernels, in workgroups: enough that each CU has
+// about 64 KB of loads in flight (a tile kernel's workgroup keeps two tiles or
+// rounds of DK + DV wide rows in flight), within 2 to 8 workgroups per CU of
+// the 256 for the state; for dQ (DK / 16 waves per workgroup) at least 8
+// waves and at most 8 workgroups per CU.
+constexpr int64_t clamp_wgs(int64_t per_cu, int64_t lo, int64_t hi) {
+    return 256 * (per_cu < lo ? lo : per_cu > hi ? hi : per_cu);
+}
+template <int DK, int DV>
+constexpr int64_t kStateTileWgs = clamp_wgs(512 / (DK + DV), 2, 8);
+template <int DK, int DV>
+constexpr int64_t kBwdQTileWgs = clamp_wgs(16384 / (DK * (DK + DV)), (128 + DK - 1) / DK, 8);
+
 template <typename T, int DK, int DV>
 SplitCfg split_config_t(int step) {
     switch (step) {
         case kStepState:
             if constexpr (kWaveKernels<T, DK, DV>) return {int64_t(StateW64::kStep) * kWaves * StateW64::kStages, 512};
-            else if constexpr (kTileKernels<T, DK, DV>) return {int64_t(StateC128::kTile) * StateC128::kStages, 512};
+            else if constexpr (kTileKernels<T, DK, DV>)
+                return {int64_t(StateTile<DK, DV>::kTile) * StateTile<DK, DV>::kStages, kStateTileWgs<DK, DV>};
             else return {StateShape<T, DK, DV>::kTT, 1024};
         case kStepBwdQ:
             if constexpr (kWaveKernels<T, DK, DV>) return {int64_t(BwdQW64::kRound) * BwdQW64::kStages, 512};
             else if constexpr (kTileKernels<T, DK, DV>)
-                return {int64_t(BwdQTile<DK>::kRound) * BwdQTile<DK>::kStages, 256};
+                return {int64_t(BwdQTile<DK, DV>::kRound) * BwdQTile<DK, DV>::kStages, kBwdQTileWgs<DK, DV>};
             else return {BwdQShape<T, DK, DV>::kG, 1024};
         case kStepBwdKV:
             return {int64_t(StreamShape<T, DK, DV>::kStages) * 16 * StreamShape<T, DK, DV>::kWaves, 1024};

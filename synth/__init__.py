@@ -137,3 +137,17 @@ WORKLOADS = {
 }
 
 HEADLINE = "B8-H16-T16384-D64-f16"
+
+
+# Measurement shapes for the other head sizes: the headline's batch, heads,
+# length and dtype with D (of Q, K) and Dv (of V) changed. Seed base 6000 + 100 i.
+HEAD_SIZE_WORKLOADS = {
+    w.name: w for w in (
+        Workload("B8-H16-T16384-D32-f16", 8, 16, 16384, 32, "f16", seed=6000),
+        Workload("B8-H16-T16384-D96-f16", 8, 16, 16384, 96, "f16", seed=6100),
+        Workload("B8-H16-T16384-D128-f16", 8, 16, 16384, 128, "f16", seed=6200),
+        Workload("B8-H16-T16384-D64-Dv128-f16", 8, 16, 16384, 64, "f16", seed=6300, Dv=128),
+        Workload("B8-H16-T16384-D128-Dv64-f16", 8, 16, 16384, 128, "f16", seed=6400, Dv=64),
+        Workload("B8-H16-T16384-D32-Dv128-f16", 8, 16, 16384, 32, "f16", seed=6500, Dv=128),
+    )
+}
