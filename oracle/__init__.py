@@ -16,13 +16,24 @@ which equals, by associativity, the quadratic "parallel" form listed on the
 flash-linear-attention README ("Different forms of linear attention",
 Parallel): O = rownorm(phi(Q) phi(K)^T) V.
 
+The causal variant (token t attends to tokens s <= t; flash-linear-attention
+README, "Different forms of linear attention") is given by its masked
+quadratic form and its recurrent form.
+
 Pins (tests/test_oracle.py): brute-force quadratic form in pure Python, a
 hand-worked example (tests/golden/), V = ones, joint K/V permutation, Q-row
 permutation, the T = 1 closed form, linearity in V, central finite
 differences of the loss, torch fp64 autograd of the quadratic form, and two
-backward identities. No function here is "parity unpinned".
+backward identities; for the causal form, a pure-Python masked brute force,
+agreement of the two causal forms, the last row against the non-causal form,
+the first row's closed form, and independence of earlier rows from later
+tokens. No function here is "parity unpinned".
 """
 from .la_oracle import (  # noqa: F401
+    causal_fwd,
+    causal_quadratic_head,
+    causal_recurrent_head,
+    causal_sampled_rows_head,
     decode,
     dphi,
     fwd,

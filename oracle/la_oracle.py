@@ -214,3 +214,71 @@ def bwd(q, k, v, do, dtype: str, eps: float, simple: bool, fm: str = "elu1"):
     for h in range(qh.shape[0]):
         dq[h], dk[h], dv[h] = bwd_head(qh[h], kh[h], vh[h], dh[h], eps, simple, fm)
     return dq.reshape(q.shape), dk.reshape(k.shape), dv.reshape(v.shape)
+
+
+# ---------------------------------------------------------------- causal form
+# flash-linear-attention README, "Different forms of linear attention": the
+# causal (autoregressive) variant, where token t attends to tokens s <= t. Its
+# Parallel form is the quadratic form with a causal mask; its FusedRecurrent
+# form carries the state S_t = S_{t-1} + phi(k_t) v_t^T from token to token.
+
+def causal_quadratic_head(q, k, v, eps: float, simple: bool, fm: str = "elu1") -> np.ndarray:
+    """Causal Parallel form for one (batch, head): A = phi(Q) phi(K)^T with
+    A[t, s] = 0 for s > t; normalised O = (A V) / (A 1 + eps), simple_la
+    O = A V. Cost O(T^2 D): tiny T only."""
+    a = np.tril(phi(q, fm) @ phi(k, fm).T)
+    num = a @ np.asarray(v, dtype=np.float64)
+    if simple:
+        return num
+    return num / (a.sum(axis=1) + eps)[:, None]
+
+
+def causal_recurrent_head(q, k, v, eps: float, simple: bool, fm: str = "elu1"):
+    """Causal Recurrent form for one (batch, head), token by token:
+    S_t = S_{t-1} + phi(k_t) v_t^T, z_t = z_{t-1} + phi(k_t) (S_0 = 0, z_0 = 0),
+    O_t = phi(q_t) S_t / (phi(q_t) . z_t + eps), or phi(q_t) S_t for simple_la.
+    Returns (O, S_T, z_T); S_T, z_T are the non-causal state of the head."""
+    qt, kt = phi(q, fm), phi(k, fm)
+    v = np.asarray(v, dtype=np.float64)
+    T, dk = kt.shape
+    s = np.zeros((dk, v.shape[1]))
+    z = np.zeros(dk)
+    o = np.empty((T, v.shape[1]))
+    for t in range(T):
+        s += np.outer(kt[t], v[t])
+        z += kt[t]
+        o[t] = qt[t] @ s
+        if not simple:
+            o[t] /= qt[t] @ z + eps
+    return o, s, z
+
+
+def causal_sampled_rows_head(q, k, v, rows, eps: float, simple: bool, fm: str = "elu1") -> np.ndarray:
+    """Causal output rows O_t, t in ``rows``, one by one from the masked
+    quadratic form: O_t = sum_{s <= t} a_ts v_s / (sum_{s <= t} a_ts + eps),
+    a_ts = phi(q_t) . phi(k_s). Cost O(t D) per row, for full-size sequences."""
+    kt = phi(k, fm)
+    v = np.asarray(v, dtype=np.float64)
+    out = np.empty((len(rows), v.shape[1]))
+    for n, t in enumerate(rows):
+        a = kt[: t + 1] @ phi(q[t], fm)
+        out[n] = a @ v[: t + 1]
+        if not simple:
+            out[n] /= a.sum() + eps
+    return out
+
+
+def causal_fwd(q, k, v, dtype: str, eps: float, simple: bool, fm: str = "elu1"):
+    """Causal forward over storage arrays Q, K [B, H, T, Dk], V [B, H, T, Dv]:
+    (O [B,H,T,Dv], S [B,H,Dk,Dv], z [B,H,Dk]) by the recurrent form; S and z are
+    the full-sequence state."""
+    lead = q.shape[:-1]
+    qh, kh, vh = _heads(q, dtype), _heads(k, dtype), _heads(v, dtype)
+    n, dk, dv = qh.shape[0], q.shape[-1], v.shape[-1]
+    o = np.empty(vh.shape)
+    s = np.empty((n, dk, dv))
+    z = np.empty((n, dk))
+    for h in range(n):
+        o[h], s[h], z[h] = causal_recurrent_head(qh[h], kh[h], vh[h], eps, simple, fm)
+    return (o.reshape(lead + (dv,)), s.reshape(lead[:-1] + (dk, dv)),
+            z.reshape(lead[:-1] + (dk,)))

@@ -454,3 +454,120 @@ def test_relu_bwd_matches_torch_autograd_of_quadratic_form(simple):
     for g, t in zip(oracle.bwd_head(q, k, v, do, eps, simple, "relu"), (tq, tk, tv)):
         ref = t.grad.numpy()
         assert np.max(np.abs(g - ref)) <= 1e-12 * np.abs(ref).max()
+
+
+# ---------------------------------------------------------------- causal form
+
+def causal_brute_force(q, k, v, eps, simple, fm="elu1"):
+    """Pure-Python masked quadratic form: O_t = sum_{s<=t} a_ts v_s / (sum_{s<=t} a_ts + eps)."""
+    def ph(x):
+        if fm == "relu":
+            return x if x > 0 else 0.0
+        if fm == "identity":
+            return x
+        return x + 1.0 if x > 0 else math.exp(x)
+    T, D, Dv = len(q), len(q[0]), len(v[0])
+    out = []
+    for t in range(T):
+        a = [sum(ph(q[t][i]) * ph(k[s][i]) for i in range(D)) for s in range(t + 1)]
+        row = [sum(a[s] * v[s][j] for s in range(t + 1)) for j in range(Dv)]
+        if not simple:
+            den = sum(a) + eps
+            row = [x / den for x in row]
+        out.append(row)
+    return np.array(out)
+
+
+@pytest.mark.parametrize("fm", ["elu1", "relu"])
+@pytest.mark.parametrize("simple", [False, True])
+@pytest.mark.parametrize("T,D,Dv", [(1, 4, 4), (9, 5, 5), (17, 6, 3), (33, 8, 12)])
+def test_causal_forms_match_brute_force(T, D, Dv, simple, fm):
+    q, k, v = rand((T, D), 81), rand((T, D), 82), rand((T, Dv), 83)
+    eps = 0.3
+    ref = causal_brute_force(q.tolist(), k.tolist(), v.tolist(), eps, simple, fm)
+    scale = np.max(np.abs(ref))
+    oq = oracle.causal_quadratic_head(q, k, v, eps, simple, fm)
+    orr, s, z = oracle.causal_recurrent_head(q, k, v, eps, simple, fm)
+    assert np.max(np.abs(oq - ref)) <= 1e-12 * scale
+    assert np.max(np.abs(orr - ref)) <= 1e-12 * scale
+    rows = sorted({0, T // 2, T - 1})
+    osr = oracle.causal_sampled_rows_head(q, k, v, rows, eps, simple, fm)
+    assert np.max(np.abs(osr - ref[rows])) <= 1e-12 * scale
+    # the recurrent form's final state is the non-causal state
+    s_ref, z_ref = oracle.state_head(k, v, fm)
+    np.testing.assert_allclose(s, s_ref, rtol=1e-12, atol=1e-12 * np.abs(s_ref).max())
+    np.testing.assert_allclose(z, z_ref, rtol=1e-12)
+
+
+@pytest.mark.parametrize("simple", [False, True])
+def test_causal_last_row_is_the_noncausal_row(simple):
+    """The last token sees every token: its causal output equals the
+    non-causal output row (pinned independently above)."""
+    T, D = 50, 16
+    q, k, v = rand((T, D), 84), rand((T, D), 85), rand((T, D), 86)
+    o_c, _, _ = oracle.causal_recurrent_head(q, k, v, 1e-6, simple)
+    o_n, _, _ = oracle.fwd_head(q, k, v, 1e-6, simple)
+    np.testing.assert_allclose(o_c[-1], o_n[-1], rtol=1e-12, atol=1e-12 * np.abs(o_n).max())
+    assert np.max(np.abs(o_c[0] - o_n[0])) > 1e-3 * np.abs(o_n).max()  # the first row differs
+
+
+@pytest.mark.parametrize("simple", [False, True])
+def test_causal_first_row_closed_form(simple):
+    """O_0 = a v_0 / (a + eps) (simple_la: a v_0) with a = phi(q_0) . phi(k_0)."""
+    T, D = 7, 6
+    q, k, v = rand((T, D), 87), rand((T, D), 88), rand((T, D), 89)
+    eps = 0.25
+    a = float(oracle.phi(q[0]) @ oracle.phi(k[0]))
+    want = a * v[0] if simple else a * v[0] / (a + eps)
+    o, _, _ = oracle.causal_recurrent_head(q, k, v, eps, simple)
+    np.testing.assert_allclose(o[0], want, rtol=1e-14)
+
+
+def test_causal_rows_ignore_later_tokens():
+    """Changing K and V after position t leaves rows 0..t unchanged."""
+    T, D, t = 40, 8, 23
+    q, k, v = rand((T, D), 90), rand((T, D), 91), rand((T, D), 92)
+    o1, _, _ = oracle.causal_recurrent_head(q, k, v, 1e-6, False)
+    k2, v2 = k.copy(), v.copy()
+    k2[t + 1:] = rand((T - t - 1, D), 93)
+    v2[t + 1:] = rand((T - t - 1, D), 94)
+    o2, _, _ = oracle.causal_recurrent_head(q, k2, v2, 1e-6, False)
+    np.testing.assert_array_equal(o1[: t + 1], o2[: t + 1])
+    assert np.max(np.abs(o1[t + 1:] - o2[t + 1:])) > 1e-3
+
+
+def test_causal_v_ones_gives_ones():
+    T, D = 30, 8
+    q, k = rand((T, D), 95), rand((T, D), 96)
+    eps = 1e-6
+    o, _, _ = oracle.causal_recurrent_head(q, k, np.ones((T, 5)), eps, False)
+    a = np.cumsum(oracle.phi(k) @ oracle.phi(q).T, axis=0).diagonal()  # sum_{s<=t} a_ts
+    np.testing.assert_allclose(o, np.repeat((a / (a + eps))[:, None], 5, axis=1), rtol=1e-13)
+
+
+def test_causal_batched_matches_per_head_and_quadratic():
+    from synth import Workload
+    w = Workload("t", 2, 3, 70, 8, "f16", seed=97, Dv=12)
+    x = make_inputs(w, with_grad=False)
+    o, s, z = oracle.causal_fwd(x["q"], x["k"], x["v"], "f16", 1e-6, False)
+    assert o.shape == w.shape_v and s.shape == (2, 3, 8, 12) and z.shape == (2, 3, 8)
+    d = {n: oracle.decode(x[n], "f16") for n in ("q", "k", "v")}
+    oq = oracle.causal_quadratic_head(d["q"][1, 2], d["k"][1, 2], d["v"][1, 2], 1e-6, False)
+    np.testing.assert_allclose(o[1, 2], oq, rtol=1e-12, atol=1e-12 * np.abs(oq).max())
+
+
+def test_causal_pins_catch_planted_mistakes():
+    """Slips planted in a copy of the causal form (mask excluding the diagonal,
+    mask transposed, the non-causal form) each fail the brute-force pin."""
+    T, D = 12, 4
+    q, k, v = rand((T, D), 98), rand((T, D), 99), rand((T, D), 100)
+    ref = causal_brute_force(q.tolist(), k.tolist(), v.tolist(), 0.3, False)
+    a_full = oracle.phi(q) @ oracle.phi(k).T
+    for kind, a in (("strict_mask", np.tril(a_full, -1)), ("upper_mask", np.triu(a_full)),
+                    ("no_mask", a_full), ("none", np.tril(a_full))):
+        o = (a @ v) / (a.sum(axis=1) + 0.3)[:, None]
+        err = np.max(np.abs(o - ref)) / np.abs(ref).max()
+        if kind == "none":
+            assert err <= 1e-12
+        else:
+            assert err > 1e-3, kind
