@@ -109,6 +109,59 @@ def cpu_baseline(w, x, max_heads: int) -> dict:
     }
 
 
+def causal_bench(args, w, q, k, v, o, state, ws, do_flush) -> int:
+    """The causal forward: one la_fwd call (segment states, their prefixes, the
+    chunked scan). Its rate counts the algorithmic minimum, one pass over Q, K,
+    V and O; the path itself reads K and V twice (states, then the scan)."""
+    def step(ev):
+        ev[0].record()
+        la.fwd(q, k, v, eps=w.eps, simple=w.simple, out=o, state=state, ws=ws, causal=True)
+        ev[1].record()
+
+    mk = lambda: [torch.cuda.Event(enable_timing=True) for _ in range(2)]  # noqa: E731
+    for _ in range(args.warmup):
+        do_flush(args.flush)
+        step(mk())
+    torch.cuda.synchronize()
+    events = [mk() for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        do_flush(args.flush)
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = np.array([ev[0].elapsed_time(ev[1]) for ev in events])
+    lb = launch_bytes(w)
+    alg = lb["fwd_state"] + lb["fwd_output"]  # Q, K, V in, O out
+    value = alg / (float(np.mean(ms)) * 1e-3) / 1e9
+    line = {
+        "metric": "causal LA fwd GB/s (algorithmic Q, K, V, O bytes) and ms",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(float(np.mean(ms)), 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": DTYPE_NAME[w.dtype],
+        "data": "synthetic: seeded N(0, sigma^2) Q, K, V rounded to the dtype",
+        "config": {"workload": w.name + "-causal", "B": w.B, "H": w.H, "T": w.T, "D": w.D, "Dv": w.dv,
+                   "mode": ("simple_la" if w.simple else "normalised") + ", causal", "pass": "fwd"},
+        "fwd_ms": round(float(np.mean(ms)), 4),
+        "fwd_ms_min": round(float(np.min(ms)), 4),
+        "fwd_ms_median": round(float(np.median(ms)), 4),
+        "fwd_frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
+        "wall_ms_per_step_incl_flush": round(wall / args.steps * 1e3, 4),
+        "roofline": {"kernel": "la_fwd causal (state, prefix, chunked scan)", "bound": "hbm",
+                     "achieved": round(value, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(value / HBM_PEAK_GBS, 4), "traffic": None},
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -121,6 +174,8 @@ def main() -> int:
     ap.add_argument("--cpu-heads", type=int, default=128, help="heads in the oracle sample")
     ap.add_argument("--all-cache-conditions", action="store_true",
                     help="also time the step after a writing flush and with no flush")
+    ap.add_argument("--causal", action="store_true",
+                    help="time the causal forward (LA_CAUSAL) instead of the bidirectional fwd+bwd")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 1 GiB device copy (for counter scaling)")
     args = ap.parse_args()
@@ -166,6 +221,9 @@ def main() -> int:
         else:
             ev[3].record()
         ev[4].record()
+
+    if args.causal:
+        return causal_bench(args, w, q, k, v, o, state, ws, do_flush)
 
     mk = lambda: [torch.cuda.Event(enable_timing=True) for _ in range(5)]  # noqa: E731
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)

@@ -88,6 +88,14 @@ typedef enum {
  * change sign; that is the caller's to avoid (simple_la has none). */
 #define LA_PHI_RELU 0x4u
 #define LA_PHI_IDENTITY 0x8u
+/* Causal (autoregressive) attention: token t attends to tokens s <= t,
+ *     O_t = phi(q_t) S_t / (phi(q_t) . z_t + eps),  S_t = sum_{s<=t} phi(k_s) v_s^T,
+ * z_t = sum_{s<=t} phi(k_s) (flash-linear-attention README, "Different forms
+ * of linear attention"). Accepted by la_fwd only, for f16 and bf16 with D and
+ * Dv in {64, 128}; `state` receives the full-sequence S, z, bit-identical to
+ * the non-causal call. Every other entry point returns LA_ERR_FLAGS with it;
+ * other dtypes give LA_ERR_DTYPE and other head sizes LA_ERR_HEAD_DIM. */
+#define LA_CAUSAL 0x10u
 
 /* Problem description shared by every call. B, H, T >= 0 (a zero size is an
  * empty problem: nothing to compute, LA_OK), B*H <= 2^24. D is the head size
@@ -103,7 +111,7 @@ typedef struct {
     int64_t B, H, T, D;
     int64_t Dv;      /* head size of V, O, dO, dV; 0 means D */
     int32_t dtype;   /* la_dtype */
-    uint32_t flags;  /* LA_SIMPLE, LA_LAYOUT_BTHD, one of LA_PHI_RELU, LA_PHI_IDENTITY */
+    uint32_t flags;  /* LA_SIMPLE, LA_LAYOUT_BTHD, one of LA_PHI_RELU, LA_PHI_IDENTITY, LA_CAUSAL */
     float eps;
 } la_problem;
 
@@ -122,7 +130,9 @@ size_t la_workspace_bytes(const la_problem* p);
 
 /* Forward: O (and the state S, z) from Q, K, V. Runs la_fwd_state, then
  * la_fwd_output. `state` may be NULL when the caller does not keep it; the
- * workspace then holds it. */
+ * workspace then holds it. With LA_CAUSAL: the state reduction per token
+ * segment, exclusive prefixes of the segment states, then one chunked scan
+ * per segment that writes O. */
 int la_fwd(const la_problem* p, const void* q, const void* k, const void* v,
            void* o, void* state, void* ws, size_t ws_bytes, void* stream);
 

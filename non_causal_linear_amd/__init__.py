@@ -20,7 +20,7 @@ import torch
 __all__ = [
     "LAError", "lib", "fwd", "bwd", "fwd_state", "fwd_output", "bwd_dq", "bwd_dkv", "linear_attention",
     "state_bytes", "workspace_bytes", "new_state", "workspace", "Problem",
-    "LA_F32", "LA_F16", "LA_BF16", "LA_SIMPLE", "LA_LAYOUT_BTHD", "LA_PHI_RELU", "LA_PHI_IDENTITY",
+    "LA_F32", "LA_F16", "LA_BF16", "LA_SIMPLE", "LA_LAYOUT_BTHD", "LA_PHI_RELU", "LA_PHI_IDENTITY", "LA_CAUSAL",
     "EXPORTS",
 ]
 
@@ -30,6 +30,7 @@ LA_F32, LA_F16, LA_BF16 = 0, 1, 2
 LA_SIMPLE = 0x1
 LA_LAYOUT_BTHD = 0x2
 LA_PHI_RELU, LA_PHI_IDENTITY = 0x4, 0x8
+LA_CAUSAL = 0x10
 LAYOUTS = ("bhtd", "bthd")
 FEATURE_MAPS = {"elu1": 0, "relu": LA_PHI_RELU, "identity": LA_PHI_IDENTITY}
 DTYPE_CODE = {torch.float32: LA_F32, torch.float16: LA_F16, torch.bfloat16: LA_BF16}
@@ -95,7 +96,7 @@ def _check(status: int) -> None:
 
 
 def make_problem(shape, dtype: torch.dtype, eps: float, simple: bool, layout: str = "bhtd",
-                 phi: str = "elu1", dv: int | None = None) -> Problem:
+                 phi: str = "elu1", dv: int | None = None, causal: bool = False) -> Problem:
     """Problem for Q/K-side tensors of ``shape``: [B, H, T, D] (layout "bhtd")
     or [B, T, H, D] (layout "bthd"), V-side tensors with head size ``dv``
     (None: D); feature map phi "elu1" (elu(x) + 1), "relu" or "identity"."""
@@ -111,7 +112,8 @@ def make_problem(shape, dtype: torch.dtype, eps: float, simple: bool, layout: st
         B, H, T, D = (int(x) for x in shape)
     else:
         B, T, H, D = (int(x) for x in shape)
-    flags = (LA_SIMPLE if simple else 0) | (LA_LAYOUT_BTHD if layout == "bthd" else 0) | FEATURE_MAPS[phi]
+    flags = ((LA_SIMPLE if simple else 0) | (LA_LAYOUT_BTHD if layout == "bthd" else 0) | FEATURE_MAPS[phi]
+             | (LA_CAUSAL if causal else 0))
     return Problem(B, H, T, D, D if dv is None else int(dv), DTYPE_CODE[dtype], flags, float(eps))
 
 
@@ -220,13 +222,16 @@ def fwd_output(q, state, *, eps=1e-6, simple=False, layout="bhtd", phi="elu1", o
     return out
 
 
-def fwd(q, k, v, *, eps=1e-6, simple=False, layout="bhtd", phi="elu1", out=None, state=None, ws=None):
-    """O = phi(Q) S / (phi(Q) z + eps) (or phi(Q) S); returns (O, state)."""
+def fwd(q, k, v, *, eps=1e-6, simple=False, layout="bhtd", phi="elu1", out=None, state=None, ws=None,
+        causal=False):
+    """O = phi(Q) S / (phi(Q) z + eps) (or phi(Q) S); returns (O, state).
+    causal=True: token t attends to tokens s <= t (f16/bf16, D and Dv in
+    {64, 128}); the state is still that of the whole sequence."""
     _tensor(q, None, "q")
     _tensor(k, q, "k")
     dv = v.shape[-1] if isinstance(v, torch.Tensor) else None
     _tensor(v, q, "v", dv)
-    prob = make_problem(q.shape, q.dtype, eps, simple, layout, phi, dv)
+    prob = make_problem(q.shape, q.dtype, eps, simple, layout, phi, dv, causal)
     out = _new_like(q, dv) if out is None else _tensor(out, q, "out", dv)
     state = new_state(prob, q.device) if state is None else _state(state, prob, q.device)
     ws, wsb = _ws(prob, q.device, ws)

@@ -58,7 +58,7 @@ la_status check_problem(const la_problem* p) {
     if (!head_size_ok(p->D) || !head_size_ok(dv_of(p))) return LA_ERR_HEAD_DIM;
     if (p->B < 0 || p->H < 0 || p->T < 0) return LA_ERR_SHAPE;
     if (p->B > kMaxHeads || p->H > kMaxHeads || p->B * p->H > kMaxHeads) return LA_ERR_SHAPE;
-    if (p->flags & ~(LA_SIMPLE | LA_LAYOUT_BTHD | LA_PHI_RELU | LA_PHI_IDENTITY)) return LA_ERR_FLAGS;
+    if (p->flags & ~(LA_SIMPLE | LA_LAYOUT_BTHD | LA_PHI_RELU | LA_PHI_IDENTITY | LA_CAUSAL)) return LA_ERR_FLAGS;
     if ((p->flags & LA_PHI_RELU) && (p->flags & LA_PHI_IDENTITY)) return LA_ERR_FLAGS;
     const int64_t row_bytes = std::max(p->D, dv_of(p)) * (p->dtype == LA_F32 ? 4 : 2);
     if (p->flags & LA_LAYOUT_BTHD) {
@@ -71,6 +71,19 @@ la_status check_problem(const la_problem* p) {
 }
 
 size_t elem_bytes(int dtype) { return dtype == LA_F32 ? 4 : 2; }
+
+// What the causal forward supports, on a problem check_problem accepted.
+la_status check_causal(const la_problem* p) {
+    if (p->dtype != LA_F16 && p->dtype != LA_BF16) return LA_ERR_DTYPE;
+    const int64_t dv = dv_of(p);
+    if ((p->D != 64 && p->D != 128) || (dv != 64 && dv != 128)) return LA_ERR_HEAD_DIM;
+    return LA_OK;
+}
+
+// Entry points other than la_fwd do not take LA_CAUSAL.
+la_status check_not_causal(const la_problem* p) {
+    return (p->flags & LA_CAUSAL) ? LA_ERR_FLAGS : LA_OK;
+}
 
 // The kernels of one (dtype, DK); the problem has been checked.
 const la::KernelSet* kernel_set(int dtype, int DK) {
@@ -195,6 +208,7 @@ int la_fwd_state(const la_problem* p, const void* k, const void* v, void* state,
                  size_t ws_bytes, void* stream) {
     la_status st = check_problem(p);
     if (st != LA_OK) return st;
+    if ((st = check_not_causal(p)) != LA_OK) return st;
     const la::Plan pl = make_plan(p);
     const size_t tk = size_t(pl.BH * pl.T * pl.DK) * elem_bytes(pl.dtype);
     const size_t tv = size_t(pl.BH * pl.T * pl.DV) * elem_bytes(pl.dtype);
@@ -211,6 +225,7 @@ int la_fwd_state(const la_problem* p, const void* k, const void* v, void* state,
 int la_fwd_output(const la_problem* p, const void* q, const void* state, void* o, void* stream) {
     la_status st = check_problem(p);
     if (st != LA_OK) return st;
+    if ((st = check_not_causal(p)) != LA_OK) return st;
     const la::Plan pl = make_plan(p);
     const size_t tk = size_t(pl.BH * pl.T * pl.DK) * elem_bytes(pl.dtype);
     const size_t tv = size_t(pl.BH * pl.T * pl.DV) * elem_bytes(pl.dtype);
@@ -226,6 +241,8 @@ int la_fwd(const la_problem* p, const void* q, const void* k, const void* v, voi
            void* ws, size_t ws_bytes, void* stream) {
     la_status st = check_problem(p);
     if (st != LA_OK) return st;
+    const bool causal = (p->flags & LA_CAUSAL) != 0;
+    if (causal && (st = check_causal(p)) != LA_OK) return st;
     const la::Plan pl = make_plan(p);
     const size_t tk = size_t(pl.BH * pl.T * pl.DK) * elem_bytes(pl.dtype);
     const size_t tv = size_t(pl.BH * pl.T * pl.DV) * elem_bytes(pl.dtype);
@@ -238,6 +255,7 @@ int la_fwd(const la_problem* p, const void* q, const void* k, const void* v, voi
     float* stp = state ? static_cast<float*>(state)
                        : reinterpret_cast<float*>(static_cast<char*>(ws) + pl.off_fstate);
     hipStream_t s = static_cast<hipStream_t>(stream);
+    if (causal) return device_status(kernel_set(pl.dtype, pl.DK)->fwd_causal(pl, q, k, v, o, stp, ws, s));
     st = device_status(kernel_set(pl.dtype, pl.DK)->fwd_state(pl, k, v, stp, ws, s));
     if (st != LA_OK || tk == 0) return st;
     return device_status(kernel_set(pl.dtype, pl.DK)->fwd_output(pl, q, stp, o, s));
@@ -247,6 +265,7 @@ int la_bwd_dq(const la_problem* p, const void* q, const void* dout, const void* 
               void* ws, size_t ws_bytes, void* stream) {
     la_status st = check_problem(p);
     if (st != LA_OK) return st;
+    if ((st = check_not_causal(p)) != LA_OK) return st;
     const la::Plan pl = make_plan(p);
     const size_t tk = size_t(pl.BH * pl.T * pl.DK) * elem_bytes(pl.dtype);
     const size_t tv = size_t(pl.BH * pl.T * pl.DV) * elem_bytes(pl.dtype);
@@ -265,6 +284,7 @@ int la_bwd_dkv(const la_problem* p, const void* k, const void* v, void* dk, void
                size_t ws_bytes, void* stream) {
     la_status st = check_problem(p);
     if (st != LA_OK) return st;
+    if ((st = check_not_causal(p)) != LA_OK) return st;
     const la::Plan pl = make_plan(p);
     const size_t tk = size_t(pl.BH * pl.T * pl.DK) * elem_bytes(pl.dtype);
     const size_t tv = size_t(pl.BH * pl.T * pl.DV) * elem_bytes(pl.dtype);
@@ -281,6 +301,7 @@ int la_bwd(const la_problem* p, const void* q, const void* k, const void* v, con
            const void* state, void* dq, void* dk, void* dv, void* ws, size_t ws_bytes, void* stream) {
     la_status st = check_problem(p);
     if (st != LA_OK) return st;
+    if ((st = check_not_causal(p)) != LA_OK) return st;
     const la::Plan pl = make_plan(p);
     const size_t tk = size_t(pl.BH * pl.T * pl.DK) * elem_bytes(pl.dtype);
     const size_t tv = size_t(pl.BH * pl.T * pl.DV) * elem_bytes(pl.dtype);

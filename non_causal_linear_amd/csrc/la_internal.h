@@ -66,6 +66,9 @@ struct KernelSet {
     hipError_t (*bwd_dkv)(const Plan& p, const void* k, const void* v, void* dk, void* dv, void* ws,
                           hipStream_t s);
     SplitCfg (*split_config)(int step, int DV);
+    // causal forward (LA_CAUSAL): 16-bit elements, DK and DV in {64, 128}
+    hipError_t (*fwd_causal)(const Plan& p, const void* q, const void* k, const void* v, void* o, float* state,
+                             void* ws, hipStream_t s);
 };
 
 // One unit per (la_dtype, DK): kernel_set_<dtype>_<DK>().

@@ -2196,6 +2196,359 @@ __global__ __launch_bounds__((StreamShape<T, DK, DV>::kThreads), (StreamShape<T,
 }
 
 // ---------------------------------------------------------------------------
+// Causal forward (LA_CAUSAL): token t attends to tokens s <= t.
+// ---------------------------------------------------------------------------
+// Each head's tokens are cut into the segments of the state reduction; a
+// segment's exclusive prefix state (S, z of all earlier segments) comes from
+// prefix_kernel. One workgroup walks its segment in 64-token chunks, in order,
+// with the running state R, z of everything before the chunk on chip:
+//   O_t = (phi(q_t) R + sum_{s in chunk, s <= t} a_ts v_s)
+//         / (phi(q_t) z + sum_{s in chunk, s <= t} a_ts + eps),  a_ts = phi(q_t) . phi(k_s),
+// then R += phi(K_c)^T V_c, z += sum phi(k). Per chunk, the four waves
+//   (a) each compute a = phi(Q) phi(K)^T for 16 query rows, mask s > t and
+//       stage it, scaled by a power of two, in their own LDS rows;
+//   (b) multiply it by [V | 1] and phi(Q) by [R | z] (R and z as 16-bit
+//       copies in LDS) and store their 16 rows of O;
+//   (c) add phi(K)^T V into their quarter of R's columns (fp32 registers;
+//       wave 0 also keeps z) and publish it, scaled by the wave's own power
+//       of two, into the other LDS copy of R for the next chunk.
+// Two barriers per chunk; the next chunk's loads are issued after the first.
+// Rows past the segment end load as zeros (K is zeroed after phi) and their
+// stores are dropped.
+template <int DK, int DV>
+struct CausalShape {
+    static constexpr int kChunk = 64;                 // tokens per chunk
+    static constexpr int kLDK = DK + 16;              // tQ, tK row stride (elements)
+    static constexpr int kLDV = DV + 16;              // tV, tR row stride
+    static constexpr int kLDA = (kChunk > DV ? kChunk : DV) + 8;  // a / O staging row stride
+    static constexpr int kMinBlocks = (DK == 64 && DV == 64) ? 2 : 1;
+};
+
+template <typename T, int DK, int DV, bool SIMPLE, int FM>
+__global__ __launch_bounds__(kThreads, (CausalShape<DK, DV>::kMinBlocks)) void fwd_causal_kernel(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const float* __restrict__ pre,
+    T* __restrict__ o, int64_t T_, const Layout lay, int P, int64_t L, float eps) {
+    using Sh = CausalShape<DK, DV>;
+    constexpr int C = Sh::kChunk, LDK = Sh::kLDK, LDV = Sh::kLDV, LDA = Sh::kLDA;
+    constexpr int NBV = DV / 16;         // output column blocks
+    constexpr int RJ = DV / 64;          // R column blocks per wave (a quarter of DV)
+    constexpr int RI = DK / 16;          // R row blocks
+    constexpr int KSK = DK / 32, KSC = C / 32;
+    constexpr int CK = DK / 8, CV = DV / 8;  // 16-byte chunks per row
+    constexpr int NCK = C * CK / kThreads, NCV = C * CV / kThreads;
+    constexpr int NST = 16 * CV / 64;    // 16-byte O chunks per lane per wave tile
+    static_assert(sizeof(T) == 2, "transposed LDS reads take 16-bit elements");
+    static_assert(NCK * kThreads == C * CK && NCV * kThreads == C * CV && NST * 64 == 16 * CV, "tiles must split");
+    static_assert(RJ >= 1 && RJ * 64 == DV, "each wave owns whole 16-column blocks of R");
+    __shared__ __attribute__((aligned(16))) T tQ[C * LDK];
+    __shared__ __attribute__((aligned(16))) T tK[C * LDK];
+    __shared__ __attribute__((aligned(16))) T tV[C * LDV];
+    __shared__ __attribute__((aligned(16))) T tR[2][DK * LDV];
+    __shared__ __attribute__((aligned(16))) T tZ[2][DK];
+    __shared__ __attribute__((aligned(16))) T tA[kWaves][16 * LDA];
+    __shared__ int sExp[2][kWaves + 1];  // exponents of the R quarters, then of z
+
+    const int wid = xcd_remap(blockIdx.x, gridDim.x);
+    const int64_t bh = wid / P;
+    const int p = wid % P;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int m = lane & 15, grp = lane >> 4;
+    const int64_t t0 = (int64_t)p * L;
+    const int64_t t1 = min(t0 + L, T_);
+    const int64_t len = t1 - t0;
+    const int nchunks = (int)(len > 0 ? (len + C - 1) / C : 0);
+    const Layout lk = lay, lv = v_layout<DK, DV>(lay);
+
+    // Running state: R[16 iR + 4 grp + r][16 (wave RJ + jR) + m] in accR[iR][jR][r];
+    // z[16 iR + 4 grp + r] in accZ[iR][r] (wave 0). From the exclusive prefix.
+    f32x4 accR[RI][RJ], accZ[RI];
+    {
+        const float* pS = (pre != nullptr && p > 0) ? pre + (bh * P + p) * (int64_t)(DK * DV + DK) : nullptr;
+#pragma unroll
+        for (int iR = 0; iR < RI; ++iR) {
+#pragma unroll
+            for (int jR = 0; jR < RJ; ++jR)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    accR[iR][jR][r] = pS ? pS[(16 * iR + 4 * grp + r) * DV + 16 * (wave * RJ + jR) + m] : 0.f;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) accZ[iR][r] = pS ? pS[DK * DV + 16 * iR + 4 * grp + r] : 0.f;
+        }
+    }
+    Frag<T> ones;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ones[e] = static_cast<T>(1.f);
+
+    auto wave_max = [](float x) {
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
+        return x;
+    };
+    // this wave's quarter of R (and z, wave 0) as 16-bit into copy `buf`
+    auto publish = [&](int buf) {
+        float mx = 0.f;
+#pragma unroll
+        for (int iR = 0; iR < RI; ++iR)
+#pragma unroll
+            for (int jR = 0; jR < RJ; ++jR)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) mx = fmaxf(mx, fabsf(accR[iR][jR][r]));
+        const int sR = Elt<T>::kScaled ? scale_exp(wave_max(mx)) : 0;
+        const float fR = ldexpf(1.f, sR);
+#pragma unroll
+        for (int iR = 0; iR < RI; ++iR)
+#pragma unroll
+            for (int jR = 0; jR < RJ; ++jR)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    tR[buf][(16 * iR + 4 * grp + r) * LDV + 16 * (wave * RJ + jR) + m] =
+                        static_cast<T>(accR[iR][jR][r] * fR);
+        if (lane == 0) sExp[buf][wave] = sR;
+        if constexpr (!SIMPLE) {
+            if (wave == 0) {
+                float mz = 0.f;
+#pragma unroll
+                for (int iR = 0; iR < RI; ++iR)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) mz = fmaxf(mz, fabsf(accZ[iR][r]));
+                const int sZ = Elt<T>::kScaled ? scale_exp(wave_max(mz)) : 0;
+                const float fZ = ldexpf(1.f, sZ);
+                if (m == 0)
+#pragma unroll
+                    for (int iR = 0; iR < RI; ++iR)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) tZ[buf][16 * iR + 4 * grp + r] = static_cast<T>(accZ[iR][r] * fZ);
+                if (lane == 0) sExp[buf][kWaves] = sZ;
+            }
+        }
+    };
+
+    struct Stage {
+        u32x4 q[NCK], k[NCK], v[NCV];
+    };
+    const HeadBuf bq = slice_buf(q, lk, bh, DK, t0, t1), bk = slice_buf(k, lk, bh, DK, t0, t1);
+    const HeadBuf bv = slice_buf(v, lv, bh, DV, t0, t1), bo = slice_buf(o, lv, bh, DV, t0, t1);
+    auto issue = [&](Stage& st, int c) {
+        const int64_t row0 = (int64_t)c * C;
+#pragma unroll
+        for (int i = 0; i < NCK; ++i) {
+            const int n = tid + kThreads * i, r = n / CK, cc = n % CK;
+            const int off = buf_off<T>(row0 + r, lk.rs, 8 * cc);
+            st.q[i] = __builtin_amdgcn_raw_buffer_load_b128(bq.rsrc, off, 0, 0);
+            st.k[i] = __builtin_amdgcn_raw_buffer_load_b128(bk.rsrc, off, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < NCV; ++i) {
+            const int n = tid + kThreads * i, r = n / CV, cc = n % CV;
+            st.v[i] = __builtin_amdgcn_raw_buffer_load_b128(bv.rsrc, buf_off<T>(row0 + r, lv.rs, 8 * cc), 0, 0);
+        }
+    };
+    auto consume = [&](const Stage& st, int c) {
+        const int64_t row0 = (int64_t)c * C;
+#pragma unroll
+        for (int i = 0; i < NCK; ++i) {
+            const int n = tid + kThreads * i, r = n / CK, cc = n % CK;
+            const bool ok = row0 + r < len;
+            Row<T, 8> qin, kin, qt, kt;
+            __builtin_memcpy(qin.e, &st.q[i], sizeof(qin));
+            __builtin_memcpy(kin.e, &st.k[i], sizeof(kin));
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                qt.e[e] = static_cast<T>(phi<FM, T>(to_f32(qin.e[e])));
+                // rows past the segment end must add nothing: mask after phi
+                kt.e[e] = ok ? static_cast<T>(phi<FM, T>(to_f32(kin.e[e]))) : static_cast<T>(0.f);
+            }
+            *reinterpret_cast<Row<T, 8>*>(&tQ[r * LDK + 8 * cc]) = qt;
+            *reinterpret_cast<Row<T, 8>*>(&tK[r * LDK + 8 * cc]) = kt;
+        }
+#pragma unroll
+        for (int i = 0; i < NCV; ++i) {
+            const int n = tid + kThreads * i, r = n / CV, cc = n % CV;
+            *reinterpret_cast<u32x4*>(&tV[r * LDV + 8 * cc]) = st.v[i];
+        }
+    };
+
+    const int rA = 8 * grp + (m >> 2), cA = 4 * (m & 3);
+    T* myA = tA[wave];
+    auto body = [&](Stage& st, int c) {
+        const int cur = c & 1;
+        const int64_t row0 = (int64_t)c * C;
+        consume(st, c);
+        __syncthreads();  // tiles of chunk c and the R, z copy `cur` are visible
+        sched_fence();
+        issue(st, c + 2);  // two chunks ahead; past the segment end these read zeros
+        sched_fence();
+
+        // (a) a[t][s] for t = 16 wave + 4 grp + r (chunk rows), s = 16 jb + m
+        f32x4 aa[C / 16];
+#pragma unroll
+        for (int jb = 0; jb < C / 16; ++jb) aa[jb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KSK; ++ks) {
+            const Frag<T> a = *reinterpret_cast<const Frag<T>*>(&tQ[(16 * wave + m) * LDK + 32 * ks + 8 * grp]);
+#pragma unroll
+            for (int jb = 0; jb < C / 16; ++jb) {
+                const Frag<T> b = *reinterpret_cast<const Frag<T>*>(&tK[(16 * jb + m) * LDK + 32 * ks + 8 * grp]);
+                aa[jb] = mma(a, b, aa[jb]);
+            }
+        }
+        float amax = 0.f;
+#pragma unroll
+        for (int jb = 0; jb < C / 16; ++jb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                if (16 * jb + m > 16 * wave + 4 * grp + r) aa[jb][r] = 0.f;
+                amax = fmaxf(amax, fabsf(aa[jb][r]));
+            }
+        const int sA = Elt<T>::kScaled ? scale_exp(wave_max(amax)) : 0;
+        {
+            const float fA = ldexpf(1.f, sA);
+#pragma unroll
+            for (int jb = 0; jb < C / 16; ++jb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) myA[(4 * grp + r) * LDA + 16 * jb + m] = static_cast<T>(aa[jb][r] * fA);
+        }
+        wave_lds_sync();
+
+        // (b) num = a [V | 1] + phi(Q) [R | z]
+        f32x4 nA[NBV], nR[NBV], dA = f32x4{0.f, 0.f, 0.f, 0.f}, dR = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int jb = 0; jb < NBV; ++jb) {
+            nA[jb] = f32x4{0.f, 0.f, 0.f, 0.f};
+            nR[jb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int ks = 0; ks < KSC; ++ks) {
+            const Frag<T> a = *reinterpret_cast<const Frag<T>*>(&myA[m * LDA + 32 * ks + 8 * grp]);
+            const int rb = 32 * ks + rA;
+#pragma unroll
+            for (int jb = 0; jb < NBV; ++jb) {
+                const Frag<T> b = join_frag<T>(lds_read_tr(&tV[rb * LDV + 16 * jb + cA]),
+                                               lds_read_tr(&tV[(rb + 4) * LDV + 16 * jb + cA]));
+                nA[jb] = mma(a, b, nA[jb]);
+            }
+            if constexpr (!SIMPLE) dA = mma(a, ones, dA);
+        }
+#pragma unroll
+        for (int ks = 0; ks < KSK; ++ks) {
+            const Frag<T> a = *reinterpret_cast<const Frag<T>*>(&tQ[(16 * wave + m) * LDK + 32 * ks + 8 * grp]);
+            const int rb = 32 * ks + rA;
+#pragma unroll
+            for (int jb = 0; jb < NBV; ++jb) {
+                const Frag<T> b = join_frag<T>(lds_read_tr(&tR[cur][rb * LDV + 16 * jb + cA]),
+                                               lds_read_tr(&tR[cur][(rb + 4) * LDV + 16 * jb + cA]));
+                nR[jb] = mma(a, b, nR[jb]);
+            }
+            if constexpr (!SIMPLE) {
+                const Frag<T> zb = *reinterpret_cast<const Frag<T>*>(&tZ[cur][32 * ks + 8 * grp]);
+                dR = mma(a, zb, dR);
+            }
+        }
+        {
+            const float uA = ldexpf(1.f, -sA);
+            float inv[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) inv[r] = 1.f;
+            if constexpr (!SIMPLE) {
+                const float uZ = ldexpf(1.f, -sExp[cur][kWaves]);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) inv[r] = 1.f / (dA[r] * uA + dR[r] * uZ + eps);
+            }
+            wave_lds_sync();
+#pragma unroll
+            for (int jb = 0; jb < NBV; ++jb) {
+                const float uR = ldexpf(1.f, -sExp[cur][jb / RJ]);
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    myA[(4 * grp + r) * LDA + 16 * jb + m] = static_cast<T>((nA[jb][r] * uA + nR[jb][r] * uR) * inv[r]);
+            }
+        }
+        wave_lds_sync();
+#pragma unroll
+        for (int kk = 0; kk < NST; ++kk) {
+            const int n = 64 * kk + lane, r = n / CV, cc = n % CV;
+            const uint4 x = *reinterpret_cast<const uint4*>(&myA[r * LDA + 8 * cc]);
+            buf_store16(bo, buf_off<T>(row0 + 16 * wave + r, lv.rs, 8 * cc), x);
+        }
+        wave_lds_sync();
+
+        // (c) R += phi(K)^T V on this wave's columns; z += sum_t phi(k_t) (wave 0)
+#pragma unroll
+        for (int ks = 0; ks < KSC; ++ks) {
+            const int rb = 32 * ks + rA;
+            Frag<T> bvf[RJ];
+#pragma unroll
+            for (int jR = 0; jR < RJ; ++jR)
+                bvf[jR] = join_frag<T>(lds_read_tr(&tV[rb * LDV + 16 * (wave * RJ + jR) + cA]),
+                                       lds_read_tr(&tV[(rb + 4) * LDV + 16 * (wave * RJ + jR) + cA]));
+#pragma unroll
+            for (int iR = 0; iR < RI; ++iR) {
+                const Frag<T> a = join_frag<T>(lds_read_tr(&tK[rb * LDK + 16 * iR + cA]),
+                                               lds_read_tr(&tK[(rb + 4) * LDK + 16 * iR + cA]));
+#pragma unroll
+                for (int jR = 0; jR < RJ; ++jR) accR[iR][jR] = mma(a, bvf[jR], accR[iR][jR]);
+                if constexpr (!SIMPLE) {
+                    if (wave == 0) accZ[iR] = mma(a, ones, accZ[iR]);
+                }
+            }
+        }
+        publish(cur ^ 1);
+        __syncthreads();  // every wave is done with the tiles and with copy `cur`
+    };
+    publish(0);
+    // Two chunks of loads in flight. The chunk count is rounded up to even so
+    // that the loop has no branch around loads (a branch makes the compiler
+    // wait for every load in flight where the paths join): a chunk past the
+    // segment end reads zeros, adds nothing to R and z, and stores nothing.
+    if (nchunks > 0) {
+        Stage s0, s1;
+        issue(s0, 0);
+        sched_fence();
+        issue(s1, 1);
+        sched_fence();
+        for (int c = 0; c < nchunks; c += 2) {
+            body(s0, c);
+            body(s1, c + 1);
+        }
+    }
+}
+
+// Exclusive prefix of the P partial (S, z) blocks of every head, in place
+// (block p becomes the sum of blocks 0 .. p-1), and their total into the
+// state: the same fixed-order additions as combine_kernel, so the state is
+// bit-identical to the non-causal one.
+template <int DK, int DV>
+__global__ __launch_bounds__(kThreads) void prefix_kernel(float* __restrict__ part, int P, float* __restrict__ outS,
+                                                          float* __restrict__ outz, int64_t BH) {
+    constexpr int E4 = (DK * DV + DK) / 4;
+    constexpr int BPH = (E4 + kThreads - 1) / kThreads;  // blocks per head
+    const int64_t bh = blockIdx.x / BPH;
+    const int i = (blockIdx.x % BPH) * kThreads + threadIdx.x;
+    if (bh >= BH || i >= E4) return;
+    float4* pb = reinterpret_cast<float4*>(part) + bh * (int64_t)P * E4 + i;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int p0 = 0; p0 < P; p0 += 8) {
+        float4 x[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) x[j] = pb[(int64_t)min(p0 + j, P - 1) * E4];
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            if (p0 + j < P) {
+                pb[(int64_t)(p0 + j) * E4] = acc;
+                acc.x += x[j].x;
+                acc.y += x[j].y;
+                acc.z += x[j].z;
+                acc.w += x[j].w;
+            }
+    }
+    const int idx = 4 * i;
+    if (idx < DK * DV)
+        *reinterpret_cast<float4*>(outS + bh * DK * DV + idx) = acc;
+    else
+        *reinterpret_cast<float4*>(outz + bh * DK + (idx - DK * DV)) = acc;
+}
+
+// ---------------------------------------------------------------------------
 // Host-side dispatch.
 // ---------------------------------------------------------------------------
 template <typename T, int DK, int DV>
@@ -2228,25 +2581,67 @@ hipError_t launch_combine(int P, const float* part, float* outS, float* outz, in
                   BH);
 }
 
+// The state reduction kernel alone: partials into the workspace (P > 1) or
+// the state itself (P = 1).
 template <typename T, int DK, int DV, int FM>
-hipError_t fwd_state_fm(const Plan& p, const void* k, const void* v, float* state, void* ws,
-                       hipStream_t s) {
+hipError_t launch_state_reduction(const Plan& p, const void* k, const void* v, float* state, float* part,
+                                  hipStream_t s) {
     const int64_t nblk = p.BH * p.P;
-    float* part = reinterpret_cast<float*>(static_cast<char*>(ws) + p.off_part);
     const T* kk = static_cast<const T*>(k);
     const T* vv = static_cast<const T*>(v);
     float* sz = state + p.BH * DK * DV;
-    hipError_t e;
     if constexpr (kWaveKernels<T, DK, DV>)
-        e = launch(fwd_state_w64_kernel<T, FM>, nblk, kThreads, s, kk, vv, state, sz, part, p.T, p.lay, p.P, p.L);
+        return launch(fwd_state_w64_kernel<T, FM>, nblk, kThreads, s, kk, vv, state, sz, part, p.T, p.lay, p.P, p.L);
     else if constexpr (kTileKernels<T, DK, DV>)
-        e = launch(fwd_state_tile_kernel<T, DK, DV, FM>, nblk, kThreads, s, kk, vv, state, sz, part, p.T, p.lay,
-                   p.P, p.L);
+        return launch(fwd_state_tile_kernel<T, DK, DV, FM>, nblk, kThreads, s, kk, vv, state, sz, part, p.T,
+                      p.lay, p.P, p.L);
     else
-        e = launch(fwd_state_kernel<T, DK, DV, FM>, nblk, kThreads, s, kk, vv, state, sz, part, p.T, p.lay, p.P,
-                   p.L);
+        return launch(fwd_state_kernel<T, DK, DV, FM>, nblk, kThreads, s, kk, vv, state, sz, part, p.T, p.lay,
+                      p.P, p.L);
+}
+
+template <typename T, int DK, int DV, int FM>
+hipError_t fwd_state_fm(const Plan& p, const void* k, const void* v, float* state, void* ws,
+                       hipStream_t s) {
+    float* part = reinterpret_cast<float*>(static_cast<char*>(ws) + p.off_part);
+    const hipError_t e = launch_state_reduction<T, DK, DV, FM>(p, k, v, state, part, s);
     if (e != hipSuccess) return e;
-    return launch_combine<DK, DV>(p.P, part, state, sz, p.BH, s);
+    return launch_combine<DK, DV>(p.P, part, state, state + p.BH * DK * DV, p.BH, s);
+}
+
+// Where the causal forward exists: 16-bit elements, DK and DV in {64, 128}.
+template <typename T, int DK, int DV>
+constexpr bool kCausalKernels = sizeof(T) == 2 && (DK == 64 || DK == 128) && (DV == 64 || DV == 128);
+
+// Causal forward: segment states, their exclusive prefixes in place (and the
+// full state), then the chunked scan of every segment.
+template <typename T, int DK, int DV, int FM>
+hipError_t fwd_causal_fm(const Plan& p, const void* q, const void* k, const void* v, void* o, float* state,
+                         void* ws, hipStream_t s) {
+    if constexpr (!kCausalKernels<T, DK, DV>) {
+        return hipErrorInvalidValue;
+    } else {
+        float* part = reinterpret_cast<float*>(static_cast<char*>(ws) + p.off_part);
+        hipError_t e = launch_state_reduction<T, DK, DV, FM>(p, k, v, state, part, s);
+        if (e != hipSuccess) return e;
+        if (p.P > 1) {
+            constexpr int E4 = (DK * DV + DK) / 4;
+            e = launch(prefix_kernel<DK, DV>, p.BH * ((E4 + kThreads - 1) / kThreads), kThreads, s, part, p.P, state,
+                       state + p.BH * DK * DV, p.BH);
+            if (e != hipSuccess) return e;
+        }
+        const float* pre = p.P > 1 ? part : nullptr;
+        const T* qq = static_cast<const T*>(q);
+        const T* kk = static_cast<const T*>(k);
+        const T* vv = static_cast<const T*>(v);
+        T* oo = static_cast<T*>(o);
+        const int64_t nblk = p.BH * p.P;
+        if (p.simple)
+            return launch(fwd_causal_kernel<T, DK, DV, true, FM>, nblk, kThreads, s, qq, kk, vv, pre, oo, p.T, p.lay,
+                          p.P, p.L, p.eps);
+        return launch(fwd_causal_kernel<T, DK, DV, false, FM>, nblk, kThreads, s, qq, kk, vv, pre, oo, p.T, p.lay,
+                      p.P, p.L, p.eps);
+    }
 }
 
 template <typename T, int DK, int DV, int FM>
@@ -2334,6 +2729,15 @@ hipError_t fwd_output_t(const Plan& p, const void* q, const float* state, void* 
     LA_FEATURE_MAP(fwd_output_fm, q, state, o, s);
 }
 template <typename T, int DK, int DV>
+hipError_t fwd_causal_t(const Plan& p, const void* q, const void* k, const void* v, void* o, float* state, void* ws,
+                        hipStream_t s) {
+    if constexpr (!kCausalKernels<T, DK, DV>) {
+        return hipErrorInvalidValue;
+    } else {
+        LA_FEATURE_MAP(fwd_causal_fm, q, k, v, o, state, ws, s);
+    }
+}
+template <typename T, int DK, int DV>
 hipError_t bwd_dq_t(const Plan& p, const void* q, const void* dout, const float* state, void* dq, void* ws,
                     hipStream_t s) {
     LA_FEATURE_MAP(bwd_dq_fm, q, dout, state, dq, ws, s);
@@ -2406,6 +2810,10 @@ hipError_t unit_fwd_state(const Plan& p, const void* k, const void* v, float* st
 hipError_t unit_fwd_output(const Plan& p, const void* q, const float* state, void* o, hipStream_t s) {
     LA_DV_DISPATCH(fwd_output_t, q, state, o, s);
 }
+hipError_t unit_fwd_causal(const Plan& p, const void* q, const void* k, const void* v, void* o, float* state,
+                           void* ws, hipStream_t s) {
+    LA_DV_DISPATCH(fwd_causal_t, q, k, v, o, state, ws, s);
+}
 hipError_t unit_bwd_dq(const Plan& p, const void* q, const void* dout, const float* state, void* dq, void* ws,
                        hipStream_t s) {
     LA_DV_DISPATCH(bwd_dq_t, q, dout, state, dq, ws, s);
@@ -2422,7 +2830,8 @@ SplitCfg unit_split_config(int step, int DV) {
     }
 }
 
-const KernelSet kUnitSet = {unit_fwd_state, unit_fwd_output, unit_bwd_dq, unit_bwd_dkv, unit_split_config};
+const KernelSet kUnitSet = {unit_fwd_state, unit_fwd_output, unit_bwd_dq, unit_bwd_dkv, unit_split_config,
+                             unit_fwd_causal};
 
 }  // namespace
 

@@ -136,7 +136,7 @@ def test_fwd_rejects_bad_problems(L):
     assert fwd_call(L, prob(T=(1 << 31) // (128 * 2), D=32, Dv=128)) == SHAPE
     assert fwd_call(L, prob(T=(1 << 31) // (128 * 2), D=128, Dv=32)) == SHAPE
     assert L.la_workspace_bytes(ctypes.byref(prob(T=(1 << 31) // (128 * 2) - 1, D=32, Dv=128))) > 0
-    assert fwd_call(L, prob(flags=0x10)) == FLAGS
+    assert fwd_call(L, prob(flags=0x20)) == FLAGS
     assert fwd_call(L, prob(flags=0x80000000)) == FLAGS
     assert fwd_call(L, prob(flags=0x4 | 0x8)) == FLAGS  # two feature maps
     assert fwd_call(L, prob(eps=-1e-3)) == EPS
@@ -234,7 +234,7 @@ def test_step_calls_validate(L):
     assert L.la_fwd_state(ctypes.byref(p), d[0], d[1], d[2], d[3], need - 1, None) == WORKSPACE
     assert L.la_fwd_state(ctypes.byref(p), d[0], d[1], d[0], d[3], need, None) == ALIAS
     assert L.la_fwd_output(ctypes.byref(p), d[0], d[1], d[0], None) == ALIAS
-    assert L.la_fwd_output(ctypes.byref(prob(flags=0x10)), d[0], d[1], d[2], None) == FLAGS
+    assert L.la_fwd_output(ctypes.byref(prob(flags=0x20)), d[0], d[1], d[2], None) == FLAGS
     assert L.la_bwd_dq(ctypes.byref(p), d[0], d[1], z, d[3], d[4], need, None) == NULL
     assert L.la_bwd_dq(ctypes.byref(p), d[0], d[1], d[2], d[1], d[4], need, None) == ALIAS
     assert L.la_bwd_dkv(ctypes.byref(p), d[0], d[1], d[2], d[2], d[4], need, None) == ALIAS
@@ -284,3 +284,24 @@ def test_token_major_layout_limits(L):
     assert L.la_workspace_bytes(ctypes.byref(prob(B=1, H=H, T=t_max + 1, D=D))) > 0
     # B = 0 stays an empty problem (nothing launched) in either layout
     assert fwd_call(L, prob(B=0, flags=BTHD)) == 0
+
+
+def test_causal_flag_accepted_by_la_fwd_only(L):
+    """LA_CAUSAL: la_fwd takes it for f16/bf16 with D, Dv in {64, 128}; every
+    other entry point rejects it before any HIP call."""
+    CAUSAL = 0x10
+    p = prob(flags=CAUSAL)
+    need = L.la_workspace_bytes(ctypes.byref(p))
+    assert need > 0 and L.la_state_bytes(ctypes.byref(p)) > 0
+    assert fwd_call(L, prob(flags=CAUSAL, dtype=0)) == DTYPE
+    for d, dv in ((32, 0), (96, 0), (64, 32), (128, 96)):
+        assert fwd_call(L, prob(flags=CAUSAL, D=d, Dv=dv)) == HEAD_DIM, (d, dv)
+    d = addrs(9)
+    assert L.la_bwd(ctypes.byref(p), *d[:9], need, None) == FLAGS
+    assert L.la_fwd_state(ctypes.byref(p), d[0], d[1], d[2], d[3], need, None) == FLAGS
+    assert L.la_fwd_output(ctypes.byref(p), d[0], d[1], d[2], None) == FLAGS
+    assert L.la_bwd_dq(ctypes.byref(p), d[0], d[1], d[2], d[3], d[4], need, None) == FLAGS
+    assert L.la_bwd_dkv(ctypes.byref(p), d[0], d[1], d[2], d[3], d[4], need, None) == FLAGS
+    # an accepted causal call with an argument error still reports that error
+    assert fwd_call(L, p, ws_bytes=need - 1) == WORKSPACE
+    assert fwd_call(L, prob(flags=CAUSAL | 0x20)) == FLAGS
