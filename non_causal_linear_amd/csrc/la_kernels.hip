@@ -2205,47 +2205,63 @@ __global__ __launch_bounds__((StreamShape<T, DK, DV>::kThreads), (StreamShape<T,
 //   O_t = (phi(q_t) R + sum_{s in chunk, s <= t} a_ts v_s)
 //         / (phi(q_t) z + sum_{s in chunk, s <= t} a_ts + eps),  a_ts = phi(q_t) . phi(k_s),
 // then R += phi(K_c)^T V_c, z += sum phi(k). Per chunk, the four waves
-//   (a) each compute a = phi(Q) phi(K)^T for 16 query rows, mask s > t and
-//       stage it, scaled by a power of two, in their own LDS rows;
-//   (b) multiply it by [V | 1] and phi(Q) by [R | z] (R and z as 16-bit
-//       copies in LDS) and store their 16 rows of O;
+//   (a) each compute a = phi(Q) phi(K)^T for 16 query rows (blocks above the
+//       diagonal skipped, the diagonal block masked) and stage it transposed,
+//       scaled by a power of two, in their own LDS area;
+//   (b) multiply it by [V | 1] and phi(Q) by [R | z] (R^T and z as 16-bit
+//       copies in LDS) and store their 16 rows of O, staged transposed;
 //   (c) add phi(K)^T V into their quarter of R's columns (fp32 registers;
 //       wave 0 also keeps z) and publish it, scaled by the wave's own power
-//       of two, into the other LDS copy of R for the next chunk.
-// Two barriers per chunk; the next chunk's loads are issued after the first.
-// Rows past the segment end load as zeros (K is zeroed after phi) and their
-// stores are dropped.
+//       of two, into the other LDS copy of R^T for the next chunk.
+// Staging is transposed wherever a lane's four MFMA results are consecutive
+// in the transposed matrix: each is one 8-byte LDS store, and transposed
+// reads give the operands back. Two barriers per chunk; two chunks of loads
+// in flight. Rows past the segment end load as zeros (K is zeroed after phi)
+// and their stores are dropped.
 template <int DK, int DV>
 struct CausalShape {
     static constexpr int kChunk = 64;                 // tokens per chunk
     static constexpr int kLDK = DK + 16;              // tQ, tK row stride (elements)
-    static constexpr int kLDV = DV + 16;              // tV, tR row stride
-    static constexpr int kLDA = (kChunk > DV ? kChunk : DV) + 8;  // a / O staging row stride
+    static constexpr int kLDV = DV + 16;              // tV row stride
+    static constexpr int kLDRT = DK + 8;              // R^T row stride (rows j, DK entries)
+    static constexpr int kLDW = 24;                   // per-wave a^T / O^T tiles: rows of 16 tokens
+    static constexpr int kWRows = kChunk > DV ? kChunk : DV;  // rows of the per-wave tile
     static constexpr int kMinBlocks = (DK == 64 && DV == 64) ? 2 : 1;
 };
+
+// Largest x over the 64 lanes of the wave (x >= 0): DPP row shifts and
+// broadcasts (lanes shifted in from outside a row read 0), then lane 63.
+__device__ __forceinline__ float wave_max_nonneg(float x) {
+    x = fmaxf(x, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x111, 0xf, 0xf, true)));
+    x = fmaxf(x, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x112, 0xf, 0xf, true)));
+    x = fmaxf(x, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x114, 0xf, 0xf, true)));
+    x = fmaxf(x, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x118, 0xf, 0xf, true)));
+    x = fmaxf(x, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x142, 0xa, 0xf, false)));
+    x = fmaxf(x, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x143, 0xc, 0xf, false)));
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 63));
+}
 
 template <typename T, int DK, int DV, bool SIMPLE, int FM>
 __global__ __launch_bounds__(kThreads, (CausalShape<DK, DV>::kMinBlocks)) void fwd_causal_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const float* __restrict__ pre,
     T* __restrict__ o, int64_t T_, const Layout lay, int P, int64_t L, float eps) {
     using Sh = CausalShape<DK, DV>;
-    constexpr int C = Sh::kChunk, LDK = Sh::kLDK, LDV = Sh::kLDV, LDA = Sh::kLDA;
+    constexpr int C = Sh::kChunk, LDK = Sh::kLDK, LDV = Sh::kLDV, LDRT = Sh::kLDRT, LDW = Sh::kLDW;
     constexpr int NBV = DV / 16;         // output column blocks
     constexpr int RJ = DV / 64;          // R column blocks per wave (a quarter of DV)
     constexpr int RI = DK / 16;          // R row blocks
     constexpr int KSK = DK / 32, KSC = C / 32;
     constexpr int CK = DK / 8, CV = DV / 8;  // 16-byte chunks per row
     constexpr int NCK = C * CK / kThreads, NCV = C * CV / kThreads;
-    constexpr int NST = 16 * CV / 64;    // 16-byte O chunks per lane per wave tile
     static_assert(sizeof(T) == 2, "transposed LDS reads take 16-bit elements");
-    static_assert(NCK * kThreads == C * CK && NCV * kThreads == C * CV && NST * 64 == 16 * CV, "tiles must split");
+    static_assert(NCK * kThreads == C * CK && NCV * kThreads == C * CV, "tiles must split evenly");
     static_assert(RJ >= 1 && RJ * 64 == DV, "each wave owns whole 16-column blocks of R");
     __shared__ __attribute__((aligned(16))) T tQ[C * LDK];
     __shared__ __attribute__((aligned(16))) T tK[C * LDK];
     __shared__ __attribute__((aligned(16))) T tV[C * LDV];
-    __shared__ __attribute__((aligned(16))) T tR[2][DK * LDV];
+    __shared__ __attribute__((aligned(16))) T tRT[2][DV * LDRT];
     __shared__ __attribute__((aligned(16))) T tZ[2][DK];
-    __shared__ __attribute__((aligned(16))) T tA[kWaves][16 * LDA];
+    __shared__ __attribute__((aligned(16))) T tW[kWaves][Sh::kWRows * LDW];
     __shared__ int sExp[2][kWaves + 1];  // exponents of the R quarters, then of z
 
     const int wid = xcd_remap(blockIdx.x, gridDim.x);
@@ -2279,45 +2295,49 @@ __global__ __launch_bounds__(kThreads, (CausalShape<DK, DV>::kMinBlocks)) void f
 #pragma unroll
     for (int e = 0; e < 8; ++e) ones[e] = static_cast<T>(1.f);
 
-    auto wave_max = [](float x) {
+    // Four consecutive 16-bit values as one 8-byte LDS store.
+    auto put4 = [](T* dst, f32x4 x, float f) {
+        typedef T t4 __attribute__((ext_vector_type(4)));
+        t4 y;
 #pragma unroll
-        for (int off = 32; off > 0; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
-        return x;
+        for (int r = 0; r < 4; ++r) y[r] = static_cast<T>(x[r] * f);
+        *reinterpret_cast<t4*>(dst) = y;
     };
-    // this wave's quarter of R (and z, wave 0) as 16-bit into copy `buf`
+    // this wave's quarter of R (as R^T) and z (wave 0) as 16-bit into copy `buf`
     auto publish = [&](int buf) {
-        float mx = 0.f;
+        int sR = 0;
+        if constexpr (Elt<T>::kScaled) {
+            float mx = 0.f;
 #pragma unroll
-        for (int iR = 0; iR < RI; ++iR)
+            for (int iR = 0; iR < RI; ++iR)
 #pragma unroll
-            for (int jR = 0; jR < RJ; ++jR)
+                for (int jR = 0; jR < RJ; ++jR)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) mx = fmaxf(mx, fabsf(accR[iR][jR][r]));
-        const int sR = Elt<T>::kScaled ? scale_exp(wave_max(mx)) : 0;
+                    for (int r = 0; r < 4; ++r) mx = fmaxf(mx, fabsf(accR[iR][jR][r]));
+            sR = scale_exp(wave_max_nonneg(mx));
+        }
         const float fR = ldexpf(1.f, sR);
 #pragma unroll
         for (int iR = 0; iR < RI; ++iR)
 #pragma unroll
             for (int jR = 0; jR < RJ; ++jR)
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    tR[buf][(16 * iR + 4 * grp + r) * LDV + 16 * (wave * RJ + jR) + m] =
-                        static_cast<T>(accR[iR][jR][r] * fR);
+                put4(&tRT[buf][(16 * (wave * RJ + jR) + m) * LDRT + 16 * iR + 4 * grp], accR[iR][jR], fR);
         if (lane == 0) sExp[buf][wave] = sR;
         if constexpr (!SIMPLE) {
             if (wave == 0) {
-                float mz = 0.f;
-#pragma unroll
-                for (int iR = 0; iR < RI; ++iR)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) mz = fmaxf(mz, fabsf(accZ[iR][r]));
-                const int sZ = Elt<T>::kScaled ? scale_exp(wave_max(mz)) : 0;
-                const float fZ = ldexpf(1.f, sZ);
-                if (m == 0)
+                int sZ = 0;
+                if constexpr (Elt<T>::kScaled) {
+                    float mz = 0.f;
 #pragma unroll
                     for (int iR = 0; iR < RI; ++iR)
 #pragma unroll
-                        for (int r = 0; r < 4; ++r) tZ[buf][16 * iR + 4 * grp + r] = static_cast<T>(accZ[iR][r] * fZ);
+                        for (int r = 0; r < 4; ++r) mz = fmaxf(mz, fabsf(accZ[iR][r]));
+                    sZ = scale_exp(wave_max_nonneg(mz));
+                }
+                const float fZ = ldexpf(1.f, sZ);
+                if (m == 0)
+#pragma unroll
+                    for (int iR = 0; iR < RI; ++iR) put4(&tZ[buf][16 * iR + 4 * grp], accZ[iR], fZ);
                 if (lane == 0) sExp[buf][kWaves] = sZ;
             }
         }
@@ -2369,17 +2389,18 @@ __global__ __launch_bounds__(kThreads, (CausalShape<DK, DV>::kMinBlocks)) void f
     };
 
     const int rA = 8 * grp + (m >> 2), cA = 4 * (m & 3);
-    T* myA = tA[wave];
+    T* myW = tW[wave];
     auto body = [&](Stage& st, int c) {
         const int cur = c & 1;
         const int64_t row0 = (int64_t)c * C;
         consume(st, c);
-        __syncthreads();  // tiles of chunk c and the R, z copy `cur` are visible
+        __syncthreads();  // tiles of chunk c and the R^T, z copy `cur` are visible
         sched_fence();
         issue(st, c + 2);  // two chunks ahead; past the segment end these read zeros
         sched_fence();
 
-        // (a) a[t][s] for t = 16 wave + 4 grp + r (chunk rows), s = 16 jb + m
+        // (a) a[t][s], t = 16 wave + 4 grp + r, s = 16 jb + m: blocks jb < wave
+        // are below the diagonal, jb = wave is masked, jb > wave stays zero
         f32x4 aa[C / 16];
 #pragma unroll
         for (int jb = 0; jb < C / 16; ++jb) aa[jb] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -2388,25 +2409,31 @@ __global__ __launch_bounds__(kThreads, (CausalShape<DK, DV>::kMinBlocks)) void f
             const Frag<T> a = *reinterpret_cast<const Frag<T>*>(&tQ[(16 * wave + m) * LDK + 32 * ks + 8 * grp]);
 #pragma unroll
             for (int jb = 0; jb < C / 16; ++jb) {
-                const Frag<T> b = *reinterpret_cast<const Frag<T>*>(&tK[(16 * jb + m) * LDK + 32 * ks + 8 * grp]);
-                aa[jb] = mma(a, b, aa[jb]);
+                if (jb <= wave) {
+                    const Frag<T> b = *reinterpret_cast<const Frag<T>*>(&tK[(16 * jb + m) * LDK + 32 * ks + 8 * grp]);
+                    aa[jb] = mma(a, b, aa[jb]);
+                }
             }
         }
-        float amax = 0.f;
 #pragma unroll
         for (int jb = 0; jb < C / 16; ++jb)
+            if (jb == wave)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                if (16 * jb + m > 16 * wave + 4 * grp + r) aa[jb][r] = 0.f;
-                amax = fmaxf(amax, fabsf(aa[jb][r]));
-            }
-        const int sA = Elt<T>::kScaled ? scale_exp(wave_max(amax)) : 0;
-        {
-            const float fA = ldexpf(1.f, sA);
+                for (int r = 0; r < 4; ++r) aa[jb][r] = m > 4 * grp + r ? 0.f : aa[jb][r];
+        int sA = 0;
+        if constexpr (Elt<T>::kScaled) {
+            float amax = 0.f;
 #pragma unroll
             for (int jb = 0; jb < C / 16; ++jb)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) myA[(4 * grp + r) * LDA + 16 * jb + m] = static_cast<T>(aa[jb][r] * fA);
+                for (int r = 0; r < 4; ++r) amax = fmaxf(amax, fabsf(aa[jb][r]));
+            sA = scale_exp(wave_max_nonneg(amax));
+        }
+        {
+            const float fA = ldexpf(1.f, sA);
+            // a^T: row s, columns t = 4 grp .. 4 grp + 3 of this wave
+#pragma unroll
+            for (int jb = 0; jb < C / 16; ++jb) put4(&myW[(16 * jb + m) * LDW + 4 * grp], aa[jb], fA);
         }
         wave_lds_sync();
 
@@ -2419,8 +2446,8 @@ __global__ __launch_bounds__(kThreads, (CausalShape<DK, DV>::kMinBlocks)) void f
         }
 #pragma unroll
         for (int ks = 0; ks < KSC; ++ks) {
-            const Frag<T> a = *reinterpret_cast<const Frag<T>*>(&myA[m * LDA + 32 * ks + 8 * grp]);
             const int rb = 32 * ks + rA;
+            const Frag<T> a = join_frag<T>(lds_read_tr(&myW[rb * LDW + cA]), lds_read_tr(&myW[(rb + 4) * LDW + cA]));
 #pragma unroll
             for (int jb = 0; jb < NBV; ++jb) {
                 const Frag<T> b = join_frag<T>(lds_read_tr(&tV[rb * LDV + 16 * jb + cA]),
@@ -2432,11 +2459,9 @@ __global__ __launch_bounds__(kThreads, (CausalShape<DK, DV>::kMinBlocks)) void f
 #pragma unroll
         for (int ks = 0; ks < KSK; ++ks) {
             const Frag<T> a = *reinterpret_cast<const Frag<T>*>(&tQ[(16 * wave + m) * LDK + 32 * ks + 8 * grp]);
-            const int rb = 32 * ks + rA;
 #pragma unroll
             for (int jb = 0; jb < NBV; ++jb) {
-                const Frag<T> b = join_frag<T>(lds_read_tr(&tR[cur][rb * LDV + 16 * jb + cA]),
-                                               lds_read_tr(&tR[cur][(rb + 4) * LDV + 16 * jb + cA]));
+                const Frag<T> b = *reinterpret_cast<const Frag<T>*>(&tRT[cur][(16 * jb + m) * LDRT + 32 * ks + 8 * grp]);
                 nR[jb] = mma(a, b, nR[jb]);
             }
             if constexpr (!SIMPLE) {
@@ -2446,29 +2471,32 @@ __global__ __launch_bounds__(kThreads, (CausalShape<DK, DV>::kMinBlocks)) void f
         }
         {
             const float uA = ldexpf(1.f, -sA);
-            float inv[4];
+            f32x4 ia, ir;  // per row: factors on the a part and (times 2^-sR) on the R part
 #pragma unroll
-            for (int r = 0; r < 4; ++r) inv[r] = 1.f;
-            if constexpr (!SIMPLE) {
-                const float uZ = ldexpf(1.f, -sExp[cur][kWaves]);
-#pragma unroll
-                for (int r = 0; r < 4; ++r) inv[r] = 1.f / (dA[r] * uA + dR[r] * uZ + eps);
+            for (int r = 0; r < 4; ++r) {
+                float inv = 1.f;
+                if constexpr (!SIMPLE) inv = 1.f / (dA[r] * uA + dR[r] * ldexpf(1.f, -sExp[cur][kWaves]) + eps);
+                ia[r] = uA * inv;
+                ir[r] = inv;
             }
             wave_lds_sync();
 #pragma unroll
             for (int jb = 0; jb < NBV; ++jb) {
                 const float uR = ldexpf(1.f, -sExp[cur][jb / RJ]);
+                f32x4 y;
 #pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    myA[(4 * grp + r) * LDA + 16 * jb + m] = static_cast<T>((nA[jb][r] * uA + nR[jb][r] * uR) * inv[r]);
+                for (int r = 0; r < 4; ++r) y[r] = nA[jb][r] * ia[r] + nR[jb][r] * (uR * ir[r]);
+                // O^T: row j, columns t = 4 grp .. 4 grp + 3 of this wave
+                put4(&myW[(16 * jb + m) * LDW + 4 * grp], y, 1.f);
             }
         }
         wave_lds_sync();
+        // row t = m of this wave, columns 32 kk + 8 grp .. + 7
 #pragma unroll
-        for (int kk = 0; kk < NST; ++kk) {
-            const int n = 64 * kk + lane, r = n / CV, cc = n % CV;
-            const uint4 x = *reinterpret_cast<const uint4*>(&myA[r * LDA + 8 * cc]);
-            buf_store16(bo, buf_off<T>(row0 + 16 * wave + r, lv.rs, 8 * cc), x);
+        for (int kk = 0; kk < DV / 32; ++kk) {
+            const int rb = 32 * kk + rA;
+            const Frag<T> x = join_frag<T>(lds_read_tr(&myW[rb * LDW + cA]), lds_read_tr(&myW[(rb + 4) * LDW + cA]));
+            buf_store16(bo, buf_off<T>(row0 + 16 * wave + m, lv.rs, 32 * kk + 8 * grp), __builtin_bit_cast(uint4, x));
         }
         wave_lds_sync();
 
