@@ -1141,6 +1141,27 @@ __global__ __launch_bounds__((StreamShape<T, DK, DV>::kThreads), (StreamShape<T,
     const float* S = stS + bh * DK * DV;
     const float* z = stz + bh * DK;
 
+    // The first two turns' loads are issued before the prologue, which they
+    // overlap. Each wave takes blocks of 16 U tokens, NW blocks apart, with the
+    // loads of its next two blocks in flight while it computes one. Blocks go
+    // in rotated order, two per turn with no early exit; rows are counted from
+    // c0, rows past the chunk end load as zeros and their stores are dropped.
+    constexpr int BT = 16 * U;
+    const HeadBuf bq = slice_buf(q, lk, bh, DK, c0, c1), bo = slice_buf(o, lv, bh, DV, c0, c1);
+    constexpr int NS = Sh::kStages;
+    const Rotation rot((int)((c1 - c0 + BT - 1) / BT), NS * NW, wid);
+    T* stg = stage + wave * 16 * LDR;
+    auto issue = [&](Row<T, FK> (&b)[U], int blk) {
+        const int64_t bs = (int64_t)rot(blk) * BT;
+#pragma unroll
+        for (int u = 0; u < U; ++u) load_row_buf<T, FK>(b[u], bq, bs + 16 * u + m, lk.rs, FK * grp);
+    };
+    Row<T, FK> stg_q[NS][U];
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+        issue(stg_q[i], wave + i * NW);
+        sched_fence();
+    }
     int sS = 0, sz = 0;
     if constexpr (kStaged) {
         constexpr int LD = StagedState<DK, DV>::kLD;
@@ -1171,20 +1192,6 @@ __global__ __launch_bounds__((StreamShape<T, DK, DV>::kThreads), (StreamShape<T,
     __syncthreads();
     const float uS = ldexpf(1.f, -sS), uz = ldexpf(1.f, -sz);
 
-    // Each wave takes blocks of 16 U tokens, NW blocks apart, with the
-    // loads of its next two blocks in flight while it computes one. Blocks go
-    // in rotated order, two per turn with no early exit; rows are counted from
-    // c0, rows past the chunk end load as zeros and their stores are dropped.
-    constexpr int BT = 16 * U;
-    const HeadBuf bq = slice_buf(q, lk, bh, DK, c0, c1), bo = slice_buf(o, lv, bh, DV, c0, c1);
-    constexpr int NS = Sh::kStages;
-    const Rotation rot((int)((c1 - c0 + BT - 1) / BT), NS * NW, wid);
-    T* stg = stage + wave * 16 * LDR;
-    auto issue = [&](Row<T, FK> (&b)[U], int blk) {
-        const int64_t bs = (int64_t)rot(blk) * BT;
-#pragma unroll
-        for (int u = 0; u < U; ++u) load_row_buf<T, FK>(b[u], bq, bs + 16 * u + m, lk.rs, FK * grp);
-    };
     auto body = [&](Row<T, FK> (&qr)[U], int blk) {
         Frag<T> bq[U][KS];
 #pragma unroll
@@ -1239,12 +1246,6 @@ __global__ __launch_bounds__((StreamShape<T, DK, DV>::kThreads), (StreamShape<T,
             store_tile_rows<T, DV>(stg, out, bo, (int64_t)rot(blk) * BT + 16 * u, lv.rs);
         }
     };
-    Row<T, FK> stg_q[NS][U];
-#pragma unroll
-    for (int i = 0; i < NS; ++i) {
-        issue(stg_q[i], wave + i * NW);
-        sched_fence();
-    }
     for (int blk = wave; blk < rot.npad; blk += NS * NW) {
 #pragma unroll
         for (int i = 0; i < NS; ++i) body(stg_q[i], blk + i * NW);
@@ -1528,6 +1529,34 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_w64_kernel(
     T* sW = sQ + STEP * LDR;
     T* sO = sW + STEP * LDR;
 
+    // A stage holds the loaded words as they are; unpacked at the load, the
+    // halves would be carried around the loop and unpacking them would wait
+    // for the loads right after they are issued.
+    struct Stage {
+        u32x4 q[2], d[2];
+    };
+    // Rows past the slice end load as zeros (dO = 0 gives u = 0, r = 0,
+    // beta = 0, so such rows add nothing to dS or dz) and their dQ stores are
+    // dropped. Rows are counted from t0.
+    const HeadBuf bq = slice_buf(q, lay, bh, D, t0, t1), bd = slice_buf(dout, lay, bh, D, t0, t1),
+                  bdq = slice_buf(dq, lay, bh, D, t0, t1);
+    const Rotation rot(nsteps, BwdQW64::kStages * kWaves, wid);
+    auto issue = [&](Stage& st, int step) {
+        const int off = buf_off<T>((int64_t)rot(step) * STEP + m, lay.rs, F * grp);
+        st.q[0] = __builtin_amdgcn_raw_buffer_load_b128(bq.rsrc, off, 0, 0);
+        st.q[1] = __builtin_amdgcn_raw_buffer_load_b128(bq.rsrc, off + 16, 0, 0);
+        st.d[0] = __builtin_amdgcn_raw_buffer_load_b128(bd.rsrc, off, 0, 0);
+        st.d[1] = __builtin_amdgcn_raw_buffer_load_b128(bd.rsrc, off + 16, 0, 0);
+    };
+    // The first two steps' loads are issued before the prologue, which they
+    // overlap (with no steps they read zeros and the loop below does not run).
+    constexpr int kStages = BwdQW64::kStages;
+    Stage stg[kStages];
+#pragma unroll
+    for (int i = 0; i < kStages; ++i) {
+        issue(stg[i], wave + i * kWaves);
+        sched_fence();
+    }
     // The state is staged in the tile area (which the loop alone uses) and
     // the fragments are built from there.
     static_assert(StagedState<D, D>::kFloats * 4 <= kTileBytes, "state staging exceeds the tile area");
@@ -1563,25 +1592,6 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_w64_kernel(
 #pragma unroll
         for (int j = 0; j < NJ; ++j) dsacc[b][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // A stage holds the loaded words as they are; unpacked at the load, the
-    // halves would be carried around the loop and unpacking them would wait
-    // for the loads right after they are issued.
-    struct Stage {
-        u32x4 q[2], d[2];
-    };
-    // Rows past the slice end load as zeros (dO = 0 gives u = 0, r = 0,
-    // beta = 0, so such rows add nothing to dS or dz) and their dQ stores are
-    // dropped. Rows are counted from t0.
-    const HeadBuf bq = slice_buf(q, lay, bh, D, t0, t1), bd = slice_buf(dout, lay, bh, D, t0, t1),
-                  bdq = slice_buf(dq, lay, bh, D, t0, t1);
-    const Rotation rot(nsteps, BwdQW64::kStages * kWaves, wid);
-    auto issue = [&](Stage& st, int step) {
-        const int off = buf_off<T>((int64_t)rot(step) * STEP + m, lay.rs, F * grp);
-        st.q[0] = __builtin_amdgcn_raw_buffer_load_b128(bq.rsrc, off, 0, 0);
-        st.q[1] = __builtin_amdgcn_raw_buffer_load_b128(bq.rsrc, off + 16, 0, 0);
-        st.d[0] = __builtin_amdgcn_raw_buffer_load_b128(bd.rsrc, off, 0, 0);
-        st.d[1] = __builtin_amdgcn_raw_buffer_load_b128(bd.rsrc, off + 16, 0, 0);
-    };
     const int rA = 4 * grp + (m >> 2), cA = 4 * (m & 3);
     auto body = [&](Stage& st, int step) {
         sched_fence();  // keeps this stage's unpacking out of the previous step
@@ -1672,18 +1682,9 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_w64_kernel(
         wave_lds_sync();
     };
 
-    if (nsteps > 0) {
-        constexpr int kStages = BwdQW64::kStages;
-        Stage stg[kStages];
+    for (int st = wave; st < rot.npad; st += kStages * kWaves) {
 #pragma unroll
-        for (int i = 0; i < kStages; ++i) {
-            issue(stg[i], wave + i * kWaves);
-            sched_fence();
-        }
-        for (int st = wave; st < rot.npad; st += kStages * kWaves) {
-#pragma unroll
-            for (int i = 0; i < kStages; ++i) body(stg[i], st + i * kWaves);
-        }
+        for (int i = 0; i < kStages; ++i) body(stg[i], st + i * kWaves);
     }
 
     // fixed-order sum of the four waves: (w0 + w2) + (w1 + w3); column 0 of
@@ -1810,6 +1811,29 @@ __global__ __launch_bounds__((BwdQTile<DK, DV>::kThreads), (BwdQTile<DK, DV>::kM
     T* tA = reinterpret_cast<T*>(smem + kFragBytes);
     T* tW = tA + RT * LDA;
 
+    // The loaded words as they are (see the D = 64 kernel).
+    struct Stage {
+        u32x4 q[NQK], d[NQV];
+    };
+    const HeadBuf bq = slice_buf(q, lk, bh, DK, t0, t1), bd = slice_buf(dout, lv, bh, DV, t0, t1),
+                  bdq = slice_buf(dq, lk, bh, DK, t0, t1);
+    const Rotation rot(nrounds, Sh::kStages, wid);
+    auto issue = [&](Stage& st, int round) {
+        const int64_t row = (int64_t)rot(round) * RT + wave * STEP + m;
+        const int oq = buf_off<T>(row, lk.rs, FK * grp), od = buf_off<T>(row, lv.rs, FV * grp);
+#pragma unroll
+        for (int i = 0; i < (NQK > NQV ? NQK : NQV); ++i) {
+            if (i < NQK) st.q[i] = __builtin_amdgcn_raw_buffer_load_b128(bq.rsrc, oq + 16 * i, 0, 0);
+            if (i < NQV) st.d[i] = __builtin_amdgcn_raw_buffer_load_b128(bd.rsrc, od + 16 * i, 0, 0);
+        }
+    };
+    // The first two rounds' loads are issued before the prologue, which they
+    // overlap (with no rounds they read zeros and the loop below does not run).
+    Stage s0, s1;
+    issue(s0, 0);
+    sched_fence();
+    issue(s1, 1);
+    sched_fence();
     // The state is staged in the tile area (which the rounds alone use) and
     // the fragments are built from there.
     int sS = 0, sz = 0, sw = 0;
@@ -1843,22 +1867,6 @@ __global__ __launch_bounds__((BwdQTile<DK, DV>::kThreads), (BwdQTile<DK, DV>::kM
 #pragma unroll
     for (int j = 0; j < NJ; ++j) dsacc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // The loaded words as they are (see the D = 64 kernel).
-    struct Stage {
-        u32x4 q[NQK], d[NQV];
-    };
-    const HeadBuf bq = slice_buf(q, lk, bh, DK, t0, t1), bd = slice_buf(dout, lv, bh, DV, t0, t1),
-                  bdq = slice_buf(dq, lk, bh, DK, t0, t1);
-    const Rotation rot(nrounds, Sh::kStages, wid);
-    auto issue = [&](Stage& st, int round) {
-        const int64_t row = (int64_t)rot(round) * RT + wave * STEP + m;
-        const int oq = buf_off<T>(row, lk.rs, FK * grp), od = buf_off<T>(row, lv.rs, FV * grp);
-#pragma unroll
-        for (int i = 0; i < (NQK > NQV ? NQK : NQV); ++i) {
-            if (i < NQK) st.q[i] = __builtin_amdgcn_raw_buffer_load_b128(bq.rsrc, oq + 16 * i, 0, 0);
-            if (i < NQV) st.d[i] = __builtin_amdgcn_raw_buffer_load_b128(bd.rsrc, od + 16 * i, 0, 0);
-        }
-    };
     const int rA = 8 * grp + (m >> 2), cA = 4 * (m & 3);
     const int row = wave * STEP + m;  // this lane's token within the round tile
     auto body = [&](Stage& st, int round) {
@@ -1955,16 +1963,9 @@ __global__ __launch_bounds__((BwdQTile<DK, DV>::kThreads), (BwdQTile<DK, DV>::kM
         __syncthreads();
     };
 
-    if (nrounds > 0) {
-        Stage s0, s1;
-        issue(s0, 0);
-        sched_fence();
-        issue(s1, 1);
-        sched_fence();
-        for (int r = 0; r < rot.npad; r += 2) {
-            body(s0, r);
-            body(s1, r + 1);
-        }
+    for (int r = 0; r < rot.npad; r += 2) {
+        body(s0, r);
+        body(s1, r + 1);
     }
 
     // wave w holds rows [16 w, 16 w + 16) of 2^sw dS; column 0 of the last
@@ -2033,6 +2034,41 @@ __global__ __launch_bounds__((StreamShape<T, DK, DV>::kThreads), (StreamShape<T,
     const float* dS = dSg + bh * DK * DV;
     const float* dz = dzg + bh * DK;
 
+    // The first two turns' loads are issued before the prologue, which they
+    // overlap. Rows are counted from c0. The loop takes two blocks per turn with no
+    // early exit (an exit makes the compiler wait for every load in flight
+    // where the paths join): the chunk's buffer descriptors read rows past its
+    // end as zeros and drop their stores.
+    const HeadBuf bk = slice_buf(k, lk, bh, DK, c0, c1), bv_ = slice_buf(v, lv, bh, DV, c0, c1);
+    const HeadBuf bdk = slice_buf(dk, lk, bh, DK, c0, c1), bdv = slice_buf(dv, lv, bh, DV, c0, c1);
+    T* stg = stage + (kStage ? wave * 16 * LDR : 0);
+    // The loaded words as they are (see the dQ kernel).
+    constexpr int NQK = FK * (int)sizeof(T) / 16;  // 16-byte words per quarter row of K
+    constexpr int NQV = FV * (int)sizeof(T) / 16;  // ... of V
+    struct Stage {
+        u32x4 k[U][NQK], v[U][NQV];
+    };
+    constexpr int NS = Sh::kStages;
+    const Rotation rot((int)((c1 - c0 + 16 * U - 1) / (16 * U)), NS * NW, wid);
+    auto issue = [&](Stage& st, int blk) {
+        const int64_t bs = (int64_t)rot(blk) * 16 * U;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int ok_ = buf_off<T>(bs + 16 * u + m, lk.rs, FK * grp);
+            const int ov_ = buf_off<T>(bs + 16 * u + m, lv.rs, FV * grp);
+#pragma unroll
+            for (int i = 0; i < (NQK > NQV ? NQK : NQV); ++i) {
+                if (i < NQK) st.k[u][i] = __builtin_amdgcn_raw_buffer_load_b128(bk.rsrc, ok_ + 16 * i, 0, 0);
+                if (i < NQV) st.v[u][i] = __builtin_amdgcn_raw_buffer_load_b128(bv_.rsrc, ov_ + 16 * i, 0, 0);
+            }
+        }
+    };
+    Stage stq[NS];
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+        issue(stq[i], wave + i * NW);
+        sched_fence();
+    }
     // fragments [0, NF1): dK side, rows i, contraction j -> dS[i][j];
     // [NF1, NF1 + NF2): dV side, rows j, contraction i -> dS[i][j]
     int sD = 0;
@@ -2062,34 +2098,6 @@ __global__ __launch_bounds__((StreamShape<T, DK, DV>::kThreads), (StreamShape<T,
     const float uD = ldexpf(1.f, -sD);
     __syncthreads();
 
-    // Rows are counted from c0. The loop takes two blocks per turn with no
-    // early exit (an exit makes the compiler wait for every load in flight
-    // where the paths join): the chunk's buffer descriptors read rows past its
-    // end as zeros and drop their stores.
-    const HeadBuf bk = slice_buf(k, lk, bh, DK, c0, c1), bv_ = slice_buf(v, lv, bh, DV, c0, c1);
-    const HeadBuf bdk = slice_buf(dk, lk, bh, DK, c0, c1), bdv = slice_buf(dv, lv, bh, DV, c0, c1);
-    T* stg = stage + (kStage ? wave * 16 * LDR : 0);
-    // The loaded words as they are (see the dQ kernel).
-    constexpr int NQK = FK * (int)sizeof(T) / 16;  // 16-byte words per quarter row of K
-    constexpr int NQV = FV * (int)sizeof(T) / 16;  // ... of V
-    struct Stage {
-        u32x4 k[U][NQK], v[U][NQV];
-    };
-    constexpr int NS = Sh::kStages;
-    const Rotation rot((int)((c1 - c0 + 16 * U - 1) / (16 * U)), NS * NW, wid);
-    auto issue = [&](Stage& st, int blk) {
-        const int64_t bs = (int64_t)rot(blk) * 16 * U;
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int ok_ = buf_off<T>(bs + 16 * u + m, lk.rs, FK * grp);
-            const int ov_ = buf_off<T>(bs + 16 * u + m, lv.rs, FV * grp);
-#pragma unroll
-            for (int i = 0; i < (NQK > NQV ? NQK : NQV); ++i) {
-                if (i < NQK) st.k[u][i] = __builtin_amdgcn_raw_buffer_load_b128(bk.rsrc, ok_ + 16 * i, 0, 0);
-                if (i < NQV) st.v[u][i] = __builtin_amdgcn_raw_buffer_load_b128(bv_.rsrc, ov_ + 16 * i, 0, 0);
-            }
-        }
-    };
     auto body = [&](Stage& st, int blk) {
         const int64_t base = (int64_t)rot(blk) * 16 * U;
         sched_fence();
@@ -2183,12 +2191,6 @@ __global__ __launch_bounds__((StreamShape<T, DK, DV>::kThreads), (StreamShape<T,
             }
         }
     };
-    Stage stq[NS];
-#pragma unroll
-    for (int i = 0; i < NS; ++i) {
-        issue(stq[i], wave + i * NW);
-        sched_fence();
-    }
     for (int blk = wave; blk < rot.npad; blk += NS * NW) {
 #pragma unroll
         for (int i = 0; i < NS; ++i) body(stq[i], blk + i * NW);
