@@ -27,9 +27,14 @@ differences of the loss, torch fp64 autograd of the quadratic form, and two
 backward identities; for the causal form, a pure-Python masked brute force,
 agreement of the two causal forms, the last row against the non-causal form,
 the first row's closed form, and independence of earlier rows from later
-tokens. No function here is "parity unpinned".
+tokens; for the causal backward, torch fp64 autograd of the masked quadratic
+form, central finite differences, the non-causal backward when only the last
+row has a gradient, and the dV column-sum identity. No function here is
+"parity unpinned".
 """
 from .la_oracle import (  # noqa: F401
+    causal_bwd,
+    causal_bwd_head,
     causal_fwd,
     causal_quadratic_head,
     causal_recurrent_head,

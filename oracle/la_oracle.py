@@ -282,3 +282,58 @@ def causal_fwd(q, k, v, dtype: str, eps: float, simple: bool, fm: str = "elu1"):
         o[h], s[h], z[h] = causal_recurrent_head(qh[h], kh[h], vh[h], eps, simple, fm)
     return (o.reshape(lead + (dv,)), s.reshape(lead[:-1] + (dk, dv)),
             z.reshape(lead[:-1] + (dk,)))
+
+
+def causal_bwd_head(q, k, v, do, eps: float, simple: bool, fm: str = "elu1"):
+    """Vector-Jacobian product of L = sum(O * dO) for the causal form of one
+    (batch, head), eps held constant: the chain rule through the recurrent
+    form (causal_recurrent_head). With the inclusive prefixes S_t, z_t,
+      den_t = phi(q_t) . z_t + eps,  u_t = S_t dO_t,  r_t = phi(q_t) . u_t,
+      c_t = -r_t / den_t^2,  w_t = dO_t / den_t,
+      dphi(q_t) = u_t / den_t + c_t z_t           (simple_la: u_t)
+    and with the suffixes G_s = sum_{t >= s} phi(q_t) w_t^T (simple_la: dO_t),
+    g_s = sum_{t >= s} c_t phi(q_t) (simple_la: 0),
+      dphi(k_s) = G_s v_s + g_s,  dV_s = G_s^T phi(k_s).
+    dQ = dphi(q) * phi'(q), dK = dphi(k) * phi'(k). Returns (dQ, dK, dV)."""
+    qt, kt = phi(q, fm), phi(k, fm)
+    v = np.asarray(v, dtype=np.float64)
+    do = np.asarray(do, dtype=np.float64)
+    T, dk = kt.shape
+    dv_ = v.shape[1]
+    s = np.zeros((dk, dv_))
+    z = np.zeros(dk)
+    dqt = np.empty((T, dk))
+    w = np.empty((T, dv_))
+    c = np.zeros(T)
+    for t in range(T):  # forward over the prefix
+        s += np.outer(kt[t], v[t])
+        z += kt[t]
+        u = s @ do[t]
+        if simple:
+            dqt[t] = u
+            w[t] = do[t]
+        else:
+            den = qt[t] @ z + eps
+            c[t] = -(qt[t] @ u) / den**2
+            dqt[t] = u / den + c[t] * z
+            w[t] = do[t] / den
+    g = np.zeros((dk, dv_))
+    gz = np.zeros(dk)
+    dkt = np.empty((T, dk))
+    dv = np.empty((T, dv_))
+    for t in range(T - 1, -1, -1):  # backward over the suffix
+        g += np.outer(qt[t], w[t])
+        gz += c[t] * qt[t]
+        dkt[t] = g @ v[t] + gz
+        dv[t] = g.T @ kt[t]
+    return dqt * dphi(q, fm), dkt * dphi(k, fm), dv
+
+
+def causal_bwd(q, k, v, do, dtype: str, eps: float, simple: bool, fm: str = "elu1"):
+    """Causal backward over storage arrays Q, K [B, H, T, Dk] and V, dO
+    [B, H, T, Dv]: (dQ, dK, dV), float64, shaped like Q, K, V."""
+    qh, kh, vh, dh = (_heads(x, dtype) for x in (q, k, v, do))
+    dq, dk, dv = np.empty(qh.shape), np.empty(kh.shape), np.empty(vh.shape)
+    for h in range(qh.shape[0]):
+        dq[h], dk[h], dv[h] = causal_bwd_head(qh[h], kh[h], vh[h], dh[h], eps, simple, fm)
+    return dq.reshape(q.shape), dk.reshape(k.shape), dv.reshape(v.shape)

@@ -571,3 +571,76 @@ def test_causal_pins_catch_planted_mistakes():
             assert err <= 1e-12
         else:
             assert err > 1e-3, kind
+
+
+def causal_loss(q, k, v, do, eps, simple, fm="elu1"):
+    return float(np.sum(oracle.causal_quadratic_head(q, k, v, eps, simple, fm) * do))
+
+
+@pytest.mark.parametrize("simple", [False, True])
+@pytest.mark.parametrize("D,Dv", [(16, 16), (8, 12)])
+def test_causal_bwd_matches_torch_autograd(D, Dv, simple):
+    torch = pytest.importorskip("torch")
+    T = 40
+    q, k = rand((T, D), 110), rand((T, D), 111)
+    v, do = rand((T, Dv), 112), rand((T, Dv), 113)
+    eps = 0.05
+    tq, tk, tv = (torch.tensor(a, dtype=torch.float64, requires_grad=True) for a in (q, k, v))
+    a = torch.tril((torch.nn.functional.elu(tq) + 1) @ (torch.nn.functional.elu(tk) + 1).T)
+    o = a @ tv
+    if not simple:
+        o = o / (a.sum(dim=1, keepdim=True) + eps)
+    (o * torch.tensor(do)).sum().backward()
+    got = oracle.causal_bwd_head(q, k, v, do, eps, simple)
+    for g, t in zip(got, (tq, tk, tv)):
+        ref = t.grad.numpy()
+        assert np.max(np.abs(g - ref)) <= 1e-12 * np.abs(ref).max()
+
+
+@pytest.mark.parametrize("fm", ["elu1", "relu"])
+@pytest.mark.parametrize("simple", [False, True])
+def test_causal_bwd_matches_finite_differences(simple, fm):
+    T, D, Dv = 7, 3, 4
+    q = away_from_zero(rand((T, D), 114), 1e-4)
+    k = away_from_zero(rand((T, D), 115), 1e-4)
+    v, do = rand((T, Dv), 116), rand((T, Dv), 117)
+    eps = 0.5
+    got = oracle.causal_bwd_head(q, k, v, do, eps, simple, fm)
+    arrs = {"q": q, "k": k, "v": v}
+    h = 1e-6
+    for name, g in zip(("q", "k", "v"), got):
+        cols = Dv if name == "v" else D
+        fd = np.empty((T, cols))
+        for t in range(T):
+            for d in range(cols):
+                plus = {n: a.copy() for n, a in arrs.items()}
+                minus = {n: a.copy() for n, a in arrs.items()}
+                plus[name][t, d] += h
+                minus[name][t, d] -= h
+                fd[t, d] = (causal_loss(plus["q"], plus["k"], plus["v"], do, eps, simple, fm)
+                            - causal_loss(minus["q"], minus["k"], minus["v"], do, eps, simple, fm)) / (2 * h)
+        assert np.max(np.abs(g - fd)) <= 1e-6 * max(1.0, np.abs(fd).max()), name
+
+
+@pytest.mark.parametrize("simple", [False, True])
+def test_causal_bwd_last_row_gradient_is_noncausal(simple):
+    """With dO zero except on the last row, only that row (which sees every
+    token) carries a gradient: the causal VJP equals the non-causal one."""
+    T, D = 30, 8
+    q, k, v = rand((T, D), 118), rand((T, D), 119), rand((T, D), 120)
+    do = np.zeros((T, D))
+    do[-1] = rand((1, D), 121)[0]
+    got = oracle.causal_bwd_head(q, k, v, do, 0.1, simple)
+    ref = oracle.bwd_head(q, k, v, do, 0.1, simple)
+    for g, r in zip(got, ref):
+        np.testing.assert_allclose(g, r, rtol=1e-12, atol=1e-12 * np.abs(r).max())
+
+
+def test_causal_bwd_dv_column_sum():
+    """sum_s dV_s = sum_t dO_t a_t / (a_t + eps), a_t = sum_{s <= t} a_ts."""
+    T, D = 25, 6
+    q, k, v, do = (rand((T, D), s_) for s_ in (122, 123, 124, 125))
+    eps = 0.2
+    _, _, dv = oracle.causal_bwd_head(q, k, v, do, eps, False)
+    a = np.tril(oracle.phi(q) @ oracle.phi(k).T).sum(axis=1)
+    np.testing.assert_allclose(dv.sum(axis=0), (do * (a / (a + eps))[:, None]).sum(axis=0), rtol=1e-12)
