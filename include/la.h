@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define LA_VERSION 3
+#define LA_VERSION 4
 
 typedef enum {
     LA_F32 = 0,
@@ -91,10 +91,12 @@ typedef enum {
 /* Causal (autoregressive) attention: token t attends to tokens s <= t,
  *     O_t = phi(q_t) S_t / (phi(q_t) . z_t + eps),  S_t = sum_{s<=t} phi(k_s) v_s^T,
  * z_t = sum_{s<=t} phi(k_s) (flash-linear-attention README, "Different forms
- * of linear attention"). Accepted by la_fwd only, for f16 and bf16 with D and
- * Dv in {64, 128}; `state` receives the full-sequence S, z, bit-identical to
- * the non-causal call. Every other entry point returns LA_ERR_FLAGS with it;
- * other dtypes give LA_ERR_DTYPE and other head sizes LA_ERR_HEAD_DIM. */
+ * of linear attention"). Accepted by la_fwd and la_bwd, for f16 and bf16
+ * with D and Dv in {64, 128}; la_fwd's `state` receives the full-sequence S,
+ * z, bit-identical to the non-causal call; la_bwd does not read `state`. The
+ * step calls return LA_ERR_FLAGS with it; other dtypes give LA_ERR_DTYPE and
+ * other head sizes LA_ERR_HEAD_DIM. la_workspace_bytes counts the causal
+ * backward's scratch when the flag is set. */
 #define LA_CAUSAL 0x10u
 
 /* Problem description shared by every call. B, H, T >= 0 (a zero size is an
@@ -138,7 +140,12 @@ int la_fwd(const la_problem* p, const void* q, const void* k, const void* v,
 
 /* Backward: dQ, dK, dV from Q, K, V, dO and the state la_fwd wrote (the
  * state is required: S and z are not recomputed). Runs la_bwd_dq, then
- * la_bwd_dkv. */
+ * la_bwd_dkv. With LA_CAUSAL: the vector-Jacobian product of sum(O * dO)
+ * through the recurrent form (eps held constant); `state` is not read and may
+ * be NULL. The segment states and their exclusive prefixes are recomputed
+ * from K, V, a forward-order chunked scan per segment writes dQ and keeps
+ * 1/den and c per token in the workspace, exclusive suffixes of its
+ * per-segment sums follow, and a reverse-order scan writes dK and dV. */
 int la_bwd(const la_problem* p, const void* q, const void* k, const void* v,
            const void* dout, const void* state, void* dq, void* dk, void* dv,
            void* ws, size_t ws_bytes, void* stream);

@@ -268,15 +268,19 @@ def bwd_dkv(k, v, *, eps=1e-6, simple=False, layout="bhtd", phi="elu1", dk=None,
     return dk, dv
 
 
-def bwd(q, k, v, do, state, *, eps=1e-6, simple=False, layout="bhtd", phi="elu1", dq=None, dk=None, dv=None, ws=None):
-    """dQ, dK, dV of L = sum(O * dO), from the state fwd returned."""
+def bwd(q, k, v, do, state=None, *, eps=1e-6, simple=False, layout="bhtd", phi="elu1", dq=None, dk=None, dv=None,
+        ws=None, causal=False):
+    """dQ, dK, dV of L = sum(O * dO), from the state fwd returned.
+    causal=True: the backward of the causal form (f16/bf16, D and Dv in
+    {64, 128}); no state is read (pass None)."""
     _tensor(q, None, "q")
     _tensor(k, q, "k")
     hv = v.shape[-1] if isinstance(v, torch.Tensor) else None
     _tensor(v, q, "v", hv)
     _tensor(do, q, "do", hv)
-    prob = make_problem(q.shape, q.dtype, eps, simple, layout, phi, hv)
-    _state(state, prob, q.device)
+    prob = make_problem(q.shape, q.dtype, eps, simple, layout, phi, hv, causal)
+    if not causal or state is not None:
+        _state(state, prob, q.device)
     dq = torch.empty_like(q) if dq is None else _tensor(dq, q, "dq")
     dk = torch.empty_like(q) if dk is None else _tensor(dk, q, "dk")
     dv = _new_like(q, hv) if dv is None else _tensor(dv, q, "dv", hv)

@@ -127,6 +127,14 @@ la::Plan make_plan(const la_problem* p) {
     pl.off_dstate = part;
     pl.off_fstate = pl.off_dstate + st;
     pl.ws_bytes = pl.off_fstate + st;
+    if (p->flags & LA_CAUSAL) {
+        // 64-token chunks per segment, rounded up to even (the scans walk chunk pairs)
+        pl.nche = static_cast<int>(((pl.L + 63) / 64 + 1) / 2 * 2);
+        pl.off_cgpart = pl.ws_bytes;
+        pl.off_cwc = pl.off_cgpart + (pl.P > 1 ? align256(size_t(pl.BH) * pl.P * E * 4) : 0);
+        pl.off_ces = pl.off_cwc + align256(size_t(pl.BH) * pl.T * 8);
+        pl.ws_bytes = pl.off_ces + align256(size_t(pl.BH) * pl.P * pl.nche * 4);
+    }
     return pl;
 }
 
@@ -301,12 +309,13 @@ int la_bwd(const la_problem* p, const void* q, const void* k, const void* v, con
            const void* state, void* dq, void* dk, void* dv, void* ws, size_t ws_bytes, void* stream) {
     la_status st = check_problem(p);
     if (st != LA_OK) return st;
-    if ((st = check_not_causal(p)) != LA_OK) return st;
+    const bool causal = (p->flags & LA_CAUSAL) != 0;
+    if (causal && (st = check_causal(p)) != LA_OK) return st;
     const la::Plan pl = make_plan(p);
     const size_t tk = size_t(pl.BH * pl.T * pl.DK) * elem_bytes(pl.dtype);
     const size_t tv = size_t(pl.BH * pl.T * pl.DV) * elem_bytes(pl.dtype);
-    const size_t sb = la_state_bytes(p);
-    if (pl.BH > 0 && !state) return LA_ERR_NULL;
+    const size_t sb = causal ? 0 : la_state_bytes(p);  // the causal backward does not read the state
+    if (pl.BH > 0 && !state && !causal) return LA_ERR_NULL;
     if (ws_bytes < pl.ws_bytes) return LA_ERR_WORKSPACE;
     st = check_buffers({{q, tk}, {k, tk}, {v, tv}, {dout, tv}, {state, sb}},
                        {{dq, tk}, {dk, tk}, {dv, tv}, {ws, pl.ws_bytes}}, {16, 16, 16, 16, 16},
@@ -314,6 +323,8 @@ int la_bwd(const la_problem* p, const void* q, const void* k, const void* v, con
     if (st != LA_OK) return st;
     if (tk == 0) return LA_OK;
     hipStream_t s = static_cast<hipStream_t>(stream);
+    if (causal)
+        return device_status(kernel_set(pl.dtype, pl.DK)->bwd_causal(pl, q, k, v, dout, dq, dk, dv, ws, s));
     st = device_status(kernel_set(pl.dtype, pl.DK)->bwd_dq(pl, q, dout, static_cast<const float*>(state), dq, ws, s));
     if (st != LA_OK) return st;
     return device_status(kernel_set(pl.dtype, pl.DK)->bwd_dkv(pl, k, v, dk, dv, ws, s));

@@ -42,6 +42,10 @@ struct Plan {
     int64_t LK = 0;
     // workspace carving (byte offsets)
     size_t off_part = 0, off_dstate = 0, off_fstate = 0;
+    // causal backward (LA_CAUSAL): the per-segment (G, g) sums, w and c^ per
+    // token, and one exponent per 64-token chunk (nche chunks per segment)
+    size_t off_cgpart = 0, off_cwc = 0, off_ces = 0;
+    int nche = 0;
     size_t ws_bytes = 0;
 };
 
@@ -69,6 +73,9 @@ struct KernelSet {
     // causal forward (LA_CAUSAL): 16-bit elements, DK and DV in {64, 128}
     hipError_t (*fwd_causal)(const Plan& p, const void* q, const void* k, const void* v, void* o, float* state,
                              void* ws, hipStream_t s);
+    // causal backward (LA_CAUSAL), same element types and sizes
+    hipError_t (*bwd_causal)(const Plan& p, const void* q, const void* k, const void* v, const void* dout,
+                             void* dq, void* dk, void* dv, void* ws, hipStream_t s);
 };
 
 // One unit per (la_dtype, DK): kernel_set_<dtype>_<DK>().

@@ -400,6 +400,11 @@ __device__ __forceinline__ int scale_exp(float maxabs) {
     return min(max(15 - e, -120), 120);
 }
 
+// scale_exp for an exponent that is combined with others by taking the
+// smallest: an all-zero block then gives the largest exponent, which leaves
+// the others' choice alone.
+__device__ __forceinline__ int scale_exp_for_min(float maxabs) { return maxabs == 0.f ? 120 : scale_exp(maxabs); }
+
 // Fixed-order sum of the P partial (S, z) blocks of every head: one thread per
 // 4 consecutive floats of a head's DK*DV + DK block, slices added in ascending
 // order, eight 16-byte loads in flight per batch. A kernel of its own: the
@@ -2579,6 +2584,980 @@ __global__ __launch_bounds__(kThreads) void prefix_kernel(float* __restrict__ pa
 }
 
 // ---------------------------------------------------------------------------
+// Causal backward (LA_CAUSAL): the vector-Jacobian product of sum(O * dO)
+// through the recurrent form, eps held constant.
+// ---------------------------------------------------------------------------
+// With the inclusive prefix states S_t = sum_{s<=t} phi(k_s) v_s^T and
+// z_t = sum_{s<=t} phi(k_s):
+//   den_t = phi(q_t) . z_t + eps,  w_t = 1 / den_t,  u_t = S_t dO_t,
+//   c_t = -(phi(q_t) . u_t) w_t^2,  dphi(q_t) = w_t u_t + c_t z_t,
+// and with the inclusive suffix sums G_s = sum_{t>=s} Qw_t dO_t^T and
+// g_s = sum_{t>=s} c_t phi(q_t), where Qw_t = w_t phi(q_t):
+//   dphi(k_s) = G_s v_s + g_s,  dV_s = G_s^T phi(k_s).
+// simple_la: w = 1, c = 0. Two scans over the segments of the state
+// reduction, in 64-token chunks:
+//  bwd_causal_q_kernel walks its segment forward from the exclusive prefix
+//   (R, z) of the earlier segments, as the causal forward does, and writes
+//   dQ, w_t and c^_t = c_t / w_t per token, the exponent with which the
+//   chunk's Qw was staged, and the segment's own sums of Qw_t dO_t^T and
+//   c_t phi(q_t);
+//  suffix_kernel turns those into exclusive suffixes (the later segments);
+//  bwd_causal_kv_kernel walks its segment backward from that suffix (G, g),
+//   staging Qw at the chunk's exponent, and writes dK and dV.
+// Within a chunk, with a_ts = phi(q_t) . phi(k_s) and b_ts = dO_t . v_s:
+//   dphi(q_t) = w_t (dO_t R^T) + c_t z + sum_{s<=t} (w_t b_ts + c_t) phi(k_s)
+//   dphi(k_s) = G v_s + g + sum_{t>=s} (b_ts + c^_t) Qw_t
+//   dV_s = G^T phi(k_s) + sum_{t>=s} (Qw_t . phi(k_s)) dO_t
+// (R, z: everything before the chunk; G, g: everything after it).
+template <int DK, int DV>
+struct CausalBwdShape {
+    static constexpr int kChunk = 64;
+    static constexpr int kLDK = DK + 16;      // tQ, tK row stride (elements)
+    static constexpr int kLDV = DV + 16;      // tV, tD row stride
+    static constexpr int kLDRT = DK + 8;      // R^T or G^T: rows j, DK entries
+    static constexpr int kLDQT = kChunk + 8;  // Qw^T: rows i, one chunk of tokens
+    static constexpr int kLDW = 24;           // per-wave transposed tiles: rows of 16 tokens
+    static constexpr int kMax = DK > DV ? DK : DV;
+    static constexpr int kWRows = kMax > kChunk ? kMax : kChunk;
+    static constexpr int kMinBlocks = (DK == 64 && DV == 64) ? 2 : 1;
+};
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xf, 0xf, false));
+}
+// Sum over each row of 16 lanes (a lane group); every lane of the row gets
+// the same total.
+__device__ __forceinline__ float row16_sum(float x) {
+    x += dpp_f<0xb1>(x);   // quad_perm [1, 0, 3, 2]
+    x += dpp_f<0x4e>(x);   // quad_perm [2, 3, 0, 1]
+    x += dpp_f<0x141>(x);  // row_half_mirror
+    x += dpp_f<0x140>(x);  // row_mirror
+    return x;
+}
+
+// A 16-bit fragment times a power of two, through fp32.
+template <typename T>
+__device__ __forceinline__ Frag<T> scale_frag(Frag<T> x, float f) {
+    Frag<T> y;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) y[e] = static_cast<T>(static_cast<float>(x[e]) * f);
+    return y;
+}
+
+// Four consecutive 16-bit values as one 8-byte LDS store.
+template <typename T>
+__device__ __forceinline__ void put4t(T* dst, f32x4 x, float f) {
+    typedef T t4 __attribute__((ext_vector_type(4)));
+    t4 y;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) y[r] = static_cast<T>(x[r] * f);
+    *reinterpret_cast<t4*>(dst) = y;
+}
+
+// Forward-order scan of one segment: dQ, w and c^ per token, the chunk's Qw
+// exponent, and (P > 1) the segment's sums of Qw dO^T and c phi(q). The four
+// waves each own 16 query rows of the chunk and a quarter of the rows of R
+// and of the G sum. Per chunk:
+//   (a) a and b on the wave's rows (blocks above the diagonal skipped);
+//   (b) Y = dO R^T (R^T as 16-bit in LDS, one power of two per owner wave);
+//   (c) den and phi(q) . u per row from a, b, Y and phi(q) read at the
+//       result positions, reduced over the 16 lanes of a row;
+//   (d) P = mask(w b + c), staged transposed, times phi(K);
+//   (e) dQ = (w Y + c z + P phi(K)) phi'(q), staged transposed and stored
+//       as rows;
+//   (f) R += phi(K)^T V, z += sum phi(k) on the wave's rows of R;
+//   (g) Qw of the wave's rows into the shared Qw^T tile at the wave's own
+//       power of two; after a barrier every wave takes the smallest of the
+//       four exponents and rescales the other waves' columns to it as it
+//       reads them for G += Qw^T dO.
+// R^T and z are published at the top of the next chunk, after the barrier
+// that ends this one. Three barriers per chunk; two chunks of loads in flight.
+template <typename T, int DK, int DV, bool SIMPLE, int FM>
+__global__ __launch_bounds__(kThreads, (CausalBwdShape<DK, DV>::kMinBlocks)) void bwd_causal_q_kernel(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const T* __restrict__ dout,
+    const float* __restrict__ pre, T* __restrict__ dq, float* __restrict__ wc, int* __restrict__ es,
+    float* __restrict__ gpart, int64_t T_, const Layout lay, int P, int64_t L, int nche, float eps) {
+    using Sh = CausalBwdShape<DK, DV>;
+    constexpr int C = Sh::kChunk, LDK = Sh::kLDK, LDV = Sh::kLDV, LDRT = Sh::kLDRT, LDQT = Sh::kLDQT;
+    constexpr int LDW = Sh::kLDW;
+    constexpr int NBI = DK / 16, NBV = DV / 16, NBC = C / 16;
+    constexpr int RIW = DK / 64;  // 16-row blocks of R and of the G sum per wave
+    constexpr int KSK = DK / 32, KSV = DV / 32, KSC = C / 32;
+    constexpr int CK = DK / 8, CV = DV / 8;
+    constexpr int NCK = C * CK / kThreads, NCV = C * CV / kThreads;
+    static_assert(sizeof(T) == 2, "transposed LDS reads take 16-bit elements");
+    static_assert(NCK * kThreads == C * CK && NCV * kThreads == C * CV, "tiles must split evenly");
+    static_assert(RIW >= 1 && RIW * 64 == DK, "each wave owns whole 16-row blocks");
+    __shared__ __attribute__((aligned(16))) T tQ[C * LDK];
+    __shared__ __attribute__((aligned(16))) T tK[C * LDK];
+    __shared__ __attribute__((aligned(16))) T tV[C * LDV];
+    __shared__ __attribute__((aligned(16))) T tD[C * LDV];
+    __shared__ __attribute__((aligned(16))) T tRT[DV * LDRT];
+    __shared__ __attribute__((aligned(16))) T tQT[DK * LDQT];
+    __shared__ __attribute__((aligned(16))) T tW[kWaves][Sh::kWRows * LDW];
+    __shared__ float sZ[DK];
+    __shared__ int sExpR[kWaves], sExpQ[kWaves];
+
+    const int wid = xcd_remap(blockIdx.x, gridDim.x);
+    const int64_t bh = wid / P;
+    const int p = wid % P;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int m = lane & 15, grp = lane >> 4;
+    const int64_t t0 = (int64_t)p * L;
+    const int64_t t1 = min(t0 + L, T_);
+    const int64_t len = t1 - t0;
+    // rounded up to even: the loop body comes in pairs (see below)
+    const int nchunks = (int)(len > 0 ? (((len + C - 1) / C) + 1) / 2 * 2 : 0);
+    const Layout lk = lay, lv = v_layout<DK, DV>(lay);
+
+    // R[16 (wave RIW + iR) + 4 grp + r][16 jb + m] in accR[iR][jb][r], z of
+    // the same rows in accZ[iR][r], likewise the G sum in accG.
+    f32x4 accR[RIW][NBV], accZ[RIW], accG[RIW][NBV];
+    float gzp[NBI];  // sum of c_t phi(q_t)[16 ib + m] over this lane's rows
+    {
+        const float* pS = (pre != nullptr && p > 0) ? pre + (bh * P + p) * (int64_t)(DK * DV + DK) : nullptr;
+#pragma unroll
+        for (int iR = 0; iR < RIW; ++iR) {
+            const int i0 = 16 * (wave * RIW + iR) + 4 * grp;
+#pragma unroll
+            for (int jb = 0; jb < NBV; ++jb) {
+                accG[iR][jb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int r = 0; r < 4; ++r) accR[iR][jb][r] = pS ? pS[(i0 + r) * DV + 16 * jb + m] : 0.f;
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) accZ[iR][r] = pS ? pS[DK * DV + i0 + r] : 0.f;
+        }
+#pragma unroll
+        for (int ib = 0; ib < NBI; ++ib) gzp[ib] = 0.f;
+    }
+    Frag<T> ones;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ones[e] = static_cast<T>(1.f);
+
+    auto publish = [&]() {
+        int sR = 0;
+        if constexpr (Elt<T>::kScaled) {
+            float mx = 0.f;
+#pragma unroll
+            for (int iR = 0; iR < RIW; ++iR)
+#pragma unroll
+                for (int jb = 0; jb < NBV; ++jb)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) mx = fmaxf(mx, fabsf(accR[iR][jb][r]));
+            sR = scale_exp(wave_max_nonneg(mx));
+        }
+        const float fR = ldexpf(1.f, sR);
+#pragma unroll
+        for (int iR = 0; iR < RIW; ++iR)
+#pragma unroll
+            for (int jb = 0; jb < NBV; ++jb)
+                put4t(&tRT[(16 * jb + m) * LDRT + 16 * (wave * RIW + iR) + 4 * grp], accR[iR][jb], fR);
+        if (lane == 0) sExpR[wave] = sR;
+        if constexpr (!SIMPLE) {
+            if (m == 0)
+#pragma unroll
+                for (int iR = 0; iR < RIW; ++iR)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) sZ[16 * (wave * RIW + iR) + 4 * grp + r] = accZ[iR][r];
+        }
+    };
+
+    struct Stage {
+        u32x4 q[NCK], k[NCK], v[NCV], d[NCV];
+    };
+    const HeadBuf bq = slice_buf(q, lk, bh, DK, t0, t1), bk = slice_buf(k, lk, bh, DK, t0, t1);
+    const HeadBuf bv = slice_buf(v, lv, bh, DV, t0, t1), bd = slice_buf(dout, lv, bh, DV, t0, t1);
+    const HeadBuf bdq = slice_buf(dq, lk, bh, DK, t0, t1);
+    auto issue = [&](Stage& st, int c) {
+        const int64_t row0 = (int64_t)c * C;
+#pragma unroll
+        for (int i = 0; i < NCK; ++i) {
+            const int n = tid + kThreads * i, r = n / CK, cc = n % CK;
+            const int off = buf_off<T>(row0 + r, lk.rs, 8 * cc);
+            st.q[i] = __builtin_amdgcn_raw_buffer_load_b128(bq.rsrc, off, 0, 0);
+            st.k[i] = __builtin_amdgcn_raw_buffer_load_b128(bk.rsrc, off, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < NCV; ++i) {
+            const int n = tid + kThreads * i, r = n / CV, cc = n % CV;
+            const int off = buf_off<T>(row0 + r, lv.rs, 8 * cc);
+            st.v[i] = __builtin_amdgcn_raw_buffer_load_b128(bv.rsrc, off, 0, 0);
+            st.d[i] = __builtin_amdgcn_raw_buffer_load_b128(bd.rsrc, off, 0, 0);
+        }
+    };
+    auto consume = [&](const Stage& st, int c) {
+        const int64_t row0 = (int64_t)c * C;
+#pragma unroll
+        for (int i = 0; i < NCK; ++i) {
+            const int n = tid + kThreads * i, r = n / CK, cc = n % CK;
+            const bool ok = row0 + r < len;
+            Row<T, 8> qin, kin, qt, kt;
+            __builtin_memcpy(qin.e, &st.q[i], sizeof(qin));
+            __builtin_memcpy(kin.e, &st.k[i], sizeof(kin));
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                qt.e[e] = static_cast<T>(phi<FM, T>(to_f32(qin.e[e])));
+                kt.e[e] = ok ? static_cast<T>(phi<FM, T>(to_f32(kin.e[e]))) : static_cast<T>(0.f);
+            }
+            *reinterpret_cast<Row<T, 8>*>(&tQ[r * LDK + 8 * cc]) = qt;
+            *reinterpret_cast<Row<T, 8>*>(&tK[r * LDK + 8 * cc]) = kt;
+        }
+#pragma unroll
+        for (int i = 0; i < NCV; ++i) {
+            const int n = tid + kThreads * i, r = n / CV, cc = n % CV;
+            *reinterpret_cast<u32x4*>(&tV[r * LDV + 8 * cc]) = st.v[i];
+            *reinterpret_cast<u32x4*>(&tD[r * LDV + 8 * cc]) = st.d[i];
+        }
+    };
+
+    const int rA = 8 * grp + (m >> 2), cA = 4 * (m & 3);
+    T* myW = tW[wave];
+    const int tq = 16 * wave + 4 * grp;  // this lane's first result row in the chunk
+    float* wcb = wc + 2 * (bh * T_ + t0);
+    int* esb = es + (bh * P + p) * (int64_t)nche;
+    auto body = [&](Stage& st, int c) {
+        const int64_t row0 = (int64_t)c * C;
+        publish();
+        consume(st, c);
+        __syncthreads();  // tiles of chunk c, R^T and z are visible
+        sched_fence();
+        issue(st, c + 2);  // two chunks ahead; past the segment end these read zeros
+        sched_fence();
+
+        // (a) a[t][s] and b[t][s], t = tq + r, s = 16 jb + m, s <= t
+        f32x4 aa[NBC], bb[NBC];
+#pragma unroll
+        for (int jb = 0; jb < NBC; ++jb) {
+            aa[jb] = f32x4{0.f, 0.f, 0.f, 0.f};
+            bb[jb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+        Frag<T> fd[KSV];
+#pragma unroll
+        for (int ks = 0; ks < KSV; ++ks)
+            fd[ks] = *reinterpret_cast<const Frag<T>*>(&tD[(16 * wave + m) * LDV + 32 * ks + 8 * grp]);
+#pragma unroll
+        for (int ks = 0; ks < KSK; ++ks) {
+            const Frag<T> a = *reinterpret_cast<const Frag<T>*>(&tQ[(16 * wave + m) * LDK + 32 * ks + 8 * grp]);
+#pragma unroll
+            for (int jb = 0; jb < NBC; ++jb)
+                if (jb <= wave)
+                    aa[jb] = mma(a, *reinterpret_cast<const Frag<T>*>(&tK[(16 * jb + m) * LDK + 32 * ks + 8 * grp]),
+                                 aa[jb]);
+        }
+#pragma unroll
+        for (int ks = 0; ks < KSV; ++ks)
+#pragma unroll
+            for (int jb = 0; jb < NBC; ++jb)
+                if (jb <= wave)
+                    bb[jb] = mma(fd[ks], *reinterpret_cast<const Frag<T>*>(&tV[(16 * jb + m) * LDV + 32 * ks + 8 * grp]),
+                                 bb[jb]);
+#pragma unroll
+        for (int jb = 0; jb < NBC; ++jb)
+            if (jb == wave)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    aa[jb][r] = m > 4 * grp + r ? 0.f : aa[jb][r];
+                    bb[jb][r] = m > 4 * grp + r ? 0.f : bb[jb][r];
+                }
+
+        // (b) Y = dO R^T, unscaled per column block
+        f32x4 Y[NBI];
+#pragma unroll
+        for (int ib = 0; ib < NBI; ++ib) Y[ib] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KSV; ++ks) {
+            const int rb = 32 * ks + rA;
+#pragma unroll
+            for (int ib = 0; ib < NBI; ++ib) {
+                const Frag<T> b = join_frag<T>(lds_read_tr(&tRT[rb * LDRT + 16 * ib + cA]),
+                                               lds_read_tr(&tRT[(rb + 4) * LDRT + 16 * ib + cA]));
+                Y[ib] = mma(fd[ks], b, Y[ib]);
+            }
+        }
+#pragma unroll
+        for (int ib = 0; ib < NBI; ++ib) {
+            const float uR = ldexpf(1.f, -sExpR[ib / RIW]);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) Y[ib][r] *= uR;
+        }
+
+        // (c) phi(q) at the result positions; den, w and c per row
+        float ph[NBI][4];
+#pragma unroll
+        for (int ib = 0; ib < NBI; ++ib)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) ph[ib][r] = to_f32(tQ[(tq + r) * LDK + 16 * ib + m]);
+        float wr[4], cr[4];
+        if constexpr (SIMPLE) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                wr[r] = row0 + tq + r < len ? 1.f : 0.f;
+                cr[r] = 0.f;
+            }
+        } else {
+            float sa[4], sb[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                sa[r] = 0.f;
+                sb[r] = 0.f;
+#pragma unroll
+                for (int jb = 0; jb < NBC; ++jb)
+                    if (jb <= wave) {
+                        sa[r] += aa[jb][r];
+                        sb[r] += aa[jb][r] * bb[jb][r];
+                    }
+            }
+#pragma unroll
+            for (int ib = 0; ib < NBI; ++ib) {
+                const float zi = sZ[16 * ib + m];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    sa[r] += ph[ib][r] * zi;
+                    sb[r] += ph[ib][r] * Y[ib][r];
+                }
+            }
+            float wst = 0.f, cst = 0.f;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float den = row16_sum(sa[r]) + eps;
+                const float ru = row16_sum(sb[r]);
+                const bool ok = row0 + tq + r < len;
+                const float inv = 1.f / den;
+                wr[r] = ok ? inv : 0.f;
+                cr[r] = ok ? -ru * inv * inv : 0.f;
+                if (m == r) {
+                    wst = inv;
+                    cst = -ru * inv;
+                }
+            }
+            // w and c^ of row tq + m, by lanes m < 4
+            if (m < 4 && row0 + tq + m < len)
+                *reinterpret_cast<float2*>(&wcb[2 * (row0 + tq + m)]) = make_float2(wst, cst);
+        }
+
+        // (d) P = mask(w b + c), staged transposed: rows s, columns t of this wave
+        f32x4 pp[NBC];
+        float pmx = 0.f;
+#pragma unroll
+        for (int jb = 0; jb < NBC; ++jb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const bool keep = jb < wave || (jb == wave && m <= 4 * grp + r);
+                const float x = SIMPLE ? bb[jb][r] : wr[r] * bb[jb][r] + cr[r];
+                pp[jb][r] = keep ? x : 0.f;
+                pmx = fmaxf(pmx, fabsf(pp[jb][r]));
+            }
+        int sP = 0;
+        if constexpr (Elt<T>::kScaled) sP = scale_exp(wave_max_nonneg(pmx));
+        {
+            const float fP = ldexpf(1.f, sP);
+#pragma unroll
+            for (int jb = 0; jb < NBC; ++jb) put4t(&myW[(16 * jb + m) * LDW + 4 * grp], pp[jb], fP);
+        }
+        wave_lds_sync();
+        f32x4 pk[NBI];
+#pragma unroll
+        for (int ib = 0; ib < NBI; ++ib) pk[ib] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KSC; ++ks) {
+            if (ks <= wave / 2) {  // rows s >= 32 (ks + 1) of P are zero
+                const int rb = 32 * ks + rA;
+                const Frag<T> a = join_frag<T>(lds_read_tr(&myW[rb * LDW + cA]), lds_read_tr(&myW[(rb + 4) * LDW + cA]));
+#pragma unroll
+                for (int ib = 0; ib < NBI; ++ib) {
+                    const Frag<T> b = join_frag<T>(lds_read_tr(&tK[rb * LDK + 16 * ib + cA]),
+                                                   lds_read_tr(&tK[(rb + 4) * LDK + 16 * ib + cA]));
+                    pk[ib] = mma(a, b, pk[ib]);
+                }
+            }
+        }
+
+        // (e) dQ = (w Y + c z + P phi(K)) phi'(q), staged transposed, stored as rows
+        {
+            const float uP = ldexpf(1.f, -sP);
+            f32x4 g[NBI];
+#pragma unroll
+            for (int ib = 0; ib < NBI; ++ib) {
+                const float zi = SIMPLE ? 0.f : sZ[16 * ib + m];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float d = SIMPLE ? Y[ib][r] + pk[ib][r] * uP : wr[r] * Y[ib][r] + cr[r] * zi + pk[ib][r] * uP;
+                    g[ib][r] = d * dphi_of<FM>(ph[ib][r]);
+                }
+            }
+            wave_lds_sync();
+#pragma unroll
+            for (int ib = 0; ib < NBI; ++ib) put4t(&myW[(16 * ib + m) * LDW + 4 * grp], g[ib], 1.f);
+            wave_lds_sync();
+            // row 16 wave + m, columns 32 kk + 8 grp .. + 7
+#pragma unroll
+            for (int kk = 0; kk < DK / 32; ++kk) {
+                const int rb = 32 * kk + rA;
+                const Frag<T> x = join_frag<T>(lds_read_tr(&myW[rb * LDW + cA]), lds_read_tr(&myW[(rb + 4) * LDW + cA]));
+                buf_store16(bdq, buf_off<T>(row0 + 16 * wave + m, lk.rs, 32 * kk + 8 * grp), __builtin_bit_cast(uint4, x));
+            }
+            wave_lds_sync();
+        }
+
+        // (f) R += phi(K)^T V and z += sum phi(k) on this wave's rows of R
+#pragma unroll
+        for (int ks = 0; ks < KSC; ++ks) {
+            const int rb = 32 * ks + rA;
+            Frag<T> bvf[NBV];
+#pragma unroll
+            for (int jb = 0; jb < NBV; ++jb)
+                bvf[jb] = join_frag<T>(lds_read_tr(&tV[rb * LDV + 16 * jb + cA]),
+                                       lds_read_tr(&tV[(rb + 4) * LDV + 16 * jb + cA]));
+#pragma unroll
+            for (int iR = 0; iR < RIW; ++iR) {
+                const int i0 = 16 * (wave * RIW + iR);
+                const Frag<T> a = join_frag<T>(lds_read_tr(&tK[rb * LDK + i0 + cA]),
+                                               lds_read_tr(&tK[(rb + 4) * LDK + i0 + cA]));
+#pragma unroll
+                for (int jb = 0; jb < NBV; ++jb) accR[iR][jb] = mma(a, bvf[jb], accR[iR][jb]);
+                if constexpr (!SIMPLE) accZ[iR] = mma(a, ones, accZ[iR]);
+            }
+        }
+
+        // (g) Qw of this wave's rows into Qw^T (rows i, columns t); c phi(q) into gzp
+        {
+            f32x4 qw[NBI];
+            float qmx = 0.f;
+#pragma unroll
+            for (int ib = 0; ib < NBI; ++ib)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    qw[ib][r] = ph[ib][r] * wr[r];
+                    qmx = fmaxf(qmx, fabsf(qw[ib][r]));
+                }
+            int sQ = 0;
+            if constexpr (Elt<T>::kScaled) sQ = scale_exp_for_min(wave_max_nonneg(qmx));
+            const float fQ = ldexpf(1.f, sQ);
+#pragma unroll
+            for (int ib = 0; ib < NBI; ++ib) put4t(&tQT[(16 * ib + m) * LDQT + tq], qw[ib], fQ);
+            if (lane == 0) sExpQ[wave] = sQ;
+            if constexpr (!SIMPLE) {
+#pragma unroll
+                for (int ib = 0; ib < NBI; ++ib)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) gzp[ib] += cr[r] * ph[ib][r];
+            }
+        }
+        __syncthreads();  // Qw^T and its four exponents are visible
+
+        // G += Qw^T dO on this wave's rows of the G sum, at the common exponent
+        {
+            int sM = 0;
+            if constexpr (Elt<T>::kScaled) sM = min(min(sExpQ[0], sExpQ[1]), min(sExpQ[2], sExpQ[3]));
+            if (tid == 0) esb[c] = sM;
+            const float uM = ldexpf(1.f, -sM);
+#pragma unroll
+            for (int iR = 0; iR < RIW; ++iR) {
+                const int i0 = 16 * (wave * RIW + iR);
+                Frag<T> qa[KSC];
+#pragma unroll
+                for (int ks = 0; ks < KSC; ++ks) {
+                    qa[ks] = *reinterpret_cast<const Frag<T>*>(&tQT[(i0 + m) * LDQT + 32 * ks + 8 * grp]);
+                    // columns 32 ks + 8 grp .. + 7 were staged by wave 2 ks + grp / 2
+                    if constexpr (Elt<T>::kScaled) qa[ks] = scale_frag<T>(qa[ks], ldexpf(1.f, sM - sExpQ[2 * ks + (grp >> 1)]));
+                }
+#pragma unroll
+                for (int jb = 0; jb < NBV; ++jb) {
+                    f32x4 t = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int ks = 0; ks < KSC; ++ks) {
+                        const int rb = 32 * ks + rA;
+                        const Frag<T> b = join_frag<T>(lds_read_tr(&tD[rb * LDV + 16 * jb + cA]),
+                                                       lds_read_tr(&tD[(rb + 4) * LDV + 16 * jb + cA]));
+                        t = mma(qa[ks], b, t);
+                    }
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) accG[iR][jb][r] += t[r] * uM;
+                }
+            }
+        }
+        __syncthreads();  // every wave is done with the tiles, R^T, z and Qw^T
+    };
+    // Two chunks of loads in flight; the chunk count is even so that the loop
+    // has no branch around loads. A chunk past the segment end reads zeros,
+    // adds nothing and stores nothing.
+    if (nchunks > 0) {
+        Stage s0, s1;
+        issue(s0, 0);
+        sched_fence();
+        issue(s1, 1);
+        sched_fence();
+        for (int c = 0; c < nchunks; c += 2) {
+            body(s0, c);
+            body(s1, c + 1);
+        }
+    }
+    if (gpart != nullptr) {
+        float* gp = gpart + (bh * P + p) * (int64_t)(DK * DV + DK);
+#pragma unroll
+        for (int iR = 0; iR < RIW; ++iR) {
+            const int i0 = 16 * (wave * RIW + iR) + 4 * grp;
+#pragma unroll
+            for (int jb = 0; jb < NBV; ++jb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) gp[(i0 + r) * DV + 16 * jb + m] = accG[iR][jb][r];
+        }
+        // g: the lanes' sums over their rows, then over the four waves in order
+        float* red = reinterpret_cast<float*>(&tW[0][0]);  // free after the last barrier
+#pragma unroll
+        for (int ib = 0; ib < NBI; ++ib) {
+            float x = gzp[ib];
+            x += __shfl_xor(x, 16);
+            x += __shfl_xor(x, 32);
+            if (grp == 0) red[wave * DK + 16 * ib + m] = x;
+        }
+        __syncthreads();
+        if (tid < DK) gp[DK * DV + tid] = ((red[tid] + red[DK + tid]) + red[2 * DK + tid]) + red[3 * DK + tid];
+    }
+}
+
+// Exclusive suffix of the P partial (G, g) blocks of every head, in place:
+// block p becomes the sum of blocks p + 1 .. P - 1, added from the last down.
+template <int DK, int DV>
+__global__ __launch_bounds__(kThreads) void suffix_kernel(float* __restrict__ part, int P, int64_t BH) {
+    constexpr int E4 = (DK * DV + DK) / 4;
+    constexpr int BPH = (E4 + kThreads - 1) / kThreads;
+    const int64_t bh = blockIdx.x / BPH;
+    const int i = (blockIdx.x % BPH) * kThreads + threadIdx.x;
+    if (bh >= BH || i >= E4) return;
+    float4* pb = reinterpret_cast<float4*>(part) + bh * (int64_t)P * E4 + i;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int p1 = P; p1 > 0; p1 -= 8) {
+        float4 x[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) x[j] = pb[(int64_t)max(p1 - 1 - j, 0) * E4];
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            if (p1 - 1 - j >= 0) {
+                pb[(int64_t)(p1 - 1 - j) * E4] = acc;
+                acc.x += x[j].x;
+                acc.y += x[j].y;
+                acc.z += x[j].z;
+                acc.w += x[j].w;
+            }
+    }
+}
+
+// Reverse-order scan of one segment: dK and dV. The four waves each own 16
+// key rows of the chunk and a quarter of the rows of G. Qw = w phi(q) is
+// staged at the exponent bwd_causal_q_kernel chose for the chunk. Per chunk:
+//   (a) a~[s][t] = phi(k_s) . Qw_t and b[s][t] = v_s . dO_t for t >= s;
+//   (b) dK = ((mask(b + c^) Qw) + V G^T + g) phi'(k): the first product
+//       from the transposed staging of mask(b + c^), V G^T from G^T in LDS
+//       (one power of two per owner wave, constant along each result column);
+//   (c) dV = a~ dO + phi(K) G: phi(K) G sums over the owners' quarters, so
+//       the A operand is rescaled per quarter to the smallest exponent;
+//   (d) G += Qw^T dO, g += Qw^T c^ on the wave's rows of G.
+// G^T and g are published at the top of the next chunk. Two barriers per chunk.
+template <typename T, int DK, int DV, bool SIMPLE, int FM>
+__global__ __launch_bounds__(kThreads, (CausalBwdShape<DK, DV>::kMinBlocks)) void bwd_causal_kv_kernel(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const T* __restrict__ dout,
+    const float* __restrict__ wc, const int* __restrict__ es, const float* __restrict__ suf, T* __restrict__ dk,
+    T* __restrict__ dv, int64_t T_, const Layout lay, int P, int64_t L, int nche) {
+    using Sh = CausalBwdShape<DK, DV>;
+    constexpr int C = Sh::kChunk, LDK = Sh::kLDK, LDV = Sh::kLDV, LDRT = Sh::kLDRT, LDW = Sh::kLDW;
+    constexpr int NBI = DK / 16, NBV = DV / 16, NBC = C / 16;
+    constexpr int RIW = DK / 64;
+    constexpr int KSK = DK / 32, KSV = DV / 32, KSC = C / 32;
+    constexpr int CK = DK / 8, CV = DV / 8;
+    constexpr int NCK = C * CK / kThreads, NCV = C * CV / kThreads;
+    constexpr int QW = DK / 4;  // columns of G^T per owner wave
+    static_assert(sizeof(T) == 2, "transposed LDS reads take 16-bit elements");
+    static_assert(NCK * kThreads == C * CK && NCV * kThreads == C * CV, "tiles must split evenly");
+    static_assert(RIW >= 1 && RIW * 64 == DK, "each wave owns whole 16-row blocks");
+    __shared__ __attribute__((aligned(16))) T tQ[C * LDK];  // Qw, scaled
+    __shared__ __attribute__((aligned(16))) T tK[C * LDK];
+    __shared__ __attribute__((aligned(16))) T tV[C * LDV];
+    __shared__ __attribute__((aligned(16))) T tD[C * LDV];
+    __shared__ __attribute__((aligned(16))) T tGT[DV * LDRT];
+    __shared__ __attribute__((aligned(16))) T tW[kWaves][Sh::kWRows * LDW];
+    __shared__ __attribute__((aligned(16))) float sGz[DK];
+    __shared__ __attribute__((aligned(16))) float sC[C];
+    __shared__ int sExpG[kWaves];
+
+    const int wid = xcd_remap(blockIdx.x, gridDim.x);
+    const int64_t bh = wid / P;
+    const int p = wid % P;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int m = lane & 15, grp = lane >> 4;
+    const int64_t t0 = (int64_t)p * L;
+    const int64_t t1 = min(t0 + L, T_);
+    const int64_t len = t1 - t0;
+    const int nreal = (int)(len > 0 ? (len + C - 1) / C : 0);
+    const int nchunks = (nreal + 1) / 2 * 2;
+    const Layout lk = lay, lv = v_layout<DK, DV>(lay);
+
+    f32x4 accG[RIW][NBV], accGz[RIW];
+    {
+        const float* pG = suf != nullptr ? suf + (bh * P + p) * (int64_t)(DK * DV + DK) : nullptr;
+#pragma unroll
+        for (int iR = 0; iR < RIW; ++iR) {
+            const int i0 = 16 * (wave * RIW + iR) + 4 * grp;
+#pragma unroll
+            for (int jb = 0; jb < NBV; ++jb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) accG[iR][jb][r] = pG ? pG[(i0 + r) * DV + 16 * jb + m] : 0.f;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) accGz[iR][r] = pG ? pG[DK * DV + i0 + r] : 0.f;
+        }
+    }
+
+    auto publish = [&]() {
+        int sG = 0;
+        if constexpr (Elt<T>::kScaled) {
+            float mx = 0.f;
+#pragma unroll
+            for (int iR = 0; iR < RIW; ++iR)
+#pragma unroll
+                for (int jb = 0; jb < NBV; ++jb)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) mx = fmaxf(mx, fabsf(accG[iR][jb][r]));
+            sG = scale_exp_for_min(wave_max_nonneg(mx));
+        }
+        const float fG = ldexpf(1.f, sG);
+#pragma unroll
+        for (int iR = 0; iR < RIW; ++iR)
+#pragma unroll
+            for (int jb = 0; jb < NBV; ++jb)
+                put4t(&tGT[(16 * jb + m) * LDRT + 16 * (wave * RIW + iR) + 4 * grp], accG[iR][jb], fG);
+        if (lane == 0) sExpG[wave] = sG;
+        if constexpr (!SIMPLE) {
+            if (m == 0)
+#pragma unroll
+                for (int iR = 0; iR < RIW; ++iR)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) sGz[16 * (wave * RIW + iR) + 4 * grp + r] = accGz[iR][r];
+        }
+    };
+
+    struct Stage {
+        u32x4 q[NCK], k[NCK], v[NCV], d[NCV];
+        unsigned w, ch;  // w and c^ of token `lane` of the chunk
+        int es;
+    };
+    const HeadBuf bq = slice_buf(q, lk, bh, DK, t0, t1), bk = slice_buf(k, lk, bh, DK, t0, t1);
+    const HeadBuf bv = slice_buf(v, lv, bh, DV, t0, t1), bd = slice_buf(dout, lv, bh, DV, t0, t1);
+    const HeadBuf bdk = slice_buf(dk, lk, bh, DK, t0, t1), bdv = slice_buf(dv, lv, bh, DV, t0, t1);
+    // w and c^ of the segment's tokens (8 bytes each); zeros past the end
+    const HeadBuf bwc{__builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(wc + 2 * (bh * T_ + t0)), 0,
+                                                        (int)(len > 0 ? 8 * len : 0), 0x00020000)};
+    const int* esb = es + (bh * P + p) * (int64_t)nche;
+    // step n of the walk visits chunk nchunks - 1 - n; the prefetches past the
+    // first chunk go to chunks past the segment end, which read zeros
+    auto chunk_of = [&](int n) { return n < nchunks ? nchunks - 1 - n : n; };
+    auto issue = [&](Stage& st, int n) {
+        const int c = chunk_of(n);
+        const int64_t row0 = (int64_t)c * C;
+#pragma unroll
+        for (int i = 0; i < NCK; ++i) {
+            const int nn = tid + kThreads * i, r = nn / CK, cc = nn % CK;
+            const int off = buf_off<T>(row0 + r, lk.rs, 8 * cc);
+            st.q[i] = __builtin_amdgcn_raw_buffer_load_b128(bq.rsrc, off, 0, 0);
+            st.k[i] = __builtin_amdgcn_raw_buffer_load_b128(bk.rsrc, off, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < NCV; ++i) {
+            const int nn = tid + kThreads * i, r = nn / CV, cc = nn % CV;
+            const int off = buf_off<T>(row0 + r, lv.rs, 8 * cc);
+            st.v[i] = __builtin_amdgcn_raw_buffer_load_b128(bv.rsrc, off, 0, 0);
+            st.d[i] = __builtin_amdgcn_raw_buffer_load_b128(bd.rsrc, off, 0, 0);
+        }
+        if constexpr (!SIMPLE) {
+            // two dword loads: the 8-byte buffer-load builtin drops the upper dword with this compiler
+            const int off = (int)((uint32_t)(row0 + lane) * 8u);
+            st.w = __builtin_amdgcn_raw_buffer_load_b32(bwc.rsrc, off, 0, 0);
+            st.ch = __builtin_amdgcn_raw_buffer_load_b32(bwc.rsrc, off + 4, 0, 0);
+        }
+        // the exponent of a written chunk (chunks past the end hold zeros, any finite scale will do)
+        st.es = nreal > 0 ? esb[min(c, nreal - 1)] : 0;
+    };
+    // returns the chunk's Qw exponent
+    auto consume = [&](const Stage& st, int n, float& cmx) -> int {
+        const int c = chunk_of(n);
+        const int64_t row0 = (int64_t)c * C;
+        const int sQ = st.es;
+        const float fQ = ldexpf(1.f, sQ);
+        float wl = 1.f, cl = 0.f;
+        if constexpr (!SIMPLE) {
+            wl = __builtin_bit_cast(float, st.w);
+            cl = __builtin_bit_cast(float, st.ch);
+        }
+#pragma unroll
+        for (int i = 0; i < NCK; ++i) {
+            const int nn = tid + kThreads * i, r = nn / CK, cc = nn % CK;
+            const bool ok = row0 + r < len;
+            float wt = 1.f;
+            if constexpr (!SIMPLE) wt = __shfl(wl, r);
+            const float f = ok ? wt * fQ : 0.f;
+            Row<T, 8> qin, kin, qt, kt;
+            __builtin_memcpy(qin.e, &st.q[i], sizeof(qin));
+            __builtin_memcpy(kin.e, &st.k[i], sizeof(kin));
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                qt.e[e] = static_cast<T>(phi<FM, T>(to_f32(qin.e[e])) * f);
+                kt.e[e] = ok ? static_cast<T>(phi<FM, T>(to_f32(kin.e[e]))) : static_cast<T>(0.f);
+            }
+            *reinterpret_cast<Row<T, 8>*>(&tQ[r * LDK + 8 * cc]) = qt;
+            *reinterpret_cast<Row<T, 8>*>(&tK[r * LDK + 8 * cc]) = kt;
+        }
+#pragma unroll
+        for (int i = 0; i < NCV; ++i) {
+            const int nn = tid + kThreads * i, r = nn / CV, cc = nn % CV;
+            *reinterpret_cast<u32x4*>(&tV[r * LDV + 8 * cc]) = st.v[i];
+            *reinterpret_cast<u32x4*>(&tD[r * LDV + 8 * cc]) = st.d[i];
+        }
+        if constexpr (!SIMPLE) {
+            if (wave == 0) sC[lane] = cl;
+            cmx = wave_max_nonneg(fabsf(cl));  // the same in every wave
+        }
+        return sQ;
+    };
+
+    const int rA = 8 * grp + (m >> 2), cA = 4 * (m & 3);
+    T* myW = tW[wave];
+    const int ts = 16 * wave + 4 * grp;  // this lane's first result row (key) in the chunk
+    auto body = [&](Stage& st, int n) {
+        const int c = chunk_of(n);
+        const int64_t row0 = (int64_t)c * C;
+        publish();
+        float cmx = 0.f;
+        const int sQ = consume(st, n, cmx);
+        __syncthreads();  // tiles, G^T and g are visible
+        sched_fence();
+        issue(st, n + 2);
+        sched_fence();
+        const float uQ = ldexpf(1.f, -sQ);
+
+        // (a) a~[s][t], b[s][t]: s = ts + r, t = 16 jb + m, t >= s
+        f32x4 aa[NBC], bb[NBC];
+#pragma unroll
+        for (int jb = 0; jb < NBC; ++jb) {
+            aa[jb] = f32x4{0.f, 0.f, 0.f, 0.f};
+            bb[jb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+        Frag<T> fk[KSK], fv[KSV];
+#pragma unroll
+        for (int ks = 0; ks < KSK; ++ks)
+            fk[ks] = *reinterpret_cast<const Frag<T>*>(&tK[(16 * wave + m) * LDK + 32 * ks + 8 * grp]);
+#pragma unroll
+        for (int ks = 0; ks < KSV; ++ks)
+            fv[ks] = *reinterpret_cast<const Frag<T>*>(&tV[(16 * wave + m) * LDV + 32 * ks + 8 * grp]);
+#pragma unroll
+        for (int ks = 0; ks < KSK; ++ks)
+#pragma unroll
+            for (int jb = 0; jb < NBC; ++jb)
+                if (jb >= wave)
+                    aa[jb] = mma(fk[ks], *reinterpret_cast<const Frag<T>*>(&tQ[(16 * jb + m) * LDK + 32 * ks + 8 * grp]),
+                                 aa[jb]);
+#pragma unroll
+        for (int ks = 0; ks < KSV; ++ks)
+#pragma unroll
+            for (int jb = 0; jb < NBC; ++jb)
+                if (jb >= wave)
+                    bb[jb] = mma(fv[ks], *reinterpret_cast<const Frag<T>*>(&tD[(16 * jb + m) * LDV + 32 * ks + 8 * grp]),
+                                 bb[jb]);
+        float pmx = 0.f, amx = 0.f;
+#pragma unroll
+        for (int jb = 0; jb < NBC; ++jb) {
+            const float ch = SIMPLE ? 0.f : sC[16 * jb + m];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const bool keep = jb > wave || (jb == wave && m >= 4 * grp + r);
+                aa[jb][r] = keep ? aa[jb][r] : 0.f;
+                bb[jb][r] = keep ? bb[jb][r] + ch : 0.f;  // now mask(b + c^)
+                pmx = fmaxf(pmx, fabsf(bb[jb][r]));
+                amx = fmaxf(amx, fabsf(aa[jb][r]));
+            }
+        }
+        // phi(k) at the result positions
+        float pk[NBI][4];
+#pragma unroll
+        for (int ib = 0; ib < NBI; ++ib)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) pk[ib][r] = to_f32(tK[(ts + r) * LDK + 16 * ib + m]);
+
+        // (b) dK
+        {
+            int sP = 0;
+            if constexpr (Elt<T>::kScaled) sP = scale_exp(wave_max_nonneg(pmx));
+            const float fP = ldexpf(1.f, sP);
+#pragma unroll
+            for (int jb = 0; jb < NBC; ++jb) put4t(&myW[(16 * jb + m) * LDW + 4 * grp], bb[jb], fP);
+            wave_lds_sync();
+            f32x4 x1[NBI], x2[NBI];
+#pragma unroll
+            for (int ib = 0; ib < NBI; ++ib) {
+                x1[ib] = f32x4{0.f, 0.f, 0.f, 0.f};
+                x2[ib] = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+#pragma unroll
+            for (int ks = 0; ks < KSC; ++ks) {
+                if (ks >= wave / 2) {  // rows t < 32 ks + 32 <= 16 wave of mask(b + c^) are zero
+                    const int rb = 32 * ks + rA;
+                    const Frag<T> a = join_frag<T>(lds_read_tr(&myW[rb * LDW + cA]), lds_read_tr(&myW[(rb + 4) * LDW + cA]));
+#pragma unroll
+                    for (int ib = 0; ib < NBI; ++ib) {
+                        const Frag<T> b = join_frag<T>(lds_read_tr(&tQ[rb * LDK + 16 * ib + cA]),
+                                                       lds_read_tr(&tQ[(rb + 4) * LDK + 16 * ib + cA]));
+                        x1[ib] = mma(a, b, x1[ib]);
+                    }
+                }
+            }
+#pragma unroll
+            for (int ks = 0; ks < KSV; ++ks) {
+                const int rb = 32 * ks + rA;
+#pragma unroll
+                for (int ib = 0; ib < NBI; ++ib) {
+                    const Frag<T> b = join_frag<T>(lds_read_tr(&tGT[rb * LDRT + 16 * ib + cA]),
+                                                   lds_read_tr(&tGT[(rb + 4) * LDRT + 16 * ib + cA]));
+                    x2[ib] = mma(fv[ks], b, x2[ib]);
+                }
+            }
+            const float u1 = ldexpf(1.f, -sP) * uQ;
+            f32x4 g[NBI];
+#pragma unroll
+            for (int ib = 0; ib < NBI; ++ib) {
+                const float u2 = ldexpf(1.f, -sExpG[ib / RIW]);
+                const float gz = SIMPLE ? 0.f : sGz[16 * ib + m];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) g[ib][r] = (x1[ib][r] * u1 + x2[ib][r] * u2 + gz) * dphi_of<FM>(pk[ib][r]);
+            }
+            wave_lds_sync();
+#pragma unroll
+            for (int ib = 0; ib < NBI; ++ib) put4t(&myW[(16 * ib + m) * LDW + 4 * grp], g[ib], 1.f);
+            wave_lds_sync();
+#pragma unroll
+            for (int kk = 0; kk < DK / 32; ++kk) {
+                const int rb = 32 * kk + rA;
+                const Frag<T> x = join_frag<T>(lds_read_tr(&myW[rb * LDW + cA]), lds_read_tr(&myW[(rb + 4) * LDW + cA]));
+                buf_store16(bdk, buf_off<T>(row0 + 16 * wave + m, lk.rs, 32 * kk + 8 * grp), __builtin_bit_cast(uint4, x));
+            }
+            wave_lds_sync();
+        }
+
+        // (c) dV = a~ dO + phi(K) G
+        {
+            int sA = 0;
+            if constexpr (Elt<T>::kScaled) sA = scale_exp(wave_max_nonneg(amx));
+            const float fA = ldexpf(1.f, sA);
+#pragma unroll
+            for (int jb = 0; jb < NBC; ++jb) put4t(&myW[(16 * jb + m) * LDW + 4 * grp], aa[jb], fA);
+            wave_lds_sync();
+            f32x4 y1[NBV], y2[NBV];
+#pragma unroll
+            for (int jv = 0; jv < NBV; ++jv) {
+                y1[jv] = f32x4{0.f, 0.f, 0.f, 0.f};
+                y2[jv] = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+#pragma unroll
+            for (int ks = 0; ks < KSC; ++ks) {
+                if (ks >= wave / 2) {
+                    const int rb = 32 * ks + rA;
+                    const Frag<T> a = join_frag<T>(lds_read_tr(&myW[rb * LDW + cA]), lds_read_tr(&myW[(rb + 4) * LDW + cA]));
+#pragma unroll
+                    for (int jv = 0; jv < NBV; ++jv) {
+                        const Frag<T> b = join_frag<T>(lds_read_tr(&tD[rb * LDV + 16 * jv + cA]),
+                                                       lds_read_tr(&tD[(rb + 4) * LDV + 16 * jv + cA]));
+                        y1[jv] = mma(a, b, y1[jv]);
+                    }
+                }
+            }
+            int sM = 0;
+            if constexpr (Elt<T>::kScaled) sM = min(min(sExpG[0], sExpG[1]), min(sExpG[2], sExpG[3]));
+#pragma unroll
+            for (int ks = 0; ks < KSK; ++ks) {
+                // features 32 ks + 8 grp .. + 7 of G^T were published by wave (32 ks + 8 grp) / QW
+                Frag<T> a = fk[ks];
+                if constexpr (Elt<T>::kScaled) a = scale_frag<T>(a, ldexpf(1.f, sM - sExpG[(32 * ks + 8 * grp) / QW]));
+#pragma unroll
+                for (int jv = 0; jv < NBV; ++jv)
+                    y2[jv] = mma(a, *reinterpret_cast<const Frag<T>*>(&tGT[(16 * jv + m) * LDRT + 32 * ks + 8 * grp]),
+                                 y2[jv]);
+            }
+            const float u1 = ldexpf(1.f, -sA) * uQ, u2 = ldexpf(1.f, -sM);
+            f32x4 g[NBV];
+#pragma unroll
+            for (int jv = 0; jv < NBV; ++jv)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) g[jv][r] = y1[jv][r] * u1 + y2[jv][r] * u2;
+            wave_lds_sync();
+#pragma unroll
+            for (int jv = 0; jv < NBV; ++jv) put4t(&myW[(16 * jv + m) * LDW + 4 * grp], g[jv], 1.f);
+            wave_lds_sync();
+#pragma unroll
+            for (int kk = 0; kk < DV / 32; ++kk) {
+                const int rb = 32 * kk + rA;
+                const Frag<T> x = join_frag<T>(lds_read_tr(&myW[rb * LDW + cA]), lds_read_tr(&myW[(rb + 4) * LDW + cA]));
+                buf_store16(bdv, buf_off<T>(row0 + 16 * wave + m, lv.rs, 32 * kk + 8 * grp), __builtin_bit_cast(uint4, x));
+            }
+            wave_lds_sync();
+        }
+
+        // (d) G += Qw^T dO, g += Qw^T c^ on this wave's rows of G
+        {
+            int sC2 = 0;
+            if constexpr (!SIMPLE && Elt<T>::kScaled) sC2 = scale_exp(cmx);
+            const float fC = ldexpf(1.f, sC2);
+#pragma unroll
+            for (int iR = 0; iR < RIW; ++iR) {
+                const int i0 = 16 * (wave * RIW + iR);
+                Frag<T> qa[KSC];
+#pragma unroll
+                for (int ks = 0; ks < KSC; ++ks) {
+                    const int rb = 32 * ks + rA;
+                    qa[ks] = join_frag<T>(lds_read_tr(&tQ[rb * LDK + i0 + cA]), lds_read_tr(&tQ[(rb + 4) * LDK + i0 + cA]));
+                }
+#pragma unroll
+                for (int jv = 0; jv < NBV; ++jv) {
+                    f32x4 t = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int ks = 0; ks < KSC; ++ks) {
+                        const int rb = 32 * ks + rA;
+                        const Frag<T> b = join_frag<T>(lds_read_tr(&tD[rb * LDV + 16 * jv + cA]),
+                                                       lds_read_tr(&tD[(rb + 4) * LDV + 16 * jv + cA]));
+                        t = mma(qa[ks], b, t);
+                    }
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) accG[iR][jv][r] += t[r] * uQ;
+                }
+                if constexpr (!SIMPLE) {
+                    f32x4 t = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int ks = 0; ks < KSC; ++ks) {
+                        Frag<T> cf;
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) cf[e] = static_cast<T>(sC[32 * ks + 8 * grp + e] * fC);
+                        t = mma(qa[ks], cf, t);
+                    }
+                    const float u = uQ * ldexpf(1.f, -sC2);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) accGz[iR][r] += t[r] * u;
+                }
+            }
+        }
+        __syncthreads();  // every wave is done with the tiles, G^T and g
+    };
+    if (nchunks > 0) {
+        Stage s0, s1;
+        issue(s0, 0);
+        sched_fence();
+        issue(s1, 1);
+        sched_fence();
+        for (int n = 0; n < nchunks; n += 2) {
+            body(s0, n);
+            body(s1, n + 1);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Host-side dispatch.
 // ---------------------------------------------------------------------------
 template <typename T, int DK, int DV>
@@ -2671,6 +3650,53 @@ hipError_t fwd_causal_fm(const Plan& p, const void* q, const void* k, const void
                           p.P, p.L, p.eps);
         return launch(fwd_causal_kernel<T, DK, DV, false, FM>, nblk, kThreads, s, qq, kk, vv, pre, oo, p.T, p.lay,
                       p.P, p.L, p.eps);
+    }
+}
+
+// Causal backward: segment states and their exclusive prefixes (as in the
+// causal forward), the forward-order dQ scan, the exclusive suffixes of its
+// per-segment (G, g) sums, then the reverse-order dK, dV scan.
+template <typename T, int DK, int DV, int FM>
+hipError_t bwd_causal_fm(const Plan& p, const void* q, const void* k, const void* v, const void* dout, void* dq,
+                         void* dk, void* dv, void* ws, hipStream_t s) {
+    if constexpr (!kCausalKernels<T, DK, DV>) {
+        return hipErrorInvalidValue;
+    } else {
+        char* w = static_cast<char*>(ws);
+        float* part = reinterpret_cast<float*>(w + p.off_part);
+        float* gpart = reinterpret_cast<float*>(w + p.off_cgpart);
+        float* wcp = reinterpret_cast<float*>(w + p.off_cwc);
+        int* esp = reinterpret_cast<int*>(w + p.off_ces);
+        float* total = reinterpret_cast<float*>(w + p.off_fstate);  // the full state; not needed here
+        constexpr int E4 = (DK * DV + DK) / 4;
+        const int64_t nred = p.BH * ((E4 + kThreads - 1) / kThreads);
+        hipError_t e;
+        if (p.P > 1) {
+            e = launch_state_reduction<T, DK, DV, FM>(p, k, v, total, part, s);
+            if (e != hipSuccess) return e;
+            e = launch(prefix_kernel<DK, DV>, nred, kThreads, s, part, p.P, total, total + p.BH * DK * DV, p.BH);
+            if (e != hipSuccess) return e;
+        }
+        const float* pre = p.P > 1 ? part : nullptr;
+        float* gp = p.P > 1 ? gpart : nullptr;
+        const T* qq = static_cast<const T*>(q);
+        const T* kk = static_cast<const T*>(k);
+        const T* vv = static_cast<const T*>(v);
+        const T* dd = static_cast<const T*>(dout);
+        const int64_t nblk = p.BH * p.P;
+        e = p.simple ? launch(bwd_causal_q_kernel<T, DK, DV, true, FM>, nblk, kThreads, s, qq, kk, vv, dd, pre,
+                              static_cast<T*>(dq), wcp, esp, gp, p.T, p.lay, p.P, p.L, p.nche, p.eps)
+                     : launch(bwd_causal_q_kernel<T, DK, DV, false, FM>, nblk, kThreads, s, qq, kk, vv, dd, pre,
+                              static_cast<T*>(dq), wcp, esp, gp, p.T, p.lay, p.P, p.L, p.nche, p.eps);
+        if (e != hipSuccess) return e;
+        if (p.P > 1) {
+            e = launch(suffix_kernel<DK, DV>, nred, kThreads, s, gpart, p.P, p.BH);
+            if (e != hipSuccess) return e;
+        }
+        return p.simple ? launch(bwd_causal_kv_kernel<T, DK, DV, true, FM>, nblk, kThreads, s, qq, kk, vv, dd, wcp,
+                                 esp, gp, static_cast<T*>(dk), static_cast<T*>(dv), p.T, p.lay, p.P, p.L, p.nche)
+                        : launch(bwd_causal_kv_kernel<T, DK, DV, false, FM>, nblk, kThreads, s, qq, kk, vv, dd, wcp,
+                                 esp, gp, static_cast<T*>(dk), static_cast<T*>(dv), p.T, p.lay, p.P, p.L, p.nche);
     }
 }
 
@@ -2768,6 +3794,15 @@ hipError_t fwd_causal_t(const Plan& p, const void* q, const void* k, const void*
     }
 }
 template <typename T, int DK, int DV>
+hipError_t bwd_causal_t(const Plan& p, const void* q, const void* k, const void* v, const void* dout, void* dq,
+                        void* dk, void* dv, void* ws, hipStream_t s) {
+    if constexpr (!kCausalKernels<T, DK, DV>) {
+        return hipErrorInvalidValue;
+    } else {
+        LA_FEATURE_MAP(bwd_causal_fm, q, k, v, dout, dq, dk, dv, ws, s);
+    }
+}
+template <typename T, int DK, int DV>
 hipError_t bwd_dq_t(const Plan& p, const void* q, const void* dout, const float* state, void* dq, void* ws,
                     hipStream_t s) {
     LA_FEATURE_MAP(bwd_dq_fm, q, dout, state, dq, ws, s);
@@ -2851,6 +3886,10 @@ hipError_t unit_bwd_dq(const Plan& p, const void* q, const void* dout, const flo
 hipError_t unit_bwd_dkv(const Plan& p, const void* k, const void* v, void* dk, void* dv, void* ws, hipStream_t s) {
     LA_DV_DISPATCH(bwd_dkv_t, k, v, dk, dv, ws, s);
 }
+hipError_t unit_bwd_causal(const Plan& p, const void* q, const void* k, const void* v, const void* dout, void* dq,
+                           void* dk, void* dv, void* ws, hipStream_t s) {
+    LA_DV_DISPATCH(bwd_causal_t, q, k, v, dout, dq, dk, dv, ws, s);
+}
 SplitCfg unit_split_config(int step, int DV) {
     switch (DV) {
         case 32: return split_config_t<UT, UDK, 32>(step);
@@ -2860,8 +3899,8 @@ SplitCfg unit_split_config(int step, int DV) {
     }
 }
 
-const KernelSet kUnitSet = {unit_fwd_state, unit_fwd_output, unit_bwd_dq, unit_bwd_dkv, unit_split_config,
-                             unit_fwd_causal};
+const KernelSet kUnitSet = {unit_fwd_state, unit_fwd_output, unit_bwd_dq,    unit_bwd_dkv,
+                             unit_split_config, unit_fwd_causal, unit_bwd_causal};
 
 }  // namespace
 

@@ -48,7 +48,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.la_version() == 3
+    assert L.la_version() == 4
     for s in range(11):
         txt = L.la_status_str(s).decode()
         assert txt.startswith("LA_"), txt
@@ -286,18 +286,28 @@ def test_token_major_layout_limits(L):
     assert fwd_call(L, prob(B=0, flags=BTHD)) == 0
 
 
-def test_causal_flag_accepted_by_la_fwd_only(L):
-    """LA_CAUSAL: la_fwd takes it for f16/bf16 with D, Dv in {64, 128}; every
-    other entry point rejects it before any HIP call."""
+def test_causal_flag_accepted_by_la_fwd_and_la_bwd_only(L):
+    """LA_CAUSAL: la_fwd and la_bwd take it for f16/bf16 with D, Dv in
+    {64, 128}; the step calls reject it before any HIP call. Every call here
+    ends in an argument error."""
     CAUSAL = 0x10
     p = prob(flags=CAUSAL)
     need = L.la_workspace_bytes(ctypes.byref(p))
-    assert need > 0 and L.la_state_bytes(ctypes.byref(p)) > 0
+    assert need > L.la_workspace_bytes(ctypes.byref(prob())), "causal backward scratch not counted"
+    assert L.la_state_bytes(ctypes.byref(p)) > 0
     assert fwd_call(L, prob(flags=CAUSAL, dtype=0)) == DTYPE
     for d, dv in ((32, 0), (96, 0), (64, 32), (128, 96)):
         assert fwd_call(L, prob(flags=CAUSAL, D=d, Dv=dv)) == HEAD_DIM, (d, dv)
     d = addrs(9)
-    assert L.la_bwd(ctypes.byref(p), *d[:9], need, None) == FLAGS
+    p32 = prob(flags=CAUSAL, dtype=0)
+    assert L.la_bwd(ctypes.byref(p32), *d[:9], L.la_workspace_bytes(ctypes.byref(p32)), None) == DTYPE
+    p96 = prob(flags=CAUSAL, D=96)
+    assert L.la_bwd(ctypes.byref(p96), *d[:9], 1 << 30, None) == HEAD_DIM
+    # the causal backward reads no state: NULL passes that check and the
+    # workspace check reports; without the flag NULL is reported first
+    args = [d[0], d[1], d[2], d[3], None, d[5], d[6], d[7], d[8]]
+    assert L.la_bwd(ctypes.byref(p), *args, need - 1, None) == WORKSPACE
+    assert L.la_bwd(ctypes.byref(prob()), *args, need - 1, None) == NULL
     assert L.la_fwd_state(ctypes.byref(p), d[0], d[1], d[2], d[3], need, None) == FLAGS
     assert L.la_fwd_output(ctypes.byref(p), d[0], d[1], d[2], None) == FLAGS
     assert L.la_bwd_dq(ctypes.byref(p), d[0], d[1], d[2], d[3], d[4], need, None) == FLAGS
