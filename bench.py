@@ -109,16 +109,26 @@ def cpu_baseline(w, x, max_heads: int) -> dict:
     }
 
 
-def causal_bench(args, w, q, k, v, o, state, ws, do_flush) -> int:
-    """The causal forward: one la_fwd call (segment states, their prefixes, the
-    chunked scan). Its rate counts the algorithmic minimum, one pass over Q, K,
-    V and O; the path itself reads K and V twice (states, then the scan)."""
+def causal_bench(args, w, t, do_flush) -> int:
+    """The causal path: one la_fwd call (segment states, their prefixes, the
+    chunked scan), then one la_bwd call (segment states and prefixes again,
+    the forward-order dQ scan, the suffixes of its segment sums, the
+    reverse-order dK, dV scan). Rates count the algorithmic minimum: one pass
+    over Q, K, V and O forward, over Q, K, V, dO and dQ, dK, dV backward; the
+    path itself reads K and V once more in each pass (the segment states)."""
+    q, k, v, do, o, dq, dk, dv = (t[n] for n in ("q", "k", "v", "do", "o", "dq", "dk", "dv"))
+    prob = la.make_problem(q.shape, q.dtype, w.eps, w.simple, dv=w.dv, causal=True)
+    state = la.new_state(prob, q.device)
+    ws = la.workspace(prob, q.device)
+
     def step(ev):
         ev[0].record()
         la.fwd(q, k, v, eps=w.eps, simple=w.simple, out=o, state=state, ws=ws, causal=True)
         ev[1].record()
+        la.bwd(q, k, v, do, None, eps=w.eps, simple=w.simple, dq=dq, dk=dk, dv=dv, ws=ws, causal=True)
+        ev[2].record()
 
-    mk = lambda: [torch.cuda.Event(enable_timing=True) for _ in range(2)]  # noqa: E731
+    mk = lambda: [torch.cuda.Event(enable_timing=True) for _ in range(3)]  # noqa: E731
     for _ in range(args.warmup):
         do_flush(args.flush)
         step(mk())
@@ -130,10 +140,13 @@ def causal_bench(args, w, q, k, v, o, state, ws, do_flush) -> int:
         step(events[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms = np.array([ev[0].elapsed_time(ev[1]) for ev in events])
+    fwd_ms = np.array([ev[0].elapsed_time(ev[1]) for ev in events])
+    bwd_ms = np.array([ev[1].elapsed_time(ev[2]) for ev in events])
     lb = launch_bytes(w)
-    alg = lb["fwd_state"] + lb["fwd_output"]  # Q, K, V in, O out
-    value = alg / (float(np.mean(ms)) * 1e-3) / 1e9
+    alg_f = lb["fwd_state"] + lb["fwd_output"]  # Q, K, V in, O out
+    alg_b = lb["bwd_dq"] + lb["bwd_dkv"]  # Q, K, V, dO in, dQ, dK, dV out
+    value = alg_f / (float(np.mean(fwd_ms)) * 1e-3) / 1e9
+    bwd_rate = alg_b / (float(np.mean(bwd_ms)) * 1e-3) / 1e9
     line = {
         "metric": "causal LA fwd GB/s (algorithmic Q, K, V, O bytes) and ms",
         "value": round(value, 1),
@@ -141,18 +154,22 @@ def causal_bench(args, w, q, k, v, o, state, ws, do_flush) -> int:
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(float(np.mean(ms)), 4),
+        "ms_per_step": round(float(np.mean(fwd_ms + bwd_ms)), 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": DTYPE_NAME[w.dtype],
-        "data": "synthetic: seeded N(0, sigma^2) Q, K, V rounded to the dtype",
+        "data": "synthetic: seeded N(0, sigma^2) Q, K, V, dO rounded to the dtype",
         "config": {"workload": w.name + "-causal", "B": w.B, "H": w.H, "T": w.T, "D": w.D, "Dv": w.dv,
-                   "mode": ("simple_la" if w.simple else "normalised") + ", causal", "pass": "fwd"},
-        "fwd_ms": round(float(np.mean(ms)), 4),
-        "fwd_ms_min": round(float(np.min(ms)), 4),
-        "fwd_ms_median": round(float(np.median(ms)), 4),
+                   "mode": ("simple_la" if w.simple else "normalised") + ", causal", "pass": "fwd+bwd"},
+        "fwd_ms": round(float(np.mean(fwd_ms)), 4),
+        "fwd_ms_min": round(float(np.min(fwd_ms)), 4),
+        "fwd_ms_median": round(float(np.median(fwd_ms)), 4),
         "fwd_frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
+        "bwd_ms": round(float(np.mean(bwd_ms)), 4),
+        "bwd_ms_median": round(float(np.median(bwd_ms)), 4),
+        "bwd_GBps_algorithmic": round(bwd_rate, 1),
+        "bwd_frac_of_hbm_peak": round(bwd_rate / HBM_PEAK_GBS, 4),
         "wall_ms_per_step_incl_flush": round(wall / args.steps * 1e3, 4),
         "roofline": {"kernel": "la_fwd causal (state, prefix, chunked scan)", "bound": "hbm",
                      "achieved": round(value, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -175,7 +192,7 @@ def main() -> int:
     ap.add_argument("--all-cache-conditions", action="store_true",
                     help="also time the step after a writing flush and with no flush")
     ap.add_argument("--causal", action="store_true",
-                    help="time the causal forward (LA_CAUSAL) instead of the bidirectional fwd+bwd")
+                    help="time the causal forward and backward (LA_CAUSAL) instead of the bidirectional path")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 1 GiB device copy (for counter scaling)")
     args = ap.parse_args()
@@ -223,7 +240,8 @@ def main() -> int:
         ev[4].record()
 
     if args.causal:
-        return causal_bench(args, w, q, k, v, o, state, ws, do_flush)
+        return causal_bench(args, w, {"q": q, "k": k, "v": v, "do": do, "o": o, "dq": dq, "dk": dk, "dv": dv},
+                            do_flush)
 
     mk = lambda: [torch.cuda.Event(enable_timing=True) for _ in range(5)]  # noqa: E731
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)

@@ -2672,7 +2672,7 @@ __device__ __forceinline__ void put4t(T* dst, f32x4 x, float f) {
 //       four exponents and rescales the other waves' columns to it as it
 //       reads them for G += Qw^T dO.
 // R^T and z are published at the top of the next chunk, after the barrier
-// that ends this one. Three barriers per chunk; two chunks of loads in flight.
+// that ends this one. Three barriers per chunk; one chunk of loads in flight.
 template <typename T, int DK, int DV, bool SIMPLE, int FM>
 __global__ __launch_bounds__(kThreads, (CausalBwdShape<DK, DV>::kMinBlocks)) void bwd_causal_q_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const T* __restrict__ dout,
@@ -2823,7 +2823,7 @@ __global__ __launch_bounds__(kThreads, (CausalBwdShape<DK, DV>::kMinBlocks)) voi
         consume(st, c);
         __syncthreads();  // tiles of chunk c, R^T and z are visible
         sched_fence();
-        issue(st, c + 2);  // two chunks ahead; past the segment end these read zeros
+        issue(st, c + 1);  // past the segment end these read zeros
         sched_fence();
 
         // (a) a[t][s] and b[t][s], t = tq + r, s = 16 jb + m, s <= t
@@ -3080,19 +3080,15 @@ __global__ __launch_bounds__(kThreads, (CausalBwdShape<DK, DV>::kMinBlocks)) voi
         }
         __syncthreads();  // every wave is done with the tiles, R^T, z and Qw^T
     };
-    // Two chunks of loads in flight; the chunk count is even so that the loop
-    // has no branch around loads. A chunk past the segment end reads zeros,
-    // adds nothing and stores nothing.
+    // One chunk of loads in flight (a chunk's work outlasts the load latency
+    // many times over; a second stage only adds registers). The chunk count is
+    // even (the K/V scan indexes the exponents the same way); a chunk past the
+    // segment end reads zeros, adds nothing and stores nothing.
     if (nchunks > 0) {
-        Stage s0, s1;
-        issue(s0, 0);
+        Stage st;
+        issue(st, 0);
         sched_fence();
-        issue(s1, 1);
-        sched_fence();
-        for (int c = 0; c < nchunks; c += 2) {
-            body(s0, c);
-            body(s1, c + 1);
-        }
+        for (int c = 0; c < nchunks; ++c) body(st, c);
     }
     if (gpart != nullptr) {
         float* gp = gpart + (bh * P + p) * (int64_t)(DK * DV + DK);
@@ -3249,8 +3245,8 @@ __global__ __launch_bounds__(kThreads, (CausalBwdShape<DK, DV>::kMinBlocks)) voi
     const HeadBuf bwc{__builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(wc + 2 * (bh * T_ + t0)), 0,
                                                         (int)(len > 0 ? 8 * len : 0), 0x00020000)};
     const int* esb = es + (bh * P + p) * (int64_t)nche;
-    // step n of the walk visits chunk nchunks - 1 - n; the prefetches past the
-    // first chunk go to chunks past the segment end, which read zeros
+    // step n of the walk visits chunk nchunks - 1 - n; the prefetch after the
+    // first chunk goes to a chunk past the segment end, which reads zeros
     auto chunk_of = [&](int n) { return n < nchunks ? nchunks - 1 - n : n; };
     auto issue = [&](Stage& st, int n) {
         const int c = chunk_of(n);
@@ -3331,7 +3327,7 @@ __global__ __launch_bounds__(kThreads, (CausalBwdShape<DK, DV>::kMinBlocks)) voi
         const int sQ = consume(st, n, cmx);
         __syncthreads();  // tiles, G^T and g are visible
         sched_fence();
-        issue(st, n + 2);
+        issue(st, n + 1);
         sched_fence();
         const float uQ = ldexpf(1.f, -sQ);
 
@@ -3545,15 +3541,10 @@ __global__ __launch_bounds__(kThreads, (CausalBwdShape<DK, DV>::kMinBlocks)) voi
         __syncthreads();  // every wave is done with the tiles, G^T and g
     };
     if (nchunks > 0) {
-        Stage s0, s1;
-        issue(s0, 0);
+        Stage st;
+        issue(st, 0);
         sched_fence();
-        issue(s1, 1);
-        sched_fence();
-        for (int n = 0; n < nchunks; n += 2) {
-            body(s0, n);
-            body(s1, n + 1);
-        }
+        for (int n = 0; n < nchunks; ++n) body(st, n);
     }
 }
 
