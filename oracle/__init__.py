@@ -20,6 +20,9 @@ The causal variant (token t attends to tokens s <= t; flash-linear-attention
 README, "Different forms of linear attention") is given by its masked
 quadratic form and its recurrent form.
 
+Every function takes an optional `scale` that multiplies phi(q) (default 1:
+the method as stated).
+
 Pins (tests/test_oracle.py): brute-force quadratic form in pure Python, a
 hand-worked example (tests/golden/), V = ones, joint K/V permutation, Q-row
 permutation, the T = 1 closed form, linearity in V, central finite
@@ -50,6 +53,7 @@ from .la_oracle import (  # noqa: F401
     bwd_leading_terms_head,
     bwd_q_side_head,
     phi,
+    qfeat,
     quadratic_head,
     sampled_rows_head,
     state_head,

@@ -41,6 +41,13 @@ def phi(x: np.ndarray, fm: str = "elu1") -> np.ndarray:
     return np.where(x > 0, x + 1.0, np.exp(np.minimum(x, 0.0)))
 
 
+def qfeat(q: np.ndarray, fm: str = "elu1", scale: float = 1.0) -> np.ndarray:
+    """The query feature scale * phi(q). The optional scale multiplies phi(q),
+    as flash-linear-attention's kernels multiply the (feature-mapped) query by
+    their `scale` argument; 1 leaves the method as stated."""
+    return scale * phi(q, fm)
+
+
 def dphi(x: np.ndarray, fm: str = "elu1") -> np.ndarray:
     """Derivative of phi. elu1: 1 for x > 0, exp(x) for x <= 0 (both sides are
     1 at 0). relu: 1 for x > 0, 0 for x <= 0 (0 at the kink). identity: 1."""
@@ -53,7 +60,7 @@ def dphi(x: np.ndarray, fm: str = "elu1") -> np.ndarray:
     return np.where(x > 0, 1.0, np.exp(np.minimum(x, 0.0)))
 
 
-def quadratic_head(q, k, v, eps: float, simple: bool, fm: str = "elu1") -> np.ndarray:
+def quadratic_head(q, k, v, eps: float, simple: bool, fm: str = "elu1", scale: float = 1.0) -> np.ndarray:
     """Quadratic ("parallel") form for one (batch, head): Q, K [T, Dk] and
     V [T, Dv] -> O [T, Dv].
 
@@ -61,18 +68,18 @@ def quadratic_head(q, k, v, eps: float, simple: bool, fm: str = "elu1") -> np.nd
     simple_la: O = A V. flash-linear-attention README, "Different forms of
     linear attention", Parallel. Cost O(T^2 D): tiny T only.
     """
-    a = phi(q, fm) @ phi(k, fm).T
+    a = qfeat(q, fm, scale) @ phi(k, fm).T
     num = a @ np.asarray(v, dtype=np.float64)
     if simple:
         return num
     return num / (a.sum(axis=1) + eps)[:, None]
 
 
-def output_head(q, s, z, eps: float, simple: bool, fm: str = "elu1") -> np.ndarray:
+def output_head(q, s, z, eps: float, simple: bool, fm: str = "elu1", scale: float = 1.0) -> np.ndarray:
     """Last step of the forward for one (batch, head), from a given state:
     O = phi(Q) S / (phi(Q) z + eps), or phi(Q) S for simple_la (FBi-LA
     README, intro and "Update" 2024-12-28)."""
-    qt = phi(q, fm)
+    qt = qfeat(q, fm, scale)
     num = qt @ s
     if simple:
         return num
@@ -80,17 +87,17 @@ def output_head(q, s, z, eps: float, simple: bool, fm: str = "elu1") -> np.ndarr
     return num / den[:, None]
 
 
-def fwd_head(q, k, v, eps: float, simple: bool, fm: str = "elu1"):
+def fwd_head(q, k, v, eps: float, simple: bool, fm: str = "elu1", scale: float = 1.0):
     """Linear form for one (batch, head): returns (O, S, z).
 
     S = phi(K)^T V (Dk x Dv, S[i, j] = sum_t phi(k_t)[i] v_t[j]),
     z = sum_t phi(k_t), then O from output_head.
     """
     s, z = state_head(k, v, fm)
-    return output_head(q, s, z, eps, simple, fm), s, z
+    return output_head(q, s, z, eps, simple, fm, scale), s, z
 
 
-def bwd_q_side_head(q, do, s, z, eps: float, simple: bool, fm: str = "elu1"):
+def bwd_q_side_head(q, do, s, z, eps: float, simple: bool, fm: str = "elu1", scale: float = 1.0):
     """Q side of the backward for one (batch, head), from the forward state.
 
     The chain rule applied to the formula of fwd_head (the FBi-LA README's
@@ -104,15 +111,16 @@ def bwd_q_side_head(q, do, s, z, eps: float, simple: bool, fm: str = "elu1"):
       dQ = dphi(q) * phi'(q)
     """
     do = np.asarray(do, dtype=np.float64)
-    qt = phi(q, fm)
+    qt = qfeat(q, fm, scale)
     u = do @ s.T  # row t is S dO_t
+    dq_of = scale * dphi(q, fm)  # d(scale phi(q)) / dq
     if simple:
-        return u * dphi(q, fm), qt.T @ do, np.zeros_like(z)
+        return u * dq_of, qt.T @ do, np.zeros_like(z)
     den = qt @ z + eps
     r = np.einsum("td,td->t", qt, u)
     c = -r / den**2
     dqt = u / den[:, None] + c[:, None] * z[None, :]
-    return dqt * dphi(q, fm), qt.T @ (do / den[:, None]), c @ qt
+    return dqt * dq_of, qt.T @ (do / den[:, None]), c @ qt
 
 
 def bwd_kv_side_head(k, v, ds, dz, simple: bool, fm: str = "elu1"):
@@ -127,7 +135,7 @@ def bwd_kv_side_head(k, v, ds, dz, simple: bool, fm: str = "elu1"):
     return dkt * dphi(k, fm), kt @ ds
 
 
-def bwd_head(q, k, v, do, eps: float, simple: bool, fm: str = "elu1"):
+def bwd_head(q, k, v, do, eps: float, simple: bool, fm: str = "elu1", scale: float = 1.0):
     """Vector-Jacobian product of L = sum(O * dO) for one (batch, head).
 
     Returns (dQ, dK, dV). eps is a constant. Derived by the chain rule from
@@ -136,7 +144,7 @@ def bwd_head(q, k, v, do, eps: float, simple: bool, fm: str = "elu1"):
     bwd_kv_side_head.
     """
     s, z = state_head(k, v, fm)
-    dq, ds, dz = bwd_q_side_head(q, do, s, z, eps, simple, fm)
+    dq, ds, dz = bwd_q_side_head(q, do, s, z, eps, simple, fm, scale)
     dk, dv = bwd_kv_side_head(k, v, ds, dz, simple, fm)
     return dq, dk, dv
 
@@ -168,7 +176,7 @@ def state_head(k, v, fm: str = "elu1"):
     return kt.T @ np.asarray(v, dtype=np.float64), kt.sum(axis=0)
 
 
-def sampled_rows_head(q, k, v, rows, eps: float, simple: bool, fm: str = "elu1") -> np.ndarray:
+def sampled_rows_head(q, k, v, rows, eps: float, simple: bool, fm: str = "elu1", scale: float = 1.0) -> np.ndarray:
     """Output rows O_t, t in ``rows``, computed one by one from the quadratic form.
 
     O_t = sum_s a_ts v_s / (sum_s a_ts + eps) with a_ts = phi(q_t) . phi(k_s);
@@ -178,7 +186,7 @@ def sampled_rows_head(q, k, v, rows, eps: float, simple: bool, fm: str = "elu1")
     v = np.asarray(v, dtype=np.float64)
     out = np.empty((len(rows), v.shape[1]))
     for n, t in enumerate(rows):
-        a = kt @ phi(q[t], fm)
+        a = kt @ qfeat(q[t], fm, scale)
         out[n] = a @ v
         if not simple:
             out[n] /= a.sum() + eps
@@ -191,7 +199,7 @@ def _heads(x: np.ndarray, dtype: str):
     return d.reshape(-1, d.shape[-2], d.shape[-1])
 
 
-def fwd(q, k, v, dtype: str, eps: float, simple: bool, fm: str = "elu1"):
+def fwd(q, k, v, dtype: str, eps: float, simple: bool, fm: str = "elu1", scale: float = 1.0):
     """Forward over storage arrays Q, K [B, H, T, Dk] and V [B, H, T, Dv]:
     (O [B,H,T,Dv], S [B,H,Dk,Dv], z [B,H,Dk])."""
     lead = q.shape[:-1]
@@ -201,18 +209,18 @@ def fwd(q, k, v, dtype: str, eps: float, simple: bool, fm: str = "elu1"):
     s = np.empty((n, dk, dv))
     z = np.empty((n, dk))
     for h in range(n):
-        o[h], s[h], z[h] = fwd_head(qh[h], kh[h], vh[h], eps, simple, fm)
+        o[h], s[h], z[h] = fwd_head(qh[h], kh[h], vh[h], eps, simple, fm, scale)
     return (o.reshape(lead + (dv,)), s.reshape(lead[:-1] + (dk, dv)),
             z.reshape(lead[:-1] + (dk,)))
 
 
-def bwd(q, k, v, do, dtype: str, eps: float, simple: bool, fm: str = "elu1"):
+def bwd(q, k, v, do, dtype: str, eps: float, simple: bool, fm: str = "elu1", scale: float = 1.0):
     """Backward over storage arrays Q, K [B, H, T, Dk] and V, dO [B, H, T, Dv]:
     (dQ, dK, dV), float64, shaped like Q, K, V."""
     qh, kh, vh, dh = (_heads(x, dtype) for x in (q, k, v, do))
     dq, dk, dv = np.empty(qh.shape), np.empty(kh.shape), np.empty(vh.shape)
     for h in range(qh.shape[0]):
-        dq[h], dk[h], dv[h] = bwd_head(qh[h], kh[h], vh[h], dh[h], eps, simple, fm)
+        dq[h], dk[h], dv[h] = bwd_head(qh[h], kh[h], vh[h], dh[h], eps, simple, fm, scale)
     return dq.reshape(q.shape), dk.reshape(k.shape), dv.reshape(v.shape)
 
 
@@ -222,23 +230,23 @@ def bwd(q, k, v, do, dtype: str, eps: float, simple: bool, fm: str = "elu1"):
 # Parallel form is the quadratic form with a causal mask; its FusedRecurrent
 # form carries the state S_t = S_{t-1} + phi(k_t) v_t^T from token to token.
 
-def causal_quadratic_head(q, k, v, eps: float, simple: bool, fm: str = "elu1") -> np.ndarray:
+def causal_quadratic_head(q, k, v, eps: float, simple: bool, fm: str = "elu1", scale: float = 1.0) -> np.ndarray:
     """Causal Parallel form for one (batch, head): A = phi(Q) phi(K)^T with
     A[t, s] = 0 for s > t; normalised O = (A V) / (A 1 + eps), simple_la
     O = A V. Cost O(T^2 D): tiny T only."""
-    a = np.tril(phi(q, fm) @ phi(k, fm).T)
+    a = np.tril(qfeat(q, fm, scale) @ phi(k, fm).T)
     num = a @ np.asarray(v, dtype=np.float64)
     if simple:
         return num
     return num / (a.sum(axis=1) + eps)[:, None]
 
 
-def causal_recurrent_head(q, k, v, eps: float, simple: bool, fm: str = "elu1"):
+def causal_recurrent_head(q, k, v, eps: float, simple: bool, fm: str = "elu1", scale: float = 1.0):
     """Causal Recurrent form for one (batch, head), token by token:
     S_t = S_{t-1} + phi(k_t) v_t^T, z_t = z_{t-1} + phi(k_t) (S_0 = 0, z_0 = 0),
     O_t = phi(q_t) S_t / (phi(q_t) . z_t + eps), or phi(q_t) S_t for simple_la.
     Returns (O, S_T, z_T); S_T, z_T are the non-causal state of the head."""
-    qt, kt = phi(q, fm), phi(k, fm)
+    qt, kt = qfeat(q, fm, scale), phi(k, fm)
     v = np.asarray(v, dtype=np.float64)
     T, dk = kt.shape
     s = np.zeros((dk, v.shape[1]))
@@ -253,7 +261,7 @@ def causal_recurrent_head(q, k, v, eps: float, simple: bool, fm: str = "elu1"):
     return o, s, z
 
 
-def causal_sampled_rows_head(q, k, v, rows, eps: float, simple: bool, fm: str = "elu1") -> np.ndarray:
+def causal_sampled_rows_head(q, k, v, rows, eps: float, simple: bool, fm: str = "elu1", scale: float = 1.0) -> np.ndarray:
     """Causal output rows O_t, t in ``rows``, one by one from the masked
     quadratic form: O_t = sum_{s <= t} a_ts v_s / (sum_{s <= t} a_ts + eps),
     a_ts = phi(q_t) . phi(k_s). Cost O(t D) per row, for full-size sequences."""
@@ -261,14 +269,14 @@ def causal_sampled_rows_head(q, k, v, rows, eps: float, simple: bool, fm: str = 
     v = np.asarray(v, dtype=np.float64)
     out = np.empty((len(rows), v.shape[1]))
     for n, t in enumerate(rows):
-        a = kt[: t + 1] @ phi(q[t], fm)
+        a = kt[: t + 1] @ qfeat(q[t], fm, scale)
         out[n] = a @ v[: t + 1]
         if not simple:
             out[n] /= a.sum() + eps
     return out
 
 
-def causal_fwd(q, k, v, dtype: str, eps: float, simple: bool, fm: str = "elu1"):
+def causal_fwd(q, k, v, dtype: str, eps: float, simple: bool, fm: str = "elu1", scale: float = 1.0):
     """Causal forward over storage arrays Q, K [B, H, T, Dk], V [B, H, T, Dv]:
     (O [B,H,T,Dv], S [B,H,Dk,Dv], z [B,H,Dk]) by the recurrent form; S and z are
     the full-sequence state."""
@@ -279,12 +287,12 @@ def causal_fwd(q, k, v, dtype: str, eps: float, simple: bool, fm: str = "elu1"):
     s = np.empty((n, dk, dv))
     z = np.empty((n, dk))
     for h in range(n):
-        o[h], s[h], z[h] = causal_recurrent_head(qh[h], kh[h], vh[h], eps, simple, fm)
+        o[h], s[h], z[h] = causal_recurrent_head(qh[h], kh[h], vh[h], eps, simple, fm, scale)
     return (o.reshape(lead + (dv,)), s.reshape(lead[:-1] + (dk, dv)),
             z.reshape(lead[:-1] + (dk,)))
 
 
-def causal_bwd_head(q, k, v, do, eps: float, simple: bool, fm: str = "elu1"):
+def causal_bwd_head(q, k, v, do, eps: float, simple: bool, fm: str = "elu1", scale: float = 1.0):
     """Vector-Jacobian product of L = sum(O * dO) for the causal form of one
     (batch, head), eps held constant: the chain rule through the recurrent
     form (causal_recurrent_head). With the inclusive prefixes S_t, z_t,
@@ -294,8 +302,10 @@ def causal_bwd_head(q, k, v, do, eps: float, simple: bool, fm: str = "elu1"):
     and with the suffixes G_s = sum_{t >= s} phi(q_t) w_t^T (simple_la: dO_t),
     g_s = sum_{t >= s} c_t phi(q_t) (simple_la: 0),
       dphi(k_s) = G_s v_s + g_s,  dV_s = G_s^T phi(k_s).
-    dQ = dphi(q) * phi'(q), dK = dphi(k) * phi'(k). Returns (dQ, dK, dV)."""
-    qt, kt = phi(q, fm), phi(k, fm)
+    dQ = dphi(q) * phi'(q), dK = dphi(k) * phi'(k). Returns (dQ, dK, dV).
+    With a scale, phi(q) stands for scale * phi(q) throughout and dQ gains
+    the factor scale."""
+    qt, kt = qfeat(q, fm, scale), phi(k, fm)
     v = np.asarray(v, dtype=np.float64)
     do = np.asarray(do, dtype=np.float64)
     T, dk = kt.shape
@@ -326,14 +336,14 @@ def causal_bwd_head(q, k, v, do, eps: float, simple: bool, fm: str = "elu1"):
         gz += c[t] * qt[t]
         dkt[t] = g @ v[t] + gz
         dv[t] = g.T @ kt[t]
-    return dqt * dphi(q, fm), dkt * dphi(k, fm), dv
+    return dqt * (scale * dphi(q, fm)), dkt * dphi(k, fm), dv
 
 
-def causal_bwd(q, k, v, do, dtype: str, eps: float, simple: bool, fm: str = "elu1"):
+def causal_bwd(q, k, v, do, dtype: str, eps: float, simple: bool, fm: str = "elu1", scale: float = 1.0):
     """Causal backward over storage arrays Q, K [B, H, T, Dk] and V, dO
     [B, H, T, Dv]: (dQ, dK, dV), float64, shaped like Q, K, V."""
     qh, kh, vh, dh = (_heads(x, dtype) for x in (q, k, v, do))
     dq, dk, dv = np.empty(qh.shape), np.empty(kh.shape), np.empty(vh.shape)
     for h in range(qh.shape[0]):
-        dq[h], dk[h], dv[h] = causal_bwd_head(qh[h], kh[h], vh[h], dh[h], eps, simple, fm)
+        dq[h], dk[h], dv[h] = causal_bwd_head(qh[h], kh[h], vh[h], dh[h], eps, simple, fm, scale)
     return dq.reshape(q.shape), dk.reshape(k.shape), dv.reshape(v.shape)

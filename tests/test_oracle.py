@@ -60,8 +60,9 @@ def test_phi_special_values_and_derivative():
 
 # ---------------------------------------------------------------- forward
 
-def brute_force(q, k, v, eps, simple, fm="elu1"):
-    """Pure-Python quadratic form: O_t = sum_s a_ts v_s / (sum_s a_ts + eps)."""
+def brute_force(q, k, v, eps, simple, fm="elu1", scale=1.0):
+    """Pure-Python quadratic form: O_t = sum_s a_ts v_s / (sum_s a_ts + eps),
+    a_ts = (scale phi(q_t)) . phi(k_s)."""
     def ph(x):
         if fm == "relu":
             return x if x > 0 else 0.0
@@ -71,7 +72,7 @@ def brute_force(q, k, v, eps, simple, fm="elu1"):
     T, D, Dv = len(q), len(q[0]), len(v[0])
     out = []
     for t in range(T):
-        a = [sum(ph(q[t][i]) * ph(k[s][i]) for i in range(D)) for s in range(T)]
+        a = [sum(scale * ph(q[t][i]) * ph(k[s][i]) for i in range(D)) for s in range(T)]
         row = [sum(a[s] * v[s][j] for s in range(T)) for j in range(Dv)]
         if not simple:
             den = sum(a) + eps
@@ -197,12 +198,12 @@ def test_batched_fwd_matches_per_head_and_decodes():
 
 # ---------------------------------------------------------------- backward
 
-def loss(q, k, v, do, eps, simple, fm="elu1"):
-    o, _, _ = oracle.fwd_head(q, k, v, eps, simple, fm)
+def loss(q, k, v, do, eps, simple, fm="elu1", scale=1.0):
+    o, _, _ = oracle.fwd_head(q, k, v, eps, simple, fm, scale)
     return float(np.sum(o * do))
 
 
-def finite_difference(q, k, v, do, eps, simple, which, coords, h=1e-6, fm="elu1"):
+def finite_difference(q, k, v, do, eps, simple, which, coords, h=1e-6, fm="elu1", scale=1.0):
     arrs = {"q": q, "k": k, "v": v}
     out = []
     for (t, d) in coords:
@@ -210,8 +211,8 @@ def finite_difference(q, k, v, do, eps, simple, which, coords, h=1e-6, fm="elu1"
         minus = {n: a.copy() for n, a in arrs.items()}
         plus[which][t, d] += h
         minus[which][t, d] -= h
-        out.append((loss(plus["q"], plus["k"], plus["v"], do, eps, simple, fm)
-                    - loss(minus["q"], minus["k"], minus["v"], do, eps, simple, fm)) / (2 * h))
+        out.append((loss(plus["q"], plus["k"], plus["v"], do, eps, simple, fm, scale)
+                    - loss(minus["q"], minus["k"], minus["v"], do, eps, simple, fm, scale)) / (2 * h))
     return np.array(out)
 
 
@@ -458,7 +459,7 @@ def test_relu_bwd_matches_torch_autograd_of_quadratic_form(simple):
 
 # ---------------------------------------------------------------- causal form
 
-def causal_brute_force(q, k, v, eps, simple, fm="elu1"):
+def causal_brute_force(q, k, v, eps, simple, fm="elu1", scale=1.0):
     """Pure-Python masked quadratic form: O_t = sum_{s<=t} a_ts v_s / (sum_{s<=t} a_ts + eps)."""
     def ph(x):
         if fm == "relu":
@@ -469,7 +470,7 @@ def causal_brute_force(q, k, v, eps, simple, fm="elu1"):
     T, D, Dv = len(q), len(q[0]), len(v[0])
     out = []
     for t in range(T):
-        a = [sum(ph(q[t][i]) * ph(k[s][i]) for i in range(D)) for s in range(t + 1)]
+        a = [sum(scale * ph(q[t][i]) * ph(k[s][i]) for i in range(D)) for s in range(t + 1)]
         row = [sum(a[s] * v[s][j] for s in range(t + 1)) for j in range(Dv)]
         if not simple:
             den = sum(a) + eps
@@ -644,3 +645,76 @@ def test_causal_bwd_dv_column_sum():
     _, _, dv = oracle.causal_bwd_head(q, k, v, do, eps, False)
     a = np.tril(oracle.phi(q) @ oracle.phi(k).T).sum(axis=1)
     np.testing.assert_allclose(dv.sum(axis=0), (do * (a / (a + eps))[:, None]).sum(axis=0), rtol=1e-12)
+
+
+# ------------------------------------------------------------- optional scale
+# The scale multiplies phi(q) (flash-linear-attention's kernels scale the
+# feature-mapped query the same way); 1 is the method as stated.
+
+@pytest.mark.parametrize("scale", [0.125, 3.0])
+@pytest.mark.parametrize("simple", [False, True])
+def test_scale_matches_brute_force(simple, scale):
+    T, D, Dv = 9, 5, 4
+    q, k, v = rand((T, D), 130), rand((T, D), 131), rand((T, Dv), 132)
+    eps = 0.3
+    ref = brute_force(q.tolist(), k.tolist(), v.tolist(), eps, simple, scale=scale)
+    o, _, _ = oracle.fwd_head(q, k, v, eps, simple, scale=scale)
+    np.testing.assert_allclose(o, ref, rtol=1e-12, atol=1e-12 * np.abs(ref).max())
+    np.testing.assert_allclose(oracle.quadratic_head(q, k, v, eps, simple, scale=scale), ref, rtol=1e-12,
+                               atol=1e-12 * np.abs(ref).max())
+    cref = causal_brute_force(q.tolist(), k.tolist(), v.tolist(), eps, simple, scale=scale)
+    co, _, _ = oracle.causal_recurrent_head(q, k, v, eps, simple, scale=scale)
+    np.testing.assert_allclose(co, cref, rtol=1e-12, atol=1e-12 * np.abs(cref).max())
+
+
+def test_scale_invariants():
+    """simple_la is homogeneous of degree 1 in the scale (O and every
+    gradient); in normalised mode scale s with eps equals scale 1 with eps/s
+    (O and every gradient, eps held constant)."""
+    T, D, Dv = 30, 6, 5
+    q, k, v, do = rand((T, D), 133), rand((T, D), 134), rand((T, Dv), 135), rand((T, Dv), 136)
+    s_, eps = 0.37, 0.05
+    for fwd, bwd in ((oracle.fwd_head, oracle.bwd_head), (oracle.causal_recurrent_head, oracle.causal_bwd_head)):
+        o1 = fwd(q, k, v, eps, True)[0]
+        os_ = fwd(q, k, v, eps, True, scale=s_)[0]
+        np.testing.assert_allclose(os_, s_ * o1, rtol=1e-12)
+        for a, b in zip(bwd(q, k, v, do, eps, True, scale=s_), bwd(q, k, v, do, eps, True)):
+            np.testing.assert_allclose(a, s_ * b, rtol=1e-11, atol=1e-12 * np.abs(b).max())
+        np.testing.assert_allclose(fwd(q, k, v, eps, False, scale=s_)[0], fwd(q, k, v, eps / s_, False)[0],
+                                   rtol=1e-12)
+        for a, b in zip(bwd(q, k, v, do, eps, False, scale=s_), bwd(q, k, v, do, eps / s_, False)):
+            np.testing.assert_allclose(a, b, rtol=1e-10, atol=1e-12 * np.abs(b).max())
+
+
+@pytest.mark.parametrize("simple", [False, True])
+def test_scale_bwd_matches_finite_differences(simple):
+    T, D, Dv = 6, 3, 4
+    q = away_from_zero(rand((T, D), 137), 1e-4)
+    k = away_from_zero(rand((T, D), 138), 1e-4)
+    v, do = rand((T, Dv), 139), rand((T, Dv), 140)
+    eps, s_ = 0.5, 2.5
+    got = oracle.bwd_head(q, k, v, do, eps, simple, scale=s_)
+    coords = {"q": [(t, d) for t in range(T) for d in range(D)], "k": [(t, d) for t in range(T) for d in range(D)],
+              "v": [(t, d) for t in range(T) for d in range(Dv)]}
+    for name, g in zip(("q", "k", "v"), got):
+        fd = finite_difference(q, k, v, do, eps, simple, name, coords[name], scale=s_)
+        np.testing.assert_allclose(g.reshape(-1), fd, rtol=1e-6, atol=1e-6 * np.abs(fd).max())
+
+
+@pytest.mark.parametrize("simple", [False, True])
+def test_scale_causal_bwd_matches_torch_autograd(simple):
+    torch = pytest.importorskip("torch")
+    T, D, Dv = 24, 8, 6
+    q, k = rand((T, D), 141), rand((T, D), 142)
+    v, do = rand((T, Dv), 143), rand((T, Dv), 144)
+    eps, s_ = 0.05, 0.3
+    tq, tk, tv = (torch.tensor(a, dtype=torch.float64, requires_grad=True) for a in (q, k, v))
+    a = torch.tril(s_ * (torch.nn.functional.elu(tq) + 1) @ (torch.nn.functional.elu(tk) + 1).T)
+    o = a @ tv
+    if not simple:
+        o = o / (a.sum(dim=1, keepdim=True) + eps)
+    (o * torch.tensor(do)).sum().backward()
+    got = oracle.causal_bwd_head(q, k, v, do, eps, simple, scale=s_)
+    for g, t in zip(got, (tq, tk, tv)):
+        ref = t.grad.numpy()
+        assert np.max(np.abs(g - ref)) <= 1e-12 * np.abs(ref).max()
