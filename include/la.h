@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define LA_VERSION 4
+#define LA_VERSION 5
 
 typedef enum {
     LA_F32 = 0,
@@ -76,7 +76,8 @@ typedef enum {
     LA_ERR_WORKSPACE = 7,  /* ws_bytes below la_workspace_bytes()             */
     LA_ERR_ALIGN = 8,      /* a tensor is not 16-byte aligned, ws not 256     */
     LA_ERR_ALIAS = 9,      /* an output overlaps an input or another output   */
-    LA_ERR_DEVICE = 10     /* HIP reported an error on launch                 */
+    LA_ERR_DEVICE = 10,    /* HIP reported an error on launch                 */
+    LA_ERR_SCALE = 11      /* scale not finite                                */
 } la_status;
 
 /* Drop the denominator: simple_la (FBi-LA README, "Update" 2024-12-28). */
@@ -108,13 +109,21 @@ typedef enum {
  * M = max(D, Dv), T * M * elt < 2^31 in [B, H, T, *]; (T + 1024) * H * M * elt
  * < 2^31 in [B, T, H, *], where a head's rows are H * M elements apart at most
  * (the 1024 rows keep the offsets of the padded blocks past a slice below 2^31
- * too). elt is the element size. */
+ * too). elt is the element size.
+ * scale (optional) multiplies the query feature: phi(q) is replaced by
+ * scale * phi(q) in every formula, as flash-linear-attention's kernels scale
+ * the feature-mapped query (the pages give no scale; 0 or 1 leaves the method
+ * as stated). In normalised mode this equals eps / scale with no scale; in
+ * simple mode it multiplies O and the three gradients. Any finite value; a
+ * non-finite one gives LA_ERR_SCALE. The struct is zero-initialisable: a
+ * zero scale stands for 1. */
 typedef struct {
     int64_t B, H, T, D;
     int64_t Dv;      /* head size of V, O, dO, dV; 0 means D */
     int32_t dtype;   /* la_dtype */
     uint32_t flags;  /* LA_SIMPLE, LA_LAYOUT_BTHD, one of LA_PHI_RELU, LA_PHI_IDENTITY, LA_CAUSAL */
     float eps;
+    float scale;     /* multiplies phi(q); 0 stands for 1 (see below)     */
 } la_problem;
 
 /* Library version (LA_VERSION of the build). */

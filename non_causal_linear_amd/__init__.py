@@ -44,7 +44,7 @@ class Problem(ctypes.Structure):
     """Mirror of la_problem."""
     _fields_ = [("B", ctypes.c_int64), ("H", ctypes.c_int64), ("T", ctypes.c_int64),
                 ("D", ctypes.c_int64), ("Dv", ctypes.c_int64), ("dtype", ctypes.c_int32),
-                ("flags", ctypes.c_uint32), ("eps", ctypes.c_float)]
+                ("flags", ctypes.c_uint32), ("eps", ctypes.c_float), ("scale", ctypes.c_float)]
 
 
 class LAError(RuntimeError):
@@ -96,10 +96,12 @@ def _check(status: int) -> None:
 
 
 def make_problem(shape, dtype: torch.dtype, eps: float, simple: bool, layout: str = "bhtd",
-                 phi: str = "elu1", dv: int | None = None, causal: bool = False) -> Problem:
+                 phi: str = "elu1", dv: int | None = None, causal: bool = False,
+                 scale: float | None = None) -> Problem:
     """Problem for Q/K-side tensors of ``shape``: [B, H, T, D] (layout "bhtd")
     or [B, T, H, D] (layout "bthd"), V-side tensors with head size ``dv``
-    (None: D); feature map phi "elu1" (elu(x) + 1), "relu" or "identity"."""
+    (None: D); feature map phi "elu1" (elu(x) + 1), "relu" or "identity";
+    ``scale`` multiplies phi(q) (None: 1)."""
     if layout not in LAYOUTS:
         raise ValueError(f"layout must be one of {LAYOUTS}, got {layout!r}")
     if phi not in FEATURE_MAPS:
@@ -114,7 +116,8 @@ def make_problem(shape, dtype: torch.dtype, eps: float, simple: bool, layout: st
         B, T, H, D = (int(x) for x in shape)
     flags = ((LA_SIMPLE if simple else 0) | (LA_LAYOUT_BTHD if layout == "bthd" else 0) | FEATURE_MAPS[phi]
              | (LA_CAUSAL if causal else 0))
-    return Problem(B, H, T, D, D if dv is None else int(dv), DTYPE_CODE[dtype], flags, float(eps))
+    return Problem(B, H, T, D, D if dv is None else int(dv), DTYPE_CODE[dtype], flags, float(eps),
+                   1.0 if scale is None else float(scale))
 
 
 def _tensor(x: torch.Tensor, like: torch.Tensor | None, name: str, last: int | None = None) -> torch.Tensor:
@@ -209,13 +212,13 @@ def fwd_state(k, v, *, eps=1e-6, simple=False, layout="bhtd", phi="elu1", state=
     return state
 
 
-def fwd_output(q, state, *, eps=1e-6, simple=False, layout="bhtd", phi="elu1", out=None, dv=None):
+def fwd_output(q, state, *, eps=1e-6, simple=False, layout="bhtd", phi="elu1", out=None, dv=None, scale=None):
     """Step 4: O from Q and a complete state; dv is the head size of V and O
     (None: that of out if given, else D)."""
     _tensor(q, None, "q")
     if dv is None:
         dv = out.shape[-1] if isinstance(out, torch.Tensor) else q.shape[-1]
-    prob = make_problem(q.shape, q.dtype, eps, simple, layout, phi, dv)
+    prob = make_problem(q.shape, q.dtype, eps, simple, layout, phi, dv, scale=scale)
     _state(state, prob, q.device)
     out = _new_like(q, dv) if out is None else _tensor(out, q, "out", dv)
     _check(lib().la_fwd_output(ctypes.byref(prob), _ptr(q), _ptr(state), _ptr(out), _stream(q.device)))
@@ -223,7 +226,7 @@ def fwd_output(q, state, *, eps=1e-6, simple=False, layout="bhtd", phi="elu1", o
 
 
 def fwd(q, k, v, *, eps=1e-6, simple=False, layout="bhtd", phi="elu1", out=None, state=None, ws=None,
-        causal=False):
+        causal=False, scale=None):
     """O = phi(Q) S / (phi(Q) z + eps) (or phi(Q) S); returns (O, state).
     causal=True: token t attends to tokens s <= t (f16/bf16, D and Dv in
     {64, 128}); the state is still that of the whole sequence."""
@@ -231,7 +234,7 @@ def fwd(q, k, v, *, eps=1e-6, simple=False, layout="bhtd", phi="elu1", out=None,
     _tensor(k, q, "k")
     dv = v.shape[-1] if isinstance(v, torch.Tensor) else None
     _tensor(v, q, "v", dv)
-    prob = make_problem(q.shape, q.dtype, eps, simple, layout, phi, dv, causal)
+    prob = make_problem(q.shape, q.dtype, eps, simple, layout, phi, dv, causal, scale)
     out = _new_like(q, dv) if out is None else _tensor(out, q, "out", dv)
     state = new_state(prob, q.device) if state is None else _state(state, prob, q.device)
     ws, wsb = _ws(prob, q.device, ws)
@@ -240,12 +243,12 @@ def fwd(q, k, v, *, eps=1e-6, simple=False, layout="bhtd", phi="elu1", out=None,
     return out, state
 
 
-def bwd_dq(q, do, state, *, eps=1e-6, simple=False, layout="bhtd", phi="elu1", dq=None, ws=None):
+def bwd_dq(q, do, state, *, eps=1e-6, simple=False, layout="bhtd", phi="elu1", dq=None, ws=None, scale=None):
     """Steps 5-6: dQ; leaves dS, dz in the workspace for bwd_dkv."""
     _tensor(q, None, "q")
     dv = do.shape[-1] if isinstance(do, torch.Tensor) else None
     _tensor(do, q, "do", dv)
-    prob = make_problem(q.shape, q.dtype, eps, simple, layout, phi, dv)
+    prob = make_problem(q.shape, q.dtype, eps, simple, layout, phi, dv, scale=scale)
     _state(state, prob, q.device)
     dq = torch.empty_like(q) if dq is None else _tensor(dq, q, "dq")
     ws, wsb = _ws(prob, q.device, ws)
@@ -269,7 +272,7 @@ def bwd_dkv(k, v, *, eps=1e-6, simple=False, layout="bhtd", phi="elu1", dk=None,
 
 
 def bwd(q, k, v, do, state=None, *, eps=1e-6, simple=False, layout="bhtd", phi="elu1", dq=None, dk=None, dv=None,
-        ws=None, causal=False):
+        ws=None, causal=False, scale=None):
     """dQ, dK, dV of L = sum(O * dO), from the state fwd returned.
     causal=True: the backward of the causal form (f16/bf16, D and Dv in
     {64, 128}); no state is read (pass None)."""
@@ -278,7 +281,7 @@ def bwd(q, k, v, do, state=None, *, eps=1e-6, simple=False, layout="bhtd", phi="
     hv = v.shape[-1] if isinstance(v, torch.Tensor) else None
     _tensor(v, q, "v", hv)
     _tensor(do, q, "do", hv)
-    prob = make_problem(q.shape, q.dtype, eps, simple, layout, phi, hv, causal)
+    prob = make_problem(q.shape, q.dtype, eps, simple, layout, phi, hv, causal, scale)
     if not causal or state is not None:
         _state(state, prob, q.device)
     dq = torch.empty_like(q) if dq is None else _tensor(dq, q, "dq")
@@ -296,27 +299,35 @@ class _LinearAttention(torch.autograd.Function):
     and does not recompute S."""
 
     @staticmethod
-    def forward(ctx, q, k, v, eps, simple, layout, phi):
+    def forward(ctx, q, k, v, eps, simple, layout, phi, causal, scale):
         q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
-        o, state = fwd(q, k, v, eps=eps, simple=simple, layout=layout, phi=phi)
-        ctx.save_for_backward(q, k, v, state)
-        ctx.eps, ctx.simple, ctx.layout, ctx.phi = eps, simple, layout, phi
+        o, state = fwd(q, k, v, eps=eps, simple=simple, layout=layout, phi=phi, causal=causal, scale=scale)
+        if causal:
+            state = None  # the causal backward does not read it
+            ctx.save_for_backward(q, k, v)
+        else:
+            ctx.save_for_backward(q, k, v, state)
+        ctx.eps, ctx.simple, ctx.layout, ctx.phi, ctx.causal, ctx.scale = eps, simple, layout, phi, causal, scale
         return o
 
     @staticmethod
     def backward(ctx, do):
-        q, k, v, state = ctx.saved_tensors
+        saved = ctx.saved_tensors
+        q, k, v = saved[:3]
+        state = saved[3] if len(saved) > 3 else None
         dq, dk, dv = bwd(q, k, v, do.contiguous(), state, eps=ctx.eps, simple=ctx.simple, layout=ctx.layout,
-                         phi=ctx.phi)
-        return dq, dk, dv, None, None, None, None
+                         phi=ctx.phi, causal=ctx.causal, scale=ctx.scale)
+        return dq, dk, dv, None, None, None, None, None, None
 
 
 def linear_attention(q, k, v, *, eps: float = 1e-6, simple: bool = False, layout: str = "bhtd",
-                     phi: str = "elu1") -> torch.Tensor:
+                     phi: str = "elu1", causal: bool = False, scale: float | None = None) -> torch.Tensor:
     """O = phi(Q) S / (phi(Q) z + eps) (or phi(Q) S with simple=True), with
     gradients for q, k and v through the library's backward. Tensors are
     [B, H, T, D] (layout "bhtd") or [B, T, H, D] (layout "bthd") on a GPU in
     float32, float16 or bfloat16, with D (of q, k) and Dv (of v) each in
     {32, 64, 96, 128}; phi is "elu1" (elu + 1),
-    "relu" or "identity"."""
-    return _LinearAttention.apply(q, k, v, float(eps), bool(simple), layout, phi)
+    "relu" or "identity". causal=True: token t attends to tokens s <= t
+    (f16/bf16, D and Dv in {64, 128}). scale multiplies phi(q) (None: 1)."""
+    return _LinearAttention.apply(q, k, v, float(eps), bool(simple), layout, phi, bool(causal),
+                                  None if scale is None else float(scale))

@@ -67,6 +67,7 @@ la_status check_problem(const la_problem* p) {
         return LA_ERR_SHAPE;
     }
     if (!(p->eps >= 0.f) || !isfinite(p->eps)) return LA_ERR_EPS;
+    if (!isfinite(p->scale)) return LA_ERR_SCALE;
     return LA_OK;
 }
 
@@ -102,7 +103,11 @@ la::Plan make_plan(const la_problem* p) {
     pl.DV = static_cast<int>(dv_of(p));
     pl.dtype = p->dtype;
     pl.simple = (p->flags & LA_SIMPLE) != 0;
-    pl.eps = p->eps;
+    // The query scale s folds into one number the kernels already take:
+    // normalised, s phi(q) S / (s phi(q) . z + eps) = phi(q) S / (phi(q) . z + eps / s);
+    // simple_la, the output (and every gradient) is s times the unscaled one.
+    const float qscale = p->scale == 0.f ? 1.f : p->scale;
+    pl.eps = pl.simple ? qscale : p->eps / qscale;
     pl.fm = (p->flags & LA_PHI_RELU) ? 1 : (p->flags & LA_PHI_IDENTITY) ? 2 : 0;
     pl.lay.H = p->H > 0 ? p->H : 1;
     if (p->flags & LA_LAYOUT_BTHD) {
@@ -194,6 +199,7 @@ const char* la_status_str(int s) {
         case LA_ERR_HEAD_DIM: return "LA_ERR_HEAD_DIM: D and Dv must be 32, 64, 96 or 128";
         case LA_ERR_FLAGS: return "LA_ERR_FLAGS: unknown flag bit or two feature maps";
         case LA_ERR_EPS: return "LA_ERR_EPS: eps must be finite and >= 0";
+        case LA_ERR_SCALE: return "LA_ERR_SCALE: scale must be finite";
         case LA_ERR_WORKSPACE: return "LA_ERR_WORKSPACE: workspace smaller than la_workspace_bytes()";
         case LA_ERR_ALIGN: return "LA_ERR_ALIGN: tensors need 16-byte, workspace 256-byte alignment";
         case LA_ERR_ALIAS: return "LA_ERR_ALIAS: an output overlaps another buffer";

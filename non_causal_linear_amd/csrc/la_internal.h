@@ -25,6 +25,8 @@ struct Plan {
     int64_t BH = 0, T = 0;
     int DK = 0, DV = 0, dtype = 0;
     bool simple = false;
+    // normalised: eps / scale; simple_la: the query scale (1 without one).
+    // Either way the kernels' one float folds the optional query scale.
     float eps = 0.f;
     int fm = 0;  // feature map: 0 elu + 1, 1 relu, 2 identity
     Layout lay;

@@ -1236,10 +1236,11 @@ __global__ __launch_bounds__((StreamShape<T, DK, DV>::kThreads), (StreamShape<T,
         for (int u = 0; u < U; ++u) {
             Row<T, FV> out;
             if constexpr (SIMPLE) {
+                const float f = uS * eps;  // simple_la: eps carries the query scale
 #pragma unroll
                 for (int b = 0; b < NB; ++b)
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) out.e[4 * b + r] = static_cast<T>(acc[u][b][r] * uS);
+                    for (int r = 0; r < 4; ++r) out.e[4 * b + r] = static_cast<T>(acc[u][b][r] * f);
             } else {
                 // one division per token: O = num 2^-sS / (den 2^-sz + eps)
                 const float inv = uS / (accd[u][0] * uz + eps);
@@ -1383,7 +1384,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(
 #pragma unroll
                 for (int b = 0; b < NBK; ++b)
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) dqt[4 * b + r] = au[b][r] * uS;
+                    for (int r = 0; r < 4; ++r) dqt[4 * b + r] = au[b][r] * (uS * eps);  // eps: the query scale
 #pragma unroll
                 for (int o = 0; o < FV; ++o) wv[o] = to_f32(dr.e[o]);
             } else {
@@ -1454,7 +1455,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(
         oS = part + (bh * PB + p) * (int64_t)(DK * DV + DK);
         oz = oS + DK * DV;
     }
-    const float uw = ldexpf(1.f, -sw);
+    const float uw = ldexpf(1.f, -sw) * (SIMPLE ? eps : 1.f);  // simple_la: times the query scale
 #pragma unroll
     for (int ii = 0; ii < NI; ++ii) {
         const int i0 = (wi * NI + ii) * 16 + 4 * grp;
@@ -1638,7 +1639,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_w64_kernel(
 #pragma unroll
             for (int b = 0; b < NB; ++b)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) dqt[4 * b + r] = au[b][r] * uS;
+                for (int r = 0; r < 4; ++r) dqt[4 * b + r] = au[b][r] * (uS * eps);  // eps: the query scale
         } else {
             f32x4 ad = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -1696,7 +1697,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_w64_kernel(
     // the last block holds dz
     __syncthreads();
     float* red = reinterpret_cast<float*>(smem);
-    const float uw = ldexpf(1.f, -sw);
+    const float uw = ldexpf(1.f, -sw) * (SIMPLE ? eps : 1.f);  // simple_la: times the query scale
     if (wave >= 2) {
         float* dst = red + (wave - 2) * E;
 #pragma unroll
@@ -1914,7 +1915,7 @@ __global__ __launch_bounds__((BwdQTile<DK, DV>::kThreads), (BwdQTile<DK, DV>::kM
         issue(st, round + Sh::kStages);
         sched_fence();
         float aq = 1.f;  // factor on phi(q) in the reduction operand
-        float ku = uS, cc = 0.f;
+        float ku = SIMPLE ? uS * eps : uS, cc = 0.f;  // simple_la: eps carries the query scale
         if constexpr (!SIMPLE) {
             float rr = 0.f;
 #pragma unroll
@@ -1975,7 +1976,7 @@ __global__ __launch_bounds__((BwdQTile<DK, DV>::kThreads), (BwdQTile<DK, DV>::kM
 
     // wave w holds rows [16 w, 16 w + 16) of 2^sw dS; column 0 of the last
     // block holds 2^sw dz
-    const float uw = ldexpf(1.f, -sw);
+    const float uw = ldexpf(1.f, -sw) * (SIMPLE ? eps : 1.f);  // simple_la: times the query scale
     float* oS;
     float* oz;
     if (PB == 1) {
@@ -2481,7 +2482,7 @@ __global__ __launch_bounds__(kThreads, (CausalShape<DK, DV>::kMinBlocks)) void f
             f32x4 ia, ir;  // per row: factors on the a part and (times 2^-sR) on the R part
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                float inv = 1.f;
+                float inv = eps;  // simple_la: eps carries the query scale
                 if constexpr (!SIMPLE) inv = 1.f / (dA[r] * uA + dR[r] * ldexpf(1.f, -sExp[cur][kWaves]) + eps);
                 ia[r] = uA * inv;
                 ir[r] = inv;
@@ -2893,7 +2894,7 @@ __global__ __launch_bounds__(kThreads, (CausalBwdShape<DK, DV>::kMinBlocks)) voi
         if constexpr (SIMPLE) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                wr[r] = row0 + tq + r < len ? 1.f : 0.f;
+                wr[r] = row0 + tq + r < len ? eps : 0.f;  // simple_la: eps carries the query scale
                 cr[r] = 0.f;
             }
         } else {
@@ -2983,7 +2984,8 @@ __global__ __launch_bounds__(kThreads, (CausalBwdShape<DK, DV>::kMinBlocks)) voi
                 const float zi = SIMPLE ? 0.f : sZ[16 * ib + m];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const float d = SIMPLE ? Y[ib][r] + pk[ib][r] * uP : wr[r] * Y[ib][r] + cr[r] * zi + pk[ib][r] * uP;
+                    const float d = SIMPLE ? wr[r] * (Y[ib][r] + pk[ib][r] * uP)
+                                           : wr[r] * Y[ib][r] + cr[r] * zi + pk[ib][r] * uP;
                     g[ib][r] = d * dphi_of<FM>(ph[ib][r]);
                 }
             }
@@ -3156,7 +3158,7 @@ template <typename T, int DK, int DV, bool SIMPLE, int FM>
 __global__ __launch_bounds__(kThreads, (CausalBwdShape<DK, DV>::kMinBlocks)) void bwd_causal_kv_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const T* __restrict__ dout,
     const float* __restrict__ wc, const int* __restrict__ es, const float* __restrict__ suf, T* __restrict__ dk,
-    T* __restrict__ dv, int64_t T_, const Layout lay, int P, int64_t L, int nche) {
+    T* __restrict__ dv, int64_t T_, const Layout lay, int P, int64_t L, int nche, float qscale) {
     using Sh = CausalBwdShape<DK, DV>;
     constexpr int C = Sh::kChunk, LDK = Sh::kLDK, LDV = Sh::kLDV, LDRT = Sh::kLDRT, LDW = Sh::kLDW;
     constexpr int NBI = DK / 16, NBV = DV / 16, NBC = C / 16;
@@ -3289,7 +3291,7 @@ __global__ __launch_bounds__(kThreads, (CausalBwdShape<DK, DV>::kMinBlocks)) voi
         for (int i = 0; i < NCK; ++i) {
             const int nn = tid + kThreads * i, r = nn / CK, cc = nn % CK;
             const bool ok = row0 + r < len;
-            float wt = 1.f;
+            float wt = qscale;  // simple_la: w is the query scale
             if constexpr (!SIMPLE) wt = __shfl(wl, r);
             const float f = ok ? wt * fQ : 0.f;
             Row<T, 8> qin, kin, qt, kt;
@@ -3685,9 +3687,11 @@ hipError_t bwd_causal_fm(const Plan& p, const void* q, const void* k, const void
             if (e != hipSuccess) return e;
         }
         return p.simple ? launch(bwd_causal_kv_kernel<T, DK, DV, true, FM>, nblk, kThreads, s, qq, kk, vv, dd, wcp,
-                                 esp, gp, static_cast<T*>(dk), static_cast<T*>(dv), p.T, p.lay, p.P, p.L, p.nche)
+                                 esp, gp, static_cast<T*>(dk), static_cast<T*>(dv), p.T, p.lay, p.P, p.L, p.nche,
+                                 p.eps)
                         : launch(bwd_causal_kv_kernel<T, DK, DV, false, FM>, nblk, kThreads, s, qq, kk, vv, dd, wcp,
-                                 esp, gp, static_cast<T*>(dk), static_cast<T*>(dv), p.T, p.lay, p.P, p.L, p.nche);
+                                 esp, gp, static_cast<T*>(dk), static_cast<T*>(dv), p.T, p.lay, p.P, p.L, p.nche,
+                                 1.f);
     }
 }
 

@@ -17,7 +17,7 @@ from non_causal_linear_amd import Problem
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "la.h")
 
-OK, NULL, SHAPE, DTYPE, HEAD_DIM, FLAGS, EPS, WORKSPACE, ALIGN, ALIAS, DEVICE = range(11)
+OK, NULL, SHAPE, DTYPE, HEAD_DIM, FLAGS, EPS, WORKSPACE, ALIGN, ALIAS, DEVICE, SCALE = range(12)
 
 
 @pytest.fixture(scope="module")
@@ -48,22 +48,22 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.la_version() == 4
-    for s in range(11):
+    assert L.la_version() == 5
+    for s in range(12):
         txt = L.la_status_str(s).decode()
         assert txt.startswith("LA_"), txt
     assert L.la_status_str(99).decode() == "unknown la_status"
     assert "HEAD_DIM" in L.la_status_str(HEAD_DIM).decode()
 
 
-def prob(B=2, H=3, T=100, D=64, dtype=1, flags=0, eps=1e-6, Dv=0):
-    return Problem(B, H, T, D, Dv, dtype, flags, eps)
+def prob(B=2, H=3, T=100, D=64, dtype=1, flags=0, eps=1e-6, Dv=0, scale=0.0):
+    return Problem(B, H, T, D, Dv, dtype, flags, eps, scale)
 
 
 def test_problem_struct_matches_header():
-    # int64 B, H, T, D, Dv; int32 dtype; uint32 flags; float eps; padded to 8
+    # int64 B, H, T, D, Dv; int32 dtype; uint32 flags; float eps, scale
     assert ctypes.sizeof(Problem) == 56
-    assert [f[0] for f in Problem._fields_] == ["B", "H", "T", "D", "Dv", "dtype", "flags", "eps"]
+    assert [f[0] for f in Problem._fields_] == ["B", "H", "T", "D", "Dv", "dtype", "flags", "eps", "scale"]
 
 
 def test_state_bytes_formula(L):
@@ -142,6 +142,9 @@ def test_fwd_rejects_bad_problems(L):
     assert fwd_call(L, prob(eps=-1e-3)) == EPS
     assert fwd_call(L, prob(eps=float("nan"))) == EPS
     assert fwd_call(L, prob(eps=float("inf"))) == EPS
+    assert fwd_call(L, prob(scale=float("nan"))) == SCALE
+    assert fwd_call(L, prob(scale=float("-inf"))) == SCALE
+    assert "SCALE" in L.la_status_str(SCALE).decode()
 
 
 def test_fwd_rejects_bad_buffers(L):
