@@ -20,33 +20,36 @@ def gpu():
     la.lib()
 
 
-def eager(dev, w):
-    o, st = la.fwd(dev["q"], dev["k"], dev["v"], eps=w.eps, simple=w.simple)
-    dq, dk, dv = la.bwd(dev["q"], dev["k"], dev["v"], dev["do"], st, eps=w.eps, simple=w.simple)
+def eager(dev, w, causal=False):
+    o, st = la.fwd(dev["q"], dev["k"], dev["v"], eps=w.eps, simple=w.simple, causal=causal)
+    dq, dk, dv = la.bwd(dev["q"], dev["k"], dev["v"], dev["do"], None if causal else st, eps=w.eps,
+                        simple=w.simple, causal=causal)
     torch.cuda.synchronize()
     return {"o": o, "state": st, "dq": dq, "dk": dk, "dv": dv}
 
 
-@pytest.mark.parametrize("D,Dv,dtype,simple", [(64, 64, "f16", False), (128, 128, "bf16", False),
-                                                (96, 32, "f16", True)],
-                         ids=["D64-f16", "D128-bf16", "D96-Dv32-f16-simple"])
-def test_graph_replays_match_eager(D, Dv, dtype, simple):
+@pytest.mark.parametrize("D,Dv,dtype,simple,causal", [(64, 64, "f16", False, False), (128, 128, "bf16", False, False),
+                                                       (96, 32, "f16", True, False), (64, 64, "f16", False, True),
+                                                       (128, 64, "bf16", True, True)],
+                         ids=["D64-f16", "D128-bf16", "D96-Dv32-f16-simple", "causal-D64-f16",
+                              "causal-D128-Dv64-bf16-simple"])
+def test_graph_replays_match_eager(D, Dv, dtype, simple, causal):
     w = Workload("graph", 2, 4, 3000, D, dtype, simple=simple, seed=70_000 + D + Dv, Dv=Dv)
-    print(f"case graph D={D} Dv={Dv} {dtype} simple={simple} seed={w.seed}", flush=True)
+    print(f"case graph D={D} Dv={Dv} {dtype} simple={simple} causal={causal} seed={w.seed}", flush=True)
     x = make_inputs(w)
     dev = {n: to_device(a, w.dtype) for n, a in x.items()}
-    ref = eager(dev, w)
+    ref = eager(dev, w, causal)
 
     q, k, v, do = dev["q"], dev["k"], dev["v"], dev["do"]
-    prob = la.make_problem(q.shape, q.dtype, w.eps, simple, dv=Dv)
+    prob = la.make_problem(q.shape, q.dtype, w.eps, simple, dv=Dv, causal=causal)
     out = {"o": torch.empty_like(v), "state": la.new_state(prob, q.device), "dq": torch.empty_like(q),
            "dk": torch.empty_like(k), "dv": torch.empty_like(v)}
     ws = torch.empty(la.workspace_bytes(prob), dtype=torch.uint8, device=q.device)
 
     def calls():
-        la.fwd(q, k, v, eps=w.eps, simple=simple, out=out["o"], state=out["state"], ws=ws)
-        la.bwd(q, k, v, do, out["state"], eps=w.eps, simple=simple, dq=out["dq"], dk=out["dk"], dv=out["dv"],
-               ws=ws)
+        la.fwd(q, k, v, eps=w.eps, simple=simple, out=out["o"], state=out["state"], ws=ws, causal=causal)
+        la.bwd(q, k, v, do, None if causal else out["state"], eps=w.eps, simple=simple, dq=out["dq"], dk=out["dk"],
+               dv=out["dv"], ws=ws, causal=causal)
 
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
@@ -60,7 +63,7 @@ def test_graph_replays_match_eager(D, Dv, dtype, simple):
     torch.cuda.synchronize()
 
     for i in range(4):
-        for t in out.values():
+        for t in list(out.values()) + [ws]:
             t.view(torch.uint8).fill_(0xFF)  # eager overwrite between replays (NaN patterns)
         torch.cuda.synchronize()
         g.replay()
@@ -72,7 +75,7 @@ def test_graph_replays_match_eager(D, Dv, dtype, simple):
     x2 = make_inputs(Workload("graph2", 2, 4, 3000, D, dtype, simple=simple, seed=w.seed + 1, Dv=Dv))
     for n, a in x2.items():
         dev[n].copy_(to_device(a, w.dtype))
-    ref2 = eager(dev, w)
+    ref2 = eager(dev, w, causal)
     g.replay()
     torch.cuda.synchronize()
     for nm in ref2:
