@@ -167,7 +167,7 @@ def test_fwd_rejects_bad_buffers(L):
 
 def test_buffer_checks_use_each_tensors_head_size(L):
     """With D != Dv, q/k/dq/dk span T*D and v/o/dout/dv span T*Dv elements per
-    head: overlaps are judged on those spans. Every call below is rejected."""
+    head: overlaps are checked on those spans. Every call below is rejected."""
     p = prob(D=32, Dv=128)
     tk, tv = 2 * 3 * 100 * 32 * 2, 2 * 3 * 100 * 128 * 2
     need = L.la_workspace_bytes(ctypes.byref(p))
