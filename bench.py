@@ -109,6 +109,70 @@ def cpu_baseline(w, x, max_heads: int) -> dict:
     }
 
 
+def copy_bandwidth(reps: int = 10) -> float:
+    """GB/s of a plain 1 GiB device-to-device copy (read + write bytes over the
+    mean time): what a streaming kernel can reach on this machine. Context, not
+    the target."""
+    src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a, b in ev:
+        a.record()
+        dst.copy_(src)
+        b.record()
+    torch.cuda.synchronize()
+    ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    del src, dst
+    return 2 * (1 << 30) / (ms * 1e-3) / 1e9
+
+
+def torch_eager(w, q, k, v, do, do_flush, reps: int = 3) -> dict:
+    """The same formula in plain torch ops, fp32, forward and forward + backward
+    (autograd), on the same inputs and with the same flush: the eager
+    baseline a torch user would write. Context only."""
+    def forward(q32, k32, v32):
+        qt = torch.nn.functional.elu(q32) + 1
+        kt = torch.nn.functional.elu(k32) + 1
+        s_ = torch.matmul(kt.transpose(-1, -2).contiguous(), v32)
+        num = torch.matmul(qt, s_)
+        if w.simple:
+            return num
+        z = kt.sum(dim=-2, keepdim=True)
+        return num / ((qt * z).sum(dim=-1, keepdim=True) + w.eps)
+
+    def once(bwd):
+        q32, k32, v32 = (x.float().requires_grad_(bwd) for x in (q, k, v))
+        o = forward(q32, k32, v32)
+        if bwd:
+            o.backward(do.float())
+        return o
+
+    with torch.no_grad():
+        once(False)
+    once(True)
+    torch.cuda.synchronize()
+    out = {}
+    for key, bwd in (("fwd_ms", False), ("fwd_bwd_ms", True)):
+        ts = []
+        for _ in range(reps):
+            do_flush("read")
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            if bwd:
+                once(True)
+            else:
+                with torch.no_grad():
+                    once(False)
+            b.record()
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b))
+        out[key] = round(float(np.mean(ts)), 3)
+    torch.cuda.empty_cache()
+    return out
+
+
 def causal_bench(args, w, t, do_flush) -> int:
     """The causal path: one la_fwd call (segment states, their prefixes, the
     chunked scan), then one la_bwd call (segment states and prefixes again,
@@ -193,6 +257,8 @@ def main() -> int:
                     help="also time the step after a writing flush and with no flush")
     ap.add_argument("--causal", action="store_true",
                     help="time the causal forward and backward (LA_CAUSAL) instead of the bidirectional path")
+    ap.add_argument("--no-context", action="store_true",
+                    help="skip the context measurements (device copy bandwidth, torch eager baseline)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 1 GiB device copy (for counter scaling)")
     args = ap.parse_args()
@@ -358,6 +424,11 @@ def main() -> int:
     if w.name == HEADLINE:
         line["context_pages_a800_triton"] = {"fwd_ms": PAGE_A800_FWD_MS, "bwd_ms": PAGE_A800_BWD_MS,
                                              "note": "another GPU, dtype unstated: context only"}
+    if not args.no_context:
+        print("[bench] context: device copy, torch eager", file=sys.stderr, flush=True)
+        line["context_copy_1GiB_GBps"] = round(copy_bandwidth(), 1)
+        if w.bwd:
+            line["context_torch_eager_fp32"] = torch_eager(w, q, k, v, do, do_flush)
     if not args.no_cpu_baseline:
         print("[bench] oracle on host cores", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(w, x, args.cpu_heads)
