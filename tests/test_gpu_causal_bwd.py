@@ -150,3 +150,39 @@ def test_causal_bwd_rejects_unsupported():
     y = torch.zeros(1, 2, 8, 96, dtype=torch.float16, device="cuda")
     with pytest.raises(la.LAError):
         la.bwd(y, y, y, y, causal=True)  # D = 96
+
+
+def test_causal_long_sequence_few_heads():
+    """B2 H8 T262144 D64 bf16 simple_la (16 heads, 64 segments each): the
+    forward and backward of one whole head against the oracle, sampled output
+    rows of every head, and bit-identical reruns."""
+    w = Workload("causal-c5", 2, 8, 262144, 64, "bf16", simple=True, seed=99_000)
+    print(f"case causal B2 H8 T262144 bf16 simple seed={w.seed}", flush=True)
+    x = make_inputs(w, with_grad=True)
+    dev = {n: to_device(a, "bf16") for n, a in x.items()}
+    o, _ = la.fwd(dev["q"], dev["k"], dev["v"], simple=True, causal=True)
+    g = la.bwd(dev["q"], dev["k"], dev["v"], dev["do"], None, simple=True, causal=True)
+    torch.cuda.synchronize()
+    n = w.B * w.H
+    hx = head_slices(x, n, w.T)
+    h = 11
+    args = [hx[nm][h][None, None] for nm in ("q", "k", "v", "do")]
+    o_ref, _, _ = oracle.causal_fwd(*args[:3], "bf16", w.eps, True)
+    check("O", decode(o.reshape(n, w.T, -1)[h], "bf16"), o_ref[0, 0], "bf16", f" head {h}")
+    for name, gg, r in zip(("dQ", "dK", "dV"), g, oracle.causal_bwd(*args, "bf16", w.eps, True)):
+        check(name, decode(gg.reshape(n, w.T, -1)[h], "bf16"), r[0, 0], "bf16", f" head {h}")
+    rng = np.random.default_rng(w.seed)
+    hd = {nm: oracle.decode(a, "bf16").reshape(n, w.T, -1) for nm, a in x.items() if nm != "do"}
+    worst = 0.0
+    for hh in range(n):
+        rows = sorted({0, w.T - 1} | {int(t) for t in rng.integers(0, w.T, size=6)})
+        ref = oracle.causal_sampled_rows_head(hd["q"][hh], hd["k"][hh], hd["v"][hh], rows, w.eps, True)
+        worst = max(worst, max_rel_err(decode(o.reshape(n, w.T, -1)[hh][rows], "bf16"), ref))
+    print(f"  O sampled rows, all heads: {worst:.3e}", flush=True)
+    assert worst <= TOL["bf16"]
+    o2, _ = la.fwd(dev["q"], dev["k"], dev["v"], simple=True, causal=True)
+    g2 = la.bwd(dev["q"], dev["k"], dev["v"], dev["do"], None, simple=True, causal=True)
+    torch.cuda.synchronize()
+    assert bytes_equal(o, o2)
+    for a, b in zip(g, g2):
+        assert bytes_equal(a, b)
