@@ -2226,6 +2226,16 @@ __global__ __launch_bounds__((StreamShape<T, DK, DV>::kThreads), (StreamShape<T,
 // reads give the operands back. Two barriers per chunk; two chunks of loads
 // in flight. Rows past the segment end load as zeros (K is zeroed after phi)
 // and their stores are dropped.
+// Four consecutive 16-bit values as one 8-byte LDS store.
+template <typename T>
+__device__ __forceinline__ void put4t(T* dst, f32x4 x, float f) {
+    typedef T t4 __attribute__((ext_vector_type(4)));
+    t4 y;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) y[r] = static_cast<T>(x[r] * f);
+    *reinterpret_cast<t4*>(dst) = y;
+}
+
 template <int DK, int DV>
 struct CausalShape {
     static constexpr int kChunk = 64;                 // tokens per chunk
@@ -2303,14 +2313,6 @@ __global__ __launch_bounds__(kThreads, (CausalShape<DK, DV>::kMinBlocks)) void f
 #pragma unroll
     for (int e = 0; e < 8; ++e) ones[e] = static_cast<T>(1.f);
 
-    // Four consecutive 16-bit values as one 8-byte LDS store.
-    auto put4 = [](T* dst, f32x4 x, float f) {
-        typedef T t4 __attribute__((ext_vector_type(4)));
-        t4 y;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) y[r] = static_cast<T>(x[r] * f);
-        *reinterpret_cast<t4*>(dst) = y;
-    };
     // this wave's quarter of R (as R^T) and z (wave 0) as 16-bit into copy `buf`
     auto publish = [&](int buf) {
         int sR = 0;
@@ -2329,7 +2331,7 @@ __global__ __launch_bounds__(kThreads, (CausalShape<DK, DV>::kMinBlocks)) void f
         for (int iR = 0; iR < RI; ++iR)
 #pragma unroll
             for (int jR = 0; jR < RJ; ++jR)
-                put4(&tRT[buf][(16 * (wave * RJ + jR) + m) * LDRT + 16 * iR + 4 * grp], accR[iR][jR], fR);
+                put4t(&tRT[buf][(16 * (wave * RJ + jR) + m) * LDRT + 16 * iR + 4 * grp], accR[iR][jR], fR);
         if (lane == 0) sExp[buf][wave] = sR;
         if constexpr (!SIMPLE) {
             if (wave == 0) {
@@ -2345,7 +2347,7 @@ __global__ __launch_bounds__(kThreads, (CausalShape<DK, DV>::kMinBlocks)) void f
                 const float fZ = ldexpf(1.f, sZ);
                 if (m == 0)
 #pragma unroll
-                    for (int iR = 0; iR < RI; ++iR) put4(&tZ[buf][16 * iR + 4 * grp], accZ[iR], fZ);
+                    for (int iR = 0; iR < RI; ++iR) put4t(&tZ[buf][16 * iR + 4 * grp], accZ[iR], fZ);
                 if (lane == 0) sExp[buf][kWaves] = sZ;
             }
         }
@@ -2441,7 +2443,7 @@ __global__ __launch_bounds__(kThreads, (CausalShape<DK, DV>::kMinBlocks)) void f
             const float fA = ldexpf(1.f, sA);
             // a^T: row s, columns t = 4 grp .. 4 grp + 3 of this wave
 #pragma unroll
-            for (int jb = 0; jb < C / 16; ++jb) put4(&myW[(16 * jb + m) * LDW + 4 * grp], aa[jb], fA);
+            for (int jb = 0; jb < C / 16; ++jb) put4t(&myW[(16 * jb + m) * LDW + 4 * grp], aa[jb], fA);
         }
         wave_lds_sync();
 
@@ -2495,7 +2497,7 @@ __global__ __launch_bounds__(kThreads, (CausalShape<DK, DV>::kMinBlocks)) void f
 #pragma unroll
                 for (int r = 0; r < 4; ++r) y[r] = nA[jb][r] * ia[r] + nR[jb][r] * (uR * ir[r]);
                 // O^T: row j, columns t = 4 grp .. 4 grp + 3 of this wave
-                put4(&myW[(16 * jb + m) * LDW + 4 * grp], y, 1.f);
+                put4t(&myW[(16 * jb + m) * LDW + 4 * grp], y, 1.f);
             }
         }
         wave_lds_sync();
@@ -2646,15 +2648,6 @@ __device__ __forceinline__ Frag<T> scale_frag(Frag<T> x, float f) {
     return y;
 }
 
-// Four consecutive 16-bit values as one 8-byte LDS store.
-template <typename T>
-__device__ __forceinline__ void put4t(T* dst, f32x4 x, float f) {
-    typedef T t4 __attribute__((ext_vector_type(4)));
-    t4 y;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) y[r] = static_cast<T>(x[r] * f);
-    *reinterpret_cast<t4*>(dst) = y;
-}
 
 // Forward-order scan of one segment: dQ, w and c^ per token, the chunk's Qw
 // exponent, and (P > 1) the segment's sums of Qw dO^T and c phi(q). The four
