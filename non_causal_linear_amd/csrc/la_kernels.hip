@@ -2485,7 +2485,7 @@ __global__ __launch_bounds__(kThreads, (CausalShape<DK, DV>::kMinBlocks)) void f
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 float inv = eps;  // simple_la: eps carries the query scale
-                if constexpr (!SIMPLE) inv = 1.f / (dA[r] * uA + dR[r] * ldexpf(1.f, -sExp[cur][kWaves]) + eps);
+                if constexpr (!SIMPLE) inv = __builtin_amdgcn_rcpf(dA[r] * uA + dR[r] * ldexpf(1.f, -sExp[cur][kWaves]) + eps);
                 ia[r] = uA * inv;
                 ir[r] = inv;
             }
@@ -2918,7 +2918,7 @@ __global__ __launch_bounds__(kThreads, (CausalBwdShape<DK, DV>::kMinBlocks)) voi
                 const float den = row16_sum(sa[r]) + eps;
                 const float ru = row16_sum(sb[r]);
                 const bool ok = row0 + tq + r < len;
-                const float inv = 1.f / den;
+                const float inv = __builtin_amdgcn_rcpf(den);  // v_rcp_f32, 1 ulp
                 wr[r] = ok ? inv : 0.f;
                 cr[r] = ok ? -ru * inv * inv : 0.f;
                 if (m == r) {
@@ -2935,14 +2935,17 @@ __global__ __launch_bounds__(kThreads, (CausalBwdShape<DK, DV>::kMinBlocks)) voi
         f32x4 pp[NBC];
         float pmx = 0.f;
 #pragma unroll
-        for (int jb = 0; jb < NBC; ++jb)
+        for (int jb = 0; jb < NBC; ++jb) {
+            pp[jb] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (jb <= wave) {  // blocks above the diagonal stay zero
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const bool keep = jb < wave || (jb == wave && m <= 4 * grp + r);
-                const float x = SIMPLE ? bb[jb][r] : wr[r] * bb[jb][r] + cr[r];
-                pp[jb][r] = keep ? x : 0.f;
-                pmx = fmaxf(pmx, fabsf(pp[jb][r]));
+                for (int r = 0; r < 4; ++r) {
+                    const float x = SIMPLE ? bb[jb][r] : wr[r] * bb[jb][r] + cr[r];
+                    pp[jb][r] = jb < wave || m <= 4 * grp + r ? x : 0.f;
+                    pmx = fmaxf(pmx, fabsf(pp[jb][r]));
+                }
             }
+        }
         int sP = 0;
         if constexpr (Elt<T>::kScaled) sP = scale_exp(wave_max_nonneg(pmx));
         {
@@ -3357,10 +3360,11 @@ __global__ __launch_bounds__(kThreads, (CausalBwdShape<DK, DV>::kMinBlocks)) voi
         float pmx = 0.f, amx = 0.f;
 #pragma unroll
         for (int jb = 0; jb < NBC; ++jb) {
+            if (jb < wave) continue;  // below the diagonal: a~ and b were never computed, stay zero
             const float ch = SIMPLE ? 0.f : sC[16 * jb + m];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const bool keep = jb > wave || (jb == wave && m >= 4 * grp + r);
+                const bool keep = jb > wave || m >= 4 * grp + r;
                 aa[jb][r] = keep ? aa[jb][r] : 0.f;
                 bb[jb][r] = keep ? bb[jb][r] + ch : 0.f;  // now mask(b + c^)
                 pmx = fmaxf(pmx, fabsf(bb[jb][r]));
