@@ -259,13 +259,25 @@ __device__ __forceinline__ int buf_off(int64_t row, int64_t rs, int col) {
     return (int)((uint32_t)row * (uint32_t)(rs * (int)sizeof(T)) + (uint32_t)(col * (int)sizeof(T)));
 }
 
+// Cache policy of a buffer access (the instruction's cache-policy bits; hints
+// only, results are the same). The 16-bit state reductions load K and V
+// non-temporally: 104 -> 93 us at B8-H16-T16384-D64 f16 (207 -> 182 us at
+// D128 bf16), with the rest of the step unchanged. Elsewhere it did not pay:
+// on the output or K/V-side kernels' accesses it cost 5-25%, and on the dQ
+// stores it only moved time from the K/V kernel to the dQ kernel (the
+// write-back of lines left in the 256 MB infinity cache falls on whichever
+// kernel runs next).
+enum CachePolicy { kCacheDefault = 0, kNonTemporal = 2 };
+
+template <int CP = kCacheDefault>
 __device__ __forceinline__ uint4 buf_load16(const HeadBuf& b, int byte_off) {
-    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(b.rsrc, byte_off, 0, 0);
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(b.rsrc, byte_off, 0, CP);
     return make_uint4(v.x, v.y, v.z, v.w);
 }
+template <int CP = kCacheDefault>
 __device__ __forceinline__ void buf_store16(const HeadBuf& b, int byte_off, uint4 x) {
     const u32x4 v = {x.x, x.y, x.z, x.w};
-    __builtin_amdgcn_raw_buffer_store_b128(v, b.rsrc, byte_off, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b128(v, b.rsrc, byte_off, 0, CP);
 }
 
 // N contiguous elements of row `row` (rows rs elements apart) starting at
@@ -283,7 +295,7 @@ __device__ __forceinline__ void load_row_buf(Row<T, N>& r, const HeadBuf& b, int
 // n + 16 g, as full contiguous rows: the lanes first write their quarter rows
 // to this wave's LDS staging area (row stride D + 16 bytes), then each lane
 // reads 16 bytes back so that one store instruction covers whole 128-byte lines.
-template <typename T, int D>
+template <typename T, int D, int CP = kCacheDefault>
 __device__ __forceinline__ void store_tile_rows(T* stage, const Row<T, D / 4>& vals, const HeadBuf& b,
                                                 int64_t row0, int64_t rs) {
     constexpr int F = D / 4, EPC = 16 / (int)sizeof(T), LDR = D + EPC;
@@ -299,7 +311,7 @@ __device__ __forceinline__ void store_tile_rows(T* stage, const Row<T, D / 4>& v
     for (int k = 0; k < NC; ++k) {
         const int n = 64 * k + lane, r = n / CPR, c = n % CPR;
         const uint4 x = *reinterpret_cast<const uint4*>(&stage[r * LDR + EPC * c]);
-        buf_store16(b, buf_off<T>(row0 + r, rs, EPC * c), x);
+        buf_store16<CP>(b, buf_off<T>(row0 + r, rs, EPC * c), x);
     }
     wave_lds_sync();
 }
@@ -748,8 +760,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_state_w64_kernel(
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int off = buf_off<T>((int64_t)ps * STEP + rg + 8 * r, lay.rs, 8 * c);
-            st.k[r] = buf_load16(bk, off);
-            st.v[r] = buf_load16(bv, off);
+            st.k[r] = buf_load16<kNonTemporal>(bk, off);
+            st.v[r] = buf_load16<kNonTemporal>(bv, off);
         }
     };
     // phi on K (fp32, rounded to T), padded rows zeroed after phi, row-major to LDS
@@ -934,12 +946,14 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_state_tile_kernel(
 #pragma unroll
         for (int i = 0; i < NCK; ++i) {
             const int n = tid + kThreads * i, r = n / CK, c = n % CK;
-            st.k[i] = __builtin_amdgcn_raw_buffer_load_b128(bk.rsrc, buf_off<T>((int64_t)row0 + r, lk.rs, 8 * c), 0, 0);
+            st.k[i] = __builtin_amdgcn_raw_buffer_load_b128(bk.rsrc, buf_off<T>((int64_t)row0 + r, lk.rs, 8 * c), 0,
+                                                            kNonTemporal);
         }
 #pragma unroll
         for (int i = 0; i < NCV; ++i) {
             const int n = tid + kThreads * i, r = n / CV, c = n % CV;
-            st.v[i] = __builtin_amdgcn_raw_buffer_load_b128(bv.rsrc, buf_off<T>((int64_t)row0 + r, lv.rs, 8 * c), 0, 0);
+            st.v[i] = __builtin_amdgcn_raw_buffer_load_b128(bv.rsrc, buf_off<T>((int64_t)row0 + r, lv.rs, 8 * c), 0,
+                                                            kNonTemporal);
         }
     };
     auto consume = [&](const Stage& st, int tile, int buf) {
