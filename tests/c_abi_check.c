@@ -1,0 +1,52 @@
+/* A plain C99 caller of libla.so: the header compiles as C and the exported
+ * entry points link and answer. Only calls that need no GPU are made: the
+ * queries, and calls that fail argument validation before any HIP call. */
+#include <math.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "la.h"
+
+static int fails = 0;
+#define CHECK(cond)                                            \
+    do {                                                       \
+        if (!(cond)) {                                         \
+            fprintf(stderr, "check failed: %s\n", #cond);      \
+            ++fails;                                           \
+        }                                                      \
+    } while (0)
+
+int main(void) {
+    la_problem p;
+    memset(&p, 0, sizeof p); /* zero-initialised: Dv = D, scale = 1 */
+    p.B = 2;
+    p.H = 3;
+    p.T = 100;
+    p.D = 64;
+    p.dtype = LA_F16;
+    p.eps = 1e-6f;
+
+    CHECK(la_version() == LA_VERSION);
+    CHECK(strncmp(la_status_str(LA_ERR_HEAD_DIM), "LA_ERR_HEAD_DIM", 15) == 0);
+    CHECK(la_state_bytes(&p) == (size_t)(2 * 3 * (64 * 64 + 64) * 4));
+    CHECK(la_workspace_bytes(&p) > 0);
+
+    /* validation errors, before any HIP call */
+    CHECK(la_fwd(NULL, NULL, NULL, NULL, NULL, NULL, NULL, 0, NULL) == LA_ERR_NULL);
+    p.D = 48;
+    CHECK(la_fwd(&p, NULL, NULL, NULL, NULL, NULL, NULL, 0, NULL) == LA_ERR_HEAD_DIM);
+    p.D = 64;
+    p.eps = -1.0f;
+    CHECK(la_fwd(&p, NULL, NULL, NULL, NULL, NULL, NULL, 0, NULL) == LA_ERR_EPS);
+    p.eps = 1e-6f;
+    p.scale = NAN;
+    CHECK(la_fwd(&p, NULL, NULL, NULL, NULL, NULL, NULL, 0, NULL) == LA_ERR_SCALE);
+    p.scale = 0.0f;
+    p.flags = LA_CAUSAL;
+    CHECK(la_fwd_state(&p, NULL, NULL, NULL, NULL, 0, NULL) == LA_ERR_FLAGS);
+    p.dtype = LA_F32;
+    CHECK(la_bwd(&p, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, 0, NULL) == LA_ERR_DTYPE);
+
+    if (fails == 0) printf("c abi ok\n");
+    return fails == 0 ? 0 : 1;
+}
