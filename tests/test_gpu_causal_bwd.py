@@ -186,3 +186,18 @@ def test_causal_long_sequence_few_heads():
     assert bytes_equal(o, o2)
     for a, b in zip(g, g2):
         assert bytes_equal(a, b)
+
+
+@pytest.mark.parametrize("D,Dv", [(64, 64), (128, 64)], ids=["D64", "D128-Dv64"])
+def test_causal_empty_sequence(D, Dv):
+    """T = 0: the causal forward writes a zero state (as the bidirectional one
+    does) and the backward returns at once."""
+    q = torch.zeros(2, 3, 0, D, dtype=torch.float16, device="cuda")
+    v = torch.zeros(2, 3, 0, Dv, dtype=torch.float16, device="cuda")
+    prob = la.make_problem(q.shape, q.dtype, 1e-6, False, dv=Dv, causal=True)
+    state = torch.full((la.state_bytes(prob) // 4,), 7.0, device="cuda")
+    o, st = la.fwd(q, q, v, causal=True, state=state)
+    dq, dk, dv = la.bwd(q, q, v, v, None, causal=True)
+    torch.cuda.synchronize()
+    assert o.numel() == 0 and dq.numel() == 0 and dk.numel() == 0 and dv.numel() == 0
+    assert torch.count_nonzero(st).item() == 0
