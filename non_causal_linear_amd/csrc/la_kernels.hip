@@ -20,6 +20,15 @@
 //                      partial dS = phi(Q)^T (dO / den) on MFMA and
 //                      dz = sum_t c_t phi(q_t), combined like the forward state;
 //   bwd_dkv_kernel     dK = (V dS^T + dz) * phi'(K), dV = phi(K) dS.
+// The causal form (LA_CAUSAL; flash-linear-attention README, "Different forms
+// of linear attention"), 16-bit with DK, DV in {64, 128}, reuses the state
+// reduction per segment and adds:
+//   prefix_kernel, suffix_kernel  exclusive prefixes / suffixes of the
+//                      per-segment sums, in place;
+//   fwd_causal_kernel  the forward as a chunked scan of each segment;
+//   bwd_causal_q_kernel, bwd_causal_kv_kernel  the backward as a forward-order
+//                      scan (dQ) and a reverse-order scan (dK, dV).
+// The optional query scale needs no kernel of its own (see Plan::eps).
 //
 // MFMA conventions (v_mfma_f32_16x16x32_{f16,bf16}; for fp32 operands eight
 // v_mfma_f32_16x16x4f32 cover the same 32-long contraction): a wave holds A
