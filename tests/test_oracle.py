@@ -371,6 +371,102 @@ def test_leading_terms_cancel_at_t1():
                                rtol=1e-6, atol=1e-300)
 
 
+def leading_terms_loop(q, k, v, do, eps, fm="elu1"):
+    """Pure-Python loops over both summands of the normalised gradients, one
+    element at a time (no numpy), from the definitions
+      dphi(q_t)[i] = u_t[i] / den_t + c_t z[i],   u_t[i] = sum_j S[i][j] dO_t[j],
+      dphi(k_s)[i] = (dS v_s)[i] + dz[i],          dS[i][j] = sum_t phi(q_t)[i] dO_t[j] / den_t,
+    returning the largest |u_t[i] / den_t * phi'(q_t[i])| and the largest
+    |(dS v_s)[i] * phi'(k_s[i])|: the first summand of each, times phi'."""
+    def ph(x):
+        if fm == "relu":
+            return max(x, 0.0)
+        return x + 1.0 if x > 0 else math.exp(x)
+
+    def dph(x):
+        if fm == "relu":
+            return 1.0 if x > 0 else 0.0
+        return 1.0 if x > 0 else math.exp(x)
+
+    T, D, Dv = len(q), len(q[0]), len(v[0])
+    S = [[sum(ph(k[s][i]) * v[s][j] for s in range(T)) for j in range(Dv)] for i in range(D)]
+    z = [sum(ph(k[s][i]) for s in range(T)) for i in range(D)]
+    den = [sum(ph(q[t][i]) * z[i] for i in range(D)) + eps for t in range(T)]
+    mq = 0.0
+    for t in range(T):
+        for i in range(D):
+            u = sum(S[i][j] * do[t][j] for j in range(Dv))
+            mq = max(mq, abs(u / den[t] * dph(q[t][i])))
+    dS = [[sum(ph(q[t][i]) * do[t][j] / den[t] for t in range(T)) for j in range(Dv)] for i in range(D)]
+    mk = 0.0
+    for s in range(T):
+        for i in range(D):
+            g = sum(dS[i][j] * v[s][j] for j in range(Dv))
+            mk = max(mk, abs(g * dph(k[s][i])))
+    return mq, mk
+
+
+@pytest.mark.parametrize("fm", ["elu1", "relu"])
+@pytest.mark.parametrize("T,D,Dv,eps", [(1, 8, 8, 1e-6), (1, 5, 3, 0.7), (6, 4, 4, 1e-6), (9, 5, 7, 2.0)])
+def test_leading_terms_match_elementwise_loop(T, D, Dv, eps, fm):
+    """bwd_leading_terms_head (the error scale of the T = 1 normalised gradient
+    checks) against a pure-Python element-by-element loop over its summands."""
+    q, k, do = rand((T, D), 130 + T), rand((T, D), 131 + T), rand((T, Dv), 132 + T)
+    v = rand((T, Dv), 133 + T)
+    if fm == "relu":  # keep every row's denominator away from eps alone
+        q, k = np.abs(q) + 0.1, np.abs(k) + 0.1
+    got = oracle.bwd_leading_terms_head(q, k, v, do, eps, fm)
+    ref = leading_terms_loop(q.tolist(), k.tolist(), v.tolist(), do.tolist(), eps, fm)
+    np.testing.assert_allclose(got, ref, rtol=1e-12)
+
+
+def test_leading_terms_pins_catch_planted_mistakes():
+    """Slips planted in a copy of bwd_leading_terms_head (phi' dropped from
+    either term, a sum over elements for the max, eps left out of den, the
+    dS of simple_la) each fail the element-by-element loop. Q and K are all
+    negative here, so phi' < 1 on every element and dropping it changes each
+    maximum; eps is of the size of den, so leaving it out shows."""
+    T, D, Dv, eps = 5, 4, 6, 1.5
+    q, k = -np.abs(rand((T, D), 141)) - 0.3, -np.abs(rand((T, D), 142)) - 0.3
+    v, do = rand((T, Dv), 143), rand((T, Dv), 144)
+    ref = np.array(leading_terms_loop(q.tolist(), k.tolist(), v.tolist(), do.tolist(), eps))
+
+    def variant(kind):
+        qt, kt = oracle.phi(q), oracle.phi(k)
+        s, z = kt.T @ v, kt.sum(axis=0)
+        den = qt @ z + (0.0 if kind == "no_eps" else eps)
+        u = do @ s.T
+        ds = qt.T @ (do if kind == "simple_ds" else do / den[:, None])
+        dq_term = u / den[:, None] * (1.0 if kind == "no_dphi_q" else oracle.dphi(q))
+        dk_term = (v @ ds.T) * (1.0 if kind == "no_dphi_k" else oracle.dphi(k))
+        red = (lambda a: float(np.sum(np.abs(a)))) if kind == "sum_not_max" else (lambda a: float(np.max(np.abs(a))))
+        return np.array([red(dq_term), red(dk_term)])
+
+    np.testing.assert_allclose(variant("none"), ref, rtol=1e-12)
+    np.testing.assert_allclose(oracle.bwd_leading_terms_head(q, k, v, do, eps), ref, rtol=1e-12)
+    for kind in ("no_eps", "simple_ds", "no_dphi_q", "no_dphi_k", "sum_not_max"):
+        bad = variant(kind)
+        assert np.max(np.abs(bad - ref) / ref) > 1e-3, kind
+
+
+@pytest.mark.parametrize("simple", [False, True])
+def test_causal_batched_bwd_matches_per_head(simple):
+    """The batched causal backward is causal_bwd_head on each decoded head,
+    in place, bitwise, with D != Dv and heads that differ."""
+    from synth import Workload
+    w = Workload("t", 2, 3, 21, 6, "bf16", seed=151, Dv=10)
+    x = make_inputs(w)
+    dq, dk, dv = oracle.causal_bwd(x["q"], x["k"], x["v"], x["do"], "bf16", 0.2, simple)
+    assert dq.shape == dk.shape == w.shape and dv.shape == w.shape_v
+    d = {n: oracle.decode(x[n], "bf16") for n in ("q", "k", "v", "do")}
+    for b in range(2):
+        for h in range(3):
+            ref = oracle.causal_bwd_head(d["q"][b, h], d["k"][b, h], d["v"][b, h], d["do"][b, h], 0.2, simple)
+            for got, r in zip((dq[b, h], dk[b, h], dv[b, h]), ref):
+                np.testing.assert_array_equal(got, r)
+    assert not np.array_equal(dq[0, 0], dq[1, 2])
+
+
 @pytest.mark.parametrize("simple", [False, True])
 def test_backward_halves_compose_and_add_over_tokens(simple):
     """The Q side and K/V side of the backward, taken one at a time: with the
