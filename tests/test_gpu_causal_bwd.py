@@ -10,6 +10,7 @@ import torch
 import non_causal_linear_amd as la
 import oracle
 from synth import Workload, make_inputs
+from tests import oracle_pool
 from tests.la_testutil import TOL, bytes_equal, decode, max_rel_err, to_device
 
 pytestmark = pytest.mark.gpu
@@ -80,6 +81,19 @@ def test_causal_bwd_many_heads_one_segment(dtype):
     check_all(w, x, run(w, x, False), False)
 
 
+def boundary_rows(T, seed, extra=24):
+    """Both sides of every boundary of a power-of-two split of T into up to 64
+    segments, both sides of every 64-token chunk boundary near them, the ends,
+    and seeded picks."""
+    rows = {0, 1, T - 2, T - 1}
+    for p in (2, 4, 8, 16, 32, 64):
+        for i in range(1, p):
+            b = i * T // p
+            rows.update((b - 1, b, b + 63, b + 64))
+    rows.update(int(t) for t in np.random.default_rng(seed).integers(0, T, size=extra))
+    return sorted(r for r in rows if 0 <= r < T)
+
+
 def head_slices(x, n, T):
     return {nm: a.reshape(n, T, -1) for nm, a in x.items()}
 
@@ -89,7 +103,8 @@ def head_slices(x, n, T):
                          ids=["D64-f16", "D128-bf16", "D64-bf16-simple", "D64-Dv128-f16"])
 def test_causal_bwd_long_sequence_whole_heads(D, Dv, dtype, simple):
     """B8 H16 T16384 (every segment boundary of the split): three whole heads
-    against the oracle; bit-identical reruns."""
+    against the oracle, sampled rows (segment and chunk boundaries included)
+    of every head; bit-identical reruns."""
     w = Workload("causal-bwd-long", 8, 16, 16384, D, dtype, simple=simple, seed=92_000 + D + Dv + (3 if simple else 0),
                  Dv=Dv)
     print(f"case causal bwd B8 H16 T16384 D={D} Dv={Dv} {dtype} simple={simple} seed={w.seed}", flush=True)
@@ -97,10 +112,23 @@ def test_causal_bwd_long_sequence_whole_heads(D, Dv, dtype, simple):
     g = run(w, x, simple)
     n = w.B * w.H
     hx = head_slices(x, n, w.T)
-    for h in (0, 77, n - 1):
+    whole = (0, 77, n - 1)
+    for h in whole:
         ref = oracle.causal_bwd(*(hx[nm][h][None, None] for nm in ("q", "k", "v", "do")), dtype, w.eps, simple)
         for name, gg, r in zip(("dQ", "dK", "dV"), g, ref):
             check(name, decode(gg.reshape(n, w.T, -1)[h], dtype), r[0, 0], dtype, f" head {h}")
+    # every other head: sampled rows, the oracle run in a process pool
+    rows = boundary_rows(w.T, w.seed + 5)
+    idx = torch.tensor(rows, device="cuda")
+    got = [decode(gg.reshape(n, w.T, -1).index_select(1, idx), dtype) for gg in g]
+    dec = {nm: oracle.decode(hx[nm], dtype) for nm in ("q", "k", "v", "do")}
+    others = [h for h in range(n) if h not in whole]
+    jobs = [(dec["q"][h], dec["k"][h], dec["v"][h], dec["do"][h], rows, w.eps, simple, "elu1") for h in others]
+    res = oracle_pool.map_heads(oracle_pool.causal_bwd_rows, jobs)
+    for i, name in enumerate(("dQ", "dK", "dV")):
+        worst = max(max_rel_err(got[i][h], r[i]) for h, r in zip(others, res))
+        print(f"  {name}, {len(rows)} rows on all {len(others)} other heads: max rel err {worst:.3e}", flush=True)
+        assert worst <= TOL[dtype], f"{name} sampled rows: {worst:.3e} > {TOL[dtype]}"
     g2 = run(w, x, simple)
     for a, b in zip(g, g2):
         assert bytes_equal(a, b)

@@ -3,8 +3,9 @@
 Small cases compare every element; they span several tiles and slices and end
 on ragged tails. The five named workloads run at full size in the launch
 configuration the benchmark times: the fp32 state (S, z) is checked for every
-head, O/dQ/dK/dV completely on four heads (first, last, two seeded picks) and
-O on sampled rows of every other head. Results must also be bit-identical
+head, O/dQ/dK/dV completely on four heads (first, last, two seeded picks), O on
+sampled rows of every other head, and dQ/dK/dV on the same sampled rows of every
+head (slice boundaries included). Results must also be bit-identical
 across reruns.
 """
 import numpy as np
@@ -163,6 +164,18 @@ def test_max_head_size_periodic(D, dtype):
 
 # ------------------------------------------------------------- full-size workloads
 
+def grad_rows(T, seed, extra=40):
+    """Rows at both sides of every boundary of a power-of-two split of T into
+    up to 64 pieces, the first and last rows, and seeded picks."""
+    rows = {0, 1, T - 2, T - 1}
+    for p in (2, 4, 8, 16, 32, 64):
+        for i in range(1, p):
+            b = i * T // p
+            rows.update((b - 1, b))
+    rows.update(int(t) for t in np.random.default_rng(seed).integers(0, T, size=extra))
+    return sorted(r for r in rows if 0 <= r < T)
+
+
 def sampled_heads(n, seed):
     rng = np.random.default_rng(seed)
     picks = [0, n - 1] + [int(h) for h in rng.choice(np.arange(1, max(n - 1, 2)), size=2)]
@@ -182,14 +195,36 @@ def test_workload_full_size(name):
         qh, kh, vh = heads_of(x["q"], w.dtype), heads_of(x["k"], w.dtype), heads_of(x["v"], w.dtype)
         s_got, z_got = split_state(out["state"], w.B, w.H, w.D)
         s_got, z_got = s_got.reshape(n, w.D, w.D), z_got.reshape(n, w.D)
-        # state of every head
+        # the same sampled rows of dQ, dK, dV on every head: the slice and
+        # chunk boundaries of every power-of-two split up to 64 (either side),
+        # the ends, and seeded picks
+        if w.bwd:
+            rows = grad_rows(w.T, w.seed + 41)
+            idx = torch.tensor(rows, device="cuda")
+            g_rows = {nm: decode(out[nm].reshape(n, w.T, w.D).index_select(1, idx), w.dtype)
+                      for nm in ("dq", "dk", "dv")}
+            dh_all = heads_of(x["do"], w.dtype)
+        # state of every head, and its gradient rows from the oracle's two
+        # halves of the backward with that head's own S, z, dS, dz
         worst_s = worst_z = 0.0
+        worst_g = {"dq": 0.0, "dk": 0.0, "dv": 0.0}
         for h in range(n):
             s_ref, z_ref = oracle.state_head(kh[h], vh[h])
             worst_s = max(worst_s, max_rel_err(s_got[h], s_ref))
             worst_z = max(worst_z, max_rel_err(z_got[h], z_ref))
+            if w.bwd:
+                dq_ref, ds_ref, dz_ref = oracle.bwd_q_side_head(qh[h], dh_all[h], s_ref, z_ref, w.eps, simple)
+                dk_ref, dv_ref = oracle.bwd_kv_side_head(kh[h][rows], vh[h][rows], ds_ref, dz_ref, simple)
+                for nm, ref in (("dq", dq_ref[rows]), ("dk", dk_ref), ("dv", dv_ref)):
+                    worst_g[nm] = max(worst_g[nm], max_rel_err(g_rows[nm][h], ref))
         print(f"  state, all {n} heads: S {worst_s:.3e}  z {worst_z:.3e}", flush=True)
         assert worst_s <= TOL[w.dtype] and worst_z <= TOL[w.dtype]
+        if w.bwd:
+            print(f"  gradients, {len(rows)} rows on all {n} heads: dQ {worst_g['dq']:.3e}  "
+                  f"dK {worst_g['dk']:.3e}  dV {worst_g['dv']:.3e}", flush=True)
+            for nm, e in worst_g.items():
+                assert e <= TOL[w.dtype], f"{nm} sampled rows, all heads: {e:.3e} > {TOL[w.dtype]}"
+            del g_rows, dh_all
         o_all = out["o"].reshape(n, w.T, w.D)
         # complete tensors on sampled heads
         heads = sampled_heads(n, w.seed + 17)
