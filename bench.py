@@ -56,8 +56,14 @@ def to_device(x: np.ndarray, dtype: str) -> torch.Tensor:
     return torch.from_numpy(np.ascontiguousarray(x)).cuda()
 
 
-def cpu_baseline(w, x, max_heads: int) -> dict:
-    """The fp64 oracle as it stands, forward then backward, per head on a thread pool."""
+def cpu_baseline(w, x, max_heads: int, gpu_out: dict | None = None) -> dict:
+    """The fp64 oracle as it stands, forward then backward, per head on a
+    thread pool of the host's cores (at most 16: one GPU's share of the box).
+
+    The oracle's outputs for the sampled heads are then held against the
+    GPU's outputs of the timed steps (gpu_out: device tensors O, dQ, dK, dV),
+    outside every timed region: the bench line carries the normwise max
+    relative error of each tensor over those heads."""
     from concurrent.futures import ThreadPoolExecutor
 
     from threadpoolctl import threadpool_limits
@@ -66,26 +72,26 @@ def cpu_baseline(w, x, max_heads: int) -> dict:
 
     n = w.B * w.H
     heads = min(n, max_heads)
-    cores = len(os.sched_getaffinity(0))
-    cores = max(1, min(cores, 16))
+    available = len(os.sched_getaffinity(0))
+    cores = max(1, min(available, 16))
     qh, kh = (x[nm].reshape(n, w.T, w.D) for nm in ("q", "k"))
     vh, dh = (x[nm].reshape(n, w.T, w.dv) for nm in ("v", "do"))
 
     def fwd_one(h):
         return oracle.fwd_head(oracle.decode(qh[h], w.dtype), oracle.decode(kh[h], w.dtype),
-                               oracle.decode(vh[h], w.dtype), w.eps, w.simple)[0].shape
+                               oracle.decode(vh[h], w.dtype), w.eps, w.simple)[0]
 
     def bwd_one(h):
         return oracle.bwd_head(oracle.decode(qh[h], w.dtype), oracle.decode(kh[h], w.dtype),
                                oracle.decode(vh[h], w.dtype), oracle.decode(dh[h], w.dtype),
-                               w.eps, w.simple)[0].shape
+                               w.eps, w.simple)
 
     with threadpool_limits(1), ThreadPoolExecutor(max_workers=cores) as pool:
         list(pool.map(fwd_one, range(min(heads, cores))))  # warm-up
         t0 = time.perf_counter()
-        list(pool.map(fwd_one, range(heads)))
+        o_ref = list(pool.map(fwd_one, range(heads)))
         t1 = time.perf_counter()
-        list(pool.map(bwd_one, range(heads)))
+        g_ref = list(pool.map(bwd_one, range(heads)))
         t2 = time.perf_counter()
     fwd_bytes = 2 * heads * w.T * (w.D + w.dv) * w.elem_bytes
     model = ""
@@ -96,17 +102,76 @@ def cpu_baseline(w, x, max_heads: int) -> dict:
                 break
     except OSError:
         pass
-    return {
+    res = {
         "value": fwd_bytes / (t1 - t0) / 1e9,
         "unit": "GB/s",
         "cores": cores,
+        "cores_available": available,
         "kind": "oracle",
         "sample": f"{heads} of {n} heads at T={w.T}, D={w.D}, Dv={w.dv}: fp64 forward then backward, "
-                  f"one head per thread",
+                  f"one head per thread on {cores} threads",
         "fwd_ms_sample": (t1 - t0) * 1e3,
         "bwd_ms_sample": (t2 - t1) * 1e3,
         "cpu": model,
     }
+    if gpu_out is not None:
+        res["parity_vs_oracle"] = parity(w, heads, gpu_out, o_ref, g_ref)
+    return res
+
+
+def parity(w, heads: int, gpu_out: dict, o_ref, g_ref) -> dict:
+    """Normwise max relative error max|X - R| / max|R| per tensor and head
+    (the worst head reported) of the timed steps' outputs against the oracle."""
+    import oracle
+
+    n = w.B * w.H
+    worst = {}
+    for name, refs, width in (("O", o_ref, w.dv), ("dQ", [g[0] for g in g_ref], w.D),
+                              ("dK", [g[1] for g in g_ref], w.D), ("dV", [g[2] for g in g_ref], w.dv)):
+        t = gpu_out.get(name)
+        if t is None:
+            continue
+        t = t.reshape(n, w.T, width)
+        e = 0.0
+        for h in range(heads):
+            got = oracle.decode(storage(t[h]), w.dtype)
+            r = refs[h]
+            e = max(e, float(np.max(np.abs(got - r)) / max(float(np.max(np.abs(r))), 1e-300)))
+        worst[name] = float(f"{e:.3e}")
+    tol = 2e-2 if w.dtype == "bf16" else 5e-3
+    return {"max_rel_err": worst, "heads": heads, "tolerance": tol,
+            "pass": all(v <= tol for v in worst.values()),
+            "metric": "per tensor, the worst over the heads of max|X - R| / max|R|"}
+
+
+def storage(t: torch.Tensor) -> np.ndarray:
+    """Device tensor to the host storage format the oracle decodes."""
+    t = t.detach().cpu()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
+
+
+def versions() -> dict:
+    """Toolchain and library versions of this run."""
+    import subprocess
+
+    out = {"torch": torch.__version__, "torch_hip": getattr(torch.version, "hip", None),
+           "la_version": int(la.lib().la_version())}
+    try:
+        out["rocm"] = open("/opt/rocm/.info/version").read().strip()
+    except OSError:
+        out["rocm"] = None
+    try:
+        r = subprocess.run(["/opt/rocm/bin/hipcc", "--version"], capture_output=True, text=True, timeout=30)
+        out["hipcc"] = next((ln.strip() for ln in r.stdout.splitlines() if "HIP version" in ln), None)
+    except (OSError, subprocess.SubprocessError):
+        out["hipcc"] = None
+    try:
+        out["gpu"] = torch.cuda.get_device_properties(0).gcnArchName
+    except (AttributeError, RuntimeError):
+        out["gpu"] = None
+    return out
 
 
 def copy_bandwidth(reps: int = 10) -> float:
@@ -358,6 +423,18 @@ def main() -> int:
     dom_bytes = lb[dominant]
     achieved = dom_bytes / (avg[dominant] * 1e-3) / 1e9
 
+    # one more step after the timed ones (untimed): its outputs must equal the
+    # last timed step's byte for byte
+    outs = {"O": o, "state": state}
+    if w.bwd:
+        outs.update({"dQ": dq, "dK": dk, "dV": dv})
+    kept = {nm: t.clone() for nm, t in outs.items()}
+    do_flush(args.flush)
+    step(mk())
+    torch.cuda.synchronize()
+    bit_identical = all(torch.equal(kept[nm].view(torch.uint8), outs[nm].view(torch.uint8)) for nm in outs)
+    del kept
+
     if args.copy_calibration:
         src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)
@@ -393,6 +470,8 @@ def main() -> int:
         "kernel_ms": {kname: round(a, 4) for kname, a in avg.items()},
         "wall_ms_per_step_incl_flush": round(wall / args.steps * 1e3, 4),
         **({"other_cache_conditions": other} if other else {}),
+        "bit_identical_rerun": bit_identical,
+        "versions": versions(),
         "roofline": {
             "kernel": dominant,
             "bound": "hbm",
@@ -415,6 +494,8 @@ def main() -> int:
             line["roofline"]["traffic"] = round(tb)
             line["roofline"]["traffic_unit"] = "bytes/launch"
             line["roofline"]["traffic_over_algorithmic"] = round(tb / dom_bytes, 4)
+            line["roofline"]["traffic_source"] = (f"stored rocprofv3 FETCH_SIZE and WRITE_SIZE runs on this "
+                                                  f"kernel source (sha256 {h}), profiles/traffic_{w.name}.json")
     if w.bwd:
         bwd_ms = per["bwd_dq"] + per["bwd_dkv"]
         line["bwd_ms"] = round(float(np.mean(bwd_ms)), 4)
@@ -431,7 +512,10 @@ def main() -> int:
             line["context_torch_eager_fp32"] = torch_eager(w, q, k, v, do, do_flush)
     if not args.no_cpu_baseline:
         print("[bench] oracle on host cores", file=sys.stderr, flush=True)
-        line["cpu_baseline"] = cpu_baseline(w, x, args.cpu_heads)
+        gpu_out = {"O": o}
+        if w.bwd:
+            gpu_out.update({"dQ": dq, "dK": dk, "dV": dv})
+        line["cpu_baseline"] = cpu_baseline(w, x, args.cpu_heads, gpu_out)
     print(json.dumps(line), flush=True)
     return 0
 
