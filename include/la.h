@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define LA_VERSION 5
+#define LA_VERSION 6
 
 typedef enum {
     LA_F32 = 0,
@@ -77,7 +77,9 @@ typedef enum {
     LA_ERR_ALIGN = 8,      /* a tensor is not 16-byte aligned, ws not 256     */
     LA_ERR_ALIAS = 9,      /* an output overlaps an input or another output   */
     LA_ERR_DEVICE = 10,    /* HIP reported an error on launch                 */
-    LA_ERR_SCALE = 11      /* scale not finite                                */
+    LA_ERR_SCALE = 11,     /* scale not finite                                */
+    LA_ERR_SCRATCH = 12    /* la_fwd_noalloc: the problem needs more than
+                              LA_NOALLOC_SCRATCH_BYTES of scratch             */
 } la_status;
 
 /* Drop the denominator: simple_la (FBi-LA README, "Update" 2024-12-28). */
@@ -158,6 +160,33 @@ int la_fwd(const la_problem* p, const void* q, const void* k, const void* v,
 int la_bwd(const la_problem* p, const void* q, const void* k, const void* v,
            const void* dout, const void* state, void* dq, void* dk, void* dv,
            void* ws, size_t ws_bytes, void* stream);
+
+/* Bytes of the static device scratch that la_fwd_noalloc uses (64 MiB). */
+#define LA_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+/* For callers that cannot allocate: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc. la_fwd with the same
+ * problem and buffers, computing the same bits, except that the split
+ * partials go into a static device array of LA_NOALLOC_SCRATCH_BYTES that the
+ * library holds on each GPU from the moment its code loads there until the
+ * process ends, instead of a caller workspace. `state` is required here
+ * (LA_ERR_NULL without it). The call allocates and frees nothing, and
+ * issues no memset: every scratch byte it reads it has written earlier in the
+ * same call. A problem that needs more scratch than the array holds gets
+ * LA_ERR_SCRATCH and enqueues nothing. A problem needs B*H*P*(D*Dv + D)*4
+ * bytes when the planner splits each head into P > 1 token slices, none when
+ * P = 1 (as soon as B*H fills the state kernel's grid of 512 to 2048
+ * workgroups); every 16-bit problem with D and Dv up to 96 and every fp32
+ * problem with D and Dv up to 64 fits, and so do B8-H16-T16384-D64 (8.5 MB)
+ * and B8-H32-T8192-D128 (33.8 MB). The scratch is
+ * shared by every la_fwd_noalloc call on a GPU: calls that may overlap in time
+ * on one GPU (different streams with no ordering between them, or different
+ * host threads) race on it; calls in one stream's order do not. The current
+ * device must be the stream's device. The first call on each device looks up
+ * the array's address there (no allocation); make that first call outside
+ * graph capture. */
+int la_fwd_noalloc(const la_problem* p, const void* q, const void* k, const void* v, void* o,
+                   void* state, void* stream);
 
 /* ---- The steps of the path, one call each (la_fwd and la_bwd are exactly
  * these calls in order). ---- */

@@ -18,7 +18,7 @@ import os
 import torch
 
 __all__ = [
-    "LAError", "lib", "fwd", "bwd", "fwd_state", "fwd_output", "bwd_dq", "bwd_dkv", "linear_attention",
+    "LAError", "lib", "fwd", "bwd", "fwd_noalloc", "NOALLOC_SCRATCH_BYTES", "fwd_state", "fwd_output", "bwd_dq", "bwd_dkv", "linear_attention",
     "state_bytes", "workspace_bytes", "new_state", "workspace", "Problem",
     "LA_F32", "LA_F16", "LA_BF16", "LA_SIMPLE", "LA_LAYOUT_BTHD", "LA_PHI_RELU", "LA_PHI_IDENTITY", "LA_CAUSAL",
     "EXPORTS",
@@ -37,7 +37,9 @@ DTYPE_CODE = {torch.float32: LA_F32, torch.float16: LA_F16, torch.bfloat16: LA_B
 
 # Every symbol include/la.h declares.
 EXPORTS = ("la_version", "la_status_str", "la_state_bytes", "la_workspace_bytes", "la_fwd",
-           "la_bwd", "la_fwd_state", "la_fwd_output", "la_bwd_dq", "la_bwd_dkv")
+           "la_bwd", "la_fwd_state", "la_fwd_output", "la_bwd_dq", "la_bwd_dkv", "la_fwd_noalloc")
+# Size of the static device scratch behind la_fwd_noalloc (LA_NOALLOC_SCRATCH_BYTES).
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 class Problem(ctypes.Structure):
@@ -81,6 +83,7 @@ def lib() -> ctypes.CDLL:
         "la_fwd_output": [P, vp, vp, vp, vp],
         "la_bwd_dq": [P, vp, vp, vp, vp, vp, sz, vp],
         "la_bwd_dkv": [P, vp, vp, vp, vp, vp, sz, vp],
+        "la_fwd_noalloc": [P, vp, vp, vp, vp, vp, vp],
     }
     for name, args in sigs.items():
         fn = getattr(L, name)
@@ -240,6 +243,25 @@ def fwd(q, k, v, *, eps=1e-6, simple=False, layout="bhtd", phi="elu1", out=None,
     ws, wsb = _ws(prob, q.device, ws)
     _check(lib().la_fwd(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(state),
                         _ptr(ws), wsb, _stream(q.device)))
+    return out, state
+
+
+def fwd_noalloc(q, k, v, *, out, state, eps=1e-6, simple=False, layout="bhtd", phi="elu1", causal=False,
+                scale=None):
+    """fwd through la_fwd_noalloc: the library call allocates nothing (its
+    partials go into the library's static device scratch), so the caller
+    passes both outputs, ``out`` and ``state``; writes and returns them. The
+    same bits as fwd. Calls that overlap in time on one GPU race on the
+    scratch."""
+    _tensor(q, None, "q")
+    _tensor(k, q, "k")
+    dv = v.shape[-1] if isinstance(v, torch.Tensor) else None
+    _tensor(v, q, "v", dv)
+    prob = make_problem(q.shape, q.dtype, eps, simple, layout, phi, dv, causal, scale)
+    _tensor(out, q, "out", dv)
+    _state(state, prob, q.device)
+    _check(lib().la_fwd_noalloc(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(state),
+                                _stream(q.device)))
     return out, state
 
 

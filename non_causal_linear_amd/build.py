@@ -3,7 +3,8 @@
     python -m non_causal_linear_amd.build
 
 csrc/la_kernels.hip is compiled once per (element type, Q/K head size) unit,
-the units in parallel, and linked with csrc/la_api.cpp into
+the units in parallel, and linked with csrc/la_api.cpp and csrc/la_scratch.hip
+(the static device scratch of la_fwd_noalloc) into
 non_causal_linear_amd/libla.so (written to a temporary name and renamed, so
 a process that has the old library open keeps a consistent file).
 """
@@ -24,6 +25,7 @@ LIB = os.path.join(PKG, "libla.so")
 
 KERNELS = "la_kernels.hip"
 API = "la_api.cpp"
+SCRATCH = "la_scratch.hip"
 # (la_dtype, DK) of every kernel unit; each covers all DV
 UNITS = [(dt, dk) for dt in (0, 1, 2) for dk in (32, 64, 96, 128)]
 
@@ -74,7 +76,7 @@ def build(verbose: bool = False, jobs: int | None = None) -> str:
         tmp = LIB + ".tmp%d" % os.getpid()
         try:
             warnings.append(_run([cc, *HIPCC_FLAGS, "-shared", *inc, *objs, os.path.join(CSRC, API),
-                                  "-o", tmp], verbose))
+                                  os.path.join(CSRC, SCRATCH), "-o", tmp], verbose))
         except Exception:
             if os.path.exists(tmp):
                 os.unlink(tmp)

@@ -204,6 +204,7 @@ const char* la_status_str(int s) {
         case LA_ERR_ALIGN: return "LA_ERR_ALIGN: tensors need 16-byte, workspace 256-byte alignment";
         case LA_ERR_ALIAS: return "LA_ERR_ALIAS: an output overlaps another buffer";
         case LA_ERR_DEVICE: return "LA_ERR_DEVICE: HIP launch error";
+        case LA_ERR_SCRATCH: return "LA_ERR_SCRATCH: the problem needs more than LA_NOALLOC_SCRATCH_BYTES of scratch";
         default: return "unknown la_status";
     }
 }
@@ -268,6 +269,34 @@ int la_fwd(const la_problem* p, const void* q, const void* k, const void* v, voi
     if (pl.BH == 0) return LA_OK;
     float* stp = state ? static_cast<float*>(state)
                        : reinterpret_cast<float*>(static_cast<char*>(ws) + pl.off_fstate);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (causal) return device_status(kernel_set(pl.dtype, pl.DK)->fwd_causal(pl, q, k, v, o, stp, ws, s));
+    st = device_status(kernel_set(pl.dtype, pl.DK)->fwd_state(pl, k, v, stp, ws, s));
+    if (st != LA_OK || tk == 0) return st;
+    return device_status(kernel_set(pl.dtype, pl.DK)->fwd_output(pl, q, stp, o, s));
+}
+
+int la_fwd_noalloc(const la_problem* p, const void* q, const void* k, const void* v, void* o, void* state,
+                   void* stream) {
+    static_assert(LA_NOALLOC_SCRATCH_BYTES == la::kScratchBytes, "scratch size in la.h and the library differ");
+    la_status st = check_problem(p);
+    if (st != LA_OK) return st;
+    const bool causal = (p->flags & LA_CAUSAL) != 0;
+    if (causal && (st = check_causal(p)) != LA_OK) return st;
+    const la::Plan pl = make_plan(p);
+    const size_t tk = size_t(pl.BH * pl.T * pl.DK) * elem_bytes(pl.dtype);
+    const size_t tv = size_t(pl.BH * pl.T * pl.DV) * elem_bytes(pl.dtype);
+    const size_t sb = la_state_bytes(p);
+    if (pl.BH > 0 && !state) return LA_ERR_NULL;
+    st = check_buffers({{q, tk}, {k, tk}, {v, tv}}, {{o, tv}, {state, sb}}, {16, 16, 16}, {16, 16});
+    if (st != LA_OK) return st;
+    // the forward's only scratch: the split partials, at offset 0 (off_part)
+    const size_t need = pl.P > 1 ? size_t(pl.BH) * pl.P * (size_t(pl.DK) * pl.DV + pl.DK) * 4 : 0;
+    if (need > la::kScratchBytes) return LA_ERR_SCRATCH;
+    if (pl.BH == 0) return LA_OK;
+    void* ws = nullptr;
+    if (la::scratch_device_ptr(&ws) != hipSuccess) return LA_ERR_DEVICE;
+    float* stp = static_cast<float*>(state);
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (causal) return device_status(kernel_set(pl.dtype, pl.DK)->fwd_causal(pl, q, k, v, o, stp, ws, s));
     st = device_status(kernel_set(pl.dtype, pl.DK)->fwd_state(pl, k, v, stp, ws, s));

@@ -80,6 +80,13 @@ struct KernelSet {
                              void* dq, void* dk, void* dv, void* ws, hipStream_t s);
 };
 
+// Bytes of the static device scratch of la_fwd_noalloc (LA_NOALLOC_SCRATCH_BYTES).
+constexpr size_t kScratchBytes = size_t(64) << 20;
+
+// Device address of that scratch on the current device, looked up with
+// hipGetSymbolAddress on the first call per device and kept (la_scratch.hip).
+hipError_t scratch_device_ptr(void** out);
+
 // One unit per (la_dtype, DK): kernel_set_<dtype>_<DK>().
 #define LA_KERNEL_UNITS(X) \
     X(0, 32) X(0, 64) X(0, 96) X(0, 128) X(1, 32) X(1, 64) X(1, 96) X(1, 128) \

@@ -33,6 +33,8 @@ int main(void) {
 
     /* validation errors, before any HIP call */
     CHECK(la_fwd(NULL, NULL, NULL, NULL, NULL, NULL, NULL, 0, NULL) == LA_ERR_NULL);
+    CHECK(la_fwd_noalloc(NULL, NULL, NULL, NULL, NULL, NULL, NULL) == LA_ERR_NULL);
+    CHECK(LA_NOALLOC_SCRATCH_BYTES == 64u * 1024u * 1024u);
     p.D = 48;
     CHECK(la_fwd(&p, NULL, NULL, NULL, NULL, NULL, NULL, 0, NULL) == LA_ERR_HEAD_DIM);
     p.D = 64;
