@@ -18,9 +18,12 @@
  * dout, dv dense row-major [B, H, T, Dv] arrays of `dtype` elements (the last
  * dimension contiguous), each 16-byte aligned; with LA_LAYOUT_BTHD in flags
  * they are [B, T, H, D] and [B, T, H, Dv] instead (each row still contiguous,
- * heads interleaved token by token). `state` is fp32: B*H blocks of S (D*Dv
- * floats, S[i][j] at i*Dv + j) followed by B*H blocks of z (D floats);
- * la_state_bytes() gives its size.
+ * heads interleaved token by token). With la_problem.strides set, every
+ * tensor has its own batch, head and token strides instead (strided views,
+ * such as the Q, K and V of a packed [B, T, 3, H, D] projection, need no
+ * copy). `state` is fp32: B*H blocks of S (D*Dv floats, S[i][j] at
+ * i*Dv + j) followed by B*H blocks of z (D floats); la_state_bytes() gives
+ * its size.
  *
  * Ownership. The caller allocates and owns all device memory: tensors, state
  * and workspace. The library never allocates, frees, synchronises or prints.
@@ -57,7 +60,7 @@
 extern "C" {
 #endif
 
-#define LA_VERSION 6
+#define LA_VERSION 7
 
 typedef enum {
     LA_F32 = 0,
@@ -78,8 +81,11 @@ typedef enum {
     LA_ERR_ALIAS = 9,      /* an output overlaps an input or another output   */
     LA_ERR_DEVICE = 10,    /* HIP reported an error on launch                 */
     LA_ERR_SCALE = 11,     /* scale not finite                                */
-    LA_ERR_SCRATCH = 12    /* la_fwd_noalloc: the problem needs more than
+    LA_ERR_SCRATCH = 12,   /* la_fwd_noalloc: the problem needs more than
                               LA_NOALLOC_SCRATCH_BYTES of scratch             */
+    LA_ERR_STRIDE = 13     /* a stride is negative or not a multiple of 16
+                              bytes, rows overlap, or an output's rows overlap
+                              each other                                      */
 } la_status;
 
 /* Drop the denominator: simple_la (FBi-LA README, "Update" 2024-12-28). */
@@ -102,6 +108,29 @@ typedef enum {
  * backward's scratch when the flag is set. */
 #define LA_CAUSAL 0x10u
 
+/* Strides of one tensor, in elements: element f of token t of head h of
+ * batch b sits at base + b*batch + h*head + t*token + f (the D or Dv features
+ * of a row are contiguous). */
+typedef struct {
+    int64_t batch, head, token;
+} la_tensor_strides;
+
+/* The strides of every tensor a call may touch; a call reads only the
+ * entries of the tensors it takes (la_fwd: q, k, v, o; la_bwd: q, k, v, dout,
+ * dq, dk, dv; the step calls their own). Requirements, per tensor used
+ * (LA_ERR_STRIDE otherwise): every stride >= 0 and a multiple of 16 bytes;
+ * token >= the row width (D or Dv), so rows do not overlap; one head's rows
+ * addressable with 32-bit offsets, (T + 1024) * token * elt < 2^31; and for
+ * outputs (o, dq, dk, dv) rows that no other (b, h, t) of the same tensor
+ * overlaps: taking the dimensions of extent > 1 by increasing stride, each
+ * stride at least the span of the ones before it (row width first). Inputs
+ * may overlap each other (q, k, v of one packed buffer) and may repeat rows
+ * across heads (head = 0). Outputs must not overlap any other buffer of the
+ * call, compared by the byte ranges they span. */
+typedef struct {
+    la_tensor_strides q, k, v, o, dout, dq, dk, dv;
+} la_strides;
+
 /* Problem description shared by every call. B, H, T >= 0 (a zero size is an
  * empty problem: nothing to compute, LA_OK), B*H <= 2^24. D is the head size
  * of Q and K (and of dQ, dK), Dv that of V (and of O, dO, dV); 0 in Dv stands
@@ -118,7 +147,7 @@ typedef enum {
  * as stated). In normalised mode this equals eps / scale with no scale; in
  * simple mode it multiplies O and the three gradients. Any finite value; a
  * non-finite one gives LA_ERR_SCALE. The struct is zero-initialisable: a
- * zero scale stands for 1. */
+ * zero scale stands for 1, NULL strides for the dense layout. */
 typedef struct {
     int64_t B, H, T, D;
     int64_t Dv;      /* head size of V, O, dO, dV; 0 means D */
@@ -126,6 +155,9 @@ typedef struct {
     uint32_t flags;  /* LA_SIMPLE, LA_LAYOUT_BTHD, one of LA_PHI_RELU, LA_PHI_IDENTITY, LA_CAUSAL */
     float eps;
     float scale;     /* multiplies phi(q); 0 stands for 1 (see below)     */
+    const la_strides* strides;  /* NULL: dense, as LA_LAYOUT_BTHD says; else
+                                   every tensor's strides (LA_LAYOUT_BTHD must
+                                   then be clear: LA_ERR_FLAGS) */
 } la_problem;
 
 /* Library version (LA_VERSION of the build). */

@@ -18,7 +18,7 @@ import os
 import torch
 
 __all__ = [
-    "LAError", "lib", "fwd", "bwd", "fwd_noalloc", "NOALLOC_SCRATCH_BYTES", "fwd_state", "fwd_output", "bwd_dq", "bwd_dkv", "linear_attention",
+    "LAError", "lib", "fwd", "bwd", "fwd_noalloc", "NOALLOC_SCRATCH_BYTES", "Strides", "TensorStrides", "fwd_state", "fwd_output", "bwd_dq", "bwd_dkv", "linear_attention",
     "state_bytes", "workspace_bytes", "new_state", "workspace", "Problem",
     "LA_F32", "LA_F16", "LA_BF16", "LA_SIMPLE", "LA_LAYOUT_BTHD", "LA_PHI_RELU", "LA_PHI_IDENTITY", "LA_CAUSAL",
     "EXPORTS",
@@ -42,11 +42,25 @@ EXPORTS = ("la_version", "la_status_str", "la_state_bytes", "la_workspace_bytes"
 NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
+class TensorStrides(ctypes.Structure):
+    """Mirror of la_tensor_strides (elements)."""
+    _fields_ = [("batch", ctypes.c_int64), ("head", ctypes.c_int64), ("token", ctypes.c_int64)]
+
+
+STRIDED = ("q", "k", "v", "o", "dout", "dq", "dk", "dv")
+
+
+class Strides(ctypes.Structure):
+    """Mirror of la_strides."""
+    _fields_ = [(n, TensorStrides) for n in STRIDED]
+
+
 class Problem(ctypes.Structure):
     """Mirror of la_problem."""
     _fields_ = [("B", ctypes.c_int64), ("H", ctypes.c_int64), ("T", ctypes.c_int64),
                 ("D", ctypes.c_int64), ("Dv", ctypes.c_int64), ("dtype", ctypes.c_int32),
-                ("flags", ctypes.c_uint32), ("eps", ctypes.c_float), ("scale", ctypes.c_float)]
+                ("flags", ctypes.c_uint32), ("eps", ctypes.c_float), ("scale", ctypes.c_float),
+                ("strides", ctypes.POINTER(Strides))]
 
 
 class LAError(RuntimeError):
@@ -124,15 +138,16 @@ def make_problem(shape, dtype: torch.dtype, eps: float, simple: bool, layout: st
 
 
 def _tensor(x: torch.Tensor, like: torch.Tensor | None, name: str, last: int | None = None) -> torch.Tensor:
-    """x must be a contiguous GPU tensor; given ``like``, with its dtype,
-    device and leading three dimensions, and a last dimension of ``last``
-    (None: like's)."""
+    """x must be a GPU tensor whose last (feature) dimension is contiguous;
+    given ``like``, with its dtype, device and leading three dimensions, and a
+    last dimension of ``last`` (None: like's). The other dimensions may be
+    strided (a view into a larger buffer): the library takes their strides."""
     if not isinstance(x, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
     if x.device.type != "cuda":
         raise ValueError(f"{name} must be on a GPU, got {x.device}")
-    if not x.is_contiguous():
-        raise ValueError(f"{name} must be contiguous [B, H, T, D]")
+    if x.dim() != 4 or (x.shape[-1] > 1 and x.stride(-1) != 1):
+        raise ValueError(f"{name} must be a 4-d tensor with a contiguous last dimension")
     if like is not None:
         want = tuple(like.shape[:-1]) + ((like.shape[-1] if last is None else last),)
         if tuple(x.shape) != want or x.dtype != like.dtype or x.device != like.device:
@@ -154,6 +169,32 @@ def _state(state, prob: Problem, device: torch.device, name: str = "state") -> t
     if state.numel() * 4 < state_bytes(prob):
         raise ValueError(f"{name} holds {state.numel() * 4} bytes; the problem needs {state_bytes(prob)}")
     return state
+
+
+def _tensor_strides(x: torch.Tensor, layout: str) -> TensorStrides:
+    """Batch, head and token strides of a [B, H, T, D] ("bhtd") or [B, T, H, D]
+    ("bthd") tensor. A dimension of extent 1 has no meaningful stride: it is
+    given as 0 (batch, head) or the row width (token)."""
+    if layout == "bhtd":
+        (B, H, T, W), (sb, sh, st) = x.shape, x.stride()[:3]
+    else:
+        (B, T, H, W), (sb, st, sh) = x.shape, x.stride()[:3]
+    return TensorStrides(sb if B > 1 else 0, sh if H > 1 else 0, st if T > 1 else W)
+
+
+def _attach_strides(prob: Problem, layout: str, tensors: dict) -> Problem:
+    """Describe the call's tensors by their strides when any of them is not
+    dense in ``layout`` (a dense call keeps strides NULL and runs exactly as
+    before). tensors: la_strides field name -> tensor."""
+    if all(t.is_contiguous() for t in tensors.values()):
+        return prob
+    st = Strides()
+    for name, t in tensors.items():
+        setattr(st, name, _tensor_strides(t, layout))
+    prob.flags &= ~LA_LAYOUT_BTHD
+    prob.strides = ctypes.pointer(st)
+    prob._strides_keepalive = st
+    return prob
 
 
 def _ptr(x: torch.Tensor | None):
@@ -208,6 +249,7 @@ def fwd_state(k, v, *, eps=1e-6, simple=False, layout="bhtd", phi="elu1", state=
     _tensor(k, None, "k")
     _tensor(v, k, "v", v.shape[-1] if isinstance(v, torch.Tensor) else None)
     prob = make_problem(k.shape, k.dtype, eps, simple, layout, phi, v.shape[-1])
+    _attach_strides(prob, layout, {"k": k, "v": v})
     state = new_state(prob, k.device) if state is None else _state(state, prob, k.device)
     ws, wsb = _ws(prob, k.device, ws)
     _check(lib().la_fwd_state(ctypes.byref(prob), _ptr(k), _ptr(v), _ptr(state), _ptr(ws), wsb,
@@ -224,6 +266,7 @@ def fwd_output(q, state, *, eps=1e-6, simple=False, layout="bhtd", phi="elu1", o
     prob = make_problem(q.shape, q.dtype, eps, simple, layout, phi, dv, scale=scale)
     _state(state, prob, q.device)
     out = _new_like(q, dv) if out is None else _tensor(out, q, "out", dv)
+    _attach_strides(prob, layout, {"q": q, "o": out})
     _check(lib().la_fwd_output(ctypes.byref(prob), _ptr(q), _ptr(state), _ptr(out), _stream(q.device)))
     return out
 
@@ -239,6 +282,7 @@ def fwd(q, k, v, *, eps=1e-6, simple=False, layout="bhtd", phi="elu1", out=None,
     _tensor(v, q, "v", dv)
     prob = make_problem(q.shape, q.dtype, eps, simple, layout, phi, dv, causal, scale)
     out = _new_like(q, dv) if out is None else _tensor(out, q, "out", dv)
+    _attach_strides(prob, layout, {"q": q, "k": k, "v": v, "o": out})
     state = new_state(prob, q.device) if state is None else _state(state, prob, q.device)
     ws, wsb = _ws(prob, q.device, ws)
     _check(lib().la_fwd(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(state),
@@ -259,6 +303,7 @@ def fwd_noalloc(q, k, v, *, out, state, eps=1e-6, simple=False, layout="bhtd", p
     _tensor(v, q, "v", dv)
     prob = make_problem(q.shape, q.dtype, eps, simple, layout, phi, dv, causal, scale)
     _tensor(out, q, "out", dv)
+    _attach_strides(prob, layout, {"q": q, "k": k, "v": v, "o": out})
     _state(state, prob, q.device)
     _check(lib().la_fwd_noalloc(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(state),
                                 _stream(q.device)))
@@ -272,7 +317,8 @@ def bwd_dq(q, do, state, *, eps=1e-6, simple=False, layout="bhtd", phi="elu1", d
     _tensor(do, q, "do", dv)
     prob = make_problem(q.shape, q.dtype, eps, simple, layout, phi, dv, scale=scale)
     _state(state, prob, q.device)
-    dq = torch.empty_like(q) if dq is None else _tensor(dq, q, "dq")
+    dq = _new_like(q, q.shape[-1]) if dq is None else _tensor(dq, q, "dq")
+    _attach_strides(prob, layout, {"q": q, "dout": do, "dq": dq})
     ws, wsb = _ws(prob, q.device, ws)
     _check(lib().la_bwd_dq(ctypes.byref(prob), _ptr(q), _ptr(do), _ptr(state), _ptr(dq), _ptr(ws), wsb,
                            _stream(q.device)))
@@ -285,8 +331,9 @@ def bwd_dkv(k, v, *, eps=1e-6, simple=False, layout="bhtd", phi="elu1", dk=None,
     hv = v.shape[-1] if isinstance(v, torch.Tensor) else None
     _tensor(v, k, "v", hv)
     prob = make_problem(k.shape, k.dtype, eps, simple, layout, phi, hv)
-    dk = torch.empty_like(k) if dk is None else _tensor(dk, k, "dk")
+    dk = _new_like(k, k.shape[-1]) if dk is None else _tensor(dk, k, "dk")
     dv = _new_like(k, hv) if dv is None else _tensor(dv, k, "dv", hv)
+    _attach_strides(prob, layout, {"k": k, "v": v, "dk": dk, "dv": dv})
     ws, wsb = _ws(prob, k.device, ws)
     _check(lib().la_bwd_dkv(ctypes.byref(prob), _ptr(k), _ptr(v), _ptr(dk), _ptr(dv), _ptr(ws), wsb,
                             _stream(k.device)))
@@ -306,9 +353,10 @@ def bwd(q, k, v, do, state=None, *, eps=1e-6, simple=False, layout="bhtd", phi="
     prob = make_problem(q.shape, q.dtype, eps, simple, layout, phi, hv, causal, scale)
     if not causal or state is not None:
         _state(state, prob, q.device)
-    dq = torch.empty_like(q) if dq is None else _tensor(dq, q, "dq")
-    dk = torch.empty_like(q) if dk is None else _tensor(dk, q, "dk")
+    dq = _new_like(q, q.shape[-1]) if dq is None else _tensor(dq, q, "dq")
+    dk = _new_like(q, q.shape[-1]) if dk is None else _tensor(dk, q, "dk")
     dv = _new_like(q, hv) if dv is None else _tensor(dv, q, "dv", hv)
+    _attach_strides(prob, layout, {"q": q, "k": k, "v": v, "dout": do, "dq": dq, "dk": dk, "dv": dv})
     ws, wsb = _ws(prob, q.device, ws)
     _check(lib().la_bwd(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(state),
                         _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws), wsb, _stream(q.device)))
@@ -322,7 +370,6 @@ class _LinearAttention(torch.autograd.Function):
 
     @staticmethod
     def forward(ctx, q, k, v, eps, simple, layout, phi, causal, scale):
-        q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
         o, state = fwd(q, k, v, eps=eps, simple=simple, layout=layout, phi=phi, causal=causal, scale=scale)
         if causal:
             state = None  # the causal backward does not read it
@@ -337,7 +384,9 @@ class _LinearAttention(torch.autograd.Function):
         saved = ctx.saved_tensors
         q, k, v = saved[:3]
         state = saved[3] if len(saved) > 3 else None
-        dq, dk, dv = bwd(q, k, v, do.contiguous(), state, eps=ctx.eps, simple=ctx.simple, layout=ctx.layout,
+        if do.shape[-1] > 1 and do.stride(-1) != 1:
+            do = do.contiguous()
+        dq, dk, dv = bwd(q, k, v, do, state, eps=ctx.eps, simple=ctx.simple, layout=ctx.layout,
                          phi=ctx.phi, causal=ctx.causal, scale=ctx.scale)
         return dq, dk, dv, None, None, None, None, None, None
 

@@ -24,6 +24,10 @@ constexpr int64_t kMaxHeads = int64_t(1) << 24;
 // workgroup may address past the end of its slice.
 constexpr int64_t kMaxHeadBytes = (int64_t(1) << 31) - 1;
 constexpr int64_t kRowSlack = 1024;
+// Largest token count, and the largest caller stride (elements): keeps every
+// product of sizes and strides in the checks far from 64-bit overflow.
+constexpr int64_t kMaxTokens = int64_t(1) << 40;
+constexpr int64_t kMaxStride = int64_t(1) << 46;
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -60,8 +64,12 @@ la_status check_problem(const la_problem* p) {
     if (p->B > kMaxHeads || p->H > kMaxHeads || p->B * p->H > kMaxHeads) return LA_ERR_SHAPE;
     if (p->flags & ~(LA_SIMPLE | LA_LAYOUT_BTHD | LA_PHI_RELU | LA_PHI_IDENTITY | LA_CAUSAL)) return LA_ERR_FLAGS;
     if ((p->flags & LA_PHI_RELU) && (p->flags & LA_PHI_IDENTITY)) return LA_ERR_FLAGS;
+    if (p->strides && (p->flags & LA_LAYOUT_BTHD)) return LA_ERR_FLAGS;
+    if (p->T > kMaxTokens) return LA_ERR_SHAPE;
     const int64_t row_bytes = std::max(p->D, dv_of(p)) * (p->dtype == LA_F32 ? 4 : 2);
-    if (p->flags & LA_LAYOUT_BTHD) {
+    if (p->strides) {
+        // checked per tensor by the calls (check_strides)
+    } else if (p->flags & LA_LAYOUT_BTHD) {
         if (p->H > 0 && p->T + kRowSlack > kMaxHeadBytes / (p->H * row_bytes)) return LA_ERR_SHAPE;
     } else if (p->T > kMaxHeadBytes / row_bytes) {
         return LA_ERR_SHAPE;
@@ -72,6 +80,99 @@ la_status check_problem(const la_problem* p) {
 }
 
 size_t elem_bytes(int dtype) { return dtype == LA_F32 ? 4 : 2; }
+
+// The tensors of the path. Rows of Q, K, dQ, dK hold D elements, rows of V,
+// O, dO, dV hold Dv.
+enum Tensor { kQ, kK, kV, kO, kDO, kDQ, kDK, kDV };
+
+int64_t width(const la_problem* p, Tensor t) {
+    return (t == kV || t == kO || t == kDO || t == kDV) ? dv_of(p) : p->D;
+}
+
+const la_tensor_strides& given_strides(const la_strides* s, Tensor t) {
+    switch (t) {
+        case kQ: return s->q;
+        case kK: return s->k;
+        case kV: return s->v;
+        case kO: return s->o;
+        case kDO: return s->dout;
+        case kDQ: return s->dq;
+        case kDK: return s->dk;
+        default: return s->dv;
+    }
+}
+
+// Where tensor t's rows live: the caller's strides, else the dense layout the
+// flags name.
+la::Layout layout_of(const la_problem* p, Tensor t) {
+    la::Layout L;
+    L.H = p->H > 0 ? p->H : 1;
+    const int64_t W = width(p, t);
+    if (p->strides) {
+        const la_tensor_strides& g = given_strides(p->strides, t);
+        L.sb = g.batch;
+        L.sh = g.head;
+        L.rs = g.token;
+    } else if (p->flags & LA_LAYOUT_BTHD) {
+        L.sb = p->T * p->H * W;
+        L.sh = W;
+        L.rs = p->H * W;
+    } else {
+        L.sb = p->H * p->T * W;
+        L.sh = p->T * W;
+        L.rs = W;
+    }
+    return L;
+}
+
+// Bytes from the tensor's base to the end of its last element (0 when empty);
+// the strides have passed check_strides, so this fits easily in 64 bits.
+size_t span_bytes(const la_problem* p, Tensor t) {
+    if (p->B == 0 || p->H == 0 || p->T == 0) return 0;
+    const la::Layout L = layout_of(p, t);
+    const __int128 e = __int128(p->B - 1) * L.sb + __int128(p->H - 1) * L.sh + __int128(p->T - 1) * L.rs + width(p, t);
+    return size_t(e * __int128(elem_bytes(p->dtype)));
+}
+
+// Caller strides of tensor t (nothing to check for the dense layouts, which
+// check_problem covered): non-negative, 16-byte multiples, rows at least a
+// row wide, one head addressable with 32-bit offsets (kRowSlack rows of
+// padded blocks included), a span well inside 64 bits; and for an output,
+// rows that no other (b, h, t) of the tensor overlaps.
+la_status check_strides(const la_problem* p, Tensor t, bool output) {
+    if (!p->strides) return LA_OK;
+    const la::Layout L = layout_of(p, t);
+    const int64_t W = width(p, t), elt = static_cast<int64_t>(elem_bytes(p->dtype));
+    const int64_t st[3] = {L.rs, L.sh, L.sb};
+    for (int64_t x : st)
+        if (x < 0 || x > kMaxStride || (x * elt) % 16 != 0) return LA_ERR_STRIDE;
+    if (L.rs < W) return LA_ERR_STRIDE;
+    if (L.rs * elt > kMaxHeadBytes / (p->T + kRowSlack)) return LA_ERR_STRIDE;
+    if (!output) return LA_OK;
+    // dimensions of extent > 1 by increasing stride: each stride must clear
+    // the span of those before it, which makes every row its own
+    struct Dim {
+        int64_t extent, stride;
+    } d[3] = {{p->T, L.rs}, {p->H, L.sh}, {p->B, L.sb}};
+    std::sort(d, d + 3, [](const Dim& a, const Dim& b) { return a.stride < b.stride; });
+    __int128 span = W;
+    for (const Dim& x : d) {
+        if (x.extent <= 1) continue;
+        if (__int128(x.stride) < span) return LA_ERR_STRIDE;
+        span += __int128(x.stride) * (x.extent - 1);
+    }
+    return LA_OK;
+}
+
+// check_strides over the tensors of one call: ins read, outs written.
+la_status check_all_strides(const la_problem* p, std::initializer_list<Tensor> ins,
+                            std::initializer_list<Tensor> outs) {
+    for (Tensor t : ins)
+        if (la_status st = check_strides(p, t, false); st != LA_OK) return st;
+    for (Tensor t : outs)
+        if (la_status st = check_strides(p, t, true); st != LA_OK) return st;
+    return LA_OK;
+}
 
 // What the causal forward supports, on a problem check_problem accepted.
 la_status check_causal(const la_problem* p) {
@@ -109,16 +210,14 @@ la::Plan make_plan(const la_problem* p) {
     const float qscale = p->scale == 0.f ? 1.f : p->scale;
     pl.eps = pl.simple ? qscale : p->eps / qscale;
     pl.fm = (p->flags & LA_PHI_RELU) ? 1 : (p->flags & LA_PHI_IDENTITY) ? 2 : 0;
-    pl.lay.H = p->H > 0 ? p->H : 1;
-    if (p->flags & LA_LAYOUT_BTHD) {
-        pl.lay.sb = p->T * p->H * p->D;
-        pl.lay.sh = p->D;
-        pl.lay.rs = p->H * p->D;
-    } else {
-        pl.lay.sb = p->H * p->T * p->D;
-        pl.lay.sh = p->T * p->D;
-        pl.lay.rs = p->D;
-    }
+    pl.lay.q = layout_of(p, kQ);
+    pl.lay.k = layout_of(p, kK);
+    pl.lay.v = layout_of(p, kV);
+    pl.lay.o = layout_of(p, kO);
+    pl.lay.dout = layout_of(p, kDO);
+    pl.lay.dq = layout_of(p, kDQ);
+    pl.lay.dk = layout_of(p, kDK);
+    pl.lay.dv = layout_of(p, kDV);
     const la::KernelSet* ks = kernel_set(pl.dtype, pl.DK);
     split(pl.BH, pl.T, ks->split_config(la::kStepState, pl.DV), pl.P, pl.L);
     split(pl.BH, pl.T, ks->split_config(la::kStepBwdQ, pl.DV), pl.PB, pl.LB);
@@ -204,6 +303,7 @@ const char* la_status_str(int s) {
         case LA_ERR_ALIGN: return "LA_ERR_ALIGN: tensors need 16-byte, workspace 256-byte alignment";
         case LA_ERR_ALIAS: return "LA_ERR_ALIAS: an output overlaps another buffer";
         case LA_ERR_DEVICE: return "LA_ERR_DEVICE: HIP launch error";
+        case LA_ERR_STRIDE: return "LA_ERR_STRIDE: a stride is negative, not a 16-byte multiple, or rows overlap";
         case LA_ERR_SCRATCH: return "LA_ERR_SCRATCH: the problem needs more than LA_NOALLOC_SCRATCH_BYTES of scratch";
         default: return "unknown la_status";
     }
@@ -225,12 +325,11 @@ int la_fwd_state(const la_problem* p, const void* k, const void* v, void* state,
     if (st != LA_OK) return st;
     if ((st = check_not_causal(p)) != LA_OK) return st;
     const la::Plan pl = make_plan(p);
-    const size_t tk = size_t(pl.BH * pl.T * pl.DK) * elem_bytes(pl.dtype);
-    const size_t tv = size_t(pl.BH * pl.T * pl.DV) * elem_bytes(pl.dtype);
+    if ((st = check_all_strides(p, {kK, kV}, {})) != LA_OK) return st;
     const size_t sb = la_state_bytes(p);
     if (pl.BH > 0 && !state) return LA_ERR_NULL;
     if (ws_bytes < pl.ws_bytes) return LA_ERR_WORKSPACE;
-    st = check_buffers({{k, tk}, {v, tv}}, {{state, sb}, {ws, pl.ws_bytes}}, {16, 16}, {16, 256});
+    st = check_buffers({{k, span_bytes(p, kK)}, {v, span_bytes(p, kV)}}, {{state, sb}, {ws, pl.ws_bytes}}, {16, 16}, {16, 256});
     if (st != LA_OK) return st;
     if (pl.BH == 0) return LA_OK;
     return device_status(kernel_set(pl.dtype, pl.DK)->fwd_state(pl, k, v, static_cast<float*>(state), ws,
@@ -242,12 +341,11 @@ int la_fwd_output(const la_problem* p, const void* q, const void* state, void* o
     if (st != LA_OK) return st;
     if ((st = check_not_causal(p)) != LA_OK) return st;
     const la::Plan pl = make_plan(p);
-    const size_t tk = size_t(pl.BH * pl.T * pl.DK) * elem_bytes(pl.dtype);
-    const size_t tv = size_t(pl.BH * pl.T * pl.DV) * elem_bytes(pl.dtype);
+    if ((st = check_all_strides(p, {kQ}, {kO})) != LA_OK) return st;
     const size_t sb = la_state_bytes(p);
-    st = check_buffers({{q, tk}, {state, sb}}, {{o, tv}}, {16, 16}, {16});
+    st = check_buffers({{q, span_bytes(p, kQ)}, {state, sb}}, {{o, span_bytes(p, kO)}}, {16, 16}, {16});
     if (st != LA_OK) return st;
-    if (tk == 0) return LA_OK;
+    if (pl.BH == 0 || pl.T == 0) return LA_OK;
     return device_status(kernel_set(pl.dtype, pl.DK)->fwd_output(pl, q, static_cast<const float*>(state), o,
                                                static_cast<hipStream_t>(stream)));
 }
@@ -259,11 +357,10 @@ int la_fwd(const la_problem* p, const void* q, const void* k, const void* v, voi
     const bool causal = (p->flags & LA_CAUSAL) != 0;
     if (causal && (st = check_causal(p)) != LA_OK) return st;
     const la::Plan pl = make_plan(p);
-    const size_t tk = size_t(pl.BH * pl.T * pl.DK) * elem_bytes(pl.dtype);
-    const size_t tv = size_t(pl.BH * pl.T * pl.DV) * elem_bytes(pl.dtype);
+    if ((st = check_all_strides(p, {kQ, kK, kV}, {kO})) != LA_OK) return st;
     const size_t sb = la_state_bytes(p);
     if (ws_bytes < pl.ws_bytes) return LA_ERR_WORKSPACE;
-    st = check_buffers({{q, tk}, {k, tk}, {v, tv}}, {{o, tv}, {state, state ? sb : 0}, {ws, pl.ws_bytes}},
+    st = check_buffers({{q, span_bytes(p, kQ)}, {k, span_bytes(p, kK)}, {v, span_bytes(p, kV)}}, {{o, span_bytes(p, kO)}, {state, state ? sb : 0}, {ws, pl.ws_bytes}},
                        {16, 16, 16}, {16, 16, 256});
     if (st != LA_OK) return st;
     if (pl.BH == 0) return LA_OK;
@@ -272,7 +369,7 @@ int la_fwd(const la_problem* p, const void* q, const void* k, const void* v, voi
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (causal) return device_status(kernel_set(pl.dtype, pl.DK)->fwd_causal(pl, q, k, v, o, stp, ws, s));
     st = device_status(kernel_set(pl.dtype, pl.DK)->fwd_state(pl, k, v, stp, ws, s));
-    if (st != LA_OK || tk == 0) return st;
+    if (st != LA_OK || pl.T == 0) return st;
     return device_status(kernel_set(pl.dtype, pl.DK)->fwd_output(pl, q, stp, o, s));
 }
 
@@ -284,11 +381,10 @@ int la_fwd_noalloc(const la_problem* p, const void* q, const void* k, const void
     const bool causal = (p->flags & LA_CAUSAL) != 0;
     if (causal && (st = check_causal(p)) != LA_OK) return st;
     const la::Plan pl = make_plan(p);
-    const size_t tk = size_t(pl.BH * pl.T * pl.DK) * elem_bytes(pl.dtype);
-    const size_t tv = size_t(pl.BH * pl.T * pl.DV) * elem_bytes(pl.dtype);
+    if ((st = check_all_strides(p, {kQ, kK, kV}, {kO})) != LA_OK) return st;
     const size_t sb = la_state_bytes(p);
     if (pl.BH > 0 && !state) return LA_ERR_NULL;
-    st = check_buffers({{q, tk}, {k, tk}, {v, tv}}, {{o, tv}, {state, sb}}, {16, 16, 16}, {16, 16});
+    st = check_buffers({{q, span_bytes(p, kQ)}, {k, span_bytes(p, kK)}, {v, span_bytes(p, kV)}}, {{o, span_bytes(p, kO)}, {state, sb}}, {16, 16, 16}, {16, 16});
     if (st != LA_OK) return st;
     // the forward's only scratch: the split partials, at offset 0 (off_part)
     const size_t need = pl.P > 1 ? size_t(pl.BH) * pl.P * (size_t(pl.DK) * pl.DV + pl.DK) * 4 : 0;
@@ -300,7 +396,7 @@ int la_fwd_noalloc(const la_problem* p, const void* q, const void* k, const void
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (causal) return device_status(kernel_set(pl.dtype, pl.DK)->fwd_causal(pl, q, k, v, o, stp, ws, s));
     st = device_status(kernel_set(pl.dtype, pl.DK)->fwd_state(pl, k, v, stp, ws, s));
-    if (st != LA_OK || tk == 0) return st;
+    if (st != LA_OK || pl.T == 0) return st;
     return device_status(kernel_set(pl.dtype, pl.DK)->fwd_output(pl, q, stp, o, s));
 }
 
@@ -310,15 +406,14 @@ int la_bwd_dq(const la_problem* p, const void* q, const void* dout, const void* 
     if (st != LA_OK) return st;
     if ((st = check_not_causal(p)) != LA_OK) return st;
     const la::Plan pl = make_plan(p);
-    const size_t tk = size_t(pl.BH * pl.T * pl.DK) * elem_bytes(pl.dtype);
-    const size_t tv = size_t(pl.BH * pl.T * pl.DV) * elem_bytes(pl.dtype);
+    if ((st = check_all_strides(p, {kQ, kDO}, {kDQ})) != LA_OK) return st;
     const size_t sb = la_state_bytes(p);
     if (pl.BH > 0 && !state) return LA_ERR_NULL;
     if (ws_bytes < pl.ws_bytes) return LA_ERR_WORKSPACE;
-    st = check_buffers({{q, tk}, {dout, tv}, {state, sb}}, {{dq, tk}, {ws, pl.ws_bytes}}, {16, 16, 16},
+    st = check_buffers({{q, span_bytes(p, kQ)}, {dout, span_bytes(p, kDO)}, {state, sb}}, {{dq, span_bytes(p, kDQ)}, {ws, pl.ws_bytes}}, {16, 16, 16},
                        {16, 256});
     if (st != LA_OK) return st;
-    if (tk == 0) return LA_OK;
+    if (pl.BH == 0 || pl.T == 0) return LA_OK;
     return device_status(kernel_set(pl.dtype, pl.DK)->bwd_dq(pl, q, dout, static_cast<const float*>(state), dq, ws,
                                            static_cast<hipStream_t>(stream)));
 }
@@ -329,14 +424,15 @@ int la_bwd_dkv(const la_problem* p, const void* k, const void* v, void* dk, void
     if (st != LA_OK) return st;
     if ((st = check_not_causal(p)) != LA_OK) return st;
     const la::Plan pl = make_plan(p);
-    const size_t tk = size_t(pl.BH * pl.T * pl.DK) * elem_bytes(pl.dtype);
-    const size_t tv = size_t(pl.BH * pl.T * pl.DV) * elem_bytes(pl.dtype);
+    if ((st = check_all_strides(p, {kK, kV}, {kDK, kDV})) != LA_OK) return st;
     if (ws_bytes < pl.ws_bytes) return LA_ERR_WORKSPACE;
-    if (tk && !ws) return LA_ERR_NULL;
-    st = check_buffers({{k, tk}, {v, tv}, {ws, tk ? pl.ws_bytes : 0}}, {{dk, tk}, {dv, tv}},
+    const bool work = pl.BH > 0 && pl.T > 0;
+    if (work && !ws) return LA_ERR_NULL;
+    st = check_buffers({{k, span_bytes(p, kK)}, {v, span_bytes(p, kV)}, {ws, work ? pl.ws_bytes : 0}},
+                       {{dk, span_bytes(p, kDK)}, {dv, span_bytes(p, kDV)}},
                        {16, 16, 256}, {16, 16});
     if (st != LA_OK) return st;
-    if (tk == 0) return LA_OK;
+    if (!work) return LA_OK;
     return device_status(kernel_set(pl.dtype, pl.DK)->bwd_dkv(pl, k, v, dk, dv, ws, static_cast<hipStream_t>(stream)));
 }
 
@@ -347,16 +443,15 @@ int la_bwd(const la_problem* p, const void* q, const void* k, const void* v, con
     const bool causal = (p->flags & LA_CAUSAL) != 0;
     if (causal && (st = check_causal(p)) != LA_OK) return st;
     const la::Plan pl = make_plan(p);
-    const size_t tk = size_t(pl.BH * pl.T * pl.DK) * elem_bytes(pl.dtype);
-    const size_t tv = size_t(pl.BH * pl.T * pl.DV) * elem_bytes(pl.dtype);
+    if ((st = check_all_strides(p, {kQ, kK, kV, kDO}, {kDQ, kDK, kDV})) != LA_OK) return st;
     const size_t sb = causal ? 0 : la_state_bytes(p);  // the causal backward does not read the state
     if (pl.BH > 0 && !state && !causal) return LA_ERR_NULL;
     if (ws_bytes < pl.ws_bytes) return LA_ERR_WORKSPACE;
-    st = check_buffers({{q, tk}, {k, tk}, {v, tv}, {dout, tv}, {state, sb}},
-                       {{dq, tk}, {dk, tk}, {dv, tv}, {ws, pl.ws_bytes}}, {16, 16, 16, 16, 16},
+    st = check_buffers({{q, span_bytes(p, kQ)}, {k, span_bytes(p, kK)}, {v, span_bytes(p, kV)}, {dout, span_bytes(p, kDO)}, {state, sb}},
+                       {{dq, span_bytes(p, kDQ)}, {dk, span_bytes(p, kDK)}, {dv, span_bytes(p, kDV)}, {ws, pl.ws_bytes}}, {16, 16, 16, 16, 16},
                        {16, 16, 16, 256});
     if (st != LA_OK) return st;
-    if (tk == 0) return LA_OK;
+    if (pl.BH == 0 || pl.T == 0) return LA_OK;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (causal)
         return device_status(kernel_set(pl.dtype, pl.DK)->bwd_causal(pl, q, k, v, dout, dq, dk, dv, ws, s));

@@ -7,15 +7,21 @@
 
 namespace la {
 
-// Where the rows of head bh = b H + h live, in elements: the head's row 0 at
-// (bh / H) sb + (bh % H) sh, consecutive rows rs apart. Given for the Q-side
-// tensors (Q, K, dQ, dK: rows of DK elements); the V-side tensors (V, O, dO,
-// dV) have the same layout with rows of DV elements, every stride scaled by
-// DV / DK.
+// Where the rows of head bh = b H + h of one tensor live, in elements: the
+// head's row 0 at (bh / H) sb + (bh % H) sh, consecutive rows rs apart, the
+// row's D elements contiguous.
 //   [B, H, T, D]: sb = H T D, sh = T D, rs = D
 //   [B, T, H, D]: sb = T H D, sh = D,   rs = H D
+//   strided views: the caller's batch, head and token strides
 struct Layout {
     int64_t H = 1, sb = 0, sh = 0, rs = 0;
+};
+
+// The layout of each tensor of a call: rows of Q, K, dQ, dK hold DK elements,
+// rows of V, O, dO, dV hold DV. Dense [B, H, T, D] or [B, T, H, D] unless the
+// caller gave strides.
+struct Layouts {
+    Layout q, k, v, o, dout, dq, dk, dv;
 };
 
 // Work split for one problem. Every field is a pure function of
@@ -29,7 +35,7 @@ struct Plan {
     // Either way the kernels' one float folds the optional query scale.
     float eps = 0.f;
     int fm = 0;  // feature map: 0 elu + 1, 1 relu, 2 identity
-    Layout lay;
+    Layouts lay;
     // state reduction (fwd steps 1-3): P slices of L tokens per head
     int P = 1;
     int64_t L = 0;

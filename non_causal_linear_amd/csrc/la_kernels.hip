@@ -41,9 +41,11 @@
 // permuted so that the same lane receives D/4 contiguous output features of
 // that token, which it stores contiguously.
 //
-// Tensors are [B, H, T, D] (or [B, T, H, D]) row-major. The work split is a
-// pure function of the shape and there are no floating-point atomics, so
-// results are bit-identical across runs.
+// Every tensor has its own layout (Layouts): batch, head and token strides in
+// elements, dense [B, H, T, D] or [B, T, H, D] unless the caller passed
+// strides; a row's D features are contiguous. The work split is a pure
+// function of the shape and there are no floating-point atomics, so results
+// are bit-identical across runs.
 
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -105,6 +107,17 @@ template <> __device__ __forceinline__ f32x4 mma_k16<f16>(i16x4 a, i16x4 b, f32x
 template <> __device__ __forceinline__ f32x4 mma_k16<bf16>(i16x4 a, i16x4 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
 }
+
+// Index of this thread's wave in the workgroup, as a value the compiler knows
+// is the same on every lane of the wave (it lives in a scalar register).
+// Branches on it, or on block indices derived from it, then compile to scalar
+// branches. Computed as threadIdx.x / 64, the compiler cannot tell that it is
+// wave-uniform and lowers such branches by masking lanes; the register
+// allocator has then been seen to save a live vector register to an
+// accumulation register inside one arm of such a branch and restore it after
+// the join on every lane, which corrupts that register on the waves that took
+// the other arm (wrong results, no error).
+__device__ __forceinline__ int wave_index() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
 // Keeps the compiler from moving instructions across this point. Used between
 // the load batches of a prefetch pipeline: the vector-memory counter retires
@@ -207,23 +220,6 @@ struct HeadBuf {
 __device__ __forceinline__ int64_t head_offset(const Layout& L, int64_t bh) {
     const int64_t b = (int)bh / (int)L.H;
     return b * L.sb + (bh - b * L.H) * L.sh;
-}
-
-// The layout of the V-side tensors (V, O, dO, dV: rows of DV elements) from
-// that of the Q-side ones (rows of DK elements): every stride is a multiple
-// of the row size, so the rescaling is exact, and the identity when DK = DV.
-template <int DK, int DV>
-__device__ __forceinline__ Layout v_layout(const Layout& L) {
-    if constexpr (DK == DV) {
-        return L;
-    } else {
-        Layout r;
-        r.H = L.H;
-        r.sb = L.sb / DK * DV;
-        r.sh = L.sh / DK * DV;
-        r.rs = L.rs / DK * DV;
-        return r;
-    }
 }
 
 template <typename T>
@@ -381,7 +377,7 @@ template <int NW = kWaves>
 __device__ __forceinline__ float block_max(float v, float* red) {
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
-    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+    if ((threadIdx.x & 63) == 0) red[wave_index()] = v;
     __syncthreads();
     float x[NW];
 #pragma unroll
@@ -398,7 +394,7 @@ template <int NW = kWaves>
 __device__ __forceinline__ float block_sum(float v, float* red) {
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
-    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+    if ((threadIdx.x & 63) == 0) red[wave_index()] = v;
     __syncthreads();
     float x[NW];
 #pragma unroll
@@ -509,7 +505,7 @@ __device__ __forceinline__ StagedState<DK, DV> stage_state(const float* __restri
                                                            const float* __restrict__ z, float* s, float* red) {
     constexpr int PER = DK * DV / 4 / NT, LD = StagedState<DK, DV>::kLD, NW = NT / 64;
     static_assert(PER * 4 * NT == DK * DV && DK / 4 <= NT, "thread count must tile the matrix");
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wave = wave_index();
     float4 v[PER];
 #pragma unroll
     for (int i = 0; i < PER; ++i) v[i] = reinterpret_cast<const float4*>(M)[tid + i * NT];
@@ -594,9 +590,9 @@ struct StateShape {
 template <typename T, int DK, int DV, int FM>
 __global__ __launch_bounds__(kThreads) void fwd_state_kernel(
     const T* __restrict__ k, const T* __restrict__ v, float* __restrict__ stS,
-    float* __restrict__ stz, float* __restrict__ part, int64_t T_, const Layout lay, int P, int64_t L) {
+    float* __restrict__ stz, float* __restrict__ part, int64_t T_, const Layouts lay, int P, int64_t L) {
     using Sh = StateShape<T, DK, DV>;
-    const Layout lk = lay, lv = v_layout<DK, DV>(lay);
+    const Layout lk = lay.k, lv = lay.v;
     constexpr int EPC = Sh::kEPC, TT = Sh::kTT, LDT = Sh::kLDT, CK = Sh::kCK, CV = Sh::kCV, NK = Sh::kNK,
                   NV = Sh::kNV, NI = Sh::kNI, NJ = Sh::kNJ, KS = Sh::kKS;
     __shared__ __attribute__((aligned(16))) T sK[DK * LDT];
@@ -605,7 +601,7 @@ __global__ __launch_bounds__(kThreads) void fwd_state_kernel(
     const int wid = xcd_remap(blockIdx.x, gridDim.x);
     const int64_t bh = wid / P;
     const int p = wid % P;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wave = wave_index();
     const int m = lane & 15, grp = lane >> 4;
     const int wi = wave & 1, wj = wave >> 1;
     const int64_t t0 = (int64_t)p * L;
@@ -726,7 +722,7 @@ struct StateW64 {
 template <typename T, int FM>
 __global__ __launch_bounds__(kThreads, 2) void fwd_state_w64_kernel(
     const T* __restrict__ k, const T* __restrict__ v, float* __restrict__ stS,
-    float* __restrict__ stz, float* __restrict__ part, int64_t T_, const Layout lay, int P,
+    float* __restrict__ stz, float* __restrict__ part, int64_t T_, const Layouts lay, int P,
     int64_t L) {
     constexpr int D = 64, NB = 4, E = D * D + D;
     constexpr int STEP = StateW64::kStep, LDR = StateW64::kLDR, TILE = StateW64::kTile;
@@ -737,7 +733,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_state_w64_kernel(
     const int wid = xcd_remap(blockIdx.x, gridDim.x);
     const int64_t bh = wid / P;
     const int p = wid % P;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wave = wave_index();
     const int m = lane & 15, grp = lane >> 4;
     const int c = lane & 7, rg = lane >> 3;
     const int64_t t0 = (int64_t)p * L;
@@ -761,16 +757,16 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_state_w64_kernel(
     // phi(k) is masked for them. Steps go in rotated order, two per wave and
     // turn, with no early exit (an exit makes the compiler wait for every
     // load in flight where the paths join).
-    const HeadBuf bk = slice_buf(k, lay, bh, D, t0, t1), bv = slice_buf(v, lay, bh, D, t0, t1);
+    const HeadBuf bk = slice_buf(k, lay.k, bh, D, t0, t1), bv = slice_buf(v, lay.v, bh, D, t0, t1);
     constexpr int NS = StateW64::kStages;
     const Rotation rot(nsteps, NS * kWaves, wid);
     auto issue = [&](Stage& st, int step) {
         const int ps = rot(step);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int off = buf_off<T>((int64_t)ps * STEP + rg + 8 * r, lay.rs, 8 * c);
-            st.k[r] = buf_load16<kNonTemporal>(bk, off);
-            st.v[r] = buf_load16<kNonTemporal>(bv, off);
+            const int64_t row = (int64_t)ps * STEP + rg + 8 * r;
+            st.k[r] = buf_load16<kNonTemporal>(bk, buf_off<T>(row, lay.k.rs, 8 * c));
+            st.v[r] = buf_load16<kNonTemporal>(bv, buf_off<T>(row, lay.v.rs, 8 * c));
         }
     };
     // phi on K (fp32, rounded to T), padded rows zeroed after phi, row-major to LDS
@@ -911,7 +907,7 @@ struct StateTile {
 template <typename T, int DK, int DV, int FM>
 __global__ __launch_bounds__(kThreads, 2) void fwd_state_tile_kernel(
     const T* __restrict__ k, const T* __restrict__ v, float* __restrict__ stS,
-    float* __restrict__ stz, float* __restrict__ part, int64_t T_, const Layout lay, int P,
+    float* __restrict__ stz, float* __restrict__ part, int64_t T_, const Layouts lay, int P,
     int64_t L) {
     using Sh = StateTile<DK, DV>;
     constexpr int TT = Sh::kTile, LDK = Sh::kLDK, LDV = Sh::kLDV, NI = Sh::kNI, NJ = Sh::kNJ;
@@ -927,14 +923,14 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_state_tile_kernel(
     const int wid = xcd_remap(blockIdx.x, gridDim.x);
     const int64_t bh = wid / P;
     const int p = wid % P;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wave = wave_index();
     const int m = lane & 15, grp = lane >> 4;
     const int wi = wave & 1, wj = wave >> 1;
     const int64_t t0 = (int64_t)p * L;
     const int64_t t1 = min(t0 + L, T_);
     const int64_t len = t1 - t0;
     const int ntiles = (int)(len > 0 ? (len + TT - 1) / TT : 0);
-    const Layout lk = lay, lv = v_layout<DK, DV>(lay);
+    const Layout lk = lay.k, lv = lay.v;
 
     f32x4 acc[NI][NJ + 1];  // column NJ: z (waves of column half 0)
 #pragma unroll
@@ -1121,7 +1117,7 @@ __device__ __forceinline__ Frag<T> build_zfrag(const float* __restrict__ z, int 
 template <typename T, int NF, int NW = kWaves, typename Make>
 __device__ __forceinline__ void build_frags(Frag<T>* sA, Make make) {
     constexpr int PER = (NF + NW - 1) / NW;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, wave = wave_index();
     Frag<T> fr[PER];
 #pragma unroll
     for (int i = 0; i < PER; ++i) fr[i] = make(min(wave + NW * i, NF - 1));
@@ -1141,9 +1137,9 @@ __device__ __forceinline__ void build_frags(Frag<T>* sA, Make make) {
 template <typename T, int DK, int DV, bool SIMPLE, int FM>
 __global__ __launch_bounds__((StreamShape<T, DK, DV>::kThreads), (StreamShape<T, DK, DV>::kOutMinBlocks)) void fwd_output_kernel(
     const T* __restrict__ q, const float* __restrict__ stS, const float* __restrict__ stz,
-    T* __restrict__ o, int64_t T_, const Layout lay, int NQ, int64_t LQ, float eps) {
+    T* __restrict__ o, int64_t T_, const Layouts lay, int NQ, int64_t LQ, float eps) {
     using Sh = StreamShape<T, DK, DV>;
-    const Layout lk = lay, lv = v_layout<DK, DV>(lay);
+    const Layout lk = lay.q, lv = lay.o;
     constexpr int FK = Sh::kFK, FV = Sh::kFV, NB = Sh::kNBV, KS = Sh::kKSK, U = Sh::kU, NW = Sh::kWaves,
                   NT = Sh::kThreads;
     constexpr int NFS = NB * KS;             // S fragments
@@ -1164,7 +1160,7 @@ __global__ __launch_bounds__((StreamShape<T, DK, DV>::kThreads), (StreamShape<T,
     const int ch = wid % NQ;
     const int64_t c0 = (int64_t)ch * LQ;
     const int64_t c1 = min(c0 + LQ, T_);
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wave = wave_index();
     const int m = lane & 15, grp = lane >> 4;
     const float* S = stS + bh * DK * DV;
     const float* z = stz + bh * DK;
@@ -1305,10 +1301,10 @@ template <typename T, int DK, int DV, bool SIMPLE, int FM>
 __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(
     const T* __restrict__ q, const T* __restrict__ dout, const float* __restrict__ stS,
     const float* __restrict__ stz, T* __restrict__ dq, float* __restrict__ part,
-    float* __restrict__ dS_out, float* __restrict__ dz_out, int64_t T_, const Layout lay, int PB,
+    float* __restrict__ dS_out, float* __restrict__ dz_out, int64_t T_, const Layouts lay, int PB,
     int64_t LB, float eps) {
     using Sh = StreamShape<T, DK, DV>;
-    const Layout lk = lay, lv = v_layout<DK, DV>(lay);
+    const Layout lk = lay.q, lv = lay.dout, lg = lay.dq;
     using Bq = BwdQShape<T, DK, DV>;
     constexpr int FK = Sh::kFK, FV = Sh::kFV, NBK = Sh::kNBK, KSK = Sh::kKSK, KSV = Sh::kKSV;
     constexpr int U = Bq::kU, G = Bq::kG, LDT = Bq::kLDT;
@@ -1326,7 +1322,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(
     const int p = wid % PB;
     const int64_t t0 = (int64_t)p * LB;
     const int64_t t1 = min(t0 + LB, T_);
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wave = wave_index();
     const int m = lane & 15, grp = lane >> 4;
     const int wi = wave & 1, wj = wave >> 1;
     const float* S = stS + bh * DK * DV;
@@ -1372,7 +1368,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(
 
     const T* qh = q + head_offset(lk, bh);
     const T* dh = dout + head_offset(lv, bh);
-    T* gh = dq + head_offset(lk, bh);
+    T* gh = dq + head_offset(lg, bh);
     for (int64_t base = t0; base < t1; base += G) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -1441,7 +1437,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(
                 float out[FK];
 #pragma unroll
                 for (int o = 0; o < FK; ++o) out[o] = dqt[o] * dphi_of<FM>(qt[o]);
-                store_row<T, FK>(gh + t * lk.rs + FK * grp, out);
+                store_row<T, FK>(gh + t * lg.rs + FK * grp, out);
             }
             const int col = (wave * U + u) * 16 + m;
 #pragma unroll
@@ -1527,7 +1523,7 @@ template <typename T, bool SIMPLE, int FM>
 __global__ __launch_bounds__(kThreads, 2) void bwd_dq_w64_kernel(
     const T* __restrict__ q, const T* __restrict__ dout, const float* __restrict__ stS,
     const float* __restrict__ stz, T* __restrict__ dq, float* __restrict__ part,
-    float* __restrict__ dS_out, float* __restrict__ dz_out, int64_t T_, const Layout lay, int PB,
+    float* __restrict__ dS_out, float* __restrict__ dz_out, int64_t T_, const Layouts lay, int PB,
     int64_t LB, float eps) {
     constexpr int D = 64, F = 16, NB = 4, KS = 2, STEP = BwdQW64::kStep, E = D * D + D;
     constexpr int LDR = 88;                   // 176-byte rows: 64 features + the beta column block
@@ -1549,7 +1545,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_w64_kernel(
     const int64_t t0 = (int64_t)p * LB;
     const int64_t t1 = min(t0 + LB, T_);
     const int nsteps = (int)(t1 > t0 ? (t1 - t0 + STEP - 1) / STEP : 0);
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wave = wave_index();
     const int m = lane & 15, grp = lane >> 4;
     const float* S = stS + bh * D * D;
     const float* z = stz + bh * D;
@@ -1567,15 +1563,16 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_w64_kernel(
     // Rows past the slice end load as zeros (dO = 0 gives u = 0, r = 0,
     // beta = 0, so such rows add nothing to dS or dz) and their dQ stores are
     // dropped. Rows are counted from t0.
-    const HeadBuf bq = slice_buf(q, lay, bh, D, t0, t1), bd = slice_buf(dout, lay, bh, D, t0, t1),
-                  bdq = slice_buf(dq, lay, bh, D, t0, t1);
+    const HeadBuf bq = slice_buf(q, lay.q, bh, D, t0, t1), bd = slice_buf(dout, lay.dout, bh, D, t0, t1),
+                  bdq = slice_buf(dq, lay.dq, bh, D, t0, t1);
     const Rotation rot(nsteps, BwdQW64::kStages * kWaves, wid);
     auto issue = [&](Stage& st, int step) {
-        const int off = buf_off<T>((int64_t)rot(step) * STEP + m, lay.rs, F * grp);
-        st.q[0] = __builtin_amdgcn_raw_buffer_load_b128(bq.rsrc, off, 0, 0);
-        st.q[1] = __builtin_amdgcn_raw_buffer_load_b128(bq.rsrc, off + 16, 0, 0);
-        st.d[0] = __builtin_amdgcn_raw_buffer_load_b128(bd.rsrc, off, 0, 0);
-        st.d[1] = __builtin_amdgcn_raw_buffer_load_b128(bd.rsrc, off + 16, 0, 0);
+        const int64_t row = (int64_t)rot(step) * STEP + m;
+        const int oq = buf_off<T>(row, lay.q.rs, F * grp), od = buf_off<T>(row, lay.dout.rs, F * grp);
+        st.q[0] = __builtin_amdgcn_raw_buffer_load_b128(bq.rsrc, oq, 0, 0);
+        st.q[1] = __builtin_amdgcn_raw_buffer_load_b128(bq.rsrc, oq + 16, 0, 0);
+        st.d[0] = __builtin_amdgcn_raw_buffer_load_b128(bd.rsrc, od, 0, 0);
+        st.d[1] = __builtin_amdgcn_raw_buffer_load_b128(bd.rsrc, od + 16, 0, 0);
     };
     // The first two steps' loads are issued before the prologue, which they
     // overlap (with no steps they read zeros and the loop below does not run).
@@ -1696,7 +1693,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_w64_kernel(
             Row<T, F> out;
 #pragma unroll
             for (int o = 0; o < F; ++o) out.e[o] = static_cast<T>(dqt[o] * dph[o]);
-            store_tile_rows<T, D>(sO, out, bdq, (int64_t)rot(step) * STEP, lay.rs);
+            store_tile_rows<T, D>(sO, out, bdq, (int64_t)rot(step) * STEP, lay.dq.rs);
         }
         wave_lds_sync();
         i16x4 a[NB];
@@ -1803,7 +1800,7 @@ template <typename T, int DK, int DV, bool SIMPLE, int FM>
 __global__ __launch_bounds__((BwdQTile<DK, DV>::kThreads), (BwdQTile<DK, DV>::kMinBlocks)) void bwd_dq_tile_kernel(
     const T* __restrict__ q, const T* __restrict__ dout, const float* __restrict__ stS,
     const float* __restrict__ stz, T* __restrict__ dq, float* __restrict__ part,
-    float* __restrict__ dS_out, float* __restrict__ dz_out, int64_t T_, const Layout lay, int PB,
+    float* __restrict__ dS_out, float* __restrict__ dz_out, int64_t T_, const Layouts lay, int PB,
     int64_t LB, float eps) {
     using Sh = BwdQTile<DK, DV>;
     constexpr int FK = DK / 4, FV = DV / 4, NBK = DK / 16, NBV = DV / 16, KSK = DK / 32, KSV = DV / 32;
@@ -1831,9 +1828,9 @@ __global__ __launch_bounds__((BwdQTile<DK, DV>::kThreads), (BwdQTile<DK, DV>::kM
     const int64_t t0 = (int64_t)p * LB;
     const int64_t t1 = min(t0 + LB, T_);
     const int nrounds = (int)(t1 > t0 ? (t1 - t0 + RT - 1) / RT : 0);
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wave = wave_index();
     const int m = lane & 15, grp = lane >> 4;
-    const Layout lk = lay, lv = v_layout<DK, DV>(lay);
+    const Layout lk = lay.q, lv = lay.dout;
     const float* S = stS + bh * DK * DV;
     const float* z = stz + bh * DK;
     Frag<T>* sA = reinterpret_cast<Frag<T>*>(smem);
@@ -1845,7 +1842,7 @@ __global__ __launch_bounds__((BwdQTile<DK, DV>::kThreads), (BwdQTile<DK, DV>::kM
         u32x4 q[NQK], d[NQV];
     };
     const HeadBuf bq = slice_buf(q, lk, bh, DK, t0, t1), bd = slice_buf(dout, lv, bh, DV, t0, t1),
-                  bdq = slice_buf(dq, lk, bh, DK, t0, t1);
+                  bdq = slice_buf(dq, lay.dq, bh, DK, t0, t1);
     const Rotation rot(nrounds, Sh::kStages, wid);
     auto issue = [&](Stage& st, int round) {
         const int64_t row = (int64_t)rot(round) * RT + wave * STEP + m;
@@ -1968,7 +1965,7 @@ __global__ __launch_bounds__((BwdQTile<DK, DV>::kThreads), (BwdQTile<DK, DV>::kM
             // staged through this wave's own rows of the A tile (16 rows of
             // DK + 8 elements fit in its 16 rows of LDA), which are written
             // with A right after
-            store_tile_rows<T, DK>(tA + wave * STEP * LDA, out, bdq, (int64_t)rot(round) * RT + wave * STEP, lk.rs);
+            store_tile_rows<T, DK>(tA + wave * STEP * LDA, out, bdq, (int64_t)rot(round) * RT + wave * STEP, lay.dq.rs);
         }
         {
             Row<T, FK> rq;
@@ -2024,13 +2021,20 @@ __global__ __launch_bounds__((BwdQTile<DK, DV>::kThreads), (BwdQTile<DK, DV>::kM
 // dphi(k_t) = dS v_t + dz and dv_t = dS^T phi(k_t): both are products of a
 // fixed D x D matrix with a token's row, so each is one set of MFMA blocks with
 // dS (or dS^T) as the A operand and the loaded K/V quarter rows as B.
+// The NK workgroups of a head share its tokens by rounds of 16 NW tokens:
+// workgroup ch takes rounds ch, ch + NK, ch + 2 NK, ..., so at any time the
+// head's workgroups stream neighbouring rounds of its four tensors, and the
+// heads' streams advance side by side. (Contiguous chunks per workgroup, the
+// other choice, keep every workgroup on a separate stretch of all four
+// tensors at once; how those concurrent streams fall on DRAM channels then
+// depends on where the buffers sit, and the kernel ran 5-10% slower.)
 template <typename T, int DK, int DV, bool SIMPLE, int FM>
 __global__ __launch_bounds__((StreamShape<T, DK, DV>::kThreads), (StreamShape<T, DK, DV>::kKvMinBlocks)) void bwd_dkv_kernel(
     const T* __restrict__ k, const T* __restrict__ v, const float* __restrict__ dSg,
-    const float* __restrict__ dzg, T* __restrict__ dk, T* __restrict__ dv, int64_t T_, const Layout lay, int NK,
+    const float* __restrict__ dzg, T* __restrict__ dk, T* __restrict__ dv, int64_t T_, const Layouts lay, int NK,
     int64_t LK) {
     using Sh = StreamShape<T, DK, DV>;
-    const Layout lk = lay, lv = v_layout<DK, DV>(lay);
+    const Layout lk = lay.k, lv = lay.v;
     constexpr int FK = Sh::kFK, FV = Sh::kFV, NBK = Sh::kNBK, NBV = Sh::kNBV, KSK = Sh::kKSK, KSV = Sh::kKSV,
                   NW = Sh::kWaves, NT = Sh::kThreads;
     constexpr int U = 1;  // one 16-token block per wave step; the prefetch gives the depth
@@ -2056,20 +2060,18 @@ __global__ __launch_bounds__((StreamShape<T, DK, DV>::kThreads), (StreamShape<T,
     const int wid = xcd_remap(blockIdx.x, gridDim.x);
     const int64_t bh = wid / NK;
     const int ch = wid % NK;
-    const int64_t c0 = (int64_t)ch * LK;
-    const int64_t c1 = min(c0 + LK, T_);
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wave = wave_index();
     const int m = lane & 15, grp = lane >> 4;
     const float* dS = dSg + bh * DK * DV;
     const float* dz = dzg + bh * DK;
 
     // The first two turns' loads are issued before the prologue, which they
-    // overlap. Rows are counted from c0. The loop takes two blocks per turn with no
-    // early exit (an exit makes the compiler wait for every load in flight
-    // where the paths join): the chunk's buffer descriptors read rows past its
-    // end as zeros and drop their stores.
-    const HeadBuf bk = slice_buf(k, lk, bh, DK, c0, c1), bv_ = slice_buf(v, lv, bh, DV, c0, c1);
-    const HeadBuf bdk = slice_buf(dk, lk, bh, DK, c0, c1), bdv = slice_buf(dv, lv, bh, DV, c0, c1);
+    // overlap. The loop takes two rounds per turn with no early exit (an exit
+    // makes the compiler wait for every load in flight where the paths join):
+    // the head's buffer descriptors read rows past its end as zeros and drop
+    // their stores.
+    const HeadBuf bk = slice_buf(k, lk, bh, DK, 0, T_), bv_ = slice_buf(v, lv, bh, DV, 0, T_);
+    const HeadBuf bdk = slice_buf(dk, lay.dk, bh, DK, 0, T_), bdv = slice_buf(dv, lay.dv, bh, DV, 0, T_);
     T* stg = stage + (kStage ? wave * 16 * LDR : 0);
     // The loaded words as they are (see the dQ kernel).
     constexpr int NQK = FK * (int)sizeof(T) / 16;  // 16-byte words per quarter row of K
@@ -2078,9 +2080,20 @@ __global__ __launch_bounds__((StreamShape<T, DK, DV>::kThreads), (StreamShape<T,
         u32x4 k[U][NQK], v[U][NQV];
     };
     constexpr int NS = Sh::kStages;
-    const Rotation rot((int)((c1 - c0 + 16 * U - 1) / (16 * U)), NS * NW, wid);
+    constexpr int RT = 16 * U * NW;  // tokens per round
+    // this workgroup's rounds, padded to whole turns of NS
+    const int64_t nrounds = (T_ + RT - 1) / RT;
+    const int nmine = (int)(nrounds > ch ? (nrounds - ch + NK - 1) / NK : 0);
+    const int npad = (nmine + NS - 1) / NS * NS;
+    // first row of the wave's block of the workgroup's j-th round; the padded
+    // rounds (and the prefetches past the last one) all read the rows just
+    // past the head's end, zeros whose stores are dropped: their 32-bit
+    // offsets stay below T + 64 rows, inside the head span the host checks
+    auto row_of = [&](int j) {
+        return (j < nmine ? ((int64_t)ch + (int64_t)NK * j) * RT : T_) + 16 * U * wave;
+    };
     auto issue = [&](Stage& st, int blk) {
-        const int64_t bs = (int64_t)rot(blk) * 16 * U;
+        const int64_t bs = row_of(blk);
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int ok_ = buf_off<T>(bs + 16 * u + m, lk.rs, FK * grp);
@@ -2095,7 +2108,7 @@ __global__ __launch_bounds__((StreamShape<T, DK, DV>::kThreads), (StreamShape<T,
     Stage stq[NS];
 #pragma unroll
     for (int i = 0; i < NS; ++i) {
-        issue(stq[i], wave + i * NW);
+        issue(stq[i], i);
         sched_fence();
     }
     // fragments [0, NF1): dK side, rows i, contraction j -> dS[i][j];
@@ -2128,7 +2141,7 @@ __global__ __launch_bounds__((StreamShape<T, DK, DV>::kThreads), (StreamShape<T,
     __syncthreads();
 
     auto body = [&](Stage& st, int blk) {
-        const int64_t base = (int64_t)rot(blk) * 16 * U;
+        const int64_t base = row_of(blk);
         sched_fence();
         float dphik[U][FK];
         Frag<T> bk[U][KSK], bv[U][KSV];
@@ -2194,7 +2207,7 @@ __global__ __launch_bounds__((StreamShape<T, DK, DV>::kThreads), (StreamShape<T,
         }
         // the stage's registers are free once the products have read V
         sched_fence();
-        issue(st, blk + NS * NW);
+        issue(st, blk + NS);
         sched_fence();
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -2212,17 +2225,17 @@ __global__ __launch_bounds__((StreamShape<T, DK, DV>::kThreads), (StreamShape<T,
 #pragma unroll
                 for (int r = 0; r < 4; ++r) gv.e[4 * b + r] = static_cast<T>(av[u][b][r] * uD);
             if constexpr (kStage) {
-                store_tile_rows<T, DK>(stg, gk, bdk, base + 16 * u, lk.rs);
-                store_tile_rows<T, DV>(stg, gv, bdv, base + 16 * u, lv.rs);
+                store_tile_rows<T, DK>(stg, gk, bdk, base + 16 * u, lay.dk.rs);
+                store_tile_rows<T, DV>(stg, gv, bdv, base + 16 * u, lay.dv.rs);
             } else {
-                store_tile_quarters<T, DK>(gk, bdk, base + 16 * u, lk.rs);
-                store_tile_quarters<T, DV>(gv, bdv, base + 16 * u, lv.rs);
+                store_tile_quarters<T, DK>(gk, bdk, base + 16 * u, lay.dk.rs);
+                store_tile_quarters<T, DV>(gv, bdv, base + 16 * u, lay.dv.rs);
             }
         }
     };
-    for (int blk = wave; blk < rot.npad; blk += NS * NW) {
+    for (int j = 0; j < npad; j += NS) {
 #pragma unroll
-        for (int i = 0; i < NS; ++i) body(stq[i], blk + i * NW);
+        for (int i = 0; i < NS; ++i) body(stq[i], j + i);
     }
 }
 
@@ -2285,7 +2298,7 @@ __device__ __forceinline__ float wave_max_nonneg(float x) {
 template <typename T, int DK, int DV, bool SIMPLE, int FM>
 __global__ __launch_bounds__(kThreads, (CausalShape<DK, DV>::kMinBlocks)) void fwd_causal_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const float* __restrict__ pre,
-    T* __restrict__ o, int64_t T_, const Layout lay, int P, int64_t L, float eps) {
+    T* __restrict__ o, int64_t T_, const Layouts lay, int P, int64_t L, float eps) {
     using Sh = CausalShape<DK, DV>;
     constexpr int C = Sh::kChunk, LDK = Sh::kLDK, LDV = Sh::kLDV, LDRT = Sh::kLDRT, LDW = Sh::kLDW;
     constexpr int NBV = DV / 16;         // output column blocks
@@ -2308,13 +2321,13 @@ __global__ __launch_bounds__(kThreads, (CausalShape<DK, DV>::kMinBlocks)) void f
     const int wid = xcd_remap(blockIdx.x, gridDim.x);
     const int64_t bh = wid / P;
     const int p = wid % P;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wave = wave_index();
     const int m = lane & 15, grp = lane >> 4;
     const int64_t t0 = (int64_t)p * L;
     const int64_t t1 = min(t0 + L, T_);
     const int64_t len = t1 - t0;
     const int nchunks = (int)(len > 0 ? (len + C - 1) / C : 0);
-    const Layout lk = lay, lv = v_layout<DK, DV>(lay);
+    const Layout lq = lay.q, lk = lay.k, lv = lay.v, lo = lay.o;
 
     // Running state: R[16 iR + 4 grp + r][16 (wave RJ + jR) + m] in accR[iR][jR][r];
     // z[16 iR + 4 grp + r] in accZ[iR][r] (wave 0). From the exclusive prefix.
@@ -2379,16 +2392,15 @@ __global__ __launch_bounds__(kThreads, (CausalShape<DK, DV>::kMinBlocks)) void f
     struct Stage {
         u32x4 q[NCK], k[NCK], v[NCV];
     };
-    const HeadBuf bq = slice_buf(q, lk, bh, DK, t0, t1), bk = slice_buf(k, lk, bh, DK, t0, t1);
-    const HeadBuf bv = slice_buf(v, lv, bh, DV, t0, t1), bo = slice_buf(o, lv, bh, DV, t0, t1);
+    const HeadBuf bq = slice_buf(q, lq, bh, DK, t0, t1), bk = slice_buf(k, lk, bh, DK, t0, t1);
+    const HeadBuf bv = slice_buf(v, lv, bh, DV, t0, t1), bo = slice_buf(o, lo, bh, DV, t0, t1);
     auto issue = [&](Stage& st, int c) {
         const int64_t row0 = (int64_t)c * C;
 #pragma unroll
         for (int i = 0; i < NCK; ++i) {
             const int n = tid + kThreads * i, r = n / CK, cc = n % CK;
-            const int off = buf_off<T>(row0 + r, lk.rs, 8 * cc);
-            st.q[i] = __builtin_amdgcn_raw_buffer_load_b128(bq.rsrc, off, 0, 0);
-            st.k[i] = __builtin_amdgcn_raw_buffer_load_b128(bk.rsrc, off, 0, 0);
+            st.q[i] = __builtin_amdgcn_raw_buffer_load_b128(bq.rsrc, buf_off<T>(row0 + r, lq.rs, 8 * cc), 0, 0);
+            st.k[i] = __builtin_amdgcn_raw_buffer_load_b128(bk.rsrc, buf_off<T>(row0 + r, lk.rs, 8 * cc), 0, 0);
         }
 #pragma unroll
         for (int i = 0; i < NCV; ++i) {
@@ -2529,7 +2541,7 @@ __global__ __launch_bounds__(kThreads, (CausalShape<DK, DV>::kMinBlocks)) void f
         for (int kk = 0; kk < DV / 32; ++kk) {
             const int rb = 32 * kk + rA;
             const Frag<T> x = join_frag<T>(lds_read_tr(&myW[rb * LDW + cA]), lds_read_tr(&myW[(rb + 4) * LDW + cA]));
-            buf_store16(bo, buf_off<T>(row0 + 16 * wave + m, lv.rs, 32 * kk + 8 * grp), __builtin_bit_cast(uint4, x));
+            buf_store16(bo, buf_off<T>(row0 + 16 * wave + m, lo.rs, 32 * kk + 8 * grp), __builtin_bit_cast(uint4, x));
         }
         wave_lds_sync();
 
@@ -2694,7 +2706,7 @@ template <typename T, int DK, int DV, bool SIMPLE, int FM>
 __global__ __launch_bounds__(kThreads, (CausalBwdShape<DK, DV>::kMinBlocks)) void bwd_causal_q_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const T* __restrict__ dout,
     const float* __restrict__ pre, T* __restrict__ dq, float* __restrict__ wc, int* __restrict__ es,
-    float* __restrict__ gpart, int64_t T_, const Layout lay, int P, int64_t L, int nche, float eps) {
+    float* __restrict__ gpart, int64_t T_, const Layouts lay, int P, int64_t L, int nche, float eps) {
     using Sh = CausalBwdShape<DK, DV>;
     constexpr int C = Sh::kChunk, LDK = Sh::kLDK, LDV = Sh::kLDV, LDRT = Sh::kLDRT, LDQT = Sh::kLDQT;
     constexpr int LDW = Sh::kLDW;
@@ -2719,14 +2731,14 @@ __global__ __launch_bounds__(kThreads, (CausalBwdShape<DK, DV>::kMinBlocks)) voi
     const int wid = xcd_remap(blockIdx.x, gridDim.x);
     const int64_t bh = wid / P;
     const int p = wid % P;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wave = wave_index();
     const int m = lane & 15, grp = lane >> 4;
     const int64_t t0 = (int64_t)p * L;
     const int64_t t1 = min(t0 + L, T_);
     const int64_t len = t1 - t0;
     // rounded up to even: the loop body comes in pairs (see below)
     const int nchunks = (int)(len > 0 ? (((len + C - 1) / C) + 1) / 2 * 2 : 0);
-    const Layout lk = lay, lv = v_layout<DK, DV>(lay);
+    const Layout lq = lay.q, lk = lay.k, lv = lay.v, ld = lay.dout;
 
     // R[16 (wave RIW + iR) + 4 grp + r][16 jb + m] in accR[iR][jb][r], z of
     // the same rows in accZ[iR][r], likewise the G sum in accG.
@@ -2784,24 +2796,22 @@ __global__ __launch_bounds__(kThreads, (CausalBwdShape<DK, DV>::kMinBlocks)) voi
     struct Stage {
         u32x4 q[NCK], k[NCK], v[NCV], d[NCV];
     };
-    const HeadBuf bq = slice_buf(q, lk, bh, DK, t0, t1), bk = slice_buf(k, lk, bh, DK, t0, t1);
-    const HeadBuf bv = slice_buf(v, lv, bh, DV, t0, t1), bd = slice_buf(dout, lv, bh, DV, t0, t1);
-    const HeadBuf bdq = slice_buf(dq, lk, bh, DK, t0, t1);
+    const HeadBuf bq = slice_buf(q, lq, bh, DK, t0, t1), bk = slice_buf(k, lk, bh, DK, t0, t1);
+    const HeadBuf bv = slice_buf(v, lv, bh, DV, t0, t1), bd = slice_buf(dout, ld, bh, DV, t0, t1);
+    const HeadBuf bdq = slice_buf(dq, lay.dq, bh, DK, t0, t1);
     auto issue = [&](Stage& st, int c) {
         const int64_t row0 = (int64_t)c * C;
 #pragma unroll
         for (int i = 0; i < NCK; ++i) {
             const int n = tid + kThreads * i, r = n / CK, cc = n % CK;
-            const int off = buf_off<T>(row0 + r, lk.rs, 8 * cc);
-            st.q[i] = __builtin_amdgcn_raw_buffer_load_b128(bq.rsrc, off, 0, 0);
-            st.k[i] = __builtin_amdgcn_raw_buffer_load_b128(bk.rsrc, off, 0, 0);
+            st.q[i] = __builtin_amdgcn_raw_buffer_load_b128(bq.rsrc, buf_off<T>(row0 + r, lq.rs, 8 * cc), 0, 0);
+            st.k[i] = __builtin_amdgcn_raw_buffer_load_b128(bk.rsrc, buf_off<T>(row0 + r, lk.rs, 8 * cc), 0, 0);
         }
 #pragma unroll
         for (int i = 0; i < NCV; ++i) {
             const int n = tid + kThreads * i, r = n / CV, cc = n % CV;
-            const int off = buf_off<T>(row0 + r, lv.rs, 8 * cc);
-            st.v[i] = __builtin_amdgcn_raw_buffer_load_b128(bv.rsrc, off, 0, 0);
-            st.d[i] = __builtin_amdgcn_raw_buffer_load_b128(bd.rsrc, off, 0, 0);
+            st.v[i] = __builtin_amdgcn_raw_buffer_load_b128(bv.rsrc, buf_off<T>(row0 + r, lv.rs, 8 * cc), 0, 0);
+            st.d[i] = __builtin_amdgcn_raw_buffer_load_b128(bd.rsrc, buf_off<T>(row0 + r, ld.rs, 8 * cc), 0, 0);
         }
     };
     auto consume = [&](const Stage& st, int c) {
@@ -3017,7 +3027,7 @@ __global__ __launch_bounds__(kThreads, (CausalBwdShape<DK, DV>::kMinBlocks)) voi
             for (int kk = 0; kk < DK / 32; ++kk) {
                 const int rb = 32 * kk + rA;
                 const Frag<T> x = join_frag<T>(lds_read_tr(&myW[rb * LDW + cA]), lds_read_tr(&myW[(rb + 4) * LDW + cA]));
-                buf_store16(bdq, buf_off<T>(row0 + 16 * wave + m, lk.rs, 32 * kk + 8 * grp), __builtin_bit_cast(uint4, x));
+                buf_store16(bdq, buf_off<T>(row0 + 16 * wave + m, lay.dq.rs, 32 * kk + 8 * grp), __builtin_bit_cast(uint4, x));
             }
             wave_lds_sync();
         }
@@ -3177,7 +3187,7 @@ template <typename T, int DK, int DV, bool SIMPLE, int FM>
 __global__ __launch_bounds__(kThreads, (CausalBwdShape<DK, DV>::kMinBlocks)) void bwd_causal_kv_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const T* __restrict__ dout,
     const float* __restrict__ wc, const int* __restrict__ es, const float* __restrict__ suf, T* __restrict__ dk,
-    T* __restrict__ dv, int64_t T_, const Layout lay, int P, int64_t L, int nche, float qscale) {
+    T* __restrict__ dv, int64_t T_, const Layouts lay, int P, int64_t L, int nche, float qscale) {
     using Sh = CausalBwdShape<DK, DV>;
     constexpr int C = Sh::kChunk, LDK = Sh::kLDK, LDV = Sh::kLDV, LDRT = Sh::kLDRT, LDW = Sh::kLDW;
     constexpr int NBI = DK / 16, NBV = DV / 16, NBC = C / 16;
@@ -3202,14 +3212,14 @@ __global__ __launch_bounds__(kThreads, (CausalBwdShape<DK, DV>::kMinBlocks)) voi
     const int wid = xcd_remap(blockIdx.x, gridDim.x);
     const int64_t bh = wid / P;
     const int p = wid % P;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wave = wave_index();
     const int m = lane & 15, grp = lane >> 4;
     const int64_t t0 = (int64_t)p * L;
     const int64_t t1 = min(t0 + L, T_);
     const int64_t len = t1 - t0;
     const int nreal = (int)(len > 0 ? (len + C - 1) / C : 0);
     const int nchunks = (nreal + 1) / 2 * 2;
-    const Layout lk = lay, lv = v_layout<DK, DV>(lay);
+    const Layout lq = lay.q, lk = lay.k, lv = lay.v, ld = lay.dout;
 
     f32x4 accG[RIW][NBV], accGz[RIW];
     {
@@ -3259,9 +3269,9 @@ __global__ __launch_bounds__(kThreads, (CausalBwdShape<DK, DV>::kMinBlocks)) voi
         unsigned w, ch;  // w and c^ of token `lane` of the chunk
         int es;
     };
-    const HeadBuf bq = slice_buf(q, lk, bh, DK, t0, t1), bk = slice_buf(k, lk, bh, DK, t0, t1);
-    const HeadBuf bv = slice_buf(v, lv, bh, DV, t0, t1), bd = slice_buf(dout, lv, bh, DV, t0, t1);
-    const HeadBuf bdk = slice_buf(dk, lk, bh, DK, t0, t1), bdv = slice_buf(dv, lv, bh, DV, t0, t1);
+    const HeadBuf bq = slice_buf(q, lq, bh, DK, t0, t1), bk = slice_buf(k, lk, bh, DK, t0, t1);
+    const HeadBuf bv = slice_buf(v, lv, bh, DV, t0, t1), bd = slice_buf(dout, ld, bh, DV, t0, t1);
+    const HeadBuf bdk = slice_buf(dk, lay.dk, bh, DK, t0, t1), bdv = slice_buf(dv, lay.dv, bh, DV, t0, t1);
     // w and c^ of the segment's tokens (8 bytes each); zeros past the end
     const HeadBuf bwc{__builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(wc + 2 * (bh * T_ + t0)), 0,
                                                         (int)(len > 0 ? 8 * len : 0), 0x00020000)};
@@ -3275,16 +3285,14 @@ __global__ __launch_bounds__(kThreads, (CausalBwdShape<DK, DV>::kMinBlocks)) voi
 #pragma unroll
         for (int i = 0; i < NCK; ++i) {
             const int nn = tid + kThreads * i, r = nn / CK, cc = nn % CK;
-            const int off = buf_off<T>(row0 + r, lk.rs, 8 * cc);
-            st.q[i] = __builtin_amdgcn_raw_buffer_load_b128(bq.rsrc, off, 0, 0);
-            st.k[i] = __builtin_amdgcn_raw_buffer_load_b128(bk.rsrc, off, 0, 0);
+            st.q[i] = __builtin_amdgcn_raw_buffer_load_b128(bq.rsrc, buf_off<T>(row0 + r, lq.rs, 8 * cc), 0, 0);
+            st.k[i] = __builtin_amdgcn_raw_buffer_load_b128(bk.rsrc, buf_off<T>(row0 + r, lk.rs, 8 * cc), 0, 0);
         }
 #pragma unroll
         for (int i = 0; i < NCV; ++i) {
             const int nn = tid + kThreads * i, r = nn / CV, cc = nn % CV;
-            const int off = buf_off<T>(row0 + r, lv.rs, 8 * cc);
-            st.v[i] = __builtin_amdgcn_raw_buffer_load_b128(bv.rsrc, off, 0, 0);
-            st.d[i] = __builtin_amdgcn_raw_buffer_load_b128(bd.rsrc, off, 0, 0);
+            st.v[i] = __builtin_amdgcn_raw_buffer_load_b128(bv.rsrc, buf_off<T>(row0 + r, lv.rs, 8 * cc), 0, 0);
+            st.d[i] = __builtin_amdgcn_raw_buffer_load_b128(bd.rsrc, buf_off<T>(row0 + r, ld.rs, 8 * cc), 0, 0);
         }
         if constexpr (!SIMPLE) {
             // two dword loads: the 8-byte buffer-load builtin drops the upper dword with this compiler
@@ -3455,7 +3463,7 @@ __global__ __launch_bounds__(kThreads, (CausalBwdShape<DK, DV>::kMinBlocks)) voi
             for (int kk = 0; kk < DK / 32; ++kk) {
                 const int rb = 32 * kk + rA;
                 const Frag<T> x = join_frag<T>(lds_read_tr(&myW[rb * LDW + cA]), lds_read_tr(&myW[(rb + 4) * LDW + cA]));
-                buf_store16(bdk, buf_off<T>(row0 + 16 * wave + m, lk.rs, 32 * kk + 8 * grp), __builtin_bit_cast(uint4, x));
+                buf_store16(bdk, buf_off<T>(row0 + 16 * wave + m, lay.dk.rs, 32 * kk + 8 * grp), __builtin_bit_cast(uint4, x));
             }
             wave_lds_sync();
         }
@@ -3513,7 +3521,7 @@ __global__ __launch_bounds__(kThreads, (CausalBwdShape<DK, DV>::kMinBlocks)) voi
             for (int kk = 0; kk < DV / 32; ++kk) {
                 const int rb = 32 * kk + rA;
                 const Frag<T> x = join_frag<T>(lds_read_tr(&myW[rb * LDW + cA]), lds_read_tr(&myW[(rb + 4) * LDW + cA]));
-                buf_store16(bdv, buf_off<T>(row0 + 16 * wave + m, lv.rs, 32 * kk + 8 * grp), __builtin_bit_cast(uint4, x));
+                buf_store16(bdv, buf_off<T>(row0 + 16 * wave + m, lay.dv.rs, 32 * kk + 8 * grp), __builtin_bit_cast(uint4, x));
             }
             wave_lds_sync();
         }
@@ -3854,7 +3862,13 @@ SplitCfg split_config_t(int step) {
                 return {int64_t(BwdQTile<DK, DV>::kRound) * BwdQTile<DK, DV>::kStages, kBwdQTileWgs<DK, DV>};
             else return {BwdQShape<T, DK, DV>::kG, 1024};
         case kStepBwdKV:
-            return {int64_t(StreamShape<T, DK, DV>::kStages) * 16 * StreamShape<T, DK, DV>::kWaves, 1024};
+            // the rounds of a head are dealt to its workgroups in turn (see the
+            // kernel); for 16-bit heads up to 64 wide (four workgroups per CU)
+            // a grid of two full turns of the chip measured best: 187 us
+            // against 200 us at one turn and 201 us with contiguous chunks
+            // (B8-H16-T16384-D64 f16)
+            return {int64_t(StreamShape<T, DK, DV>::kStages) * 16 * StreamShape<T, DK, DV>::kWaves,
+                    StreamShape<T, DK, DV>::kSmall ? 2048 : 1024};
         default:
             return {StreamShape<T, DK, DV>::kStages * StreamShape<T, DK, DV>::kG, 2048};
     }

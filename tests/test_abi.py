@@ -17,7 +17,7 @@ from non_causal_linear_amd import Problem
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "la.h")
 
-OK, NULL, SHAPE, DTYPE, HEAD_DIM, FLAGS, EPS, WORKSPACE, ALIGN, ALIAS, DEVICE, SCALE, SCRATCH = range(13)
+OK, NULL, SHAPE, DTYPE, HEAD_DIM, FLAGS, EPS, WORKSPACE, ALIGN, ALIAS, DEVICE, SCALE, SCRATCH, STRIDE = range(14)
 
 
 @pytest.fixture(scope="module")
@@ -48,8 +48,8 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.la_version() == 6
-    for s in range(13):
+    assert L.la_version() == 7
+    for s in range(14):
         txt = L.la_status_str(s).decode()
         assert txt.startswith("LA_"), txt
     assert L.la_status_str(99).decode() == "unknown la_status"
@@ -61,9 +61,12 @@ def prob(B=2, H=3, T=100, D=64, dtype=1, flags=0, eps=1e-6, Dv=0, scale=0.0):
 
 
 def test_problem_struct_matches_header():
-    # int64 B, H, T, D, Dv; int32 dtype; uint32 flags; float eps, scale
-    assert ctypes.sizeof(Problem) == 56
-    assert [f[0] for f in Problem._fields_] == ["B", "H", "T", "D", "Dv", "dtype", "flags", "eps", "scale"]
+    # int64 B, H, T, D, Dv; int32 dtype; uint32 flags; float eps, scale; pointer strides
+    assert ctypes.sizeof(Problem) == 64
+    assert [f[0] for f in Problem._fields_] == ["B", "H", "T", "D", "Dv", "dtype", "flags", "eps", "scale",
+                                                "strides"]
+    assert ctypes.sizeof(la.Strides) == 8 * 3 * 8
+    assert [f[0] for f in la.Strides._fields_] == ["q", "k", "v", "o", "dout", "dq", "dk", "dv"]
 
 
 def test_state_bytes_formula(L):
@@ -340,3 +343,63 @@ def test_fwd_noalloc_validates_before_any_hip_call(L):
     assert 1024 * (128 * 128 + 128) * 4 > la.NOALLOC_SCRATCH_BYTES
     assert f(ctypes.byref(big), q, k, v, o, st, None) == SCRATCH
     assert "SCRATCH" in L.la_status_str(SCRATCH).decode()
+
+
+def strided(B=2, H=3, T=100, D=64, dtype=1, flags=0, **over):
+    """A problem with explicit strides: every tensor dense [B, H, T, D] unless
+    overridden (name -> (batch, head, token))."""
+    st = la.Strides()
+    for n in la.STRIDED:
+        setattr(st, n, la.TensorStrides(*over.get(n, (H * T * D, T * D, D))))
+    p = prob(B=B, H=H, T=T, D=D, dtype=dtype, flags=flags)
+    p.strides = ctypes.pointer(st)
+    p._keep = st
+    return p
+
+
+def test_strides_validated_before_any_hip_call(L):
+    base = 1 << 40
+    q, k, v, o, st_ = (ctypes.c_void_p(base + i * (1 << 34)) for i in range(5))
+    ws = ctypes.c_void_p(base + 6 * (1 << 34))
+
+    def fwd(p, ws_bytes=0, out=o):
+        return L.la_fwd(ctypes.byref(p), q, k, v, out, st_, ws, ctypes.c_size_t(ws_bytes), None)
+
+    B, H, T, D = 2, 3, 100, 64
+    # dense strides given explicitly pass the checks (then the workspace is too small)
+    assert fwd(strided()) == WORKSPACE
+    # the layout flag with strides is ambiguous
+    assert fwd(strided(flags=0x2)) == FLAGS
+    # negative, unaligned (f16: 4 elements = 8 bytes), token below the row width
+    assert fwd(strided(q=(-H * T * D, T * D, D))) == STRIDE
+    assert fwd(strided(k=(H * T * D, T * D, D + 4))) == STRIDE
+    assert fwd(strided(v=(H * T * D, T * D, D - 8))) == STRIDE
+    # a head's rows must stay addressable with 32-bit offsets
+    assert fwd(strided(v=(0, 0, 1 << 26))) == STRIDE
+    # inputs may share rows across heads (head stride 0) and interleave with
+    # each other, as the q, k, v views of a packed [B, T, 3, H, D] buffer do
+    assert fwd(strided(k=(H * T * D, 0, D), v=(H * T * D, 0, D))) == WORKSPACE
+    pk = (T * 3 * H * D, D, 3 * H * D)
+    assert fwd(strided(q=pk, k=pk, v=pk)) == WORKSPACE
+    # an output whose heads overlap each other, or whose rows overlap
+    assert fwd(strided(o=(H * T * D, 0, D))) == STRIDE
+    assert fwd(strided(o=(H * T * D, D, D))) == STRIDE
+    # an output interleaved with an input (compared by byte spans): o starts
+    # one f16 row (2 D bytes) into q's span
+    p = strided(q=pk, k=pk, v=pk, o=pk)
+    need = L.la_workspace_bytes(ctypes.byref(p))
+    assert L.la_fwd(ctypes.byref(p), q, k, v, ctypes.c_void_p(q.value + 2 * D), st_, ws,
+                    ctypes.c_size_t(need), None) == ALIAS
+    # the backward's packed outputs interleave: rejected, nothing launched
+    pd = strided(dq=pk, dk=pk, dv=pk)
+    need = L.la_workspace_bytes(ctypes.byref(pd))
+    g = base + 9 * (1 << 34)
+    assert L.la_bwd(ctypes.byref(pd), q, k, v, o, st_, ctypes.c_void_p(g), ctypes.c_void_p(g + 2 * D),
+                    ctypes.c_void_p(g + 4 * D), ws, ctypes.c_size_t(need), None) == ALIAS
+
+
+def test_strides_span_and_workspace_unchanged(L):
+    # strides change no sizes: state and workspace are functions of the shape
+    for p_dense, p_str in ((prob(), strided()), (prob(B=8, H=16, T=16384), strided(B=8, H=16, T=16384))):
+        assert L.la_workspace_bytes(ctypes.byref(p_dense)) == L.la_workspace_bytes(ctypes.byref(p_str))
+        assert L.la_state_bytes(ctypes.byref(p_dense)) == L.la_state_bytes(ctypes.byref(p_str))
