@@ -73,7 +73,7 @@ typedef enum {
     LA_ERR_NULL = 1,       /* a required pointer is NULL                      */
     LA_ERR_SHAPE = 2,      /* B, H or T negative; B*H > 2^24; head too large  */
     LA_ERR_DTYPE = 3,      /* dtype not one of la_dtype                       */
-    LA_ERR_HEAD_DIM = 4,   /* D or Dv not one of 32, 64, 96, 128              */
+    LA_ERR_HEAD_DIM = 4,   /* D, Dv not in {32, 64, 96, 128} nor both 256     */
     LA_ERR_FLAGS = 5,      /* unknown bit in flags, or two feature maps       */
     LA_ERR_EPS = 6,        /* eps negative or not finite                      */
     LA_ERR_WORKSPACE = 7,  /* ws_bytes below la_workspace_bytes()             */
@@ -134,7 +134,8 @@ typedef struct {
 /* Problem description shared by every call. B, H, T >= 0 (a zero size is an
  * empty problem: nothing to compute, LA_OK), B*H <= 2^24. D is the head size
  * of Q and K (and of dQ, dK), Dv that of V (and of O, dO, dV); 0 in Dv stands
- * for Dv = D. Each of D and Dv is 32, 64, 96 or 128, in any combination.
+ * for Dv = D. Each of D and Dv is 32, 64, 96 or 128, in any combination, or
+ * both are 256 (f16 and bf16 only; not with LA_CAUSAL).
  * eps >= 0 and finite (used only in normalised mode). One head of each tensor
  * must span less than 2^31 bytes, addressed with 32-bit offsets: with
  * M = max(D, Dv), T * M * elt < 2^31 in [B, H, T, *]; (T + 1024) * H * M * elt

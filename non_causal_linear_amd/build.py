@@ -26,8 +26,8 @@ LIB = os.path.join(PKG, "libla.so")
 KERNELS = "la_kernels.hip"
 API = "la_api.cpp"
 SCRATCH = "la_scratch.hip"
-# (la_dtype, DK) of every kernel unit; each covers all DV
-UNITS = [(dt, dk) for dt in (0, 1, 2) for dk in (32, 64, 96, 128)]
+# (la_dtype, DK) of every kernel unit; each covers all DV (DK = 256: 16-bit, DV = 256)
+UNITS = [(dt, dk) for dt in (0, 1, 2) for dk in (32, 64, 96, 128)] + [(1, 256), (2, 256)]
 
 # Packed fp32 VALU forms are switched off for every HIP source.
 HIPCC_FLAGS = [

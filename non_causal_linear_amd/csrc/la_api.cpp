@@ -59,7 +59,12 @@ int64_t dv_of(const la_problem* p) { return p->Dv ? p->Dv : p->D; }
 la_status check_problem(const la_problem* p) {
     if (!p) return LA_ERR_NULL;
     if (p->dtype != LA_F32 && p->dtype != LA_F16 && p->dtype != LA_BF16) return LA_ERR_DTYPE;
-    if (!head_size_ok(p->D) || !head_size_ok(dv_of(p))) return LA_ERR_HEAD_DIM;
+    if (p->D == 256 || dv_of(p) == 256) {
+        // the wide kernels: both sizes 256, 16-bit elements
+        if (p->D != dv_of(p) || p->dtype == LA_F32) return LA_ERR_HEAD_DIM;
+    } else if (!head_size_ok(p->D) || !head_size_ok(dv_of(p))) {
+        return LA_ERR_HEAD_DIM;
+    }
     if (p->B < 0 || p->H < 0 || p->T < 0) return LA_ERR_SHAPE;
     if (p->B > kMaxHeads || p->H > kMaxHeads || p->B * p->H > kMaxHeads) return LA_ERR_SHAPE;
     if (p->flags & ~(LA_SIMPLE | LA_LAYOUT_BTHD | LA_PHI_RELU | LA_PHI_IDENTITY | LA_CAUSAL)) return LA_ERR_FLAGS;
@@ -295,7 +300,7 @@ const char* la_status_str(int s) {
         case LA_ERR_NULL: return "LA_ERR_NULL: required pointer is NULL";
         case LA_ERR_SHAPE: return "LA_ERR_SHAPE: B, H or T negative or too large";
         case LA_ERR_DTYPE: return "LA_ERR_DTYPE: unknown dtype";
-        case LA_ERR_HEAD_DIM: return "LA_ERR_HEAD_DIM: D and Dv must be 32, 64, 96 or 128";
+        case LA_ERR_HEAD_DIM: return "LA_ERR_HEAD_DIM: D and Dv must be 32, 64, 96 or 128, or both 256 (16-bit)";
         case LA_ERR_FLAGS: return "LA_ERR_FLAGS: unknown flag bit or two feature maps";
         case LA_ERR_EPS: return "LA_ERR_EPS: eps must be finite and >= 0";
         case LA_ERR_SCALE: return "LA_ERR_SCALE: scale must be finite";

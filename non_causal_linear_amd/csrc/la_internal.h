@@ -93,10 +93,11 @@ constexpr size_t kScratchBytes = size_t(64) << 20;
 // hipGetSymbolAddress on the first call per device and kept (la_scratch.hip).
 hipError_t scratch_device_ptr(void** out);
 
-// One unit per (la_dtype, DK): kernel_set_<dtype>_<DK>().
+// One unit per (la_dtype, DK): kernel_set_<dtype>_<DK>(). DK = 256 exists for
+// the 16-bit types only, with DV = 256.
 #define LA_KERNEL_UNITS(X) \
     X(0, 32) X(0, 64) X(0, 96) X(0, 128) X(1, 32) X(1, 64) X(1, 96) X(1, 128) \
-    X(2, 32) X(2, 64) X(2, 96) X(2, 128)
+    X(2, 32) X(2, 64) X(2, 96) X(2, 128) X(1, 256) X(2, 256)
 #define LA_DECLARE_UNIT(dt, dk) const KernelSet* kernel_set_##dt##_##dk();
 LA_KERNEL_UNITS(LA_DECLARE_UNIT)
 #undef LA_DECLARE_UNIT

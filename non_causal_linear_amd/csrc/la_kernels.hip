@@ -3579,6 +3579,680 @@ __global__ __launch_bounds__(kThreads, (CausalBwdShape<DK, DV>::kMinBlocks)) voi
 }
 
 // ---------------------------------------------------------------------------
+// Head size 256 (DK = DV = 256, 16-bit inputs): wide kernels.
+// ---------------------------------------------------------------------------
+// A 256 x 256 fp32 state (256 KB) fits neither one wave's registers nor a
+// workgroup's LDS, so these kernels run eight waves per workgroup and split
+// the state among them: wave w owns 32 of its rows (or columns), and tiles of
+// tokens are shared through LDS. Per 16 or 32 tokens the waves also split the
+// products: wave w computes 32 of the 256 output features of every token.
+// MFMA conventions as above; where a wave's results are token rows, the rows
+// of its two 16-row A blocks are permuted so that lane (t + 16 g) ends with the
+// eight contiguous features 32 w + 8 g .. + 7 of token t (block b gives
+// 32 w + 8 g + 4 b + r in register r), which it stores as one 16-byte piece.
+struct Wide {
+    static constexpr int D = 256;
+    static constexpr int kWaves = 8;
+    static constexpr int kThreads = 64 * kWaves;
+    // token-major LDS tile row stride (elements): four consecutive rows fall
+    // 8 banks apart, so transposed reads of 4 rows x 32 bytes do not conflict
+    static constexpr int kLD = D + 16;
+    static constexpr int kCPR = D * 2 / 16;  // 16-byte chunks per 16-bit row: 32
+    // the state or output feature that row m of A block b (0, 1) of wave w
+    // stands for, in the permuted order
+    static __device__ __forceinline__ int feat(int w, int b, int m) { return 32 * w + 8 * (m >> 2) + 4 * b + (m & 3); }
+};
+
+// Largest |x| over n floats at M (n a multiple of 4 NT), over an NT-thread
+// workgroup, in a fixed order: each thread walks its float4s in turn.
+template <int NT>
+__device__ __forceinline__ float block_absmax_loop(const float* __restrict__ M, int n, float* red) {
+    float mx = 0.f;
+    for (int i = threadIdx.x; i < n / 4; i += NT) {
+        const float4 v = reinterpret_cast<const float4*>(M)[i];
+        mx = fmaxf(mx, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+    }
+    return block_max<NT / 64>(mx, red);
+}
+
+// A operand of wave w, 16-row block b, contraction step s of a 256 x 256 fp32
+// matrix M (rows 256 floats apart), rows in the permuted order of Wide::feat,
+// contraction index 32 s + 8 g + e, scaled and rounded to T:
+//   kRowsAreColumns = false: element M[feat][k]; true: element M[k][feat].
+template <typename T, bool kRowsAreColumns>
+__device__ __forceinline__ Frag<T> wide_frag(const float* __restrict__ M, int w, int b, int s, int m, int g,
+                                             float scale) {
+    const int f = Wide::feat(w, b, m), k0 = 32 * s + 8 * g;
+    Frag<T> r;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const float x = kRowsAreColumns ? M[(k0 + e) * Wide::D + f] : M[f * Wide::D + k0 + e];
+        r[e] = static_cast<T>(x * scale);
+    }
+    return r;
+}
+
+// Steps 1-3 at D = 256: one workgroup reduces tokens [p L, min((p+1) L, T))
+// of head bh into a partial (S, z) (or the state itself when a head is one
+// slice). Per 32-token tile the threads load K and V (two 16-byte chunks of
+// each per thread), apply phi to K in fp32 and round it to T (zero past the
+// slice end), and store both tiles token-major in LDS (two buffers, one
+// barrier per tile, the next two tiles' loads in flight). Wave w accumulates
+// rows 32 w .. 32 w + 31 of S over all 256 columns (32 blocks) and of z (a
+// block of ones as B), from transposed LDS reads: A = phi(K)^T, B = V.
+template <typename T, int FM>
+__global__ __launch_bounds__(Wide::kThreads, 1) void fwd_state_wide_kernel(
+    const T* __restrict__ k, const T* __restrict__ v, float* __restrict__ stS, float* __restrict__ stz,
+    float* __restrict__ part, int64_t T_, const Layouts lay, int P, int64_t L) {
+    constexpr int D = Wide::D, NT = Wide::kThreads, LD = Wide::kLD, CPR = Wide::kCPR, E = D * D + D;
+    constexpr int TT = 32;                // tokens per tile
+    constexpr int NCH = TT * CPR / NT;    // chunks of each tensor per thread per tile: 2
+    constexpr int NJ = D / 16;            // column blocks: 16
+    __shared__ __attribute__((aligned(16))) T sK[2][TT * LD];
+    __shared__ __attribute__((aligned(16))) T sV[2][TT * LD];
+
+    const int wid = xcd_remap(blockIdx.x, gridDim.x);
+    const int64_t bh = wid / P;
+    const int p = wid % P;
+    const int tid = threadIdx.x, lane = tid & 63, wave = wave_index();
+    const int m = lane & 15, grp = lane >> 4;
+    const int64_t t0 = (int64_t)p * L;
+    const int64_t t1 = min(t0 + L, T_);
+    const int64_t len = t1 - t0;
+    const int ntiles = (int)(len > 0 ? (len + TT - 1) / TT : 0);
+    const int npad = (ntiles + 1) / 2 * 2;
+
+    f32x4 acc[2][NJ + 1];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int j = 0; j <= NJ; ++j) acc[rb][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    Frag<T> ones;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ones[e] = static_cast<T>(1.f);
+
+    // Rows are counted from t0; tiles past the slice end read zeros (and K is
+    // zeroed after phi there), so the loop always runs whole pairs of tiles.
+    const HeadBuf bk = slice_buf(k, lay.k, bh, D, t0, t1), bv = slice_buf(v, lay.v, bh, D, t0, t1);
+    struct Stage {
+        u32x4 k[NCH], v[NCH];
+    };
+    auto issue = [&](Stage& st, int tile) {
+#pragma unroll
+        for (int i = 0; i < NCH; ++i) {
+            const int n = tid + NT * i, r = n / CPR, c = n % CPR;
+            const int64_t row = (int64_t)tile * TT + r;
+            st.k[i] = __builtin_amdgcn_raw_buffer_load_b128(bk.rsrc, buf_off<T>(row, lay.k.rs, 8 * c), 0, kNonTemporal);
+            st.v[i] = __builtin_amdgcn_raw_buffer_load_b128(bv.rsrc, buf_off<T>(row, lay.v.rs, 8 * c), 0, kNonTemporal);
+        }
+    };
+    auto put = [&](const Stage& st, int tile, int buf) {
+#pragma unroll
+        for (int i = 0; i < NCH; ++i) {
+            const int n = tid + NT * i, r = n / CPR, c = n % CPR;
+            const bool ok = (int64_t)tile * TT + r < len;
+            Row<T, 8> kr;
+            __builtin_memcpy(kr.e, &st.k[i], 16);
+            Row<T, 8> kt;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) kt.e[e] = ok ? static_cast<T>(phi<FM, T>(to_f32(kr.e[e]))) : static_cast<T>(0.f);
+            *reinterpret_cast<uint4*>(&sK[buf][r * LD + 8 * c]) = *reinterpret_cast<const uint4*>(kt.e);
+            *reinterpret_cast<u32x4*>(&sV[buf][r * LD + 8 * c]) = st.v[i];
+        }
+    };
+    const int rA = 8 * grp + (m >> 2), cA = 4 * (m & 3);
+    auto mma_tile = [&](int buf) {
+        const T* kk = sK[buf];
+        const T* vv = sV[buf];
+        Frag<T> a[2];
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+            const int cb = 16 * (2 * wave + rb) + cA;
+            a[rb] = join_frag<T>(lds_read_tr(&kk[rA * LD + cb]), lds_read_tr(&kk[(rA + 4) * LD + cb]));
+        }
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            const Frag<T> b = join_frag<T>(lds_read_tr(&vv[rA * LD + 16 * j + cA]),
+                                           lds_read_tr(&vv[(rA + 4) * LD + 16 * j + cA]));
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb) acc[rb][j] = mma(a[rb], b, acc[rb][j]);
+        }
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) acc[rb][NJ] = mma(a[rb], ones, acc[rb][NJ]);
+    };
+
+    if (ntiles > 0) {
+        Stage s0, s1;
+        issue(s0, 0);
+        sched_fence();
+        issue(s1, 1);
+        sched_fence();
+        for (int tile = 0; tile < npad; tile += 2) {
+            put(s0, tile, 0);
+            sched_fence();
+            issue(s0, tile + 2);
+            sched_fence();
+            __syncthreads();
+            mma_tile(0);
+            put(s1, tile + 1, 1);
+            sched_fence();
+            issue(s1, tile + 3);
+            sched_fence();
+            __syncthreads();
+            mma_tile(1);
+        }
+    }
+
+    float* oS;
+    float* oz;
+    if (P == 1) {
+        oS = stS + bh * D * D;
+        oz = stz + bh * D;
+    } else {
+        oS = part + (bh * P + p) * (int64_t)E;
+        oz = oS + D * D;
+    }
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+        const int row0 = 32 * wave + 16 * rb + 4 * grp;
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) oS[(row0 + r) * D + 16 * j + m] = acc[rb][j][r];
+        if (m == 0)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) oz[row0 + r] = acc[rb][NJ][r];
+    }
+}
+
+// Step 4 at D = 256: one workgroup streams tokens [ch LQ, min((ch+1) LQ, T))
+// of head bh in 16-token blocks. The threads load a block of Q (one 16-byte
+// chunk each: the 32 threads of a token row are 32 lanes of one wave), apply
+// phi in fp32, store phi(q) rounded to T token-major in LDS and reduce
+// den = phi(q) . z + eps over the row's lanes with xor shuffles (z in fp32);
+// after a barrier wave w multiplies the block by its 32 columns of S, held
+// as 16 fragments in registers since the prologue (A = S^T, rows permuted,
+// B = phi(Q)^T read straight from the token-major tile), scales by 1 / den and
+// stores eight contiguous outputs per lane. Two LDS buffers, one barrier per
+// block, the loads of the next two blocks in flight.
+template <typename T, bool SIMPLE, int FM>
+__global__ __launch_bounds__(Wide::kThreads, 1) void fwd_output_wide_kernel(
+    const T* __restrict__ q, const float* __restrict__ stS, const float* __restrict__ stz, T* __restrict__ o,
+    int64_t T_, const Layouts lay, int NQ, int64_t LQ, float eps) {
+    constexpr int D = Wide::D, NT = Wide::kThreads, LD = Wide::kLD, CPR = Wide::kCPR, KS = D / 32;
+    constexpr int BT = 16;  // tokens per block
+    static_assert(BT * CPR == NT, "one chunk per thread per block");
+    __shared__ __attribute__((aligned(16))) T sQ[2][BT * LD];
+    __shared__ float sDen[2][BT];
+    __shared__ float sZ[D];
+    __shared__ float red[NT / 64];
+
+    const int wid = xcd_remap(blockIdx.x, gridDim.x);
+    const int64_t bh = wid / NQ;
+    const int ch = wid % NQ;
+    const int64_t c0 = (int64_t)ch * LQ;
+    const int64_t c1 = min(c0 + LQ, T_);
+    const int tid = threadIdx.x, lane = tid & 63, wave = wave_index();
+    const int m = lane & 15, grp = lane >> 4;
+    const int lr = tid / CPR, lc = tid % CPR;  // the chunk this thread loads: token row, 16-byte column
+    const float* S = stS + bh * D * D;
+    const float* z = stz + bh * D;
+    const int nblk = (int)(c1 > c0 ? (c1 - c0 + BT - 1) / BT : 0);
+    const int npad = (nblk + 1) / 2 * 2;
+
+    const HeadBuf bq = slice_buf(q, lay.q, bh, D, c0, c1), bo = slice_buf(o, lay.o, bh, D, c0, c1);
+    auto issue = [&](u32x4& x, int blk) {
+        x = __builtin_amdgcn_raw_buffer_load_b128(bq.rsrc, buf_off<T>((int64_t)blk * BT + lr, lay.q.rs, 8 * lc), 0, 0);
+    };
+    u32x4 x0, x1;
+    issue(x0, 0);
+    sched_fence();
+    issue(x1, 1);
+    sched_fence();
+
+    // prologue: z to LDS; S^T fragments of this wave's 32 columns, scaled by 2^sS (f16)
+    for (int i = tid; i < D; i += NT) sZ[i] = z[i];
+    int sS = 0;
+    if constexpr (Elt<T>::kScaled) sS = scale_exp(block_absmax_loop<NT>(S, D * D, red));
+    const float fS = ldexpf(1.f, sS), uS = ldexpf(1.f, -sS);
+    Frag<T> a[2][KS];
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int s = 0; s < KS; ++s) a[b][s] = wide_frag<T, true>(S, wave, b, s, m, grp, fS);
+    __syncthreads();
+
+    auto put = [&](const u32x4& x, int buf) {
+        Row<T, 8> raw, ph;
+        __builtin_memcpy(raw.e, &x, 16);
+        float d = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            ph.e[e] = static_cast<T>(phi<FM, T>(to_f32(raw.e[e])));
+            d += to_f32(ph.e[e]) * sZ[8 * lc + e];
+        }
+        *reinterpret_cast<uint4*>(&sQ[buf][lr * LD + 8 * lc]) = *reinterpret_cast<const uint4*>(ph.e);
+        if constexpr (!SIMPLE) {
+#pragma unroll
+            for (int off = 16; off > 0; off >>= 1) d += __shfl_xor(d, off);  // the 32 lanes of this row
+            if (lc == 0) sDen[buf][lr] = d;
+        }
+    };
+    auto compute = [&](int blk, int buf) {
+        const T* qq = sQ[buf];
+        f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            const Frag<T> bq_ = __builtin_bit_cast(Frag<T>, *reinterpret_cast<const u32x4*>(&qq[m * LD + 32 * s + 8 * grp]));
+#pragma unroll
+            for (int b = 0; b < 2; ++b) acc[b] = mma(a[b][s], bq_, acc[b]);
+        }
+        float f;
+        if constexpr (SIMPLE) f = uS * eps;  // simple_la: eps carries the query scale
+        else f = uS / (sDen[buf][m] + eps);
+        Row<T, 8> out;
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) out.e[4 * b + r] = static_cast<T>(acc[b][r] * f);
+        buf_store16(bo, buf_off<T>((int64_t)blk * BT + m, lay.o.rs, 32 * wave + 8 * grp), *reinterpret_cast<const uint4*>(out.e));
+    };
+
+    for (int blk = 0; blk < npad; blk += 2) {
+        put(x0, 0);
+        sched_fence();
+        issue(x0, blk + 2);
+        sched_fence();
+        __syncthreads();
+        compute(blk, 0);
+        put(x1, 1);
+        sched_fence();
+        issue(x1, blk + 3);
+        sched_fence();
+        __syncthreads();
+        compute(blk + 1, 1);
+    }
+}
+
+// Step 7 at D = 256: one workgroup of 16 waves streams tokens [ch LK,
+// min((ch+1) LK, T)) of head bh in 16-token blocks. The threads load a block
+// of K (the first 512) and of V (the others), one 16-byte chunk each, and
+// store phi(k) rounded to T, phi'(k) in fp32 and V token-major in LDS. Waves
+// 0-7 compute dK, wave w its features 32 w .. 32 w + 31 with A = dS (rows i,
+// contraction over V's features) and B = V^T; waves 8-15 compute dV with
+// A = dS^T (rows j, contraction over K's features) and B = phi(K)^T. Each
+// wave's 16 fragments stay in registers from the prologue on; B is read
+// straight from the token-major tiles.
+//   dK_t = (dS v_t + dz) * phi'(k_t),  dV_t = dS^T phi(k_t)
+// Two LDS buffers, one barrier per block, the next two blocks' loads in flight.
+struct WideKV {
+    static constexpr int kWaves = 16;
+    static constexpr int kThreads = 64 * kWaves;
+};
+
+template <typename T, bool SIMPLE, int FM>
+__global__ __launch_bounds__(WideKV::kThreads, 1) void bwd_dkv_wide_kernel(
+    const T* __restrict__ k, const T* __restrict__ v, const float* __restrict__ dSg, const float* __restrict__ dzg,
+    T* __restrict__ dk, T* __restrict__ dv, int64_t T_, const Layouts lay, int NK, int64_t LK) {
+    constexpr int D = Wide::D, NT = WideKV::kThreads, LD = Wide::kLD, CPR = Wide::kCPR, KS = D / 32;
+    constexpr int BT = 16;
+    constexpr int LDP = D + 4;  // row stride (floats) of the phi'(k) tile
+    static_assert(2 * BT * CPR == NT, "one chunk of K or V per thread per block");
+    __shared__ __attribute__((aligned(16))) T sK[2][BT * LD];
+    __shared__ __attribute__((aligned(16))) T sV[2][BT * LD];
+    __shared__ __attribute__((aligned(16))) float sP[2][BT * LDP];
+    __shared__ float sZd[D];
+    __shared__ float red[NT / 64];
+
+    const int wid = xcd_remap(blockIdx.x, gridDim.x);
+    const int64_t bh = wid / NK;
+    const int ch = wid % NK;
+    const int64_t c0 = (int64_t)ch * LK;
+    const int64_t c1 = min(c0 + LK, T_);
+    const int tid = threadIdx.x, lane = tid & 63, wave = wave_index();
+    const int m = lane & 15, grp = lane >> 4;
+    const bool vside = wave >= 8;  // uniform over the wave: dV (true) or dK
+    const int fw = wave & 7;       // the wave's group of 32 features
+    const int lt = tid & (NT / 2 - 1), lr = lt / CPR, lc = lt % CPR;  // the chunk this thread loads
+    const float* dS = dSg + bh * D * D;
+    const float* dz = dzg + bh * D;
+    const int nblk = (int)(c1 > c0 ? (c1 - c0 + BT - 1) / BT : 0);
+    const int npad = (nblk + 1) / 2 * 2;
+
+    const HeadBuf bk = slice_buf(k, lay.k, bh, D, c0, c1), bv = slice_buf(v, lay.v, bh, D, c0, c1);
+    const HeadBuf bdk = slice_buf(dk, lay.dk, bh, D, c0, c1), bdv = slice_buf(dv, lay.dv, bh, D, c0, c1);
+    auto issue = [&](u32x4& x, int blk) {
+        const int64_t row = (int64_t)blk * BT + lr;
+        // the dV waves (the upper half of the threads) load V, the dK waves K
+        if (vside) x = __builtin_amdgcn_raw_buffer_load_b128(bv.rsrc, buf_off<T>(row, lay.v.rs, 8 * lc), 0, 0);
+        else x = __builtin_amdgcn_raw_buffer_load_b128(bk.rsrc, buf_off<T>(row, lay.k.rs, 8 * lc), 0, 0);
+    };
+    u32x4 x0, x1;
+    issue(x0, 0);
+    sched_fence();
+    issue(x1, 1);
+    sched_fence();
+
+    // prologue: this wave's 16 fragments of dS (dK side) or dS^T (dV side),
+    // scaled by 2^sD (f16); dz to LDS
+    int sD = 0;
+    if constexpr (Elt<T>::kScaled) sD = scale_exp(block_absmax_loop<NT>(dS, D * D, red));
+    const float fD = ldexpf(1.f, sD), uD = ldexpf(1.f, -sD);
+    Frag<T> a[2][KS];
+    if (vside) {
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int s = 0; s < KS; ++s) a[b][s] = wide_frag<T, true>(dS, fw, b, s, m, grp, fD);
+    } else {
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int s = 0; s < KS; ++s) a[b][s] = wide_frag<T, false>(dS, fw, b, s, m, grp, fD);
+    }
+    for (int i = tid; i < D; i += NT) sZd[i] = SIMPLE ? 0.f : dz[i];
+
+    auto put = [&](const u32x4& x, int buf) {
+        if (vside) {
+            *reinterpret_cast<u32x4*>(&sV[buf][lr * LD + 8 * lc]) = x;
+        } else {
+            Row<T, 8> raw, ph;
+            __builtin_memcpy(raw.e, &x, 16);
+            float dp[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                float pv;
+                feature<FM, T>(to_f32(raw.e[e]), pv, dp[e]);
+                ph.e[e] = static_cast<T>(pv);
+            }
+            *reinterpret_cast<uint4*>(&sK[buf][lr * LD + 8 * lc]) = *reinterpret_cast<const uint4*>(ph.e);
+            float4* pp = reinterpret_cast<float4*>(&sP[buf][lr * LDP + 8 * lc]);
+            pp[0] = make_float4(dp[0], dp[1], dp[2], dp[3]);
+            pp[1] = make_float4(dp[4], dp[5], dp[6], dp[7]);
+        }
+    };
+    auto compute = [&](int blk, int buf) {
+        const T* src = vside ? sK[buf] : sV[buf];
+        f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            const Frag<T> b_ = __builtin_bit_cast(Frag<T>, *reinterpret_cast<const u32x4*>(&src[m * LD + 32 * s + 8 * grp]));
+#pragma unroll
+            for (int b = 0; b < 2; ++b) acc[b] = mma(a[b][s], b_, acc[b]);
+            if (s % 2 == 1) sched_fence();  // two steps' operands in flight: 16 fragments stay resident
+        }
+        const int f0 = 32 * fw + 8 * grp;
+        const int64_t row = (int64_t)blk * BT + m;
+        Row<T, 8> out;
+        if (vside) {
+#pragma unroll
+            for (int b = 0; b < 2; ++b)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) out.e[4 * b + r] = static_cast<T>(acc[b][r] * uD);
+            buf_store16(bdv, buf_off<T>(row, lay.dv.rs, f0), *reinterpret_cast<const uint4*>(out.e));
+        } else {
+            const float* pp = &sP[buf][m * LDP + f0];
+#pragma unroll
+            for (int b = 0; b < 2; ++b)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int e = 4 * b + r;
+                    out.e[e] = static_cast<T>((acc[b][r] * uD + sZd[f0 + e]) * pp[e]);
+                }
+            buf_store16(bdk, buf_off<T>(row, lay.dk.rs, f0), *reinterpret_cast<const uint4*>(out.e));
+        }
+    };
+    __syncthreads();
+
+    for (int blk = 0; blk < npad; blk += 2) {
+        put(x0, 0);
+        sched_fence();
+        issue(x0, blk + 2);
+        sched_fence();
+        __syncthreads();
+        compute(blk, 0);
+        put(x1, 1);
+        sched_fence();
+        issue(x1, blk + 3);
+        sched_fence();
+        __syncthreads();
+        compute(blk + 1, 1);
+    }
+}
+
+// Steps 5-6 at D = 256: one workgroup reduces tokens [p LB, min((p+1) LB, T))
+// of head bh into partial (dS, dz) and writes their dQ, in 16-token blocks:
+//   (a) the threads load a block of Q and of dO (one 16-byte chunk of each),
+//       store both raw token-major in LDS and reduce den = phi(q) . z over
+//       each row's 32 lanes with xor shuffles (phi and z in fp32);
+//   (b) wave w computes u = S dO for its 32 features (A = S, 16 fragments of
+//       this wave's rows kept in LDS since the prologue: with 32 rows of the
+//       fp32 dS sums per wave in registers, S does not fit there as well;
+//       B = dO^T read straight from the tile), and r = phi(q) . u over them,
+//       published per wave;
+//   (c) after a barrier: r summed over the waves in a fixed order, c = -r /
+//       den^2, dQ = (u / den + c z) * phi'(q) stored eight features per lane;
+//       A_t = phi(q_t) 2^sw / den_t to the wave's own token-major LDS tile,
+//       read back transposed as the A operand of dS += A^T dO (16x16x16 over
+//       the block's tokens, B = dO read transposed from the shared tile);
+//       dz += c phi(q) in fp32 per lane.
+// simple_la: den = 1, c = 0, A = phi(q). The tiles are single-buffered (the
+// S fragments take 128 KB of LDS): a barrier before each block's loads are
+// stored, one after, one between (b) and (c); the next two blocks' loads are
+// in flight in registers. Rows past the slice end load zeros: dO = 0 adds
+// nothing to dS or dz, and their dQ stores are dropped.
+template <typename T, bool SIMPLE, int FM>
+__global__ __launch_bounds__(Wide::kThreads, 1) void bwd_dq_wide_kernel(
+    const T* __restrict__ q, const T* __restrict__ dout, const float* __restrict__ stS,
+    const float* __restrict__ stz, T* __restrict__ dq, float* __restrict__ part, float* __restrict__ dS_out,
+    float* __restrict__ dz_out, int64_t T_, const Layouts lay, int PB, int64_t LB, float eps) {
+    constexpr int D = Wide::D, NT = Wide::kThreads, NW = Wide::kWaves, LD = Wide::kLD, CPR = Wide::kCPR;
+    constexpr int KS = D / 32, NJ = D / 16, E = D * D + D;
+    constexpr int BT = 16;
+    constexpr int LDA = 48;  // row stride (elements) of a wave's A tile: 32 features + 16
+    static_assert(BT * CPR == NT, "one chunk per thread per block");
+    __shared__ __attribute__((aligned(16))) Frag<T> sSf[NW * 2 * KS * 64];
+    __shared__ __attribute__((aligned(16))) T sO[BT * LD];
+    __shared__ __attribute__((aligned(16))) T sQ[BT * LD];
+    __shared__ __attribute__((aligned(16))) T sA[NW][BT * LDA];
+    __shared__ float sDen[BT];
+    __shared__ float sR[NW][BT];
+    __shared__ float red[NT / 64];
+
+    const int wid = xcd_remap(blockIdx.x, gridDim.x);
+    const int64_t bh = wid / PB;
+    const int p = wid % PB;
+    const int64_t t0 = (int64_t)p * LB;
+    const int64_t t1 = min(t0 + LB, T_);
+    const int tid = threadIdx.x, lane = tid & 63, wave = wave_index();
+    const int m = lane & 15, grp = lane >> 4;
+    const int lr = tid / CPR, lc = tid % CPR;
+    const float* S = stS + bh * D * D;
+    const float* z = stz + bh * D;
+    const int nblk = (int)(t1 > t0 ? (t1 - t0 + BT - 1) / BT : 0);
+    const int npad = (nblk + 1) / 2 * 2;
+
+    const HeadBuf bq = slice_buf(q, lay.q, bh, D, t0, t1), bd = slice_buf(dout, lay.dout, bh, D, t0, t1),
+                  bdq = slice_buf(dq, lay.dq, bh, D, t0, t1);
+    struct Stage {
+        u32x4 q, d;
+    };
+    auto issue = [&](Stage& st, int blk) {
+        const int64_t row = (int64_t)blk * BT + lr;
+        st.q = __builtin_amdgcn_raw_buffer_load_b128(bq.rsrc, buf_off<T>(row, lay.q.rs, 8 * lc), 0, 0);
+        st.d = __builtin_amdgcn_raw_buffer_load_b128(bd.rsrc, buf_off<T>(row, lay.dout.rs, 8 * lc), 0, 0);
+    };
+    Stage s0, s1;
+    issue(s0, 0);
+    sched_fence();
+    issue(s1, 1);
+    sched_fence();
+
+    // prologue: this wave's S fragments (rows in the permuted order) to LDS,
+    // scaled by 2^sS (f16); z of the loaders' and of the lane's features; the
+    // exponent sw with 2^sw <= sum(z) < 2^(sw+1) that keeps A_t near 1 (f16)
+    int sS = 0, sw = 0;
+    if constexpr (Elt<T>::kScaled) {
+        sS = scale_exp(block_absmax_loop<NT>(S, D * D, red));
+        if constexpr (!SIMPLE) {
+            float zs = 0.f;
+            if (tid < D / 4) {
+                const float4 zz = reinterpret_cast<const float4*>(z)[tid];
+                zs = (zz.x + zz.y) + (zz.z + zz.w);
+            }
+            const float sum = block_sum<NT / 64>(zs, red);
+            if (sum > 0.f && isfinite(sum)) {
+                int e;
+                frexpf(sum, &e);
+                sw = min(max(e - 1, -120), 120);
+            }
+        }
+    }
+    const float fS = ldexpf(1.f, sS), uS = ldexpf(1.f, -sS), fw = ldexpf(1.f, sw);
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+            sSf[((2 * wave + b) * KS + s) * 64 + lane] = wide_frag<T, false>(S, wave, b, s, m, grp, fS);
+    float zl[8], zq[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        zl[e] = z[32 * wave + 8 * grp + e];  // the lane's dQ features
+        zq[e] = z[8 * lc + e];               // the loader's features
+    }
+
+    f32x4 dsacc[2][NJ];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) dsacc[rb][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float dzp[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) dzp[e] = 0.f;
+    T* aw = sA[wave];
+    const int rA = 4 * grp + (m >> 2), cA = 4 * (m & 3);
+
+    auto put = [&](const Stage& st) {
+        *reinterpret_cast<u32x4*>(&sQ[lr * LD + 8 * lc]) = st.q;
+        *reinterpret_cast<u32x4*>(&sO[lr * LD + 8 * lc]) = st.d;
+        if constexpr (!SIMPLE) {
+            Row<T, 8> raw;
+            __builtin_memcpy(raw.e, &st.q, 16);
+            float d = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) d += phi<FM, T>(to_f32(raw.e[e])) * zq[e];
+#pragma unroll
+            for (int off = 16; off > 0; off >>= 1) d += __shfl_xor(d, off);  // the 32 lanes of this row
+            if (lc == 0) sDen[lr] = d;
+        }
+    };
+    auto compute = [&](int blk) {
+        // (b) u = S dO for the wave's features, r over them
+        f32x4 u[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            const Frag<T> b_ = __builtin_bit_cast(Frag<T>, *reinterpret_cast<const u32x4*>(&sO[m * LD + 32 * s + 8 * grp]));
+#pragma unroll
+            for (int b = 0; b < 2; ++b) u[b] = mma(sSf[((2 * wave + b) * KS + s) * 64 + lane], b_, u[b]);
+        }
+        Row<T, 8> raw;
+        *reinterpret_cast<u32x4*>(raw.e) = *reinterpret_cast<const u32x4*>(&sQ[m * LD + 32 * wave + 8 * grp]);
+        float ph[8], dph[8], uu[8];
+        float rp = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            feature<FM, T>(to_f32(raw.e[e]), ph[e], dph[e]);
+            uu[e] = u[e >> 2][e & 3] * uS;
+            rp += ph[e] * uu[e];
+        }
+        float inv = 1.f, cc = 0.f;
+        if constexpr (!SIMPLE) {
+            rp += __shfl_xor(rp, 16);
+            rp += __shfl_xor(rp, 32);
+            if (grp == 0) sR[wave][m] = rp;
+            __syncthreads();
+            float r = 0.f;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) r += sR[w][m];
+            inv = 1.f / (sDen[m] + eps);
+            cc = -r * inv * inv;
+        }
+        // (c) dQ, then the reduction operand and dz
+        Row<T, 8> out;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float g = SIMPLE ? uu[e] * eps : uu[e] * inv + cc * zl[e];  // simple_la: eps carries the query scale
+            out.e[e] = static_cast<T>(g * dph[e]);
+        }
+        buf_store16(bdq, buf_off<T>((int64_t)blk * BT + m, lay.dq.rs, 32 * wave + 8 * grp),
+                    *reinterpret_cast<const uint4*>(out.e));
+        Row<T, 8> at;
+        const float fa = SIMPLE ? 1.f : fw * inv;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            at.e[e] = static_cast<T>(ph[e] * fa);
+            dzp[e] += cc * ph[e];
+        }
+        *reinterpret_cast<uint4*>(&aw[m * LDA + 8 * grp]) = *reinterpret_cast<const uint4*>(at.e);
+        wave_lds_sync();
+        i16x4 a[2];
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) a[rb] = lds_read_tr(&aw[rA * LDA + 16 * rb + cA]);
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            const i16x4 bw = lds_read_tr(&sO[rA * LD + 16 * j + cA]);
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb) dsacc[rb][j] = mma_k16<T>(a[rb], bw, dsacc[rb][j]);
+        }
+        wave_lds_sync();
+    };
+
+    for (int blk = 0; blk < npad; blk += 2) {
+        __syncthreads();  // every wave is done with the previous block's tiles
+        put(s0);
+        sched_fence();
+        issue(s0, blk + 2);
+        sched_fence();
+        __syncthreads();
+        compute(blk);
+        __syncthreads();
+        put(s1);
+        sched_fence();
+        issue(s1, blk + 3);
+        sched_fence();
+        __syncthreads();
+        compute(blk + 1);
+    }
+
+    // dz over the lanes of each feature group (tokens), in a fixed order
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+#pragma unroll
+        for (int off = 1; off < 16; off <<= 1) dzp[e] += __shfl_xor(dzp[e], off);
+    float* oS;
+    float* oz;
+    if (PB == 1) {
+        oS = dS_out + bh * D * D;
+        oz = dz_out + bh * D;
+    } else {
+        oS = part + (bh * PB + p) * (int64_t)E;
+        oz = oS + D * D;
+    }
+    const float uw = ldexpf(1.f, -sw) * (SIMPLE ? eps : 1.f);  // simple_la: times the query scale
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+        const int row0 = 32 * wave + 16 * rb + 4 * grp;
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) oS[(row0 + r) * D + 16 * j + m] = dsacc[rb][j][r] * uw;
+    }
+    if (m == 0)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) oz[32 * wave + 8 * grp + e] = SIMPLE ? 0.f : dzp[e];
+}
+
+// ---------------------------------------------------------------------------
 // Host-side dispatch.
 // ---------------------------------------------------------------------------
 template <typename T, int DK, int DV>
@@ -3637,6 +4311,76 @@ hipError_t fwd_state_fm(const Plan& p, const void* k, const void* v, float* stat
     const hipError_t e = launch_state_reduction<T, DK, DV, FM>(p, k, v, state, part, s);
     if (e != hipSuccess) return e;
     return launch_combine<DK, DV>(p.P, part, state, state + p.BH * DK * DV, p.BH, s);
+}
+
+// The D = 256 unit's launchers (16-bit only; the problem checks keep fp32 and
+// mixed sizes away from them).
+template <typename T, int FM>
+hipError_t wide_fwd_state_fm(const Plan& p, const void* k, const void* v, float* state, void* ws, hipStream_t s) {
+    constexpr int D = Wide::D;
+    float* part = reinterpret_cast<float*>(static_cast<char*>(ws) + p.off_part);
+    const hipError_t e = launch(fwd_state_wide_kernel<T, FM>, p.BH * p.P, Wide::kThreads, s, static_cast<const T*>(k),
+                                static_cast<const T*>(v), state, state + p.BH * D * D, part, p.T, p.lay, p.P, p.L);
+    if (e != hipSuccess) return e;
+    return launch_combine<D, D>(p.P, part, state, state + p.BH * D * D, p.BH, s);
+}
+template <typename T, int FM>
+hipError_t wide_fwd_output_fm(const Plan& p, const void* q, const float* state, void* o, hipStream_t s) {
+    constexpr int D = Wide::D;
+    const T* qq = static_cast<const T*>(q);
+    T* oo = static_cast<T*>(o);
+    const float* sz = state + p.BH * D * D;
+    if (p.simple)
+        return launch(fwd_output_wide_kernel<T, true, FM>, p.BH * p.NQ, Wide::kThreads, s, qq, state, sz, oo, p.T,
+                      p.lay, p.NQ, p.LQ, p.eps);
+    return launch(fwd_output_wide_kernel<T, false, FM>, p.BH * p.NQ, Wide::kThreads, s, qq, state, sz, oo, p.T, p.lay,
+                  p.NQ, p.LQ, p.eps);
+}
+template <typename T, int FM>
+hipError_t wide_bwd_dq_fm(const Plan& p, const void* q, const void* dout, const float* state, void* dq, void* ws,
+                          hipStream_t s) {
+    constexpr int D = Wide::D;
+    char* w = static_cast<char*>(ws);
+    float* part = reinterpret_cast<float*>(w + p.off_part);
+    float* dS = reinterpret_cast<float*>(w + p.off_dstate);
+    float* dz = dS + p.BH * D * D;
+    const T* qq = static_cast<const T*>(q);
+    const T* dd = static_cast<const T*>(dout);
+    const float* sz = state + p.BH * D * D;
+    T* g = static_cast<T*>(dq);
+    const hipError_t e =
+        p.simple ? launch(bwd_dq_wide_kernel<T, true, FM>, p.BH * p.PB, Wide::kThreads, s, qq, dd, state, sz, g, part,
+                          dS, dz, p.T, p.lay, p.PB, p.LB, p.eps)
+                 : launch(bwd_dq_wide_kernel<T, false, FM>, p.BH * p.PB, Wide::kThreads, s, qq, dd, state, sz, g, part,
+                          dS, dz, p.T, p.lay, p.PB, p.LB, p.eps);
+    if (e != hipSuccess) return e;
+    return launch_combine<D, D>(p.PB, part, dS, dz, p.BH, s);
+}
+template <typename T, int FM>
+hipError_t wide_bwd_dkv_fm(const Plan& p, const void* k, const void* v, void* dk, void* dv, void* ws, hipStream_t s) {
+    constexpr int D = Wide::D;
+    const float* dS = reinterpret_cast<const float*>(static_cast<char*>(ws) + p.off_dstate);
+    const float* dz = dS + p.BH * D * D;
+    const T* kk = static_cast<const T*>(k);
+    const T* vv = static_cast<const T*>(v);
+    T* gk = static_cast<T*>(dk);
+    T* gv = static_cast<T*>(dv);
+    if (p.simple)
+        return launch(bwd_dkv_wide_kernel<T, true, FM>, p.BH * p.NK, WideKV::kThreads, s, kk, vv, dS, dz, gk, gv, p.T,
+                      p.lay, p.NK, p.LK);
+    return launch(bwd_dkv_wide_kernel<T, false, FM>, p.BH * p.NK, WideKV::kThreads, s, kk, vv, dS, dz, gk, gv, p.T,
+                  p.lay, p.NK, p.LK);
+}
+// Token split of the D = 256 kernels: one workgroup per CU for the
+// reductions (each writes a 263 KB partial), two turns of the chip for the
+// streaming steps.
+SplitCfg wide_split_config(int step) {
+    switch (step) {
+        case kStepState: return {64, 256};
+        case kStepBwdQ: return {32, 256};
+        case kStepBwdKV: return {32, 512};
+        default: return {32, 512};
+    }
 }
 
 // Where the causal forward exists: 16-bit elements, DK and DV in {64, 128}.
@@ -3879,7 +4623,7 @@ SplitCfg split_config_t(int step) {
 // size. The build compiles the file once per (LA_UNIT_DTYPE, LA_UNIT_DK).
 // ---------------------------------------------------------------------------
 #if !defined(LA_UNIT_DTYPE) || !defined(LA_UNIT_DK)
-#error "compile once per unit with -DLA_UNIT_DTYPE=<0|1|2> (la_dtype) -DLA_UNIT_DK=<32|64|96|128>"
+#error "compile once per unit with -DLA_UNIT_DTYPE=<0|1|2> (la_dtype) -DLA_UNIT_DK=<32|64|96|128|256>"
 #endif
 
 template <int DT> struct UnitType;
@@ -3889,6 +4633,38 @@ template <> struct UnitType<2> { using type = bf16; };
 using UT = UnitType<LA_UNIT_DTYPE>::type;
 constexpr int UDK = LA_UNIT_DK;
 
+#if LA_UNIT_DK == 256
+// D = DV = 256, 16-bit: the wide kernels (no causal form at this size).
+#define LA_WIDE_MAP(FN, ...)                                                       \
+    switch (p.fm) {                                                                \
+        case kPhiRelu: return FN<UT, kPhiRelu>(p, __VA_ARGS__);                    \
+        case kPhiIdentity: return FN<UT, kPhiIdentity>(p, __VA_ARGS__);            \
+        default: return FN<UT, kPhiElu1>(p, __VA_ARGS__);                          \
+    }
+static_assert(sizeof(UT) == 2, "head size 256 is built for 16-bit inputs only");
+hipError_t unit_fwd_state(const Plan& p, const void* k, const void* v, float* state, void* ws, hipStream_t s) {
+    LA_WIDE_MAP(wide_fwd_state_fm, k, v, state, ws, s);
+}
+hipError_t unit_fwd_output(const Plan& p, const void* q, const float* state, void* o, hipStream_t s) {
+    LA_WIDE_MAP(wide_fwd_output_fm, q, state, o, s);
+}
+hipError_t unit_bwd_dq(const Plan& p, const void* q, const void* dout, const float* state, void* dq, void* ws,
+                       hipStream_t s) {
+    LA_WIDE_MAP(wide_bwd_dq_fm, q, dout, state, dq, ws, s);
+}
+hipError_t unit_bwd_dkv(const Plan& p, const void* k, const void* v, void* dk, void* dv, void* ws, hipStream_t s) {
+    LA_WIDE_MAP(wide_bwd_dkv_fm, k, v, dk, dv, ws, s);
+}
+hipError_t unit_fwd_causal(const Plan&, const void*, const void*, const void*, void*, float*, void*, hipStream_t) {
+    return hipErrorInvalidValue;
+}
+hipError_t unit_bwd_causal(const Plan&, const void*, const void*, const void*, const void*, void*, void*, void*, void*,
+                           hipStream_t) {
+    return hipErrorInvalidValue;
+}
+SplitCfg unit_split_config(int step, int) { return wide_split_config(step); }
+#undef LA_WIDE_MAP
+#else
 #define LA_DV_DISPATCH(FN, ...)                                       \
     switch (p.DV) {                                                   \
         case 32: return FN<UT, UDK, 32>(p, __VA_ARGS__);              \
@@ -3927,6 +4703,8 @@ SplitCfg unit_split_config(int step, int DV) {
         default: return split_config_t<UT, UDK, 128>(step);
     }
 }
+
+#endif
 
 const KernelSet kUnitSet = {unit_fwd_state, unit_fwd_output, unit_bwd_dq,    unit_bwd_dkv,
                              unit_split_config, unit_fwd_causal, unit_bwd_causal};

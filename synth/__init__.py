@@ -149,5 +149,7 @@ HEAD_SIZE_WORKLOADS = {
         Workload("B8-H16-T16384-D64-Dv128-f16", 8, 16, 16384, 64, "f16", seed=6300, Dv=128),
         Workload("B8-H16-T16384-D128-Dv64-f16", 8, 16, 16384, 128, "f16", seed=6400, Dv=64),
         Workload("B8-H16-T16384-D32-Dv128-f16", 8, 16, 16384, 32, "f16", seed=6500, Dv=128),
+        # head size 256: the headline's bytes per tensor (T D per head) at a quarter of its length
+        Workload("B8-H16-T4096-D256-f16", 8, 16, 4096, 256, "f16", seed=6600),
     )
 }

@@ -87,7 +87,8 @@ def test_workspace_bytes_covers_state_and_partials(L):
     one = L.la_workspace_bytes(ctypes.byref(prob(B=1, H=1, T=1 << 20, D=64)))
     assert one >= 64 * E * 4
     # invalid problems report 0
-    assert L.la_workspace_bytes(ctypes.byref(prob(D=256))) == 0
+    assert L.la_workspace_bytes(ctypes.byref(prob(D=256, dtype=0))) == 0
+    assert L.la_workspace_bytes(ctypes.byref(prob(D=256, Dv=64))) == 0
     assert L.la_workspace_bytes(ctypes.byref(prob(Dv=48))) == 0
     assert L.la_state_bytes(ctypes.byref(prob(dtype=7))) == 0
     assert L.la_workspace_bytes(None) == 0
@@ -126,7 +127,7 @@ def test_fwd_rejects_bad_problems(L):
     assert fwd_call(L, None) == NULL
     assert fwd_call(L, prob(dtype=3)) == DTYPE
     assert fwd_call(L, prob(dtype=-1)) == DTYPE
-    for d, dv in ((48, 0), (256, 0), (0, 64), (16, 0), (64, 256), (64, 16), (64, -64), (96, 160)):
+    for d, dv in ((48, 0), (256, 128), (0, 64), (16, 0), (64, 256), (64, 16), (64, -64), (96, 160), (512, 0)):
         assert fwd_call(L, prob(D=d, Dv=dv)) == HEAD_DIM, (d, dv)
     assert fwd_call(L, prob(B=-1)) == SHAPE
     assert fwd_call(L, prob(T=-5)) == SHAPE
@@ -228,7 +229,7 @@ def test_bwd_rejects_bad_buffers(L):
     assert call(dv=d[3]) == ALIAS          # output on an input
     assert call(dq=d[4]) == ALIAS          # output on the state
     assert call(dq=ctypes.c_void_p(A + (5 << 24) + 2)) == ALIGN
-    assert L.la_bwd(ctypes.byref(prob(D=256)), *d[:9], need, None) == HEAD_DIM
+    assert L.la_bwd(ctypes.byref(prob(D=256, Dv=128)), *d[:9], need, None) == HEAD_DIM
 
 
 def test_step_calls_validate(L):
@@ -403,3 +404,26 @@ def test_strides_span_and_workspace_unchanged(L):
     for p_dense, p_str in ((prob(), strided()), (prob(B=8, H=16, T=16384), strided(B=8, H=16, T=16384))):
         assert L.la_workspace_bytes(ctypes.byref(p_dense)) == L.la_workspace_bytes(ctypes.byref(p_str))
         assert L.la_state_bytes(ctypes.byref(p_dense)) == L.la_state_bytes(ctypes.byref(p_str))
+
+
+def test_head_size_256_rules(L):
+    """D = Dv = 256 is built for 16-bit inputs; fp32, a mixed pair with 256,
+    and the causal form at 256 are refused before any HIP call."""
+    base = 1 << 40
+    q, k, v, o, st_, ws = (ctypes.c_void_p(base + i * (1 << 36)) for i in range(6))
+
+    def fwd(p):
+        return L.la_fwd(ctypes.byref(p), q, k, v, o, st_, ws, ctypes.c_size_t(0), None)
+
+    for dt in (1, 2):
+        p = prob(D=256, dtype=dt)
+        assert L.la_state_bytes(ctypes.byref(p)) == 2 * 3 * (256 * 256 + 256) * 4
+        assert fwd(p) == WORKSPACE  # accepted; the workspace is too small
+        assert fwd(prob(D=256, Dv=128, dtype=dt)) == HEAD_DIM
+        assert fwd(prob(D=64, Dv=256, dtype=dt)) == HEAD_DIM
+        assert fwd(prob(D=256, dtype=dt, flags=0x10)) == HEAD_DIM
+    assert fwd(prob(D=256, dtype=0)) == HEAD_DIM
+    # B8-H16-T4096-D256: two slices per head, their 263 KB partials in the workspace
+    p = prob(B=8, H=16, T=4096, D=256)
+    E = 256 * 256 + 256
+    assert L.la_workspace_bytes(ctypes.byref(p)) >= 128 * 2 * E * 4 + 2 * 128 * E * 4
