@@ -3774,13 +3774,14 @@ __global__ __launch_bounds__(Wide::kThreads, 1) void fwd_state_wide_kernel(
 // as 16 fragments in registers since the prologue (A = S^T, rows permuted,
 // B = phi(Q)^T read straight from the token-major tile), scales by 1 / den and
 // stores eight contiguous outputs per lane. Two LDS buffers, one barrier per
-// block, the loads of the next two blocks in flight.
+// block, the loads of the next four blocks in flight, two workgroups per CU.
 template <typename T, bool SIMPLE, int FM>
-__global__ __launch_bounds__(Wide::kThreads, 1) void fwd_output_wide_kernel(
+__global__ __launch_bounds__(Wide::kThreads, 2) void fwd_output_wide_kernel(
     const T* __restrict__ q, const float* __restrict__ stS, const float* __restrict__ stz, T* __restrict__ o,
     int64_t T_, const Layouts lay, int NQ, int64_t LQ, float eps) {
     constexpr int D = Wide::D, NT = Wide::kThreads, LD = Wide::kLD, CPR = Wide::kCPR, KS = D / 32;
     constexpr int BT = 16;  // tokens per block
+    constexpr int NS = 4;   // blocks of loads in flight per thread
     static_assert(BT * CPR == NT, "one chunk per thread per block");
     __shared__ __attribute__((aligned(16))) T sQ[2][BT * LD];
     __shared__ float sDen[2][BT];
@@ -3798,17 +3799,18 @@ __global__ __launch_bounds__(Wide::kThreads, 1) void fwd_output_wide_kernel(
     const float* S = stS + bh * D * D;
     const float* z = stz + bh * D;
     const int nblk = (int)(c1 > c0 ? (c1 - c0 + BT - 1) / BT : 0);
-    const int npad = (nblk + 1) / 2 * 2;
+    const int npad = (nblk + NS - 1) / NS * NS;
 
     const HeadBuf bq = slice_buf(q, lay.q, bh, D, c0, c1), bo = slice_buf(o, lay.o, bh, D, c0, c1);
     auto issue = [&](u32x4& x, int blk) {
         x = __builtin_amdgcn_raw_buffer_load_b128(bq.rsrc, buf_off<T>((int64_t)blk * BT + lr, lay.q.rs, 8 * lc), 0, 0);
     };
-    u32x4 x0, x1;
-    issue(x0, 0);
-    sched_fence();
-    issue(x1, 1);
-    sched_fence();
+    u32x4 x[NS];
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+        issue(x[i], i);
+        sched_fence();
+    }
 
     // prologue: z to LDS; S^T fragments of this wave's 32 columns, scaled by 2^sS (f16)
     for (int i = tid; i < D; i += NT) sZ[i] = z[i];
@@ -3858,19 +3860,17 @@ __global__ __launch_bounds__(Wide::kThreads, 1) void fwd_output_wide_kernel(
         buf_store16(bo, buf_off<T>((int64_t)blk * BT + m, lay.o.rs, 32 * wave + 8 * grp), *reinterpret_cast<const uint4*>(out.e));
     };
 
-    for (int blk = 0; blk < npad; blk += 2) {
-        put(x0, 0);
-        sched_fence();
-        issue(x0, blk + 2);
-        sched_fence();
-        __syncthreads();
-        compute(blk, 0);
-        put(x1, 1);
-        sched_fence();
-        issue(x1, blk + 3);
-        sched_fence();
-        __syncthreads();
-        compute(blk + 1, 1);
+    // (written out per stage: each stage keeps its own registers)
+    for (int blk = 0; blk < npad; blk += NS) {
+#pragma unroll
+        for (int i = 0; i < NS; ++i) {
+            put(x[i], i & 1);
+            sched_fence();
+            issue(x[i], blk + i + NS);
+            sched_fence();
+            __syncthreads();
+            compute(blk + i, i & 1);
+        }
     }
 }
 
@@ -3896,6 +3896,7 @@ __global__ __launch_bounds__(WideKV::kThreads, 1) void bwd_dkv_wide_kernel(
     T* __restrict__ dk, T* __restrict__ dv, int64_t T_, const Layouts lay, int NK, int64_t LK) {
     constexpr int D = Wide::D, NT = WideKV::kThreads, LD = Wide::kLD, CPR = Wide::kCPR, KS = D / 32;
     constexpr int BT = 16;
+    constexpr int NS = 2;       // blocks of loads in flight per thread (4 measured slower)
     constexpr int LDP = D + 4;  // row stride (floats) of the phi'(k) tile
     static_assert(2 * BT * CPR == NT, "one chunk of K or V per thread per block");
     __shared__ __attribute__((aligned(16))) T sK[2][BT * LD];
@@ -3917,7 +3918,7 @@ __global__ __launch_bounds__(WideKV::kThreads, 1) void bwd_dkv_wide_kernel(
     const float* dS = dSg + bh * D * D;
     const float* dz = dzg + bh * D;
     const int nblk = (int)(c1 > c0 ? (c1 - c0 + BT - 1) / BT : 0);
-    const int npad = (nblk + 1) / 2 * 2;
+    const int npad = (nblk + NS - 1) / NS * NS;
 
     const HeadBuf bk = slice_buf(k, lay.k, bh, D, c0, c1), bv = slice_buf(v, lay.v, bh, D, c0, c1);
     const HeadBuf bdk = slice_buf(dk, lay.dk, bh, D, c0, c1), bdv = slice_buf(dv, lay.dv, bh, D, c0, c1);
@@ -3927,11 +3928,12 @@ __global__ __launch_bounds__(WideKV::kThreads, 1) void bwd_dkv_wide_kernel(
         if (vside) x = __builtin_amdgcn_raw_buffer_load_b128(bv.rsrc, buf_off<T>(row, lay.v.rs, 8 * lc), 0, 0);
         else x = __builtin_amdgcn_raw_buffer_load_b128(bk.rsrc, buf_off<T>(row, lay.k.rs, 8 * lc), 0, 0);
     };
-    u32x4 x0, x1;
-    issue(x0, 0);
-    sched_fence();
-    issue(x1, 1);
-    sched_fence();
+    u32x4 x[NS];
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+        issue(x[i], i);
+        sched_fence();
+    }
 
     // prologue: this wave's 16 fragments of dS (dK side) or dS^T (dV side),
     // scaled by 2^sD (f16); dz to LDS
@@ -4004,60 +4006,58 @@ __global__ __launch_bounds__(WideKV::kThreads, 1) void bwd_dkv_wide_kernel(
     };
     __syncthreads();
 
-    for (int blk = 0; blk < npad; blk += 2) {
-        put(x0, 0);
-        sched_fence();
-        issue(x0, blk + 2);
-        sched_fence();
-        __syncthreads();
-        compute(blk, 0);
-        put(x1, 1);
-        sched_fence();
-        issue(x1, blk + 3);
-        sched_fence();
-        __syncthreads();
-        compute(blk + 1, 1);
+    for (int blk = 0; blk < npad; blk += NS) {
+#pragma unroll
+        for (int i = 0; i < NS; ++i) {
+            put(x[i], i & 1);
+            sched_fence();
+            issue(x[i], blk + i + NS);
+            sched_fence();
+            __syncthreads();
+            compute(blk + i, i & 1);
+        }
     }
 }
 
 // Steps 5-6 at D = 256: one workgroup reduces tokens [p LB, min((p+1) LB, T))
-// of head bh into partial (dS, dz) and writes their dQ, in 16-token blocks:
-//   (a) the threads load a block of Q and of dO (one 16-byte chunk of each),
-//       store both raw token-major in LDS and reduce den = phi(q) . z over
-//       each row's 32 lanes with xor shuffles (phi and z in fp32);
-//   (b) wave w computes u = S dO for its 32 features (A = S, 16 fragments of
-//       this wave's rows kept in LDS since the prologue: with 32 rows of the
-//       fp32 dS sums per wave in registers, S does not fit there as well;
-//       B = dO^T read straight from the tile), and r = phi(q) . u over them,
-//       published per wave;
-//   (c) after a barrier: r summed over the waves in a fixed order, c = -r /
-//       den^2, dQ = (u / den + c z) * phi'(q) stored eight features per lane;
-//       A_t = phi(q_t) 2^sw / den_t to the wave's own token-major LDS tile,
-//       read back transposed as the A operand of dS += A^T dO (16x16x16 over
-//       the block's tokens, B = dO read transposed from the shared tile);
-//       dz += c phi(q) in fp32 per lane.
-// simple_la: den = 1, c = 0, A = phi(q). The tiles are single-buffered (the
-// S fragments take 128 KB of LDS): a barrier before each block's loads are
-// stored, one after, one between (b) and (c); the next two blocks' loads are
-// in flight in registers. Rows past the slice end load zeros: dO = 0 adds
-// nothing to dS or dz, and their dQ stores are dropped.
+// of head bh into partial (dS, dz) and writes their dQ, in 16-token blocks.
+// Lane (t + 16 g) of wave w owns features 32 w + 8 g .. + 7 of token t of the
+// block: it loads that 16-byte piece of Q (kept in registers) and of dO
+// (stored token-major in LDS, double-buffered, for all waves), and
+//   (a) u = S dO for the wave's features (A = S, 16 fragments of this wave's
+//       rows kept in LDS since the prologue: with 32 rows of the fp32 dS sums
+//       per wave in registers, S does not fit there as well; B = dO^T read
+//       straight from the tile), phi(q) and phi'(q) in fp32, and over its
+//       eight features the partial sums of r = phi(q) . u and of
+//       phi(q) . z, which the waves publish per token;
+//   (b) after a barrier: r and den = phi(q) . z + eps summed over the waves in
+//       a fixed order, c = -r / den^2, dQ = (u / den + c z) * phi'(q) stored
+//       as one 16-byte piece; A_t = phi(q_t) 2^sw / den_t to the wave's own
+//       token-major LDS tile, read back transposed as the A operand of
+//       dS += A^T dO (16x16x16 over the block's tokens, B = dO read transposed
+//       from the shared tile); dz += c phi(q) in fp32 per lane.
+// simple_la: den = 1, c = 0, A = phi(q). Two barriers per block; the loads of
+// the next four blocks in flight in registers. Rows past the slice end load
+// zeros: dO = 0 adds nothing to dS or dz, and their dQ stores are dropped.
 template <typename T, bool SIMPLE, int FM>
 __global__ __launch_bounds__(Wide::kThreads, 1) void bwd_dq_wide_kernel(
     const T* __restrict__ q, const T* __restrict__ dout, const float* __restrict__ stS,
     const float* __restrict__ stz, T* __restrict__ dq, float* __restrict__ part, float* __restrict__ dS_out,
     float* __restrict__ dz_out, int64_t T_, const Layouts lay, int PB, int64_t LB, float eps) {
-    constexpr int D = Wide::D, NT = Wide::kThreads, NW = Wide::kWaves, LD = Wide::kLD, CPR = Wide::kCPR;
+    constexpr int D = Wide::D, NT = Wide::kThreads, NW = Wide::kWaves, LD = Wide::kLD;
     constexpr int KS = D / 32, NJ = D / 16, E = D * D + D;
     constexpr int BT = 16;
+    // blocks of loads in flight per thread: normalised mode needs the
+    // registers for r and den, which leave room for two
+    constexpr int NS = SIMPLE ? 4 : 2;
     constexpr int LDA = 48;  // row stride (elements) of a wave's A tile: 32 features + 16
-    static_assert(BT * CPR == NT, "one chunk per thread per block");
     __shared__ __attribute__((aligned(16))) Frag<T> sSf[NW * 2 * KS * 64];
-    __shared__ __attribute__((aligned(16))) T sO[BT * LD];
-    __shared__ __attribute__((aligned(16))) T sQ[BT * LD];
+    __shared__ __attribute__((aligned(16))) T sO[2][BT * LD];
     __shared__ __attribute__((aligned(16))) T sA[NW][BT * LDA];
-    __shared__ float sDen[BT];
-    __shared__ float sR[NW][BT];
-    __shared__ float red[NT / 64];
+    __shared__ float sR[2][NW][BT];
+    __shared__ float sDn[2][NW][BT];
+    __shared__ float sZ[D];
+    float* red = &sR[0][0][0];  // the prologue's reductions (sR is free until the loop)
 
     const int wid = xcd_remap(blockIdx.x, gridDim.x);
     const int64_t bh = wid / PB;
@@ -4066,11 +4066,11 @@ __global__ __launch_bounds__(Wide::kThreads, 1) void bwd_dq_wide_kernel(
     const int64_t t1 = min(t0 + LB, T_);
     const int tid = threadIdx.x, lane = tid & 63, wave = wave_index();
     const int m = lane & 15, grp = lane >> 4;
-    const int lr = tid / CPR, lc = tid % CPR;
+    const int f0 = 32 * wave + 8 * grp;  // the lane's eight features
     const float* S = stS + bh * D * D;
     const float* z = stz + bh * D;
     const int nblk = (int)(t1 > t0 ? (t1 - t0 + BT - 1) / BT : 0);
-    const int npad = (nblk + 1) / 2 * 2;
+    const int npad = (nblk + NS - 1) / NS * NS;
 
     const HeadBuf bq = slice_buf(q, lay.q, bh, D, t0, t1), bd = slice_buf(dout, lay.dout, bh, D, t0, t1),
                   bdq = slice_buf(dq, lay.dq, bh, D, t0, t1);
@@ -4078,19 +4078,20 @@ __global__ __launch_bounds__(Wide::kThreads, 1) void bwd_dq_wide_kernel(
         u32x4 q, d;
     };
     auto issue = [&](Stage& st, int blk) {
-        const int64_t row = (int64_t)blk * BT + lr;
-        st.q = __builtin_amdgcn_raw_buffer_load_b128(bq.rsrc, buf_off<T>(row, lay.q.rs, 8 * lc), 0, 0);
-        st.d = __builtin_amdgcn_raw_buffer_load_b128(bd.rsrc, buf_off<T>(row, lay.dout.rs, 8 * lc), 0, 0);
+        const int64_t row = (int64_t)blk * BT + m;
+        st.q = __builtin_amdgcn_raw_buffer_load_b128(bq.rsrc, buf_off<T>(row, lay.q.rs, f0), 0, 0);
+        st.d = __builtin_amdgcn_raw_buffer_load_b128(bd.rsrc, buf_off<T>(row, lay.dout.rs, f0), 0, 0);
     };
-    Stage s0, s1;
-    issue(s0, 0);
-    sched_fence();
-    issue(s1, 1);
-    sched_fence();
+    Stage stg[NS];
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+        issue(stg[i], i);
+        sched_fence();
+    }
 
     // prologue: this wave's S fragments (rows in the permuted order) to LDS,
-    // scaled by 2^sS (f16); z of the loaders' and of the lane's features; the
-    // exponent sw with 2^sw <= sum(z) < 2^(sw+1) that keeps A_t near 1 (f16)
+    // scaled by 2^sS (f16); z to LDS; the exponent sw with 2^sw <= sum(z) <
+    // 2^(sw+1) that keeps A_t near 1 (f16)
     int sS = 0, sw = 0;
     if constexpr (Elt<T>::kScaled) {
         sS = scale_exp(block_absmax_loop<NT>(S, D * D, red));
@@ -4114,12 +4115,7 @@ __global__ __launch_bounds__(Wide::kThreads, 1) void bwd_dq_wide_kernel(
 #pragma unroll
         for (int s = 0; s < KS; ++s)
             sSf[((2 * wave + b) * KS + s) * 64 + lane] = wide_frag<T, false>(S, wave, b, s, m, grp, fS);
-    float zl[8], zq[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        zl[e] = z[32 * wave + 8 * grp + e];  // the lane's dQ features
-        zq[e] = z[8 * lc + e];               // the loader's features
-    }
+    for (int i = tid; i < D; i += NT) sZ[i] = z[i];
 
     f32x4 dsacc[2][NJ];
 #pragma unroll
@@ -4132,36 +4128,31 @@ __global__ __launch_bounds__(Wide::kThreads, 1) void bwd_dq_wide_kernel(
     T* aw = sA[wave];
     const int rA = 4 * grp + (m >> 2), cA = 4 * (m & 3);
 
-    auto put = [&](const Stage& st) {
-        *reinterpret_cast<u32x4*>(&sQ[lr * LD + 8 * lc]) = st.q;
-        *reinterpret_cast<u32x4*>(&sO[lr * LD + 8 * lc]) = st.d;
-        if constexpr (!SIMPLE) {
-            Row<T, 8> raw;
-            __builtin_memcpy(raw.e, &st.q, 16);
-            float d = 0.f;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) d += phi<FM, T>(to_f32(raw.e[e])) * zq[e];
-#pragma unroll
-            for (int off = 16; off > 0; off >>= 1) d += __shfl_xor(d, off);  // the 32 lanes of this row
-            if (lc == 0) sDen[lr] = d;
-        }
-    };
-    auto compute = [&](int blk) {
-        // (b) u = S dO for the wave's features, r over them
-        f32x4 u[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-#pragma unroll
-        for (int s = 0; s < KS; ++s) {
-            const Frag<T> b_ = __builtin_bit_cast(Frag<T>, *reinterpret_cast<const u32x4*>(&sO[m * LD + 32 * s + 8 * grp]));
-#pragma unroll
-            for (int b = 0; b < 2; ++b) u[b] = mma(sSf[((2 * wave + b) * KS + s) * 64 + lane], b_, u[b]);
-        }
+    auto compute = [&](const Stage& st, int blk, int buf) {
+        *reinterpret_cast<u32x4*>(&sO[buf][m * LD + f0]) = st.d;
         Row<T, 8> raw;
-        *reinterpret_cast<u32x4*>(raw.e) = *reinterpret_cast<const u32x4*>(&sQ[m * LD + 32 * wave + 8 * grp]);
-        float ph[8], dph[8], uu[8];
-        float rp = 0.f;
+        __builtin_memcpy(raw.e, &st.q, 16);
+        float ph[8], dph[8];
+        float dp = 0.f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             feature<FM, T>(to_f32(raw.e[e]), ph[e], dph[e]);
+            dp += ph[e] * sZ[f0 + e];
+        }
+        __syncthreads();  // the block's dO tile is complete
+        // (a) u = S dO for the wave's features, r and den over them
+        f32x4 u[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+        const T* oo = sO[buf];
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            const Frag<T> b_ = __builtin_bit_cast(Frag<T>, *reinterpret_cast<const u32x4*>(&oo[m * LD + 32 * s + 8 * grp]));
+#pragma unroll
+            for (int b = 0; b < 2; ++b) u[b] = mma(sSf[((2 * wave + b) * KS + s) * 64 + lane], b_, u[b]);
+        }
+        float uu[8];
+        float rp = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
             uu[e] = u[e >> 2][e & 3] * uS;
             rp += ph[e] * uu[e];
         }
@@ -4169,23 +4160,30 @@ __global__ __launch_bounds__(Wide::kThreads, 1) void bwd_dq_wide_kernel(
         if constexpr (!SIMPLE) {
             rp += __shfl_xor(rp, 16);
             rp += __shfl_xor(rp, 32);
-            if (grp == 0) sR[wave][m] = rp;
+            dp += __shfl_xor(dp, 16);
+            dp += __shfl_xor(dp, 32);
+            if (grp == 0) {
+                sR[buf][wave][m] = rp;
+                sDn[buf][wave][m] = dp;
+            }
             __syncthreads();
-            float r = 0.f;
+            float r = 0.f, den = 0.f;
 #pragma unroll
-            for (int w = 0; w < NW; ++w) r += sR[w][m];
-            inv = 1.f / (sDen[m] + eps);
+            for (int w = 0; w < NW; ++w) {
+                r += sR[buf][w][m];
+                den += sDn[buf][w][m];
+            }
+            inv = 1.f / (den + eps);
             cc = -r * inv * inv;
         }
-        // (c) dQ, then the reduction operand and dz
+        // (b) dQ, then the reduction operand and dz
         Row<T, 8> out;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            const float g = SIMPLE ? uu[e] * eps : uu[e] * inv + cc * zl[e];  // simple_la: eps carries the query scale
+            const float g = SIMPLE ? uu[e] * eps : uu[e] * inv + cc * sZ[f0 + e];  // simple_la: eps carries the query scale
             out.e[e] = static_cast<T>(g * dph[e]);
         }
-        buf_store16(bdq, buf_off<T>((int64_t)blk * BT + m, lay.dq.rs, 32 * wave + 8 * grp),
-                    *reinterpret_cast<const uint4*>(out.e));
+        buf_store16(bdq, buf_off<T>((int64_t)blk * BT + m, lay.dq.rs, f0), *reinterpret_cast<const uint4*>(out.e));
         Row<T, 8> at;
         const float fa = SIMPLE ? 1.f : fw * inv;
 #pragma unroll
@@ -4200,28 +4198,27 @@ __global__ __launch_bounds__(Wide::kThreads, 1) void bwd_dq_wide_kernel(
         for (int rb = 0; rb < 2; ++rb) a[rb] = lds_read_tr(&aw[rA * LDA + 16 * rb + cA]);
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
-            const i16x4 bw = lds_read_tr(&sO[rA * LD + 16 * j + cA]);
+            const i16x4 bw = lds_read_tr(&oo[rA * LD + 16 * j + cA]);
 #pragma unroll
             for (int rb = 0; rb < 2; ++rb) dsacc[rb][j] = mma_k16<T>(a[rb], bw, dsacc[rb][j]);
         }
         wave_lds_sync();
+        sched_fence();  // one block at a time: the dS sums take half the registers
     };
+    __syncthreads();  // the S fragments and z are in LDS
 
-    for (int blk = 0; blk < npad; blk += 2) {
-        __syncthreads();  // every wave is done with the previous block's tiles
-        put(s0);
-        sched_fence();
-        issue(s0, blk + 2);
-        sched_fence();
-        __syncthreads();
-        compute(blk);
-        __syncthreads();
-        put(s1);
-        sched_fence();
-        issue(s1, blk + 3);
-        sched_fence();
-        __syncthreads();
-        compute(blk + 1);
+    // (written out per stage: each stage keeps its own registers). Block n
+    // writes dO tile n % 2, last read by block n - 2: the two barriers of
+    // block n - 1 lie between.
+    for (int blk = 0; blk < npad; blk += NS) {
+#pragma unroll
+        for (int i = 0; i < NS; ++i) {
+            const Stage cur = stg[i];
+            sched_fence();
+            issue(stg[i], blk + i + NS);
+            sched_fence();
+            compute(cur, blk + i, i & 1);
+        }
     }
 
     // dz over the lanes of each feature group (tokens), in a fixed order
@@ -4249,7 +4246,7 @@ __global__ __launch_bounds__(Wide::kThreads, 1) void bwd_dq_wide_kernel(
     }
     if (m == 0)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) oz[32 * wave + 8 * grp + e] = SIMPLE ? 0.f : dzp[e];
+        for (int e = 0; e < 8; ++e) oz[f0 + e] = SIMPLE ? 0.f : dzp[e];
 }
 
 // ---------------------------------------------------------------------------
