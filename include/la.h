@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define LA_VERSION 7
+#define LA_VERSION 8
 
 typedef enum {
     LA_F32 = 0,
@@ -174,7 +174,28 @@ size_t la_state_bytes(const la_problem* p);
  * this problem (the largest of them). 0 for an invalid problem. */
 size_t la_workspace_bytes(const la_problem* p);
 
-/* Forward: O (and the state S, z) from Q, K, V. Runs la_fwd_state, then
+/* How a problem's tokens are split across workgroups, per step: a pure
+ * function of the problem (shape, dtype, flags), the same for every call. The
+ * split-T reduction of the forward (steps 1-3; with LA_CAUSAL also the scan
+ * segments) cuts each head into P slices of L tokens, the backward's Q side
+ * (steps 5-6) into PB slices of LB tokens; the output (step 4) and the
+ * backward's K/V side (step 7) run NQ chunks of LQ and NK chunks of LK tokens
+ * per head. The method itself names no split (any split gives the same S, z up
+ * to rounding order); this is for logs and benchmarks. */
+typedef struct {
+    int64_t P, L, PB, LB, NQ, LQ, NK, LK;
+} la_split;
+
+/* Fills *out for a valid problem and returns LA_OK; otherwise returns the
+ * validation error (LA_ERR_NULL when p or out is NULL) and leaves *out as it
+ * was. Makes no HIP call. */
+int la_split_of(const la_problem* p, la_split* out);
+
+/* Forward: O (and the state S, z) from Q, K, V (Flash Bi-directional Linear
+ * Attention README: the introduction names the operation, "Update"
+ * 2024-12-28 its simple_la form, and the Benchmarks table times this call as
+ * its fwd column; with LA_CAUSAL, flash-linear-attention README, "Different
+ * forms of linear attention"). Runs la_fwd_state, then
  * la_fwd_output. `state` may be NULL when the caller does not keep it; the
  * workspace then holds it. With LA_CAUSAL: the state reduction per token
  * segment, exclusive prefixes of the segment states, then one chunked scan
@@ -182,7 +203,11 @@ size_t la_workspace_bytes(const la_problem* p);
 int la_fwd(const la_problem* p, const void* q, const void* k, const void* v,
            void* o, void* state, void* ws, size_t ws_bytes, void* stream);
 
-/* Backward: dQ, dK, dV from Q, K, V, dO and the state la_fwd wrote (the
+/* Backward (Flash Bi-directional Linear Attention README, "Update"
+ * 2024-12-30, which names the backward, and the Benchmarks table's bwd
+ * column; the pages print no gradient formula, so the gradients are those of
+ * the forward's formulas by the chain rule): dQ, dK, dV from Q, K, V, dO and
+ * the state la_fwd wrote (the
  * state is required: S and z are not recomputed). Runs la_bwd_dq, then
  * la_bwd_dkv. With LA_CAUSAL: the vector-Jacobian product of sum(O * dO)
  * through the recurrent form (eps held constant); `state` is not read and may
@@ -224,24 +249,29 @@ int la_fwd_noalloc(const la_problem* p, const void* q, const void* k, const void
 /* ---- The steps of the path, one call each (la_fwd and la_bwd are exactly
  * these calls in order). ---- */
 
-/* Steps 1-3: phi on K, split-T reduction of each head's token range into
+/* Steps 1-3 (the S and z sums of the forward, Flash Bi-directional Linear
+ * Attention README, introduction): phi on K, split-T reduction of each head's token range into
  * partial (S, z) on MFMA, then a fixed-order sum of the partials into
  * `state` (non-NULL here). */
 int la_fwd_state(const la_problem* p, const void* k, const void* v, void* state,
                  void* ws, size_t ws_bytes, void* stream);
 
-/* Step 4: O_t = phi(q_t) S / (phi(q_t) . z + eps) (or phi(q_t) S) from a
+/* Step 4 (the forward's output, Flash Bi-directional Linear Attention README,
+ * introduction, and "Update" 2024-12-28 for simple_la):
+ * O_t = phi(q_t) S / (phi(q_t) . z + eps) (or phi(q_t) S) from a
  * complete state. Needs no workspace. */
 int la_fwd_output(const la_problem* p, const void* q, const void* state, void* o,
                   void* stream);
 
-/* Steps 5-6: dQ, and the backward state dS = sum_t phi(q_t) (dO_t/den_t)^T,
+/* Steps 5-6 (first half of the backward, Flash Bi-directional Linear
+ * Attention README, "Update" 2024-12-30): dQ, and the backward state dS = sum_t phi(q_t) (dO_t/den_t)^T,
  * dz = sum_t c_t phi(q_t) (simple_la: dS = phi(Q)^T dO, dz = 0), reduced split-T
  * with a fixed-order combine into the workspace. */
 int la_bwd_dq(const la_problem* p, const void* q, const void* dout, const void* state,
               void* dq, void* ws, size_t ws_bytes, void* stream);
 
-/* Step 7: dK = (dS v_t + dz) * phi'(k_t), dV_t = dS^T phi(k_t) (dS is D x Dv), reading the
+/* Step 7 (second half of the backward, same passage):
+ * dK = (dS v_t + dz) * phi'(k_t), dV_t = dS^T phi(k_t) (dS is D x Dv), reading the
  * backward state that la_bwd_dq left in the same workspace. */
 int la_bwd_dkv(const la_problem* p, const void* k, const void* v, void* dk, void* dv,
                void* ws, size_t ws_bytes, void* stream);

@@ -19,7 +19,7 @@ import torch
 
 __all__ = [
     "LAError", "lib", "fwd", "bwd", "fwd_noalloc", "NOALLOC_SCRATCH_BYTES", "Strides", "TensorStrides", "fwd_state", "fwd_output", "bwd_dq", "bwd_dkv", "linear_attention",
-    "state_bytes", "workspace_bytes", "new_state", "workspace", "Problem",
+    "state_bytes", "workspace_bytes", "split_of", "Split", "new_state", "workspace", "Problem",
     "LA_F32", "LA_F16", "LA_BF16", "LA_SIMPLE", "LA_LAYOUT_BTHD", "LA_PHI_RELU", "LA_PHI_IDENTITY", "LA_CAUSAL",
     "EXPORTS",
 ]
@@ -37,9 +37,16 @@ DTYPE_CODE = {torch.float32: LA_F32, torch.float16: LA_F16, torch.bfloat16: LA_B
 
 # Every symbol include/la.h declares.
 EXPORTS = ("la_version", "la_status_str", "la_state_bytes", "la_workspace_bytes", "la_fwd",
-           "la_bwd", "la_fwd_state", "la_fwd_output", "la_bwd_dq", "la_bwd_dkv", "la_fwd_noalloc")
+           "la_bwd", "la_fwd_state", "la_fwd_output", "la_bwd_dq", "la_bwd_dkv", "la_fwd_noalloc",
+           "la_split_of")
 # Size of the static device scratch behind la_fwd_noalloc (LA_NOALLOC_SCRATCH_BYTES).
 NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+class Split(ctypes.Structure):
+    """Mirror of la_split: P slices of L tokens (forward reduction), PB of LB
+    (backward Q side), NQ chunks of LQ (output), NK of LK (backward K/V side)."""
+    _fields_ = [(n, ctypes.c_int64) for n in ("P", "L", "PB", "LB", "NQ", "LQ", "NK", "LK")]
 
 
 class TensorStrides(ctypes.Structure):
@@ -98,6 +105,7 @@ def lib() -> ctypes.CDLL:
         "la_bwd_dq": [P, vp, vp, vp, vp, vp, sz, vp],
         "la_bwd_dkv": [P, vp, vp, vp, vp, vp, sz, vp],
         "la_fwd_noalloc": [P, vp, vp, vp, vp, vp, vp],
+        "la_split_of": [P, ctypes.POINTER(Split)],
     }
     for name, args in sigs.items():
         fn = getattr(L, name)
@@ -203,6 +211,13 @@ def _ptr(x: torch.Tensor | None):
 
 def _stream(device: torch.device):
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def split_of(prob: Problem) -> dict:
+    """The library's token split for this problem, per step (la_split_of)."""
+    out = Split()
+    _check(lib().la_split_of(ctypes.byref(prob), ctypes.byref(out)))
+    return {name: int(getattr(out, name)) for name, _ in Split._fields_}
 
 
 def state_bytes(prob: Problem) -> int:

@@ -324,6 +324,16 @@ size_t la_workspace_bytes(const la_problem* p) {
     return make_plan(p).ws_bytes;
 }
 
+int la_split_of(const la_problem* p, la_split* out) {
+    if (!p || !out) return LA_ERR_NULL;
+    la_status st = check_problem(p);
+    if (st != LA_OK) return st;
+    if ((p->flags & LA_CAUSAL) && (st = check_causal(p)) != LA_OK) return st;
+    const la::Plan pl = make_plan(p);
+    *out = la_split{pl.P, pl.L, pl.PB, pl.LB, pl.NQ, pl.LQ, pl.NK, pl.LK};
+    return LA_OK;
+}
+
 int la_fwd_state(const la_problem* p, const void* k, const void* v, void* state, void* ws,
                  size_t ws_bytes, void* stream) {
     la_status st = check_problem(p);

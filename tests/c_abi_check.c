@@ -30,6 +30,12 @@ int main(void) {
     CHECK(strncmp(la_status_str(LA_ERR_HEAD_DIM), "LA_ERR_HEAD_DIM", 15) == 0);
     CHECK(la_state_bytes(&p) == (size_t)(2 * 3 * (64 * 64 + 64) * 4));
     CHECK(la_workspace_bytes(&p) > 0);
+    {
+        la_split sp;
+        CHECK(la_split_of(&p, &sp) == LA_OK);
+        CHECK(sp.P >= 1 && sp.P * sp.L >= p.T && sp.NK >= 1 && sp.NK * sp.LK >= p.T);
+        CHECK(la_split_of(&p, NULL) == LA_ERR_NULL);
+    }
 
     /* validation errors, before any HIP call */
     CHECK(la_fwd(NULL, NULL, NULL, NULL, NULL, NULL, NULL, 0, NULL) == LA_ERR_NULL);

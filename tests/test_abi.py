@@ -48,7 +48,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.la_version() == 7
+    assert L.la_version() == 8
     for s in range(14):
         txt = L.la_status_str(s).decode()
         assert txt.startswith("LA_"), txt
@@ -98,6 +98,38 @@ def test_workspace_is_pure_function_of_shape(L):
     a = L.la_workspace_bytes(ctypes.byref(prob(B=2, H=8, T=262144, D=64, dtype=2, flags=1)))
     b = L.la_workspace_bytes(ctypes.byref(prob(B=2, H=8, T=262144, D=64, dtype=2, flags=1)))
     assert a == b > 0
+
+
+def test_split_query(L):
+    """la_split_of: each step's pieces cover the head's tokens exactly (the
+    last piece may be short, none is empty), the answer is a pure function of
+    the problem, and invalid problems or NULL pointers return the error and
+    leave the output untouched."""
+    for kw in (dict(B=8, H=16, T=16384, D=64), dict(B=1, H=1, T=1 << 20, D=128, dtype=2),
+               dict(B=4, H=3, T=1, D=32, Dv=96, dtype=0), dict(B=8, H=16, T=4096, D=256),
+               dict(B=2, H=8, T=262144, D=64, flags=0x10), dict(B=3, H=5, T=0, D=64)):
+        p = prob(**kw)
+        out = la.Split()
+        assert L.la_split_of(ctypes.byref(p), ctypes.byref(out)) == 0, kw
+        T = kw["T"]
+        for n, length in (("P", "L"), ("PB", "LB"), ("NQ", "LQ"), ("NK", "LK")):
+            pieces, size = getattr(out, n), getattr(out, length)
+            assert pieces >= 1, (kw, n)
+            if T > 0:
+                assert pieces * size >= T and (pieces - 1) * size < T, (kw, n, pieces, size)
+        again = la.Split()
+        L.la_split_of(ctypes.byref(p), ctypes.byref(again))
+        assert bytes(again) == bytes(out)
+    # the long single head is cut into more slices than one
+    out = la.Split()
+    L.la_split_of(ctypes.byref(prob(B=1, H=1, T=1 << 20, D=64)), ctypes.byref(out))
+    assert out.P > 1 and out.PB > 1
+    sentinel = la.Split(*([-7] * 8))
+    assert L.la_split_of(ctypes.byref(prob(D=48)), ctypes.byref(sentinel)) == HEAD_DIM
+    assert L.la_split_of(ctypes.byref(prob(dtype=9)), ctypes.byref(sentinel)) == DTYPE
+    assert list(bytes(sentinel)) == list(bytes(la.Split(*([-7] * 8))))
+    assert L.la_split_of(None, ctypes.byref(sentinel)) == NULL
+    assert L.la_split_of(ctypes.byref(prob()), None) == NULL
 
 
 A = 0x100000  # fake, 256-aligned, never dereferenced
