@@ -297,6 +297,7 @@ def causal_bench(args, w, t, do_flush) -> int:
         "fwd_frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
         "bwd_ms": round(float(np.mean(bwd_ms)), 4),
         "bwd_ms_median": round(float(np.median(bwd_ms)), 4),
+        "split": la.split_of(prob),
         "bwd_GBps_algorithmic": round(bwd_rate, 1),
         "bwd_frac_of_hbm_peak": round(bwd_rate / HBM_PEAK_GBS, 4),
         "wall_ms_per_step_incl_flush": round(wall / args.steps * 1e3, 4),
@@ -471,6 +472,7 @@ def main() -> int:
         "wall_ms_per_step_incl_flush": round(wall / args.steps * 1e3, 4),
         **({"other_cache_conditions": other} if other else {}),
         "bit_identical_rerun": bit_identical,
+        "split": la.split_of(prob),
         "versions": versions(),
         "roofline": {
             "kernel": dominant,

@@ -126,7 +126,11 @@ def make_problem(shape, dtype: torch.dtype, eps: float, simple: bool, layout: st
     """Problem for Q/K-side tensors of ``shape``: [B, H, T, D] (layout "bhtd")
     or [B, T, H, D] (layout "bthd"), V-side tensors with head size ``dv``
     (None: D); feature map phi "elu1" (elu(x) + 1), "relu" or "identity";
-    ``scale`` multiplies phi(q) (None: 1)."""
+    ``scale`` multiplies phi(q) (None: 1). A zero scale is refused here: in
+    the C struct 0 stands for 1 (a zero-initialised problem), which a caller
+    who asks for 0 would not expect."""
+    if scale is not None and float(scale) == 0.0:
+        raise ValueError("scale must be non-zero (None for no scale)")
     if layout not in LAYOUTS:
         raise ValueError(f"layout must be one of {LAYOUTS}, got {layout!r}")
     if phi not in FEATURE_MAPS:
@@ -414,6 +418,6 @@ def linear_attention(q, k, v, *, eps: float = 1e-6, simple: bool = False, layout
     float32, float16 or bfloat16, with D (of q, k) and Dv (of v) each in
     {32, 64, 96, 128}; phi is "elu1" (elu + 1),
     "relu" or "identity". causal=True: token t attends to tokens s <= t
-    (f16/bf16, D and Dv in {64, 128}). scale multiplies phi(q) (None: 1)."""
+    (f16/bf16, D and Dv in {64, 128}). scale multiplies phi(q) (None: 1; 0 is refused)."""
     return _LinearAttention.apply(q, k, v, float(eps), bool(simple), layout, phi, bool(causal),
                                   None if scale is None else float(scale))

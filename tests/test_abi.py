@@ -289,6 +289,10 @@ def test_binding_marshalling_rejects_cpu_tensors():
         la.make_problem((1, 4, 64), torch.float16, 1e-6, False)
     with pytest.raises(ValueError):
         la.make_problem((1, 1, 4, 64), torch.int32, 1e-6, False)
+    # a zero scale would read as "no scale" in the C struct: the binding refuses it
+    with pytest.raises(ValueError):
+        la.make_problem((1, 1, 4, 64), torch.float16, 1e-6, False, scale=0.0)
+    assert la.make_problem((1, 1, 4, 64), torch.float16, 1e-6, False, scale=-0.5).scale == -0.5
 
 
 def test_binding_validates_state_buffers():

@@ -3,6 +3,8 @@ scale * phi(q)) against the fp64 oracle with the same scale: the bidirectional
 and causal paths, forward and backward, both modes, the step calls, autograd,
 a full-size simple_la case; scale 1 is byte-identical to no scale. eps is
 large in normalised mode so that eps / scale visibly moves the result."""
+import ctypes
+
 import numpy as np
 import pytest
 import torch
@@ -88,12 +90,23 @@ def test_scale_one_is_no_scale(causal):
     x = make_inputs(w, with_grad=True)
     dev = {n: to_device(a, "f16") for n, a in x.items()}
     outs = []
-    for sc in (None, 1.0, 0.0):  # 0 in the struct stands for 1
+    for sc in (None, 1.0):
         o, st = la.fwd(dev["q"], dev["k"], dev["v"], eps=w.eps, scale=sc, causal=causal)
         g = la.bwd(dev["q"], dev["k"], dev["v"], dev["do"], None if causal else st, eps=w.eps, scale=sc,
                    causal=causal)
         outs.append((o,) + tuple(g))
+    # a zero scale in the C struct stands for 1 (the binding refuses 0 itself)
+    prob = la.make_problem(dev["q"].shape, dev["q"].dtype, w.eps, False, causal=causal)
+    prob.scale = 0.0
+    o0 = torch.empty_like(outs[0][0])
+    ws = la.workspace(prob, dev["q"].device)
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    ptr = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+    status = la.lib().la_fwd(ctypes.byref(prob), ptr(dev["q"]), ptr(dev["k"]), ptr(dev["v"]), ptr(o0), None,
+                             ptr(ws), ctypes.c_size_t(ws.numel()), stream)
+    assert status == 0
     torch.cuda.synchronize()
+    assert bytes_equal(o0, outs[0][0])
     for other in outs[1:]:
         for a, b in zip(outs[0], other):
             assert bytes_equal(a, b)
