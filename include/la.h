@@ -100,12 +100,14 @@ typedef enum {
 /* Causal (autoregressive) attention: token t attends to tokens s <= t,
  *     O_t = phi(q_t) S_t / (phi(q_t) . z_t + eps),  S_t = sum_{s<=t} phi(k_s) v_s^T,
  * z_t = sum_{s<=t} phi(k_s) (flash-linear-attention README, "Different forms
- * of linear attention"). Accepted by la_fwd and la_bwd, for f16 and bf16
- * with D and Dv in {64, 128}; la_fwd's `state` receives the full-sequence S,
- * z, bit-identical to the non-causal call; la_bwd does not read `state`. The
- * step calls return LA_ERR_FLAGS with it; other dtypes give LA_ERR_DTYPE and
- * other head sizes LA_ERR_HEAD_DIM. la_workspace_bytes counts the causal
- * backward's scratch when the flag is set. */
+ * of linear attention"). Accepted by la_fwd and la_bwd for every dtype and
+ * every D, Dv in {32, 64, 96, 128} (not 256: LA_ERR_HEAD_DIM). f16 and bf16
+ * with D and Dv in {64, 128} run scans on 16-bit MFMA operands; every other
+ * shape runs scans on fp32 operands (fp32 MFMA, the 16-bit inputs widened).
+ * la_fwd's `state` receives the full-sequence S, z, bit-identical to the
+ * non-causal call; la_bwd does not read `state`. The step calls return
+ * LA_ERR_FLAGS with it. la_workspace_bytes counts the causal backward's
+ * scratch when the flag is set. */
 #define LA_CAUSAL 0x10u
 
 /* Strides of one tensor, in elements: element f of token t of head h of

@@ -293,8 +293,8 @@ def fwd_output(q, state, *, eps=1e-6, simple=False, layout="bhtd", phi="elu1", o
 def fwd(q, k, v, *, eps=1e-6, simple=False, layout="bhtd", phi="elu1", out=None, state=None, ws=None,
         causal=False, scale=None):
     """O = phi(Q) S / (phi(Q) z + eps) (or phi(Q) S); returns (O, state).
-    causal=True: token t attends to tokens s <= t (f16/bf16, D and Dv in
-    {64, 128}); the state is still that of the whole sequence."""
+    causal=True: token t attends to tokens s <= t (D and Dv up to 128); the
+    state is still that of the whole sequence."""
     _tensor(q, None, "q")
     _tensor(k, q, "k")
     dv = v.shape[-1] if isinstance(v, torch.Tensor) else None
@@ -362,8 +362,8 @@ def bwd_dkv(k, v, *, eps=1e-6, simple=False, layout="bhtd", phi="elu1", dk=None,
 def bwd(q, k, v, do, state=None, *, eps=1e-6, simple=False, layout="bhtd", phi="elu1", dq=None, dk=None, dv=None,
         ws=None, causal=False, scale=None):
     """dQ, dK, dV of L = sum(O * dO), from the state fwd returned.
-    causal=True: the backward of the causal form (f16/bf16, D and Dv in
-    {64, 128}); no state is read (pass None)."""
+    causal=True: the backward of the causal form (D and Dv up to 128); no
+    state is read (pass None)."""
     _tensor(q, None, "q")
     _tensor(k, q, "k")
     hv = v.shape[-1] if isinstance(v, torch.Tensor) else None
@@ -418,6 +418,6 @@ def linear_attention(q, k, v, *, eps: float = 1e-6, simple: bool = False, layout
     float32, float16 or bfloat16, with D (of q, k) and Dv (of v) each in
     {32, 64, 96, 128}; phi is "elu1" (elu + 1),
     "relu" or "identity". causal=True: token t attends to tokens s <= t
-    (f16/bf16, D and Dv in {64, 128}). scale multiplies phi(q) (None: 1; 0 is refused)."""
+    (any dtype, D and Dv up to 128). scale multiplies phi(q) (None: 1; 0 is refused)."""
     return _LinearAttention.apply(q, k, v, float(eps), bool(simple), layout, phi, bool(causal),
                                   None if scale is None else float(scale))

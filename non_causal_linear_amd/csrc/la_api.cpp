@@ -181,9 +181,8 @@ la_status check_all_strides(const la_problem* p, std::initializer_list<Tensor> i
 
 // What the causal forward supports, on a problem check_problem accepted.
 la_status check_causal(const la_problem* p) {
-    if (p->dtype != LA_F16 && p->dtype != LA_BF16) return LA_ERR_DTYPE;
-    const int64_t dv = dv_of(p);
-    if ((p->D != 64 && p->D != 128) || (dv != 64 && dv != 128)) return LA_ERR_HEAD_DIM;
+    // every dtype and head size except 256 (the wide kernels have no causal form)
+    if (p->D == 256 || dv_of(p) == 256) return LA_ERR_HEAD_DIM;
     return LA_OK;
 }
 

@@ -3579,6 +3579,594 @@ __global__ __launch_bounds__(kThreads, (CausalBwdShape<DK, DV>::kMinBlocks)) voi
 }
 
 // ---------------------------------------------------------------------------
+// Causal scans on fp32 operands: the causal shapes the 16-bit scans above do
+// not take (fp32 inputs, and 16-bit inputs with D or Dv of 32 or 96).
+// ---------------------------------------------------------------------------
+// The same recurrences, segments, prefix and suffix kernels and workspace as
+// the 16-bit scans, in a plainer form. A chunk's tiles are staged in LDS as
+// fp32 (phi applied on the way, rows past the segment end zeroed), the running
+// state (R, z forward; G, g in the reverse scan) stays in LDS, and every
+// product is cut into 16 x 16 result tiles dealt round-robin to the four
+// waves, each tile a chain of 16x16x4 fp32 MFMAs reading both operands from
+// LDS. fp32 MFMA runs at the fp32 vector rate, so these scans are bound by
+// their products (about 4 D Dv + 2 C (D + Dv) multiply-adds per token), not by
+// HBM. Chunks are 32 tokens: a 128 x 128 fp32 state plus the chunk's tiles
+// fit one workgroup's LDS. The next chunk's loads are in flight in registers
+// while a chunk is processed.
+struct CF {
+    static constexpr int C = 32;             // tokens per chunk
+    static constexpr int NT = C / 16;        // 16-token blocks per chunk
+    static constexpr int NL = NT * (NT + 1) / 2;  // blocks on or below the diagonal
+    static constexpr int LC = C + 4;         // row stride of C x C tiles (floats)
+};
+
+// Block (tb, sb), sb <= tb, of the n-th block on or below the diagonal.
+__device__ __forceinline__ void lower_block(int n, int& tb, int& sb) {
+    tb = 0;
+    while (n > tb) {
+        n -= tb + 1;
+        ++tb;
+    }
+    sb = n;
+}
+
+// acc[m][n] += sum_{k0 <= k < k1} X(m, k) Y(n, k) over one 16 x 16 tile on
+// 16x16x4 fp32 MFMA. X(m, k) = x[m ldx + k] when XK (k contiguous), else
+// x[k ldx + m]; the same for Y. With XS, X(m, k) is also multiplied by xs[k].
+// Lane (m, g) = (lane % 16, lane / 16) feeds k = k' + 4 g + e to the e-th
+// MFMA of each 16-wide step k' (the same permutation of the contraction index
+// for both operands). k0 and k1 are multiples of 16. The result sits in the
+// MFMA layout: lane (m, g), register r holds row 4 g + r, column m.
+template <bool XK, bool YK, bool XS = false>
+__device__ __forceinline__ f32x4 tile_f32(f32x4 acc, const float* x, int ldx, const float* y, int ldy, int k0,
+                                          int k1, const float* xs = nullptr) {
+    const int lane = threadIdx.x & 63, m = lane & 15, g = lane >> 4;
+#pragma unroll 2
+    for (int kk = k0; kk < k1; kk += 16) {
+        const int k = kk + 4 * g;
+        float a[4], b[4];
+        if constexpr (XK) {
+            const float4 t = *reinterpret_cast<const float4*>(x + m * ldx + k);
+            a[0] = t.x, a[1] = t.y, a[2] = t.z, a[3] = t.w;
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) a[e] = x[(k + e) * ldx + m];
+        }
+        if constexpr (YK) {
+            const float4 t = *reinterpret_cast<const float4*>(y + m * ldy + k);
+            b[0] = t.x, b[1] = t.y, b[2] = t.z, b[3] = t.w;
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) b[e] = y[(k + e) * ldy + m];
+        }
+        if constexpr (XS) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) a[e] *= xs[k + e];
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[e], b[e], acc, 0, 0, 0);
+    }
+    return acc;
+}
+
+// One chunk (CF::C rows of W elements) of a tensor in flight: 16-byte pieces
+// dealt over the workgroup's threads, loaded unconditionally through the
+// segment's buffer descriptor (rows past its end read zeros).
+template <typename T, int W>
+struct ChunkLoad {
+    static constexpr int VEC = 16 / (int)sizeof(T), PPR = W / VEC, NP = CF::C * PPR;
+    static constexpr int NPT = (NP + kThreads - 1) / kThreads;
+    u32x4 x[NPT];
+    __device__ __forceinline__ void issue(const HeadBuf& b, int64_t rs, int64_t row0) {
+#pragma unroll
+        for (int i = 0; i < NPT; ++i) {
+            const int n = min((int)threadIdx.x + kThreads * i, NP - 1);
+            x[i] = __builtin_amdgcn_raw_buffer_load_b128(b.rsrc, buf_off<T>(row0 + n / PPR, rs, VEC * (n % PPR)), 0, 0);
+        }
+    }
+    // Row r, element j of the chunk goes to dst[r ld + j] as f(r, value).
+    template <typename F>
+    __device__ __forceinline__ void put(float* dst, int ld, F f) const {
+#pragma unroll
+        for (int i = 0; i < NPT; ++i) {
+            const int n = (int)threadIdx.x + kThreads * i;
+            if (NP % kThreads == 0 || n < NP) {
+                const int r = n / PPR, c0 = VEC * (n % PPR);
+                const T* e = reinterpret_cast<const T*>(&x[i]);
+                float y[VEC];
+#pragma unroll
+                for (int j = 0; j < VEC; ++j) y[j] = f(r, to_f32(e[j]));
+#pragma unroll
+                for (int j = 0; j < VEC; j += 4)
+                    *reinterpret_cast<float4*>(dst + r * ld + c0 + j) = make_float4(y[j], y[j + 1], y[j + 2], y[j + 3]);
+            }
+        }
+    }
+};
+
+// Rows [0, CF::C) of an fp32 LDS tile (row stride ld) rounded to T and stored
+// as 16-byte pieces at rows row0.. of a segment (rows past its end dropped).
+template <typename T, int W>
+__device__ __forceinline__ void store_chunk(const float* src, int ld, const HeadBuf& b, int64_t rs, int64_t row0) {
+    constexpr int VEC = 16 / (int)sizeof(T), PPR = W / VEC, NP = CF::C * PPR;
+    for (int n = threadIdx.x; n < NP; n += kThreads) {
+        const int r = n / PPR, c0 = VEC * (n % PPR);
+        Row<T, VEC> out;
+#pragma unroll
+        for (int j = 0; j < VEC; ++j) out.e[j] = static_cast<T>(src[r * ld + c0 + j]);
+        buf_store16(b, buf_off<T>(row0 + r, rs, c0), *reinterpret_cast<const uint4*>(out.e));
+    }
+}
+
+// Causal forward, fp32 operands: one workgroup per segment, 32-token chunks
+// in order. Per chunk, with R, z the state before it:
+//   A = mask(phi(Q) phi(K)^T) (s <= t), 1/den_t = 1 / (phi(q_t) . z + sum_s A_ts + eps),
+//   O = (phi(Q) R + A V) / den (simple_la: times the query scale instead),
+//   R += phi(K)^T V, z += sum_s phi(k_s).
+template <typename T, int DK, int DV, bool SIMPLE, int FM>
+__global__ __launch_bounds__(kThreads) void fwd_causal_f32_kernel(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const float* __restrict__ pre,
+    T* __restrict__ o, int64_t T_, const Layouts lay, int P, int64_t L, float eps) {
+    constexpr int C = CF::C, NT = CF::NT, NL = CF::NL, LC = CF::LC;
+    constexpr int NI = DK / 16, NJ = DV / 16, LK = DK + 4, LV = DV + 4;
+    __shared__ __attribute__((aligned(16))) float sR[DK * LV];
+    __shared__ __attribute__((aligned(16))) float sQ[C * LK];
+    __shared__ __attribute__((aligned(16))) float sK[C * LK];
+    __shared__ __attribute__((aligned(16))) float sV[C * LV];
+    __shared__ __attribute__((aligned(16))) float sO[C * LV];
+    __shared__ __attribute__((aligned(16))) float sA[C * LC];
+    __shared__ float sZ[DK], sRcp[C];
+
+    const int wid = xcd_remap(blockIdx.x, gridDim.x);
+    const int64_t bh = wid / P;
+    const int p = wid % P;
+    const int tid = threadIdx.x, lane = tid & 63, wave = wave_index();
+    const int m = lane & 15, g = lane >> 4;
+    const int64_t t0 = (int64_t)p * L, t1 = min(t0 + L, T_), len = t1 - t0;
+    const int nch = (int)(len > 0 ? (len + C - 1) / C : 0);
+
+    const float* st = pre ? pre + (bh * P + p) * (int64_t)(DK * DV + DK) : nullptr;
+    for (int e = tid; e < DK * DV; e += kThreads) sR[(e / DV) * LV + e % DV] = st ? st[e] : 0.f;
+    for (int e = tid; e < DK; e += kThreads) sZ[e] = st ? st[DK * DV + e] : 0.f;
+
+    const HeadBuf bq = slice_buf(q, lay.q, bh, DK, t0, t1), bk = slice_buf(k, lay.k, bh, DK, t0, t1);
+    const HeadBuf bv = slice_buf(v, lay.v, bh, DV, t0, t1), bo = slice_buf(o, lay.o, bh, DV, t0, t1);
+    ChunkLoad<T, DK> lq, lk;
+    ChunkLoad<T, DV> lv;
+    lq.issue(bq, lay.q.rs, 0);
+    lk.issue(bk, lay.k.rs, 0);
+    lv.issue(bv, lay.v.rs, 0);
+
+    for (int c = 0; c < nch; ++c) {
+        const int nvalid = (int)min((int64_t)C, len - (int64_t)c * C);
+        const auto feat = [&](int r, float x) { return r < nvalid ? phi<FM, T>(x) : 0.f; };
+        lq.put(sQ, LK, feat);
+        lk.put(sK, LK, feat);
+        lv.put(sV, LV, [](int, float x) { return x; });
+        const int64_t next = (int64_t)min(c + 1, nch - 1) * C;
+        lq.issue(bq, lay.q.rs, next);
+        lk.issue(bk, lay.k.rs, next);
+        lv.issue(bv, lay.v.rs, next);
+        __syncthreads();
+
+        for (int n = wave; n < NL; n += kWaves) {
+            int tb, sb;
+            lower_block(n, tb, sb);
+            const f32x4 a = tile_f32<true, true>(f32x4{0.f, 0.f, 0.f, 0.f}, sQ + 16 * tb * LK, LK, sK + 16 * sb * LK,
+                                                 LK, 0, DK);
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                sA[(16 * tb + 4 * g + r) * LC + 16 * sb + m] = (sb < tb || m <= 4 * g + r) ? a[r] : 0.f;
+        }
+        __syncthreads();
+
+        if (tid < C) {
+            if constexpr (SIMPLE) {
+                sRcp[tid] = eps;  // the query scale
+            } else {
+                float den = 0.f;
+                for (int s = 0; s <= tid; ++s) den += sA[tid * LC + s];
+                float qz = 0.f;
+                for (int i = 0; i < DK; ++i) qz += sQ[tid * LK + i] * sZ[i];
+                sRcp[tid] = 1.f / (qz + den + eps);
+            }
+        }
+        __syncthreads();
+
+#pragma unroll 1
+        for (int jj = 0; jj < NT * NJ / kWaves; ++jj) {
+            const int n = wave + kWaves * jj, tb = n / NJ, jb = n % NJ;
+            f32x4 acc = tile_f32<true, false>(f32x4{0.f, 0.f, 0.f, 0.f}, sQ + 16 * tb * LK, LK, sR + 16 * jb, LV, 0, DK);
+            acc = tile_f32<true, false>(acc, sA + 16 * tb * LC, LC, sV + 16 * jb, LV, 0, 16 * (tb + 1));
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = 16 * tb + 4 * g + r;
+                sO[row * LV + 16 * jb + m] = acc[r] * sRcp[row];
+            }
+        }
+        __syncthreads();
+
+#pragma unroll 1
+        for (int jj = 0; jj < NI * NJ / kWaves; ++jj) {
+            const int n = wave + kWaves * jj, ib = n / NJ, jb = n % NJ;
+            float* rt = sR + 16 * ib * LV + 16 * jb;
+            f32x4 acc;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[r] = rt[(4 * g + r) * LV + m];
+            acc = tile_f32<false, false>(acc, sK + 16 * ib, LK, sV + 16 * jb, LV, 0, C);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) rt[(4 * g + r) * LV + m] = acc[r];
+        }
+        for (int i = tid; i < DK; i += kThreads) {
+            float s = 0.f;
+            for (int r = 0; r < C; ++r) s += sK[r * LK + i];
+            sZ[i] += s;
+        }
+        store_chunk<T, DV>(sO, LV, bo, lay.o.rs, (int64_t)c * C);
+        __syncthreads();
+    }
+}
+
+// Forward-order dQ scan, fp32 operands. Per chunk, with R, z the state
+// before it (the quantities of the 16-bit scan's comment):
+//   A = mask(phi(Q) phi(K)^T), B = mask(dO V^T) (s <= t), Y = dO R^T;
+//   den_t = phi(q_t) . z + sum_s A_ts + eps, w_t = 1 / den_t,
+//   c_t = -(phi(q_t) . Y_t + sum_s A_ts B_ts) w_t^2   (simple_la: w = scale, c = 0);
+//   P = mask(w B + c), dphi(Q) = w Y + c z^T + P phi(K), dQ = dphi(Q) phi'(Q);
+//   R += phi(K)^T V, z += sum_s phi(k_s);
+// and w_t, c^_t = c_t / w_t per token into wc (normalised mode). With
+// gpart (P > 1) the segment's own sums G = sum_t w_t phi(q_t) dO_t^T and
+// g = sum_t c_t phi(q_t) are kept (G in registers, spread over the waves) and
+// written there at the end.
+template <typename T, int DK, int DV, bool SIMPLE, int FM>
+__global__ __launch_bounds__(kThreads) void bwd_causal_q_f32_kernel(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const T* __restrict__ dout,
+    const float* __restrict__ pre, T* __restrict__ dq, float* __restrict__ wc, float* __restrict__ gpart, int64_t T_,
+    const Layouts lay, int P, int64_t L, float eps) {
+    constexpr int C = CF::C, NT = CF::NT, NL = CF::NL, LC = CF::LC;
+    constexpr int NI = DK / 16, NJ = DV / 16, LK = DK + 4, LV = DV + 4;
+    constexpr int NY = NT * NI / kWaves;  // dQ tiles per wave
+    constexpr int NG = NI * NJ / kWaves;  // G tiles per wave
+    __shared__ __attribute__((aligned(16))) float sR[DK * LV];
+    __shared__ __attribute__((aligned(16))) float sQ[C * LK];
+    __shared__ __attribute__((aligned(16))) float sK[C * LK];
+    __shared__ __attribute__((aligned(16))) float sV[C * LV];
+    __shared__ __attribute__((aligned(16))) float sD[C * LV];
+    __shared__ __attribute__((aligned(16))) float sA[C * LC];
+    __shared__ __attribute__((aligned(16))) float sB[C * LC];
+    __shared__ float sZ[DK], sPart[NI * C], sW[C], sC[C];
+
+    const int wid = xcd_remap(blockIdx.x, gridDim.x);
+    const int64_t bh = wid / P;
+    const int p = wid % P;
+    const int tid = threadIdx.x, lane = tid & 63, wave = wave_index();
+    const int m = lane & 15, g = lane >> 4;
+    const int64_t t0 = (int64_t)p * L, t1 = min(t0 + L, T_), len = t1 - t0;
+    const int nch = (int)(len > 0 ? (len + C - 1) / C : 0);
+
+    const float* st = pre ? pre + (bh * P + p) * (int64_t)(DK * DV + DK) : nullptr;
+    for (int e = tid; e < DK * DV; e += kThreads) sR[(e / DV) * LV + e % DV] = st ? st[e] : 0.f;
+    for (int e = tid; e < DK; e += kThreads) sZ[e] = st ? st[DK * DV + e] : 0.f;
+
+    const HeadBuf bq = slice_buf(q, lay.q, bh, DK, t0, t1), bk = slice_buf(k, lay.k, bh, DK, t0, t1);
+    const HeadBuf bv = slice_buf(v, lay.v, bh, DV, t0, t1), bd = slice_buf(dout, lay.dout, bh, DV, t0, t1);
+    const HeadBuf bdq = slice_buf(dq, lay.dq, bh, DK, t0, t1);
+    ChunkLoad<T, DK> lq, lk;
+    ChunkLoad<T, DV> lv, ld;
+    lq.issue(bq, lay.q.rs, 0);
+    lk.issue(bk, lay.k.rs, 0);
+    lv.issue(bv, lay.v.rs, 0);
+    ld.issue(bd, lay.dout.rs, 0);
+
+    const bool sums = gpart != nullptr;
+    f32x4 G[NG];
+#pragma unroll
+    for (int j = 0; j < NG; ++j) G[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float gsum = 0.f;  // thread i < DK: g_i
+
+    for (int c = 0; c < nch; ++c) {
+        const int nvalid = (int)min((int64_t)C, len - (int64_t)c * C);
+        const auto feat = [&](int r, float x) { return r < nvalid ? phi<FM, T>(x) : 0.f; };
+        const auto raw = [](int, float x) { return x; };
+        lq.put(sQ, LK, feat);
+        lk.put(sK, LK, feat);
+        lv.put(sV, LV, raw);
+        ld.put(sD, LV, raw);
+        const int64_t next = (int64_t)min(c + 1, nch - 1) * C;
+        lq.issue(bq, lay.q.rs, next);
+        lk.issue(bk, lay.k.rs, next);
+        lv.issue(bv, lay.v.rs, next);
+        ld.issue(bd, lay.dout.rs, next);
+        __syncthreads();
+
+        // (a) A and B on the blocks on or below the diagonal; Y on this
+        // wave's tiles, with its share of phi(q) . Y per row
+        for (int n = wave; n < 2 * NL; n += kWaves) {
+            const bool isA = n < NL;
+            if (SIMPLE && isA) continue;
+            int tb, sb;
+            lower_block(isA ? n : n - NL, tb, sb);
+            const f32x4 a = isA ? tile_f32<true, true>(f32x4{0.f, 0.f, 0.f, 0.f}, sQ + 16 * tb * LK, LK,
+                                                       sK + 16 * sb * LK, LK, 0, DK)
+                                : tile_f32<true, true>(f32x4{0.f, 0.f, 0.f, 0.f}, sD + 16 * tb * LV, LV,
+                                                       sV + 16 * sb * LV, LV, 0, DV);
+            float* dst = isA ? sA : sB;
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                dst[(16 * tb + 4 * g + r) * LC + 16 * sb + m] = (sb < tb || m <= 4 * g + r) ? a[r] : 0.f;
+        }
+        f32x4 Y[NY];
+#pragma unroll
+        for (int jj = 0; jj < NY; ++jj) {
+            const int n = wave + kWaves * jj, tb = n / NI, ib = n % NI;
+            Y[jj] = tile_f32<true, true>(f32x4{0.f, 0.f, 0.f, 0.f}, sD + 16 * tb * LV, LV, sR + 16 * ib * LV, LV, 0, DV);
+            if constexpr (!SIMPLE) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int row = 16 * tb + 4 * g + r;
+                    const float d = row16_sum(Y[jj][r] * sQ[row * LK + 16 * ib + m]);
+                    if (m == 0) sPart[ib * C + row] = d;
+                }
+            }
+        }
+        __syncthreads();
+
+        // (b) per row: w, c, P = mask(w B + c) in place of B
+        if (tid < C) {
+            const int t = tid;
+            const bool ok = t < nvalid;
+            float w, cc = 0.f;
+            if constexpr (SIMPLE) {
+                w = ok ? eps : 0.f;  // the query scale
+            } else {
+                float den = 0.f, ab = 0.f;
+                for (int s = 0; s <= t; ++s) {
+                    den += sA[t * LC + s];
+                    ab += sA[t * LC + s] * sB[t * LC + s];
+                }
+                float qz = 0.f;
+                for (int i = 0; i < DK; ++i) qz += sQ[t * LK + i] * sZ[i];
+                float qy = 0.f;
+                for (int ib = 0; ib < NI; ++ib) qy += sPart[ib * C + t];
+                w = ok ? 1.f / (qz + den + eps) : 0.f;
+                const float chat = -(qy + ab) * w;  // c / w
+                cc = chat * w;
+                if (ok) {
+                    float* wt = wc + (bh * T_ + t0 + (int64_t)c * C + t) * 2;
+                    wt[0] = w;
+                    wt[1] = chat;
+                }
+            }
+            sW[t] = w;
+            sC[t] = cc;
+            for (int s = 0; s < C; ++s) sB[t * LC + s] = s <= t ? w * sB[t * LC + s] + cc : 0.f;
+        }
+        __syncthreads();
+
+        // (c) dQ on this wave's tiles (kept in Y); the segment sums
+#pragma unroll
+        for (int jj = 0; jj < NY; ++jj) {
+            const int n = wave + kWaves * jj, tb = n / NI, ib = n % NI;
+            const f32x4 pk = tile_f32<true, false>(f32x4{0.f, 0.f, 0.f, 0.f}, sB + 16 * tb * LC, LC, sK + 16 * ib, LK,
+                                                   0, 16 * (tb + 1));
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = 16 * tb + 4 * g + r, col = 16 * ib + m;
+                const float d = sW[row] * Y[jj][r] + sC[row] * sZ[col] + pk[r];
+                Y[jj][r] = d * dphi_of<FM>(sQ[row * LK + col]);
+            }
+        }
+        if (sums) {
+#pragma unroll
+            for (int jj = 0; jj < NG; ++jj) {
+                const int n = wave + kWaves * jj, ib = n / NJ, jb = n % NJ;
+                G[jj] = tile_f32<false, false, true>(G[jj], sQ + 16 * ib, LK, sD + 16 * jb, LV, 0, C, sW);
+            }
+            if (tid < DK) {
+                float s = 0.f;
+                for (int r = 0; r < C; ++r) s += sC[r] * sQ[r * LK + tid];
+                gsum += s;
+            }
+        }
+        __syncthreads();
+
+        // (d) dQ into sQ's place; R += phi(K)^T V, z += sum phi(k)
+#pragma unroll
+        for (int jj = 0; jj < NY; ++jj) {
+            const int n = wave + kWaves * jj, tb = n / NI, ib = n % NI;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sQ[(16 * tb + 4 * g + r) * LK + 16 * ib + m] = Y[jj][r];
+        }
+#pragma unroll 1
+        for (int jj = 0; jj < NI * NJ / kWaves; ++jj) {
+            const int n = wave + kWaves * jj, ib = n / NJ, jb = n % NJ;
+            float* rt = sR + 16 * ib * LV + 16 * jb;
+            f32x4 acc;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[r] = rt[(4 * g + r) * LV + m];
+            acc = tile_f32<false, false>(acc, sK + 16 * ib, LK, sV + 16 * jb, LV, 0, C);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) rt[(4 * g + r) * LV + m] = acc[r];
+        }
+        for (int i = tid; i < DK; i += kThreads) {
+            float s = 0.f;
+            for (int r = 0; r < C; ++r) s += sK[r * LK + i];
+            sZ[i] += s;
+        }
+        __syncthreads();
+        store_chunk<T, DK>(sQ, LK, bdq, lay.dq.rs, (int64_t)c * C);
+        __syncthreads();
+    }
+
+    if (sums) {
+        float* gp = gpart + (bh * P + p) * (int64_t)(DK * DV + DK);
+#pragma unroll
+        for (int jj = 0; jj < NG; ++jj) {
+            const int n = wave + kWaves * jj, ib = n / NJ, jb = n % NJ;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) gp[(16 * ib + 4 * g + r) * DV + 16 * jb + m] = G[jj][r];
+        }
+        if (tid < DK) gp[DK * DV + tid] = gsum;
+    }
+}
+
+// Reverse-order dK, dV scan, fp32 operands: chunks from the segment's last
+// to its first, starting from the suffix (G, g) of the later segments. Per
+// chunk, with Qw_t = w_t phi(q_t) and G, g the sums over everything after it:
+//   P~[s][t] = mask(v_s . dO_t + c^_t) w_t,  A~[s][t] = mask(phi(k_s) . phi(q_t)) w_t  (t >= s);
+//   dK = (V G^T + g + P~ phi(Q)) phi'(K),  dV = phi(K) G + A~ dO;
+//   G += Qw^T dO,  g += sum_t c^_t Qw_t.
+template <typename T, int DK, int DV, bool SIMPLE, int FM>
+__global__ __launch_bounds__(kThreads) void bwd_causal_kv_f32_kernel(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const T* __restrict__ dout,
+    const float* __restrict__ wc, const float* __restrict__ suf, T* __restrict__ dk, T* __restrict__ dv, int64_t T_,
+    const Layouts lay, int P, int64_t L, float qscale) {
+    constexpr int C = CF::C, NT = CF::NT, NL = CF::NL, LC = CF::LC;
+    constexpr int NI = DK / 16, NJ = DV / 16, LK = DK + 4, LV = DV + 4;
+    constexpr int NDK = NT * NI / kWaves, NDV = NT * NJ / kWaves;
+    __shared__ __attribute__((aligned(16))) float sG[DK * LV];
+    __shared__ __attribute__((aligned(16))) float sQ[C * LK];
+    __shared__ __attribute__((aligned(16))) float sK[C * LK];
+    __shared__ __attribute__((aligned(16))) float sV[C * LV];
+    __shared__ __attribute__((aligned(16))) float sD[C * LV];
+    __shared__ __attribute__((aligned(16))) float sP[C * LC];
+    __shared__ __attribute__((aligned(16))) float sT[C * LC];
+    __shared__ float sg[DK], sW[C], sCh[C];
+
+    const int wid = xcd_remap(blockIdx.x, gridDim.x);
+    const int64_t bh = wid / P;
+    const int p = wid % P;
+    const int tid = threadIdx.x, lane = tid & 63, wave = wave_index();
+    const int m = lane & 15, g = lane >> 4;
+    const int64_t t0 = (int64_t)p * L, t1 = min(t0 + L, T_), len = t1 - t0;
+    const int nch = (int)(len > 0 ? (len + C - 1) / C : 0);
+
+    const float* st = suf ? suf + (bh * P + p) * (int64_t)(DK * DV + DK) : nullptr;
+    for (int e = tid; e < DK * DV; e += kThreads) sG[(e / DV) * LV + e % DV] = st ? st[e] : 0.f;
+    for (int e = tid; e < DK; e += kThreads) sg[e] = st ? st[DK * DV + e] : 0.f;
+
+    const HeadBuf bq = slice_buf(q, lay.q, bh, DK, t0, t1), bk = slice_buf(k, lay.k, bh, DK, t0, t1);
+    const HeadBuf bv = slice_buf(v, lay.v, bh, DV, t0, t1), bd = slice_buf(dout, lay.dout, bh, DV, t0, t1);
+    const HeadBuf bdk = slice_buf(dk, lay.dk, bh, DK, t0, t1), bdv = slice_buf(dv, lay.dv, bh, DV, t0, t1);
+    ChunkLoad<T, DK> lq, lk;
+    ChunkLoad<T, DV> lv, ld;
+    const int64_t first = (int64_t)max(nch - 1, 0) * C;
+    lq.issue(bq, lay.q.rs, first);
+    lk.issue(bk, lay.k.rs, first);
+    lv.issue(bv, lay.v.rs, first);
+    ld.issue(bd, lay.dout.rs, first);
+    // w_t, c^_t of this thread's row (tid < C) of the chunk in flight
+    const float* wch = wc + (bh * T_ + t0) * 2;
+    float nw = 0.f, nch_ = 0.f;
+    const auto load_wc = [&](int cidx) {
+        if constexpr (!SIMPLE) {
+            if (tid < C && len > 0) {
+                const int64_t t = min((int64_t)cidx * C + tid, len - 1);
+                nw = wch[2 * t];
+                nch_ = wch[2 * t + 1];
+            }
+        }
+    };
+    load_wc(max(nch - 1, 0));
+
+    for (int c = nch - 1; c >= 0; --c) {
+        const int nvalid = (int)min((int64_t)C, len - (int64_t)c * C);
+        const auto feat = [&](int r, float x) { return r < nvalid ? phi<FM, T>(x) : 0.f; };
+        const auto raw = [](int, float x) { return x; };
+        lq.put(sQ, LK, feat);
+        lk.put(sK, LK, feat);
+        lv.put(sV, LV, raw);
+        ld.put(sD, LV, raw);
+        if (tid < C) {
+            const bool ok = tid < nvalid;
+            sW[tid] = ok ? (SIMPLE ? qscale : nw) : 0.f;
+            sCh[tid] = ok && !SIMPLE ? nch_ : 0.f;
+        }
+        const int64_t next = (int64_t)max(c - 1, 0) * C;
+        lq.issue(bq, lay.q.rs, next);
+        lk.issue(bk, lay.k.rs, next);
+        lv.issue(bv, lay.v.rs, next);
+        ld.issue(bd, lay.dout.rs, next);
+        load_wc(max(c - 1, 0));
+        __syncthreads();
+
+        // (a) P~ and A~ on the blocks on or above the diagonal (t >= s)
+        for (int n = wave; n < 2 * NL; n += kWaves) {
+            const bool isP = n < NL;
+            int tb, sb;
+            lower_block(isP ? n : n - NL, tb, sb);  // tb >= sb: key block sb, query block tb
+            const f32x4 a = isP ? tile_f32<true, true>(f32x4{0.f, 0.f, 0.f, 0.f}, sV + 16 * sb * LV, LV,
+                                                       sD + 16 * tb * LV, LV, 0, DV)
+                                : tile_f32<true, true>(f32x4{0.f, 0.f, 0.f, 0.f}, sK + 16 * sb * LK, LK,
+                                                       sQ + 16 * tb * LK, LK, 0, DK);
+            float* dst = isP ? sP : sT;
+            const int t = 16 * tb + m;
+            const float wt = sW[t], ct = isP ? sCh[t] : 0.f;
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                dst[(16 * sb + 4 * g + r) * LC + t] = (sb < tb || m >= 4 * g + r) ? (a[r] + ct) * wt : 0.f;
+        }
+        __syncthreads();
+
+        // (b) dK and dV on this wave's tiles
+        f32x4 rk[NDK], rv[NDV];
+#pragma unroll
+        for (int jj = 0; jj < NDK; ++jj) {
+            const int n = wave + kWaves * jj, sb = n / NI, ib = n % NI;
+            f32x4 acc = tile_f32<true, true>(f32x4{0.f, 0.f, 0.f, 0.f}, sV + 16 * sb * LV, LV, sG + 16 * ib * LV, LV,
+                                             0, DV);
+            acc = tile_f32<true, false>(acc, sP + 16 * sb * LC, LC, sQ + 16 * ib, LK, 16 * sb, C);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = 16 * sb + 4 * g + r, col = 16 * ib + m;
+                rk[jj][r] = (acc[r] + sg[col]) * dphi_of<FM>(sK[row * LK + col]);
+            }
+        }
+#pragma unroll
+        for (int jj = 0; jj < NDV; ++jj) {
+            const int n = wave + kWaves * jj, sb = n / NJ, jb = n % NJ;
+            f32x4 acc = tile_f32<true, false>(f32x4{0.f, 0.f, 0.f, 0.f}, sK + 16 * sb * LK, LK, sG + 16 * jb, LV, 0, DK);
+            rv[jj] = tile_f32<true, false>(acc, sT + 16 * sb * LC, LC, sD + 16 * jb, LV, 16 * sb, C);
+        }
+        __syncthreads();
+
+        // (c) G += Qw^T dO, g += sum c^ Qw; dK, dV into the K and V tiles
+#pragma unroll 1
+        for (int jj = 0; jj < NI * NJ / kWaves; ++jj) {
+            const int n = wave + kWaves * jj, ib = n / NJ, jb = n % NJ;
+            float* gt = sG + 16 * ib * LV + 16 * jb;
+            f32x4 acc;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[r] = gt[(4 * g + r) * LV + m];
+            acc = tile_f32<false, false, true>(acc, sQ + 16 * ib, LK, sD + 16 * jb, LV, 0, C, sW);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) gt[(4 * g + r) * LV + m] = acc[r];
+        }
+        for (int i = tid; i < DK; i += kThreads) {
+            float s = 0.f;
+            for (int r = 0; r < C; ++r) s += sCh[r] * sW[r] * sQ[r * LK + i];
+            sg[i] += s;
+        }
+#pragma unroll
+        for (int jj = 0; jj < NDK; ++jj) {
+            const int n = wave + kWaves * jj, sb = n / NI, ib = n % NI;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sK[(16 * sb + 4 * g + r) * LK + 16 * ib + m] = rk[jj][r];
+        }
+#pragma unroll
+        for (int jj = 0; jj < NDV; ++jj) {
+            const int n = wave + kWaves * jj, sb = n / NJ, jb = n % NJ;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sV[(16 * sb + 4 * g + r) * LV + 16 * jb + m] = rv[jj][r];
+        }
+        __syncthreads();
+        store_chunk<T, DK>(sK, LK, bdk, lay.dk.rs, (int64_t)c * C);
+        store_chunk<T, DV>(sV, LV, bdv, lay.dv.rs, (int64_t)c * C);
+        __syncthreads();
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Head size 256 (DK = DV = 256, 16-bit inputs): wide kernels.
 // ---------------------------------------------------------------------------
 // A 256 x 256 fp32 state (256 KB) fits neither one wave's registers nor a
@@ -4380,7 +4968,8 @@ SplitCfg wide_split_config(int step) {
     }
 }
 
-// Where the causal forward exists: 16-bit elements, DK and DV in {64, 128}.
+// Where the 16-bit causal scans run: 16-bit elements, DK and DV in {64, 128};
+// every other causal shape takes the fp32-operand scans.
 template <typename T, int DK, int DV>
 constexpr bool kCausalKernels = sizeof(T) == 2 && (DK == 64 || DK == 128) && (DV == 64 || DV == 128);
 
@@ -4389,29 +4978,33 @@ constexpr bool kCausalKernels = sizeof(T) == 2 && (DK == 64 || DK == 128) && (DV
 template <typename T, int DK, int DV, int FM>
 hipError_t fwd_causal_fm(const Plan& p, const void* q, const void* k, const void* v, void* o, float* state,
                          void* ws, hipStream_t s) {
-    if constexpr (!kCausalKernels<T, DK, DV>) {
-        return hipErrorInvalidValue;
-    } else {
-        float* part = reinterpret_cast<float*>(static_cast<char*>(ws) + p.off_part);
-        hipError_t e = launch_state_reduction<T, DK, DV, FM>(p, k, v, state, part, s);
+    float* part = reinterpret_cast<float*>(static_cast<char*>(ws) + p.off_part);
+    hipError_t e = launch_state_reduction<T, DK, DV, FM>(p, k, v, state, part, s);
+    if (e != hipSuccess) return e;
+    if (p.P > 1) {
+        constexpr int E4 = (DK * DV + DK) / 4;
+        e = launch(prefix_kernel<DK, DV>, p.BH * ((E4 + kThreads - 1) / kThreads), kThreads, s, part, p.P, state,
+                   state + p.BH * DK * DV, p.BH);
         if (e != hipSuccess) return e;
-        if (p.P > 1) {
-            constexpr int E4 = (DK * DV + DK) / 4;
-            e = launch(prefix_kernel<DK, DV>, p.BH * ((E4 + kThreads - 1) / kThreads), kThreads, s, part, p.P, state,
-                       state + p.BH * DK * DV, p.BH);
-            if (e != hipSuccess) return e;
-        }
-        const float* pre = p.P > 1 ? part : nullptr;
-        const T* qq = static_cast<const T*>(q);
-        const T* kk = static_cast<const T*>(k);
-        const T* vv = static_cast<const T*>(v);
-        T* oo = static_cast<T*>(o);
-        const int64_t nblk = p.BH * p.P;
+    }
+    const float* pre = p.P > 1 ? part : nullptr;
+    const T* qq = static_cast<const T*>(q);
+    const T* kk = static_cast<const T*>(k);
+    const T* vv = static_cast<const T*>(v);
+    T* oo = static_cast<T*>(o);
+    const int64_t nblk = p.BH * p.P;
+    if constexpr (kCausalKernels<T, DK, DV>) {
         if (p.simple)
             return launch(fwd_causal_kernel<T, DK, DV, true, FM>, nblk, kThreads, s, qq, kk, vv, pre, oo, p.T, p.lay,
                           p.P, p.L, p.eps);
         return launch(fwd_causal_kernel<T, DK, DV, false, FM>, nblk, kThreads, s, qq, kk, vv, pre, oo, p.T, p.lay,
                       p.P, p.L, p.eps);
+    } else {
+        if (p.simple)
+            return launch(fwd_causal_f32_kernel<T, DK, DV, true, FM>, nblk, kThreads, s, qq, kk, vv, pre, oo, p.T,
+                          p.lay, p.P, p.L, p.eps);
+        return launch(fwd_causal_f32_kernel<T, DK, DV, false, FM>, nblk, kThreads, s, qq, kk, vv, pre, oo, p.T,
+                      p.lay, p.P, p.L, p.eps);
     }
 }
 
@@ -4421,46 +5014,57 @@ hipError_t fwd_causal_fm(const Plan& p, const void* q, const void* k, const void
 template <typename T, int DK, int DV, int FM>
 hipError_t bwd_causal_fm(const Plan& p, const void* q, const void* k, const void* v, const void* dout, void* dq,
                          void* dk, void* dv, void* ws, hipStream_t s) {
-    if constexpr (!kCausalKernels<T, DK, DV>) {
-        return hipErrorInvalidValue;
-    } else {
-        char* w = static_cast<char*>(ws);
-        float* part = reinterpret_cast<float*>(w + p.off_part);
-        float* gpart = reinterpret_cast<float*>(w + p.off_cgpart);
-        float* wcp = reinterpret_cast<float*>(w + p.off_cwc);
-        int* esp = reinterpret_cast<int*>(w + p.off_ces);
-        float* total = reinterpret_cast<float*>(w + p.off_fstate);  // the full state; not needed here
-        constexpr int E4 = (DK * DV + DK) / 4;
-        const int64_t nred = p.BH * ((E4 + kThreads - 1) / kThreads);
-        hipError_t e;
-        if (p.P > 1) {
-            e = launch_state_reduction<T, DK, DV, FM>(p, k, v, total, part, s);
-            if (e != hipSuccess) return e;
-            e = launch(prefix_kernel<DK, DV>, nred, kThreads, s, part, p.P, total, total + p.BH * DK * DV, p.BH);
-            if (e != hipSuccess) return e;
-        }
-        const float* pre = p.P > 1 ? part : nullptr;
-        float* gp = p.P > 1 ? gpart : nullptr;
-        const T* qq = static_cast<const T*>(q);
-        const T* kk = static_cast<const T*>(k);
-        const T* vv = static_cast<const T*>(v);
-        const T* dd = static_cast<const T*>(dout);
-        const int64_t nblk = p.BH * p.P;
-        e = p.simple ? launch(bwd_causal_q_kernel<T, DK, DV, true, FM>, nblk, kThreads, s, qq, kk, vv, dd, pre,
-                              static_cast<T*>(dq), wcp, esp, gp, p.T, p.lay, p.P, p.L, p.nche, p.eps)
-                     : launch(bwd_causal_q_kernel<T, DK, DV, false, FM>, nblk, kThreads, s, qq, kk, vv, dd, pre,
-                              static_cast<T*>(dq), wcp, esp, gp, p.T, p.lay, p.P, p.L, p.nche, p.eps);
+    char* w = static_cast<char*>(ws);
+    float* part = reinterpret_cast<float*>(w + p.off_part);
+    float* gpart = reinterpret_cast<float*>(w + p.off_cgpart);
+    float* wcp = reinterpret_cast<float*>(w + p.off_cwc);
+    int* esp = reinterpret_cast<int*>(w + p.off_ces);
+    float* total = reinterpret_cast<float*>(w + p.off_fstate);  // the full state; not needed here
+    constexpr int E4 = (DK * DV + DK) / 4;
+    const int64_t nred = p.BH * ((E4 + kThreads - 1) / kThreads);
+    hipError_t e;
+    if (p.P > 1) {
+        e = launch_state_reduction<T, DK, DV, FM>(p, k, v, total, part, s);
         if (e != hipSuccess) return e;
-        if (p.P > 1) {
-            e = launch(suffix_kernel<DK, DV>, nred, kThreads, s, gpart, p.P, p.BH);
-            if (e != hipSuccess) return e;
-        }
+        e = launch(prefix_kernel<DK, DV>, nred, kThreads, s, part, p.P, total, total + p.BH * DK * DV, p.BH);
+        if (e != hipSuccess) return e;
+    }
+    const float* pre = p.P > 1 ? part : nullptr;
+    float* gp = p.P > 1 ? gpart : nullptr;
+    const T* qq = static_cast<const T*>(q);
+    const T* kk = static_cast<const T*>(k);
+    const T* vv = static_cast<const T*>(v);
+    const T* dd = static_cast<const T*>(dout);
+    T* dqq = static_cast<T*>(dq);
+    T* dkk = static_cast<T*>(dk);
+    T* dvv = static_cast<T*>(dv);
+    const int64_t nblk = p.BH * p.P;
+    if constexpr (kCausalKernels<T, DK, DV>) {
+        e = p.simple ? launch(bwd_causal_q_kernel<T, DK, DV, true, FM>, nblk, kThreads, s, qq, kk, vv, dd, pre, dqq,
+                              wcp, esp, gp, p.T, p.lay, p.P, p.L, p.nche, p.eps)
+                     : launch(bwd_causal_q_kernel<T, DK, DV, false, FM>, nblk, kThreads, s, qq, kk, vv, dd, pre, dqq,
+                              wcp, esp, gp, p.T, p.lay, p.P, p.L, p.nche, p.eps);
+    } else {
+        e = p.simple ? launch(bwd_causal_q_f32_kernel<T, DK, DV, true, FM>, nblk, kThreads, s, qq, kk, vv, dd, pre,
+                              dqq, wcp, gp, p.T, p.lay, p.P, p.L, p.eps)
+                     : launch(bwd_causal_q_f32_kernel<T, DK, DV, false, FM>, nblk, kThreads, s, qq, kk, vv, dd, pre,
+                              dqq, wcp, gp, p.T, p.lay, p.P, p.L, p.eps);
+    }
+    if (e != hipSuccess) return e;
+    if (p.P > 1) {
+        e = launch(suffix_kernel<DK, DV>, nred, kThreads, s, gpart, p.P, p.BH);
+        if (e != hipSuccess) return e;
+    }
+    if constexpr (kCausalKernels<T, DK, DV>) {
         return p.simple ? launch(bwd_causal_kv_kernel<T, DK, DV, true, FM>, nblk, kThreads, s, qq, kk, vv, dd, wcp,
-                                 esp, gp, static_cast<T*>(dk), static_cast<T*>(dv), p.T, p.lay, p.P, p.L, p.nche,
-                                 p.eps)
+                                 esp, gp, dkk, dvv, p.T, p.lay, p.P, p.L, p.nche, p.eps)
                         : launch(bwd_causal_kv_kernel<T, DK, DV, false, FM>, nblk, kThreads, s, qq, kk, vv, dd, wcp,
-                                 esp, gp, static_cast<T*>(dk), static_cast<T*>(dv), p.T, p.lay, p.P, p.L, p.nche,
-                                 1.f);
+                                 esp, gp, dkk, dvv, p.T, p.lay, p.P, p.L, p.nche, 1.f);
+    } else {
+        return p.simple ? launch(bwd_causal_kv_f32_kernel<T, DK, DV, true, FM>, nblk, kThreads, s, qq, kk, vv, dd,
+                                 wcp, gp, dkk, dvv, p.T, p.lay, p.P, p.L, p.eps)
+                        : launch(bwd_causal_kv_f32_kernel<T, DK, DV, false, FM>, nblk, kThreads, s, qq, kk, vv, dd,
+                                 wcp, gp, dkk, dvv, p.T, p.lay, p.P, p.L, p.eps);
     }
 }
 
@@ -4551,20 +5155,12 @@ hipError_t fwd_output_t(const Plan& p, const void* q, const float* state, void* 
 template <typename T, int DK, int DV>
 hipError_t fwd_causal_t(const Plan& p, const void* q, const void* k, const void* v, void* o, float* state, void* ws,
                         hipStream_t s) {
-    if constexpr (!kCausalKernels<T, DK, DV>) {
-        return hipErrorInvalidValue;
-    } else {
-        LA_FEATURE_MAP(fwd_causal_fm, q, k, v, o, state, ws, s);
-    }
+    LA_FEATURE_MAP(fwd_causal_fm, q, k, v, o, state, ws, s);
 }
 template <typename T, int DK, int DV>
 hipError_t bwd_causal_t(const Plan& p, const void* q, const void* k, const void* v, const void* dout, void* dq,
                         void* dk, void* dv, void* ws, hipStream_t s) {
-    if constexpr (!kCausalKernels<T, DK, DV>) {
-        return hipErrorInvalidValue;
-    } else {
-        LA_FEATURE_MAP(bwd_causal_fm, q, k, v, dout, dq, dk, dv, ws, s);
-    }
+    LA_FEATURE_MAP(bwd_causal_fm, q, k, v, dout, dq, dk, dv, ws, s);
 }
 template <typename T, int DK, int DV>
 hipError_t bwd_dq_t(const Plan& p, const void* q, const void* dout, const float* state, void* dq, void* ws,

@@ -151,5 +151,7 @@ HEAD_SIZE_WORKLOADS = {
         Workload("B8-H16-T16384-D32-Dv128-f16", 8, 16, 16384, 32, "f16", seed=6500, Dv=128),
         # head size 256: the headline's bytes per tensor (T D per head) at a quarter of its length
         Workload("B8-H16-T4096-D256-f16", 8, 16, 4096, 256, "f16", seed=6600),
+        # the headline shape with fp32 elements (fp32 MFMA throughout)
+        Workload("B8-H16-T16384-D64-f32", 8, 16, 16384, 64, "f32", seed=6700),
     )
 }

@@ -52,8 +52,11 @@ int main(void) {
     p.scale = 0.0f;
     p.flags = LA_CAUSAL;
     CHECK(la_fwd_state(&p, NULL, NULL, NULL, NULL, 0, NULL) == LA_ERR_FLAGS);
-    p.dtype = LA_F32;
-    CHECK(la_bwd(&p, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, 0, NULL) == LA_ERR_DTYPE);
+    p.dtype = LA_F32; /* the causal form takes fp32 too: the missing workspace is reported */
+    CHECK(la_bwd(&p, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, 0, NULL) == LA_ERR_WORKSPACE);
+    p.D = 256;
+    p.dtype = LA_F16;
+    CHECK(la_bwd(&p, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, 0, NULL) == LA_ERR_HEAD_DIM);
 
     if (fails == 0) printf("c abi ok\n");
     return fails == 0 ? 0 : 1;

@@ -330,22 +330,25 @@ def test_token_major_layout_limits(L):
 
 
 def test_causal_flag_accepted_by_la_fwd_and_la_bwd_only(L):
-    """LA_CAUSAL: la_fwd and la_bwd take it for f16/bf16 with D, Dv in
-    {64, 128}; the step calls reject it before any HIP call. Every call here
-    ends in an argument error."""
+    """LA_CAUSAL: la_fwd and la_bwd take it for every dtype and for D, Dv in
+    {32, 64, 96, 128} (not 256); the step calls reject it before any HIP call.
+    Every call here ends in an argument error."""
     CAUSAL = 0x10
     p = prob(flags=CAUSAL)
     need = L.la_workspace_bytes(ctypes.byref(p))
     assert need > L.la_workspace_bytes(ctypes.byref(prob())), "causal backward scratch not counted"
     assert L.la_state_bytes(ctypes.byref(p)) > 0
-    assert fwd_call(L, prob(flags=CAUSAL, dtype=0)) == DTYPE
-    for d, dv in ((32, 0), (96, 0), (64, 32), (128, 96)):
-        assert fwd_call(L, prob(flags=CAUSAL, D=d, Dv=dv)) == HEAD_DIM, (d, dv)
     d = addrs(9)
-    p32 = prob(flags=CAUSAL, dtype=0)
-    assert L.la_bwd(ctypes.byref(p32), *d[:9], L.la_workspace_bytes(ctypes.byref(p32)), None) == DTYPE
-    p96 = prob(flags=CAUSAL, D=96)
-    assert L.la_bwd(ctypes.byref(p96), *d[:9], 1 << 30, None) == HEAD_DIM
+    for dt in (0, 1, 2):
+        for dd, dv in ((32, 0), (96, 0), (64, 32), (128, 96), (64, 0), (128, 64)):
+            pc = prob(flags=CAUSAL, D=dd, Dv=dv, dtype=dt)
+            n = L.la_workspace_bytes(ctypes.byref(pc))
+            assert n > 0, (dt, dd, dv)
+            # accepted: the short workspace is the error reported
+            assert fwd_call(L, pc, ws_bytes=n - 1) == WORKSPACE, (dt, dd, dv)
+            assert L.la_bwd(ctypes.byref(pc), *d[:9], n - 1, None) == WORKSPACE, (dt, dd, dv)
+    for dd, dv in ((256, 0), (256, 64), (64, 256)):
+        assert fwd_call(L, prob(flags=CAUSAL, D=dd, Dv=dv, dtype=1), ws_bytes=1 << 30) == HEAD_DIM, (dd, dv)
     # the causal backward reads no state: NULL passes that check and the
     # workspace check reports; without the flag NULL is reported first
     args = [d[0], d[1], d[2], d[3], None, d[5], d[6], d[7], d[8]]
@@ -373,7 +376,7 @@ def test_fwd_noalloc_validates_before_any_hip_call(L):
     assert f(ctypes.byref(prob()), q, k, v, o, None, None) == NULL
     assert f(ctypes.byref(prob()), q, k, v, q, st, None) == ALIAS
     assert f(ctypes.byref(prob()), ctypes.c_void_p(base + 8), k, v, o, st, None) == ALIGN
-    assert f(ctypes.byref(prob(flags=0x10, dtype=0)), q, k, v, o, st, None) == DTYPE
+    assert f(ctypes.byref(prob(flags=0x10, D=256)), q, k, v, o, st, None) == HEAD_DIM
     # fp32, D = Dv = 128, one head of 2^18 tokens: split into 1024 slices whose
     # partials (1024 * (128 * 128 + 128) * 4 bytes) exceed 64 MiB
     big = prob(B=1, H=1, T=1 << 18, D=128, dtype=0)

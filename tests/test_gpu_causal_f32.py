@@ -1,0 +1,171 @@
+"""GPU parity of the causal scans on fp32 operands, which take every causal
+shape the 16-bit scans do not (fp32 inputs, and f16/bf16 inputs with D or Dv
+of 32 or 96), against the fp64 oracle's causal forms: forward and backward on
+every element at small sizes (several segments and 32-token chunks, ragged
+tails, T = 1), simple_la, the other feature maps, the query scale, the
+token-major layout and strided views, a long sequence with many segments,
+the empty sequence and bit-identical reruns. fp32 inputs are held to the
+tight fp32 bar, 16-bit ones to their dtype's bar."""
+import numpy as np
+import pytest
+import torch
+
+import non_causal_linear_amd as la
+import oracle
+from synth import Workload, make_inputs, normal, to_storage
+from tests.la_testutil import TIGHT, TOL, TORCH_DTYPE, bytes_equal, decode, max_rel_err, split_state, to_device
+
+pytestmark = pytest.mark.gpu
+
+PAIRS_F32 = [(32, 32), (64, 64), (96, 96), (128, 128), (32, 128), (128, 96)]
+PAIRS_16 = [(32, 32), (96, 96), (64, 32), (32, 96), (128, 96)]
+CASES = [(d, dv, "f32") for d, dv in PAIRS_F32] + [(d, dv, dt) for d, dv in PAIRS_16 for dt in ("f16", "bf16")]
+
+
+def tol(dtype):
+    return TIGHT.get(dtype, TOL[dtype])
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    la.lib()
+
+
+def check(name, got, ref, dtype, where="", scale=None):
+    err = max_rel_err(got, ref) if scale is None else float(np.max(np.abs(got - ref))) / scale
+    print(f"  {name}{where}: max rel err {err:.3e}", flush=True)
+    assert np.all(np.isfinite(got)), f"{name}{where}: non-finite output"
+    assert err <= tol(dtype), f"{name}{where}: {err:.3e} > {tol(dtype)}"
+
+
+def run(w, x, simple, phi="elu1", scale=None, layout="bhtd"):
+    dev = {n: to_device(a, w.dtype) for n, a in x.items()}
+    if layout == "bthd":
+        dev = {n: t.transpose(1, 2).contiguous() for n, t in dev.items()}
+    o, st = la.fwd(dev["q"], dev["k"], dev["v"], eps=w.eps, simple=simple, phi=phi, causal=True, scale=scale,
+                   layout=layout)
+    g = la.bwd(dev["q"], dev["k"], dev["v"], dev["do"], None, eps=w.eps, simple=simple, phi=phi, causal=True,
+               scale=scale, layout=layout)
+    torch.cuda.synchronize()
+    return dev, o, st, g
+
+
+def check_all(w, x, o, st, g, simple, fm="elu1", scale=1.0):
+    o_ref, s_ref, z_ref = oracle.causal_fwd(x["q"], x["k"], x["v"], w.dtype, w.eps, simple, fm, scale)
+    check("O", decode(o, w.dtype), o_ref, w.dtype)
+    s_got, z_got = split_state(st, w.B, w.H, w.D, w.dv)
+    check("S", s_got, s_ref, w.dtype)
+    check("z", z_got, z_ref, w.dtype)
+    refs = oracle.causal_bwd(x["q"], x["k"], x["v"], x["do"], w.dtype, w.eps, simple, fm, scale)
+    scales = [None, None, None]
+    if w.T == 1 and not simple:
+        # one token: the exact dQ, dK are O(eps), two O(1) summands cancelling;
+        # measure the error against those summands
+        sc = [oracle.bwd_leading_terms_head(*(oracle.decode(x[n], w.dtype)[b, h] for n in ("q", "k", "v", "do")),
+                                            w.eps, fm)
+              for b in range(w.B) for h in range(w.H)]
+        scales[:2] = [max(a for a, _ in sc), max(b for _, b in sc)]
+    for name, t, r, sc in zip(("dQ", "dK", "dV"), g, refs, scales):
+        check(name, decode(t, w.dtype), r, w.dtype, scale=sc)
+
+
+@pytest.mark.parametrize("simple", [False, True], ids=["norm", "simple"])
+@pytest.mark.parametrize("D,Dv,dtype", CASES, ids=[f"D{a}-Dv{b}-{c}" for a, b, c in CASES])
+@pytest.mark.parametrize("T", [1, 100, 1000, 4097])
+def test_all_elements(T, D, Dv, dtype, simple):
+    seed = 120_000 + 97 * T + 13 * D + Dv + 7 * ["f32", "f16", "bf16"].index(dtype) + (3 if simple else 0)
+    w = Workload("causal-f32", 2, 3, T, D, dtype, simple=simple, seed=seed, Dv=Dv)
+    split = la.split_of(la.make_problem(w.shape, TORCH_DTYPE[dtype], w.eps, simple, dv=Dv, causal=True))
+    print(f"case causal fp32-operand T={T} D={D} Dv={Dv} {dtype} simple={simple} seed={seed} split={split}",
+          flush=True)
+    x = make_inputs(w)
+    _, o, st, g = run(w, x, simple)
+    check_all(w, x, o, st, g, simple)
+
+
+@pytest.mark.parametrize("fm,simple", [("relu", False), ("relu", True), ("identity", True), ("identity", False)])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_other_feature_maps(dtype, fm, simple):
+    D, Dv = (96, 64) if dtype == "f32" else (32, 96)
+    w = Workload("causal-f32-maps", 1, 3, 777, D, dtype, simple=simple, seed=121_000 + 5 * ["relu", "identity"].index(fm)
+                 + simple, Dv=Dv)
+    print(f"case causal fp32-operand phi={fm} simple={simple} {dtype} D={D} Dv={Dv} seed={w.seed}", flush=True)
+    x = make_inputs(w)
+    if fm == "identity" and not simple:
+        # keep the identity map's normaliser away from zero
+        for n in ("q", "k"):
+            x[n] = to_storage((np.abs(oracle.decode(x[n], dtype)) + 0.5).astype(np.float32), dtype)
+    _, o, st, g = run(w, x, simple, fm)
+    check_all(w, x, o, st, g, simple, fm)
+
+
+@pytest.mark.parametrize("simple", [False, True], ids=["norm", "simple"])
+def test_query_scale(simple):
+    # eps large, so that eps / scale visibly moves the normalised result
+    w = Workload("causal-f32-scale", 2, 2, 900, 64, "f32", simple=simple, eps=0.5, seed=122_000 + simple, Dv=32)
+    x = make_inputs(w)
+    _, o, st, g = run(w, x, simple, scale=0.375)
+    check_all(w, x, o, st, g, simple, scale=0.375)
+
+
+def test_token_major_and_strided_views():
+    """[B, T, H, D] tensors, and the q, k, v views of a packed [B, T, 3, H, D]
+    fp32 buffer, give the dense call's bytes."""
+    B, T, H, D = 2, 700, 3, 96
+    buf = to_device(normal((B, T, 3, H, D), 122_500, 1.0, "f32"), "f32")
+    q, k, v = buf[:, :, 0], buf[:, :, 1], buf[:, :, 2]
+    do = to_device(normal((B, T, H, D), 122_501, 1.0, "f32"), "f32")
+    o, st = la.fwd(q, k, v, layout="bthd", causal=True)
+    g = la.bwd(q, k, v, do, None, layout="bthd", causal=True)
+    dense = [t.transpose(1, 2).contiguous() for t in (q, k, v, do)]
+    o2, st2 = la.fwd(*dense[:3], causal=True)
+    g2 = la.bwd(*dense, None, causal=True)
+    torch.cuda.synchronize()
+    assert bytes_equal(st, st2)
+    assert bytes_equal(o.transpose(1, 2).contiguous(), o2)
+    for a, b in zip(g, g2):
+        assert bytes_equal(a.transpose(1, 2).contiguous(), b)
+
+
+@pytest.mark.parametrize("D,Dv,dtype", [(64, 64, "f32"), (96, 32, "f16")], ids=["D64-f32", "D96-Dv32-f16"])
+def test_long_sequence_many_segments(D, Dv, dtype):
+    """B1 H2 T16384: dozens of segments per head (prefix and suffix passes
+    over many blocks); one whole head forward and backward, rows sampled on
+    the other; bit-identical reruns; the state equals the non-causal one."""
+    w = Workload("causal-f32-long", 1, 2, 16384, D, dtype, seed=123_000 + D + Dv, Dv=Dv)
+    prob = la.make_problem(w.shape, TORCH_DTYPE[dtype], w.eps, False, dv=Dv, causal=True)
+    split = la.split_of(prob)
+    print(f"case causal fp32-operand B1 H2 T16384 D={D} Dv={Dv} {dtype} seed={w.seed} split={split}", flush=True)
+    assert split["P"] > 8
+    x = make_inputs(w)
+    dev, o, st, g = run(w, x, False)
+    hd = {nm: oracle.decode(a, dtype)[0] for nm, a in x.items()}
+    args = [hd[nm][0][None, None] for nm in ("q", "k", "v", "do")]
+    o_ref, _, _ = oracle.causal_fwd(*args[:3], "f32", w.eps, False)
+    check("O", decode(o, dtype)[0, 0], o_ref[0, 0], dtype, " head 0")
+    for name, gg, r in zip(("dQ", "dK", "dV"), g, oracle.causal_bwd(*args, "f32", w.eps, False)):
+        check(name, decode(gg, dtype)[0, 0], r[0, 0], dtype, " head 0")
+    rows = sorted({0, 1, w.T - 1} | {int(t) for t in np.random.default_rng(w.seed).integers(0, w.T, size=24)})
+    ref = oracle.causal_sampled_rows_head(hd["q"][1], hd["k"][1], hd["v"][1], rows, w.eps, False)
+    check("O rows", decode(o, dtype)[0, 1][rows], ref, dtype, " head 1")
+    _, o2, st2, g2 = run(w, x, False)
+    assert bytes_equal(o, o2) and bytes_equal(st, st2)
+    for a, b in zip(g, g2):
+        assert bytes_equal(a, b)
+    _, st_nc = la.fwd(dev["q"], dev["k"], dev["v"], eps=w.eps)
+    torch.cuda.synchronize()
+    assert bytes_equal(st, st_nc), "causal state differs from the non-causal state"
+
+
+def test_empty_sequence_fp32():
+    q = torch.zeros(2, 3, 0, 32, device="cuda")
+    v = torch.zeros(2, 3, 0, 96, device="cuda")
+    prob = la.make_problem(q.shape, q.dtype, 1e-6, False, dv=96, causal=True)
+    state = torch.full((la.state_bytes(prob) // 4,), 7.0, device="cuda")
+    o, st = la.fwd(q, q, v, causal=True, state=state)
+    dq, dk, dv = la.bwd(q, q, v, v, None, causal=True)
+    torch.cuda.synchronize()
+    assert o.numel() == 0 and dq.numel() == 0 and dk.numel() == 0 and dv.numel() == 0
+    assert torch.count_nonzero(st).item() == 0
