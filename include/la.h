@@ -102,8 +102,9 @@ typedef enum {
  * z_t = sum_{s<=t} phi(k_s) (flash-linear-attention README, "Different forms
  * of linear attention"). Accepted by la_fwd and la_bwd for every dtype and
  * every D, Dv in {32, 64, 96, 128} (not 256: LA_ERR_HEAD_DIM). f16 and bf16
- * with D and Dv in {64, 128} run scans on 16-bit MFMA operands; every other
- * shape runs scans on fp32 operands (fp32 MFMA, the 16-bit inputs widened).
+ * run scans on 16-bit MFMA operands (a head size of 32 or 96 padded to 64 or
+ * 128 inside the kernel, the padding never read from or written to memory);
+ * fp32 runs scans on fp32 operands.
  * la_fwd's `state` receives the full-sequence S, z, bit-identical to the
  * non-causal call; la_bwd does not read `state`. The step calls return
  * LA_ERR_FLAGS with it. la_workspace_bytes counts the causal backward's

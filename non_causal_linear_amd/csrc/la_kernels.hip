@@ -264,6 +264,20 @@ __device__ __forceinline__ int buf_off(int64_t row, int64_t rs, int col) {
     return (int)((uint32_t)row * (uint32_t)(rs * (int)sizeof(T)) + (uint32_t)(col * (int)sizeof(T)));
 }
 
+// The offset of a 16-byte piece at element `col` of a row that a kernel built
+// for rows of W elements holds with only REAL of them (a head size padded up
+// inside the kernel): pieces at or past REAL get an offset past the range of
+// every descriptor (heads span less than 2^31 bytes), so their loads read
+// zeros and their stores are dropped. REAL = W leaves the offset as it is.
+template <int W, int REAL>
+__device__ __forceinline__ int pad_off(int off, int col) {
+    if constexpr (REAL >= W) {
+        return off;
+    } else {
+        return col < REAL ? off : (int)0x80000000u;
+    }
+}
+
 // Cache policy of a buffer access (the instruction's cache-policy bits; hints
 // only, results are the same). The 16-bit state reductions load K and V
 // non-temporally: 104 -> 93 us at B8-H16-T16384-D64 f16 (207 -> 182 us at
@@ -2295,7 +2309,7 @@ __device__ __forceinline__ float wave_max_nonneg(float x) {
     return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 63));
 }
 
-template <typename T, int DK, int DV, bool SIMPLE, int FM>
+template <typename T, int DK, int DV, bool SIMPLE, int FM, int DKR = DK, int DVR = DV>
 __global__ __launch_bounds__(kThreads, (CausalShape<DK, DV>::kMinBlocks)) void fwd_causal_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const float* __restrict__ pre,
     T* __restrict__ o, int64_t T_, const Layouts lay, int P, int64_t L, float eps) {
@@ -2333,16 +2347,19 @@ __global__ __launch_bounds__(kThreads, (CausalShape<DK, DV>::kMinBlocks)) void f
     // z[16 iR + 4 grp + r] in accZ[iR][r] (wave 0). From the exclusive prefix.
     f32x4 accR[RI][RJ], accZ[RI];
     {
-        const float* pS = (pre != nullptr && p > 0) ? pre + (bh * P + p) * (int64_t)(DK * DV + DK) : nullptr;
+        const float* pS = (pre != nullptr && p > 0) ? pre + (bh * P + p) * (int64_t)(DKR * DVR + DKR) : nullptr;
 #pragma unroll
         for (int iR = 0; iR < RI; ++iR) {
 #pragma unroll
             for (int jR = 0; jR < RJ; ++jR)
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
-                    accR[iR][jR][r] = pS ? pS[(16 * iR + 4 * grp + r) * DV + 16 * (wave * RJ + jR) + m] : 0.f;
+                    {
+                        const int i = 16 * iR + 4 * grp + r, j = 16 * (wave * RJ + jR) + m;
+                        accR[iR][jR][r] = (pS && i < DKR && j < DVR) ? pS[i * DVR + j] : 0.f;
+                    }
 #pragma unroll
-            for (int r = 0; r < 4; ++r) accZ[iR][r] = pS ? pS[DK * DV + 16 * iR + 4 * grp + r] : 0.f;
+            for (int r = 0; r < 4; ++r) accZ[iR][r] = (pS && 16 * iR + 4 * grp + r < DKR) ? pS[DKR * DVR + 16 * iR + 4 * grp + r] : 0.f;
         }
     }
     Frag<T> ones;
@@ -2392,20 +2409,20 @@ __global__ __launch_bounds__(kThreads, (CausalShape<DK, DV>::kMinBlocks)) void f
     struct Stage {
         u32x4 q[NCK], k[NCK], v[NCV];
     };
-    const HeadBuf bq = slice_buf(q, lq, bh, DK, t0, t1), bk = slice_buf(k, lk, bh, DK, t0, t1);
-    const HeadBuf bv = slice_buf(v, lv, bh, DV, t0, t1), bo = slice_buf(o, lo, bh, DV, t0, t1);
+    const HeadBuf bq = slice_buf(q, lq, bh, DKR, t0, t1), bk = slice_buf(k, lk, bh, DKR, t0, t1);
+    const HeadBuf bv = slice_buf(v, lv, bh, DVR, t0, t1), bo = slice_buf(o, lo, bh, DVR, t0, t1);
     auto issue = [&](Stage& st, int c) {
         const int64_t row0 = (int64_t)c * C;
 #pragma unroll
         for (int i = 0; i < NCK; ++i) {
             const int n = tid + kThreads * i, r = n / CK, cc = n % CK;
-            st.q[i] = __builtin_amdgcn_raw_buffer_load_b128(bq.rsrc, buf_off<T>(row0 + r, lq.rs, 8 * cc), 0, 0);
-            st.k[i] = __builtin_amdgcn_raw_buffer_load_b128(bk.rsrc, buf_off<T>(row0 + r, lk.rs, 8 * cc), 0, 0);
+            st.q[i] = __builtin_amdgcn_raw_buffer_load_b128(bq.rsrc, pad_off<DK, DKR>(buf_off<T>(row0 + r, lq.rs, 8 * cc), 8 * cc), 0, 0);
+            st.k[i] = __builtin_amdgcn_raw_buffer_load_b128(bk.rsrc, pad_off<DK, DKR>(buf_off<T>(row0 + r, lk.rs, 8 * cc), 8 * cc), 0, 0);
         }
 #pragma unroll
         for (int i = 0; i < NCV; ++i) {
             const int n = tid + kThreads * i, r = n / CV, cc = n % CV;
-            st.v[i] = __builtin_amdgcn_raw_buffer_load_b128(bv.rsrc, buf_off<T>(row0 + r, lv.rs, 8 * cc), 0, 0);
+            st.v[i] = __builtin_amdgcn_raw_buffer_load_b128(bv.rsrc, pad_off<DV, DVR>(buf_off<T>(row0 + r, lv.rs, 8 * cc), 8 * cc), 0, 0);
         }
     };
     auto consume = [&](const Stage& st, int c) {
@@ -2413,13 +2430,14 @@ __global__ __launch_bounds__(kThreads, (CausalShape<DK, DV>::kMinBlocks)) void f
 #pragma unroll
         for (int i = 0; i < NCK; ++i) {
             const int n = tid + kThreads * i, r = n / CK, cc = n % CK;
-            const bool ok = row0 + r < len;
+            // rows past the segment end and padded feature columns add nothing
+            const bool okq = DKR == DK || 8 * cc < DKR, ok = okq && row0 + r < len;
             Row<T, 8> qin, kin, qt, kt;
             __builtin_memcpy(qin.e, &st.q[i], sizeof(qin));
             __builtin_memcpy(kin.e, &st.k[i], sizeof(kin));
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                qt.e[e] = static_cast<T>(phi<FM, T>(to_f32(qin.e[e])));
+                qt.e[e] = okq ? static_cast<T>(phi<FM, T>(to_f32(qin.e[e]))) : static_cast<T>(0.f);
                 // rows past the segment end must add nothing: mask after phi
                 kt.e[e] = ok ? static_cast<T>(phi<FM, T>(to_f32(kin.e[e]))) : static_cast<T>(0.f);
             }
@@ -2541,7 +2559,7 @@ __global__ __launch_bounds__(kThreads, (CausalShape<DK, DV>::kMinBlocks)) void f
         for (int kk = 0; kk < DV / 32; ++kk) {
             const int rb = 32 * kk + rA;
             const Frag<T> x = join_frag<T>(lds_read_tr(&myW[rb * LDW + cA]), lds_read_tr(&myW[(rb + 4) * LDW + cA]));
-            buf_store16(bo, buf_off<T>(row0 + 16 * wave + m, lo.rs, 32 * kk + 8 * grp), __builtin_bit_cast(uint4, x));
+            buf_store16(bo, pad_off<DV, DVR>(buf_off<T>(row0 + 16 * wave + m, lo.rs, 32 * kk + 8 * grp), 32 * kk + 8 * grp), __builtin_bit_cast(uint4, x));
         }
         wave_lds_sync();
 
@@ -2702,7 +2720,7 @@ __device__ __forceinline__ Frag<T> scale_frag(Frag<T> x, float f) {
 //       reads them for G += Qw^T dO.
 // R^T and z are published at the top of the next chunk, after the barrier
 // that ends this one. Three barriers per chunk; one chunk of loads in flight.
-template <typename T, int DK, int DV, bool SIMPLE, int FM>
+template <typename T, int DK, int DV, bool SIMPLE, int FM, int DKR = DK, int DVR = DV>
 __global__ __launch_bounds__(kThreads, (CausalBwdShape<DK, DV>::kMinBlocks)) void bwd_causal_q_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const T* __restrict__ dout,
     const float* __restrict__ pre, T* __restrict__ dq, float* __restrict__ wc, int* __restrict__ es,
@@ -2745,7 +2763,7 @@ __global__ __launch_bounds__(kThreads, (CausalBwdShape<DK, DV>::kMinBlocks)) voi
     f32x4 accR[RIW][NBV], accZ[RIW], accG[RIW][NBV];
     float gzp[NBI];  // sum of c_t phi(q_t)[16 ib + m] over this lane's rows
     {
-        const float* pS = (pre != nullptr && p > 0) ? pre + (bh * P + p) * (int64_t)(DK * DV + DK) : nullptr;
+        const float* pS = (pre != nullptr && p > 0) ? pre + (bh * P + p) * (int64_t)(DKR * DVR + DKR) : nullptr;
 #pragma unroll
         for (int iR = 0; iR < RIW; ++iR) {
             const int i0 = 16 * (wave * RIW + iR) + 4 * grp;
@@ -2753,10 +2771,11 @@ __global__ __launch_bounds__(kThreads, (CausalBwdShape<DK, DV>::kMinBlocks)) voi
             for (int jb = 0; jb < NBV; ++jb) {
                 accG[iR][jb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int r = 0; r < 4; ++r) accR[iR][jb][r] = pS ? pS[(i0 + r) * DV + 16 * jb + m] : 0.f;
+                for (int r = 0; r < 4; ++r)
+                    accR[iR][jb][r] = (pS && i0 + r < DKR && 16 * jb + m < DVR) ? pS[(i0 + r) * DVR + 16 * jb + m] : 0.f;
             }
 #pragma unroll
-            for (int r = 0; r < 4; ++r) accZ[iR][r] = pS ? pS[DK * DV + i0 + r] : 0.f;
+            for (int r = 0; r < 4; ++r) accZ[iR][r] = (pS && i0 + r < DKR) ? pS[DKR * DVR + i0 + r] : 0.f;
         }
 #pragma unroll
         for (int ib = 0; ib < NBI; ++ib) gzp[ib] = 0.f;
@@ -2796,22 +2815,22 @@ __global__ __launch_bounds__(kThreads, (CausalBwdShape<DK, DV>::kMinBlocks)) voi
     struct Stage {
         u32x4 q[NCK], k[NCK], v[NCV], d[NCV];
     };
-    const HeadBuf bq = slice_buf(q, lq, bh, DK, t0, t1), bk = slice_buf(k, lk, bh, DK, t0, t1);
-    const HeadBuf bv = slice_buf(v, lv, bh, DV, t0, t1), bd = slice_buf(dout, ld, bh, DV, t0, t1);
-    const HeadBuf bdq = slice_buf(dq, lay.dq, bh, DK, t0, t1);
+    const HeadBuf bq = slice_buf(q, lq, bh, DKR, t0, t1), bk = slice_buf(k, lk, bh, DKR, t0, t1);
+    const HeadBuf bv = slice_buf(v, lv, bh, DVR, t0, t1), bd = slice_buf(dout, ld, bh, DVR, t0, t1);
+    const HeadBuf bdq = slice_buf(dq, lay.dq, bh, DKR, t0, t1);
     auto issue = [&](Stage& st, int c) {
         const int64_t row0 = (int64_t)c * C;
 #pragma unroll
         for (int i = 0; i < NCK; ++i) {
             const int n = tid + kThreads * i, r = n / CK, cc = n % CK;
-            st.q[i] = __builtin_amdgcn_raw_buffer_load_b128(bq.rsrc, buf_off<T>(row0 + r, lq.rs, 8 * cc), 0, 0);
-            st.k[i] = __builtin_amdgcn_raw_buffer_load_b128(bk.rsrc, buf_off<T>(row0 + r, lk.rs, 8 * cc), 0, 0);
+            st.q[i] = __builtin_amdgcn_raw_buffer_load_b128(bq.rsrc, pad_off<DK, DKR>(buf_off<T>(row0 + r, lq.rs, 8 * cc), 8 * cc), 0, 0);
+            st.k[i] = __builtin_amdgcn_raw_buffer_load_b128(bk.rsrc, pad_off<DK, DKR>(buf_off<T>(row0 + r, lk.rs, 8 * cc), 8 * cc), 0, 0);
         }
 #pragma unroll
         for (int i = 0; i < NCV; ++i) {
             const int n = tid + kThreads * i, r = n / CV, cc = n % CV;
-            st.v[i] = __builtin_amdgcn_raw_buffer_load_b128(bv.rsrc, buf_off<T>(row0 + r, lv.rs, 8 * cc), 0, 0);
-            st.d[i] = __builtin_amdgcn_raw_buffer_load_b128(bd.rsrc, buf_off<T>(row0 + r, ld.rs, 8 * cc), 0, 0);
+            st.v[i] = __builtin_amdgcn_raw_buffer_load_b128(bv.rsrc, pad_off<DV, DVR>(buf_off<T>(row0 + r, lv.rs, 8 * cc), 8 * cc), 0, 0);
+            st.d[i] = __builtin_amdgcn_raw_buffer_load_b128(bd.rsrc, pad_off<DV, DVR>(buf_off<T>(row0 + r, ld.rs, 8 * cc), 8 * cc), 0, 0);
         }
     };
     auto consume = [&](const Stage& st, int c) {
@@ -2819,13 +2838,14 @@ __global__ __launch_bounds__(kThreads, (CausalBwdShape<DK, DV>::kMinBlocks)) voi
 #pragma unroll
         for (int i = 0; i < NCK; ++i) {
             const int n = tid + kThreads * i, r = n / CK, cc = n % CK;
-            const bool ok = row0 + r < len;
+            // rows past the segment end and padded feature columns add nothing
+            const bool okq = DKR == DK || 8 * cc < DKR, ok = okq && row0 + r < len;
             Row<T, 8> qin, kin, qt, kt;
             __builtin_memcpy(qin.e, &st.q[i], sizeof(qin));
             __builtin_memcpy(kin.e, &st.k[i], sizeof(kin));
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                qt.e[e] = static_cast<T>(phi<FM, T>(to_f32(qin.e[e])));
+                qt.e[e] = okq ? static_cast<T>(phi<FM, T>(to_f32(qin.e[e]))) : static_cast<T>(0.f);
                 kt.e[e] = ok ? static_cast<T>(phi<FM, T>(to_f32(kin.e[e]))) : static_cast<T>(0.f);
             }
             *reinterpret_cast<Row<T, 8>*>(&tQ[r * LDK + 8 * cc]) = qt;
@@ -3027,7 +3047,7 @@ __global__ __launch_bounds__(kThreads, (CausalBwdShape<DK, DV>::kMinBlocks)) voi
             for (int kk = 0; kk < DK / 32; ++kk) {
                 const int rb = 32 * kk + rA;
                 const Frag<T> x = join_frag<T>(lds_read_tr(&myW[rb * LDW + cA]), lds_read_tr(&myW[(rb + 4) * LDW + cA]));
-                buf_store16(bdq, buf_off<T>(row0 + 16 * wave + m, lay.dq.rs, 32 * kk + 8 * grp), __builtin_bit_cast(uint4, x));
+                buf_store16(bdq, pad_off<DK, DKR>(buf_off<T>(row0 + 16 * wave + m, lay.dq.rs, 32 * kk + 8 * grp), 32 * kk + 8 * grp), __builtin_bit_cast(uint4, x));
             }
             wave_lds_sync();
         }
@@ -3122,14 +3142,15 @@ __global__ __launch_bounds__(kThreads, (CausalBwdShape<DK, DV>::kMinBlocks)) voi
         for (int c = 0; c < nchunks; ++c) body(st, c);
     }
     if (gpart != nullptr) {
-        float* gp = gpart + (bh * P + p) * (int64_t)(DK * DV + DK);
+        float* gp = gpart + (bh * P + p) * (int64_t)(DKR * DVR + DKR);
 #pragma unroll
         for (int iR = 0; iR < RIW; ++iR) {
             const int i0 = 16 * (wave * RIW + iR) + 4 * grp;
 #pragma unroll
             for (int jb = 0; jb < NBV; ++jb)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) gp[(i0 + r) * DV + 16 * jb + m] = accG[iR][jb][r];
+                for (int r = 0; r < 4; ++r)
+                    if (i0 + r < DKR && 16 * jb + m < DVR) gp[(i0 + r) * DVR + 16 * jb + m] = accG[iR][jb][r];
         }
         // g: the lanes' sums over their rows, then over the four waves in order
         float* red = reinterpret_cast<float*>(&tW[0][0]);  // free after the last barrier
@@ -3141,7 +3162,7 @@ __global__ __launch_bounds__(kThreads, (CausalBwdShape<DK, DV>::kMinBlocks)) voi
             if (grp == 0) red[wave * DK + 16 * ib + m] = x;
         }
         __syncthreads();
-        if (tid < DK) gp[DK * DV + tid] = ((red[tid] + red[DK + tid]) + red[2 * DK + tid]) + red[3 * DK + tid];
+        if (tid < DKR) gp[DKR * DVR + tid] = ((red[tid] + red[DK + tid]) + red[2 * DK + tid]) + red[3 * DK + tid];
     }
 }
 
@@ -3183,7 +3204,7 @@ __global__ __launch_bounds__(kThreads) void suffix_kernel(float* __restrict__ pa
 //       the A operand is rescaled per quarter to the smallest exponent;
 //   (d) G += Qw^T dO, g += Qw^T c^ on the wave's rows of G.
 // G^T and g are published at the top of the next chunk. Two barriers per chunk.
-template <typename T, int DK, int DV, bool SIMPLE, int FM>
+template <typename T, int DK, int DV, bool SIMPLE, int FM, int DKR = DK, int DVR = DV>
 __global__ __launch_bounds__(kThreads, (CausalBwdShape<DK, DV>::kMinBlocks)) void bwd_causal_kv_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const T* __restrict__ dout,
     const float* __restrict__ wc, const int* __restrict__ es, const float* __restrict__ suf, T* __restrict__ dk,
@@ -3223,16 +3244,17 @@ __global__ __launch_bounds__(kThreads, (CausalBwdShape<DK, DV>::kMinBlocks)) voi
 
     f32x4 accG[RIW][NBV], accGz[RIW];
     {
-        const float* pG = suf != nullptr ? suf + (bh * P + p) * (int64_t)(DK * DV + DK) : nullptr;
+        const float* pG = suf != nullptr ? suf + (bh * P + p) * (int64_t)(DKR * DVR + DKR) : nullptr;
 #pragma unroll
         for (int iR = 0; iR < RIW; ++iR) {
             const int i0 = 16 * (wave * RIW + iR) + 4 * grp;
 #pragma unroll
             for (int jb = 0; jb < NBV; ++jb)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) accG[iR][jb][r] = pG ? pG[(i0 + r) * DV + 16 * jb + m] : 0.f;
+                for (int r = 0; r < 4; ++r)
+                    accG[iR][jb][r] = (pG && i0 + r < DKR && 16 * jb + m < DVR) ? pG[(i0 + r) * DVR + 16 * jb + m] : 0.f;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) accGz[iR][r] = pG ? pG[DK * DV + i0 + r] : 0.f;
+            for (int r = 0; r < 4; ++r) accGz[iR][r] = (pG && i0 + r < DKR) ? pG[DKR * DVR + i0 + r] : 0.f;
         }
     }
 
@@ -3269,9 +3291,9 @@ __global__ __launch_bounds__(kThreads, (CausalBwdShape<DK, DV>::kMinBlocks)) voi
         unsigned w, ch;  // w and c^ of token `lane` of the chunk
         int es;
     };
-    const HeadBuf bq = slice_buf(q, lq, bh, DK, t0, t1), bk = slice_buf(k, lk, bh, DK, t0, t1);
-    const HeadBuf bv = slice_buf(v, lv, bh, DV, t0, t1), bd = slice_buf(dout, ld, bh, DV, t0, t1);
-    const HeadBuf bdk = slice_buf(dk, lay.dk, bh, DK, t0, t1), bdv = slice_buf(dv, lay.dv, bh, DV, t0, t1);
+    const HeadBuf bq = slice_buf(q, lq, bh, DKR, t0, t1), bk = slice_buf(k, lk, bh, DKR, t0, t1);
+    const HeadBuf bv = slice_buf(v, lv, bh, DVR, t0, t1), bd = slice_buf(dout, ld, bh, DVR, t0, t1);
+    const HeadBuf bdk = slice_buf(dk, lay.dk, bh, DKR, t0, t1), bdv = slice_buf(dv, lay.dv, bh, DVR, t0, t1);
     // w and c^ of the segment's tokens (8 bytes each); zeros past the end
     const HeadBuf bwc{__builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(wc + 2 * (bh * T_ + t0)), 0,
                                                         (int)(len > 0 ? 8 * len : 0), 0x00020000)};
@@ -3285,14 +3307,14 @@ __global__ __launch_bounds__(kThreads, (CausalBwdShape<DK, DV>::kMinBlocks)) voi
 #pragma unroll
         for (int i = 0; i < NCK; ++i) {
             const int nn = tid + kThreads * i, r = nn / CK, cc = nn % CK;
-            st.q[i] = __builtin_amdgcn_raw_buffer_load_b128(bq.rsrc, buf_off<T>(row0 + r, lq.rs, 8 * cc), 0, 0);
-            st.k[i] = __builtin_amdgcn_raw_buffer_load_b128(bk.rsrc, buf_off<T>(row0 + r, lk.rs, 8 * cc), 0, 0);
+            st.q[i] = __builtin_amdgcn_raw_buffer_load_b128(bq.rsrc, pad_off<DK, DKR>(buf_off<T>(row0 + r, lq.rs, 8 * cc), 8 * cc), 0, 0);
+            st.k[i] = __builtin_amdgcn_raw_buffer_load_b128(bk.rsrc, pad_off<DK, DKR>(buf_off<T>(row0 + r, lk.rs, 8 * cc), 8 * cc), 0, 0);
         }
 #pragma unroll
         for (int i = 0; i < NCV; ++i) {
             const int nn = tid + kThreads * i, r = nn / CV, cc = nn % CV;
-            st.v[i] = __builtin_amdgcn_raw_buffer_load_b128(bv.rsrc, buf_off<T>(row0 + r, lv.rs, 8 * cc), 0, 0);
-            st.d[i] = __builtin_amdgcn_raw_buffer_load_b128(bd.rsrc, buf_off<T>(row0 + r, ld.rs, 8 * cc), 0, 0);
+            st.v[i] = __builtin_amdgcn_raw_buffer_load_b128(bv.rsrc, pad_off<DV, DVR>(buf_off<T>(row0 + r, lv.rs, 8 * cc), 8 * cc), 0, 0);
+            st.d[i] = __builtin_amdgcn_raw_buffer_load_b128(bd.rsrc, pad_off<DV, DVR>(buf_off<T>(row0 + r, ld.rs, 8 * cc), 8 * cc), 0, 0);
         }
         if constexpr (!SIMPLE) {
             // two dword loads: the 8-byte buffer-load builtin drops the upper dword with this compiler
@@ -3317,7 +3339,8 @@ __global__ __launch_bounds__(kThreads, (CausalBwdShape<DK, DV>::kMinBlocks)) voi
 #pragma unroll
         for (int i = 0; i < NCK; ++i) {
             const int nn = tid + kThreads * i, r = nn / CK, cc = nn % CK;
-            const bool ok = row0 + r < len;
+            // rows past the segment end and padded feature columns add nothing
+            const bool ok = (DKR == DK || 8 * cc < DKR) && row0 + r < len;
             float wt = qscale;  // simple_la: w is the query scale
             if constexpr (!SIMPLE) wt = __shfl(wl, r);
             const float f = ok ? wt * fQ : 0.f;
@@ -3463,7 +3486,7 @@ __global__ __launch_bounds__(kThreads, (CausalBwdShape<DK, DV>::kMinBlocks)) voi
             for (int kk = 0; kk < DK / 32; ++kk) {
                 const int rb = 32 * kk + rA;
                 const Frag<T> x = join_frag<T>(lds_read_tr(&myW[rb * LDW + cA]), lds_read_tr(&myW[(rb + 4) * LDW + cA]));
-                buf_store16(bdk, buf_off<T>(row0 + 16 * wave + m, lay.dk.rs, 32 * kk + 8 * grp), __builtin_bit_cast(uint4, x));
+                buf_store16(bdk, pad_off<DK, DKR>(buf_off<T>(row0 + 16 * wave + m, lay.dk.rs, 32 * kk + 8 * grp), 32 * kk + 8 * grp), __builtin_bit_cast(uint4, x));
             }
             wave_lds_sync();
         }
@@ -3521,7 +3544,7 @@ __global__ __launch_bounds__(kThreads, (CausalBwdShape<DK, DV>::kMinBlocks)) voi
             for (int kk = 0; kk < DV / 32; ++kk) {
                 const int rb = 32 * kk + rA;
                 const Frag<T> x = join_frag<T>(lds_read_tr(&myW[rb * LDW + cA]), lds_read_tr(&myW[(rb + 4) * LDW + cA]));
-                buf_store16(bdv, buf_off<T>(row0 + 16 * wave + m, lay.dv.rs, 32 * kk + 8 * grp), __builtin_bit_cast(uint4, x));
+                buf_store16(bdv, pad_off<DV, DVR>(buf_off<T>(row0 + 16 * wave + m, lay.dv.rs, 32 * kk + 8 * grp), 32 * kk + 8 * grp), __builtin_bit_cast(uint4, x));
             }
             wave_lds_sync();
         }
@@ -3579,8 +3602,7 @@ __global__ __launch_bounds__(kThreads, (CausalBwdShape<DK, DV>::kMinBlocks)) voi
 }
 
 // ---------------------------------------------------------------------------
-// Causal scans on fp32 operands: the causal shapes the 16-bit scans above do
-// not take (fp32 inputs, and 16-bit inputs with D or Dv of 32 or 96).
+// Causal scans on fp32 operands (fp32 inputs, every head size up to 128).
 // ---------------------------------------------------------------------------
 // The same recurrences, segments, prefix and suffix kernels and workspace as
 // the 16-bit scans, in a plainer form. A chunk's tiles are staged in LDS as
@@ -3594,11 +3616,12 @@ __global__ __launch_bounds__(kThreads, (CausalBwdShape<DK, DV>::kMinBlocks)) voi
 // fit one workgroup's LDS. The next chunk's loads are in flight in registers
 // while a chunk is processed.
 struct CF {
-    static constexpr int C = 32;             // tokens per chunk
+    static constexpr int C = 32;             // tokens per chunk (kThreads / 8: eight lanes per row)
     static constexpr int NT = C / 16;        // 16-token blocks per chunk
     static constexpr int NL = NT * (NT + 1) / 2;  // blocks on or below the diagonal
     static constexpr int LC = C + 4;         // row stride of C x C tiles (floats)
 };
+static_assert(CF::C * 8 == kThreads, "the per-row steps take eight lanes per row");
 
 // Block (tb, sb), sb <= tb, of the n-th block on or below the diagonal.
 __device__ __forceinline__ void lower_block(int n, int& tb, int& sb) {
@@ -3760,15 +3783,19 @@ __global__ __launch_bounds__(kThreads) void fwd_causal_f32_kernel(
         }
         __syncthreads();
 
-        if (tid < C) {
+        {
+            // eight lanes per row
+            const int t = tid >> 3, sub = tid & 7;
             if constexpr (SIMPLE) {
-                sRcp[tid] = eps;  // the query scale
+                if (sub == 0) sRcp[t] = eps;  // the query scale
             } else {
                 float den = 0.f;
-                for (int s = 0; s <= tid; ++s) den += sA[tid * LC + s];
-                float qz = 0.f;
-                for (int i = 0; i < DK; ++i) qz += sQ[tid * LK + i] * sZ[i];
-                sRcp[tid] = 1.f / (qz + den + eps);
+                for (int s = sub; s <= t; s += 8) den += sA[t * LC + s];
+                for (int i = sub; i < DK; i += 8) den += sQ[t * LK + i] * sZ[i];
+                den += __shfl_xor(den, 1);
+                den += __shfl_xor(den, 2);
+                den += __shfl_xor(den, 4);
+                if (sub == 0) sRcp[t] = 1.f / (den + eps);
             }
         }
         __syncthreads();
@@ -3911,35 +3938,40 @@ __global__ __launch_bounds__(kThreads) void bwd_causal_q_f32_kernel(
         }
         __syncthreads();
 
-        // (b) per row: w, c, P = mask(w B + c) in place of B
-        if (tid < C) {
-            const int t = tid;
+        // (b) per row (eight lanes each): w, c, P = mask(w B + c) in place of B
+        {
+            const int t = tid >> 3, sub = tid & 7;
             const bool ok = t < nvalid;
             float w, cc = 0.f;
             if constexpr (SIMPLE) {
                 w = ok ? eps : 0.f;  // the query scale
             } else {
-                float den = 0.f, ab = 0.f;
-                for (int s = 0; s <= t; ++s) {
+                float den = 0.f, dot = 0.f;  // phi(q) . z_t and phi(q) . u_t
+                for (int s = sub; s <= t; s += 8) {
                     den += sA[t * LC + s];
-                    ab += sA[t * LC + s] * sB[t * LC + s];
+                    dot += sA[t * LC + s] * sB[t * LC + s];
                 }
-                float qz = 0.f;
-                for (int i = 0; i < DK; ++i) qz += sQ[t * LK + i] * sZ[i];
-                float qy = 0.f;
-                for (int ib = 0; ib < NI; ++ib) qy += sPart[ib * C + t];
-                w = ok ? 1.f / (qz + den + eps) : 0.f;
-                const float chat = -(qy + ab) * w;  // c / w
+                for (int i = sub; i < DK; i += 8) den += sQ[t * LK + i] * sZ[i];
+                for (int ib = sub; ib < NI; ib += 8) dot += sPart[ib * C + t];
+#pragma unroll
+                for (int x = 1; x < 8; x <<= 1) {
+                    den += __shfl_xor(den, x);
+                    dot += __shfl_xor(dot, x);
+                }
+                w = ok ? 1.f / (den + eps) : 0.f;
+                const float chat = -dot * w;  // c / w
                 cc = chat * w;
-                if (ok) {
+                if (ok && sub == 0) {
                     float* wt = wc + (bh * T_ + t0 + (int64_t)c * C + t) * 2;
                     wt[0] = w;
                     wt[1] = chat;
                 }
             }
-            sW[t] = w;
-            sC[t] = cc;
-            for (int s = 0; s < C; ++s) sB[t * LC + s] = s <= t ? w * sB[t * LC + s] + cc : 0.f;
+            if (sub == 0) {
+                sW[t] = w;
+                sC[t] = cc;
+            }
+            for (int s = sub; s < C; s += 8) sB[t * LC + s] = s <= t ? w * sB[t * LC + s] + cc : 0.f;
         }
         __syncthreads();
 
@@ -4968,10 +5000,14 @@ SplitCfg wide_split_config(int step) {
     }
 }
 
-// Where the 16-bit causal scans run: 16-bit elements, DK and DV in {64, 128};
-// every other causal shape takes the fp32-operand scans.
+// 16-bit elements take the 16-bit causal scans, built for head sizes 64 and
+// 128: a head size of 32 or 96 runs the kernel for the next of them with the
+// missing feature columns read as zeros (phi of them zeroed too) and never
+// stored; fp32 elements take the fp32-operand scans.
 template <typename T, int DK, int DV>
-constexpr bool kCausalKernels = sizeof(T) == 2 && (DK == 64 || DK == 128) && (DV == 64 || DV == 128);
+constexpr bool kCausalKernels = sizeof(T) == 2;
+template <int D>
+constexpr int kCausalPad = D <= 64 ? 64 : 128;
 
 // Causal forward: segment states, their exclusive prefixes in place (and the
 // full state), then the chunked scan of every segment.
@@ -4994,11 +5030,12 @@ hipError_t fwd_causal_fm(const Plan& p, const void* q, const void* k, const void
     T* oo = static_cast<T*>(o);
     const int64_t nblk = p.BH * p.P;
     if constexpr (kCausalKernels<T, DK, DV>) {
+        constexpr int DKP = kCausalPad<DK>, DVP = kCausalPad<DV>;
         if (p.simple)
-            return launch(fwd_causal_kernel<T, DK, DV, true, FM>, nblk, kThreads, s, qq, kk, vv, pre, oo, p.T, p.lay,
-                          p.P, p.L, p.eps);
-        return launch(fwd_causal_kernel<T, DK, DV, false, FM>, nblk, kThreads, s, qq, kk, vv, pre, oo, p.T, p.lay,
-                      p.P, p.L, p.eps);
+            return launch(fwd_causal_kernel<T, DKP, DVP, true, FM, DK, DV>, nblk, kThreads, s, qq, kk, vv, pre, oo,
+                          p.T, p.lay, p.P, p.L, p.eps);
+        return launch(fwd_causal_kernel<T, DKP, DVP, false, FM, DK, DV>, nblk, kThreads, s, qq, kk, vv, pre, oo, p.T,
+                      p.lay, p.P, p.L, p.eps);
     } else {
         if (p.simple)
             return launch(fwd_causal_f32_kernel<T, DK, DV, true, FM>, nblk, kThreads, s, qq, kk, vv, pre, oo, p.T,
@@ -5039,11 +5076,12 @@ hipError_t bwd_causal_fm(const Plan& p, const void* q, const void* k, const void
     T* dkk = static_cast<T*>(dk);
     T* dvv = static_cast<T*>(dv);
     const int64_t nblk = p.BH * p.P;
+    constexpr int DKP = kCausalPad<DK>, DVP = kCausalPad<DV>;
     if constexpr (kCausalKernels<T, DK, DV>) {
-        e = p.simple ? launch(bwd_causal_q_kernel<T, DK, DV, true, FM>, nblk, kThreads, s, qq, kk, vv, dd, pre, dqq,
-                              wcp, esp, gp, p.T, p.lay, p.P, p.L, p.nche, p.eps)
-                     : launch(bwd_causal_q_kernel<T, DK, DV, false, FM>, nblk, kThreads, s, qq, kk, vv, dd, pre, dqq,
-                              wcp, esp, gp, p.T, p.lay, p.P, p.L, p.nche, p.eps);
+        e = p.simple ? launch(bwd_causal_q_kernel<T, DKP, DVP, true, FM, DK, DV>, nblk, kThreads, s, qq, kk, vv, dd,
+                              pre, dqq, wcp, esp, gp, p.T, p.lay, p.P, p.L, p.nche, p.eps)
+                     : launch(bwd_causal_q_kernel<T, DKP, DVP, false, FM, DK, DV>, nblk, kThreads, s, qq, kk, vv, dd,
+                              pre, dqq, wcp, esp, gp, p.T, p.lay, p.P, p.L, p.nche, p.eps);
     } else {
         e = p.simple ? launch(bwd_causal_q_f32_kernel<T, DK, DV, true, FM>, nblk, kThreads, s, qq, kk, vv, dd, pre,
                               dqq, wcp, gp, p.T, p.lay, p.P, p.L, p.eps)
@@ -5056,10 +5094,10 @@ hipError_t bwd_causal_fm(const Plan& p, const void* q, const void* k, const void
         if (e != hipSuccess) return e;
     }
     if constexpr (kCausalKernels<T, DK, DV>) {
-        return p.simple ? launch(bwd_causal_kv_kernel<T, DK, DV, true, FM>, nblk, kThreads, s, qq, kk, vv, dd, wcp,
-                                 esp, gp, dkk, dvv, p.T, p.lay, p.P, p.L, p.nche, p.eps)
-                        : launch(bwd_causal_kv_kernel<T, DK, DV, false, FM>, nblk, kThreads, s, qq, kk, vv, dd, wcp,
-                                 esp, gp, dkk, dvv, p.T, p.lay, p.P, p.L, p.nche, 1.f);
+        return p.simple ? launch(bwd_causal_kv_kernel<T, DKP, DVP, true, FM, DK, DV>, nblk, kThreads, s, qq, kk, vv,
+                                 dd, wcp, esp, gp, dkk, dvv, p.T, p.lay, p.P, p.L, p.nche, p.eps)
+                        : launch(bwd_causal_kv_kernel<T, DKP, DVP, false, FM, DK, DV>, nblk, kThreads, s, qq, kk, vv,
+                                 dd, wcp, esp, gp, dkk, dvv, p.T, p.lay, p.P, p.L, p.nche, 1.f);
     } else {
         return p.simple ? launch(bwd_causal_kv_f32_kernel<T, DK, DV, true, FM>, nblk, kThreads, s, qq, kk, vv, dd,
                                  wcp, gp, dkk, dvv, p.T, p.lay, p.P, p.L, p.eps)

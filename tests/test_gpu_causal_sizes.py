@@ -1,11 +1,12 @@
-"""GPU parity of the causal scans on fp32 operands, which take every causal
-shape the 16-bit scans do not (fp32 inputs, and f16/bf16 inputs with D or Dv
-of 32 or 96), against the fp64 oracle's causal forms: forward and backward on
-every element at small sizes (several segments and 32-token chunks, ragged
-tails, T = 1), simple_la, the other feature maps, the query scale, the
-token-major layout and strided views, a long sequence with many segments,
-the empty sequence and bit-identical reruns. fp32 inputs are held to the
-tight fp32 bar, 16-bit ones to their dtype's bar."""
+"""GPU parity of the causal form beyond f16/bf16 at head sizes 64 and 128:
+the scans on fp32 operands (fp32 inputs, every head size up to 128) and the
+16-bit scans run with a head size of 32 or 96 padded inside the kernel,
+against the fp64 oracle's causal forms: forward and backward on every element
+at small sizes (several segments and chunks, ragged tails, T = 1), simple_la,
+the other feature maps, the query scale, the token-major layout and strided
+views, a long sequence with many segments, the empty sequence and
+bit-identical reruns. fp32 inputs are held to the tight fp32 bar, 16-bit ones
+to their dtype's bar."""
 import numpy as np
 import pytest
 import torch
@@ -78,7 +79,7 @@ def test_all_elements(T, D, Dv, dtype, simple):
     seed = 120_000 + 97 * T + 13 * D + Dv + 7 * ["f32", "f16", "bf16"].index(dtype) + (3 if simple else 0)
     w = Workload("causal-f32", 2, 3, T, D, dtype, simple=simple, seed=seed, Dv=Dv)
     split = la.split_of(la.make_problem(w.shape, TORCH_DTYPE[dtype], w.eps, simple, dv=Dv, causal=True))
-    print(f"case causal fp32-operand T={T} D={D} Dv={Dv} {dtype} simple={simple} seed={seed} split={split}",
+    print(f"case causal T={T} D={D} Dv={Dv} {dtype} simple={simple} seed={seed} split={split}",
           flush=True)
     x = make_inputs(w)
     _, o, st, g = run(w, x, simple)
@@ -91,7 +92,7 @@ def test_other_feature_maps(dtype, fm, simple):
     D, Dv = (96, 64) if dtype == "f32" else (32, 96)
     w = Workload("causal-f32-maps", 1, 3, 777, D, dtype, simple=simple, seed=121_000 + 5 * ["relu", "identity"].index(fm)
                  + simple, Dv=Dv)
-    print(f"case causal fp32-operand phi={fm} simple={simple} {dtype} D={D} Dv={Dv} seed={w.seed}", flush=True)
+    print(f"case causal phi={fm} simple={simple} {dtype} D={D} Dv={Dv} seed={w.seed}", flush=True)
     x = make_inputs(w)
     if fm == "identity" and not simple:
         # keep the identity map's normaliser away from zero
@@ -137,7 +138,7 @@ def test_long_sequence_many_segments(D, Dv, dtype):
     w = Workload("causal-f32-long", 1, 2, 16384, D, dtype, seed=123_000 + D + Dv, Dv=Dv)
     prob = la.make_problem(w.shape, TORCH_DTYPE[dtype], w.eps, False, dv=Dv, causal=True)
     split = la.split_of(prob)
-    print(f"case causal fp32-operand B1 H2 T16384 D={D} Dv={Dv} {dtype} seed={w.seed} split={split}", flush=True)
+    print(f"case causal B1 H2 T16384 D={D} Dv={Dv} {dtype} seed={w.seed} split={split}", flush=True)
     assert split["P"] > 8
     x = make_inputs(w)
     dev, o, st, g = run(w, x, False)
