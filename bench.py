@@ -47,6 +47,21 @@ def launch_bytes(w) -> dict:
     dO, writes dQ; dkv reads K, V, writes dK, dV."""
     nk, nv = w.numel * w.elem_bytes, w.numel_v * w.elem_bytes
     return {"fwd_state": nk + nv, "fwd_output": nk + nv, "bwd_dq": 2 * nk + nv, "bwd_dkv": 2 * nk + 2 * nv}
+
+
+def launch_flops(w) -> dict:
+    """Algorithmic FLOPs per launch (a multiply-add counts 2), per token:
+    state S += phi(k) v^T and z += phi(k): 2 D (Dv + 1); output phi(q) S and
+    phi(q) . z: 2 D (Dv + 1); bwd Q side u = S dO, phi(q) . u, dS += phi(q) g^T
+    and dz += c phi(q): 2 D (2 Dv + 2); bwd K/V side dS v + dz and dS^T phi(k):
+    2 D (2 Dv + 1)."""
+    n, D, Dv = w.B * w.H * w.T, w.D, w.dv
+    return {"fwd_state": 2 * n * D * (Dv + 1), "fwd_output": 2 * n * D * (Dv + 1),
+            "bwd_dq": 2 * n * D * (2 * Dv + 2), "bwd_dkv": 2 * n * D * (2 * Dv + 1)}
+
+
+# Dense MFMA peaks of MI355X (published; no sparsity), TFLOP/s per operand type
+MFMA_PEAK_TFLOPS = {"f32": 157.3, "f16": 2500.0, "bf16": 2500.0}
 DTYPE_NAME = {"f32": "f32", "f16": "f16", "bf16": "bf16"}
 
 
@@ -153,8 +168,10 @@ def storage(t: torch.Tensor) -> np.ndarray:
 
 
 def versions() -> dict:
-    """Toolchain and library versions of this run."""
-    import subprocess
+    """Toolchain and library versions of this run (no child process: the
+    compiler that built libla.so is read from the file the build wrote beside
+    it, the HIP runtime's version from the runtime torch has loaded)."""
+    import ctypes
 
     out = {"torch": torch.__version__, "torch_hip": getattr(torch.version, "hip", None),
            "la_version": int(la.lib().la_version())}
@@ -163,10 +180,15 @@ def versions() -> dict:
     except OSError:
         out["rocm"] = None
     try:
-        r = subprocess.run(["/opt/rocm/bin/hipcc", "--version"], capture_output=True, text=True, timeout=30)
-        out["hipcc"] = next((ln.strip() for ln in r.stdout.splitlines() if "HIP version" in ln), None)
-    except (OSError, subprocess.SubprocessError):
+        out["hipcc"] = json.load(open(os.path.join(ROOT, "non_causal_linear_amd", "libla.build.json")))["hipcc"]
+    except (OSError, ValueError, KeyError):
         out["hipcc"] = None
+    try:
+        rt = ctypes.c_int(0)
+        if ctypes.CDLL("libamdhip64.so").hipRuntimeGetVersion(ctypes.byref(rt)) == 0:
+            out["hip_runtime"] = rt.value
+    except OSError:
+        pass
     try:
         out["gpu"] = torch.cuda.get_device_properties(0).gcnArchName
     except (AttributeError, RuntimeError):
@@ -423,6 +445,18 @@ def main() -> int:
     dominant = max(avg, key=avg.get)
     dom_bytes = lb[dominant]
     achieved = dom_bytes / (avg[dominant] * 1e-3) / 1e9
+    # the dominant kernel's bound: the larger of its HBM and MFMA fractions
+    # (fp32 operands run MFMA at 157.3 TFLOP/s, below what 8 TB/s would feed)
+    tflops = launch_flops(w)[dominant] / (avg[dominant] * 1e-3) / 1e12
+    mfma_frac = tflops / MFMA_PEAK_TFLOPS[w.dtype]
+    if mfma_frac > achieved / HBM_PEAK_GBS:
+        roof = {"kernel": dominant, "bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_PEAK_TFLOPS[w.dtype],
+                "unit": "TFLOP/s", "frac": round(mfma_frac, 4), "traffic": None,
+                "hbm_GBps": round(achieved, 1), "hbm_frac": round(achieved / HBM_PEAK_GBS, 4)}
+    else:
+        roof = {"kernel": dominant, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "mfma_TFLOPs": round(tflops, 2), "mfma_frac": round(mfma_frac, 4)}
 
     # one more step after the timed ones (untimed): its outputs must equal the
     # last timed step's byte for byte
@@ -474,15 +508,7 @@ def main() -> int:
         "bit_identical_rerun": bit_identical,
         "split": la.split_of(prob),
         "versions": versions(),
-        "roofline": {
-            "kernel": dominant,
-            "bound": "hbm",
-            "achieved": round(achieved, 1),
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None,
-        },
+        "roofline": roof,
     }
     # HBM bytes per launch measured by rocprofv3 FETCH_SIZE / WRITE_SIZE runs
     # (scaled by a 1 GiB copy), valid only while the kernels are unchanged

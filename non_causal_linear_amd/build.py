@@ -10,6 +10,7 @@ a process that has the old library open keeps a consistent file).
 """
 from __future__ import annotations
 
+import json
 import os
 import shutil
 import subprocess
@@ -22,6 +23,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libla.so")
+# what built LIB (compiler version and flags), written beside it; bench.py reports it
+BUILD_INFO = os.path.join(PKG, "libla.build.json")
 
 KERNELS = "la_kernels.hip"
 API = "la_api.cpp"
@@ -86,6 +89,11 @@ def build(verbose: bool = False, jobs: int | None = None) -> str:
         if text:
             print(text, file=sys.stderr)
     os.replace(tmp, LIB)
+    ver = subprocess.run([cc, "--version"], capture_output=True, text=True).stdout
+    info = {"hipcc": next((ln.strip() for ln in ver.splitlines() if "HIP version" in ln), None),
+            "flags": HIPCC_FLAGS, "units": [list(u) for u in UNITS]}
+    with open(BUILD_INFO, "w") as f:
+        json.dump(info, f, indent=1)
     return LIB
 
 
