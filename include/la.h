@@ -182,9 +182,10 @@ size_t la_workspace_bytes(const la_problem* p);
  * split-T reduction of the forward (steps 1-3; with LA_CAUSAL also the scan
  * segments) cuts each head into P slices of L tokens, the backward's Q side
  * (steps 5-6) into PB slices of LB tokens; the output (step 4) and the
- * backward's K/V side (step 7) run NQ chunks of LQ and NK chunks of LK tokens
- * per head. The method itself names no split (any split gives the same S, z up
- * to rounding order); this is for logs and benchmarks. */
+ * backward's K/V side (step 7) run NQ and NK workgroups per head, which take
+ * the head's token rounds in turn, about LQ and LK tokens each. The method
+ * itself names no split (any split gives the same S, z up to rounding order);
+ * this is for logs and benchmarks. */
 typedef struct {
     int64_t P, L, PB, LB, NQ, LQ, NK, LK;
 } la_split;
