@@ -105,8 +105,11 @@ typedef enum {
  * run scans on 16-bit MFMA operands (a head size of 32 or 96 padded to 64 or
  * 128 inside the kernel, the padding never read from or written to memory);
  * fp32 runs scans on fp32 operands.
- * la_fwd's `state` receives the full-sequence S, z, bit-identical to the
- * non-causal call; la_bwd does not read `state`. The step calls return
+ * la_fwd's `state` receives the full-sequence S, z, summed over the causal
+ * segments in a fixed order: bit-identical to the non-causal call's except at
+ * 16-bit D = Dv = 64, whose causal form sums twice as many segments as the
+ * non-causal call sums slices (the same values up to the order of the fp32
+ * additions). la_bwd does not read `state`. The step calls return
  * LA_ERR_FLAGS with it. la_workspace_bytes counts the causal backward's
  * scratch when the flag is set. */
 #define LA_CAUSAL 0x10u
@@ -239,8 +242,8 @@ int la_bwd(const la_problem* p, const void* q, const void* k, const void* v,
  * bytes when the planner splits each head into P > 1 token slices, none when
  * P = 1 (as soon as B*H fills the state kernel's grid of 512 to 2048
  * workgroups); every 16-bit problem with D and Dv up to 96 and every fp32
- * problem with D and Dv up to 64 fits, and so do B8-H16-T16384-D64 (8.5 MB)
- * and B8-H32-T8192-D128 (33.8 MB). The scratch is
+ * problem with D and Dv up to 64 fits, and so do B8-H16-T16384-D64 (4.3 MB;
+ * 8.5 MB causal) and B8-H32-T8192-D128 (33.8 MB). The scratch is
  * shared by every la_fwd_noalloc call on a GPU: calls that may overlap in time
  * on one GPU (different streams with no ordering between them, or different
  * host threads) race on it; calls in one stream's order do not. The current

@@ -223,7 +223,8 @@ la::Plan make_plan(const la_problem* p) {
     pl.lay.dk = layout_of(p, kDK);
     pl.lay.dv = layout_of(p, kDV);
     const la::KernelSet* ks = kernel_set(pl.dtype, pl.DK);
-    split(pl.BH, pl.T, ks->split_config(la::kStepState, pl.DV), pl.P, pl.L);
+    const bool causal = (p->flags & LA_CAUSAL) != 0;
+    split(pl.BH, pl.T, ks->split_config(causal ? la::kStepCausalState : la::kStepState, pl.DV), pl.P, pl.L);
     split(pl.BH, pl.T, ks->split_config(la::kStepBwdQ, pl.DV), pl.PB, pl.LB);
     split(pl.BH, pl.T, ks->split_config(la::kStepOutput, pl.DV), pl.NQ, pl.LQ);
     split(pl.BH, pl.T, ks->split_config(la::kStepBwdKV, pl.DV), pl.NK, pl.LK);
@@ -235,7 +236,7 @@ la::Plan make_plan(const la_problem* p) {
     pl.off_dstate = part;
     pl.off_fstate = pl.off_dstate + st;
     pl.ws_bytes = pl.off_fstate + st;
-    if (p->flags & LA_CAUSAL) {
+    if (causal) {
         // 64-token chunks per segment, rounded up to even (the scans walk chunk pairs)
         pl.nche = static_cast<int>(((pl.L + 63) / 64 + 1) / 2 * 2);
         pl.off_cgpart = pl.ws_bytes;

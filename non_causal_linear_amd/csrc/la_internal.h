@@ -64,7 +64,10 @@ struct SplitCfg {
     int64_t gran;
     int64_t target_wgs;
 };
-enum Step { kStepState = 0, kStepOutput = 1, kStepBwdQ = 2, kStepBwdKV = 3 };
+// kStepCausalState: the state reduction whose slices are the causal scans'
+// segments (the scans run one workgroup per segment, so they want more of them
+// than the bidirectional reduction does).
+enum Step { kStepState = 0, kStepOutput = 1, kStepBwdQ = 2, kStepBwdKV = 3, kStepCausalState = 4 };
 
 // The launchers of one compilation unit of la_kernels.hip: one element type
 // and one DK, every DV (dispatched on Plan::DV). split_config gives the
