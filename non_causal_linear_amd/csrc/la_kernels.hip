@@ -5267,7 +5267,10 @@ SplitCfg split_config_t(int step) {
             return {int64_t(StreamShape<T, DK, DV>::kStages) * 16 * StreamShape<T, DK, DV>::kWaves,
                     StreamShape<T, DK, DV>::kSmall ? 2048 : 1024};
         default:
-            return {StreamShape<T, DK, DV>::kStages * StreamShape<T, DK, DV>::kG, 2048};
+            // the output: at least four turns of the pipeline per workgroup, so
+            // that short sequences do not spend their workgroups on prologues
+            // (B8-H16-T4096-D64 f16: 34.9 -> 29.2 us; T = 16384 unchanged)
+            return {4 * StreamShape<T, DK, DV>::kStages * StreamShape<T, DK, DV>::kG, 2048};
     }
 }
 
