@@ -47,6 +47,7 @@ void split(int64_t BH, int64_t T, la::SplitCfg cfg, int& P, int64_t& L) {
     const int64_t maxp = std::max<int64_t>(1, T / kMinSlice);
     int64_t p = 1;
     while (p * 2 <= want && p * 2 <= maxp) p *= 2;
+    while (cfg.max_len > 0 && cdiv(T, p) > cfg.max_len && p * 2 <= maxp) p *= 2;
     L = cdiv(cdiv(T, p), gran) * gran;
     P = static_cast<int>(cdiv(T, L));
 }

@@ -63,6 +63,7 @@ struct Plan {
 struct SplitCfg {
     int64_t gran;
     int64_t target_wgs;
+    int64_t max_len = 0;  // if set, more pieces until each holds at most this many tokens
 };
 // kStepCausalState: the state reduction whose slices are the causal scans'
 // segments (the scans run one workgroup per segment, so they want more of them

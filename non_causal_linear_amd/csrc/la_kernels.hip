@@ -5265,7 +5265,12 @@ SplitCfg split_config_t(int step) {
             // against 200 us at one turn and 201 us with contiguous chunks
             // (B8-H16-T16384-D64 f16)
             return {int64_t(StreamShape<T, DK, DV>::kStages) * 16 * StreamShape<T, DK, DV>::kWaves,
-                    StreamShape<T, DK, DV>::kSmall ? 2048 : 1024};
+                    StreamShape<T, DK, DV>::kSmall ? 2048 : 1024,
+                    // and at most 1024 tokens per workgroup where that asks for
+                    // more: B2-H8-T262144-D64 bf16 417 us against 440 us at 2048
+                    // workgroups (2048 tokens each); the headline shape is at
+                    // 1024 tokens already
+                    StreamShape<T, DK, DV>::kSmall ? 1024 : 0};
         default:
             // the output: at least four turns of the pipeline per workgroup, so
             // that short sequences do not spend their workgroups on prologues
