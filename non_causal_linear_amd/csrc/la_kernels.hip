@@ -193,6 +193,7 @@ __device__ __forceinline__ float dphi_of(float p) {
 template <typename T>
 __device__ __forceinline__ float to_f32(T x) { return static_cast<float>(x); }
 
+
 // Hardware places workgroup b on XCD b % 8. Renumber so that consecutive
 // logical ids (the slices or chunks of one head) share an XCD and its L2.
 __device__ __forceinline__ int xcd_remap(int b, int n) {
@@ -213,6 +214,126 @@ struct alignas(16) Row {
 // the head continues: the kernels need no clamping or branches at the ragged
 // end of a slice.
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+// phi of eight 16-bit values (one 16-byte row piece), each rounded to the
+// element type: the bits of static_cast<T>(phi<FM, T>(x)) for every x. For
+// f16 the work runs on packed halves, four instructions an element instead of
+// about eight:
+//   elu + 1 = max(x, 0) + e^min(x, 0). For x > 0 the exponential is exp2(0) =
+//     1 and the f16 sum is x + 1 rounded once, as the fp32 sum rounded to f16
+//     is (that sum is exact in fp32 wherever the f16 rounding could be near a
+//     tie); for x <= 0 it is 0 plus e^x rounded to f16. The exponent x log2(e)
+//     is formed in fp32 from the f16 input, as in feature(). The IEEE
+//     minimum / maximum forms carry NaN through, and phi(inf) = inf,
+//     phi(-inf) = 0 as before.
+//   relu = maximum(x, 0) (+0 for an input of -0, where the scalar form keeps
+//     -0: the same value).
+// Other element types take the scalar form.
+template <int FM, typename T>
+__device__ __forceinline__ u32x4 phi8(u32x4 raw) {
+    static_assert(sizeof(T) == 2, "eight 16-bit values in 16 bytes");
+    if constexpr (FM == kPhiIdentity) {
+        return raw;
+    } else if constexpr (std::is_same<T, f16>::value) {
+        typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+        h2 x[4];
+        __builtin_memcpy(x, &raw, sizeof(x));
+        const h2 zero = {static_cast<f16>(0.f), static_cast<f16>(0.f)};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if constexpr (FM == kPhiRelu) {
+                x[i] = __builtin_elementwise_maximum(x[i], zero);
+            } else {
+                const h2 mn = __builtin_elementwise_minimum(x[i], zero);
+                const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(static_cast<float>(mn[0]), 1.4426950408889634f, 0.f));
+                const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(static_cast<float>(mn[1]), 1.4426950408889634f, 0.f));
+                const h2 e = {static_cast<f16>(e0), static_cast<f16>(e1)};
+                x[i] = __builtin_elementwise_maximum(x[i], zero) + e;
+            }
+        }
+        u32x4 out;
+        __builtin_memcpy(&out, x, sizeof(out));
+        return out;
+    } else {
+        T v[8];
+        __builtin_memcpy(v, &raw, sizeof(v));
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = static_cast<T>(phi<FM, T>(to_f32(v[e])));
+        u32x4 out;
+        __builtin_memcpy(&out, v, sizeof(out));
+        return out;
+    }
+}
+
+// phi of eight 16-bit values in fp32: the values of phi<FM, T>(x), the same
+// identities as phi8 with the final sum max(x, 0) + e formed in fp32 (one
+// rounding, as x + 1 in the scalar form; 0 + e = e below zero).
+template <int FM, typename T>
+__device__ __forceinline__ void phi8_f32(u32x4 raw, float (&p)[8]) {
+    static_assert(sizeof(T) == 2, "eight 16-bit values in 16 bytes");
+    if constexpr (std::is_same<T, f16>::value && FM != kPhiIdentity) {
+        typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+        h2 x[4];
+        __builtin_memcpy(x, &raw, sizeof(x));
+        const h2 zero = {static_cast<f16>(0.f), static_cast<f16>(0.f)};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const h2 mx = __builtin_elementwise_maximum(x[i], zero);
+            if constexpr (FM == kPhiRelu) {
+                p[2 * i] = static_cast<float>(mx[0]);
+                p[2 * i + 1] = static_cast<float>(mx[1]);
+            } else {
+                const h2 mn = __builtin_elementwise_minimum(x[i], zero);
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(static_cast<float>(mn[h]), 1.4426950408889634f, 0.f));
+                    p[2 * i + h] = __builtin_fmaf(static_cast<float>(mx[h]), 1.f, e);
+                }
+            }
+        }
+    } else {
+        T v[8];
+        __builtin_memcpy(v, &raw, sizeof(v));
+#pragma unroll
+        for (int e = 0; e < 8; ++e) p[e] = phi<FM, T>(to_f32(v[e]));
+    }
+}
+
+// phi and phi' of eight 16-bit values in fp32: the values feature() gives.
+// For elu + 1 on f16 from the identities of phi8, with phi'(x) = e^min(x, 0)
+// itself (exp2(0) = 1 for x > 0); the other cases take feature().
+template <int FM, typename T>
+__device__ __forceinline__ void feature8(u32x4 raw, float* p, float* dp) {
+    static_assert(sizeof(T) == 2, "eight 16-bit values in 16 bytes");
+    if constexpr (std::is_same<T, f16>::value && FM == kPhiElu1) {
+        typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+        h2 x[4];
+        __builtin_memcpy(x, &raw, sizeof(x));
+        const h2 zero = {static_cast<f16>(0.f), static_cast<f16>(0.f)};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const h2 mx = __builtin_elementwise_maximum(x[i], zero);
+            const h2 mn = __builtin_elementwise_minimum(x[i], zero);
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(static_cast<float>(mn[h]), 1.4426950408889634f, 0.f));
+                p[2 * i + h] = __builtin_fmaf(static_cast<float>(mx[h]), 1.f, e);
+                dp[2 * i + h] = e;
+            }
+        }
+    } else {
+        T v[8];
+        __builtin_memcpy(v, &raw, sizeof(v));
+#pragma unroll
+        for (int e = 0; e < 8; ++e) feature<FM, T>(to_f32(v[e]), p[e], dp[e]);
+    }
+}
+
+// keep ? x : 0 on a 16-byte row piece
+__device__ __forceinline__ u32x4 keep_or_zero(u32x4 x, bool keep) {
+    return keep ? x : u32x4{0u, 0u, 0u, 0u};
+}
+
 struct HeadBuf {
     __amdgpu_buffer_rsrc_t rsrc;
 };
@@ -789,12 +910,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_state_w64_kernel(
         for (int r = 0; r < 4; ++r) {
             const int row = rg + 8 * r;
             const bool ok = (int64_t)rot(step) * STEP + row < t1 - t0;
-            const T* ke = reinterpret_cast<const T*>(&st.k[r]);
-            Row<T, 8> kt;
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-                kt.e[e] = ok ? static_cast<T>(phi<FM, T>(to_f32(ke[e]))) : static_cast<T>(0.f);
-            *reinterpret_cast<uint4*>(&sK[row * LDR + 8 * c]) = *reinterpret_cast<const uint4*>(kt.e);
+            const uint4 kr = st.k[r];
+            *reinterpret_cast<u32x4*>(&sK[row * LDR + 8 * c]) = keep_or_zero(phi8<FM, T>(u32x4{kr.x, kr.y, kr.z, kr.w}), ok);
             *reinterpret_cast<uint4*>(&sV[row * LDR + 8 * c]) = st.v[r];
         }
     };
@@ -983,11 +1100,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_state_tile_kernel(
         for (int i = 0; i < NCK; ++i) {
             const int n = tid + kThreads * i, r = n / CK, c = n % CK;
             const bool ok = row0 + r < len;
-            Row<T, 8> kin, kt;
-            __builtin_memcpy(kin.e, &st.k[i], sizeof(kin));
-#pragma unroll
-            for (int e = 0; e < 8; ++e) kt.e[e] = ok ? static_cast<T>(phi<FM, T>(to_f32(kin.e[e]))) : static_cast<T>(0.f);
-            *reinterpret_cast<Row<T, 8>*>(&dK[r * LDK + 8 * c]) = kt;
+            *reinterpret_cast<u32x4*>(&dK[r * LDK + 8 * c]) = keep_or_zero(phi8<FM, T>(st.k[i]), ok);
         }
 #pragma unroll
         for (int i = 0; i < NCV; ++i) {
@@ -1246,10 +1359,16 @@ __global__ __launch_bounds__((StreamShape<T, DK, DV>::kThreads), (StreamShape<T,
 #pragma unroll
         for (int u = 0; u < U; ++u)
 #pragma unroll
-            for (int s = 0; s < KS; ++s)
+            for (int s = 0; s < KS; ++s) {
+                if constexpr (sizeof(T) == 2) {
+                    u32x4 raw;
+                    __builtin_memcpy(&raw, &qr[u].e[8 * s], sizeof(raw));
+                    bq[u][s] = __builtin_bit_cast(Frag<T>, phi8<FM, T>(raw));
+                } else {
 #pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    bq[u][s][e] = static_cast<T>(phi<FM, T>(to_f32(qr[u].e[8 * s + e])));
+                    for (int e = 0; e < 8; ++e) bq[u][s][e] = phi<FM, T>(qr[u].e[8 * s + e]);
+                }
+            }
         sched_fence();
         issue(qr, blk + NS * NW);
         sched_fence();
@@ -1651,8 +1770,10 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_w64_kernel(
         float qt[F], dph[F];
         Frag<T> bq[KS], bd[KS];
 #pragma unroll
-        for (int o = 0; o < F; ++o) {
-            feature<FM, T>(to_f32(lq.e[o]), qt[o], dph[o]);
+        for (int s = 0; s < F / 8; ++s) {
+            u32x4 raw;
+            __builtin_memcpy(&raw, &lq.e[8 * s], sizeof(raw));
+            feature8<FM, T>(raw, &qt[8 * s], &dph[8 * s]);
         }
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
@@ -2177,9 +2298,16 @@ __global__ __launch_bounds__((StreamShape<T, DK, DV>::kThreads), (StreamShape<T,
             __builtin_memcpy(lk_.e, st.k[u], sizeof(lk_));
             __builtin_memcpy(lv_.e, st.v[u], sizeof(lv_));
             float kt[FK];
+            if constexpr (sizeof(T) == 2) {
 #pragma unroll
-            for (int o = 0; o < FK; ++o) {
-                feature<FM, T>(to_f32(lk_.e[o]), kt[o], dphik[u][o]);
+                for (int s = 0; s < FK / 8; ++s) {
+                    u32x4 raw;
+                    __builtin_memcpy(&raw, &lk_.e[8 * s], sizeof(raw));
+                    feature8<FM, T>(raw, &kt[8 * s], &dphik[u][8 * s]);
+                }
+            } else {
+#pragma unroll
+                for (int o = 0; o < FK; ++o) feature<FM, T>(to_f32(lk_.e[o]), kt[o], dphik[u][o]);
             }
 #pragma unroll
             for (int s = 0; s < KSK; ++s)
@@ -2443,17 +2571,9 @@ __global__ __launch_bounds__(kThreads, (CausalShape<DK, DV>::kMinBlocks)) void f
             const int n = tid + kThreads * i, r = n / CK, cc = n % CK;
             // rows past the segment end and padded feature columns add nothing
             const bool okq = DKR == DK || 8 * cc < DKR, ok = okq && row0 + r < len;
-            Row<T, 8> qin, kin, qt, kt;
-            __builtin_memcpy(qin.e, &st.q[i], sizeof(qin));
-            __builtin_memcpy(kin.e, &st.k[i], sizeof(kin));
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                qt.e[e] = okq ? static_cast<T>(phi<FM, T>(to_f32(qin.e[e]))) : static_cast<T>(0.f);
-                // rows past the segment end must add nothing: mask after phi
-                kt.e[e] = ok ? static_cast<T>(phi<FM, T>(to_f32(kin.e[e]))) : static_cast<T>(0.f);
-            }
-            *reinterpret_cast<Row<T, 8>*>(&tQ[r * LDK + 8 * cc]) = qt;
-            *reinterpret_cast<Row<T, 8>*>(&tK[r * LDK + 8 * cc]) = kt;
+            // rows past the segment end must add nothing: mask after phi
+            *reinterpret_cast<u32x4*>(&tQ[r * LDK + 8 * cc]) = keep_or_zero(phi8<FM, T>(st.q[i]), okq);
+            *reinterpret_cast<u32x4*>(&tK[r * LDK + 8 * cc]) = keep_or_zero(phi8<FM, T>(st.k[i]), ok);
         }
 #pragma unroll
         for (int i = 0; i < NCV; ++i) {
@@ -2473,27 +2593,27 @@ __global__ __launch_bounds__(kThreads, (CausalShape<DK, DV>::kMinBlocks)) void f
         issue(st, c + 2);  // two chunks ahead; past the segment end these read zeros
         sched_fence();
 
-        // (a) a[t][s], t = 16 wave + 4 grp + r, s = 16 jb + m: blocks jb < wave
-        // are below the diagonal, jb = wave is masked, jb > wave stays zero
+        // (a) a[t][s], t = 16 wave + 4 grp + r, s = 16 jb + m. Slot i holds
+        // block jb = (wave - i) mod 4: slot 0 is the diagonal block (masked),
+        // slots 1 .. wave lie below it, and the slots past wave are the blocks
+        // above the diagonal, which stay zero. Only slot 0 needs a mask, with
+        // no test of the wave index per block.
         f32x4 aa[C / 16];
 #pragma unroll
-        for (int jb = 0; jb < C / 16; ++jb) aa[jb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int i = 0; i < C / 16; ++i) aa[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < KSK; ++ks) {
             const Frag<T> a = *reinterpret_cast<const Frag<T>*>(&tQ[(16 * wave + m) * LDK + 32 * ks + 8 * grp]);
 #pragma unroll
-            for (int jb = 0; jb < C / 16; ++jb) {
-                if (jb <= wave) {
-                    const Frag<T> b = *reinterpret_cast<const Frag<T>*>(&tK[(16 * jb + m) * LDK + 32 * ks + 8 * grp]);
-                    aa[jb] = mma(a, b, aa[jb]);
+            for (int i = 0; i < C / 16; ++i) {
+                if (i <= wave) {
+                    const Frag<T> b = *reinterpret_cast<const Frag<T>*>(&tK[(16 * (wave - i) + m) * LDK + 32 * ks + 8 * grp]);
+                    aa[i] = mma(a, b, aa[i]);
                 }
             }
         }
 #pragma unroll
-        for (int jb = 0; jb < C / 16; ++jb)
-            if (jb == wave)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) aa[jb][r] = m > 4 * grp + r ? 0.f : aa[jb][r];
+        for (int r = 0; r < 4; ++r) aa[0][r] = m > 4 * grp + r ? 0.f : aa[0][r];
         int sA = 0;
         if constexpr (Elt<T>::kScaled) {
             float amax = 0.f;
@@ -2507,7 +2627,8 @@ __global__ __launch_bounds__(kThreads, (CausalShape<DK, DV>::kMinBlocks)) void f
             const float fA = ldexpf(1.f, sA);
             // a^T: row s, columns t = 4 grp .. 4 grp + 3 of this wave
 #pragma unroll
-            for (int jb = 0; jb < C / 16; ++jb) put4t(&myW[(16 * jb + m) * LDW + 4 * grp], aa[jb], fA);
+            for (int i = 0; i < C / 16; ++i)
+                put4t(&myW[(16 * ((wave - i) & (C / 16 - 1)) + m) * LDW + 4 * grp], aa[i], fA);
         }
         wave_lds_sync();
 
@@ -2853,16 +2974,8 @@ __global__ __launch_bounds__(kThreads, (CausalBwdShape<DK, DV>::kMinBlocks)) voi
             const int n = tid + kThreads * i, r = n / CK, cc = n % CK;
             // rows past the segment end and padded feature columns add nothing
             const bool okq = DKR == DK || 8 * cc < DKR, ok = okq && row0 + r < len;
-            Row<T, 8> qin, kin, qt, kt;
-            __builtin_memcpy(qin.e, &st.q[i], sizeof(qin));
-            __builtin_memcpy(kin.e, &st.k[i], sizeof(kin));
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                qt.e[e] = okq ? static_cast<T>(phi<FM, T>(to_f32(qin.e[e]))) : static_cast<T>(0.f);
-                kt.e[e] = ok ? static_cast<T>(phi<FM, T>(to_f32(kin.e[e]))) : static_cast<T>(0.f);
-            }
-            *reinterpret_cast<Row<T, 8>*>(&tQ[r * LDK + 8 * cc]) = qt;
-            *reinterpret_cast<Row<T, 8>*>(&tK[r * LDK + 8 * cc]) = kt;
+            *reinterpret_cast<u32x4*>(&tQ[r * LDK + 8 * cc]) = keep_or_zero(phi8<FM, T>(st.q[i]), okq);
+            *reinterpret_cast<u32x4*>(&tK[r * LDK + 8 * cc]) = keep_or_zero(phi8<FM, T>(st.k[i]), ok);
         }
 #pragma unroll
         for (int i = 0; i < NCV; ++i) {
@@ -2897,30 +3010,30 @@ __global__ __launch_bounds__(kThreads, (CausalBwdShape<DK, DV>::kMinBlocks)) voi
 #pragma unroll
         for (int ks = 0; ks < KSV; ++ks)
             fd[ks] = *reinterpret_cast<const Frag<T>*>(&tD[(16 * wave + m) * LDV + 32 * ks + 8 * grp]);
+        // slot i holds block jb = wave - i (slot 0 is the diagonal block,
+        // the only one masked); slots past wave are above the diagonal and
+        // stay zero
 #pragma unroll
         for (int ks = 0; ks < KSK; ++ks) {
             const Frag<T> a = *reinterpret_cast<const Frag<T>*>(&tQ[(16 * wave + m) * LDK + 32 * ks + 8 * grp]);
 #pragma unroll
-            for (int jb = 0; jb < NBC; ++jb)
-                if (jb <= wave)
-                    aa[jb] = mma(a, *reinterpret_cast<const Frag<T>*>(&tK[(16 * jb + m) * LDK + 32 * ks + 8 * grp]),
-                                 aa[jb]);
+            for (int i = 0; i < NBC; ++i)
+                if (i <= wave)
+                    aa[i] = mma(a, *reinterpret_cast<const Frag<T>*>(&tK[(16 * (wave - i) + m) * LDK + 32 * ks + 8 * grp]),
+                                aa[i]);
         }
 #pragma unroll
         for (int ks = 0; ks < KSV; ++ks)
 #pragma unroll
-            for (int jb = 0; jb < NBC; ++jb)
-                if (jb <= wave)
-                    bb[jb] = mma(fd[ks], *reinterpret_cast<const Frag<T>*>(&tV[(16 * jb + m) * LDV + 32 * ks + 8 * grp]),
-                                 bb[jb]);
+            for (int i = 0; i < NBC; ++i)
+                if (i <= wave)
+                    bb[i] = mma(fd[ks], *reinterpret_cast<const Frag<T>*>(&tV[(16 * (wave - i) + m) * LDV + 32 * ks + 8 * grp]),
+                                bb[i]);
 #pragma unroll
-        for (int jb = 0; jb < NBC; ++jb)
-            if (jb == wave)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    aa[jb][r] = m > 4 * grp + r ? 0.f : aa[jb][r];
-                    bb[jb][r] = m > 4 * grp + r ? 0.f : bb[jb][r];
-                }
+        for (int r = 0; r < 4; ++r) {
+            aa[0][r] = m > 4 * grp + r ? 0.f : aa[0][r];
+            bb[0][r] = m > 4 * grp + r ? 0.f : bb[0][r];
+        }
 
         // (b) Y = dO R^T, unscaled per column block
         f32x4 Y[NBI];
@@ -2962,11 +3075,12 @@ __global__ __launch_bounds__(kThreads, (CausalBwdShape<DK, DV>::kMinBlocks)) voi
             for (int r = 0; r < 4; ++r) {
                 sa[r] = 0.f;
                 sb[r] = 0.f;
+                // blocks in ascending order: slots from the last down
 #pragma unroll
-                for (int jb = 0; jb < NBC; ++jb)
-                    if (jb <= wave) {
-                        sa[r] += aa[jb][r];
-                        sb[r] += aa[jb][r] * bb[jb][r];
+                for (int i = NBC - 1; i >= 0; --i)
+                    if (i <= wave) {
+                        sa[r] += aa[i][r];
+                        sb[r] += aa[i][r] * bb[i][r];
                     }
             }
 #pragma unroll
@@ -3001,14 +3115,14 @@ __global__ __launch_bounds__(kThreads, (CausalBwdShape<DK, DV>::kMinBlocks)) voi
         f32x4 pp[NBC];
         float pmx = 0.f;
 #pragma unroll
-        for (int jb = 0; jb < NBC; ++jb) {
-            pp[jb] = f32x4{0.f, 0.f, 0.f, 0.f};
-            if (jb <= wave) {  // blocks above the diagonal stay zero
+        for (int i = 0; i < NBC; ++i) {
+            pp[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (i <= wave) {  // blocks above the diagonal stay zero
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const float x = SIMPLE ? bb[jb][r] : wr[r] * bb[jb][r] + cr[r];
-                    pp[jb][r] = jb < wave || m <= 4 * grp + r ? x : 0.f;
-                    pmx = fmaxf(pmx, fabsf(pp[jb][r]));
+                    const float x = SIMPLE ? bb[i][r] : wr[r] * bb[i][r] + cr[r];
+                    pp[i][r] = i > 0 || m <= 4 * grp + r ? x : 0.f;
+                    pmx = fmaxf(pmx, fabsf(pp[i][r]));
                 }
             }
         }
@@ -3017,7 +3131,7 @@ __global__ __launch_bounds__(kThreads, (CausalBwdShape<DK, DV>::kMinBlocks)) voi
         {
             const float fP = ldexpf(1.f, sP);
 #pragma unroll
-            for (int jb = 0; jb < NBC; ++jb) put4t(&myW[(16 * jb + m) * LDW + 4 * grp], pp[jb], fP);
+            for (int i = 0; i < NBC; ++i) put4t(&myW[(16 * ((wave - i) & (NBC - 1)) + m) * LDW + 4 * grp], pp[i], fP);
         }
         wave_lds_sync();
         f32x4 pk[NBI];
@@ -3357,16 +3471,13 @@ __global__ __launch_bounds__(kThreads, (CausalBwdShape<DK, DV>::kMinBlocks)) voi
             float wt = qscale;  // simple_la: w is the query scale
             if constexpr (!SIMPLE) wt = __shfl(wl, r);
             const float f = ok ? wt * fQ : 0.f;
-            Row<T, 8> qin, kin, qt, kt;
-            __builtin_memcpy(qin.e, &st.q[i], sizeof(qin));
-            __builtin_memcpy(kin.e, &st.k[i], sizeof(kin));
+            float pq[8];
+            phi8_f32<FM, T>(st.q[i], pq);
+            Row<T, 8> qt;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                qt.e[e] = static_cast<T>(phi<FM, T>(to_f32(qin.e[e])) * f);
-                kt.e[e] = ok ? static_cast<T>(phi<FM, T>(to_f32(kin.e[e]))) : static_cast<T>(0.f);
-            }
+            for (int e = 0; e < 8; ++e) qt.e[e] = static_cast<T>(pq[e] * f);
             *reinterpret_cast<Row<T, 8>*>(&tQ[r * LDK + 8 * cc]) = qt;
-            *reinterpret_cast<Row<T, 8>*>(&tK[r * LDK + 8 * cc]) = kt;
+            *reinterpret_cast<u32x4*>(&tK[r * LDK + 8 * cc]) = keep_or_zero(phi8<FM, T>(st.k[i]), ok);
         }
 #pragma unroll
         for (int i = 0; i < NCV; ++i) {
@@ -3396,7 +3507,10 @@ __global__ __launch_bounds__(kThreads, (CausalBwdShape<DK, DV>::kMinBlocks)) voi
         sched_fence();
         const float uQ = ldexpf(1.f, -sQ);
 
-        // (a) a~[s][t], b[s][t]: s = ts + r, t = 16 jb + m, t >= s
+        // (a) a~[s][t], b[s][t]: s = ts + r, t = 16 jb + m, t >= s. Slot i
+        // holds block jb = (wave + i) mod 4: slot 0 is the diagonal block,
+        // the only one masked; slots with wave + i past the last block are
+        // below the diagonal and stay zero.
         f32x4 aa[NBC], bb[NBC];
 #pragma unroll
         for (int jb = 0; jb < NBC; ++jb) {
@@ -3413,29 +3527,29 @@ __global__ __launch_bounds__(kThreads, (CausalBwdShape<DK, DV>::kMinBlocks)) voi
 #pragma unroll
         for (int ks = 0; ks < KSK; ++ks)
 #pragma unroll
-            for (int jb = 0; jb < NBC; ++jb)
-                if (jb >= wave)
-                    aa[jb] = mma(fk[ks], *reinterpret_cast<const Frag<T>*>(&tQ[(16 * jb + m) * LDK + 32 * ks + 8 * grp]),
-                                 aa[jb]);
+            for (int i = 0; i < NBC; ++i)
+                if (wave + i < NBC)
+                    aa[i] = mma(fk[ks], *reinterpret_cast<const Frag<T>*>(&tQ[(16 * (wave + i) + m) * LDK + 32 * ks + 8 * grp]),
+                                aa[i]);
 #pragma unroll
         for (int ks = 0; ks < KSV; ++ks)
 #pragma unroll
-            for (int jb = 0; jb < NBC; ++jb)
-                if (jb >= wave)
-                    bb[jb] = mma(fv[ks], *reinterpret_cast<const Frag<T>*>(&tD[(16 * jb + m) * LDV + 32 * ks + 8 * grp]),
-                                 bb[jb]);
+            for (int i = 0; i < NBC; ++i)
+                if (wave + i < NBC)
+                    bb[i] = mma(fv[ks], *reinterpret_cast<const Frag<T>*>(&tD[(16 * (wave + i) + m) * LDV + 32 * ks + 8 * grp]),
+                                bb[i]);
         float pmx = 0.f, amx = 0.f;
 #pragma unroll
-        for (int jb = 0; jb < NBC; ++jb) {
-            if (jb < wave) continue;  // below the diagonal: a~ and b were never computed, stay zero
-            const float ch = SIMPLE ? 0.f : sC[16 * jb + m];
+        for (int i = 0; i < NBC; ++i) {
+            if (wave + i >= NBC) continue;  // below the diagonal: a~ and b were never computed, stay zero
+            const float ch = SIMPLE ? 0.f : sC[16 * (wave + i) + m];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const bool keep = jb > wave || m >= 4 * grp + r;
-                aa[jb][r] = keep ? aa[jb][r] : 0.f;
-                bb[jb][r] = keep ? bb[jb][r] + ch : 0.f;  // now mask(b + c^)
-                pmx = fmaxf(pmx, fabsf(bb[jb][r]));
-                amx = fmaxf(amx, fabsf(aa[jb][r]));
+                const bool keep = i > 0 || m >= 4 * grp + r;
+                aa[i][r] = keep ? aa[i][r] : 0.f;
+                bb[i][r] = keep ? bb[i][r] + ch : 0.f;  // now mask(b + c^)
+                pmx = fmaxf(pmx, fabsf(bb[i][r]));
+                amx = fmaxf(amx, fabsf(aa[i][r]));
             }
         }
         // phi(k) at the result positions
@@ -3451,7 +3565,7 @@ __global__ __launch_bounds__(kThreads, (CausalBwdShape<DK, DV>::kMinBlocks)) voi
             if constexpr (Elt<T>::kScaled) sP = scale_exp(wave_max_nonneg(pmx));
             const float fP = ldexpf(1.f, sP);
 #pragma unroll
-            for (int jb = 0; jb < NBC; ++jb) put4t(&myW[(16 * jb + m) * LDW + 4 * grp], bb[jb], fP);
+            for (int i = 0; i < NBC; ++i) put4t(&myW[(16 * ((wave + i) & (NBC - 1)) + m) * LDW + 4 * grp], bb[i], fP);
             wave_lds_sync();
             f32x4 x1[NBI], x2[NBI];
 #pragma unroll
@@ -3510,7 +3624,7 @@ __global__ __launch_bounds__(kThreads, (CausalBwdShape<DK, DV>::kMinBlocks)) voi
             if constexpr (Elt<T>::kScaled) sA = scale_exp(wave_max_nonneg(amx));
             const float fA = ldexpf(1.f, sA);
 #pragma unroll
-            for (int jb = 0; jb < NBC; ++jb) put4t(&myW[(16 * jb + m) * LDW + 4 * grp], aa[jb], fA);
+            for (int i = 0; i < NBC; ++i) put4t(&myW[(16 * ((wave + i) & (NBC - 1)) + m) * LDW + 4 * grp], aa[i], fA);
             wave_lds_sync();
             f32x4 y1[NBV], y2[NBV];
 #pragma unroll
