@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define LA_VERSION 8
+#define LA_VERSION 9
 
 typedef enum {
     LA_F32 = 0,
@@ -113,6 +113,19 @@ typedef enum {
  * LA_ERR_FLAGS with it. la_workspace_bytes counts the causal backward's
  * scratch when the flag is set. */
 #define LA_CAUSAL 0x10u
+/* With LA_CAUSAL, in la_bwd: `ws` already holds the causal segment prefixes
+ * (the exclusive prefix sums of S and z over the segments) that a la_fwd
+ * call wrote into it for the same problem (every other field and flag equal)
+ * and the same K and V, and nothing has written to `ws` since. la_bwd then
+ * reads them from there instead of recomputing them, skipping one pass over
+ * K and V (the state reduction and prefix kernels). The workspace works like
+ * a reserve space that the forward fills for the backward. The library cannot
+ * check the contract: a workspace that does not hold those prefixes gives
+ * wrong gradients without an error. la_fwd ignores the bit (it always leaves
+ * the prefixes in `ws`), so one problem serves both calls. Without LA_CAUSAL,
+ * in la_fwd_noalloc (whose prefixes stay in its own scratch) and in the step
+ * calls: LA_ERR_FLAGS. */
+#define LA_REUSE_PREFIX 0x20u
 
 /* Strides of one tensor, in elements: element f of token t of head h of
  * batch b sits at base + b*batch + h*head + t*token + f (the D or Dv features
@@ -219,7 +232,8 @@ int la_fwd(const la_problem* p, const void* q, const void* k, const void* v,
  * la_bwd_dkv. With LA_CAUSAL: the vector-Jacobian product of sum(O * dO)
  * through the recurrent form (eps held constant); `state` is not read and may
  * be NULL. The segment states and their exclusive prefixes are recomputed
- * from K, V, a forward-order chunked scan per segment writes dQ and keeps
+ * from K, V (or, with LA_REUSE_PREFIX, read from the workspace the forward
+ * left them in), a forward-order chunked scan per segment writes dQ and keeps
  * 1/den and c per token in the workspace, exclusive suffixes of its
  * per-segment sums follow, and a reverse-order scan writes dK and dV. */
 int la_bwd(const la_problem* p, const void* q, const void* k, const void* v,

@@ -21,7 +21,7 @@ __all__ = [
     "LAError", "lib", "fwd", "bwd", "fwd_noalloc", "NOALLOC_SCRATCH_BYTES", "Strides", "TensorStrides", "fwd_state", "fwd_output", "bwd_dq", "bwd_dkv", "linear_attention",
     "state_bytes", "workspace_bytes", "split_of", "Split", "new_state", "workspace", "Problem",
     "LA_F32", "LA_F16", "LA_BF16", "LA_SIMPLE", "LA_LAYOUT_BTHD", "LA_PHI_RELU", "LA_PHI_IDENTITY", "LA_CAUSAL",
-    "EXPORTS",
+    "LA_REUSE_PREFIX", "EXPORTS",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libla.so")
@@ -31,6 +31,7 @@ LA_SIMPLE = 0x1
 LA_LAYOUT_BTHD = 0x2
 LA_PHI_RELU, LA_PHI_IDENTITY = 0x4, 0x8
 LA_CAUSAL = 0x10
+LA_REUSE_PREFIX = 0x20
 LAYOUTS = ("bhtd", "bthd")
 FEATURE_MAPS = {"elu1": 0, "relu": LA_PHI_RELU, "identity": LA_PHI_IDENTITY}
 DTYPE_CODE = {torch.float32: LA_F32, torch.float16: LA_F16, torch.bfloat16: LA_BF16}
@@ -360,16 +361,21 @@ def bwd_dkv(k, v, *, eps=1e-6, simple=False, layout="bhtd", phi="elu1", dk=None,
 
 
 def bwd(q, k, v, do, state=None, *, eps=1e-6, simple=False, layout="bhtd", phi="elu1", dq=None, dk=None, dv=None,
-        ws=None, causal=False, scale=None):
+        ws=None, causal=False, scale=None, reuse_prefix=False):
     """dQ, dK, dV of L = sum(O * dO), from the state fwd returned.
     causal=True: the backward of the causal form (D and Dv up to 128); no
-    state is read (pass None)."""
+    state is read (pass None). reuse_prefix=True (causal only): ``ws`` still
+    holds the segment prefixes the causal fwd on the same problem and K, V
+    wrote into it, and the backward reads them instead of recomputing them
+    (LA_REUSE_PREFIX; the library cannot check this)."""
     _tensor(q, None, "q")
     _tensor(k, q, "k")
     hv = v.shape[-1] if isinstance(v, torch.Tensor) else None
     _tensor(v, q, "v", hv)
     _tensor(do, q, "do", hv)
     prob = make_problem(q.shape, q.dtype, eps, simple, layout, phi, hv, causal, scale)
+    if reuse_prefix:
+        prob.flags |= LA_REUSE_PREFIX
     if not causal or state is not None:
         _state(state, prob, q.device)
     dq = _new_like(q, q.shape[-1]) if dq is None else _tensor(dq, q, "dq")
@@ -385,16 +391,25 @@ def bwd(q, k, v, do, state=None, *, eps=1e-6, simple=False, layout="bhtd", phi="
 class _LinearAttention(torch.autograd.Function):
     """Autograd node over la_fwd / la_bwd. The forward keeps the fp32 state
     (S, z) for the backward, which therefore reads Q, K, V, dO and the state
-    and does not recompute S."""
+    and does not recompute S. The causal forward runs in a workspace of its
+    own, kept for the backward, which reads the segment prefixes from it
+    (LA_REUSE_PREFIX) instead of recomputing them; nothing else writes to it
+    in between."""
 
     @staticmethod
     def forward(ctx, q, k, v, eps, simple, layout, phi, causal, scale):
-        o, state = fwd(q, k, v, eps=eps, simple=simple, layout=layout, phi=phi, causal=causal, scale=scale)
+        ws = None
+        if causal:
+            dv = v.shape[-1] if isinstance(v, torch.Tensor) else None
+            prob = make_problem(q.shape, q.dtype, eps, simple, layout, phi, dv, causal, scale)
+            ws = torch.empty(max(workspace_bytes(prob), 256), dtype=torch.uint8, device=q.device)
+        o, state = fwd(q, k, v, eps=eps, simple=simple, layout=layout, phi=phi, causal=causal, scale=scale, ws=ws)
         if causal:
             state = None  # the causal backward does not read it
             ctx.save_for_backward(q, k, v)
         else:
             ctx.save_for_backward(q, k, v, state)
+        ctx.ws = ws
         ctx.eps, ctx.simple, ctx.layout, ctx.phi, ctx.causal, ctx.scale = eps, simple, layout, phi, causal, scale
         return o
 
@@ -406,7 +421,8 @@ class _LinearAttention(torch.autograd.Function):
         if do.shape[-1] > 1 and do.stride(-1) != 1:
             do = do.contiguous()
         dq, dk, dv = bwd(q, k, v, do, state, eps=ctx.eps, simple=ctx.simple, layout=ctx.layout,
-                         phi=ctx.phi, causal=ctx.causal, scale=ctx.scale)
+                         phi=ctx.phi, causal=ctx.causal, scale=ctx.scale, ws=ctx.ws,
+                         reuse_prefix=ctx.causal)
         return dq, dk, dv, None, None, None, None, None, None
 
 

@@ -68,7 +68,10 @@ la_status check_problem(const la_problem* p) {
     }
     if (p->B < 0 || p->H < 0 || p->T < 0) return LA_ERR_SHAPE;
     if (p->B > kMaxHeads || p->H > kMaxHeads || p->B * p->H > kMaxHeads) return LA_ERR_SHAPE;
-    if (p->flags & ~(LA_SIMPLE | LA_LAYOUT_BTHD | LA_PHI_RELU | LA_PHI_IDENTITY | LA_CAUSAL)) return LA_ERR_FLAGS;
+    if (p->flags & ~(LA_SIMPLE | LA_LAYOUT_BTHD | LA_PHI_RELU | LA_PHI_IDENTITY | LA_CAUSAL | LA_REUSE_PREFIX))
+        return LA_ERR_FLAGS;
+    // the prefixes to reuse are those of the causal form
+    if ((p->flags & LA_REUSE_PREFIX) && !(p->flags & LA_CAUSAL)) return LA_ERR_FLAGS;
     if ((p->flags & LA_PHI_RELU) && (p->flags & LA_PHI_IDENTITY)) return LA_ERR_FLAGS;
     if (p->strides && (p->flags & LA_LAYOUT_BTHD)) return LA_ERR_FLAGS;
     if (p->T > kMaxTokens) return LA_ERR_SHAPE;
@@ -215,6 +218,7 @@ la::Plan make_plan(const la_problem* p) {
     const float qscale = p->scale == 0.f ? 1.f : p->scale;
     pl.eps = pl.simple ? qscale : p->eps / qscale;
     pl.fm = (p->flags & LA_PHI_RELU) ? 1 : (p->flags & LA_PHI_IDENTITY) ? 2 : 0;
+    pl.reuse_prefix = (p->flags & LA_REUSE_PREFIX) != 0;
     pl.lay.q = layout_of(p, kQ);
     pl.lay.k = layout_of(p, kK);
     pl.lay.v = layout_of(p, kV);
@@ -394,6 +398,8 @@ int la_fwd_noalloc(const la_problem* p, const void* q, const void* k, const void
     static_assert(LA_NOALLOC_SCRATCH_BYTES == la::kScratchBytes, "scratch size in la.h and the library differ");
     la_status st = check_problem(p);
     if (st != LA_OK) return st;
+    // its prefixes stay in the library's scratch, where no la_bwd can find them
+    if (p->flags & LA_REUSE_PREFIX) return LA_ERR_FLAGS;
     const bool causal = (p->flags & LA_CAUSAL) != 0;
     if (causal && (st = check_causal(p)) != LA_OK) return st;
     const la::Plan pl = make_plan(p);

@@ -35,6 +35,8 @@ struct Plan {
     // Either way the kernels' one float folds the optional query scale.
     float eps = 0.f;
     int fm = 0;  // feature map: 0 elu + 1, 1 relu, 2 identity
+    // causal backward: the segment prefixes are already in the workspace
+    bool reuse_prefix = false;
     Layouts lay;
     // state reduction (fwd steps 1-3): P slices of L tokens per head
     int P = 1;

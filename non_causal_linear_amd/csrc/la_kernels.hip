@@ -5174,8 +5174,9 @@ hipError_t fwd_causal_fm(const Plan& p, const void* q, const void* k, const void
 }
 
 // Causal backward: segment states and their exclusive prefixes (as in the
-// causal forward), the forward-order dQ scan, the exclusive suffixes of its
-// per-segment (G, g) sums, then the reverse-order dK, dV scan.
+// causal forward; with reuse_prefix they are already in the workspace, where
+// the forward left them), the forward-order dQ scan, the exclusive suffixes
+// of its per-segment (G, g) sums, then the reverse-order dK, dV scan.
 template <typename T, int DK, int DV, int FM>
 hipError_t bwd_causal_fm(const Plan& p, const void* q, const void* k, const void* v, const void* dout, void* dq,
                          void* dk, void* dv, void* ws, hipStream_t s) {
@@ -5188,7 +5189,7 @@ hipError_t bwd_causal_fm(const Plan& p, const void* q, const void* k, const void
     constexpr int E4 = (DK * DV + DK) / 4;
     const int64_t nred = p.BH * ((E4 + kThreads - 1) / kThreads);
     hipError_t e;
-    if (p.P > 1) {
+    if (p.P > 1 && !p.reuse_prefix) {
         e = launch_state_reduction<T, DK, DV, FM>(p, k, v, total, part, s);
         if (e != hipSuccess) return e;
         e = launch(prefix_kernel<DK, DV>, nred, kThreads, s, part, p.P, total, total + p.BH * DK * DV, p.BH);

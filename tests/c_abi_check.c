@@ -57,6 +57,14 @@ int main(void) {
     p.D = 256;
     p.dtype = LA_F16;
     CHECK(la_bwd(&p, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, 0, NULL) == LA_ERR_HEAD_DIM);
+    p.D = 64;
+    /* reusing the forward's prefixes: causal la_fwd / la_bwd only */
+    p.flags = LA_CAUSAL | LA_REUSE_PREFIX;
+    CHECK(la_bwd(&p, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, 0, NULL) == LA_ERR_WORKSPACE);
+    CHECK(la_fwd(&p, NULL, NULL, NULL, NULL, NULL, NULL, 0, NULL) == LA_ERR_WORKSPACE);
+    CHECK(la_fwd_noalloc(&p, NULL, NULL, NULL, NULL, NULL, NULL) == LA_ERR_FLAGS);
+    p.flags = LA_REUSE_PREFIX;
+    CHECK(la_bwd(&p, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, 0, NULL) == LA_ERR_FLAGS);
 
     if (fails == 0) printf("c abi ok\n");
     return fails == 0 ? 0 : 1;

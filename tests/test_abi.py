@@ -48,7 +48,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.la_version() == 8
+    assert L.la_version() == 9
     for s in range(14):
         txt = L.la_status_str(s).decode()
         assert txt.startswith("LA_"), txt
@@ -172,7 +172,7 @@ def test_fwd_rejects_bad_problems(L):
     assert fwd_call(L, prob(T=(1 << 31) // (128 * 2), D=32, Dv=128)) == SHAPE
     assert fwd_call(L, prob(T=(1 << 31) // (128 * 2), D=128, Dv=32)) == SHAPE
     assert L.la_workspace_bytes(ctypes.byref(prob(T=(1 << 31) // (128 * 2) - 1, D=32, Dv=128))) > 0
-    assert fwd_call(L, prob(flags=0x20)) == FLAGS
+    assert fwd_call(L, prob(flags=0x40)) == FLAGS
     assert fwd_call(L, prob(flags=0x80000000)) == FLAGS
     assert fwd_call(L, prob(flags=0x4 | 0x8)) == FLAGS  # two feature maps
     assert fwd_call(L, prob(eps=-1e-3)) == EPS
@@ -273,7 +273,7 @@ def test_step_calls_validate(L):
     assert L.la_fwd_state(ctypes.byref(p), d[0], d[1], d[2], d[3], need - 1, None) == WORKSPACE
     assert L.la_fwd_state(ctypes.byref(p), d[0], d[1], d[0], d[3], need, None) == ALIAS
     assert L.la_fwd_output(ctypes.byref(p), d[0], d[1], d[0], None) == ALIAS
-    assert L.la_fwd_output(ctypes.byref(prob(flags=0x20)), d[0], d[1], d[2], None) == FLAGS
+    assert L.la_fwd_output(ctypes.byref(prob(flags=0x40)), d[0], d[1], d[2], None) == FLAGS
     assert L.la_bwd_dq(ctypes.byref(p), d[0], d[1], z, d[3], d[4], need, None) == NULL
     assert L.la_bwd_dq(ctypes.byref(p), d[0], d[1], d[2], d[1], d[4], need, None) == ALIAS
     assert L.la_bwd_dkv(ctypes.byref(p), d[0], d[1], d[2], d[2], d[4], need, None) == ALIAS
@@ -360,7 +360,34 @@ def test_causal_flag_accepted_by_la_fwd_and_la_bwd_only(L):
     assert L.la_bwd_dkv(ctypes.byref(p), d[0], d[1], d[2], d[3], d[4], need, None) == FLAGS
     # an accepted causal call with an argument error still reports that error
     assert fwd_call(L, p, ws_bytes=need - 1) == WORKSPACE
-    assert fwd_call(L, prob(flags=CAUSAL | 0x20)) == FLAGS
+    assert fwd_call(L, prob(flags=CAUSAL | 0x40)) == FLAGS
+
+
+def test_reuse_prefix_flag(L):
+    """LA_REUSE_PREFIX: accepted with LA_CAUSAL by la_fwd (which ignores it)
+    and la_bwd, with the same workspace size and split as without it;
+    refused without LA_CAUSAL, by la_fwd_noalloc and by the step calls.
+    Every call here ends in an argument error."""
+    CAUSAL, REUSE = 0x10, 0x20
+    assert la.LA_REUSE_PREFIX == REUSE
+    d = addrs(9)
+    for dt, dd, dv in ((1, 64, 0), (2, 128, 0), (0, 64, 0), (1, 32, 96)):
+        pc, pr = prob(flags=CAUSAL, D=dd, Dv=dv, dtype=dt), prob(flags=CAUSAL | REUSE, D=dd, Dv=dv, dtype=dt)
+        n = L.la_workspace_bytes(ctypes.byref(pc))
+        assert L.la_workspace_bytes(ctypes.byref(pr)) == n > 0
+        assert la.split_of(pr) == la.split_of(pc)
+        assert fwd_call(L, pr, ws_bytes=n - 1) == WORKSPACE
+        assert L.la_bwd(ctypes.byref(pr), *d[:4], None, *d[5:9], n - 1, None) == WORKSPACE
+        assert L.la_fwd_noalloc(ctypes.byref(pr), *d[:5], None) == FLAGS
+    pr = prob(flags=CAUSAL | REUSE)
+    need = L.la_workspace_bytes(ctypes.byref(pr))
+    assert L.la_fwd_state(ctypes.byref(pr), d[0], d[1], d[2], d[3], need, None) == FLAGS
+    assert L.la_bwd_dq(ctypes.byref(pr), d[0], d[1], d[2], d[3], d[4], need, None) == FLAGS
+    p = prob(flags=REUSE)
+    assert L.la_workspace_bytes(ctypes.byref(p)) == 0
+    assert fwd_call(L, p) == FLAGS
+    assert L.la_bwd(ctypes.byref(p), *d[:9], need, None) == FLAGS
+    assert L.la_fwd_noalloc(ctypes.byref(p), *d[:5], None) == FLAGS
 
 
 def test_fwd_noalloc_validates_before_any_hip_call(L):
