@@ -28,14 +28,21 @@ def eager(dev, w, causal=False):
     return {"o": o, "state": st, "dq": dq, "dk": dk, "dv": dv}
 
 
-@pytest.mark.parametrize("D,Dv,dtype,simple,causal", [(64, 64, "f16", False, False), (128, 128, "bf16", False, False),
-                                                       (96, 32, "f16", True, False), (64, 64, "f16", False, True),
-                                                       (128, 64, "bf16", True, True)],
+@pytest.mark.parametrize("D,Dv,dtype,simple,causal,reuse", [(64, 64, "f16", False, False, False),
+                                                             (128, 128, "bf16", False, False, False),
+                                                             (96, 32, "f16", True, False, False),
+                                                             (64, 64, "f16", False, True, False),
+                                                             (128, 64, "bf16", True, True, False),
+                                                             (64, 64, "f16", False, True, True)],
                          ids=["D64-f16", "D128-bf16", "D96-Dv32-f16-simple", "causal-D64-f16",
-                              "causal-D128-Dv64-bf16-simple"])
-def test_graph_replays_match_eager(D, Dv, dtype, simple, causal):
+                              "causal-D128-Dv64-bf16-simple", "causal-D64-f16-reuse-prefix"])
+def test_graph_replays_match_eager(D, Dv, dtype, simple, causal, reuse):
+    """reuse: the captured backward reads the segment prefixes the captured
+    forward left in the workspace (LA_REUSE_PREFIX); the workspace is
+    overwritten between replays, so each replay's forward must refill them."""
     w = Workload("graph", 2, 4, 3000, D, dtype, simple=simple, seed=70_000 + D + Dv, Dv=Dv)
-    print(f"case graph D={D} Dv={Dv} {dtype} simple={simple} causal={causal} seed={w.seed}", flush=True)
+    print(f"case graph D={D} Dv={Dv} {dtype} simple={simple} causal={causal} reuse={reuse} seed={w.seed}",
+          flush=True)
     x = make_inputs(w)
     dev = {n: to_device(a, w.dtype) for n, a in x.items()}
     ref = eager(dev, w, causal)
@@ -49,7 +56,7 @@ def test_graph_replays_match_eager(D, Dv, dtype, simple, causal):
     def calls():
         la.fwd(q, k, v, eps=w.eps, simple=simple, out=out["o"], state=out["state"], ws=ws, causal=causal)
         la.bwd(q, k, v, do, None if causal else out["state"], eps=w.eps, simple=simple, dq=out["dq"], dk=out["dk"],
-               dv=out["dv"], ws=ws, causal=causal)
+               dv=out["dv"], ws=ws, causal=causal, reuse_prefix=reuse)
 
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
