@@ -420,6 +420,17 @@ __device__ __forceinline__ void buf_store16(const HeadBuf& b, int byte_off, uint
     __builtin_amdgcn_raw_buffer_store_b128(v, b.rsrc, byte_off, 0, CP);
 }
 
+// Four fp32 values rounded to the 16-bit element type, as one 8-byte store.
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+template <typename T>
+__device__ __forceinline__ void buf_store4(const HeadBuf& b, int byte_off, f32x4 x) {
+    typedef T t4 __attribute__((ext_vector_type(4)));
+    t4 y;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) y[r] = static_cast<T>(x[r]);
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, y), b.rsrc, byte_off, 0, 0);
+}
+
 // N contiguous elements of row `row` (rows rs elements apart) starting at
 // element `col`, by buffer loads.
 template <typename T, int N>
@@ -2431,8 +2442,6 @@ struct CausalShape {
     static constexpr int kLDK = DK + 16;              // tQ, tK row stride (elements)
     static constexpr int kLDV = DV + 16;              // tV row stride
     static constexpr int kLDRT = DK + 8;              // R^T row stride (rows j, DK entries)
-    static constexpr int kLDW = 24;                   // per-wave a^T / O^T tiles: rows of 16 tokens
-    static constexpr int kWRows = kChunk > DV ? kChunk : DV;  // rows of the per-wave tile
     static constexpr int kMinBlocks = (DK == 64 && DV == 64) ? 2 : 1;
 };
 
@@ -2453,7 +2462,7 @@ __global__ __launch_bounds__(kThreads, (CausalShape<DK, DV>::kMinBlocks)) void f
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const float* __restrict__ pre,
     T* __restrict__ o, int64_t T_, const Layouts lay, int P, int64_t L, float eps) {
     using Sh = CausalShape<DK, DV>;
-    constexpr int C = Sh::kChunk, LDK = Sh::kLDK, LDV = Sh::kLDV, LDRT = Sh::kLDRT, LDW = Sh::kLDW;
+    constexpr int C = Sh::kChunk, LDK = Sh::kLDK, LDV = Sh::kLDV, LDRT = Sh::kLDRT;
     constexpr int NBV = DV / 16;         // output column blocks
     constexpr int RJ = DV / 64;          // R column blocks per wave (a quarter of DV)
     constexpr int RI = DK / 16;          // R row blocks
@@ -2468,7 +2477,6 @@ __global__ __launch_bounds__(kThreads, (CausalShape<DK, DV>::kMinBlocks)) void f
     __shared__ __attribute__((aligned(16))) T tV[C * LDV];
     __shared__ __attribute__((aligned(16))) T tRT[2][DV * LDRT];
     __shared__ __attribute__((aligned(16))) T tZ[2][DK];
-    __shared__ __attribute__((aligned(16))) T tW[kWaves][Sh::kWRows * LDW];
     __shared__ int sExp[2][kWaves + 1];  // exponents of the R quarters, then of z
 
     const int wid = xcd_remap(blockIdx.x, gridDim.x);
@@ -2583,7 +2591,6 @@ __global__ __launch_bounds__(kThreads, (CausalShape<DK, DV>::kMinBlocks)) void f
     };
 
     const int rA = 8 * grp + (m >> 2), cA = 4 * (m & 3);
-    T* myW = tW[wave];
     auto body = [&](Stage& st, int c) {
         const int cur = c & 1;
         const int64_t row0 = (int64_t)c * C;
@@ -2593,107 +2600,109 @@ __global__ __launch_bounds__(kThreads, (CausalShape<DK, DV>::kMinBlocks)) void f
         issue(st, c + 2);  // two chunks ahead; past the segment end these read zeros
         sched_fence();
 
-        // (a) a[t][s], t = 16 wave + 4 grp + r, s = 16 jb + m. Slot i holds
-        // block jb = (wave - i) mod 4: slot 0 is the diagonal block (masked),
-        // slots 1 .. wave lie below it, and the slots past wave are the blocks
-        // above the diagonal, which stay zero. Only slot 0 needs a mask, with
-        // no test of the wave index per block.
+        // (a) a^T[s][t] = phi(k_s) . phi(q_t) for the wave's query rows
+        // t = 16 wave + m (one per lane) and the keys s = 16 sb + 4 grp + r of
+        // block sb (the lane's four values). This result layout, with s along
+        // a lane's values, is already the operand layout of the contraction
+        // over s in (b), so a stays in registers. Slot i holds key block
+        // sb = (wave - i) mod 4: slot 0 is the diagonal block (masked to
+        // s <= t), slots 1 .. wave lie below it, and the slots past wave are
+        // the blocks above the diagonal, which stay zero.
         f32x4 aa[C / 16];
 #pragma unroll
         for (int i = 0; i < C / 16; ++i) aa[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < KSK; ++ks) {
-            const Frag<T> a = *reinterpret_cast<const Frag<T>*>(&tQ[(16 * wave + m) * LDK + 32 * ks + 8 * grp]);
+            const Frag<T> bq = *reinterpret_cast<const Frag<T>*>(&tQ[(16 * wave + m) * LDK + 32 * ks + 8 * grp]);
 #pragma unroll
             for (int i = 0; i < C / 16; ++i) {
                 if (i <= wave) {
-                    const Frag<T> b = *reinterpret_cast<const Frag<T>*>(&tK[(16 * (wave - i) + m) * LDK + 32 * ks + 8 * grp]);
-                    aa[i] = mma(a, b, aa[i]);
+                    const Frag<T> ak = *reinterpret_cast<const Frag<T>*>(&tK[(16 * (wave - i) + m) * LDK + 32 * ks + 8 * grp]);
+                    aa[i] = mma(ak, bq, aa[i]);
                 }
             }
         }
 #pragma unroll
-        for (int r = 0; r < 4; ++r) aa[0][r] = m > 4 * grp + r ? 0.f : aa[0][r];
+        for (int r = 0; r < 4; ++r) aa[0][r] = 4 * grp + r > m ? 0.f : aa[0][r];
         int sA = 0;
         if constexpr (Elt<T>::kScaled) {
             float amax = 0.f;
 #pragma unroll
-            for (int jb = 0; jb < C / 16; ++jb)
+            for (int i = 0; i < C / 16; ++i)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) amax = fmaxf(amax, fabsf(aa[jb][r]));
+                for (int r = 0; r < 4; ++r) amax = fmaxf(amax, fabsf(aa[i][r]));
             sA = scale_exp(wave_max_nonneg(amax));
         }
+        // operands over the keys of slots 2 ks and 2 ks + 1: values 0..3 of a
+        // lane are the keys 16 sb + 4 grp + (0..3) of the first slot's block,
+        // values 4..7 those of the second
+        Frag<T> bA[KSC];
         {
             const float fA = ldexpf(1.f, sA);
-            // a^T: row s, columns t = 4 grp .. 4 grp + 3 of this wave
 #pragma unroll
-            for (int i = 0; i < C / 16; ++i)
-                put4t(&myW[(16 * ((wave - i) & (C / 16 - 1)) + m) * LDW + 4 * grp], aa[i], fA);
+            for (int ks = 0; ks < KSC; ++ks)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    bA[ks][r] = static_cast<T>(aa[2 * ks][r] * fA);
+                    bA[ks][4 + r] = static_cast<T>(aa[2 * ks + 1][r] * fA);
+                }
         }
-        wave_lds_sync();
 
-        // (b) num = a [V | 1] + phi(Q) [R | z]
+        // (b) O^T = [V | 1]^T a^T + [R | z]^T phi(Q)^T, column t = 16 wave + m;
+        // the denominator parts land in every row of dA and dR. The V^T
+        // operand is read transposed with the key order of bA.
         f32x4 nA[NBV], nR[NBV], dA = f32x4{0.f, 0.f, 0.f, 0.f}, dR = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int jb = 0; jb < NBV; ++jb) {
             nA[jb] = f32x4{0.f, 0.f, 0.f, 0.f};
             nR[jb] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
+        const int rT = 4 * grp + (m >> 2), cT = 4 * (m & 3);
 #pragma unroll
         for (int ks = 0; ks < KSC; ++ks) {
-            const int rb = 32 * ks + rA;
-            const Frag<T> a = join_frag<T>(lds_read_tr(&myW[rb * LDW + cA]), lds_read_tr(&myW[(rb + 4) * LDW + cA]));
+            if (2 * ks <= wave) {  // otherwise both slots lie above the diagonal
+                const int r0 = 16 * ((wave - 2 * ks) & (C / 16 - 1)) + rT;
+                const int r1 = 16 * ((wave - 2 * ks - 1) & (C / 16 - 1)) + rT;
 #pragma unroll
-            for (int jb = 0; jb < NBV; ++jb) {
-                const Frag<T> b = join_frag<T>(lds_read_tr(&tV[rb * LDV + 16 * jb + cA]),
-                                               lds_read_tr(&tV[(rb + 4) * LDV + 16 * jb + cA]));
-                nA[jb] = mma(a, b, nA[jb]);
+                for (int jb = 0; jb < NBV; ++jb) {
+                    const Frag<T> av = join_frag<T>(lds_read_tr(&tV[r0 * LDV + 16 * jb + cT]),
+                                                    lds_read_tr(&tV[r1 * LDV + 16 * jb + cT]));
+                    nA[jb] = mma(av, bA[ks], nA[jb]);
+                }
+                if constexpr (!SIMPLE) dA = mma(ones, bA[ks], dA);
             }
-            if constexpr (!SIMPLE) dA = mma(a, ones, dA);
         }
 #pragma unroll
         for (int ks = 0; ks < KSK; ++ks) {
-            const Frag<T> a = *reinterpret_cast<const Frag<T>*>(&tQ[(16 * wave + m) * LDK + 32 * ks + 8 * grp]);
+            const Frag<T> bq = *reinterpret_cast<const Frag<T>*>(&tQ[(16 * wave + m) * LDK + 32 * ks + 8 * grp]);
 #pragma unroll
             for (int jb = 0; jb < NBV; ++jb) {
-                const Frag<T> b = *reinterpret_cast<const Frag<T>*>(&tRT[cur][(16 * jb + m) * LDRT + 32 * ks + 8 * grp]);
-                nR[jb] = mma(a, b, nR[jb]);
+                const Frag<T> ar = *reinterpret_cast<const Frag<T>*>(&tRT[cur][(16 * jb + m) * LDRT + 32 * ks + 8 * grp]);
+                nR[jb] = mma(ar, bq, nR[jb]);
             }
             if constexpr (!SIMPLE) {
-                const Frag<T> zb = *reinterpret_cast<const Frag<T>*>(&tZ[cur][32 * ks + 8 * grp]);
-                dR = mma(a, zb, dR);
+                const Frag<T> az = *reinterpret_cast<const Frag<T>*>(&tZ[cur][32 * ks + 8 * grp]);
+                dR = mma(az, bq, dR);
             }
         }
         {
+            // one query row per lane: one reciprocal, and O row t's features
+            // 16 jb + 4 grp .. + 3 as one 8-byte store per block
             const float uA = ldexpf(1.f, -sA);
-            f32x4 ia, ir;  // per row: factors on the a part and (times 2^-sR) on the R part
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                float inv = eps;  // simple_la: eps carries the query scale
-                if constexpr (!SIMPLE) inv = __builtin_amdgcn_rcpf(dA[r] * uA + dR[r] * ldexpf(1.f, -sExp[cur][kWaves]) + eps);
-                ia[r] = uA * inv;
-                ir[r] = inv;
-            }
-            wave_lds_sync();
+            float inv = eps;  // simple_la: eps carries the query scale
+            if constexpr (!SIMPLE) inv = __builtin_amdgcn_rcpf(dA[0] * uA + dR[0] * ldexpf(1.f, -sExp[cur][kWaves]) + eps);
+            const float ia = uA * inv;
+            const int64_t row = row0 + 16 * wave + m;
 #pragma unroll
             for (int jb = 0; jb < NBV; ++jb) {
-                const float uR = ldexpf(1.f, -sExp[cur][jb / RJ]);
+                const float ir = ldexpf(1.f, -sExp[cur][jb / RJ]) * inv;
                 f32x4 y;
 #pragma unroll
-                for (int r = 0; r < 4; ++r) y[r] = nA[jb][r] * ia[r] + nR[jb][r] * (uR * ir[r]);
-                // O^T: row j, columns t = 4 grp .. 4 grp + 3 of this wave
-                put4t(&myW[(16 * jb + m) * LDW + 4 * grp], y, 1.f);
+                for (int r = 0; r < 4; ++r) y[r] = nA[jb][r] * ia + nR[jb][r] * ir;
+                const int col = 16 * jb + 4 * grp;
+                buf_store4<T>(bo, pad_off<DV, DVR>(buf_off<T>(row, lo.rs, col), col), y);
             }
         }
-        wave_lds_sync();
-        // row t = m of this wave, columns 32 kk + 8 grp .. + 7
-#pragma unroll
-        for (int kk = 0; kk < DV / 32; ++kk) {
-            const int rb = 32 * kk + rA;
-            const Frag<T> x = join_frag<T>(lds_read_tr(&myW[rb * LDW + cA]), lds_read_tr(&myW[(rb + 4) * LDW + cA]));
-            buf_store16(bo, pad_off<DV, DVR>(buf_off<T>(row0 + 16 * wave + m, lo.rs, 32 * kk + 8 * grp), 32 * kk + 8 * grp), __builtin_bit_cast(uint4, x));
-        }
-        wave_lds_sync();
 
         // (c) R += phi(K)^T V on this wave's columns; z += sum_t phi(k_t) (wave 0)
 #pragma unroll
