@@ -1977,7 +1977,7 @@ __global__ __launch_bounds__((BwdQTile<DK, DV>::kThreads), (BwdQTile<DK, DV>::kM
     static_assert(Sh::kStages == 2, "the loop below is written for two stages");
     __shared__ __attribute__((aligned(16))) unsigned char smem[kFragBytes + kAreaBytes];
     __shared__ float red[3 * NW];
-    __shared__ __attribute__((aligned(16))) float sZ[DK];
+    __shared__ float sZ[DK];
 
     const int wid = xcd_remap(blockIdx.x, gridDim.x);
     const int64_t bh = wid / PB;
@@ -2869,8 +2869,7 @@ __global__ __launch_bounds__(kThreads, (CausalBwdShape<DK, DV>::kMinBlocks)) voi
     const float* __restrict__ pre, T* __restrict__ dq, float* __restrict__ wc, int* __restrict__ es,
     float* __restrict__ gpart, int64_t T_, const Layouts lay, int P, int64_t L, int nche, float eps) {
     using Sh = CausalBwdShape<DK, DV>;
-    constexpr int C = Sh::kChunk, LDK = Sh::kLDK, LDV = Sh::kLDV, LDRT = Sh::kLDRT, LDQT = Sh::kLDQT;
-    constexpr int LDW = Sh::kLDW;
+    constexpr int C = Sh::kChunk, LDK = Sh::kLDK, LDV = Sh::kLDV, LDRT = Sh::kLDRT;
     constexpr int NBI = DK / 16, NBV = DV / 16, NBC = C / 16;
     constexpr int RIW = DK / 64;  // 16-row blocks of R and of the G sum per wave
     constexpr int KSK = DK / 32, KSV = DV / 32, KSC = C / 32;
@@ -2884,9 +2883,8 @@ __global__ __launch_bounds__(kThreads, (CausalBwdShape<DK, DV>::kMinBlocks)) voi
     __shared__ __attribute__((aligned(16))) T tV[C * LDV];
     __shared__ __attribute__((aligned(16))) T tD[C * LDV];
     __shared__ __attribute__((aligned(16))) T tRT[DV * LDRT];
-    __shared__ __attribute__((aligned(16))) T tQT[DK * LDQT];
-    __shared__ __attribute__((aligned(16))) T tW[kWaves][Sh::kWRows * LDW];
-    __shared__ float sZ[DK];
+    __shared__ __attribute__((aligned(16))) T tQw[C * LDK];
+    __shared__ __attribute__((aligned(16))) float sZ[DK];
     __shared__ int sExpR[kWaves], sExpQ[kWaves];
 
     const int wid = xcd_remap(blockIdx.x, gridDim.x);
@@ -2904,7 +2902,7 @@ __global__ __launch_bounds__(kThreads, (CausalBwdShape<DK, DV>::kMinBlocks)) voi
     // R[16 (wave RIW + iR) + 4 grp + r][16 jb + m] in accR[iR][jb][r], z of
     // the same rows in accZ[iR][r], likewise the G sum in accG.
     f32x4 accR[RIW][NBV], accZ[RIW], accG[RIW][NBV];
-    float gzp[NBI];  // sum of c_t phi(q_t)[16 ib + m] over this lane's rows
+    float gzp[NBI][4];  // sum of c_t phi(q_t)[16 ib + 4 grp + r] over this lane's query rows
     {
         const float* pS = (pre != nullptr && p > 0) ? pre + (bh * P + p) * (int64_t)(DKR * DVR + DKR) : nullptr;
 #pragma unroll
@@ -2921,7 +2919,9 @@ __global__ __launch_bounds__(kThreads, (CausalBwdShape<DK, DV>::kMinBlocks)) voi
             for (int r = 0; r < 4; ++r) accZ[iR][r] = (pS && i0 + r < DKR) ? pS[DKR * DVR + i0 + r] : 0.f;
         }
 #pragma unroll
-        for (int ib = 0; ib < NBI; ++ib) gzp[ib] = 0.f;
+        for (int ib = 0; ib < NBI; ++ib)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) gzp[ib][r] = 0.f;
     }
     Frag<T> ones;
 #pragma unroll
@@ -2995,8 +2995,6 @@ __global__ __launch_bounds__(kThreads, (CausalBwdShape<DK, DV>::kMinBlocks)) voi
     };
 
     const int rA = 8 * grp + (m >> 2), cA = 4 * (m & 3);
-    T* myW = tW[wave];
-    const int tq = 16 * wave + 4 * grp;  // this lane's first result row in the chunk
     float* wcb = wc + 2 * (bh * T_ + t0);
     int* esb = es + (bh * P + p) * (int64_t)nche;
     auto body = [&](Stage& st, int c) {
@@ -3008,43 +3006,48 @@ __global__ __launch_bounds__(kThreads, (CausalBwdShape<DK, DV>::kMinBlocks)) voi
         issue(st, c + 1);  // past the segment end these read zeros
         sched_fence();
 
-        // (a) a[t][s] and b[t][s], t = tq + r, s = 16 jb + m, s <= t
+        // (a) a^T[s][t] = phi(k_s) . phi(q_t) and b^T[s][t] = v_s . dO_t for the
+        // wave's query rows t = 16 wave + m (one per lane) and the keys
+        // s = 16 sb + 4 grp + r of block sb (the lane's four values). With s
+        // along a lane's values these results are already operands of the
+        // contraction over s in (d). Slot i holds key block sb = (wave - i)
+        // mod 4: slot 0 is the diagonal block (masked to s <= t), slots
+        // 1 .. wave lie below it, and the slots past wave stay zero.
         f32x4 aa[NBC], bb[NBC];
 #pragma unroll
-        for (int jb = 0; jb < NBC; ++jb) {
-            aa[jb] = f32x4{0.f, 0.f, 0.f, 0.f};
-            bb[jb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int i = 0; i < NBC; ++i) {
+            aa[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+            bb[i] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
-        Frag<T> fd[KSV];
+        Frag<T> fd[KSV];  // dO row t
 #pragma unroll
         for (int ks = 0; ks < KSV; ++ks)
             fd[ks] = *reinterpret_cast<const Frag<T>*>(&tD[(16 * wave + m) * LDV + 32 * ks + 8 * grp]);
-        // slot i holds block jb = wave - i (slot 0 is the diagonal block,
-        // the only one masked); slots past wave are above the diagonal and
-        // stay zero
 #pragma unroll
         for (int ks = 0; ks < KSK; ++ks) {
-            const Frag<T> a = *reinterpret_cast<const Frag<T>*>(&tQ[(16 * wave + m) * LDK + 32 * ks + 8 * grp]);
+            const Frag<T> bq = *reinterpret_cast<const Frag<T>*>(&tQ[(16 * wave + m) * LDK + 32 * ks + 8 * grp]);
 #pragma unroll
             for (int i = 0; i < NBC; ++i)
                 if (i <= wave)
-                    aa[i] = mma(a, *reinterpret_cast<const Frag<T>*>(&tK[(16 * (wave - i) + m) * LDK + 32 * ks + 8 * grp]),
-                                aa[i]);
+                    aa[i] = mma(*reinterpret_cast<const Frag<T>*>(&tK[(16 * (wave - i) + m) * LDK + 32 * ks + 8 * grp]),
+                                bq, aa[i]);
         }
 #pragma unroll
         for (int ks = 0; ks < KSV; ++ks)
 #pragma unroll
             for (int i = 0; i < NBC; ++i)
                 if (i <= wave)
-                    bb[i] = mma(fd[ks], *reinterpret_cast<const Frag<T>*>(&tV[(16 * (wave - i) + m) * LDV + 32 * ks + 8 * grp]),
-                                bb[i]);
+                    bb[i] = mma(*reinterpret_cast<const Frag<T>*>(&tV[(16 * (wave - i) + m) * LDV + 32 * ks + 8 * grp]),
+                                fd[ks], bb[i]);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            aa[0][r] = m > 4 * grp + r ? 0.f : aa[0][r];
-            bb[0][r] = m > 4 * grp + r ? 0.f : bb[0][r];
+            const bool above = 4 * grp + r > m;
+            aa[0][r] = above ? 0.f : aa[0][r];
+            bb[0][r] = above ? 0.f : bb[0][r];
         }
 
-        // (b) Y = dO R^T, unscaled per column block
+        // (b) Y^T = R dO^T: rows i = 16 ib + 4 grp + r, column t; unscaled per
+        // row block
         f32x4 Y[NBI];
 #pragma unroll
         for (int ib = 0; ib < NBI; ++ib) Y[ib] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -3053,9 +3056,9 @@ __global__ __launch_bounds__(kThreads, (CausalBwdShape<DK, DV>::kMinBlocks)) voi
             const int rb = 32 * ks + rA;
 #pragma unroll
             for (int ib = 0; ib < NBI; ++ib) {
-                const Frag<T> b = join_frag<T>(lds_read_tr(&tRT[rb * LDRT + 16 * ib + cA]),
-                                               lds_read_tr(&tRT[(rb + 4) * LDRT + 16 * ib + cA]));
-                Y[ib] = mma(fd[ks], b, Y[ib]);
+                const Frag<T> ar = join_frag<T>(lds_read_tr(&tRT[rb * LDRT + 16 * ib + cA]),
+                                                lds_read_tr(&tRT[(rb + 4) * LDRT + 16 * ib + cA]));
+                Y[ib] = mma(ar, fd[ks], Y[ib]);
             }
         }
 #pragma unroll
@@ -3065,62 +3068,58 @@ __global__ __launch_bounds__(kThreads, (CausalBwdShape<DK, DV>::kMinBlocks)) voi
             for (int r = 0; r < 4; ++r) Y[ib][r] *= uR;
         }
 
-        // (c) phi(q) at the result positions; den, w and c per row
+        // (c) phi(q_t) at the lane's features i = 16 ib + 4 grp + r (one
+        // 8-byte read per block); den, w and c of the lane's query row: the
+        // lane's partial sums, then over the four lane groups (every lane of
+        // a row gets the same bits: the additions commute pairwise)
         float ph[NBI][4];
 #pragma unroll
-        for (int ib = 0; ib < NBI; ++ib)
+        for (int ib = 0; ib < NBI; ++ib) {
+            typedef T t4 __attribute__((ext_vector_type(4)));
+            const t4 x = *reinterpret_cast<const t4*>(&tQ[(16 * wave + m) * LDK + 16 * ib + 4 * grp]);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) ph[ib][r] = to_f32(tQ[(tq + r) * LDK + 16 * ib + m]);
-        float wr[4], cr[4];
+            for (int r = 0; r < 4; ++r) ph[ib][r] = to_f32(x[r]);
+        }
+        const bool okt = row0 + 16 * wave + m < len;
+        float w, cw;  // w_t and c_t of the lane's query row
         if constexpr (SIMPLE) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                wr[r] = row0 + tq + r < len ? eps : 0.f;  // simple_la: eps carries the query scale
-                cr[r] = 0.f;
-            }
+            w = okt ? eps : 0.f;  // simple_la: eps carries the query scale
+            cw = 0.f;
         } else {
-            float sa[4], sb[4];
+            float sa = 0.f, sb = 0.f;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                sa[r] = 0.f;
-                sb[r] = 0.f;
-                // blocks in ascending order: slots from the last down
+            for (int i = NBC - 1; i >= 0; --i)
+                if (i <= wave)
 #pragma unroll
-                for (int i = NBC - 1; i >= 0; --i)
-                    if (i <= wave) {
-                        sa[r] += aa[i][r];
-                        sb[r] += aa[i][r] * bb[i][r];
+                    for (int r = 0; r < 4; ++r) {
+                        sa += aa[i][r];
+                        sb += aa[i][r] * bb[i][r];
                     }
-            }
 #pragma unroll
             for (int ib = 0; ib < NBI; ++ib) {
-                const float zi = sZ[16 * ib + m];
+                const float4 z4 = *reinterpret_cast<const float4*>(&sZ[16 * ib + 4 * grp]);
+                const float zr[4] = {z4.x, z4.y, z4.z, z4.w};
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    sa[r] += ph[ib][r] * zi;
-                    sb[r] += ph[ib][r] * Y[ib][r];
+                    sa += ph[ib][r] * zr[r];
+                    sb += ph[ib][r] * Y[ib][r];
                 }
             }
-            float wst = 0.f, cst = 0.f;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const float den = row16_sum(sa[r]) + eps;
-                const float ru = row16_sum(sb[r]);
-                const bool ok = row0 + tq + r < len;
-                const float inv = __builtin_amdgcn_rcpf(den);  // v_rcp_f32, 1 ulp
-                wr[r] = ok ? inv : 0.f;
-                cr[r] = ok ? -ru * inv * inv : 0.f;
-                if (m == r) {
-                    wst = inv;
-                    cst = -ru * inv;
-                }
-            }
-            // w and c^ of row tq + m, by lanes m < 4
-            if (m < 4 && row0 + tq + m < len)
-                *reinterpret_cast<float2*>(&wcb[2 * (row0 + tq + m)]) = make_float2(wst, cst);
+            sa += __shfl_xor(sa, 16);
+            sb += __shfl_xor(sb, 16);
+            sa += __shfl_xor(sa, 32);
+            sb += __shfl_xor(sb, 32);
+            const float inv = __builtin_amdgcn_rcpf(sa + eps);  // v_rcp_f32, 1 ulp
+            w = okt ? inv : 0.f;
+            cw = okt ? -sb * inv * inv : 0.f;
+            // w and c^ = c / w of row t, by the lanes of group 0
+            if (grp == 0 && okt)
+                *reinterpret_cast<float2*>(&wcb[2 * (row0 + 16 * wave + m)]) = make_float2(inv, -sb * inv);
         }
 
-        // (d) P = mask(w b + c), staged transposed: rows s, columns t of this wave
+        // (d) P^T = mask(w b^T + c) in the slots of (a), rounded with a power of
+        // two to operands over the keys of slots 2 ks and 2 ks + 1 (values
+        // 0..3 of a lane from the first, 4..7 from the second), times phi(K)
         f32x4 pp[NBC];
         float pmx = 0.f;
 #pragma unroll
@@ -3129,63 +3128,68 @@ __global__ __launch_bounds__(kThreads, (CausalBwdShape<DK, DV>::kMinBlocks)) voi
             if (i <= wave) {  // blocks above the diagonal stay zero
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const float x = SIMPLE ? bb[i][r] : wr[r] * bb[i][r] + cr[r];
-                    pp[i][r] = i > 0 || m <= 4 * grp + r ? x : 0.f;
+                    const float x = SIMPLE ? bb[i][r] : w * bb[i][r] + cw;
+                    pp[i][r] = i > 0 || 4 * grp + r <= m ? x : 0.f;
                     pmx = fmaxf(pmx, fabsf(pp[i][r]));
                 }
             }
         }
         int sP = 0;
         if constexpr (Elt<T>::kScaled) sP = scale_exp(wave_max_nonneg(pmx));
+        Frag<T> bP[KSC];
         {
             const float fP = ldexpf(1.f, sP);
 #pragma unroll
-            for (int i = 0; i < NBC; ++i) put4t(&myW[(16 * ((wave - i) & (NBC - 1)) + m) * LDW + 4 * grp], pp[i], fP);
+            for (int ks = 0; ks < KSC; ++ks)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    bP[ks][r] = static_cast<T>(pp[2 * ks][r] * fP);
+                    bP[ks][4 + r] = static_cast<T>(pp[2 * ks + 1][r] * fP);
+                }
         }
-        wave_lds_sync();
+        // pk^T = phi(K)^T P^T: rows i = 16 ib + 4 grp + r, column t
         f32x4 pk[NBI];
 #pragma unroll
         for (int ib = 0; ib < NBI; ++ib) pk[ib] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const int rT = 4 * grp + (m >> 2), cT = 4 * (m & 3);
 #pragma unroll
         for (int ks = 0; ks < KSC; ++ks) {
-            if (ks <= wave / 2) {  // rows s >= 32 (ks + 1) of P are zero
-                const int rb = 32 * ks + rA;
-                const Frag<T> a = join_frag<T>(lds_read_tr(&myW[rb * LDW + cA]), lds_read_tr(&myW[(rb + 4) * LDW + cA]));
+            if (2 * ks <= wave) {  // otherwise both slots lie above the diagonal
+                const int r0 = 16 * ((wave - 2 * ks) & (NBC - 1)) + rT;
+                const int r1 = 16 * ((wave - 2 * ks - 1) & (NBC - 1)) + rT;
 #pragma unroll
                 for (int ib = 0; ib < NBI; ++ib) {
-                    const Frag<T> b = join_frag<T>(lds_read_tr(&tK[rb * LDK + 16 * ib + cA]),
-                                                   lds_read_tr(&tK[(rb + 4) * LDK + 16 * ib + cA]));
-                    pk[ib] = mma(a, b, pk[ib]);
+                    const Frag<T> ak = join_frag<T>(lds_read_tr(&tK[r0 * LDK + 16 * ib + cT]),
+                                                    lds_read_tr(&tK[r1 * LDK + 16 * ib + cT]));
+                    pk[ib] = mma(ak, bP[ks], pk[ib]);
                 }
             }
         }
 
-        // (e) dQ = (w Y + c z + P phi(K)) phi'(q), staged transposed, stored as rows
+        // (e) dQ^T = (w Y^T + c z + pk^T) phi'(q): the lane's four features of
+        // row t, one 8-byte store per block
         {
             const float uP = ldexpf(1.f, -sP);
-            f32x4 g[NBI];
+            const int64_t row = row0 + 16 * wave + m;
 #pragma unroll
             for (int ib = 0; ib < NBI; ++ib) {
-                const float zi = SIMPLE ? 0.f : sZ[16 * ib + m];
+                float zr[4] = {0.f, 0.f, 0.f, 0.f};
+                if constexpr (!SIMPLE) {
+                    const float4 z4 = *reinterpret_cast<const float4*>(&sZ[16 * ib + 4 * grp]);
+                    zr[0] = z4.x;
+                    zr[1] = z4.y;
+                    zr[2] = z4.z;
+                    zr[3] = z4.w;
+                }
+                f32x4 g;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const float d = SIMPLE ? wr[r] * (Y[ib][r] + pk[ib][r] * uP)
-                                           : wr[r] * Y[ib][r] + cr[r] * zi + pk[ib][r] * uP;
-                    g[ib][r] = d * dphi_of<FM>(ph[ib][r]);
+                    const float d = SIMPLE ? w * (Y[ib][r] + pk[ib][r] * uP) : w * Y[ib][r] + cw * zr[r] + pk[ib][r] * uP;
+                    g[r] = d * dphi_of<FM>(ph[ib][r]);
                 }
+                const int col = 16 * ib + 4 * grp;
+                buf_store4<T>(bdq, pad_off<DK, DKR>(buf_off<T>(row, lay.dq.rs, col), col), g);
             }
-            wave_lds_sync();
-#pragma unroll
-            for (int ib = 0; ib < NBI; ++ib) put4t(&myW[(16 * ib + m) * LDW + 4 * grp], g[ib], 1.f);
-            wave_lds_sync();
-            // row 16 wave + m, columns 32 kk + 8 grp .. + 7
-#pragma unroll
-            for (int kk = 0; kk < DK / 32; ++kk) {
-                const int rb = 32 * kk + rA;
-                const Frag<T> x = join_frag<T>(lds_read_tr(&myW[rb * LDW + cA]), lds_read_tr(&myW[(rb + 4) * LDW + cA]));
-                buf_store16(bdq, pad_off<DK, DKR>(buf_off<T>(row0 + 16 * wave + m, lay.dq.rs, 32 * kk + 8 * grp), 32 * kk + 8 * grp), __builtin_bit_cast(uint4, x));
-            }
-            wave_lds_sync();
         }
 
         // (f) R += phi(K)^T V and z += sum phi(k) on this wave's rows of R
@@ -3208,7 +3212,8 @@ __global__ __launch_bounds__(kThreads, (CausalBwdShape<DK, DV>::kMinBlocks)) voi
             }
         }
 
-        // (g) Qw of this wave's rows into Qw^T (rows i, columns t); c phi(q) into gzp
+        // (g) Qw = w phi(q) of the wave's query rows into the Qw tile (rows t,
+        // features i: one 8-byte store per block); c phi(q) into gzp
         {
             f32x4 qw[NBI];
             float qmx = 0.f;
@@ -3216,23 +3221,23 @@ __global__ __launch_bounds__(kThreads, (CausalBwdShape<DK, DV>::kMinBlocks)) voi
             for (int ib = 0; ib < NBI; ++ib)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    qw[ib][r] = ph[ib][r] * wr[r];
+                    qw[ib][r] = ph[ib][r] * w;
                     qmx = fmaxf(qmx, fabsf(qw[ib][r]));
                 }
             int sQ = 0;
             if constexpr (Elt<T>::kScaled) sQ = scale_exp_for_min(wave_max_nonneg(qmx));
             const float fQ = ldexpf(1.f, sQ);
 #pragma unroll
-            for (int ib = 0; ib < NBI; ++ib) put4t(&tQT[(16 * ib + m) * LDQT + tq], qw[ib], fQ);
+            for (int ib = 0; ib < NBI; ++ib) put4t(&tQw[(16 * wave + m) * LDK + 16 * ib + 4 * grp], qw[ib], fQ);
             if (lane == 0) sExpQ[wave] = sQ;
             if constexpr (!SIMPLE) {
 #pragma unroll
                 for (int ib = 0; ib < NBI; ++ib)
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) gzp[ib] += cr[r] * ph[ib][r];
+                    for (int r = 0; r < 4; ++r) gzp[ib][r] += cw * ph[ib][r];
             }
         }
-        __syncthreads();  // Qw^T and its four exponents are visible
+        __syncthreads();  // the Qw tile and its four exponents are visible
 
         // G += Qw^T dO on this wave's rows of the G sum, at the common exponent
         {
@@ -3246,8 +3251,9 @@ __global__ __launch_bounds__(kThreads, (CausalBwdShape<DK, DV>::kMinBlocks)) voi
                 Frag<T> qa[KSC];
 #pragma unroll
                 for (int ks = 0; ks < KSC; ++ks) {
-                    qa[ks] = *reinterpret_cast<const Frag<T>*>(&tQT[(i0 + m) * LDQT + 32 * ks + 8 * grp]);
-                    // columns 32 ks + 8 grp .. + 7 were staged by wave 2 ks + grp / 2
+                    const int rb = 32 * ks + rA;
+                    qa[ks] = join_frag<T>(lds_read_tr(&tQw[rb * LDK + i0 + cA]), lds_read_tr(&tQw[(rb + 4) * LDK + i0 + cA]));
+                    // tokens 32 ks + 8 grp .. + 7 were staged by wave 2 ks + grp / 2
                     if constexpr (Elt<T>::kScaled) qa[ks] = scale_frag<T>(qa[ks], ldexpf(1.f, sM - sExpQ[2 * ks + (grp >> 1)]));
                 }
 #pragma unroll
@@ -3288,15 +3294,16 @@ __global__ __launch_bounds__(kThreads, (CausalBwdShape<DK, DV>::kMinBlocks)) voi
                 for (int r = 0; r < 4; ++r)
                     if (i0 + r < DKR && 16 * jb + m < DVR) gp[(i0 + r) * DVR + 16 * jb + m] = accG[iR][jb][r];
         }
-        // g: the lanes' sums over their rows, then over the four waves in order
-        float* red = reinterpret_cast<float*>(&tW[0][0]);  // free after the last barrier
+        // g: the lanes' sums over their query rows (the 16 lanes of a group),
+        // then over the four waves in order
+        float* red = reinterpret_cast<float*>(tQ);  // free after the last barrier
 #pragma unroll
-        for (int ib = 0; ib < NBI; ++ib) {
-            float x = gzp[ib];
-            x += __shfl_xor(x, 16);
-            x += __shfl_xor(x, 32);
-            if (grp == 0) red[wave * DK + 16 * ib + m] = x;
-        }
+        for (int ib = 0; ib < NBI; ++ib)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float x = row16_sum(gzp[ib][r]);
+                if (m == 0) red[wave * DK + 16 * ib + 4 * grp + r] = x;
+            }
         __syncthreads();
         if (tid < DKR) gp[DKR * DVR + tid] = ((red[tid] + red[DK + tid]) + red[2 * DK + tid]) + red[3 * DK + tid];
     }
