@@ -2814,10 +2814,6 @@ struct CausalBwdShape {
     static constexpr int kLDK = DK + 16;      // tQ, tK row stride (elements)
     static constexpr int kLDV = DV + 16;      // tV, tD row stride
     static constexpr int kLDRT = DK + 8;      // R^T or G^T: rows j, DK entries
-    static constexpr int kLDQT = kChunk + 8;  // Qw^T: rows i, one chunk of tokens
-    static constexpr int kLDW = 24;           // per-wave transposed tiles: rows of 16 tokens
-    static constexpr int kMax = DK > DV ? DK : DV;
-    static constexpr int kWRows = kMax > kChunk ? kMax : kChunk;
     static constexpr int kMinBlocks = (DK == 64 && DV == 64) ? 2 : 1;
 };
 
@@ -3353,7 +3349,7 @@ __global__ __launch_bounds__(kThreads, (CausalBwdShape<DK, DV>::kMinBlocks)) voi
     const float* __restrict__ wc, const int* __restrict__ es, const float* __restrict__ suf, T* __restrict__ dk,
     T* __restrict__ dv, int64_t T_, const Layouts lay, int P, int64_t L, int nche, float qscale) {
     using Sh = CausalBwdShape<DK, DV>;
-    constexpr int C = Sh::kChunk, LDK = Sh::kLDK, LDV = Sh::kLDV, LDRT = Sh::kLDRT, LDW = Sh::kLDW;
+    constexpr int C = Sh::kChunk, LDK = Sh::kLDK, LDV = Sh::kLDV, LDRT = Sh::kLDRT;
     constexpr int NBI = DK / 16, NBV = DV / 16, NBC = C / 16;
     constexpr int RIW = DK / 64;
     constexpr int KSK = DK / 32, KSV = DV / 32, KSC = C / 32;
@@ -3368,7 +3364,6 @@ __global__ __launch_bounds__(kThreads, (CausalBwdShape<DK, DV>::kMinBlocks)) voi
     __shared__ __attribute__((aligned(16))) T tV[C * LDV];
     __shared__ __attribute__((aligned(16))) T tD[C * LDV];
     __shared__ __attribute__((aligned(16))) T tGT[DV * LDRT];
-    __shared__ __attribute__((aligned(16))) T tW[kWaves][Sh::kWRows * LDW];
     __shared__ __attribute__((aligned(16))) float sGz[DK];
     __shared__ __attribute__((aligned(16))) float sC[C];
     __shared__ int sExpG[kWaves];
@@ -3509,8 +3504,6 @@ __global__ __launch_bounds__(kThreads, (CausalBwdShape<DK, DV>::kMinBlocks)) voi
     };
 
     const int rA = 8 * grp + (m >> 2), cA = 4 * (m & 3);
-    T* myW = tW[wave];
-    const int ts = 16 * wave + 4 * grp;  // this lane's first result row (key) in the chunk
     auto body = [&](Stage& st, int n) {
         const int c = chunk_of(n);
         const int64_t row0 = (int64_t)c * C;
@@ -3523,17 +3516,20 @@ __global__ __launch_bounds__(kThreads, (CausalBwdShape<DK, DV>::kMinBlocks)) voi
         sched_fence();
         const float uQ = ldexpf(1.f, -sQ);
 
-        // (a) a~[s][t], b[s][t]: s = ts + r, t = 16 jb + m, t >= s. Slot i
-        // holds block jb = (wave + i) mod 4: slot 0 is the diagonal block,
-        // the only one masked; slots with wave + i past the last block are
-        // below the diagonal and stay zero.
+        // (a) a~^T[t][s] = Qw_t . phi(k_s) and b^T[t][s] = dO_t . v_s for the
+        // wave's keys s = 16 wave + m (one per lane) and the queries
+        // t = 16 tb + 4 grp + r of block tb (the lane's four values): with t
+        // along a lane's values these results are already operands of the
+        // contractions over t in (b) and (c). Slot i holds query block
+        // tb = wave + i: slot 0 is the diagonal block (masked to t >= s), and
+        // the slots with wave + i past the last block stay zero.
         f32x4 aa[NBC], bb[NBC];
 #pragma unroll
-        for (int jb = 0; jb < NBC; ++jb) {
-            aa[jb] = f32x4{0.f, 0.f, 0.f, 0.f};
-            bb[jb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int i = 0; i < NBC; ++i) {
+            aa[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+            bb[i] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
-        Frag<T> fk[KSK], fv[KSV];
+        Frag<T> fk[KSK], fv[KSV];  // phi(k_s), v_s
 #pragma unroll
         for (int ks = 0; ks < KSK; ++ks)
             fk[ks] = *reinterpret_cast<const Frag<T>*>(&tK[(16 * wave + m) * LDK + 32 * ks + 8 * grp]);
@@ -3545,44 +3541,67 @@ __global__ __launch_bounds__(kThreads, (CausalBwdShape<DK, DV>::kMinBlocks)) voi
 #pragma unroll
             for (int i = 0; i < NBC; ++i)
                 if (wave + i < NBC)
-                    aa[i] = mma(fk[ks], *reinterpret_cast<const Frag<T>*>(&tQ[(16 * (wave + i) + m) * LDK + 32 * ks + 8 * grp]),
-                                aa[i]);
+                    aa[i] = mma(*reinterpret_cast<const Frag<T>*>(&tQ[(16 * (wave + i) + m) * LDK + 32 * ks + 8 * grp]),
+                                fk[ks], aa[i]);
 #pragma unroll
         for (int ks = 0; ks < KSV; ++ks)
 #pragma unroll
             for (int i = 0; i < NBC; ++i)
                 if (wave + i < NBC)
-                    bb[i] = mma(fv[ks], *reinterpret_cast<const Frag<T>*>(&tD[(16 * (wave + i) + m) * LDV + 32 * ks + 8 * grp]),
-                                bb[i]);
+                    bb[i] = mma(*reinterpret_cast<const Frag<T>*>(&tD[(16 * (wave + i) + m) * LDV + 32 * ks + 8 * grp]),
+                                fv[ks], bb[i]);
         float pmx = 0.f, amx = 0.f;
 #pragma unroll
         for (int i = 0; i < NBC; ++i) {
-            if (wave + i >= NBC) continue;  // below the diagonal: a~ and b were never computed, stay zero
-            const float ch = SIMPLE ? 0.f : sC[16 * (wave + i) + m];
+            if (wave + i >= NBC) continue;  // below the diagonal: never computed, stay zero
+            float ch[4] = {0.f, 0.f, 0.f, 0.f};
+            if constexpr (!SIMPLE) {
+                const float4 c4 = *reinterpret_cast<const float4*>(&sC[16 * (wave + i) + 4 * grp]);
+                ch[0] = c4.x;
+                ch[1] = c4.y;
+                ch[2] = c4.z;
+                ch[3] = c4.w;
+            }
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const bool keep = i > 0 || m >= 4 * grp + r;
+                const bool keep = i > 0 || 4 * grp + r >= m;
                 aa[i][r] = keep ? aa[i][r] : 0.f;
-                bb[i][r] = keep ? bb[i][r] + ch : 0.f;  // now mask(b + c^)
+                bb[i][r] = keep ? bb[i][r] + ch[r] : 0.f;  // now mask(b + c^)
                 pmx = fmaxf(pmx, fabsf(bb[i][r]));
                 amx = fmaxf(amx, fabsf(aa[i][r]));
             }
         }
-        // phi(k) at the result positions
+        // phi(k_s) at the lane's features i = 16 ib + 4 grp + r
         float pk[NBI][4];
 #pragma unroll
-        for (int ib = 0; ib < NBI; ++ib)
+        for (int ib = 0; ib < NBI; ++ib) {
+            typedef T t4 __attribute__((ext_vector_type(4)));
+            const t4 x = *reinterpret_cast<const t4*>(&tK[(16 * wave + m) * LDK + 16 * ib + 4 * grp]);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) pk[ib][r] = to_f32(tK[(ts + r) * LDK + 16 * ib + m]);
+            for (int r = 0; r < 4; ++r) pk[ib][r] = to_f32(x[r]);
+        }
+        // operands over the queries of slots 2 ks and 2 ks + 1 (values 0..3 of
+        // a lane from the first, 4..7 from the second), read transposed from a
+        // query-major tile with the same order
+        const int rT = 4 * grp + (m >> 2), cT = 4 * (m & 3);
+        auto pack = [&](const f32x4 (&x)[NBC], int sx, Frag<T> (&f)[KSC]) {
+            const float fx = ldexpf(1.f, sx);
+#pragma unroll
+            for (int ks = 0; ks < KSC; ++ks)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    f[ks][r] = static_cast<T>(x[2 * ks][r] * fx);
+                    f[ks][4 + r] = static_cast<T>(x[2 * ks + 1][r] * fx);
+                }
+        };
+        const int64_t srow = row0 + 16 * wave + m;
 
-        // (b) dK
+        // (b) dK^T = Qw^T mask(b + c^)^T + G V^T + g, times phi'(k): rows i, column s
         {
             int sP = 0;
             if constexpr (Elt<T>::kScaled) sP = scale_exp(wave_max_nonneg(pmx));
-            const float fP = ldexpf(1.f, sP);
-#pragma unroll
-            for (int i = 0; i < NBC; ++i) put4t(&myW[(16 * ((wave + i) & (NBC - 1)) + m) * LDW + 4 * grp], bb[i], fP);
-            wave_lds_sync();
+            Frag<T> bP[KSC];
+            pack(bb, sP, bP);
             f32x4 x1[NBI], x2[NBI];
 #pragma unroll
             for (int ib = 0; ib < NBI; ++ib) {
@@ -3591,14 +3610,14 @@ __global__ __launch_bounds__(kThreads, (CausalBwdShape<DK, DV>::kMinBlocks)) voi
             }
 #pragma unroll
             for (int ks = 0; ks < KSC; ++ks) {
-                if (ks >= wave / 2) {  // rows t < 32 ks + 32 <= 16 wave of mask(b + c^) are zero
-                    const int rb = 32 * ks + rA;
-                    const Frag<T> a = join_frag<T>(lds_read_tr(&myW[rb * LDW + cA]), lds_read_tr(&myW[(rb + 4) * LDW + cA]));
+                if (wave + 2 * ks < NBC) {  // otherwise both slots lie below the diagonal
+                    const int r0 = 16 * ((wave + 2 * ks) & (NBC - 1)) + rT;
+                    const int r1 = 16 * ((wave + 2 * ks + 1) & (NBC - 1)) + rT;
 #pragma unroll
                     for (int ib = 0; ib < NBI; ++ib) {
-                        const Frag<T> b = join_frag<T>(lds_read_tr(&tQ[rb * LDK + 16 * ib + cA]),
-                                                       lds_read_tr(&tQ[(rb + 4) * LDK + 16 * ib + cA]));
-                        x1[ib] = mma(a, b, x1[ib]);
+                        const Frag<T> aq = join_frag<T>(lds_read_tr(&tQ[r0 * LDK + 16 * ib + cT]),
+                                                        lds_read_tr(&tQ[r1 * LDK + 16 * ib + cT]));
+                        x1[ib] = mma(aq, bP[ks], x1[ib]);
                     }
                 }
             }
@@ -3607,41 +3626,37 @@ __global__ __launch_bounds__(kThreads, (CausalBwdShape<DK, DV>::kMinBlocks)) voi
                 const int rb = 32 * ks + rA;
 #pragma unroll
                 for (int ib = 0; ib < NBI; ++ib) {
-                    const Frag<T> b = join_frag<T>(lds_read_tr(&tGT[rb * LDRT + 16 * ib + cA]),
-                                                   lds_read_tr(&tGT[(rb + 4) * LDRT + 16 * ib + cA]));
-                    x2[ib] = mma(fv[ks], b, x2[ib]);
+                    const Frag<T> ag = join_frag<T>(lds_read_tr(&tGT[rb * LDRT + 16 * ib + cA]),
+                                                    lds_read_tr(&tGT[(rb + 4) * LDRT + 16 * ib + cA]));
+                    x2[ib] = mma(ag, fv[ks], x2[ib]);
                 }
             }
             const float u1 = ldexpf(1.f, -sP) * uQ;
-            f32x4 g[NBI];
 #pragma unroll
             for (int ib = 0; ib < NBI; ++ib) {
                 const float u2 = ldexpf(1.f, -sExpG[ib / RIW]);
-                const float gz = SIMPLE ? 0.f : sGz[16 * ib + m];
+                float gz[4] = {0.f, 0.f, 0.f, 0.f};
+                if constexpr (!SIMPLE) {
+                    const float4 g4 = *reinterpret_cast<const float4*>(&sGz[16 * ib + 4 * grp]);
+                    gz[0] = g4.x;
+                    gz[1] = g4.y;
+                    gz[2] = g4.z;
+                    gz[3] = g4.w;
+                }
+                f32x4 g;
 #pragma unroll
-                for (int r = 0; r < 4; ++r) g[ib][r] = (x1[ib][r] * u1 + x2[ib][r] * u2 + gz) * dphi_of<FM>(pk[ib][r]);
+                for (int r = 0; r < 4; ++r) g[r] = (x1[ib][r] * u1 + x2[ib][r] * u2 + gz[r]) * dphi_of<FM>(pk[ib][r]);
+                const int col = 16 * ib + 4 * grp;
+                buf_store4<T>(bdk, pad_off<DK, DKR>(buf_off<T>(srow, lay.dk.rs, col), col), g);
             }
-            wave_lds_sync();
-#pragma unroll
-            for (int ib = 0; ib < NBI; ++ib) put4t(&myW[(16 * ib + m) * LDW + 4 * grp], g[ib], 1.f);
-            wave_lds_sync();
-#pragma unroll
-            for (int kk = 0; kk < DK / 32; ++kk) {
-                const int rb = 32 * kk + rA;
-                const Frag<T> x = join_frag<T>(lds_read_tr(&myW[rb * LDW + cA]), lds_read_tr(&myW[(rb + 4) * LDW + cA]));
-                buf_store16(bdk, pad_off<DK, DKR>(buf_off<T>(row0 + 16 * wave + m, lay.dk.rs, 32 * kk + 8 * grp), 32 * kk + 8 * grp), __builtin_bit_cast(uint4, x));
-            }
-            wave_lds_sync();
         }
 
-        // (c) dV = a~ dO + phi(K) G
+        // (c) dV^T = dO^T a~^T + G^T phi(K)^T: rows j, column s
         {
             int sA = 0;
             if constexpr (Elt<T>::kScaled) sA = scale_exp(wave_max_nonneg(amx));
-            const float fA = ldexpf(1.f, sA);
-#pragma unroll
-            for (int i = 0; i < NBC; ++i) put4t(&myW[(16 * ((wave + i) & (NBC - 1)) + m) * LDW + 4 * grp], aa[i], fA);
-            wave_lds_sync();
+            Frag<T> bA[KSC];
+            pack(aa, sA, bA);
             f32x4 y1[NBV], y2[NBV];
 #pragma unroll
             for (int jv = 0; jv < NBV; ++jv) {
@@ -3650,14 +3665,14 @@ __global__ __launch_bounds__(kThreads, (CausalBwdShape<DK, DV>::kMinBlocks)) voi
             }
 #pragma unroll
             for (int ks = 0; ks < KSC; ++ks) {
-                if (ks >= wave / 2) {
-                    const int rb = 32 * ks + rA;
-                    const Frag<T> a = join_frag<T>(lds_read_tr(&myW[rb * LDW + cA]), lds_read_tr(&myW[(rb + 4) * LDW + cA]));
+                if (wave + 2 * ks < NBC) {
+                    const int r0 = 16 * ((wave + 2 * ks) & (NBC - 1)) + rT;
+                    const int r1 = 16 * ((wave + 2 * ks + 1) & (NBC - 1)) + rT;
 #pragma unroll
                     for (int jv = 0; jv < NBV; ++jv) {
-                        const Frag<T> b = join_frag<T>(lds_read_tr(&tD[rb * LDV + 16 * jv + cA]),
-                                                       lds_read_tr(&tD[(rb + 4) * LDV + 16 * jv + cA]));
-                        y1[jv] = mma(a, b, y1[jv]);
+                        const Frag<T> ad = join_frag<T>(lds_read_tr(&tD[r0 * LDV + 16 * jv + cT]),
+                                                        lds_read_tr(&tD[r1 * LDV + 16 * jv + cT]));
+                        y1[jv] = mma(ad, bA[ks], y1[jv]);
                     }
                 }
             }
@@ -3666,30 +3681,22 @@ __global__ __launch_bounds__(kThreads, (CausalBwdShape<DK, DV>::kMinBlocks)) voi
 #pragma unroll
             for (int ks = 0; ks < KSK; ++ks) {
                 // features 32 ks + 8 grp .. + 7 of G^T were published by wave (32 ks + 8 grp) / QW
-                Frag<T> a = fk[ks];
-                if constexpr (Elt<T>::kScaled) a = scale_frag<T>(a, ldexpf(1.f, sM - sExpG[(32 * ks + 8 * grp) / QW]));
+                Frag<T> b = fk[ks];
+                if constexpr (Elt<T>::kScaled) b = scale_frag<T>(b, ldexpf(1.f, sM - sExpG[(32 * ks + 8 * grp) / QW]));
 #pragma unroll
                 for (int jv = 0; jv < NBV; ++jv)
-                    y2[jv] = mma(a, *reinterpret_cast<const Frag<T>*>(&tGT[(16 * jv + m) * LDRT + 32 * ks + 8 * grp]),
+                    y2[jv] = mma(*reinterpret_cast<const Frag<T>*>(&tGT[(16 * jv + m) * LDRT + 32 * ks + 8 * grp]), b,
                                  y2[jv]);
             }
             const float u1 = ldexpf(1.f, -sA) * uQ, u2 = ldexpf(1.f, -sM);
-            f32x4 g[NBV];
 #pragma unroll
-            for (int jv = 0; jv < NBV; ++jv)
+            for (int jv = 0; jv < NBV; ++jv) {
+                f32x4 g;
 #pragma unroll
-                for (int r = 0; r < 4; ++r) g[jv][r] = y1[jv][r] * u1 + y2[jv][r] * u2;
-            wave_lds_sync();
-#pragma unroll
-            for (int jv = 0; jv < NBV; ++jv) put4t(&myW[(16 * jv + m) * LDW + 4 * grp], g[jv], 1.f);
-            wave_lds_sync();
-#pragma unroll
-            for (int kk = 0; kk < DV / 32; ++kk) {
-                const int rb = 32 * kk + rA;
-                const Frag<T> x = join_frag<T>(lds_read_tr(&myW[rb * LDW + cA]), lds_read_tr(&myW[(rb + 4) * LDW + cA]));
-                buf_store16(bdv, pad_off<DV, DVR>(buf_off<T>(row0 + 16 * wave + m, lay.dv.rs, 32 * kk + 8 * grp), 32 * kk + 8 * grp), __builtin_bit_cast(uint4, x));
+                for (int r = 0; r < 4; ++r) g[r] = y1[jv][r] * u1 + y2[jv][r] * u2;
+                const int col = 16 * jv + 4 * grp;
+                buf_store4<T>(bdv, pad_off<DV, DVR>(buf_off<T>(srow, lay.dv.rs, col), col), g);
             }
-            wave_lds_sync();
         }
 
         // (d) G += Qw^T dO, g += Qw^T c^ on this wave's rows of G
