@@ -1661,9 +1661,10 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(
 // nothing, and drop their dQ stores.
 // Per step it computes u = S dO_t, den and dQ as the workgroup kernel above.
 // For the reduction over tokens it writes A_t = phi(q_t) 2^sw / den_t and the
-// raw dO_t row-major into its own LDS area, plus one more column
-// beta_t = -r_t / den_t next to dO, and reads them back transposed (4 tokens
-// per lane) as the operands of 16x16x16 MFMAs:
+// raw dO_t row-major into its own LDS area (one area per step of a turn),
+// plus one more column beta_t = -r_t / den_t next to dO; after the turn's two
+// steps it reads both back transposed (4 tokens of each step per lane) as
+// the operands of 16x16x32 MFMAs over the turn's 32 tokens:
 //   sum_t A_t dO_t^T = 2^sw dS   and   sum_t A_t beta_t = 2^sw dz
 // (c_t phi(q_t) = (-r_t / den_t)(phi(q_t) / den_t)), so dS and dz share one
 // operand and need no per-element work beyond the scaling of phi(q). Each
@@ -1687,7 +1688,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_w64_kernel(
     constexpr int NFR = NFS + (SIMPLE ? 0 : KS);
     constexpr int kFragBytes = NFR * 64 * 16;
     constexpr int LDO = D + 16 / (int)sizeof(T);  // dQ staging row stride
-    constexpr int kTileBytes = kWaves * (2 * STEP * LDR + 16 * LDO) * (int)sizeof(T);
+    // per wave: the A and dO tiles of the two steps of a turn, then the dQ staging
+    constexpr int kTileBytes = kWaves * (4 * STEP * LDR + 16 * LDO) * (int)sizeof(T);
     constexpr int kLoopBytes = kFragBytes + kTileBytes;
     constexpr int kRedBytes = 2 * E * (int)sizeof(float);
     __shared__ __attribute__((aligned(16))) unsigned char smem[kLoopBytes > kRedBytes ? kLoopBytes : kRedBytes];
@@ -1705,9 +1707,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_w64_kernel(
     const float* S = stS + bh * D * D;
     const float* z = stz + bh * D;
     Frag<T>* sA = reinterpret_cast<Frag<T>*>(smem);
-    T* sQ = reinterpret_cast<T*>(smem + kFragBytes) + wave * (2 * STEP * LDR + 16 * LDO);
-    T* sW = sQ + STEP * LDR;
-    T* sO = sW + STEP * LDR;
+    T* const sQ0 = reinterpret_cast<T*>(smem + kFragBytes) + wave * (4 * STEP * LDR + 16 * LDO);
+    T* const sO = sQ0 + 4 * STEP * LDR;
 
     // A stage holds the loaded words as they are; unpacked at the load, the
     // halves would be carried around the loop and unpacking them would wait
@@ -1774,7 +1775,10 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_w64_kernel(
         for (int j = 0; j < NJ; ++j) dsacc[b][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     const int rA = 4 * grp + (m >> 2), cA = 4 * (m & 3);
-    auto body = [&](Stage& st, int step) {
+    // step h of a turn writes its A and dO tiles to half h
+    auto body = [&](Stage& st, int step, int h) {
+        T* const sQ = sQ0 + h * 2 * STEP * LDR;
+        T* const sW = sQ + STEP * LDR;
         sched_fence();  // keeps this stage's unpacking out of the previous step
         Row<T, F> lq;
         __builtin_memcpy(lq.e, st.q, sizeof(lq));
@@ -1852,22 +1856,34 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_w64_kernel(
             for (int o = 0; o < F; ++o) out.e[o] = static_cast<T>(dqt[o] * dph[o]);
             store_tile_rows<T, D>(sO, out, bdq, (int64_t)rot(step) * STEP, lay.dq.rs);
         }
+    };
+    // sum over the 32 tokens of a turn on 16x16x32 MFMAs: values 0..3 of a
+    // lane are tokens 4 grp + (0..3) of the first step, values 4..7 the same
+    // rows of the second, in both operands
+    auto reduce_turn = [&]() {
+        const T* q0 = sQ0;
+        const T* w0 = sQ0 + STEP * LDR;
+        const T* q1 = sQ0 + 2 * STEP * LDR;
+        const T* w1 = q1 + STEP * LDR;
         wave_lds_sync();
-        i16x4 a[NB];
+        Frag<T> a[NB];
 #pragma unroll
-        for (int b = 0; b < NB; ++b) a[b] = lds_read_tr(&sQ[rA * LDR + 16 * b + cA]);
+        for (int b = 0; b < NB; ++b)
+            a[b] = join_frag<T>(lds_read_tr(&q0[rA * LDR + 16 * b + cA]), lds_read_tr(&q1[rA * LDR + 16 * b + cA]));
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
-            const i16x4 bw = lds_read_tr(&sW[rA * LDR + 16 * j + cA]);
+            const Frag<T> bw = join_frag<T>(lds_read_tr(&w0[rA * LDR + 16 * j + cA]), lds_read_tr(&w1[rA * LDR + 16 * j + cA]));
 #pragma unroll
-            for (int b = 0; b < NB; ++b) dsacc[b][j] = mma_k16<T>(a[b], bw, dsacc[b][j]);
+            for (int b = 0; b < NB; ++b) dsacc[b][j] = mma(a[b], bw, dsacc[b][j]);
         }
         wave_lds_sync();
     };
 
+    static_assert(BwdQW64::kStages == 2, "a turn is the two steps whose tiles reduce_turn reads");
     for (int st = wave; st < rot.npad; st += kStages * kWaves) {
 #pragma unroll
-        for (int i = 0; i < kStages; ++i) body(stg[i], st + i * kWaves);
+        for (int i = 0; i < kStages; ++i) body(stg[i], st + i * kWaves, i);
+        reduce_turn();
     }
 
     // fixed-order sum of the four waves: (w0 + w2) + (w1 + w3); column 0 of
