@@ -21,13 +21,16 @@
 //                      dz = sum_t c_t phi(q_t), combined like the forward state;
 //   bwd_dkv_kernel     dK = (V dS^T + dz) * phi'(K), dV = phi(K) dS.
 // The causal form (LA_CAUSAL; flash-linear-attention README, "Different forms
-// of linear attention"), 16-bit with DK, DV in {64, 128}, reuses the state
-// reduction per segment and adds:
+// of linear attention"), for every element type and head size up to 128,
+// reuses the state reduction per segment and adds:
 //   prefix_kernel, suffix_kernel  exclusive prefixes / suffixes of the
 //                      per-segment sums, in place;
-//   fwd_causal_kernel  the forward as a chunked scan of each segment;
+//   fwd_causal_kernel  the forward as a chunked scan of each segment (16-bit;
+//                      head sizes 32 and 96 run padded to 64 and 128);
 //   bwd_causal_q_kernel, bwd_causal_kv_kernel  the backward as a forward-order
-//                      scan (dQ) and a reverse-order scan (dK, dV).
+//                      scan (dQ) and a reverse-order scan (dK, dV);
+//   fwd_causal_f32_kernel, bwd_causal_q_f32_kernel, bwd_causal_kv_f32_kernel
+//                      the same scans on fp32 operands.
 // The optional query scale needs no kernel of its own (see Plan::eps).
 //
 // MFMA conventions (v_mfma_f32_16x16x32_{f16,bf16}; for fp32 operands eight
@@ -2428,20 +2431,23 @@ __global__ __launch_bounds__((StreamShape<T, DK, DV>::kThreads), (StreamShape<T,
 // with the running state R, z of everything before the chunk on chip:
 //   O_t = (phi(q_t) R + sum_{s in chunk, s <= t} a_ts v_s)
 //         / (phi(q_t) z + sum_{s in chunk, s <= t} a_ts + eps),  a_ts = phi(q_t) . phi(k_s),
-// then R += phi(K_c)^T V_c, z += sum phi(k). Per chunk, the four waves
-//   (a) each compute a = phi(Q) phi(K)^T for 16 query rows (blocks above the
-//       diagonal skipped, the diagonal block masked) and stage it transposed,
-//       scaled by a power of two, in their own LDS area;
-//   (b) multiply it by [V | 1] and phi(Q) by [R | z] (R^T and z as 16-bit
-//       copies in LDS) and store their 16 rows of O, staged transposed;
+// then R += phi(K_c)^T V_c, z += sum phi(k). Per chunk, the four waves each
+// take 16 query rows, one per lane (t = 16 wave + lane % 16), and
+//   (a) compute a^T = phi(K) phi(Q)^T for them (key blocks above the diagonal
+//       skipped, the diagonal block masked): in the MFMA result layout a
+//       lane holds four consecutive keys of its query, which is the operand
+//       layout of a contraction over keys, so a^T, rounded to 16 bits with a
+//       power of two, feeds (b) straight from registers;
+//   (b) compute O^T = [V | 1]^T a^T + [R | z]^T phi(Q)^T (V^T read
+//       transposed from the chunk tile in the same key order; R^T and z as
+//       16-bit copies in LDS), one reciprocal per lane, and store each lane's
+//       four consecutive features of its O row as one 8-byte piece;
 //   (c) add phi(K)^T V into their quarter of R's columns (fp32 registers;
 //       wave 0 also keeps z) and publish it, scaled by the wave's own power
 //       of two, into the other LDS copy of R^T for the next chunk.
-// Staging is transposed wherever a lane's four MFMA results are consecutive
-// in the transposed matrix: each is one 8-byte LDS store, and transposed
-// reads give the operands back. Two barriers per chunk; two chunks of loads
-// in flight. Rows past the segment end load as zeros (K is zeroed after phi)
-// and their stores are dropped.
+// Two barriers per chunk; two chunks of loads in flight. Rows past the
+// segment end load as zeros (K is zeroed after phi) and their stores are
+// dropped.
 // Four consecutive 16-bit values as one 8-byte LDS store.
 template <typename T>
 __device__ __forceinline__ void put4t(T* dst, f32x4 x, float f) {
@@ -2824,6 +2830,12 @@ __global__ __launch_bounds__(kThreads) void prefix_kernel(float* __restrict__ pa
 //   dphi(k_s) = G v_s + g + sum_{t>=s} (b_ts + c^_t) Qw_t
 //   dV_s = G^T phi(k_s) + sum_{t>=s} (Qw_t . phi(k_s)) dO_t
 // (R, z: everything before the chunk; G, g: everything after it).
+// Both scans work in the transposed form of the causal forward: a lane owns
+// one row of the chunk (a query in the dQ scan, a key in the K/V scan) and
+// holds four consecutive entries of the other index in each 16 x 16 result,
+// so a^T, b^T and the masked weights are the operands of the next
+// contraction as they come out of the MFMAs, and every output row leaves as
+// 8-byte pieces straight from the accumulators.
 template <int DK, int DV>
 struct CausalBwdShape {
     static constexpr int kChunk = 64;
