@@ -79,31 +79,40 @@ def test_packed_qkv_forward_backward(dtype, D, causal):
         check_vs_oracle(name, a.transpose(1, 2), r, dtype)
 
 
+@pytest.mark.parametrize("causal", [False, True], ids=["bidir", "causal"])
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
-def test_feature_slices_and_strided_outputs(dtype):
+def test_feature_slices_and_strided_outputs(dtype, causal):
     """[B, H, T, D] views taking D = 64 features out of 128-wide rows, with
     O and the gradients written into the other half of wider buffers, whose
-    untouched bytes keep their guard value."""
+    untouched bytes keep their guard value (the causal scans store their
+    outputs as 8-byte row pieces straight from the MFMA results)."""
     B, H, T, D = 2, 3, 2100, 64
-    seed = 98_100 + ["f16", "bf16"].index(dtype)
-    print(f"case feature slices B{B} H{H} T{T} D{D} {dtype} seed={seed}", flush=True)
+    seed = 98_100 + ["f16", "bf16"].index(dtype) + (2 if causal else 0)
+    print(f"case feature slices B{B} H{H} T{T} D{D} {dtype} causal={causal} seed={seed}", flush=True)
     wide = {n: to_device(normal((B, H, T, 2 * D), seed + i, 1.0, dtype), dtype)
             for i, n in enumerate(("q", "k", "v", "do"))}
     view = {n: t[..., D:] for n, t in wide.items()}
     outs = {n: torch.full((B, H, T, 2 * D), 7.0, dtype=TDT[dtype], device="cuda") for n in ("o", "dq", "dk", "dv")}
     ov = {n: t[..., :D] for n, t in outs.items()}
-    _, st = la.fwd(view["q"], view["k"], view["v"], out=ov["o"])
-    la.bwd(view["q"], view["k"], view["v"], view["do"], st, dq=ov["dq"], dk=ov["dk"], dv=ov["dv"])
+    _, st = la.fwd(view["q"], view["k"], view["v"], out=ov["o"], causal=causal)
+    la.bwd(view["q"], view["k"], view["v"], view["do"], None if causal else st, dq=ov["dq"], dk=ov["dk"],
+           dv=ov["dv"], causal=causal)
     dense = {n: t.contiguous() for n, t in view.items()}
-    o2, st2 = la.fwd(dense["q"], dense["k"], dense["v"])
-    g2 = la.bwd(dense["q"], dense["k"], dense["v"], dense["do"], st2)
+    o2, st2 = la.fwd(dense["q"], dense["k"], dense["v"], causal=causal)
+    g2 = la.bwd(dense["q"], dense["k"], dense["v"], dense["do"], None if causal else st2, causal=causal)
     torch.cuda.synchronize()
     assert bytes_equal(st, st2)
     for n, ref in zip(("o", "dq", "dk", "dv"), (o2,) + tuple(g2)):
         assert bytes_equal(ov[n].contiguous(), ref), n
         assert torch.all(outs[n][..., D:] == 7.0), f"{n}: bytes outside the view were written"
     x = {n: np.ascontiguousarray(decode(t, dtype)) for n, t in dense.items()}
-    o_ref = oracle.fwd(x["q"], x["k"], x["v"], "f32", 1e-6, False)[0]
+    if causal:
+        o_ref = oracle.causal_fwd(x["q"], x["k"], x["v"], "f32", 1e-6, False)[0]
+        g_ref = oracle.causal_bwd(x["q"], x["k"], x["v"], x["do"], "f32", 1e-6, False)
+        for name, a, r in zip(("dQ", "dK", "dV"), (ov["dq"], ov["dk"], ov["dv"]), g_ref):
+            check_vs_oracle(name, a, r, dtype)
+    else:
+        o_ref = oracle.fwd(x["q"], x["k"], x["v"], "f32", 1e-6, False)[0]
     check_vs_oracle("O", ov["o"], o_ref, dtype)
 
 
