@@ -2905,11 +2905,19 @@ __global__ __launch_bounds__(kThreads, (CausalBwdShape<DK, DV>::kMinBlocks)) voi
     __shared__ __attribute__((aligned(16))) T tQ[C * LDK];
     __shared__ __attribute__((aligned(16))) T tK[C * LDK];
     __shared__ __attribute__((aligned(16))) T tV[C * LDV];
-    __shared__ __attribute__((aligned(16))) T tD[C * LDV];
+    // With room in LDS the G update of a chunk runs in the next chunk (dO and
+    // Qw tiles double-buffered, one barrier less per chunk); at DK = DV = 128
+    // the second buffers do not fit and it runs after a barrier of its own.
+    constexpr bool kDefer = !(DK == 128 && DV == 128);
+    constexpr int NBUF = kDefer ? 2 : 1;
+    __shared__ __attribute__((aligned(16))) T tD[NBUF][C * LDV];
     __shared__ __attribute__((aligned(16))) T tRT[DV * LDRT];
-    __shared__ __attribute__((aligned(16))) T tQw[C * LDK];
+    // the Qw tiles' rows are 16 bytes longer than a row, not 32 as in tQ,
+    // which keeps two workgroups' LDS within a CU's at DK = DV = 64
+    constexpr int LDQ = DK + 8;
+    __shared__ __attribute__((aligned(16))) T tQw[NBUF][C * LDQ];
     __shared__ __attribute__((aligned(16))) float sZ[DK];
-    __shared__ int sExpR[kWaves], sExpQ[kWaves];
+    __shared__ int sExpR[kWaves], sExpQ[NBUF][kWaves];
 
     const int wid = xcd_remap(blockIdx.x, gridDim.x);
     const int64_t bh = wid / P;
@@ -3014,13 +3022,47 @@ __global__ __launch_bounds__(kThreads, (CausalBwdShape<DK, DV>::kMinBlocks)) voi
         for (int i = 0; i < NCV; ++i) {
             const int n = tid + kThreads * i, r = n / CV, cc = n % CV;
             *reinterpret_cast<u32x4*>(&tV[r * LDV + 8 * cc]) = st.v[i];
-            *reinterpret_cast<u32x4*>(&tD[r * LDV + 8 * cc]) = st.d[i];
+            *reinterpret_cast<u32x4*>(&tD[c % NBUF][r * LDV + 8 * cc]) = st.d[i];
         }
     };
 
     const int rA = 8 * grp + (m >> 2), cA = 4 * (m & 3);
     float* wcb = wc + 2 * (bh * T_ + t0);
     int* esb = es + (bh * P + p) * (int64_t)nche;
+    // G += Qw^T dO of chunk cg on this wave's rows of the G sum, at the
+    // chunk's common exponent (the smallest of the four waves' exponents)
+    auto gupdate = [&](int cg) {
+        const int bf = cg % NBUF;
+        int sM = 0;
+        if constexpr (Elt<T>::kScaled) sM = min(min(sExpQ[bf][0], sExpQ[bf][1]), min(sExpQ[bf][2], sExpQ[bf][3]));
+        if (tid == 0) esb[cg] = sM;
+        const float uM = ldexpf(1.f, -sM);
+#pragma unroll
+        for (int iR = 0; iR < RIW; ++iR) {
+            const int i0 = 16 * (wave * RIW + iR);
+            Frag<T> qa[KSC];
+#pragma unroll
+            for (int ks = 0; ks < KSC; ++ks) {
+                const int rb = 32 * ks + rA;
+                qa[ks] = join_frag<T>(lds_read_tr(&tQw[bf][rb * LDQ + i0 + cA]), lds_read_tr(&tQw[bf][(rb + 4) * LDQ + i0 + cA]));
+                // tokens 32 ks + 8 grp .. + 7 were staged by wave 2 ks + grp / 2
+                if constexpr (Elt<T>::kScaled) qa[ks] = scale_frag<T>(qa[ks], ldexpf(1.f, sM - sExpQ[bf][2 * ks + (grp >> 1)]));
+            }
+#pragma unroll
+            for (int jb = 0; jb < NBV; ++jb) {
+                f32x4 t = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < KSC; ++ks) {
+                    const int rb = 32 * ks + rA;
+                    const Frag<T> bd = join_frag<T>(lds_read_tr(&tD[bf][rb * LDV + 16 * jb + cA]),
+                                                    lds_read_tr(&tD[bf][(rb + 4) * LDV + 16 * jb + cA]));
+                    t = mma(qa[ks], bd, t);
+                }
+#pragma unroll
+                for (int r = 0; r < 4; ++r) accG[iR][jb][r] += t[r] * uM;
+            }
+        }
+    };
     auto body = [&](Stage& st, int c) {
         const int64_t row0 = (int64_t)c * C;
         publish();
@@ -3046,7 +3088,7 @@ __global__ __launch_bounds__(kThreads, (CausalBwdShape<DK, DV>::kMinBlocks)) voi
         Frag<T> fd[KSV];  // dO row t
 #pragma unroll
         for (int ks = 0; ks < KSV; ++ks)
-            fd[ks] = *reinterpret_cast<const Frag<T>*>(&tD[(16 * wave + m) * LDV + 32 * ks + 8 * grp]);
+            fd[ks] = *reinterpret_cast<const Frag<T>*>(&tD[c % NBUF][(16 * wave + m) * LDV + 32 * ks + 8 * grp]);
 #pragma unroll
         for (int ks = 0; ks < KSK; ++ks) {
             const Frag<T> bq = *reinterpret_cast<const Frag<T>*>(&tQ[(16 * wave + m) * LDK + 32 * ks + 8 * grp]);
@@ -3252,8 +3294,8 @@ __global__ __launch_bounds__(kThreads, (CausalBwdShape<DK, DV>::kMinBlocks)) voi
             if constexpr (Elt<T>::kScaled) sQ = scale_exp_for_min(wave_max_nonneg(qmx));
             const float fQ = ldexpf(1.f, sQ);
 #pragma unroll
-            for (int ib = 0; ib < NBI; ++ib) put4t(&tQw[(16 * wave + m) * LDK + 16 * ib + 4 * grp], qw[ib], fQ);
-            if (lane == 0) sExpQ[wave] = sQ;
+            for (int ib = 0; ib < NBI; ++ib) put4t(&tQw[c % NBUF][(16 * wave + m) * LDQ + 16 * ib + 4 * grp], qw[ib], fQ);
+            if (lane == 0) sExpQ[c % NBUF][wave] = sQ;
             if constexpr (!SIMPLE) {
 #pragma unroll
                 for (int ib = 0; ib < NBI; ++ib)
@@ -3261,41 +3303,13 @@ __global__ __launch_bounds__(kThreads, (CausalBwdShape<DK, DV>::kMinBlocks)) voi
                     for (int r = 0; r < 4; ++r) gzp[ib][r] += cw * ph[ib][r];
             }
         }
-        __syncthreads();  // the Qw tile and its four exponents are visible
-
-        // G += Qw^T dO on this wave's rows of the G sum, at the common exponent
-        {
-            int sM = 0;
-            if constexpr (Elt<T>::kScaled) sM = min(min(sExpQ[0], sExpQ[1]), min(sExpQ[2], sExpQ[3]));
-            if (tid == 0) esb[c] = sM;
-            const float uM = ldexpf(1.f, -sM);
-#pragma unroll
-            for (int iR = 0; iR < RIW; ++iR) {
-                const int i0 = 16 * (wave * RIW + iR);
-                Frag<T> qa[KSC];
-#pragma unroll
-                for (int ks = 0; ks < KSC; ++ks) {
-                    const int rb = 32 * ks + rA;
-                    qa[ks] = join_frag<T>(lds_read_tr(&tQw[rb * LDK + i0 + cA]), lds_read_tr(&tQw[(rb + 4) * LDK + i0 + cA]));
-                    // tokens 32 ks + 8 grp .. + 7 were staged by wave 2 ks + grp / 2
-                    if constexpr (Elt<T>::kScaled) qa[ks] = scale_frag<T>(qa[ks], ldexpf(1.f, sM - sExpQ[2 * ks + (grp >> 1)]));
-                }
-#pragma unroll
-                for (int jb = 0; jb < NBV; ++jb) {
-                    f32x4 t = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int ks = 0; ks < KSC; ++ks) {
-                        const int rb = 32 * ks + rA;
-                        const Frag<T> b = join_frag<T>(lds_read_tr(&tD[rb * LDV + 16 * jb + cA]),
-                                                       lds_read_tr(&tD[(rb + 4) * LDV + 16 * jb + cA]));
-                        t = mma(qa[ks], b, t);
-                    }
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) accG[iR][jb][r] += t[r] * uM;
-                }
-            }
+        if constexpr (kDefer) {
+            if (c > 0) gupdate(c - 1);  // its tiles are the other buffers
+        } else {
+            __syncthreads();  // the Qw tile and its four exponents are visible
+            gupdate(c);
         }
-        __syncthreads();  // every wave is done with the tiles, R^T, z and Qw^T
+        __syncthreads();  // every wave is done with this chunk's tiles, R^T, z and the older Qw, dO tiles
     };
     // One chunk of loads in flight (a chunk's work outlasts the load latency
     // many times over; a second stage only adds registers). The chunk count is
@@ -3306,6 +3320,7 @@ __global__ __launch_bounds__(kThreads, (CausalBwdShape<DK, DV>::kMinBlocks)) voi
         issue(st, 0);
         sched_fence();
         for (int c = 0; c < nchunks; ++c) body(st, c);
+        if constexpr (kDefer) gupdate(nchunks - 1);  // after the last chunk's closing barrier
     }
     if (gpart != nullptr) {
         float* gp = gpart + (bh * P + p) * (int64_t)(DKR * DVR + DKR);
@@ -3394,6 +3409,7 @@ __global__ __launch_bounds__(kThreads, (CausalBwdShape<DK, DV>::kMinBlocks)) voi
     __shared__ __attribute__((aligned(16))) T tGT[DV * LDRT];
     __shared__ __attribute__((aligned(16))) float sGz[DK];
     __shared__ __attribute__((aligned(16))) float sC[C];
+    __shared__ __attribute__((aligned(16))) T sCh[C];  // c^ as 16-bit operands, scaled by 2^scale_exp(max |c^|)
     __shared__ int sExpG[kWaves];
 
     const int wid = xcd_remap(blockIdx.x, gridDim.x);
@@ -3525,8 +3541,13 @@ __global__ __launch_bounds__(kThreads, (CausalBwdShape<DK, DV>::kMinBlocks)) voi
             *reinterpret_cast<u32x4*>(&tD[r * LDV + 8 * cc]) = st.d[i];
         }
         if constexpr (!SIMPLE) {
-            if (wave == 0) sC[lane] = cl;
             cmx = wave_max_nonneg(fabsf(cl));  // the same in every wave
+            if (wave == 0) {
+                int sC2 = 0;
+                if constexpr (Elt<T>::kScaled) sC2 = scale_exp(cmx);
+                sC[lane] = cl;
+                sCh[lane] = static_cast<T>(cl * ldexpf(1.f, sC2));
+            }
         }
         return sQ;
     };
@@ -3730,8 +3751,7 @@ __global__ __launch_bounds__(kThreads, (CausalBwdShape<DK, DV>::kMinBlocks)) voi
         // (d) G += Qw^T dO, g += Qw^T c^ on this wave's rows of G
         {
             int sC2 = 0;
-            if constexpr (!SIMPLE && Elt<T>::kScaled) sC2 = scale_exp(cmx);
-            const float fC = ldexpf(1.f, sC2);
+            if constexpr (!SIMPLE && Elt<T>::kScaled) sC2 = scale_exp(cmx);  // the scale of sCh
 #pragma unroll
             for (int iR = 0; iR < RIW; ++iR) {
                 const int i0 = 16 * (wave * RIW + iR);
@@ -3758,9 +3778,7 @@ __global__ __launch_bounds__(kThreads, (CausalBwdShape<DK, DV>::kMinBlocks)) voi
                     f32x4 t = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                     for (int ks = 0; ks < KSC; ++ks) {
-                        Frag<T> cf;
-#pragma unroll
-                        for (int e = 0; e < 8; ++e) cf[e] = static_cast<T>(sC[32 * ks + 8 * grp + e] * fC);
+                        const Frag<T> cf = *reinterpret_cast<const Frag<T>*>(&sCh[32 * ks + 8 * grp]);
                         t = mma(qa[ks], cf, t);
                     }
                     const float u = uQ * ldexpf(1.f, -sC2);
